@@ -1,0 +1,202 @@
+"""fp64 CPU oracle for fused causal multi-head self-attention.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import, call or
+execute this module: only the tests, the graft entry's smoke check and the
+benchmark's CPU-baseline leg use it.  It shares no code with the HIP kernels
+(neither side imports the other); both consume the seeded arrays produced by
+the `workloads` module.
+
+What it computes.  nanochat calls attention as
+flash_attn_func(q, k, v, causal=True, window_size=...) on (B, T, H, D)
+tensors (apidog blog "ChatGPTを50ドルで独自にトレーニングする方法" — "How to train
+your own ChatGPT for $50" — section 5 "Flash Attention integration"; the
+(B, T, n_kv_head, head_dim) view is in section 1 "GPT model"), and decodes
+through flash_attn_with_kvcache over a prefilled prompt cache (same blog,
+section 6 "inference engine").  The pages never write the formula out.  The
+readings taken here (plainest, all listed in the design notes):
+
+  * scaled dot-product attention, softmax over keys, scale s = 1/sqrt(D);
+  * causal = top-left aligned with T_q = T_k: key j visible to query i iff j <= i;
+  * full causal window (the long "L" layers of the SSSL pattern);
+  * n_kv_head = n_head (plain multi-head attention);
+  * LSE is the natural log of sum_j exp(s * q_i . k_j) over visible keys;
+  * the loss depends on O only, so the LSE output receives no gradient;
+  * decode: the single new query is the last cached position and sees all
+    L_b cached keys (bottom-right alignment); the cache already holds it.
+
+Everything is the plain definition in float64, one (batch, head) at a time,
+with dense T x T matrices; numpy's matmul is the only library primitive.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+__all__ = [
+    "softmax_scale", "forward_head", "backward_head", "forward", "backward",
+    "decode_head", "decode", "causal_probabilities",
+]
+
+
+def softmax_scale(D: int) -> float:
+    """s = 1/sqrt(D): the usual scaled-dot-product scale (FlashAttention's
+    default when no scale is passed, as in the call the blog shows)."""
+    return 1.0 / math.sqrt(D)
+
+
+def _scores(Q: np.ndarray, K: np.ndarray) -> np.ndarray:
+    """S_ij = s * <Q_i, K_j>, with S_ij = -inf where j > i (causal mask)."""
+    T, D = Q.shape
+    S = softmax_scale(D) * (Q @ K.T)
+    S[np.triu_indices(T, k=1, m=K.shape[0])] = -np.inf
+    return S
+
+
+def causal_probabilities(Q, K):
+    """P = softmax over keys of the masked scaled scores, and LSE per row.
+
+    Returns (P, lse) with P (T, T) and lse (T,) in float64.
+    """
+    Q = np.asarray(Q, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    S = _scores(Q, K)
+    m = S.max(axis=1)                     # row max over visible keys (finite: j = i)
+    E = np.exp(S - m[:, None])            # masked entries give exp(-inf) = 0
+    l = E.sum(axis=1)
+    P = E / l[:, None]
+    lse = m + np.log(l)
+    return P, lse
+
+
+def forward_head(Q, K, V):
+    """One (batch, head): O = softmax(s Q K^T + causal mask) V and LSE.
+
+    Q, K, V: (T, D).  Returns O (T, D) and lse (T,) in float64.
+    """
+    P, lse = causal_probabilities(Q, K)
+    O = P @ np.asarray(V, dtype=np.float64)
+    return O, lse
+
+
+def backward_head(Q, K, V, dO):
+    """Analytic gradients of L = sum(O * dO) for one (batch, head).
+
+    With P the attention probabilities (recomputed here), O = P V:
+      dV = P^T dO
+      dP = dO V^T
+      delta_i = sum_d dO_id O_id          (= sum_j P_ij dP_ij)
+      dS = P * (dP - delta)               (softmax Jacobian, row by row)
+      dQ = s dS K
+      dK = s dS^T Q
+    Returns dQ, dK, dV (T, D) and delta (T,), all float64.
+    """
+    Q = np.asarray(Q, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    dO = np.asarray(dO, dtype=np.float64)
+    s = softmax_scale(Q.shape[1])
+    P, _ = causal_probabilities(Q, K)
+    O = P @ V
+    dV = P.T @ dO
+    dP = dO @ V.T
+    delta = np.sum(dO * O, axis=1)
+    dS = P * (dP - delta[:, None])
+    dQ = s * (dS @ K)
+    dK = s * (dS.T @ Q)
+    return dQ, dK, dV, delta
+
+
+def _heads(x):
+    """(B, T, H, D) -> iterator over ((b, h), (T, D) float64 slice)."""
+    B, T, H, D = x.shape
+    for b in range(B):
+        for h in range(H):
+            yield (b, h), np.asarray(x[b, :, h, :], dtype=np.float64)
+
+
+def forward(q, k, v, heads=None):
+    """Batched forward over (B, T, H, D) arrays.
+
+    heads: optional iterable of (b, h) pairs; when given, only those heads are
+    computed and the result is a dict {(b, h): (O, lse)}.  Otherwise returns
+    o (B, T, H, D) and lse (B, H, T) in float64.
+    """
+    B, T, H, D = q.shape
+    if heads is not None:
+        return {(b, h): forward_head(q[b, :, h, :], k[b, :, h, :], v[b, :, h, :])
+                for (b, h) in heads}
+    o = np.empty((B, T, H, D), dtype=np.float64)
+    lse = np.empty((B, H, T), dtype=np.float64)
+    for b in range(B):
+        for h in range(H):
+            O, L = forward_head(q[b, :, h, :], k[b, :, h, :], v[b, :, h, :])
+            o[b, :, h, :] = O
+            lse[b, h, :] = L
+    return o, lse
+
+
+def backward(q, k, v, do, heads=None):
+    """Batched backward over (B, T, H, D) arrays.
+
+    Returns dq, dk, dv (B, T, H, D) and delta (B, H, T) in float64, or, when
+    `heads` is given, a dict {(b, h): (dQ, dK, dV, delta)} for those heads.
+    """
+    B, T, H, D = q.shape
+    if heads is not None:
+        return {(b, h): backward_head(q[b, :, h, :], k[b, :, h, :], v[b, :, h, :],
+                                      do[b, :, h, :]) for (b, h) in heads}
+    dq = np.empty((B, T, H, D), dtype=np.float64)
+    dk = np.empty_like(dq)
+    dv = np.empty_like(dq)
+    delta = np.empty((B, H, T), dtype=np.float64)
+    for b in range(B):
+        for h in range(H):
+            gq, gk, gv, dl = backward_head(q[b, :, h, :], k[b, :, h, :], v[b, :, h, :],
+                                           do[b, :, h, :])
+            dq[b, :, h, :] = gq
+            dk[b, :, h, :] = gk
+            dv[b, :, h, :] = gv
+            delta[b, h, :] = dl
+    return dq, dk, dv, delta
+
+
+def decode_head(q, K, V, L: int):
+    """Single-query attention over the first L cached keys of one head.
+
+    q: (D,), K, V: (T_cap, D).  z_j = s <q, K_j> for j < L; o = softmax(z) V[:L];
+    lse = logsumexp(z).  Rows >= L are never read.  L = 0 gives o = 0 and
+    lse = -inf (an empty softmax).
+    """
+    D = q.shape[0]
+    if L <= 0:
+        return np.zeros(D), -np.inf
+    q = np.asarray(q, dtype=np.float64)
+    Kl = np.asarray(K[:L], dtype=np.float64)
+    Vl = np.asarray(V[:L], dtype=np.float64)
+    z = softmax_scale(D) * (Kl @ q)
+    m = z.max()
+    e = np.exp(z - m)
+    l = e.sum()
+    return (e / l) @ Vl, m + math.log(l)
+
+
+def decode(q, k_cache, v_cache, seqlens, pairs=None):
+    """Batched decode.  q (B, H, D); caches (B, T_cap, H, D); seqlens int [B].
+
+    Returns o (B, H, D) and lse (B, H) in float64, or a dict {(b, h): (o, lse)}
+    when `pairs` lists the (b, h) pairs to compute.
+    """
+    B, H, D = q.shape
+    if pairs is not None:
+        return {(b, h): decode_head(q[b, h], k_cache[b, :, h, :], v_cache[b, :, h, :],
+                                    int(seqlens[b])) for (b, h) in pairs}
+    o = np.empty((B, H, D), dtype=np.float64)
+    lse = np.empty((B, H), dtype=np.float64)
+    for b in range(B):
+        for h in range(H):
+            ob, lb = decode_head(q[b, h], k_cache[b, :, h, :], v_cache[b, :, h, :],
+                                 int(seqlens[b]))
+            o[b, h] = ob
+            lse[b, h] = lb
+    return o, lse

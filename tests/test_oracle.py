@@ -1,0 +1,262 @@
+"""Pins for the fp64 oracle (CPU only).
+
+Each test ties the oracle to something other than itself: central finite
+differences, closed forms, invariants of softmax attention, an independent
+library routine (torch's CPU scaled_dot_product_attention and autograd in
+float64) and exact rational arithmetic.  A plausible slip in the oracle — a
+dropped scale, a wrong mask direction, a transposed operand, a missing delta
+term — fails at least one of them.
+"""
+import math
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+
+pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
+
+
+def rnd(shape, seed, scale=1.0):
+    return np.random.default_rng(seed).standard_normal(shape) * scale
+
+
+# ---------------------------------------------------------------- gradients
+
+def _loss(q, k, v, do):
+    o, _ = oracle.forward(q, k, v)
+    return float(np.sum(o * do))
+
+
+@pytest.mark.parametrize("T,D", [(1, 4), (2, 4), (5, 4), (8, 4), (2, 8), (5, 8), (8, 8)])
+def test_finite_differences_all_entries(T, D):
+    """Analytic gradients equal central differences of sum(O * dO)."""
+    B, H = 1, 2
+    q, k, v, do = (rnd((B, T, H, D), s) for s in (1, 2, 3, 4))
+    dq, dk, dv, _ = oracle.backward(q, k, v, do)
+    eps = 1e-6
+    for x, g in ((q, dq), (k, dk), (v, dv)):
+        fd = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            old = x[idx]
+            x[idx] = old + eps
+            lp = _loss(q, k, v, do)
+            x[idx] = old - eps
+            lm = _loss(q, k, v, do)
+            x[idx] = old
+            fd[idx] = (lp - lm) / (2 * eps)
+        # relative 1e-6, plus an absolute floor for gradients that vanish
+        # (T = 1: dQ and dK are identically zero) where only FD noise is left
+        assert np.linalg.norm(fd - g) <= 1e-6 * np.linalg.norm(g) + 1e-8 * math.sqrt(g.size)
+
+
+def test_finite_differences_sampled_d128():
+    """Sampled entries at the real head dim D = 128, T = 16."""
+    B, T, H, D = 1, 16, 2, 128
+    q, k, v = (rnd((B, T, H, D), s, 0.5) for s in (11, 12, 13))
+    do = rnd((B, T, H, D), 14)
+    dq, dk, dv, _ = oracle.backward(q, k, v, do)
+    rng = np.random.default_rng(15)
+    eps = 1e-6
+    for x, g in ((q, dq), (k, dk), (v, dv)):
+        for _ in range(12):
+            idx = tuple(int(rng.integers(0, n)) for n in x.shape)
+            old = x[idx]
+            x[idx] = old + eps
+            lp = _loss(q, k, v, do)
+            x[idx] = old - eps
+            lm = _loss(q, k, v, do)
+            x[idx] = old
+            fd = (lp - lm) / (2 * eps)
+            assert abs(fd - g[idx]) <= 1e-6 * max(1.0, abs(g[idx])), (idx, fd, g[idx])
+
+
+# ---------------------------------------------------------------- forward closed forms
+
+def test_probabilities_rows_sum_to_one_and_are_causal():
+    """With V = I the output is P itself: rows sum to 1, upper triangle 0."""
+    T = 24
+    Q, K = rnd((T, 32), 21), rnd((T, 32), 22)
+    V = np.eye(T, 32)
+    O, _ = oracle.forward_head(Q, K, V)
+    P = O[:, :T]
+    assert np.all(np.abs(P.sum(axis=1) - 1.0) <= 1e-12)
+    assert np.all(P[np.triu_indices(T, 1)] == 0.0)
+    assert np.all(P >= 0.0)
+    P2, _ = oracle.causal_probabilities(Q, K)
+    assert np.allclose(P, P2, rtol=0, atol=1e-15)
+
+
+def test_q_zero_gives_running_mean_and_log_count():
+    """Q = 0: every visible score is 0, so P_ij = 1/(i+1), O_i is the mean of
+    V_0..V_i and LSE_i = ln(i+1).  Same for K = 0."""
+    T, D = 40, 16
+    V = rnd((T, D), 31)
+    mean = np.cumsum(V, axis=0) / np.arange(1, T + 1)[:, None]
+    for Q, K in ((np.zeros((T, D)), rnd((T, D), 32)), (rnd((T, D), 33), np.zeros((T, D)))):
+        O, lse = oracle.forward_head(Q, K, V)
+        assert np.allclose(O, mean, rtol=0, atol=1e-13)
+        if not Q.any():
+            assert np.allclose(lse, np.log(np.arange(1, T + 1)), rtol=0, atol=1e-14)
+
+
+def test_row_zero_and_single_token():
+    T, D = 9, 128
+    Q, K, V = rnd((T, D), 41), rnd((T, D), 42), rnd((T, D), 43)
+    O, lse = oracle.forward_head(Q, K, V)
+    assert np.array_equal(O[0], V[0])               # only key 0 is visible
+    dot = sum(float(a) * float(b) for a, b in zip(Q[0], K[0]))
+    assert abs(lse[0] - dot / math.sqrt(D)) <= 1e-12
+    O1, lse1 = oracle.forward_head(Q[:1], K[:1], V[:1])   # T = 1: O = V
+    assert np.array_equal(O1, V[:1])
+
+
+def test_exact_rational_weights():
+    """D = 4, so s = 1/2.  With q_i = (2 ln 2, 0, 0, 0) and k_j = (j, ...),
+    s q_i.k_j = j ln 2, so the visible weights of row i are 2^j / (2^(i+1) - 1)
+    and LSE_i = ln(2^(i+1) - 1).  Expected values are exact rationals."""
+    T, D = 6, 4
+    Q = np.zeros((T, D))
+    Q[:, 0] = 2 * math.log(2.0)
+    K = np.zeros((T, D))
+    K[:, 0] = np.arange(T)
+    K[:, 1:] = rnd((T, D - 1), 51)                  # orthogonal to q: no effect
+    Vint = np.random.default_rng(52).integers(-9, 10, size=(T, D))
+    O, lse = oracle.forward_head(Q, K, Vint.astype(np.float64))
+    for i in range(T):
+        den = 2 ** (i + 1) - 1
+        for d in range(D):
+            exact = Fraction(sum(2 ** j * int(Vint[j, d]) for j in range(i + 1)), den)
+            assert abs(O[i, d] - float(exact)) <= 1e-13
+        assert abs(lse[i] - math.log(den)) <= 1e-13
+
+
+def test_constant_and_affine_v():
+    T, D = 33, 64
+    Q, K = rnd((T, D), 61), rnd((T, D), 62)
+    v = rnd((D,), 63)
+    O, _ = oracle.forward_head(Q, K, np.tile(v, (T, 1)))
+    assert np.allclose(O, np.tile(v, (T, 1)), rtol=0, atol=1e-13)
+    V = rnd((T, D), 64)
+    a, b = -1.7, rnd((D,), 65)
+    O1, _ = oracle.forward_head(Q, K, V)
+    O2, _ = oracle.forward_head(Q, K, a * V + b)
+    assert np.allclose(O2, a * O1 + b, rtol=0, atol=1e-12)
+
+
+def test_key_shift_invariance():
+    """Adding u to every key shifts row i's scores by s<Q_i,u>: O unchanged,
+    LSE_i shifted by exactly that amount."""
+    T, D = 30, 128
+    Q, K, V = rnd((T, D), 71), rnd((T, D), 72), rnd((T, D), 73)
+    u = rnd((D,), 74)
+    O1, l1 = oracle.forward_head(Q, K, V)
+    O2, l2 = oracle.forward_head(Q, K + u, V)
+    assert np.allclose(O1, O2, rtol=0, atol=1e-12)
+    assert np.allclose(l2 - l1, (Q @ u) / math.sqrt(D), rtol=0, atol=1e-11)
+
+
+def test_causal_independence_bitwise():
+    """Changing keys and values after position t leaves rows <= t bit-identical."""
+    B, T, H, D = 2, 50, 3, 32
+    q, k, v = (rnd((B, T, H, D), s) for s in (81, 82, 83))
+    o1, l1 = oracle.forward(q, k, v)
+    t = 20
+    k2, v2 = k.copy(), v.copy()
+    k2[:, t + 1:] = rnd(k2[:, t + 1:].shape, 84) * 5
+    v2[:, t + 1:] = rnd(v2[:, t + 1:].shape, 85) * 5
+    o2, l2 = oracle.forward(q, k2, v2)
+    assert np.array_equal(o1[:, :t + 1], o2[:, :t + 1])
+    assert np.array_equal(l1[:, :, :t + 1], l2[:, :, :t + 1])
+    assert not np.array_equal(o1[:, t + 1:], o2[:, t + 1:])
+
+
+# ---------------------------------------------------------------- library routine
+
+@pytest.mark.parametrize("B,T,H,D", [(2, 37, 3, 16), (1, 64, 2, 128), (1, 1, 1, 8)])
+def test_against_torch_sdpa_fp64(B, T, H, D):
+    """torch's CPU scaled_dot_product_attention (is_causal, default scale
+    1/sqrt(D)) and its autograd, in float64: an independent implementation."""
+    torch = pytest.importorskip("torch")
+    q, k, v, do = (rnd((B, T, H, D), s) for s in (91, 92, 93, 94))
+    o, lse = oracle.forward(q, k, v)
+    dq, dk, dv, _ = oracle.backward(q, k, v, do)
+    tq, tk, tv = (torch.tensor(x.transpose(0, 2, 1, 3).copy(), dtype=torch.float64,
+                               requires_grad=True) for x in (q, k, v))
+    to = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=True)
+    to.backward(torch.tensor(do.transpose(0, 2, 1, 3).copy(), dtype=torch.float64))
+    back = lambda t: t.detach().numpy().transpose(0, 2, 1, 3)  # noqa: E731
+    assert np.allclose(o, back(to), rtol=0, atol=1e-12)
+    assert np.allclose(dq, back(tq.grad), rtol=0, atol=1e-11)
+    assert np.allclose(dk, back(tk.grad), rtol=0, atol=1e-11)
+    assert np.allclose(dv, back(tv.grad), rtol=0, atol=1e-11)
+    # LSE: logsumexp of torch-computed masked scores
+    S = torch.einsum("bhid,bhjd->bhij", tq.detach(), tk.detach()) / math.sqrt(D)
+    S = S.masked_fill(torch.triu(torch.ones(T, T, dtype=torch.bool), 1), float("-inf"))
+    assert np.allclose(lse, torch.logsumexp(S, dim=-1).numpy(), rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------- gradient invariants
+
+def test_gradient_invariants():
+    T, D = 45, 128
+    Q, K, V, dO = (rnd((T, D), s, 0.7) for s in (101, 102, 103, 104))
+    dQ, dK, dV, delta = oracle.backward_head(Q, K, V, dO)
+    # rows of P sum to 1  =>  sum_j dV_j = sum_i dO_i
+    assert np.allclose(dV.sum(axis=0), dO.sum(axis=0), rtol=0, atol=1e-11)
+    # rows of dS sum to 0  =>  sum_j dK_j = 0
+    assert np.allclose(dK.sum(axis=0), 0.0, rtol=0, atol=1e-11)
+    # query 0 sees one key: its softmax is constant, so dQ_0 = 0
+    assert np.allclose(dQ[0], 0.0, rtol=0, atol=1e-14)
+    # delta equals rowsum(dO * O) with O from the forward
+    O, _ = oracle.forward_head(Q, K, V)
+    assert np.allclose(delta, np.sum(dO * O, axis=1), rtol=0, atol=1e-12)
+
+
+def test_constant_v_kills_q_and_k_gradients():
+    T, D = 20, 32
+    Q, K, dO = rnd((T, D), 111), rnd((T, D), 112), rnd((T, D), 113)
+    V = np.tile(rnd((D,), 114), (T, 1))
+    dQ, dK, dV, _ = oracle.backward_head(Q, K, V, dO)
+    assert np.allclose(dQ, 0.0, atol=1e-13) and np.allclose(dK, 0.0, atol=1e-13)
+
+
+def test_q_zero_dv_closed_form():
+    """Q = 0: P_ij = 1/(i+1), so dV_j = sum_{i>=j} dO_i / (i+1)."""
+    T, D = 25, 16
+    K, V, dO = rnd((T, D), 121), rnd((T, D), 122), rnd((T, D), 123)
+    _, _, dV, _ = oracle.backward_head(np.zeros((T, D)), K, V, dO)
+    w = dO / np.arange(1, T + 1)[:, None]
+    expect = np.cumsum(w[::-1], axis=0)[::-1]
+    assert np.allclose(dV, expect, rtol=0, atol=1e-13)
+
+
+# ---------------------------------------------------------------- decode
+
+def test_decode_equals_last_forward_row_and_ignores_tail():
+    B, Tc, H, D = 3, 40, 2, 128
+    q = rnd((B, H, D), 131, 0.5)
+    kc, vc = rnd((B, Tc, H, D), 132, 0.5), rnd((B, Tc, H, D), 133, 0.5)
+    lens = np.array([1, 17, 40])
+    kp, vp = kc.copy(), vc.copy()
+    for b, L in enumerate(lens):          # poison rows the decode must not read
+        kp[b, L:] = np.nan
+        vp[b, L:] = np.nan
+    o, lse = oracle.decode(q, kp, vp, lens)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    for b, L in enumerate(lens):
+        for h in range(H):
+            Qf = kc[b, :L, h, :].copy()
+            Qf[L - 1] = q[b, h]           # the decoded query is position L-1
+            O, l = oracle.forward_head(Qf, kc[b, :L, h, :], vc[b, :L, h, :])
+            assert np.allclose(o[b, h], O[L - 1], rtol=0, atol=1e-13)
+            assert abs(lse[b, h] - l[L - 1]) <= 1e-13
+    # L = 1: o = V_0 and lse = s <q, k_0>
+    assert np.array_equal(o[0, 0], vc[0, 0, 0])
+    assert abs(lse[0, 1] - np.dot(q[0, 1], kc[0, 0, 1]) / math.sqrt(D)) <= 1e-13
+
+
+def test_decode_empty_sequence():
+    o, l = oracle.decode_head(np.ones(8), np.ones((4, 8)), np.ones((4, 8)), 0)
+    assert np.array_equal(o, np.zeros(8)) and l == -np.inf
