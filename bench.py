@@ -1,0 +1,283 @@
+#!/usr/bin/env python3
+"""Benchmark of the causal self-attention hot path on one MI355X.
+
+One step = one pass of the training hot path at the d20 shape
+(B=32, T=2048, H=10, D=128, bf16): the forward (o, lse) and the backward
+(delta, dk/dv, dq) through the C ABI.  Inputs are the seeded synthetic
+tensors of the `workloads` module, resident in HBM before timing starts.
+W untimed warmup steps, then exactly K timed steps between
+torch.cuda.synchronize() calls; per-kernel durations come from HIP events
+recorded on the launch stream around every kernel.
+
+The single-token decode over the ragged d20 cache (B=64, H=10, lengths
+uniform in [1, 2048]) is timed in its own loop and reported under "decode";
+it rotates three separately allocated caches so that no call finds its
+cache in the 256 MB Infinity Cache.
+
+The fp64 oracle runs once on a bounded sample of the same workload on the
+host cores and is reported as "cpu_baseline" (a reported baseline, not the
+target).
+
+Prints ONE JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = ("causal attn fwd+bwd TFLOP/s @ d20 (B32,T2048,H10,D128) + % bf16 peak; "
+          "decode GB/s")
+PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, published
+
+
+class HipEvents:
+    """Raw hipEvent_t handles from the HIP runtime torch has loaded."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self, n):
+        evs = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            assert self.hip.hipEventCreate(ctypes.byref(e)) == 0
+            evs.append(e)
+        return evs
+
+    def record(self, e, stream):
+        assert self.hip.hipEventRecord(e, stream) == 0
+
+    def ms(self, a, b):
+        assert self.hip.hipEventSynchronize(b) == 0
+        out = ctypes.c_float()
+        assert self.hip.hipEventElapsedTime(ctypes.byref(out), a, b) == 0
+        return float(out.value)
+
+
+def train_flops(B, T, H, D):
+    """Algorithmic FLOPs (causal = half of dense): fwd 2 matmuls, bwd 5."""
+    unit = B * H * T * T * D   # one causal matmul: 2 * (T^2 / 2) * D per (b, h)
+    return {"fwd": 2 * unit, "delta": 0, "dkdv": 4 * unit, "dq": 1 * unit, "fwd+bwd": 7 * unit}
+
+
+def cpu_baseline(inp, n_heads):
+    """Time the fp64 oracle (as it stands) on the first n_heads (b, h) heads."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max(i.get("num_threads", 1) for i in threadpool_info()) or 1
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count()
+    B, T, H, D = inp.shape
+    heads = [(b, h) for b in range(B) for h in range(H)][:n_heads]
+    t0 = time.perf_counter()
+    oracle.forward(inp.q, inp.k, inp.v, heads=heads)
+    oracle.backward(inp.q, inp.k, inp.v, inp.do, heads=heads)
+    dt = time.perf_counter() - t0
+    flops = 7 * len(heads) * T * T * D
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": (f"fp64 numpy oracle fwd+bwd on {len(heads)} of {B * H} (b,h) heads of the "
+                       f"d20 workload (T={T}), {dt:.1f} s wall, algorithmic FLOPs as the GPU"),
+            "seconds": round(dt, 3)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--decode-iters", type=int, default=60)
+    ap.add_argument("--cpu-heads", type=int, default=48,
+                    help="(b,h) heads in the oracle CPU-baseline sample (0 = skip)")
+    ap.add_argument("--no-decode", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (--gpus {args.gpus} requested); "
+              "the attention hot path has no cross-GPU step, see the design notes on sharding",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import causal_self_attention_mha_amd as na
+    import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    lib = na.load_library()
+    ev = HipEvents()
+
+    def log(msg):
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+    # ---------------- training step inputs (resident in HBM)
+    cfg = W.CONFIGS[W.HEADLINE]
+    B, T, H, D = cfg.B, cfg.T, cfg.H, cfg.D
+    log(f"generating d20 inputs B={B} T={T} H={H} D={D}")
+    inp = W.make_train_inputs(cfg)
+
+    def dev_t(store):
+        return torch.from_numpy(store.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    q, k, v, do = (dev_t(x) for x in (inp.q_store, inp.k_store, inp.v_store, inp.do_store))
+    o = torch.empty_like(q)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    lse = torch.empty((B, H, T), dtype=torch.float32, device=dev)
+    delta = torch.empty_like(lse)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    P = ctypes.c_void_p
+    ptr = lambda t: P(t.data_ptr())  # noqa: E731
+
+    n_total = args.warmup + args.steps
+    evs = [ev.create(5) for _ in range(n_total)]
+    ev_arr = [(ctypes.c_void_p * 4)(*[e.value for e in step[1:5]]) for step in evs]
+
+    def step(i):
+        e = evs[i]
+        ev.record(e[0], stream)
+        st = lib.na_attn_fwd(ptr(q), ptr(k), ptr(v), ptr(o), ptr(lse), B, T, H, D, P(stream))
+        if st:
+            raise RuntimeError(lib.na_last_error().decode())
+        st = lib.na_attn_bwd_timed(ptr(q), ptr(k), ptr(v), ptr(o), ptr(do), ptr(lse), ptr(dq),
+                                   ptr(dk), ptr(dv), ptr(delta), B, T, H, D, P(stream),
+                                   ctypes.cast(ev_arr[i], P))
+        if st:
+            raise RuntimeError(lib.na_last_error().decode())
+
+    log(f"warmup {args.warmup} steps")
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} steps")
+    t0 = time.perf_counter()
+    for i in range(args.warmup, n_total):
+        step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    names = ["fwd", "delta", "dkdv", "dq"]
+    per = {n: [] for n in names}
+    step_ms = []
+    for i in range(args.warmup, n_total):
+        e = evs[i]
+        for j, n in enumerate(names):
+            per[n].append(ev.ms(e[j], e[j + 1]))
+        step_ms.append(ev.ms(e[0], e[4]))
+    ms_per_step = float(np.mean(step_ms))
+    fl = train_flops(B, T, H, D)
+    tflops = fl["fwd+bwd"] / (ms_per_step * 1e-3) / 1e12
+    kern = {}
+    for n in names:
+        avg = float(np.mean(per[n]))
+        kern[n] = {"avg_us": round(avg * 1e3, 2), "min_us": round(min(per[n]) * 1e3, 2),
+                   "tflops": round(fl[n] / (avg * 1e-3) / 1e12, 2) if fl[n] else None}
+    log(f"step {ms_per_step:.3f} ms  {tflops:.1f} TFLOP/s  kernels {kern}")
+
+    # dominant kernel roofline (MFMA bound; algorithmic FLOPs per launch)
+    dom = max(("fwd", "dkdv", "dq"), key=lambda n: kern[n]["avg_us"])
+    dom_avg_s = kern[dom]["avg_us"] * 1e-6
+    achieved = fl[dom] / dom_avg_s / 1e12
+    roofline = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "flops_per_launch": fl[dom]}
+
+    result = {
+        "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1)*0.5 q,k,v; N(0,1)*1e-2 dO; no trained weights)",
+        "config": {"workload": "d20 causal self-attention fwd+bwd", "B": B, "T": T, "H": H,
+                   "D": D, "causal": True, "parallelism": "single GPU"},
+        "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
+        "wall_s_timed": round(wall, 4),
+        "kernels": kern,
+        "roofline": roofline,
+    }
+
+    del q, k, v, do, o, dq, dk, dv
+    torch.cuda.empty_cache()
+
+    # ---------------- decode
+    if not args.no_decode:
+        dcfg = W.CONFIGS[W.DECODE]
+        log("generating decode inputs")
+        dinp = W.make_decode_inputs(dcfg)
+        Bd, Hd, Tc = dcfg.B, dcfg.H, dcfg.T_cap
+        qd = dev_t(dinp.q_store)
+        caches = []
+        kc0, vc0 = dev_t(dinp.k_store), dev_t(dinp.v_store)
+        for r in range(3):
+            caches.append((kc0.clone(), vc0.clone()) if r else (kc0, vc0))
+        lens = torch.from_numpy(dinp.seqlens).to(dev)
+        od = torch.empty_like(qd)
+        lsed = torch.empty((Bd, Hd), dtype=torch.float32, device=dev)
+        wsb = na.decode_workspace_bytes(Bd, Hd, Tc)
+        ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+        nd = args.decode_iters
+        devs = [ev.create(3) for _ in range(nd + 5)]
+        darr = [(ctypes.c_void_p * 3)(*[e.value for e in x]) for x in devs]
+
+        def dstep(i):
+            kc, vc = caches[i % 3]
+            st = lib.na_attn_decode_timed(ptr(qd), ptr(kc), ptr(vc), ptr(lens), ptr(od), ptr(lsed),
+                                          Bd, Hd, D, Tc, ptr(ws), wsb, P(stream),
+                                          ctypes.cast(darr[i], P))
+            if st:
+                raise RuntimeError(lib.na_last_error().decode())
+
+        for i in range(5):
+            dstep(i)
+        torch.cuda.synchronize()
+        for i in range(5, nd + 5):
+            dstep(i)
+        torch.cuda.synchronize()
+        split = [ev.ms(devs[i][0], devs[i][1]) for i in range(5, nd + 5)]
+        comb = [ev.ms(devs[i][1], devs[i][2]) for i in range(5, nd + 5)]
+        tot = [ev.ms(devs[i][0], devs[i][2]) for i in range(5, nd + 5)]
+        kv_bytes = int(dinp.seqlens.astype(np.int64).sum()) * Hd * D * 2 * 2
+        io_bytes = Bd * Hd * D * 2 * 2
+        d_ms = float(np.mean(tot))
+        gbs = (kv_bytes + io_bytes) / (d_ms * 1e-3) / 1e9
+        split_gbs = kv_bytes / (float(np.mean(split)) * 1e-3) / 1e9
+        result["decode"] = {
+            "workload": "d20 decode B=64 H=10 D=128, lengths U[1,2048], T_cap=2048, bf16",
+            "GB_per_s": round(gbs, 1), "pct_hbm_peak": round(100 * gbs / PEAK_HBM_GBS, 2),
+            "us_per_call": round(d_ms * 1e3, 2), "kv_bytes": kv_bytes,
+            "split_avg_us": round(float(np.mean(split)) * 1e3, 2),
+            "combine_avg_us": round(float(np.mean(comb)) * 1e3, 2),
+            "split_GB_per_s": round(split_gbs, 1), "iters": nd, "rotated_caches": 3,
+        }
+        log(f"decode {result['decode']}")
+        del caches, kc0, vc0
+        torch.cuda.empty_cache()
+
+    # ---------------- CPU baseline: the oracle on a bounded sample
+    if args.cpu_heads > 0:
+        log(f"cpu baseline on {args.cpu_heads} heads")
+        result["cpu_baseline"] = cpu_baseline(inp, args.cpu_heads)
+    else:
+        result["cpu_baseline"] = None
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

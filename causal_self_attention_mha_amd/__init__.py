@@ -1,0 +1,184 @@
+"""Fused causal multi-head self-attention for AMD MI355X (gfx950).
+
+A thin Python binding (ctypes) over the C-ABI library libna_attn.so built from
+csrc/ (see include/na_attn.h for the entry points).  This module only
+marshals arguments: it checks dtypes, shapes, devices and contiguity, allocates
+outputs with torch.empty on the tensors' device, and passes raw device pointers
+plus torch's current HIP stream.  Every step of the computation runs in the
+library's HIP kernels; there is no CPU or PyTorch fallback, and every entry
+point raises if the library is not built or no GPU is present.
+
+Functions (names match the C entry points):
+  attn_fwd(q, k, v)                       -> (o, lse)
+  attn_bwd(q, k, v, o, dout, lse)         -> (dq, dk, dv, delta)
+  attn_decode(q, k_cache, v_cache, seqlens) -> (o, lse)
+bf16 tensors use the bf16 kernels, float32 tensors the fp32 kernels
+(forward and backward only).  Layouts: q, k, v, o, dout (B, T, H, 128);
+lse, delta (B, H, T) float32; decode q/o (B, H, 128), caches (B, T_cap, H, 128),
+seqlens int32 [B] on the device.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = ["attn_fwd", "attn_bwd", "attn_decode", "decode_workspace_bytes", "load_library",
+           "library_path", "NAError", "HEAD_DIM"]
+
+HEAD_DIM = 128
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+_STATUS = {0: "NA_OK", 1: "NA_ERR_INVALID_ARG", 2: "NA_ERR_UNSUPPORTED", 3: "NA_ERR_HIP"}
+
+
+class NAError(RuntimeError):
+    """A library call returned a non-zero na_status."""
+
+    def __init__(self, fn, status, msg):
+        super().__init__(f"{fn} failed: {_STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, "lib", "libna_attn.so")
+
+
+def load_library():
+    """Load libna_attn.so (once).  torch is imported first so that the library
+    binds to the HIP runtime torch already uses (one runtime per process)."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    import torch  # noqa: F401  (HIP runtime first; see docstring)
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is not built; run `python -m causal_self_attention_mha_amd.build` "
+            "(hipcc, gfx950).  There is no fallback path.")
+    lib = ctypes.CDLL(path)
+    vp, i, f32p, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t
+    lib.na_attn_fwd.argtypes = [vp, vp, vp, vp, f32p, i, i, i, i, vp]
+    lib.na_attn_bwd.argtypes = [vp, vp, vp, vp, vp, f32p, vp, vp, vp, f32p, i, i, i, i, vp]
+    lib.na_attn_decode.argtypes = [vp, vp, vp, vp, vp, f32p, i, i, i, i, vp, sz, vp]
+    lib.na_attn_decode_workspace_bytes.argtypes = [i, i, i, i]
+    lib.na_attn_decode_workspace_bytes.restype = sz
+    lib.na_attn_fwd_f32.argtypes = [vp, vp, vp, vp, f32p, i, i, i, i, vp]
+    lib.na_attn_bwd_f32.argtypes = [vp, vp, vp, vp, vp, f32p, vp, vp, vp, f32p, i, i, i, i, vp]
+    lib.na_attn_bwd_timed.argtypes = lib.na_attn_bwd.argtypes + [vp]
+    lib.na_attn_decode_timed.argtypes = lib.na_attn_decode.argtypes + [vp]
+    for fn in ("na_attn_fwd", "na_attn_bwd", "na_attn_decode", "na_attn_fwd_f32",
+               "na_attn_bwd_f32", "na_attn_bwd_timed", "na_attn_decode_timed"):
+        getattr(lib, fn).restype = ctypes.c_int
+    lib.na_status_string.argtypes = [ctypes.c_int]
+    lib.na_status_string.restype = ctypes.c_char_p
+    lib.na_last_error.argtypes = []
+    lib.na_last_error.restype = ctypes.c_char_p
+    _LIB = lib
+    return lib
+
+
+def _check(lib, fn, status):
+    if status != 0:
+        raise NAError(fn, status, lib.na_last_error().decode())
+
+
+def _stream(t):
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _require(cond, msg):
+    if not cond:
+        raise ValueError(msg)
+
+
+def _check_train(names, tensors, dtype=None):
+    import torch
+    ref = tensors[0]
+    _require(ref.is_cuda, f"{names[0]} must be a GPU tensor (no CPU path)")
+    _require(ref.dim() == 4 and ref.shape[-1] == HEAD_DIM,
+             f"{names[0]} must be (B, T, H, {HEAD_DIM}), got {tuple(ref.shape)}")
+    dtype = dtype or ref.dtype
+    _require(dtype in (torch.bfloat16, torch.float32), f"unsupported dtype {dtype}")
+    for n, t in zip(names, tensors):
+        _require(t.dtype == dtype, f"{n} has dtype {t.dtype}, expected {dtype}")
+        _require(t.shape == ref.shape, f"{n} has shape {tuple(t.shape)}, expected {tuple(ref.shape)}")
+        _require(t.device == ref.device, f"{n} is on {t.device}, expected {ref.device}")
+        _require(t.is_contiguous(), f"{n} must be contiguous")
+    return dtype
+
+
+def attn_fwd(q, k, v, o=None, lse=None):
+    """Causal attention forward.  Returns (o, lse): o like q, lse float32 (B, H, T)."""
+    import torch
+    lib = load_library()
+    dtype = _check_train(("q", "k", "v"), (q, k, v))
+    B, T, H, D = q.shape
+    o = torch.empty_like(q) if o is None else o
+    lse = torch.empty((B, H, T), dtype=torch.float32, device=q.device) if lse is None else lse
+    _check_train(("q", "o"), (q, o), dtype)
+    _require(lse.shape == (B, H, T) and lse.dtype == torch.float32 and lse.is_contiguous(),
+             "lse must be contiguous float32 (B, H, T)")
+    fn = "na_attn_fwd" if dtype == torch.bfloat16 else "na_attn_fwd_f32"
+    _check(lib, fn, getattr(lib, fn)(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, T, H, D,
+                                     _stream(q)))
+    return o, lse
+
+
+def attn_bwd(q, k, v, o, dout, lse, dq=None, dk=None, dv=None, delta=None):
+    """Causal attention backward.  Returns (dq, dk, dv, delta)."""
+    import torch
+    lib = load_library()
+    dtype = _check_train(("q", "k", "v", "o", "dout"), (q, k, v, o, dout))
+    B, T, H, D = q.shape
+    _require(lse.shape == (B, H, T) and lse.dtype == torch.float32 and lse.is_contiguous(),
+             "lse must be contiguous float32 (B, H, T)")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    delta = torch.empty((B, H, T), dtype=torch.float32, device=q.device) if delta is None else delta
+    _check_train(("q", "dq", "dk", "dv"), (q, dq, dk, dv), dtype)
+    fn = "na_attn_bwd" if dtype == torch.bfloat16 else "na_attn_bwd_f32"
+    _check(lib, fn, getattr(lib, fn)(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse),
+                                     _ptr(dq), _ptr(dk), _ptr(dv), _ptr(delta), B, T, H, D,
+                                     _stream(q)))
+    return dq, dk, dv, delta
+
+
+def decode_workspace_bytes(B, H, T_cap, D=HEAD_DIM):
+    return int(load_library().na_attn_decode_workspace_bytes(B, H, D, T_cap))
+
+
+def attn_decode(q, k_cache, v_cache, seqlens, o=None, lse=None, workspace=None,
+                want_lse=True):
+    """Single-token decode over a padded cache.  Returns (o, lse)."""
+    import torch
+    lib = load_library()
+    _require(q.is_cuda and q.dtype == torch.bfloat16 and q.dim() == 3 and q.shape[-1] == HEAD_DIM,
+             "q must be a bf16 GPU tensor (B, H, 128)")
+    B, H, D = q.shape
+    _require(k_cache.dim() == 4 and k_cache.shape[0] == B and k_cache.shape[2] == H
+             and k_cache.shape[3] == D, "k_cache must be (B, T_cap, H, 128)")
+    T_cap = k_cache.shape[1]
+    for n, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
+        _require(t.dtype == torch.bfloat16 and t.device == q.device and t.is_contiguous(),
+                 f"{n} must be contiguous bf16 on {q.device}")
+    _require(v_cache.shape == k_cache.shape, "v_cache must match k_cache")
+    _require(seqlens.dtype == torch.int32 and seqlens.shape == (B,) and seqlens.device == q.device
+             and seqlens.is_contiguous(), "seqlens must be int32 [B] on the GPU")
+    o = torch.empty_like(q) if o is None else o
+    if want_lse and lse is None:
+        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    need = decode_workspace_bytes(B, H, T_cap, D)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    _check(lib, "na_attn_decode",
+           lib.na_attn_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seqlens), _ptr(o),
+                              _ptr(lse), B, H, D, T_cap, _ptr(workspace),
+                              workspace.numel() * workspace.element_size(), _stream(q)))
+    return o, lse

@@ -1,0 +1,181 @@
+// C-ABI layer of the attention library: host-side argument checks, then the
+// kernel launches.  Every check runs before any HIP call, so a rejected call
+// enqueues nothing and works without a GPU present.
+#include "../../include/na_attn.h"
+#include "internal.hpp"
+
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+#include <initializer_list>
+
+namespace {
+
+thread_local char g_msg[256] = "";
+
+na_status fail(na_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+na_status fail(na_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(g_msg, sizeof g_msg, fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+na_status ok() {
+  g_msg[0] = '\0';
+  return NA_OK;
+}
+
+na_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(NA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<std::uintptr_t>(p) & 15u) == 0; }
+
+struct Ptr {
+  const void* p;
+  const char* name;
+};
+
+na_status check_ptrs(std::initializer_list<Ptr> ins, std::initializer_list<Ptr> outs) {
+  for (auto l : {ins, outs})
+    for (const Ptr& x : l) {
+      if (x.p == nullptr) return fail(NA_ERR_INVALID_ARG, "%s is NULL", x.name);
+      if (!aligned16(x.p)) return fail(NA_ERR_INVALID_ARG, "%s is not 16-byte aligned", x.name);
+    }
+  for (const Ptr& o : outs) {
+    for (const Ptr& i : ins)
+      if (o.p == i.p) return fail(NA_ERR_INVALID_ARG, "output %s aliases input %s", o.name, i.name);
+    for (const Ptr& o2 : outs)
+      if (&o2 != &o && o2.p == o.p)
+        return fail(NA_ERR_INVALID_ARG, "outputs %s and %s alias", o.name, o2.name);
+  }
+  return NA_OK;
+}
+
+// Sizes of a (B, T, H, D) problem: all >= 1, D == 128, element count and the
+// largest grid within what 64-bit indexing and HIP's grid limits allow.
+na_status check_sizes(int B, int T, int H, int D) {
+  if (B < 1 || T < 1 || H < 1 || D < 1)
+    return fail(NA_ERR_INVALID_ARG, "sizes must be >= 1 (B=%d T=%d H=%d D=%d)", B, T, H, D);
+  if (D != na::kHeadDim)
+    return fail(NA_ERR_UNSUPPORTED, "head dim D=%d is not supported (only 128)", D);
+  const long double n = (long double)B * T * H * D;
+  if (n >= 9.2e18L) return fail(NA_ERR_INVALID_ARG, "B*T*H*D overflows 64-bit indexing");
+  // every grid is at most B*H*T workgroups in x
+  if ((long double)B * H * T > 2147483647.0L)
+    return fail(NA_ERR_INVALID_ARG, "B*H*T exceeds the launch grid limit");
+  return NA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* na_status_string(na_status s) {
+  switch (s) {
+    case NA_OK: return "NA_OK";
+    case NA_ERR_INVALID_ARG: return "NA_ERR_INVALID_ARG: an argument failed a host-side check";
+    case NA_ERR_UNSUPPORTED: return "NA_ERR_UNSUPPORTED: shape or option not supported";
+    case NA_ERR_HIP: return "NA_ERR_HIP: a HIP launch failed";
+    default: return "unknown na_status";
+  }
+}
+
+const char* na_last_error(void) { return g_msg; }
+
+na_status na_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                      int T, int H, int D, void* stream) {
+  na_status st = check_sizes(B, T, H, D);
+  if (st) return st;
+  st = check_ptrs({{q, "q"}, {k, "k"}, {v, "v"}}, {{o, "o"}, {lse, "lse"}});
+  if (st) return st;
+  return hip_status(na::launch_fwd_bf16(q, k, v, o, lse, B, T, H, (hipStream_t)stream),
+                    "na_attn_fwd");
+}
+
+na_status na_attn_bwd_timed(const void* q, const void* k, const void* v, const void* o,
+                            const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                            float* delta, int B, int T, int H, int D, void* stream,
+                            void* const* events) {
+  na_status st = check_sizes(B, T, H, D);
+  if (st) return st;
+  st = check_ptrs({{q, "q"}, {k, "k"}, {v, "v"}, {o, "o"}, {dout, "dout"}, {lse, "lse"}},
+                  {{dq, "dq"}, {dk, "dk"}, {dv, "dv"}, {delta, "delta"}});
+  if (st) return st;
+  return hip_status(na::launch_bwd_bf16(q, k, v, o, dout, lse, dq, dk, dv, delta, B, T, H,
+                                        (hipStream_t)stream,
+                                        reinterpret_cast<hipEvent_t const*>(events)),
+                    "na_attn_bwd");
+}
+
+na_status na_attn_bwd(const void* q, const void* k, const void* v, const void* o,
+                      const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                      float* delta, int B, int T, int H, int D, void* stream) {
+  return na_attn_bwd_timed(q, k, v, o, dout, lse, dq, dk, dv, delta, B, T, H, D, stream, nullptr);
+}
+
+size_t na_attn_decode_workspace_bytes(int B, int H, int D, int T_cap) {
+  if (B < 1 || H < 1 || T_cap < 1 || D != na::kHeadDim) return 0;
+  return na::decode_workspace_bytes(B, H, T_cap);
+}
+
+na_status na_attn_decode_timed(const void* q, const void* k_cache, const void* v_cache,
+                               const int* seqlens, void* o, float* lse, int B, int H, int D,
+                               int T_cap, void* workspace, size_t workspace_bytes, void* stream,
+                               void* const* events) {
+  na_status st = check_sizes(B, T_cap, H, D);
+  if (st) return st;
+  if (lse != nullptr) {
+    st = check_ptrs({{q, "q"}, {k_cache, "k_cache"}, {v_cache, "v_cache"}, {seqlens, "seqlens"}},
+                    {{o, "o"}, {lse, "lse"}, {workspace, "workspace"}});
+  } else {
+    st = check_ptrs({{q, "q"}, {k_cache, "k_cache"}, {v_cache, "v_cache"}, {seqlens, "seqlens"}},
+                    {{o, "o"}, {workspace, "workspace"}});
+  }
+  if (st) return st;
+  if (B > 65535 || H > 65535)
+    return fail(NA_ERR_INVALID_ARG, "decode supports B, H <= 65535 (B=%d H=%d)", B, H);
+  const size_t need = na::decode_workspace_bytes(B, H, T_cap);
+  if (workspace_bytes < need)
+    return fail(NA_ERR_INVALID_ARG, "workspace_bytes %zu < required %zu", workspace_bytes, need);
+  return hip_status(na::launch_decode_bf16(q, k_cache, v_cache, seqlens, o, lse, B, H, T_cap,
+                                           workspace, (hipStream_t)stream,
+                                           reinterpret_cast<hipEvent_t const*>(events)),
+                    "na_attn_decode");
+}
+
+na_status na_attn_decode(const void* q, const void* k_cache, const void* v_cache,
+                         const int* seqlens, void* o, float* lse, int B, int H, int D,
+                         int T_cap, void* workspace, size_t workspace_bytes, void* stream) {
+  return na_attn_decode_timed(q, k_cache, v_cache, seqlens, o, lse, B, H, D, T_cap, workspace,
+                              workspace_bytes, stream, nullptr);
+}
+
+na_status na_attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
+                          int B, int T, int H, int D, void* stream) {
+  na_status st = check_sizes(B, T, H, D);
+  if (st) return st;
+  st = check_ptrs({{q, "q"}, {k, "k"}, {v, "v"}}, {{o, "o"}, {lse, "lse"}});
+  if (st) return st;
+  return hip_status(na::launch_fwd_f32(q, k, v, o, lse, B, T, H, (hipStream_t)stream),
+                    "na_attn_fwd_f32");
+}
+
+na_status na_attn_bwd_f32(const float* q, const float* k, const float* v, const float* o,
+                          const float* dout, const float* lse, float* dq, float* dk, float* dv,
+                          float* delta, int B, int T, int H, int D, void* stream) {
+  na_status st = check_sizes(B, T, H, D);
+  if (st) return st;
+  st = check_ptrs({{q, "q"}, {k, "k"}, {v, "v"}, {o, "o"}, {dout, "dout"}, {lse, "lse"}},
+                  {{dq, "dq"}, {dk, "dk"}, {dv, "dv"}, {delta, "delta"}});
+  if (st) return st;
+  return hip_status(na::launch_bwd_f32(q, k, v, o, dout, lse, dq, dk, dv, delta, B, T, H,
+                                       (hipStream_t)stream),
+                    "na_attn_bwd_f32");
+}
+
+}  // extern "C"

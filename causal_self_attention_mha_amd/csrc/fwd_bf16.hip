@@ -1,0 +1,212 @@
+// bf16 causal attention forward on gfx950 MFMA.
+//
+// Computes, per (batch b, head h), o = softmax(s q k^T + causal mask) v and
+// lse = ln(row sums), the attention nanochat runs through
+// flash_attn_func(q, k, v, causal=True) (apidog blog "ChatGPTを50ドルで独自に
+// トレーニングする方法", section 5 "Flash Attention integration"), with
+// s = 1/sqrt(128) and key j visible to query i iff j <= i.
+//
+// Design (one workgroup = 4 wavefronts = 128 query rows of one (b, h)):
+//   * each wavefront owns 32 query rows; its Q^T operand (32 x 128 bf16) stays
+//     in registers for the whole key loop;
+//   * K and V tiles of 64 keys are staged through LDS: K row-major, V
+//     transposed (d-major) so that the PV MFMA reads 16 contiguous bytes per
+//     lane;
+//   * scores are computed transposed, S^T = K Q^T (v_mfma_f32_32x32x16_bf16),
+//     so that each lane owns one query row: the online-softmax max and sum are
+//     lane-local apart from one exchange with lane l^32;
+//   * the output is accumulated transposed too, O^T += V^T P^T, so the per-row
+//     rescale factor is also lane-local;
+//   * the softmax runs in the exp2 domain on raw scores: p = 2^(c z - c m)
+//     with c = s log2(e), one FMA and one v_exp_f32 per score;
+//   * key tiles entirely above the diagonal are never visited; only tiles that
+//     cross the diagonal apply the causal select;
+//   * workgroups are issued heaviest query tile first.
+#include "device_common.hpp"
+#include "internal.hpp"
+
+namespace na {
+namespace {
+
+constexpr int D = kHeadDim;
+constexpr int BQ = 128;  // query rows per workgroup
+constexpr int BK = 64;   // keys per LDS tile
+constexpr int KS = D + 8;    // K tile row stride in LDS (bf16 elements)
+constexpr int VS = BK + 8;   // V^T tile row stride in LDS (bf16 elements)
+
+__global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const u16* __restrict__ q,
+                                                          const u16* __restrict__ k,
+                                                          const u16* __restrict__ v,
+                                                          u16* __restrict__ o,
+                                                          float* __restrict__ lse, int B, int T,
+                                                          int H, float c_log2, float scale) {
+  __shared__ __attribute__((aligned(16))) u16 Ks[BK * KS];
+  __shared__ __attribute__((aligned(16))) u16 Vt[D * VS];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int half = lane >> 5;   // which 8-wide k half of an MFMA operand
+  const int l32 = lane & 31;
+
+  const int BH = B * H;
+  const int n_qt = (T + BQ - 1) / BQ;
+  const int qt = n_qt - 1 - static_cast<int>(blockIdx.x) / BH;  // heaviest first
+  const int bh = static_cast<int>(blockIdx.x) % BH;
+  const int b = bh / H, h = bh % H;
+  const int q0 = qt * BQ;
+  const int qw0 = q0 + wave * 32;
+  const size_t rs = static_cast<size_t>(H) * D;                       // stride between t
+  const size_t base = static_cast<size_t>(b) * T * rs + static_cast<size_t>(h) * D;
+
+  // Q^T operand: lane holds q[qw0 + l32][16 kc + 8 half + 0..7], kc = 0..7.
+  const int qrow = qw0 + l32;
+  bf16x8 qreg[8];
+  if (qrow < T) {
+    const u16* qp = q + base + static_cast<size_t>(qrow) * rs + 8 * half;
+#pragma unroll
+    for (int kc = 0; kc < 8; ++kc) qreg[kc] = as_bf16x8(ld16(qp + 16 * kc));
+  } else {
+#pragma unroll
+    for (int kc = 0; kc < 8; ++kc) qreg[kc] = as_bf16x8(make_uint4(0, 0, 0, 0));
+  }
+
+  f32x16 oacc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) oacc[i] = f32x16{};
+  float m = -INFINITY;  // running max of raw scores for row qrow
+  float lpart = 0.f;    // running sum over this lane's half of the keys
+
+  const int last_q = min(q0 + BQ, T) - 1;
+  const int n_kt = last_q / BK + 1;  // key tiles at or left of the diagonal
+
+  // cooperative tile loads: K rows (tid>>4) + 16 i, 16-byte chunk tid&15;
+  // V keys 4*(tid>>4) + i, d chunk tid&15, written transposed.
+  const int lrow = tid >> 4;
+  const int lchunk = tid & 15;
+
+  for (int kt = 0; kt < n_kt; ++kt) {
+    const int k0 = kt * BK;
+    uint4 kv[4], vv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int kr = k0 + lrow + 16 * i;
+      kv[i] = kr < T ? ld16(k + base + static_cast<size_t>(kr) * rs + 8 * lchunk)
+                     : make_uint4(0, 0, 0, 0);
+      const int vr = k0 + 4 * lrow + i;
+      vv[i] = vr < T ? ld16(v + base + static_cast<size_t>(vr) * rs + 8 * lchunk)
+                     : make_uint4(0, 0, 0, 0);
+    }
+    __syncthreads();  // previous tile fully consumed
+#pragma unroll
+    for (int i = 0; i < 4; ++i) st16(&Ks[(lrow + 16 * i) * KS + 8 * lchunk], kv[i]);
+    // transpose V: element e of the 8-wide chunk of key 4 lrow + i goes to
+    // Vt[8 lchunk + e][4 lrow + i]
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int w = e >> 1;
+      const int sh = (e & 1) * 16;
+      uint32_t x0 = ((&vv[0].x)[w] >> sh) & 0xffffu;
+      uint32_t x1 = ((&vv[1].x)[w] >> sh) & 0xffffu;
+      uint32_t x2 = ((&vv[2].x)[w] >> sh) & 0xffffu;
+      uint32_t x3 = ((&vv[3].x)[w] >> sh) & 0xffffu;
+      uint2 pk = make_uint2(x0 | (x1 << 16), x2 | (x3 << 16));
+      *reinterpret_cast<uint2*>(&Vt[(8 * lchunk + e) * VS + 4 * lrow]) = pk;
+    }
+    __syncthreads();
+
+    if (k0 > qw0 + 31) continue;  // whole tile above this wavefront's diagonal
+
+    // S^T = K Q^T for two 32-key blocks
+    f32x16 sacc[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      sacc[kb] = f32x16{};
+      const u16* kp = &Ks[(kb * 32 + perm_row(l32)) * KS + 8 * half];
+#pragma unroll
+      for (int kc = 0; kc < 8; ++kc)
+        sacc[kb] = mfma32(as_bf16x8(ld16(kp + 16 * kc)), qreg[kc], sacc[kb]);
+    }
+
+    // causal select on tiles that cross the diagonal
+    if (k0 + BK - 1 > qw0) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = k0 + kb * 32 + acc_row(lane, r);
+          if (key > qrow) sacc[kb][r] = -INFINITY;
+        }
+    }
+
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float m_new = fmaxf(m, mx);
+    const float alpha = fast_exp2((m - m_new) * c_log2);
+    const float neg = -m_new * c_log2;
+
+    // P^T as bf16 MFMA B operands: chunk c (16 keys) = sacc[c/2][8(c%2) .. +7]
+    bf16x8 pb[4];
+    float psum = 0.f;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float p = fast_exp2(fmaf(sacc[c >> 1][8 * (c & 1) + i], c_log2, neg));
+        psum += p;
+        pb[c][i] = to_bf16(p);
+      }
+    }
+    lpart = lpart * alpha + psum;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+
+    // O^T += V^T P^T
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const bf16x8 a = as_bf16x8(ld16(&Vt[(db * 32 + l32) * VS + 16 * c + 8 * half]));
+        oacc[db] = mfma32(a, pb[c], oacc[db]);
+      }
+    }
+    m = m_new;
+  }
+
+  const float l = lpart + __shfl_xor(lpart, 32, 64);
+  if (qrow < T) {
+    const float inv = 1.f / l;
+    u16* op = o + base + static_cast<size_t>(qrow) * rs;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        // elements 4g..4g+3 are d = 32 db + 8 g + 4 half + 0..3
+        uint2 pk = make_uint2(pack_bf16x2(oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv),
+                              pack_bf16x2(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv));
+        *reinterpret_cast<uint2*>(op + 32 * db + 8 * g + 4 * half) = pk;
+      }
+    if (half == 0) lse[static_cast<size_t>(bh) * T + qrow] = m * scale + logf(l);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
+                           int B, int T, int H, hipStream_t s) {
+  const float scale = 1.0f / sqrtf(static_cast<float>(D));
+  const float c_log2 = scale * 1.4426950408889634f;
+  const int n_qt = (T + BQ - 1) / BQ;
+  const dim3 grid(static_cast<unsigned>(n_qt) * B * H);
+  return launch(fwd_bf16_kernel, grid, dim3(256), 0, s, static_cast<const u16*>(q),
+                static_cast<const u16*>(k), static_cast<const u16*>(v), static_cast<u16*>(o),
+                lse, B, T, H, c_log2, scale);
+}
+
+}  // namespace na

@@ -1,0 +1,62 @@
+// Internal launcher declarations shared by the C-ABI layer (api.cpp) and the
+// kernel translation units.  Every launcher assumes its arguments were already
+// validated by api.cpp (sizes >= 1, D == 128, aligned, non-aliased) and returns
+// the HIP status of its launches.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstddef>
+#include <cstdint>
+#include <tuple>
+#include <utility>
+
+namespace na {
+
+constexpr int kHeadDim = 128;
+
+// bf16 forward: o, lse from q, k, v.
+hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
+                           int B, int T, int H, hipStream_t s);
+
+// bf16 backward: delta, then dk/dv, then dq.
+hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const void* o,
+                           const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                           float* delta, int B, int T, int H, hipStream_t s,
+                           hipEvent_t const* ev = nullptr);
+
+// Decode workspace layout and size (bytes).
+std::size_t decode_workspace_bytes(int B, int H, int T_cap);
+hipError_t launch_decode_bf16(const void* q, const void* kc, const void* vc, const int* seqlens,
+                              void* o, float* lse, int B, int H, int T_cap, void* ws,
+                              hipStream_t s, hipEvent_t const* ev = nullptr);
+
+// Records ev[i] on s when timing events were supplied.
+inline hipError_t mark(hipEvent_t const* ev, int i, hipStream_t s) {
+  return ev ? hipEventRecord(ev[i], s) : hipSuccess;
+}
+
+// fp32 forward and backward.
+hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
+                          int B, int T, int H, hipStream_t s);
+hipError_t launch_bwd_f32(const float* q, const float* k, const float* v, const float* o,
+                          const float* dout, const float* lse, float* dq, float* dk, float* dv,
+                          float* delta, int B, int T, int H, hipStream_t s);
+
+template <typename Tuple, std::size_t... I>
+inline void fill_argv(Tuple& t, void** argv, std::index_sequence<I...>) {
+  ((argv[I] = static_cast<void*>(&std::get<I>(t))), ...);
+}
+
+// Launch helper returning the launch status directly (hipGetLastError would
+// also report stale errors left by unrelated earlier calls).
+template <typename... Params, typename... Args>
+inline hipError_t launch(void (*kernel)(Params...), dim3 grid, dim3 block, std::size_t shmem,
+                         hipStream_t stream, Args... args) {
+  static_assert(sizeof...(Params) == sizeof...(Args), "kernel argument count");
+  std::tuple<Params...> packed(static_cast<Params>(args)...);
+  void* argv[sizeof...(Params)];
+  fill_argv(packed, argv, std::index_sequence_for<Params...>{});
+  return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, argv, shmem, stream);
+}
+
+}  // namespace na

@@ -1,0 +1,135 @@
+/*
+ * na_attn.h — C ABI of the fused causal multi-head self-attention library
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * What is computed.  nanochat runs every transformer block's attention as
+ * flash_attn_func(q, k, v, causal=True, window_size=...) on (B, T, H, D)
+ * tensors, FlashAttention-3 on Hopper in bfloat16 with PyTorch SDPA as the
+ * fallback elsewhere (apidog blog "ChatGPTを50ドルで独自にトレーニングする方法",
+ * section 5 "Flash Attention integration"; the architecture list and the
+ * (B, T, n_kv_head, head_dim) view are in section 1 "GPT model").  Chat
+ * inference attends one new token per sequence against a prefilled KV cache
+ * through flash_attn_with_kvcache (same blog, section 6 "inference engine").
+ * Shapes: head dim 128, d20 = 1280 channels = 10 heads (aisight.pl article
+ * "Karpathy udostępnia nanochat ...", section "Model i założenia skalowania").
+ *
+ * Readings fixed by this library (the pages do not write them out):
+ *   - scores z_ij = s <q_i, k_j> with s = 1/sqrt(D); softmax over keys;
+ *   - causal: key j is visible to query i iff j <= i (T_q = T_k, top left);
+ *   - n_kv_head = n_head, full causal window;
+ *   - lse_i = ln sum_j exp(z_ij) over visible keys (natural log, fp32);
+ *   - bf16 inputs are rounded values; all accumulation is fp32; fp32 -> bf16
+ *     conversions round to nearest even.
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers owned by the caller.  The library
+ *     never allocates device memory; scratch space (delta, the decode
+ *     workspace) is passed in.  Inputs are only read; outputs are fully
+ *     overwritten (no need to zero them).
+ *   - bf16 tensors are stored as 16-bit bfloat16.  Layout of q, k, v, o, dout,
+ *     dq, dk, dv: (B, T, H, D) contiguous, element ((b*T + t)*H + h)*D + d.
+ *     lse and delta: fp32 (B, H, T) contiguous, element (b*H + h)*T + t.
+ *   - D must be 128 (else NA_ERR_UNSUPPORTED).  B, T, H >= 1.  Every pointer
+ *     must be 16-byte aligned.  An output may not be the same pointer as an
+ *     input (NA_ERR_INVALID_ARG).
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Calls only
+ *     enqueue work and return without synchronising.  Arguments are checked on
+ *     the host before any HIP call; on a check failure nothing is enqueued and
+ *     the status says why (na_last_error() gives a message).  A launch failure
+ *     returns NA_ERR_HIP.  Device faults surface at the caller's next sync.
+ *   - Results are bitwise deterministic (no atomics).  Calls are re-entrant.
+ */
+#ifndef NA_ATTN_H
+#define NA_ATTN_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int na_status;
+#define NA_OK 0
+#define NA_ERR_INVALID_ARG 1
+#define NA_ERR_UNSUPPORTED 2
+#define NA_ERR_HIP 3
+
+/*
+ * Forward: o = softmax(s q k^T + causal mask) v and lse, per (b, h).
+ * q, k, v: bf16 (B, T, H, D) inputs.  o: bf16 (B, T, H, D) output.
+ * lse: fp32 (B, H, T) output (needed by na_attn_bwd).
+ */
+na_status na_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                      int B, int T, int H, int D, void* stream);
+
+/*
+ * Backward of the forward above for the loss L with dL/do = dout and no
+ * gradient through lse:
+ *   delta_i = sum_d dout_id o_id          (written to `delta`)
+ *   P = exp(s q k^T - lse) (masked), dP = dout v^T, dS = P * (dP - delta)
+ *   dv = P^T dout,  dq = s dS k,  dk = s dS^T q.
+ * q, k, v, o, dout: bf16 (B, T, H, D) inputs; o and lse are the forward's
+ * outputs.  dq, dk, dv: bf16 (B, T, H, D) outputs.  delta: fp32 (B, H, T)
+ * caller-provided scratch, holds delta on return.  Enqueues three kernels:
+ * delta, then dk/dv (one workgroup per key tile), then dq (one per query tile).
+ */
+na_status na_attn_bwd(const void* q, const void* k, const void* v, const void* o,
+                      const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                      float* delta, int B, int T, int H, int D, void* stream);
+
+/*
+ * Decode: one new query per sequence against a padded KV cache.
+ * q: bf16 (B, H, D).  k_cache, v_cache: bf16 (B, T_cap, H, D); only rows
+ * t < seqlens[b] are read.  seqlens: DEVICE int32[B]; values are clamped to
+ * [0, T_cap] on the device (not checked on the host); the query sits at
+ * position seqlens[b]-1 and sees keys 0..seqlens[b]-1.  o: bf16 (B, H, D)
+ * output; lse: fp32 (B, H) output, or NULL.  A sequence of length 0 gives
+ * o = 0 and lse = -inf.  workspace: device scratch of at least
+ * na_attn_decode_workspace_bytes(B, H, D, T_cap) bytes (NA_ERR_INVALID_ARG if
+ * smaller).  Enqueues two kernels: split-KV partials, then their combine.
+ */
+na_status na_attn_decode(const void* q, const void* k_cache, const void* v_cache,
+                         const int* seqlens, void* o, float* lse, int B, int H, int D,
+                         int T_cap, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of decode workspace needed for these sizes (0 if the sizes are invalid). */
+size_t na_attn_decode_workspace_bytes(int B, int H, int D, int T_cap);
+
+/*
+ * fp32 twins of the forward and backward (fp32 storage and arithmetic
+ * throughout, no bf16 rounding anywhere); same layouts, same conventions.
+ * For correctness at fp32 tolerances, not speed.
+ */
+na_status na_attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
+                          int B, int T, int H, int D, void* stream);
+na_status na_attn_bwd_f32(const float* q, const float* k, const float* v, const float* o,
+                          const float* dout, const float* lse, float* dq, float* dk, float* dv,
+                          float* delta, int B, int T, int H, int D, void* stream);
+
+/*
+ * Per-kernel timing twins of na_attn_bwd and na_attn_decode: identical work
+ * and results, plus hipEventRecord(events[i], stream) right before kernel i
+ * and of events[n] after the last kernel, so a caller can time each kernel
+ * with HIP events on the stream it runs on.  `events` points to caller-created
+ * hipEvent_t handles: 4 for the backward (delta, dk/dv, dq), 3 for the decode
+ * (split, combine).  NULL events behaves like the plain entry point.
+ */
+na_status na_attn_bwd_timed(const void* q, const void* k, const void* v, const void* o,
+                            const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                            float* delta, int B, int T, int H, int D, void* stream,
+                            void* const* events);
+na_status na_attn_decode_timed(const void* q, const void* k_cache, const void* v_cache,
+                               const int* seqlens, void* o, float* lse, int B, int H, int D,
+                               int T_cap, void* workspace, size_t workspace_bytes, void* stream,
+                               void* const* events);
+
+/* Static text for a status code. */
+const char* na_status_string(na_status s);
+
+/* Message for the last failing call on this thread ("" if none). */
+const char* na_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* NA_ATTN_H */

@@ -1,0 +1,135 @@
+"""CPU tests of the C-ABI boundary: the library loads, exports every entry
+point include/na_attn.h declares, and rejects bad arguments on the host before
+any HIP call (so these run without a GPU).  No compute call is made here."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import causal_self_attention_mha_amd as na
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "na_attn.h")
+
+OK, INVALID, UNSUPPORTED, HIP = 0, 1, 2, 3
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(na_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(na.library_path()):
+        pytest.skip("library not built")
+    return na.load_library()
+
+
+def test_header_declares_the_entry_points():
+    syms = declared_symbols()
+    for s in ("na_attn_fwd", "na_attn_bwd", "na_attn_decode", "na_attn_decode_workspace_bytes",
+              "na_attn_fwd_f32", "na_attn_bwd_f32", "na_status_string", "na_last_error"):
+        assert s in syms
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", na.library_path()], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT\s+(\w+)", out))
+    for s in declared_symbols():
+        assert s in exported, s
+        assert hasattr(lib, s)
+
+
+def test_status_strings(lib):
+    for code, word in ((OK, b"NA_OK"), (INVALID, b"INVALID"), (UNSUPPORTED, b"UNSUPPORTED"),
+                       (HIP, b"HIP")):
+        assert word in lib.na_status_string(code)
+    assert b"unknown" in lib.na_status_string(99)
+
+
+A = 0x10000  # a fake, 16-byte aligned "device" address; never dereferenced.
+# Every call below must fail a host-side check: a call that passed them would
+# launch kernels on these addresses.
+
+
+def fwd(lib, q=A, k=A + 0x100, v=A + 0x200, o=A + 0x300, lse=A + 0x400, B=1, T=8, H=1, D=128):
+    return lib.na_attn_fwd(q, k, v, o, lse, B, T, H, D, None)
+
+
+def test_fwd_rejects_bad_arguments(lib):
+    assert fwd(lib, q=0) == INVALID and b"q is NULL" in lib.na_last_error()
+    assert fwd(lib, lse=0) == INVALID
+    assert fwd(lib, B=0) == INVALID
+    assert fwd(lib, T=-1) == INVALID
+    assert fwd(lib, H=0) == INVALID
+    assert fwd(lib, D=64) == UNSUPPORTED and b"head dim" in lib.na_last_error()
+    assert fwd(lib, k=A + 0x108) == INVALID and b"aligned" in lib.na_last_error()
+    assert fwd(lib, o=A) == INVALID and b"aliases" in lib.na_last_error()
+    assert fwd(lib, B=1 << 20, T=1 << 20, H=1 << 10) == INVALID   # grid limit
+    assert lib.na_attn_fwd_f32(A, A + 16, A + 32, A + 48, A, 1, 8, 1, 128, None) == INVALID
+
+
+def test_bwd_rejects_bad_arguments(lib):
+    p = [A + 0x100 * i for i in range(10)]
+    bad = list(p)
+    bad[3] = 0                     # o
+    assert lib.na_attn_bwd(*bad[:5], bad[5], *bad[6:9], bad[9], 1, 8, 1, 128, None) == INVALID
+    bad = list(p)
+    bad[7] = bad[6]                # dk == dq
+    assert lib.na_attn_bwd(*bad[:5], bad[5], *bad[6:9], bad[9], 1, 8, 1, 128, None) == INVALID
+    assert b"alias" in lib.na_last_error()
+    assert lib.na_attn_bwd(*p[:5], p[5], *p[6:9], p[9], 1, 8, 1, 96, None) == UNSUPPORTED
+    bad = list(p)
+    bad[9] = 0                     # delta scratch
+    assert lib.na_attn_bwd_f32(*bad[:5], bad[5], *bad[6:9], bad[9], 1, 8, 1, 128, None) == INVALID
+
+
+def test_decode_workspace_and_checks(lib):
+    need = lib.na_attn_decode_workspace_bytes(64, 10, 128, 2048)
+    assert need > 0 and need % 4 == 0
+    assert lib.na_attn_decode_workspace_bytes(64, 10, 64, 2048) == 0
+    assert lib.na_attn_decode_workspace_bytes(0, 10, 128, 2048) == 0
+    # grows with the cache capacity, never shrinks
+    assert lib.na_attn_decode_workspace_bytes(64, 10, 128, 4096) >= need
+    p = [A + 0x100 * i for i in range(7)]
+    call = lambda ws_bytes, D=128, lse=p[5]: lib.na_attn_decode(  # noqa: E731
+        p[0], p[1], p[2], p[3], p[4], lse, 64, 10, D, 2048, p[6], ws_bytes, None)
+    assert call(need - 4) == INVALID and b"workspace" in lib.na_last_error()
+    assert call(need, D=256) == UNSUPPORTED
+    q_alias = lib.na_attn_decode(p[0], p[1], p[2], p[3], p[0], p[5], 64, 10, 128, 2048, p[6],
+                                 need, None)
+    assert q_alias == INVALID
+    no_seqlens = lib.na_attn_decode(p[0], p[1], p[2], 0, p[4], p[5], 64, 10, 128, 2048, p[6],
+                                    need, None)
+    assert no_seqlens == INVALID
+
+
+def test_binding_has_no_cpu_path():
+    torch = pytest.importorskip("torch")
+    if not os.path.exists(na.library_path()):
+        pytest.skip("library not built")
+    x = torch.zeros(1, 4, 1, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU"):
+        na.attn_fwd(x, x, x)
+
+
+def test_product_and_oracle_share_no_code():
+    """Neither side imports the other; the library sources name no oracle."""
+    pkg = os.path.join(ROOT, "causal_self_attention_mha_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cpp", ".hpp", ".h")):
+                src = open(os.path.join(dirpath, f), encoding="utf-8").read()
+                assert not re.search(r"^\s*(from|import)\s+oracle\b", src, re.M), f
+                assert "#include" not in src or "oracle" not in " ".join(
+                    re.findall(r"#include\s*[<\"]([^>\"]+)", src)), f
+    for f in os.listdir(os.path.join(ROOT, "oracle")):
+        if f.endswith(".py"):
+            src = open(os.path.join(ROOT, "oracle", f), encoding="utf-8").read()
+            assert "causal_self_attention_mha_amd" not in src
+            assert not re.search(r"^\s*(from|import)\s+workloads\b", src, re.M)
