@@ -104,7 +104,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--decode-iters", type=int, default=60)
-    ap.add_argument("--cpu-heads", type=int, default=48,
+    ap.add_argument("--cpu-heads", type=int, default=256,
                     help="(b,h) heads in the oracle CPU-baseline sample (0 = skip)")
     ap.add_argument("--no-decode", action="store_true")
     args = ap.parse_args()
@@ -180,7 +180,10 @@ def main():
         for j, n in enumerate(names):
             per[n].append(ev.ms(e[j], e[j + 1]))
         step_ms.append(ev.ms(e[0], e[4]))
-    ms_per_step = float(np.mean(step_ms))
+    # ms_per_step: synchronized wall clock over exactly K steps; the HIP-event
+    # GPU time per step is reported beside it
+    ms_per_step = wall * 1e3 / args.steps
+    gpu_ms_per_step = float(np.mean(step_ms))
     fl = train_flops(B, T, H, D)
     tflops = fl["fwd+bwd"] / (ms_per_step * 1e-3) / 1e12
     kern = {}
@@ -208,6 +211,7 @@ def main():
                    "D": D, "causal": True, "parallelism": "single GPU"},
         "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
         "wall_s_timed": round(wall, 4),
+        "gpu_ms_per_step_events": round(gpu_ms_per_step, 4),
         "kernels": kern,
         "roofline": roofline,
     }

@@ -63,25 +63,15 @@ __global__ __launch_bounds__(256) void delta_kernel(const u16* __restrict__ o,
 constexpr int KT_KEYS = 128;  // keys per workgroup (32 per wavefront)
 constexpr int QT_ROWS = 64;   // queries per LDS tile
 constexpr int RS = D + 8;         // row-major tile stride (bf16 elements)
-constexpr int TS = QT_ROWS + 8;   // transposed tile stride (bf16 elements)
 
 // Write rows 4*lrow + i (i = 0..3) of a 64 x 128 tile, held as four 16-byte
-// chunks (column chunk `chunk`), into a row-major copy and a transposed copy.
+// chunks (column chunk `chunk`), into a row-major copy and a transposed
+// (swizzled, see toff) copy.
 __device__ __forceinline__ void store_tile_both(u16* nat, u16* tr, const uint4 (&x)[4], int lrow,
                                                 int chunk) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) st16(&nat[(4 * lrow + i) * RS + 8 * chunk], x[i]);
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int w = e >> 1;
-    const int sh = (e & 1) * 16;
-    const uint32_t x0 = ((&x[0].x)[w] >> sh) & 0xffffu;
-    const uint32_t x1 = ((&x[1].x)[w] >> sh) & 0xffffu;
-    const uint32_t x2 = ((&x[2].x)[w] >> sh) & 0xffffu;
-    const uint32_t x3 = ((&x[3].x)[w] >> sh) & 0xffffu;
-    *reinterpret_cast<uint2*>(&tr[(8 * chunk + e) * TS + 4 * lrow]) =
-        make_uint2(x0 | (x1 << 16), x2 | (x3 << 16));
-  }
+  tstore_4x8(tr, x, lrow, chunk);
 }
 
 __global__ __launch_bounds__(256, 1) void dkdv_kernel(
@@ -91,8 +81,8 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(
     float scale) {
   __shared__ __attribute__((aligned(16))) u16 Qs[QT_ROWS * RS];
   __shared__ __attribute__((aligned(16))) u16 Gs[QT_ROWS * RS];   // dout
-  __shared__ __attribute__((aligned(16))) u16 Qt[D * TS];
-  __shared__ __attribute__((aligned(16))) u16 Gt[D * TS];
+  __shared__ __attribute__((aligned(16))) u16 Qt[D * QT_ROWS];   // transposed, swizzled
+  __shared__ __attribute__((aligned(16))) u16 Gt[D * QT_ROWS];
   __shared__ __attribute__((aligned(16))) float lse2s[QT_ROWS];
   __shared__ __attribute__((aligned(16))) float dls[QT_ROWS];
 
@@ -209,9 +199,9 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(
     for (int c = 0; c < 4; ++c) {
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
-        const int toff = (db * 32 + l32) * TS + 16 * c + 8 * half;
-        dva[db] = mfma32(pb[c], as_bf16x8(ld16(&Gt[toff])), dva[db]);
-        dka[db] = mfma32(sb[c], as_bf16x8(ld16(&Qt[toff])), dka[db]);
+        const int t = toff(db * 32 + l32, 2 * c + half);
+        dva[db] = mfma32(pb[c], as_bf16x8(ld16(&Gt[t])), dva[db]);
+        dka[db] = mfma32(sb[c], as_bf16x8(ld16(&Qt[t])), dka[db]);
       }
     }
   }
@@ -234,7 +224,6 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(
 
 constexpr int DQ_ROWS = 128;  // queries per workgroup (32 per wavefront)
 constexpr int DQ_KEYS = 64;   // keys per LDS tile
-constexpr int KTS = DQ_KEYS + 8;
 
 __global__ __launch_bounds__(256, 1) void dq_kernel(
     const u16* __restrict__ q, const u16* __restrict__ k, const u16* __restrict__ v,
@@ -242,7 +231,7 @@ __global__ __launch_bounds__(256, 1) void dq_kernel(
     u16* __restrict__ dq, int B, int T, int H, float c_log2, float scale) {
   __shared__ __attribute__((aligned(16))) u16 Ks[DQ_KEYS * RS];
   __shared__ __attribute__((aligned(16))) u16 Vs[DQ_KEYS * RS];
-  __shared__ __attribute__((aligned(16))) u16 Kt[D * KTS];
+  __shared__ __attribute__((aligned(16))) u16 Kt[D * DQ_KEYS];  // transposed, swizzled
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -310,17 +299,7 @@ __global__ __launch_bounds__(256, 1) void dq_kernel(
       st16(&Ks[(4 * lrow + i) * RS + 8 * lchunk], xk[i]);
       st16(&Vs[(4 * lrow + i) * RS + 8 * lchunk], xv[i]);
     }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int w = e >> 1;
-      const int sh = (e & 1) * 16;
-      const uint32_t x0 = ((&xk[0].x)[w] >> sh) & 0xffffu;
-      const uint32_t x1 = ((&xk[1].x)[w] >> sh) & 0xffffu;
-      const uint32_t x2 = ((&xk[2].x)[w] >> sh) & 0xffffu;
-      const uint32_t x3 = ((&xk[3].x)[w] >> sh) & 0xffffu;
-      *reinterpret_cast<uint2*>(&Kt[(8 * lchunk + e) * KTS + 4 * lrow]) =
-          make_uint2(x0 | (x1 << 16), x2 | (x3 << 16));
-    }
+    tstore_4x8(Kt, xk, lrow, lchunk);
     __syncthreads();
 
     if (k0 > qw0 + 31) continue;
@@ -356,7 +335,7 @@ __global__ __launch_bounds__(256, 1) void dq_kernel(
     for (int c = 0; c < 4; ++c)
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
-        const bf16x8 a = as_bf16x8(ld16(&Kt[(db * 32 + l32) * KTS + 16 * c + 8 * half]));
+        const bf16x8 a = as_bf16x8(ld16(&Kt[toff(db * 32 + l32, 2 * c + half)]));
         dqa[db] = mfma32(a, sb[c], dqa[db]);
       }
   }

@@ -73,4 +73,36 @@ __device__ __forceinline__ int acc_row(int lane, int r) {
   return 8 * (lane >> 5) + (r & 7) + 16 * (r >> 3);
 }
 
+// ---------------------------------------------------------------------------
+// Transposed LDS tile: 128 rows (head-dim index d) x 64 columns (keys or
+// queries) of bf16, row stride 128 bytes, no padding.  The 16-byte column
+// group cg (columns 8 cg .. 8 cg + 7) of row d is stored at physical group
+// cg ^ tsw(d).  With gfx950's 64 four-byte LDS banks this makes both access
+// patterns below conflict-free: the 16-lane groups of a ds_read_b128 that
+// reads one column group of 16 consecutive rows, and the 32-lane groups of
+// the ds_write_b64 stores of tstore_4x8.
+__device__ __forceinline__ int tsw(int d) { return ((d >> 1) ^ (d >> 4)) & 7; }
+
+// Element offset of column group cg of row d.
+__device__ __forceinline__ int toff(int d, int cg) { return d * 64 + ((cg ^ tsw(d)) << 3); }
+
+// Store a 4-column x 8-row block into a transposed tile.  x[i] holds 16 bytes
+// (rows 8 lchunk .. 8 lchunk + 7) of column 4 lrow + i.  Odd-lchunk threads
+// walk the 8 rows in pair-swapped order so that each 32-lane store group
+// covers both row parities (and so all 64 banks).
+__device__ __forceinline__ void tstore_4x8(u16* tile, const uint4 (&x)[4], int lrow, int lchunk) {
+  const int p = lchunk & 1;
+  const uint32_t sel = p ? 0x07060302u : 0x05040100u;  // high or low halves of two dwords
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int w = e >> 1;
+    const int el = e ^ p;  // row within the 8-row chunk; el >> 1 == w
+    const uint32_t lo_sel = (e & 1) ? (sel ^ 0x02020202u) : sel;
+    const uint32_t a = __builtin_amdgcn_perm((&x[1].x)[w], (&x[0].x)[w], lo_sel);
+    const uint32_t b = __builtin_amdgcn_perm((&x[3].x)[w], (&x[2].x)[w], lo_sel);
+    const int d = 8 * lchunk + el;
+    *reinterpret_cast<uint2*>(&tile[toff(d, lrow >> 1) + 4 * (lrow & 1)]) = make_uint2(a, b);
+  }
+}
+
 }  // namespace na

@@ -9,9 +9,11 @@
 // Design (one workgroup = 4 wavefronts = 128 query rows of one (b, h)):
 //   * each wavefront owns 32 query rows; its Q^T operand (32 x 128 bf16) stays
 //     in registers for the whole key loop;
-//   * K and V tiles of 64 keys are staged through LDS: K row-major, V
-//     transposed (d-major) so that the PV MFMA reads 16 contiguous bytes per
-//     lane;
+//   * K and V tiles of 64 keys are staged through double-buffered LDS, the
+//     next tile's global loads in flight while the current one is computed:
+//     K row-major (padded rows), V transposed (d-major, XOR-swizzled 16-byte
+//     groups) so that the PV MFMA reads 16 contiguous bytes per lane and
+//     neither the stores nor the reads conflict in LDS banks;
 //   * scores are computed transposed, S^T = K Q^T (v_mfma_f32_32x32x16_bf16),
 //     so that each lane owns one query row: the online-softmax max and sum are
 //     lane-local apart from one exchange with lane l^32;
@@ -32,7 +34,10 @@ constexpr int D = kHeadDim;
 constexpr int BQ = 128;  // query rows per workgroup
 constexpr int BK = 64;   // keys per LDS tile
 constexpr int KS = D + 8;    // K tile row stride in LDS (bf16 elements)
-constexpr int VS = BK + 8;   // V^T tile row stride in LDS (bf16 elements)
+// Lazy rescaling: the running max m is only raised (and O, l rescaled) when a
+// new score exceeds it by more than 2^8 in the exp2 domain, so most tiles skip
+// the rescale; probabilities then stay below 256, harmless in fp32 and bf16.
+constexpr float kRescaleLog2 = 8.0f;
 
 __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const u16* __restrict__ q,
                                                           const u16* __restrict__ k,
@@ -40,8 +45,9 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const u16* __restrict_
                                                           u16* __restrict__ o,
                                                           float* __restrict__ lse, int B, int T,
                                                           int H, float c_log2, float scale) {
-  __shared__ __attribute__((aligned(16))) u16 Ks[BK * KS];
-  __shared__ __attribute__((aligned(16))) u16 Vt[D * VS];
+  // double-buffered K (row-major) and V^T tiles
+  __shared__ __attribute__((aligned(16))) u16 Ks[2][BK * KS];
+  __shared__ __attribute__((aligned(16))) u16 Vt[2][D * BK];  // swizzled, see toff()
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -60,15 +66,13 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const u16* __restrict_
   const size_t base = static_cast<size_t>(b) * T * rs + static_cast<size_t>(h) * D;
 
   // Q^T operand: lane holds q[qw0 + l32][16 kc + 8 half + 0..7], kc = 0..7.
+  // Rows past T (their outputs are discarded) read row T-1 instead.
   const int qrow = qw0 + l32;
   bf16x8 qreg[8];
-  if (qrow < T) {
-    const u16* qp = q + base + static_cast<size_t>(qrow) * rs + 8 * half;
+  {
+    const u16* qp = q + base + static_cast<size_t>(min(qrow, T - 1)) * rs + 8 * half;
 #pragma unroll
     for (int kc = 0; kc < 8; ++kc) qreg[kc] = as_bf16x8(ld16(qp + 16 * kc));
-  } else {
-#pragma unroll
-    for (int kc = 0; kc < 8; ++kc) qreg[kc] = as_bf16x8(make_uint4(0, 0, 0, 0));
   }
 
   f32x16 oacc[4];
@@ -76,44 +80,44 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const u16* __restrict_
   for (int i = 0; i < 4; ++i) oacc[i] = f32x16{};
   float m = -INFINITY;  // running max of raw scores for row qrow
   float lpart = 0.f;    // running sum over this lane's half of the keys
+  const float thr = kRescaleLog2 / c_log2;
 
   const int last_q = min(q0 + BQ, T) - 1;
   const int n_kt = last_q / BK + 1;  // key tiles at or left of the diagonal
 
   // cooperative tile loads: K rows (tid>>4) + 16 i, 16-byte chunk tid&15;
-  // V keys 4*(tid>>4) + i, d chunk tid&15, written transposed.
+  // V keys 4*(tid>>4) + i, d chunk tid&15, written transposed.  Key rows past
+  // T read row T-1: such keys are always masked (their P is 0), so any finite
+  // value works.
   const int lrow = tid >> 4;
   const int lchunk = tid & 15;
-
-  for (int kt = 0; kt < n_kt; ++kt) {
+  const u16* kg = k + base + 8 * lchunk;
+  const u16* vg = v + base + 8 * lchunk;
+  uint4 kv[4], vv[4];
+  auto gload = [&](int kt) {
     const int k0 = kt * BK;
-    uint4 kv[4], vv[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int kr = k0 + lrow + 16 * i;
-      kv[i] = kr < T ? ld16(k + base + static_cast<size_t>(kr) * rs + 8 * lchunk)
-                     : make_uint4(0, 0, 0, 0);
-      const int vr = k0 + 4 * lrow + i;
-      vv[i] = vr < T ? ld16(v + base + static_cast<size_t>(vr) * rs + 8 * lchunk)
-                     : make_uint4(0, 0, 0, 0);
+      kv[i] = ld16(kg + static_cast<size_t>(min(k0 + lrow + 16 * i, T - 1)) * rs);
+      vv[i] = ld16(vg + static_cast<size_t>(min(k0 + 4 * lrow + i, T - 1)) * rs);
     }
-    __syncthreads();  // previous tile fully consumed
+  };
+  auto lstore = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) st16(&Ks[(lrow + 16 * i) * KS + 8 * lchunk], kv[i]);
-    // transpose V: element e of the 8-wide chunk of key 4 lrow + i goes to
-    // Vt[8 lchunk + e][4 lrow + i]
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int w = e >> 1;
-      const int sh = (e & 1) * 16;
-      uint32_t x0 = ((&vv[0].x)[w] >> sh) & 0xffffu;
-      uint32_t x1 = ((&vv[1].x)[w] >> sh) & 0xffffu;
-      uint32_t x2 = ((&vv[2].x)[w] >> sh) & 0xffffu;
-      uint32_t x3 = ((&vv[3].x)[w] >> sh) & 0xffffu;
-      uint2 pk = make_uint2(x0 | (x1 << 16), x2 | (x3 << 16));
-      *reinterpret_cast<uint2*>(&Vt[(8 * lchunk + e) * VS + 4 * lrow]) = pk;
-    }
+    for (int i = 0; i < 4; ++i) st16(&Ks[buf][(lrow + 16 * i) * KS + 8 * lchunk], kv[i]);
+    tstore_4x8(Vt[buf], vv, lrow, lchunk);  // V^T: row d, column key
+  };
+
+  gload(0);
+  for (int kt = 0; kt < n_kt; ++kt) {
+    const int buf = kt & 1;
+    const int k0 = kt * BK;
+    lstore(buf);
+    // One barrier per tile: it publishes buffer `buf` and, because every
+    // wavefront passed it only after finishing tile kt-1, it also frees
+    // buffer buf^1 for the next store.
     __syncthreads();
+    if (kt + 1 < n_kt) gload(kt + 1);  // next tile in flight during this one
 
     if (k0 > qw0 + 31) continue;  // whole tile above this wavefront's diagonal
 
@@ -121,11 +125,13 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const u16* __restrict_
     f32x16 sacc[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      sacc[kb] = f32x16{};
-      const u16* kp = &Ks[(kb * 32 + perm_row(l32)) * KS + 8 * half];
+      const u16* kp = &Ks[buf][(kb * 32 + perm_row(l32)) * KS + 8 * half];
+      bf16x8 a[8];
 #pragma unroll
-      for (int kc = 0; kc < 8; ++kc)
-        sacc[kb] = mfma32(as_bf16x8(ld16(kp + 16 * kc)), qreg[kc], sacc[kb]);
+      for (int kc = 0; kc < 8; ++kc) a[kc] = as_bf16x8(ld16(kp + 16 * kc));
+      sacc[kb] = f32x16{};
+#pragma unroll
+      for (int kc = 0; kc < 8; ++kc) sacc[kb] = mfma32(a[kc], qreg[kc], sacc[kb]);
     }
 
     // causal select on tiles that cross the diagonal
@@ -145,9 +151,17 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const u16* __restrict_
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m, mx);
-    const float alpha = fast_exp2((m - m_new) * c_log2);
-    const float neg = -m_new * c_log2;
+    if (__any(mx > m + thr)) {  // wavefront-uniform
+      const float m_new = fmaxf(m, mx);
+      const float alpha = fast_exp2((m - m_new) * c_log2);  // 0 on the first tile
+      lpart *= alpha;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+      m = m_new;
+    }
+    const float neg = -m * c_log2;
 
     // P^T as bf16 MFMA B operands: chunk c (16 keys) = sacc[c/2][8(c%2) .. +7]
     bf16x8 pb[4];
@@ -161,22 +175,18 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const u16* __restrict_
         pb[c][i] = to_bf16(p);
       }
     }
-    lpart = lpart * alpha + psum;
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+    lpart += psum;
 
     // O^T += V^T P^T
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
+      bf16x8 a[4];
 #pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        const bf16x8 a = as_bf16x8(ld16(&Vt[(db * 32 + l32) * VS + 16 * c + 8 * half]));
-        oacc[db] = mfma32(a, pb[c], oacc[db]);
-      }
+      for (int db = 0; db < 4; ++db)
+        a[db] = as_bf16x8(ld16(&Vt[buf][toff(db * 32 + l32, 2 * c + half)]));
+#pragma unroll
+      for (int db = 0; db < 4; ++db) oacc[db] = mfma32(a[db], pb[c], oacc[db]);
     }
-    m = m_new;
   }
 
   const float l = lpart + __shfl_xor(lpart, 32, 64);
