@@ -62,16 +62,119 @@ __global__ __launch_bounds__(256) void delta_kernel(const u16* __restrict__ o,
 
 constexpr int KT_KEYS = 128;  // keys per workgroup (32 per wavefront)
 constexpr int QT_ROWS = 64;   // queries per LDS tile
-constexpr int RS = D + 8;         // row-major tile stride (bf16 elements)
+constexpr int RS = D + 8;     // row-major tile stride (bf16 elements)
 
-// Write rows 4*lrow + i (i = 0..3) of a 64 x 128 tile, held as four 16-byte
-// chunks (column chunk `chunk`), into a row-major copy and a transposed
-// (swizzled, see toff) copy.
-__device__ __forceinline__ void store_tile_both(u16* nat, u16* tr, const uint4 (&x)[4], int lrow,
-                                                int chunk) {
+// One 32-query block of a dK/dV step for one wavefront (32 keys), in three
+// phases:
+//   scores:  S = Q K^T, dP = dout V^T   (A = Q / dout rows from LDS, B = K / V
+//            in registers; lane: key, element r: query acc_row(lane, r))
+//   probs:   P = exp2(c S - lse2), dS = P (dP - delta), rounded to bf16
+//   accum:   dV += P^T dout, dK += dS^T Q  (A = P^T / dS^T from registers,
+//            B = transposed query tiles)
+// The steady-state loop overlaps the scores MFMAs of block j+1 with the probs
+// VALU work of block j.
+__device__ __forceinline__ void dkdv_scores(const u16* Qs, const u16* Gs, int row0,
+                                            const bf16x8 (&kreg)[8], const bf16x8 (&vreg)[8],
+                                            f32x16& sacc, f32x16& pacc, int lane) {
+  const int half = lane >> 5;
+  const int l32 = lane & 31;
+  sacc = f32x16{};
+  pacc = f32x16{};
+  const u16* qp = &Qs[(row0 + perm_row(l32)) * RS + 8 * half];
+  const u16* gp = &Gs[(row0 + perm_row(l32)) * RS + 8 * half];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) st16(&nat[(4 * lrow + i) * RS + 8 * chunk], x[i]);
-  tstore_4x8(tr, x, lrow, chunk);
+  for (int k4 = 0; k4 < 8; k4 += 4) {
+    bf16x8 aq[4], ag[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      aq[i] = as_bf16x8(ld16(qp + 16 * (k4 + i)));
+      ag[i] = as_bf16x8(ld16(gp + 16 * (k4 + i)));
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      sacc = mfma32(aq[i], kreg[k4 + i], sacc);
+      pacc = mfma32(ag[i], vreg[k4 + i], pacc);
+    }
+  }
+}
+
+template <bool MASK>
+__device__ __forceinline__ void dkdv_probs(const f32x16& sacc, const f32x16& pacc,
+                                           const float* lse2s, const float* dls, int row0,
+                                           bf16x8 (&pb)[2], bf16x8 (&sb)[2], int lane,
+                                           int key_minus_q0, float c_log2) {
+  const int r0 = row0 + 8 * (lane >> 5);  // element r: query row r0 + 16 (r/8) + r%8
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const float4 la = *reinterpret_cast<const float4*>(&lse2s[r0 + 16 * j]);
+    const float4 lb = *reinterpret_cast<const float4*>(&lse2s[r0 + 16 * j + 4]);
+    const float4 da = *reinterpret_cast<const float4*>(&dls[r0 + 16 * j]);
+    const float4 db = *reinterpret_cast<const float4*>(&dls[r0 + 16 * j + 4]);
+    const float l8[8] = {la.x, la.y, la.z, la.w, lb.x, lb.y, lb.z, lb.w};
+    const float d8[8] = {da.x, da.y, da.z, da.w, db.x, db.y, db.z, db.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = 8 * j + i;
+      float p = fast_exp2(fmaf(sacc[r], c_log2, -l8[i]));
+      if (MASK && key_minus_q0 > r0 + 16 * j + i) p = 0.f;  // key after query
+      pb[j][i] = to_bf16(p);
+      sb[j][i] = to_bf16(p * (pacc[r] - d8[i]));
+    }
+  }
+}
+
+__device__ __forceinline__ void dkdv_accum(const bf16x8 (&pb)[2], const bf16x8 (&sb)[2],
+                                           const u16* Qt, const u16* Gt, int row0,
+                                           f32x16 (&dka)[4], f32x16 (&dva)[4], int lane) {
+  const int half = lane >> 5;
+  const int l32 = lane & 31;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int cg = row0 / 8 + 2 * j + half;  // queries row0 + 16 j + 8 half + 0..7
+    bf16x8 bg[4], bq[4];
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      const int t = toff(db * 32 + l32, cg);
+      bg[db] = as_bf16x8(ld16(&Gt[t]));
+      bq[db] = as_bf16x8(ld16(&Qt[t]));
+    }
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      dva[db] = mfma32(pb[j], bg[db], dva[db]);
+      dka[db] = mfma32(sb[j], bq[db], dka[db]);
+    }
+  }
+}
+
+template <bool MASK>
+__device__ __forceinline__ void dkdv_block(const u16* Qs, const u16* Gs, const u16* Qt,
+                                           const u16* Gt, const float* lse2s, const float* dls,
+                                           const bf16x8 (&kreg)[8], const bf16x8 (&vreg)[8],
+                                           f32x16 (&dka)[4], f32x16 (&dva)[4], int qb, int lane,
+                                           int key_minus_q0, float c_log2) {
+  f32x16 sacc, pacc;
+  dkdv_scores(Qs, Gs, 32 * qb, kreg, vreg, sacc, pacc, lane);
+  bf16x8 pb[2], sb[2];
+  dkdv_probs<MASK>(sacc, pacc, lse2s, dls, 32 * qb, pb, sb, lane, key_minus_q0, c_log2);
+  dkdv_accum(pb, sb, Qt, Gt, 32 * qb, dka, dva, lane);
+}
+
+// Steady-state step: probabilities of the current block (held in s_cur,
+// p_cur), scores of the next block (if HAS_NEXT) into s_nxt, p_nxt, then the
+// current block's dK/dV accumulation.  One basic block, so the scheduler can
+// interleave the next block's MFMAs with this block's VALU work.
+template <bool HAS_NEXT>
+__device__ __forceinline__ void dkdv_step(const u16* QsN, const u16* GsN, int rowN,
+                                          const float* lse2s, const float* dls, const u16* Qt,
+                                          const u16* Gt, int rowC, const bf16x8 (&kreg)[8],
+                                          const bf16x8 (&vreg)[8], const f32x16& s_cur,
+                                          const f32x16& p_cur, f32x16& s_nxt, f32x16& p_nxt,
+                                          f32x16 (&dka)[4], f32x16 (&dva)[4], int lane,
+                                          float c_log2) {
+  bf16x8 pb[2], sb[2];
+  dkdv_probs<false>(s_cur, p_cur, lse2s, dls, rowC, pb, sb, lane, 0, c_log2);
+  if (HAS_NEXT) dkdv_scores(QsN, GsN, rowN, kreg, vreg, s_nxt, p_nxt, lane);
+  dkdv_accum(pb, sb, Qt, Gt, rowC, dka, dva, lane);
 }
 
 __global__ __launch_bounds__(256, 1) void dkdv_kernel(
@@ -79,12 +182,13 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(
     const u16* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
     u16* __restrict__ dk, u16* __restrict__ dv, int B, int T, int H, float c_log2,
     float scale) {
-  __shared__ __attribute__((aligned(16))) u16 Qs[QT_ROWS * RS];
-  __shared__ __attribute__((aligned(16))) u16 Gs[QT_ROWS * RS];   // dout
-  __shared__ __attribute__((aligned(16))) u16 Qt[D * QT_ROWS];   // transposed, swizzled
-  __shared__ __attribute__((aligned(16))) u16 Gt[D * QT_ROWS];
-  __shared__ __attribute__((aligned(16))) float lse2s[QT_ROWS];
-  __shared__ __attribute__((aligned(16))) float dls[QT_ROWS];
+  // double-buffered query tiles: Q and dout row-major, and transposed (swizzled)
+  __shared__ __attribute__((aligned(16))) u16 Qs[2][QT_ROWS * RS];
+  __shared__ __attribute__((aligned(16))) u16 Gs[2][QT_ROWS * RS];
+  __shared__ __attribute__((aligned(16))) u16 Qt[2][D * QT_ROWS];
+  __shared__ __attribute__((aligned(16))) u16 Gt[2][D * QT_ROWS];
+  __shared__ __attribute__((aligned(16))) float lse2s[2][QT_ROWS];
+  __shared__ __attribute__((aligned(16))) float dls[2][QT_ROWS];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -103,23 +207,16 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(
   const float* lse_bh = lse + static_cast<size_t>(bh) * T;
   const float* del_bh = delta + static_cast<size_t>(bh) * T;
 
-  // K^T and V^T operands of S = Q K^T and dP = dout V^T: lane holds row
-  // kw0 + l32, elements 16 kc + 8 half + 0..7.
+  // K^T and V^T operands: lane holds row kw0 + l32 (rows past T read row
+  // T-1; their gradients are never stored), elements 16 kc + 8 half + 0..7.
   const int krow = kw0 + l32;
   bf16x8 kreg[8], vreg[8];
-  if (krow < T) {
-    const u16* kp = k + base + static_cast<size_t>(krow) * rs + 8 * half;
-    const u16* vp = v + base + static_cast<size_t>(krow) * rs + 8 * half;
+  {
+    const size_t off = base + static_cast<size_t>(min(krow, T - 1)) * rs + 8 * half;
 #pragma unroll
     for (int kc = 0; kc < 8; ++kc) {
-      kreg[kc] = as_bf16x8(ld16(kp + 16 * kc));
-      vreg[kc] = as_bf16x8(ld16(vp + 16 * kc));
-    }
-  } else {
-#pragma unroll
-    for (int kc = 0; kc < 8; ++kc) {
-      kreg[kc] = as_bf16x8(make_uint4(0, 0, 0, 0));
-      vreg[kc] = kreg[kc];
+      kreg[kc] = as_bf16x8(ld16(k + off + 16 * kc));
+      vreg[kc] = as_bf16x8(ld16(v + off + 16 * kc));
     }
   }
 
@@ -131,78 +228,101 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(
   }
 
   const int n_qt = (T + QT_ROWS - 1) / QT_ROWS;
+  const int qt0 = k0 / QT_ROWS;
   const int lrow = tid >> 4;
   const int lchunk = tid & 15;
-
-  for (int qt = k0 / QT_ROWS; qt < n_qt; ++qt) {
+  // query rows past T: q and dout read row T-1 and lse2 = +inf, so P = 0
+  uint4 xq[4], xg[4];
+  float l2 = 0.f, dl = 0.f;
+  auto gload = [&](int qt) {
     const int q0 = qt * QT_ROWS;
-    uint4 xq[4], xg[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int r = q0 + 4 * lrow + i;
-      if (r < T) {
-        xq[i] = ld16(q + base + static_cast<size_t>(r) * rs + 8 * lchunk);
-        xg[i] = ld16(dout + base + static_cast<size_t>(r) * rs + 8 * lchunk);
-      } else {
-        xq[i] = make_uint4(0, 0, 0, 0);
-        xg[i] = xq[i];
-      }
+      const size_t off =
+          base + static_cast<size_t>(min(q0 + 4 * lrow + i, T - 1)) * rs + 8 * lchunk;
+      xq[i] = ld16(q + off);
+      xg[i] = ld16(dout + off);
     }
-    float l2 = 0.f, dl = 0.f;
     if (tid < QT_ROWS) {
       const int r = q0 + tid;
-      l2 = r < T ? lse_bh[r] * kLog2e : INFINITY;  // padded rows get P = 0
+      l2 = r < T ? lse_bh[r] * kLog2e : INFINITY;
       dl = r < T ? del_bh[r] : 0.f;
     }
-    __syncthreads();
-    store_tile_both(Qs, Qt, xq, lrow, lchunk);
-    store_tile_both(Gs, Gt, xg, lrow, lchunk);
-    if (tid < QT_ROWS) {
-      lse2s[tid] = l2;
-      dls[tid] = dl;
+  };
+
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      st16(&Qs[buf][(4 * lrow + i) * RS + 8 * lchunk], xq[i]);
+      st16(&Gs[buf][(4 * lrow + i) * RS + 8 * lchunk], xg[i]);
     }
-    __syncthreads();
+    tstore_4x8(Qt[buf], xq, lrow, lchunk);
+    tstore_4x8(Gt[buf], xg, lrow, lchunk);
+    if (tid < QT_ROWS) {
+      lse2s[buf][tid] = l2;
+      dls[buf][tid] = dl;
+    }
+  };
+
+  // Diagonal part: the first two query tiles hold every (query, key) pair of
+  // this workgroup that the causal mask can cut; one barrier per tile.
+  const int qt_diag_end = min(qt0 + 2, n_qt);
+  gload(qt0);
+  for (int qt = qt0; qt < qt_diag_end; ++qt) {
+    const int buf = (qt - qt0) & 1;
+    const int q0 = qt * QT_ROWS;
+    lstore(buf);
+    __syncthreads();  // publishes `buf`; frees buf^1 (see the forward kernel)
+    if (qt + 1 < n_qt) gload(qt + 1);
 
     if (q0 + QT_ROWS - 1 < kw0) continue;  // every query precedes this wavefront's keys
-
-    f32x16 sacc[2], pacc[2];
+    const int kq = krow - q0;
+    if (q0 < kw0 + 31) {  // tile crosses this wavefront's diagonal
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      sacc[qb] = f32x16{};
-      pacc[qb] = f32x16{};
-      const u16* qp = &Qs[(qb * 32 + perm_row(l32)) * RS + 8 * half];
-      const u16* gp = &Gs[(qb * 32 + perm_row(l32)) * RS + 8 * half];
+      for (int qb = 0; qb < 2; ++qb) {
+        if (q0 + 32 * qb + 31 >= kw0)
+          dkdv_block<true>(Qs[buf], Gs[buf], Qt[buf], Gt[buf], lse2s[buf], dls[buf], kreg, vreg,
+                           dka, dva, qb, lane, kq, c_log2);
+        __builtin_amdgcn_sched_barrier(0);  // keep the two blocks' live ranges apart
+      }
+    } else {
 #pragma unroll
-      for (int kc = 0; kc < 8; ++kc) {
-        sacc[qb] = mfma32(as_bf16x8(ld16(qp + 16 * kc)), kreg[kc], sacc[qb]);
-        pacc[qb] = mfma32(as_bf16x8(ld16(gp + 16 * kc)), vreg[kc], pacc[qb]);
+      for (int qb = 0; qb < 2; ++qb) {
+        dkdv_block<false>(Qs[buf], Gs[buf], Qt[buf], Gt[buf], lse2s[buf], dls[buf], kreg, vreg,
+                          dka, dva, qb, lane, kq, c_log2);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
+  }
 
-    // lane holds key krow; element r of block qb is query q0 + 32 qb + acc_row(lane, r)
-    const bool diag = q0 < kw0 + 31;
-    bf16x8 pb[4], sb[4];
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int qi = 32 * qb + acc_row(lane, r);
-        float p = fast_exp2(fmaf(sacc[qb][r], c_log2, -lse2s[qi]));
-        if (diag && krow > q0 + qi) p = 0.f;
-        const float ds = p * (pacc[qb][r] - dls[qi]);
-        pb[2 * qb + (r >> 3)][r & 7] = to_bf16(p);
-        sb[2 * qb + (r >> 3)][r & 7] = to_bf16(ds);
-      }
-
-    // dV += P^T dout, dK += dS^T Q  (chunk c = queries 16 c + 8 half + 0..7)
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-#pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        const int t = toff(db * 32 + l32, 2 * c + half);
-        dva[db] = mfma32(pb[c], as_bf16x8(ld16(&Gt[t])), dva[db]);
-        dka[db] = mfma32(sb[c], as_bf16x8(ld16(&Qt[t])), dka[db]);
-      }
+  // Steady part: every query follows every key, no mask, no skipped block.
+  // Software pipeline over 32-query blocks: the step for block j computes the
+  // probabilities of j, the scores of j+1 and the dK/dV update of j.  Block
+  // j+1 may live in the next tile, so each tile takes two barriers: one before
+  // its successor overwrites the buffer of its predecessor, one to publish it.
+  if (qt_diag_end < n_qt) {
+    const int ts = qt_diag_end;
+    int b = (ts - qt0) & 1;  // buffer of tile ts; it last held tile ts-2, long retired
+    lstore(b);
+    __syncthreads();
+    gload(min(ts + 1, n_qt - 1));
+    f32x16 s0, p0, s1, p1;
+    dkdv_scores(Qs[b], Gs[b], 0, kreg, vreg, s0, p0, lane);
+    // Branch-free body: after the last tile the second step still computes
+    // scores of a block past the end (from a buffer refilled with clamped
+    // rows); they are never used.
+    for (int t = ts; t < n_qt; ++t) {
+      // block 2t (rows 0..31 of tile t) while computing scores of rows 32..63
+      dkdv_step<true>(Qs[b], Gs[b], 32, lse2s[b], dls[b], Qt[b], Gt[b], 0, kreg, vreg, s0, p0,
+                      s1, p1, dka, dva, lane, c_log2);
+      __syncthreads();  // every wavefront is done with tile t-1 (buffer b^1)
+      lstore(b ^ 1);
+      __syncthreads();
+      gload(min(t + 2, n_qt - 1));
+      // block 2t+1 (rows 32..63 of tile t) while computing scores of tile t+1 rows 0..31
+      dkdv_step<true>(Qs[b ^ 1], Gs[b ^ 1], 0, lse2s[b], dls[b], Qt[b], Gt[b], 32, kreg, vreg,
+                      s1, p1, s0, p0, dka, dva, lane, c_log2);
+      b ^= 1;
     }
   }
 
@@ -225,13 +345,61 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(
 constexpr int DQ_ROWS = 128;  // queries per workgroup (32 per wavefront)
 constexpr int DQ_KEYS = 64;   // keys per LDS tile
 
+// One 32-key block of a dQ step for one wavefront (32 queries).
+//   S^T = K Q^T, dP^T = V dout^T  (A = K / V rows from LDS, B = Q / dout in registers)
+//   P = exp2(c S - lse2), dS = P (dP - delta)      (lane: query, element r: key)
+//   dQ^T += K^T dS^T              (A = transposed K tile, B = dS^T from registers)
+template <bool MASK>
+__device__ __forceinline__ void dq_block(const u16* Ks, const u16* Vs, const u16* Kt,
+                                         const bf16x8 (&qreg)[8], const bf16x8 (&greg)[8],
+                                         f32x16 (&dqa)[4], int kb, int lane, int qrow_minus_k0,
+                                         float lse2, float dl, float c_log2) {
+  const int half = lane >> 5;
+  const int l32 = lane & 31;
+  f32x16 sacc = f32x16{}, pacc = f32x16{};
+  {
+    const u16* kp = &Ks[(kb * 32 + perm_row(l32)) * RS + 8 * half];
+    const u16* vp = &Vs[(kb * 32 + perm_row(l32)) * RS + 8 * half];
+#pragma unroll
+    for (int k4 = 0; k4 < 8; k4 += 4) {
+      bf16x8 ak[4], av[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        ak[i] = as_bf16x8(ld16(kp + 16 * (k4 + i)));
+        av[i] = as_bf16x8(ld16(vp + 16 * (k4 + i)));
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        sacc = mfma32(ak[i], qreg[k4 + i], sacc);
+        pacc = mfma32(av[i], greg[k4 + i], pacc);
+      }
+    }
+  }
+  bf16x8 sb[2];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    float p = fast_exp2(fmaf(sacc[r], c_log2, -lse2));
+    if (MASK && 32 * kb + acc_row(lane, r) > qrow_minus_k0) p = 0.f;  // key after query
+    sb[r >> 3][r & 7] = to_bf16(p * (pacc[r] - dl));
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int cg = 2 * (2 * kb + j) + half;  // keys 16 (2kb + j) + 8 half + 0..7
+    bf16x8 a[4];
+#pragma unroll
+    for (int db = 0; db < 4; ++db) a[db] = as_bf16x8(ld16(&Kt[toff(db * 32 + l32, cg)]));
+#pragma unroll
+    for (int db = 0; db < 4; ++db) dqa[db] = mfma32(a[db], sb[j], dqa[db]);
+  }
+}
+
 __global__ __launch_bounds__(256, 1) void dq_kernel(
     const u16* __restrict__ q, const u16* __restrict__ k, const u16* __restrict__ v,
     const u16* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
     u16* __restrict__ dq, int B, int T, int H, float c_log2, float scale) {
-  __shared__ __attribute__((aligned(16))) u16 Ks[DQ_KEYS * RS];
-  __shared__ __attribute__((aligned(16))) u16 Vs[DQ_KEYS * RS];
-  __shared__ __attribute__((aligned(16))) u16 Kt[D * DQ_KEYS];  // transposed, swizzled
+  __shared__ __attribute__((aligned(16))) u16 Ks[2][DQ_KEYS * RS];
+  __shared__ __attribute__((aligned(16))) u16 Vs[2][DQ_KEYS * RS];
+  __shared__ __attribute__((aligned(16))) u16 Kt[2][D * DQ_KEYS];  // transposed, swizzled
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -249,26 +417,20 @@ __global__ __launch_bounds__(256, 1) void dq_kernel(
   const size_t rs = static_cast<size_t>(H) * D;
   const size_t base = static_cast<size_t>(b) * T * rs + static_cast<size_t>(h) * D;
 
+  // rows past T read row T-1 (their dq is never stored)
   const int qrow = qw0 + l32;
+  const int qr = min(qrow, T - 1);
   bf16x8 qreg[8], greg[8];
-  float lse2 = INFINITY, dl = 0.f;
-  if (qrow < T) {
-    const u16* qp = q + base + static_cast<size_t>(qrow) * rs + 8 * half;
-    const u16* gp = dout + base + static_cast<size_t>(qrow) * rs + 8 * half;
+  {
+    const size_t off = base + static_cast<size_t>(qr) * rs + 8 * half;
 #pragma unroll
     for (int kc = 0; kc < 8; ++kc) {
-      qreg[kc] = as_bf16x8(ld16(qp + 16 * kc));
-      greg[kc] = as_bf16x8(ld16(gp + 16 * kc));
-    }
-    lse2 = lse[static_cast<size_t>(bh) * T + qrow] * kLog2e;
-    dl = delta[static_cast<size_t>(bh) * T + qrow];
-  } else {
-#pragma unroll
-    for (int kc = 0; kc < 8; ++kc) {
-      qreg[kc] = as_bf16x8(make_uint4(0, 0, 0, 0));
-      greg[kc] = qreg[kc];
+      qreg[kc] = as_bf16x8(ld16(q + off + 16 * kc));
+      greg[kc] = as_bf16x8(ld16(dout + off + 16 * kc));
     }
   }
+  const float lse2 = lse[static_cast<size_t>(bh) * T + qr] * kLog2e;
+  const float dl = delta[static_cast<size_t>(bh) * T + qr];
 
   f32x16 dqa[4];
 #pragma unroll
@@ -278,66 +440,50 @@ __global__ __launch_bounds__(256, 1) void dq_kernel(
   const int n_kt = last_q / DQ_KEYS + 1;
   const int lrow = tid >> 4;
   const int lchunk = tid & 15;
-
-  for (int kt = 0; kt < n_kt; ++kt) {
+  // key rows past T read row T-1: always masked, any finite value works
+  uint4 xk[4], xv[4];
+  auto gload = [&](int kt) {
     const int k0 = kt * DQ_KEYS;
-    uint4 xk[4], xv[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int r = k0 + 4 * lrow + i;
-      if (r < T) {
-        xk[i] = ld16(k + base + static_cast<size_t>(r) * rs + 8 * lchunk);
-        xv[i] = ld16(v + base + static_cast<size_t>(r) * rs + 8 * lchunk);
-      } else {
-        xk[i] = make_uint4(0, 0, 0, 0);
-        xv[i] = xk[i];
-      }
+      const size_t off =
+          base + static_cast<size_t>(min(k0 + 4 * lrow + i, T - 1)) * rs + 8 * lchunk;
+      xk[i] = ld16(k + off);
+      xv[i] = ld16(v + off);
     }
-    __syncthreads();
+  };
+
+  gload(0);
+  for (int kt = 0; kt < n_kt; ++kt) {
+    const int buf = kt & 1;
+    const int k0 = kt * DQ_KEYS;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      st16(&Ks[(4 * lrow + i) * RS + 8 * lchunk], xk[i]);
-      st16(&Vs[(4 * lrow + i) * RS + 8 * lchunk], xv[i]);
+      st16(&Ks[buf][(4 * lrow + i) * RS + 8 * lchunk], xk[i]);
+      st16(&Vs[buf][(4 * lrow + i) * RS + 8 * lchunk], xv[i]);
     }
-    tstore_4x8(Kt, xk, lrow, lchunk);
+    tstore_4x8(Kt[buf], xk, lrow, lchunk);
     __syncthreads();
+    if (kt + 1 < n_kt) gload(kt + 1);
 
-    if (k0 > qw0 + 31) continue;
-
-    f32x16 sacc[2], pacc[2];
+    if (k0 > qw0 + 31) continue;  // whole tile after this wavefront's queries
+    const int qk = qrow - k0;
+    if (k0 + DQ_KEYS - 1 > qw0) {  // tile crosses the diagonal
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      sacc[kb] = f32x16{};
-      pacc[kb] = f32x16{};
-      const u16* kp = &Ks[(kb * 32 + perm_row(l32)) * RS + 8 * half];
-      const u16* vp = &Vs[(kb * 32 + perm_row(l32)) * RS + 8 * half];
+      for (int kb = 0; kb < 2; ++kb) {
+        if (k0 + 32 * kb <= qw0 + 31)
+          dq_block<true>(Ks[buf], Vs[buf], Kt[buf], qreg, greg, dqa, kb, lane, qk, lse2, dl,
+                         c_log2);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
 #pragma unroll
-      for (int kc = 0; kc < 8; ++kc) {
-        sacc[kb] = mfma32(as_bf16x8(ld16(kp + 16 * kc)), qreg[kc], sacc[kb]);
-        pacc[kb] = mfma32(as_bf16x8(ld16(vp + 16 * kc)), greg[kc], pacc[kb]);
+      for (int kb = 0; kb < 2; ++kb) {
+        dq_block<false>(Ks[buf], Vs[buf], Kt[buf], qreg, greg, dqa, kb, lane, qk, lse2, dl,
+                        c_log2);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
-
-    const bool diag = k0 + DQ_KEYS - 1 > qw0;
-    bf16x8 sb[4];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = k0 + 32 * kb + acc_row(lane, r);
-        float p = fast_exp2(fmaf(sacc[kb][r], c_log2, -lse2));
-        if (diag && key > qrow) p = 0.f;
-        sb[2 * kb + (r >> 3)][r & 7] = to_bf16(p * (pacc[kb][r] - dl));
-      }
-
-    // dQ^T += K^T dS^T  (chunk c = keys 16 c + 8 half + 0..7)
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-#pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        const bf16x8 a = as_bf16x8(ld16(&Kt[toff(db * 32 + l32, 2 * c + half)]));
-        dqa[db] = mfma32(a, sb[c], dqa[db]);
-      }
   }
 
   if (qrow < T) {
