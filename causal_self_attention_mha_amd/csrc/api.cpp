@@ -65,6 +65,10 @@ na_status check_sizes(int B, int T, int H, int D) {
     return fail(NA_ERR_UNSUPPORTED, "head dim D=%d is not supported (only 128)", D);
   const long double n = (long double)B * T * H * D;
   if (n >= 9.2e18L) return fail(NA_ERR_INVALID_ARG, "B*T*H*D overflows 64-bit indexing");
+  // kernels index rows of one batch with 32-bit offsets
+  if ((long double)T * H * D > 2147483647.0L)
+    return fail(NA_ERR_UNSUPPORTED, "T*H*D = %.0Lf per batch exceeds 2^31-1",
+                (long double)T * H * D);
   // every grid is at most B*H*T workgroups in x
   if ((long double)B * H * T > 2147483647.0L)
     return fail(NA_ERR_INVALID_ARG, "B*H*T exceeds the launch grid limit");

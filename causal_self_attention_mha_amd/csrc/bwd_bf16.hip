@@ -160,10 +160,12 @@ __device__ __forceinline__ void dkdv_block(const u16* Qs, const u16* Gs, const u
 }
 
 // Steady-state step: probabilities of the current block (held in s_cur,
-// p_cur), scores of the next block (if HAS_NEXT) into s_nxt, p_nxt, then the
-// current block's dK/dV accumulation.  One basic block, so the scheduler can
-// interleave the next block's MFMAs with this block's VALU work.
-template <bool HAS_NEXT>
+// p_cur), scores of the next block into s_nxt, p_nxt, then the current
+// block's dK/dV accumulation.  The order is fixed by hand in eight rounds,
+// separated by scheduling fences: each round issues the LDS reads two rounds
+// ahead, one score MFMA for S and one for dP, and the probability math of two
+// of this lane's sixteen (key, query) elements, so the VALU work runs while
+// the matrix cores are busy.
 __device__ __forceinline__ void dkdv_step(const u16* QsN, const u16* GsN, int rowN,
                                           const float* lse2s, const float* dls, const u16* Qt,
                                           const u16* Gt, int rowC, const bf16x8 (&kreg)[8],
@@ -171,10 +173,81 @@ __device__ __forceinline__ void dkdv_step(const u16* QsN, const u16* GsN, int ro
                                           const f32x16& p_cur, f32x16& s_nxt, f32x16& p_nxt,
                                           f32x16 (&dka)[4], f32x16 (&dva)[4], int lane,
                                           float c_log2) {
-  bf16x8 pb[2], sb[2];
-  dkdv_probs<false>(s_cur, p_cur, lse2s, dls, rowC, pb, sb, lane, 0, c_log2);
-  if (HAS_NEXT) dkdv_scores(QsN, GsN, rowN, kreg, vreg, s_nxt, p_nxt, lane);
-  dkdv_accum(pb, sb, Qt, Gt, rowC, dka, dva, lane);
+  const int half = lane >> 5;
+  const int l32 = lane & 31;
+  const u16* qp = &QsN[(rowN + perm_row(l32)) * RS + 8 * half];
+  const u16* gp = &GsN[(rowN + perm_row(l32)) * RS + 8 * half];
+  // element r of the current block: query row r0 + 16 (r/8) + r%8
+  const int r0 = rowC + 8 * half;
+  float l16[16], d16[16];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const float4 a = *reinterpret_cast<const float4*>(&lse2s[r0 + 16 * j + 4 * k]);
+      const float4 d = *reinterpret_cast<const float4*>(&dls[r0 + 16 * j + 4 * k]);
+      l16[8 * j + 4 * k] = a.x; l16[8 * j + 4 * k + 1] = a.y;
+      l16[8 * j + 4 * k + 2] = a.z; l16[8 * j + 4 * k + 3] = a.w;
+      d16[8 * j + 4 * k] = d.x; d16[8 * j + 4 * k + 1] = d.y;
+      d16[8 * j + 4 * k + 2] = d.z; d16[8 * j + 4 * k + 3] = d.w;
+    }
+  bf16x8 aq[8], ag[8];
+  aq[0] = as_bf16x8(ld16(qp));
+  ag[0] = as_bf16x8(ld16(gp));
+  aq[1] = as_bf16x8(ld16(qp + 16));
+  ag[1] = as_bf16x8(ld16(gp + 16));
+  s_nxt = f32x16{};
+  p_nxt = f32x16{};
+  uint32_t pw[8], sw[8];  // bf16 pairs (elements 2i, 2i+1)
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    if (i + 2 < 8) {
+      aq[i + 2] = as_bf16x8(ld16(qp + 16 * (i + 2)));
+      ag[i + 2] = as_bf16x8(ld16(gp + 16 * (i + 2)));
+    }
+    s_nxt = mfma32(aq[i], kreg[i], s_nxt);
+    const int r = 2 * i;
+    const float p0 = fast_exp2(fmaf(s_cur[r], c_log2, -l16[r]));
+    const float p1 = fast_exp2(fmaf(s_cur[r + 1], c_log2, -l16[r + 1]));
+    pw[i] = pack_bf16x2(p0, p1);
+    sw[i] = pack_bf16x2(p0 * (p_cur[r] - d16[r]), p1 * (p_cur[r + 1] - d16[r + 1]));
+    // keep this round's VALU work in this round (no sinking to the first use)
+    asm volatile("" : "+v"(pw[i]), "+v"(sw[i]));
+    p_nxt = mfma32(ag[i], vreg[i], p_nxt);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  const bf16x8 pb[2] = {as_bf16x8(make_uint4(pw[0], pw[1], pw[2], pw[3])),
+                        as_bf16x8(make_uint4(pw[4], pw[5], pw[6], pw[7]))};
+  const bf16x8 sb[2] = {as_bf16x8(make_uint4(sw[0], sw[1], sw[2], sw[3])),
+                        as_bf16x8(make_uint4(sw[4], sw[5], sw[6], sw[7]))};
+  // dV += P^T dout, dK += dS^T Q for the current block: operands of chunk j+1
+  // are read while chunk j's MFMAs run
+  bf16x8 bg[2][4], bq[2][4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db) {
+    const int t = toff(db * 32 + l32, rowC / 8 + half);
+    bg[0][db] = as_bf16x8(ld16(&Gt[t]));
+    bq[0][db] = as_bf16x8(ld16(&Qt[t]));
+  }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    if (j == 0) {
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const int t = toff(db * 32 + l32, rowC / 8 + 2 + half);
+        bg[1][db] = as_bf16x8(ld16(&Gt[t]));
+        bq[1][db] = as_bf16x8(ld16(&Qt[t]));
+      }
+    }
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      dva[db] = mfma32(pb[j], bg[j][db], dva[db]);
+      dka[db] = mfma32(sb[j], bq[j][db], dka[db]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
 }
 
 __global__ __launch_bounds__(256, 1) void dkdv_kernel(
@@ -202,7 +275,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(
   const int b = bh / H, h = bh % H;
   const int k0 = kt * KT_KEYS;
   const int kw0 = k0 + 32 * wave;
-  const size_t rs = static_cast<size_t>(H) * D;
+  const int rs = H * D;  // 32-bit row offsets within one (b, h) slice
   const size_t base = static_cast<size_t>(b) * T * rs + static_cast<size_t>(h) * D;
   const float* lse_bh = lse + static_cast<size_t>(bh) * T;
   const float* del_bh = delta + static_cast<size_t>(bh) * T;
@@ -212,7 +285,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(
   const int krow = kw0 + l32;
   bf16x8 kreg[8], vreg[8];
   {
-    const size_t off = base + static_cast<size_t>(min(krow, T - 1)) * rs + 8 * half;
+    const size_t off = base + min(krow, T - 1) * rs + 8 * half;
 #pragma unroll
     for (int kc = 0; kc < 8; ++kc) {
       kreg[kc] = as_bf16x8(ld16(k + off + 16 * kc));
@@ -238,8 +311,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(
     const int q0 = qt * QT_ROWS;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const size_t off =
-          base + static_cast<size_t>(min(q0 + 4 * lrow + i, T - 1)) * rs + 8 * lchunk;
+      const size_t off = base + min(q0 + 4 * lrow + i, T - 1) * rs + 8 * lchunk;
       xq[i] = ld16(q + off);
       xg[i] = ld16(dout + off);
     }
@@ -313,14 +385,14 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(
     // rows); they are never used.
     for (int t = ts; t < n_qt; ++t) {
       // block 2t (rows 0..31 of tile t) while computing scores of rows 32..63
-      dkdv_step<true>(Qs[b], Gs[b], 32, lse2s[b], dls[b], Qt[b], Gt[b], 0, kreg, vreg, s0, p0,
+      dkdv_step(Qs[b], Gs[b], 32, lse2s[b], dls[b], Qt[b], Gt[b], 0, kreg, vreg, s0, p0,
                       s1, p1, dka, dva, lane, c_log2);
       __syncthreads();  // every wavefront is done with tile t-1 (buffer b^1)
       lstore(b ^ 1);
       __syncthreads();
       gload(min(t + 2, n_qt - 1));
       // block 2t+1 (rows 32..63 of tile t) while computing scores of tile t+1 rows 0..31
-      dkdv_step<true>(Qs[b ^ 1], Gs[b ^ 1], 0, lse2s[b], dls[b], Qt[b], Gt[b], 32, kreg, vreg,
+      dkdv_step(Qs[b ^ 1], Gs[b ^ 1], 0, lse2s[b], dls[b], Qt[b], Gt[b], 32, kreg, vreg,
                       s1, p1, s0, p0, dka, dva, lane, c_log2);
       b ^= 1;
     }
@@ -333,7 +405,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(
     for (int r = 0; r < 16; ++r) {
       const int key = kw0 + 8 * (r >> 2) + 4 * half + (r & 3);
       if (key < T) {
-        const size_t off = base + static_cast<size_t>(key) * rs + 32 * db + l32;
+        const size_t off = base + key * rs + 32 * db + l32;
         dk[off] = __builtin_bit_cast(u16, to_bf16(dka[db][r] * scale));
         dv[off] = __builtin_bit_cast(u16, to_bf16(dva[db][r]));
       }
@@ -345,51 +417,100 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(
 constexpr int DQ_ROWS = 128;  // queries per workgroup (32 per wavefront)
 constexpr int DQ_KEYS = 64;   // keys per LDS tile
 
-// One 32-key block of a dQ step for one wavefront (32 queries).
-//   S^T = K Q^T, dP^T = V dout^T  (A = K / V rows from LDS, B = Q / dout in registers)
-//   P = exp2(c S - lse2), dS = P (dP - delta)      (lane: query, element r: key)
-//   dQ^T += K^T dS^T              (A = transposed K tile, B = dS^T from registers)
-template <bool MASK>
-__device__ __forceinline__ void dq_block(const u16* Ks, const u16* Vs, const u16* Kt,
-                                         const bf16x8 (&qreg)[8], const bf16x8 (&greg)[8],
-                                         f32x16 (&dqa)[4], int kb, int lane, int qrow_minus_k0,
-                                         float lse2, float dl, float c_log2) {
+// One 32-key block of a dQ step for one wavefront (32 queries), in three
+// phases:
+//   scores:  S^T = K Q^T, dP^T = V dout^T  (A = K / V rows from LDS, B = Q /
+//            dout in registers; lane: query, element r: key acc_row(lane, r))
+//   probs:   P = exp2(c S - lse2), dS = P (dP - delta), rounded to bf16
+//   accum:   dQ^T += K^T dS^T  (A = transposed K tile, B = dS^T from registers)
+__device__ __forceinline__ void dq_scores(const u16* Ks, const u16* Vs, int row0,
+                                          const bf16x8 (&qreg)[8], const bf16x8 (&greg)[8],
+                                          f32x16& sacc, f32x16& pacc, int lane) {
   const int half = lane >> 5;
   const int l32 = lane & 31;
-  f32x16 sacc = f32x16{}, pacc = f32x16{};
-  {
-    const u16* kp = &Ks[(kb * 32 + perm_row(l32)) * RS + 8 * half];
-    const u16* vp = &Vs[(kb * 32 + perm_row(l32)) * RS + 8 * half];
+  sacc = f32x16{};
+  pacc = f32x16{};
+  const u16* kp = &Ks[(row0 + perm_row(l32)) * RS + 8 * half];
+  const u16* vp = &Vs[(row0 + perm_row(l32)) * RS + 8 * half];
 #pragma unroll
-    for (int k4 = 0; k4 < 8; k4 += 4) {
-      bf16x8 ak[4], av[4];
+  for (int k4 = 0; k4 < 8; k4 += 4) {
+    bf16x8 ak[4], av[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        ak[i] = as_bf16x8(ld16(kp + 16 * (k4 + i)));
-        av[i] = as_bf16x8(ld16(vp + 16 * (k4 + i)));
-      }
+    for (int i = 0; i < 4; ++i) {
+      ak[i] = as_bf16x8(ld16(kp + 16 * (k4 + i)));
+      av[i] = as_bf16x8(ld16(vp + 16 * (k4 + i)));
+    }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        sacc = mfma32(ak[i], qreg[k4 + i], sacc);
-        pacc = mfma32(av[i], greg[k4 + i], pacc);
-      }
+    for (int i = 0; i < 4; ++i) {
+      sacc = mfma32(ak[i], qreg[k4 + i], sacc);
+      pacc = mfma32(av[i], greg[k4 + i], pacc);
     }
   }
-  bf16x8 sb[2];
+}
+
+template <bool MASK>
+__device__ __forceinline__ void dq_probs(const f32x16& sacc, const f32x16& pacc, bf16x8 (&sb)[2],
+                                         int lane, int qrow_minus_k0, int row0, float lse2,
+                                         float dl, float c_log2) {
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     float p = fast_exp2(fmaf(sacc[r], c_log2, -lse2));
-    if (MASK && 32 * kb + acc_row(lane, r) > qrow_minus_k0) p = 0.f;  // key after query
+    if (MASK && row0 + acc_row(lane, r) > qrow_minus_k0) p = 0.f;  // key after query
     sb[r >> 3][r & 7] = to_bf16(p * (pacc[r] - dl));
   }
+}
+
+__device__ __forceinline__ void dq_accum(const bf16x8 (&sb)[2], const u16* Kt, int row0,
+                                         f32x16 (&dqa)[4], int lane) {
+  const int half = lane >> 5;
+  const int l32 = lane & 31;
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    const int cg = 2 * (2 * kb + j) + half;  // keys 16 (2kb + j) + 8 half + 0..7
+    const int cg = row0 / 8 + 2 * j + half;  // keys row0 + 16 j + 8 half + 0..7
     bf16x8 a[4];
 #pragma unroll
     for (int db = 0; db < 4; ++db) a[db] = as_bf16x8(ld16(&Kt[toff(db * 32 + l32, cg)]));
 #pragma unroll
     for (int db = 0; db < 4; ++db) dqa[db] = mfma32(a[db], sb[j], dqa[db]);
+  }
+}
+
+template <bool MASK>
+__device__ __forceinline__ void dq_block(const u16* Ks, const u16* Vs, const u16* Kt,
+                                         const bf16x8 (&qreg)[8], const bf16x8 (&greg)[8],
+                                         f32x16 (&dqa)[4], int kb, int lane, int qrow_minus_k0,
+                                         float lse2, float dl, float c_log2) {
+  f32x16 sacc, pacc;
+  dq_scores(Ks, Vs, 32 * kb, qreg, greg, sacc, pacc, lane);
+  bf16x8 sb[2];
+  dq_probs<MASK>(sacc, pacc, sb, lane, qrow_minus_k0, 32 * kb, lse2, dl, c_log2);
+  dq_accum(sb, Kt, 32 * kb, dqa, lane);
+}
+
+// Steady-state step: probabilities of the current block, scores of the next
+// block, the current block's dQ update; one basic block.
+__device__ __forceinline__ void dq_step(const u16* KsN, const u16* VsN, int rowN, const u16* Kt,
+                                        int rowC, const bf16x8 (&qreg)[8],
+                                        const bf16x8 (&greg)[8], const f32x16& s_cur,
+                                        const f32x16& p_cur, f32x16& s_nxt, f32x16& p_nxt,
+                                        f32x16 (&dqa)[4], int lane, float lse2, float dl,
+                                        float c_log2) {
+  bf16x8 sb[2];
+  dq_probs<false>(s_cur, p_cur, sb, lane, 0, rowC, lse2, dl, c_log2);
+  dq_scores(KsN, VsN, rowN, qreg, greg, s_nxt, p_nxt, lane);
+  dq_accum(sb, Kt, rowC, dqa, lane);
+  __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // DS read
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+    __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // VALU
+    __builtin_amdgcn_sched_group_barrier(0x400, 1, 0);  // TRANS
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);  // VALU
   }
 }
 
@@ -414,7 +535,7 @@ __global__ __launch_bounds__(256, 1) void dq_kernel(
   const int b = bh / H, h = bh % H;
   const int q0 = qt * DQ_ROWS;
   const int qw0 = q0 + 32 * wave;
-  const size_t rs = static_cast<size_t>(H) * D;
+  const int rs = H * D;  // 32-bit row offsets within one (b, h) slice
   const size_t base = static_cast<size_t>(b) * T * rs + static_cast<size_t>(h) * D;
 
   // rows past T read row T-1 (their dq is never stored)
@@ -422,7 +543,7 @@ __global__ __launch_bounds__(256, 1) void dq_kernel(
   const int qr = min(qrow, T - 1);
   bf16x8 qreg[8], greg[8];
   {
-    const size_t off = base + static_cast<size_t>(qr) * rs + 8 * half;
+    const size_t off = base + qr * rs + 8 * half;
 #pragma unroll
     for (int kc = 0; kc < 8; ++kc) {
       qreg[kc] = as_bf16x8(ld16(q + off + 16 * kc));
@@ -443,26 +564,58 @@ __global__ __launch_bounds__(256, 1) void dq_kernel(
   // key rows past T read row T-1: always masked, any finite value works
   uint4 xk[4], xv[4];
   auto gload = [&](int kt) {
-    const int k0 = kt * DQ_KEYS;
+    const int k0 = kt * DQ_KEYS;  // rows clamp to T-1
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const size_t off =
-          base + static_cast<size_t>(min(k0 + 4 * lrow + i, T - 1)) * rs + 8 * lchunk;
+      const size_t off = base + min(k0 + 4 * lrow + i, T - 1) * rs + 8 * lchunk;
       xk[i] = ld16(k + off);
       xv[i] = ld16(v + off);
     }
   };
 
-  gload(0);
-  for (int kt = 0; kt < n_kt; ++kt) {
-    const int buf = kt & 1;
-    const int k0 = kt * DQ_KEYS;
+  auto lstore = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       st16(&Ks[buf][(4 * lrow + i) * RS + 8 * lchunk], xk[i]);
       st16(&Vs[buf][(4 * lrow + i) * RS + 8 * lchunk], xv[i]);
     }
     tstore_4x8(Kt[buf], xk, lrow, lchunk);
+  };
+
+  // Steady part: key tiles entirely before every query of this workgroup
+  // (no mask, no skipped block), software-pipelined over 32-key blocks as in
+  // the dK/dV kernel.  The last step computes scores of one block past the
+  // steady range; they are never used.
+  const int ns = q0 / DQ_KEYS;
+  if (ns > 0) {
+    int b = 0;
+    gload(0);
+    lstore(b);
+    __syncthreads();
+    gload(1);
+    f32x16 s0, p0, s1, p1;
+    dq_scores(Ks[b], Vs[b], 0, qreg, greg, s0, p0, lane);
+    for (int t = 0; t < ns; ++t) {
+      dq_step(Ks[b], Vs[b], 32, Kt[b], 0, qreg, greg, s0, p0, s1, p1, dqa, lane, lse2, dl,
+              c_log2);
+      __syncthreads();  // every wavefront is done with tile t-1 (buffer b^1)
+      lstore(b ^ 1);
+      __syncthreads();
+      gload(min(t + 2, n_kt - 1));
+      dq_step(Ks[b ^ 1], Vs[b ^ 1], 0, Kt[b], 32, qreg, greg, s1, p1, s0, p0, dqa, lane, lse2,
+              dl, c_log2);
+      b ^= 1;
+    }
+    __syncthreads();  // all wavefronts leave the pipelined loop before buffers are reused
+  }
+
+  // Diagonal part: the key tiles that overlap this workgroup's queries, one
+  // barrier per tile, causal select where a tile crosses a wavefront's rows.
+  gload(ns);
+  for (int kt = ns; kt < n_kt; ++kt) {
+    const int buf = (kt - ns) & 1;
+    const int k0 = kt * DQ_KEYS;
+    lstore(buf);
     __syncthreads();
     if (kt + 1 < n_kt) gload(kt + 1);
 
@@ -487,7 +640,7 @@ __global__ __launch_bounds__(256, 1) void dq_kernel(
   }
 
   if (qrow < T) {
-    u16* qp = dq + base + static_cast<size_t>(qrow) * rs;
+    u16* qp = dq + base + qrow * rs;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll

@@ -62,7 +62,8 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const u16* __restrict_
   const int b = bh / H, h = bh % H;
   const int q0 = qt * BQ;
   const int qw0 = q0 + wave * 32;
-  const size_t rs = static_cast<size_t>(H) * D;                       // stride between t
+  // 32-bit row offsets within one (b, h) slice (T * H * D < 2^31 is checked on the host)
+  const int rs = H * D;  // stride between t
   const size_t base = static_cast<size_t>(b) * T * rs + static_cast<size_t>(h) * D;
 
   // Q^T operand: lane holds q[qw0 + l32][16 kc + 8 half + 0..7], kc = 0..7.
@@ -70,7 +71,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const u16* __restrict_
   const int qrow = qw0 + l32;
   bf16x8 qreg[8];
   {
-    const u16* qp = q + base + static_cast<size_t>(min(qrow, T - 1)) * rs + 8 * half;
+    const u16* qp = q + base + min(qrow, T - 1) * rs + 8 * half;
 #pragma unroll
     for (int kc = 0; kc < 8; ++kc) qreg[kc] = as_bf16x8(ld16(qp + 16 * kc));
   }
@@ -98,8 +99,8 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const u16* __restrict_
     const int k0 = kt * BK;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      kv[i] = ld16(kg + static_cast<size_t>(min(k0 + lrow + 16 * i, T - 1)) * rs);
-      vv[i] = ld16(vg + static_cast<size_t>(min(k0 + 4 * lrow + i, T - 1)) * rs);
+      kv[i] = ld16(kg + min(k0 + lrow + 16 * i, T - 1) * rs);
+      vv[i] = ld16(vg + min(k0 + 4 * lrow + i, T - 1) * rs);
     }
   };
   auto lstore = [&](int buf) {
@@ -192,7 +193,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const u16* __restrict_
   const float l = lpart + __shfl_xor(lpart, 32, 64);
   if (qrow < T) {
     const float inv = 1.f / l;
-    u16* op = o + base + static_cast<size_t>(qrow) * rs;
+    u16* op = o + base + qrow * rs;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll

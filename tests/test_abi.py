@@ -70,7 +70,8 @@ def test_fwd_rejects_bad_arguments(lib):
     assert fwd(lib, D=64) == UNSUPPORTED and b"head dim" in lib.na_last_error()
     assert fwd(lib, k=A + 0x108) == INVALID and b"aligned" in lib.na_last_error()
     assert fwd(lib, o=A) == INVALID and b"aliases" in lib.na_last_error()
-    assert fwd(lib, B=1 << 20, T=1 << 20, H=1 << 10) == INVALID   # grid limit
+    assert fwd(lib, B=1, T=1 << 20, H=1 << 10) == UNSUPPORTED    # T*H*D >= 2^31 per batch
+    assert fwd(lib, B=1 << 20, T=1 << 12, H=1) == INVALID        # B*H*T over the grid limit
     assert lib.na_attn_fwd_f32(A, A + 16, A + 32, A + 48, A, 1, 8, 1, 128, None) == INVALID
 
 
