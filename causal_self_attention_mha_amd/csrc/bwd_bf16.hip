@@ -30,7 +30,9 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 // ---------------------------------------------------------------- delta
 
-// 16 lanes per (b, t, h) row, 16 rows per 256-thread workgroup.
+// 16 lanes per row, 16 rows per 256-thread workgroup.  Rows are walked in
+// (b, h, t) order, t fastest, so the fp32 delta stores of neighbouring groups
+// are contiguous; each group still reads 256 contiguous bytes of o and dout.
 __global__ __launch_bounds__(256) void delta_kernel(const u16* __restrict__ o,
                                                     const u16* __restrict__ dout,
                                                     float* __restrict__ delta, int B, int T,
@@ -39,8 +41,13 @@ __global__ __launch_bounds__(256) void delta_kernel(const u16* __restrict__ o,
   const long n_rows = static_cast<long>(B) * T * H;
   if (row >= n_rows) return;  // whole 16-lane groups drop out together
   const int chunk = threadIdx.x & 15;
-  const uint4 a = ld16(o + row * D + 8 * chunk);
-  const uint4 g = ld16(dout + row * D + 8 * chunk);
+  const int t = static_cast<int>(row % T);
+  const long bh = row / T;
+  const int h = static_cast<int>(bh % H);
+  const int b = static_cast<int>(bh / H);
+  const size_t off = ((static_cast<size_t>(b) * T + t) * H + h) * D + 8 * chunk;
+  const uint4 a = ld16(o + off);
+  const uint4 g = ld16(dout + off);
   float acc = 0.f;
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
@@ -49,13 +56,7 @@ __global__ __launch_bounds__(256) void delta_kernel(const u16* __restrict__ o,
     acc = fmaf(__uint_as_float(x & 0xffff0000u), __uint_as_float(y & 0xffff0000u), acc);
   }
   acc = sum16(acc);
-  if (chunk == 0) {
-    const int h = static_cast<int>(row % H);
-    const long bt = row / H;
-    const int t = static_cast<int>(bt % T);
-    const int b = static_cast<int>(bt / T);
-    delta[(static_cast<size_t>(b) * H + h) * T + t] = acc;
-  }
+  if (chunk == 0) delta[row] = acc;  // row == (b * H + h) * T + t
 }
 
 // ---------------------------------------------------------------- dK, dV
@@ -270,8 +271,9 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(
   const int l32 = lane & 31;
 
   const int BH = B * H;
-  const int kt = static_cast<int>(blockIdx.x) / BH;  // key tile 0 has the most work: first
-  const int bh = static_cast<int>(blockIdx.x) % BH;
+  const int n_ktiles = (T + KT_KEYS - 1) / KT_KEYS;
+  int bh, kt;  // key tile 0 has the most work: first
+  xcd_tile_map(static_cast<int>(blockIdx.x), BH, n_ktiles, bh, kt);
   const int b = bh / H, h = bh % H;
   const int k0 = kt * KT_KEYS;
   const int kw0 = k0 + 32 * wave;
@@ -530,8 +532,9 @@ __global__ __launch_bounds__(256, 1) void dq_kernel(
 
   const int BH = B * H;
   const int n_qt = (T + DQ_ROWS - 1) / DQ_ROWS;
-  const int qt = n_qt - 1 - static_cast<int>(blockIdx.x) / BH;  // heaviest first
-  const int bh = static_cast<int>(blockIdx.x) % BH;
+  int bh, t;
+  xcd_tile_map(static_cast<int>(blockIdx.x), BH, n_qt, bh, t);
+  const int qt = n_qt - 1 - t;  // heaviest (last) query tile first
   const int b = bh / H, h = bh % H;
   const int q0 = qt * DQ_ROWS;
   const int qw0 = q0 + 32 * wave;

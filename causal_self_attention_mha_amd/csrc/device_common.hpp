@@ -73,6 +73,24 @@ __device__ __forceinline__ int acc_row(int lane, int r) {
   return 8 * (lane >> 5) + (r & 7) + 16 * (r >> 3);
 }
 
+// Maps workgroup index bid to a (batch*head, tile) pair.  The hardware hands
+// workgroup i to XCD i % 8, and each XCD has its own L2; this order makes the
+// workgroups of one XCD cover one head's tiles back to back (tile 0 first,
+// which callers make the heaviest), so the K/V (or Q/dout) rows that all
+// tiles of a head share stay in that XCD's L2.  Falls back to head-fastest
+// order when the head count is not a multiple of 8.
+__device__ __forceinline__ void xcd_tile_map(int bid, int BH, int n_tiles, int& bh, int& t) {
+  constexpr int kXcds = 8;
+  if (BH % kXcds == 0) {
+    const int x = bid % kXcds, w = bid / kXcds;
+    bh = x + kXcds * (w / n_tiles);
+    t = w % n_tiles;
+  } else {
+    bh = bid % BH;
+    t = bid / BH;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Transposed LDS tile: 128 rows (head-dim index d) x 64 columns (keys or
 // queries) of bf16, row stride 128 bytes, no padding.  The 16-byte column

@@ -23,7 +23,8 @@
 //     with c = s log2(e), one FMA and one v_exp_f32 per score;
 //   * key tiles entirely above the diagonal are never visited; only tiles that
 //     cross the diagonal apply the causal select;
-//   * workgroups are issued heaviest query tile first.
+//   * each XCD runs one head's query tiles back to back, heaviest first, so
+//     the head's K and V stay in that XCD's L2.
 #include "device_common.hpp"
 #include "internal.hpp"
 
@@ -57,8 +58,9 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const u16* __restrict_
 
   const int BH = B * H;
   const int n_qt = (T + BQ - 1) / BQ;
-  const int qt = n_qt - 1 - static_cast<int>(blockIdx.x) / BH;  // heaviest first
-  const int bh = static_cast<int>(blockIdx.x) % BH;
+  int bh, t;
+  xcd_tile_map(static_cast<int>(blockIdx.x), BH, n_qt, bh, t);
+  const int qt = n_qt - 1 - t;  // heaviest (last) query tile first
   const int b = bh / H, h = bh % H;
   const int q0 = qt * BQ;
   const int qw0 = q0 + wave * 32;
