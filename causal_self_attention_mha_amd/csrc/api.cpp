@@ -141,8 +141,8 @@ na_status na_attn_decode_timed(const void* q, const void* k_cache, const void* v
                     {{o, "o"}, {workspace, "workspace"}});
   }
   if (st) return st;
-  if (B > 65535 || H > 65535)
-    return fail(NA_ERR_INVALID_ARG, "decode supports B, H <= 65535 (B=%d H=%d)", B, H);
+  if (B > 65535) return fail(NA_ERR_INVALID_ARG, "decode supports B <= 65535 (B=%d)", B);
+  if (H > 32) return fail(NA_ERR_UNSUPPORTED, "decode supports H <= 32 (H=%d)", H);
   const size_t need = na::decode_workspace_bytes(B, H, T_cap);
   if (workspace_bytes < need)
     return fail(NA_ERR_INVALID_ARG, "workspace_bytes %zu < required %zu", workspace_bytes, need);

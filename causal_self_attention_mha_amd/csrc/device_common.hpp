@@ -44,10 +44,21 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
-// Sum over aligned groups of 16 lanes.
+// DPP lane permutation of x within each 16-lane row (no LDS traffic).
+template <int kCtrl>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), kCtrl, 0xf, 0xf, false));
+}
+
+// Sum over aligned groups of 16 lanes (one DPP row); every lane gets the sum.
+// Butterfly: swap neighbours, swap pairs (quad_perm), then mirror within each
+// half row and within the row.
 __device__ __forceinline__ float sum16(float x) {
-#pragma unroll
-  for (int off = 8; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
+  x += dpp<0xB1>(x);   // quad_perm [1,0,3,2]
+  x += dpp<0x4E>(x);   // quad_perm [2,3,0,1]
+  x += dpp<0x141>(x);  // row_half_mirror
+  x += dpp<0x140>(x);  // row_mirror
   return x;
 }
 

@@ -86,7 +86,8 @@ na_status na_attn_bwd(const void* q, const void* k, const void* v, const void* o
  * output; lse: fp32 (B, H) output, or NULL.  A sequence of length 0 gives
  * o = 0 and lse = -inf.  workspace: device scratch of at least
  * na_attn_decode_workspace_bytes(B, H, D, T_cap) bytes (NA_ERR_INVALID_ARG if
- * smaller).  Enqueues two kernels: split-KV partials, then their combine.
+ * smaller).  H <= 32 (else NA_ERR_UNSUPPORTED), B <= 65535.  Enqueues two
+ * kernels: split-KV partials, then their combine.
  */
 na_status na_attn_decode(const void* q, const void* k_cache, const void* v_cache,
                          const int* seqlens, void* o, float* lse, int B, int H, int D,
