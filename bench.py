@@ -194,6 +194,8 @@ def main():
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     lse = torch.empty((B, H, T), dtype=torch.float32, device=dev)
     delta = torch.empty_like(lse)
+    ws_bytes = na.bwd_workspace_bytes(B, T, H)     # dS scratch for the dQ GEMM
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev).cuda_stream
     P = ctypes.c_void_p
     ptr = lambda t: P(t.data_ptr())  # noqa: E731
@@ -209,8 +211,8 @@ def main():
         if st:
             raise RuntimeError(lib.na_last_error().decode())
         st = lib.na_attn_bwd_timed(ptr(q), ptr(k), ptr(v), ptr(o), ptr(do), ptr(lse), ptr(dq),
-                                   ptr(dk), ptr(dv), ptr(delta), B, T, H, D, P(stream),
-                                   ctypes.cast(ev_arr[i], P))
+                                   ptr(dk), ptr(dv), ptr(delta), ptr(ws), ws_bytes, B, T, H, D,
+                                   P(stream), ctypes.cast(ev_arr[i], P))
         if st:
             raise RuntimeError(lib.na_last_error().decode())
 
@@ -269,7 +271,7 @@ def main():
         "roofline": roofline,
     }
 
-    del q, k, v, do, o, dq, dk, dv
+    del q, k, v, do, o, dq, dk, dv, ws
     torch.cuda.empty_cache()
 
     # ---------------- decode

@@ -22,7 +22,8 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["attn_fwd", "attn_bwd", "attn_decode", "decode_workspace_bytes", "load_library",
+__all__ = ["attn_fwd", "attn_bwd", "attn_decode", "decode_workspace_bytes", "bwd_workspace_bytes",
+           "load_library",
            "library_path", "NAError", "HEAD_DIM"]
 
 HEAD_DIM = 128
@@ -59,13 +60,16 @@ def load_library():
     lib = ctypes.CDLL(path)
     vp, i, f32p, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t
     lib.na_attn_fwd.argtypes = [vp, vp, vp, vp, f32p, i, i, i, i, vp]
-    lib.na_attn_bwd.argtypes = [vp, vp, vp, vp, vp, f32p, vp, vp, vp, f32p, i, i, i, i, vp]
+    lib.na_attn_bwd.argtypes = [vp, vp, vp, vp, vp, f32p, vp, vp, vp, f32p, vp, sz, i, i, i, i,
+                                vp]
+    lib.na_attn_bwd_workspace_bytes.argtypes = [i, i, i, i]
+    lib.na_attn_bwd_workspace_bytes.restype = sz
     lib.na_attn_decode.argtypes = [vp, vp, vp, vp, vp, f32p, i, i, i, i, vp, sz, vp]
     lib.na_attn_decode_workspace_bytes.argtypes = [i, i, i, i]
     lib.na_attn_decode_workspace_bytes.restype = sz
     lib.na_attn_fwd_f32.argtypes = [vp, vp, vp, vp, f32p, i, i, i, i, vp]
     lib.na_attn_bwd_f32.argtypes = [vp, vp, vp, vp, vp, f32p, vp, vp, vp, f32p, i, i, i, i, vp]
-    lib.na_attn_bwd_timed.argtypes = lib.na_attn_bwd.argtypes + [vp]
+    lib.na_attn_bwd_timed.argtypes = lib.na_attn_bwd.argtypes + [vp]  # + events
     lib.na_attn_decode_timed.argtypes = lib.na_attn_decode.argtypes + [vp]
     for fn in ("na_attn_fwd", "na_attn_bwd", "na_attn_decode", "na_attn_fwd_f32",
                "na_attn_bwd_f32", "na_attn_bwd_timed", "na_attn_decode_timed"):
@@ -130,8 +134,17 @@ def attn_fwd(q, k, v, o=None, lse=None):
     return o, lse
 
 
-def attn_bwd(q, k, v, o, dout, lse, dq=None, dk=None, dv=None, delta=None):
-    """Causal attention backward.  Returns (dq, dk, dv, delta)."""
+def bwd_workspace_bytes(B, T, H, D=HEAD_DIM):
+    return int(load_library().na_attn_bwd_workspace_bytes(B, T, H, D))
+
+
+def attn_bwd(q, k, v, o, dout, lse, dq=None, dk=None, dv=None, delta=None, workspace=None,
+             recompute_dq=False):
+    """Causal attention backward.  Returns (dq, dk, dv, delta).
+
+    bf16: by default a dS workspace is allocated (or `workspace` is used) so
+    that dq is a GEMM over the stored dS; recompute_dq=True passes no
+    workspace and the dq pass recomputes S and dP.  fp32 has one path."""
     import torch
     lib = load_library()
     dtype = _check_train(("q", "k", "v", "o", "dout"), (q, k, v, o, dout))
@@ -143,10 +156,25 @@ def attn_bwd(q, k, v, o, dout, lse, dq=None, dk=None, dv=None, delta=None):
     dv = torch.empty_like(v) if dv is None else dv
     delta = torch.empty((B, H, T), dtype=torch.float32, device=q.device) if delta is None else delta
     _check_train(("q", "dq", "dk", "dv"), (q, dq, dk, dv), dtype)
-    fn = "na_attn_bwd" if dtype == torch.bfloat16 else "na_attn_bwd_f32"
-    _check(lib, fn, getattr(lib, fn)(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse),
-                                     _ptr(dq), _ptr(dk), _ptr(dv), _ptr(delta), B, T, H, D,
-                                     _stream(q)))
+    if dtype == torch.bfloat16:
+        ws_bytes = 0
+        if not recompute_dq:
+            ws_bytes = bwd_workspace_bytes(B, T, H, D)
+            if workspace is None:
+                workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+            else:
+                ws_bytes = workspace.numel() * workspace.element_size()
+        else:
+            workspace = None
+        _check(lib, "na_attn_bwd",
+               lib.na_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq),
+                               _ptr(dk), _ptr(dv), _ptr(delta), _ptr(workspace), ws_bytes, B, T,
+                               H, D, _stream(q)))
+    else:
+        _check(lib, "na_attn_bwd_f32",
+               lib.na_attn_bwd_f32(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse),
+                                   _ptr(dq), _ptr(dk), _ptr(dv), _ptr(delta), B, T, H, D,
+                                   _stream(q)))
     return dq, dk, dv, delta
 
 

@@ -101,25 +101,45 @@ na_status na_attn_fwd(const void* q, const void* k, const void* v, void* o, floa
                     "na_attn_fwd");
 }
 
+size_t na_attn_bwd_workspace_bytes(int B, int T, int H, int D) {
+  if (B < 1 || T < 1 || H < 1 || D != na::kHeadDim || T > 1048576) return 0;
+  return na::bwd_workspace_bytes(B, T, H);
+}
+
 na_status na_attn_bwd_timed(const void* q, const void* k, const void* v, const void* o,
                             const void* dout, const float* lse, void* dq, void* dk, void* dv,
-                            float* delta, int B, int T, int H, int D, void* stream,
-                            void* const* events) {
+                            float* delta, void* workspace, size_t workspace_bytes, int B,
+                            int T, int H, int D, void* stream, void* const* events) {
   na_status st = check_sizes(B, T, H, D);
   if (st) return st;
-  st = check_ptrs({{q, "q"}, {k, "k"}, {v, "v"}, {o, "o"}, {dout, "dout"}, {lse, "lse"}},
-                  {{dq, "dq"}, {dk, "dk"}, {dv, "dv"}, {delta, "delta"}});
-  if (st) return st;
-  return hip_status(na::launch_bwd_bf16(q, k, v, o, dout, lse, dq, dk, dv, delta, B, T, H,
-                                        (hipStream_t)stream,
+  if (workspace != nullptr) {
+    st = check_ptrs({{q, "q"}, {k, "k"}, {v, "v"}, {o, "o"}, {dout, "dout"}, {lse, "lse"}},
+                    {{dq, "dq"}, {dk, "dk"}, {dv, "dv"}, {delta, "delta"},
+                     {workspace, "workspace"}});
+    if (st) return st;
+    if (T > 1048576)
+      return fail(NA_ERR_UNSUPPORTED, "the dS workspace path needs T <= 1048576 (T=%d)", T);
+    const size_t need = na::bwd_workspace_bytes(B, T, H);
+    if (workspace_bytes < need)
+      return fail(NA_ERR_INVALID_ARG, "workspace_bytes %zu < required %zu", workspace_bytes,
+                  need);
+  } else {
+    st = check_ptrs({{q, "q"}, {k, "k"}, {v, "v"}, {o, "o"}, {dout, "dout"}, {lse, "lse"}},
+                    {{dq, "dq"}, {dk, "dk"}, {dv, "dv"}, {delta, "delta"}});
+    if (st) return st;
+  }
+  return hip_status(na::launch_bwd_bf16(q, k, v, o, dout, lse, dq, dk, dv, delta, workspace, B,
+                                        T, H, (hipStream_t)stream,
                                         reinterpret_cast<hipEvent_t const*>(events)),
                     "na_attn_bwd");
 }
 
 na_status na_attn_bwd(const void* q, const void* k, const void* v, const void* o,
                       const void* dout, const float* lse, void* dq, void* dk, void* dv,
-                      float* delta, int B, int T, int H, int D, void* stream) {
-  return na_attn_bwd_timed(q, k, v, o, dout, lse, dq, dk, dv, delta, B, T, H, D, stream, nullptr);
+                      float* delta, void* workspace, size_t workspace_bytes, int B, int T,
+                      int H, int D, void* stream) {
+  return na_attn_bwd_timed(q, k, v, o, dout, lse, dq, dk, dv, delta, workspace, workspace_bytes,
+                           B, T, H, D, stream, nullptr);
 }
 
 size_t na_attn_decode_workspace_bytes(int B, int H, int D, int T_cap) {

@@ -147,16 +147,31 @@ __device__ __forceinline__ void dkdv_accum(const bf16x8 (&pb)[2], const bf16x8 (
   }
 }
 
+// dS of one 32-query x 32-key block, kept for the dQ GEMM: stored as a
+// 32 x 32 bf16 matrix [key][query] (row = this lane's key, 8 queries per
+// 16-byte store).  Blocks of a head are packed lower-triangularly: block
+// (qblk, kblk), kblk <= qblk, at index qblk (qblk + 1) / 2 + kblk.
+__device__ __forceinline__ size_t ds_block_index(int bh, int nbt, int qblk, int kblk) {
+  return (static_cast<size_t>(bh) * nbt + qblk * (qblk + 1) / 2 + kblk) * 1024;
+}
+
+__device__ __forceinline__ void store_ds(u16* blk, const bf16x8 (&sb)[2], int lane) {
+  const int l32 = lane & 31, half = lane >> 5;
+  st16(blk + l32 * 32 + 8 * half, __builtin_bit_cast(uint4, sb[0]));
+  st16(blk + l32 * 32 + 16 + 8 * half, __builtin_bit_cast(uint4, sb[1]));
+}
+
 template <bool MASK>
 __device__ __forceinline__ void dkdv_block(const u16* Qs, const u16* Gs, const u16* Qt,
                                            const u16* Gt, const float* lse2s, const float* dls,
                                            const bf16x8 (&kreg)[8], const bf16x8 (&vreg)[8],
                                            f32x16 (&dka)[4], f32x16 (&dva)[4], int qb, int lane,
-                                           int key_minus_q0, float c_log2) {
+                                           int key_minus_q0, float c_log2, u16* ds_blk) {
   f32x16 sacc, pacc;
   dkdv_scores(Qs, Gs, 32 * qb, kreg, vreg, sacc, pacc, lane);
   bf16x8 pb[2], sb[2];
   dkdv_probs<MASK>(sacc, pacc, lse2s, dls, 32 * qb, pb, sb, lane, key_minus_q0, c_log2);
+  if (ds_blk) store_ds(ds_blk, sb, lane);
   dkdv_accum(pb, sb, Qt, Gt, 32 * qb, dka, dva, lane);
 }
 
@@ -173,7 +188,7 @@ __device__ __forceinline__ void dkdv_step(const u16* QsN, const u16* GsN, int ro
                                           const bf16x8 (&vreg)[8], const f32x16& s_cur,
                                           const f32x16& p_cur, f32x16& s_nxt, f32x16& p_nxt,
                                           f32x16 (&dka)[4], f32x16 (&dva)[4], int lane,
-                                          float c_log2) {
+                                          float c_log2, u16* ds_blk) {
   const int half = lane >> 5;
   const int l32 = lane & 31;
   const u16* qp = &QsN[(rowN + perm_row(l32)) * RS + 8 * half];
@@ -222,6 +237,7 @@ __device__ __forceinline__ void dkdv_step(const u16* QsN, const u16* GsN, int ro
                         as_bf16x8(make_uint4(pw[4], pw[5], pw[6], pw[7]))};
   const bf16x8 sb[2] = {as_bf16x8(make_uint4(sw[0], sw[1], sw[2], sw[3])),
                         as_bf16x8(make_uint4(sw[4], sw[5], sw[6], sw[7]))};
+  if (ds_blk) store_ds(ds_blk, sb, lane);
   // dV += P^T dout, dK += dS^T Q for the current block: operands of chunk j+1
   // are read while chunk j's MFMAs run
   bf16x8 bg[2][4], bq[2][4];
@@ -254,8 +270,8 @@ __device__ __forceinline__ void dkdv_step(const u16* QsN, const u16* GsN, int ro
 __global__ __launch_bounds__(256, 1) void dkdv_kernel(
     const u16* __restrict__ q, const u16* __restrict__ k, const u16* __restrict__ v,
     const u16* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
-    u16* __restrict__ dk, u16* __restrict__ dv, int B, int T, int H, float c_log2,
-    float scale) {
+    u16* __restrict__ dk, u16* __restrict__ dv, u16* __restrict__ dsw, int nbt, int B, int T,
+    int H, float c_log2, float scale) {
   // double-buffered query tiles: Q and dout row-major, and transposed (swizzled)
   __shared__ __attribute__((aligned(16))) u16 Qs[2][QT_ROWS * RS];
   __shared__ __attribute__((aligned(16))) u16 Gs[2][QT_ROWS * RS];
@@ -338,6 +354,15 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(
     }
   };
 
+  // dS blocks of this wavefront's 32 keys (when a dS workspace is given).
+  // Only blocks with a query row < T exist in the packed layout; a block made
+  // of padding rows only (the tail of the last tile) is not stored.  Stored
+  // blocks always have kblk <= qblk.
+  const int kblk = kw0 / 32;
+  auto ds_of = [&](int qblk) -> u16* {
+    return (dsw && 32 * qblk < T) ? dsw + ds_block_index(bh, nbt, qblk, kblk) : nullptr;
+  };
+
   // Diagonal part: the first two query tiles hold every (query, key) pair of
   // this workgroup that the causal mask can cut; one barrier per tile.
   const int qt_diag_end = min(qt0 + 2, n_qt);
@@ -356,14 +381,14 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(
       for (int qb = 0; qb < 2; ++qb) {
         if (q0 + 32 * qb + 31 >= kw0)
           dkdv_block<true>(Qs[buf], Gs[buf], Qt[buf], Gt[buf], lse2s[buf], dls[buf], kreg, vreg,
-                           dka, dva, qb, lane, kq, c_log2);
+                           dka, dva, qb, lane, kq, c_log2, ds_of(q0 / 32 + qb));
         __builtin_amdgcn_sched_barrier(0);  // keep the two blocks' live ranges apart
       }
     } else {
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
         dkdv_block<false>(Qs[buf], Gs[buf], Qt[buf], Gt[buf], lse2s[buf], dls[buf], kreg, vreg,
-                          dka, dva, qb, lane, kq, c_log2);
+                          dka, dva, qb, lane, kq, c_log2, ds_of(q0 / 32 + qb));
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -388,14 +413,14 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(
     for (int t = ts; t < n_qt; ++t) {
       // block 2t (rows 0..31 of tile t) while computing scores of rows 32..63
       dkdv_step(Qs[b], Gs[b], 32, lse2s[b], dls[b], Qt[b], Gt[b], 0, kreg, vreg, s0, p0,
-                      s1, p1, dka, dva, lane, c_log2);
+                s1, p1, dka, dva, lane, c_log2, ds_of(2 * t));
       __syncthreads();  // every wavefront is done with tile t-1 (buffer b^1)
       lstore(b ^ 1);
       __syncthreads();
       gload(min(t + 2, n_qt - 1));
       // block 2t+1 (rows 32..63 of tile t) while computing scores of tile t+1 rows 0..31
       dkdv_step(Qs[b ^ 1], Gs[b ^ 1], 0, lse2s[b], dls[b], Qt[b], Gt[b], 32, kreg, vreg,
-                      s1, p1, s0, p0, dka, dva, lane, c_log2);
+                s1, p1, s0, p0, dka, dva, lane, c_log2, ds_of(2 * t + 1));
       b ^= 1;
     }
   }
@@ -655,11 +680,152 @@ __global__ __launch_bounds__(256, 1) void dq_kernel(
   }
 }
 
+// ---------------------------------------------------------------- dQ from stored dS
+
+// With a dS workspace the dK/dV kernel keeps dS (bf16, 32 x 32 blocks), and
+// dQ = s dS K is a plain GEMM over the lower-triangular blocks instead of a
+// pass that recomputes S and dP.  Per wavefront (32 queries) and 32-key block:
+//   dQ^T += K^T dS^T   (A = transposed K tile from LDS, B = dS^T)
+// The B operand needs lane = query, eight consecutive keys, while the stored
+// block is [key][query]; each wavefront stages its block in LDS and reads it
+// with ds_read_b64_tr_b16, which within each 16-lane group gives lane j
+// element j&3 of the four-element rows supplied by lanes 4e + (j>>2): lanes
+// supplying rows key0 + i/4 at columns 4 (i%4) leave lane j with the column
+// query0 + j of keys key0 .. key0 + 3.
+constexpr int DG_ROWS = 128;  // queries per workgroup (32 per wavefront)
+constexpr int DG_KEYS = 64;   // keys per K tile
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+__device__ __forceinline__ uint2 ds_read_tr16(const u16* lds) {
+  const lds_i16x4* p =
+      (const lds_i16x4*)((__attribute__((address_space(3))) const u16*)lds);  // NOLINT
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p));
+}
+
+__global__ __launch_bounds__(256, 2) void dq_gemm_kernel(const u16* __restrict__ k,
+                                                         const u16* __restrict__ dsw,
+                                                         u16* __restrict__ dq, int nbt, int B,
+                                                         int T, int H, float scale) {
+  __shared__ __attribute__((aligned(16))) u16 Kt[2][D * DG_KEYS];  // transposed, swizzled
+  __shared__ __attribute__((aligned(16))) u16 Sst[4][2][32 * 32];  // per-wavefront dS staging
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int half = lane >> 5;
+  const int l32 = lane & 31;
+  const int gi = lane >> 4;   // 16-lane group
+  const int i16 = lane & 15;
+
+  const int BH = B * H;
+  const int n_qt = (T + DG_ROWS - 1) / DG_ROWS;
+  int bh, t;
+  xcd_tile_map(static_cast<int>(blockIdx.x), BH, n_qt, bh, t);
+  const int qt = n_qt - 1 - t;  // heaviest (last) query tile first
+  const int b = bh / H, h = bh % H;
+  const int q0 = qt * DG_ROWS;
+  const int qw0 = q0 + 32 * wave;
+  const int qblk = qw0 / 32;
+  const bool live = qw0 < T;  // wavefront has at least one real query row
+  const int rs = H * D;
+  const size_t base = static_cast<size_t>(b) * T * rs + static_cast<size_t>(h) * D;
+  const u16* dsh = dsw + ds_block_index(bh, nbt, 0, 0);
+
+  f32x16 dqa[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) dqa[i] = f32x16{};
+
+  const int last_q = min(q0 + DG_ROWS, T) - 1;
+  const int n_kt = last_q / DG_KEYS + 1;
+  const int lrow = tid >> 4;
+  const int lchunk = tid & 15;
+  uint4 xk[4];
+  auto kload = [&](int kt) {  // key rows past T read row T-1: their dS is 0
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      xk[i] = ld16(k + base + min(kt * DG_KEYS + 4 * lrow + i, T - 1) * rs + 8 * lchunk);
+  };
+  // this wavefront's two dS blocks of key tile kt (32 bytes per lane each)
+  uint4 xs[2][2];
+  auto sload = [&](int kt) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int kblk = 2 * kt + kb;
+      if (live && kblk <= qblk) {
+        const u16* p = dsh + (static_cast<size_t>(qblk) * (qblk + 1) / 2 + kblk) * 1024 + 16 * lane;
+        xs[kb][0] = ld16(p);
+        xs[kb][1] = ld16(p + 8);
+      }
+    }
+  };
+
+  kload(0);
+  sload(0);
+  for (int kt = 0; kt < n_kt; ++kt) {
+    const int buf = kt & 1;
+    tstore_4x8(Kt[buf], xk, lrow, lchunk);
+    __syncthreads();  // publishes `buf`; frees buf^1 (see the forward kernel)
+    uint4 cur[2][2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      cur[kb][0] = xs[kb][0];
+      cur[kb][1] = xs[kb][1];
+    }
+    if (kt + 1 < n_kt) {
+      kload(kt + 1);
+      sload(kt + 1);
+    }
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int kblk = 2 * kt + kb;
+      if (!live || kblk > qblk) continue;  // wavefront-uniform
+      u16* st = Sst[wave][kb];
+      st16(st + 16 * lane, cur[kb][0]);
+      st16(st + 16 * lane + 8, cur[kb][1]);
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        // keys 16 c + 8 half + 4 r + 0..3 of column (query) l32
+        const int row = 16 * c + 8 * half + (i16 >> 2);
+        const int col = 16 * (gi & 1) + 4 * (i16 & 3);
+        const uint2 r0 = ds_read_tr16(st + row * 32 + col);
+        const uint2 r1 = ds_read_tr16(st + (row + 4) * 32 + col);
+        const bf16x8 bs = as_bf16x8(make_uint4(r0.x, r0.y, r1.x, r1.y));
+        bf16x8 a[4];
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+          a[db] = as_bf16x8(ld16(&Kt[buf][toff(db * 32 + l32, 4 * kb + 2 * c + half)]));
+#pragma unroll
+        for (int db = 0; db < 4; ++db) dqa[db] = mfma32(a[db], bs, dqa[db]);
+      }
+    }
+  }
+
+  const int qrow = qw0 + l32;
+  if (qrow < T) {
+    u16* qp = dq + base + qrow * rs;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        uint2 pk = make_uint2(pack_bf16x2(dqa[db][4 * g] * scale, dqa[db][4 * g + 1] * scale),
+                              pack_bf16x2(dqa[db][4 * g + 2] * scale, dqa[db][4 * g + 3] * scale));
+        *reinterpret_cast<uint2*>(qp + 32 * db + 8 * g + 4 * half) = pk;
+      }
+  }
+}
+
 }  // namespace
+
+std::size_t bwd_workspace_bytes(int B, int T, int H) {
+  const std::size_t nblk = (static_cast<std::size_t>(T) + 31) / 32;
+  return static_cast<std::size_t>(B) * H * (nblk * (nblk + 1) / 2) * 1024 * sizeof(u16);
+}
 
 hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const void* o,
                            const void* dout, const float* lse, void* dq, void* dk, void* dv,
-                           float* delta, int B, int T, int H, hipStream_t s,
+                           float* delta, void* ws, int B, int T, int H, hipStream_t s,
                            hipEvent_t const* ev) {
   const float scale = 1.0f / sqrtf(static_cast<float>(D));
   const float c_log2 = scale * kLog2e;
@@ -667,23 +833,32 @@ hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const vo
   const u16* k16 = static_cast<const u16*>(k);
   const u16* v16 = static_cast<const u16*>(v);
   const u16* g16 = static_cast<const u16*>(dout);
+  u16* dsw = static_cast<u16*>(ws);
+  const int nblk = (T + 31) / 32;
+  const int nbt = nblk * (nblk + 1) / 2;
   const long rows = static_cast<long>(B) * T * H;
   hipError_t e = mark(ev, 0, s);
   if (e != hipSuccess) return e;
-  e = launch(delta_kernel, dim3(static_cast<unsigned>((rows + 15) / 16)), dim3(256), 0,
-                        s, static_cast<const u16*>(o), g16, delta, B, T, H);
+  e = launch(delta_kernel, dim3(static_cast<unsigned>((rows + 15) / 16)), dim3(256), 0, s,
+             static_cast<const u16*>(o), g16, delta, B, T, H);
   if (e != hipSuccess) return e;
   if ((e = mark(ev, 1, s)) != hipSuccess) return e;
   const int n_kt = (T + KT_KEYS - 1) / KT_KEYS;
   e = launch(dkdv_kernel, dim3(static_cast<unsigned>(n_kt) * B * H), dim3(256), 0, s, q16, k16,
              v16, g16, lse, static_cast<const float*>(delta), static_cast<u16*>(dk),
-             static_cast<u16*>(dv), B, T, H, c_log2, scale);
+             static_cast<u16*>(dv), dsw, nbt, B, T, H, c_log2, scale);
   if (e != hipSuccess) return e;
   if ((e = mark(ev, 2, s)) != hipSuccess) return e;
-  const int n_qt = (T + DQ_ROWS - 1) / DQ_ROWS;
-  e = launch(dq_kernel, dim3(static_cast<unsigned>(n_qt) * B * H), dim3(256), 0, s, q16, k16, v16,
-             g16, lse, static_cast<const float*>(delta), static_cast<u16*>(dq), B, T, H, c_log2,
-             scale);
+  if (dsw != nullptr) {
+    const int n_qt = (T + DG_ROWS - 1) / DG_ROWS;
+    e = launch(dq_gemm_kernel, dim3(static_cast<unsigned>(n_qt) * B * H), dim3(256), 0, s, k16,
+               static_cast<const u16*>(dsw), static_cast<u16*>(dq), nbt, B, T, H, scale);
+  } else {
+    const int n_qt = (T + DQ_ROWS - 1) / DQ_ROWS;
+    e = launch(dq_kernel, dim3(static_cast<unsigned>(n_qt) * B * H), dim3(256), 0, s, q16, k16,
+               v16, g16, lse, static_cast<const float*>(delta), static_cast<u16*>(dq), B, T, H,
+               c_log2, scale);
+  }
   if (e != hipSuccess) return e;
   return mark(ev, 3, s);
 }

@@ -19,10 +19,13 @@ hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o,
                            int B, int T, int H, hipStream_t s);
 
 // bf16 backward: delta, then dk/dv, then dq.
+// ws: optional dS workspace of bwd_workspace_bytes(B, T, H) bytes; with it dQ
+// is a GEMM over the stored dS, without it the dQ pass recomputes S and dP.
 hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const void* o,
                            const void* dout, const float* lse, void* dq, void* dk, void* dv,
-                           float* delta, int B, int T, int H, hipStream_t s,
+                           float* delta, void* ws, int B, int T, int H, hipStream_t s,
                            hipEvent_t const* ev = nullptr);
+std::size_t bwd_workspace_bytes(int B, int T, int H);
 
 // Decode workspace layout and size (bytes).
 std::size_t decode_workspace_bytes(int B, int H, int T_cap);

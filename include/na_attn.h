@@ -70,12 +70,23 @@ na_status na_attn_fwd(const void* q, const void* k, const void* v, void* o, floa
  *   dv = P^T dout,  dq = s dS k,  dk = s dS^T q.
  * q, k, v, o, dout: bf16 (B, T, H, D) inputs; o and lse are the forward's
  * outputs.  dq, dk, dv: bf16 (B, T, H, D) outputs.  delta: fp32 (B, H, T)
- * caller-provided scratch, holds delta on return.  Enqueues three kernels:
- * delta, then dk/dv (one workgroup per key tile), then dq (one per query tile).
+ * caller-provided scratch, holds delta on return.
+ * workspace: optional device scratch for dS, at least
+ * na_attn_bwd_workspace_bytes(B, T, H, D) bytes (NA_ERR_INVALID_ARG if
+ * smaller).  With it, the dk/dv kernel stores dS (bf16) once and dq is a GEMM
+ * over it; with workspace == NULL (workspace_bytes ignored) the dq pass
+ * recomputes S and dP instead.  Both give the same result up to rounding.
+ * Enqueues three kernels: delta, dk/dv (one workgroup per key tile), dq (one
+ * per query tile).  The workspace path needs T <= 1048576.
  */
 na_status na_attn_bwd(const void* q, const void* k, const void* v, const void* o,
                       const void* dout, const float* lse, void* dq, void* dk, void* dv,
-                      float* delta, int B, int T, int H, int D, void* stream);
+                      float* delta, void* workspace, size_t workspace_bytes, int B, int T,
+                      int H, int D, void* stream);
+
+/* Bytes of dS workspace for na_attn_bwd (0 if the sizes are invalid): B*H
+ * lower-triangular sets of 32 x 32 bf16 blocks, about B*H*T*T bytes. */
+size_t na_attn_bwd_workspace_bytes(int B, int T, int H, int D);
 
 /*
  * Decode: one new query per sequence against a padded KV cache.
@@ -117,8 +128,8 @@ na_status na_attn_bwd_f32(const float* q, const float* k, const float* v, const 
  */
 na_status na_attn_bwd_timed(const void* q, const void* k, const void* v, const void* o,
                             const void* dout, const float* lse, void* dq, void* dk, void* dv,
-                            float* delta, int B, int T, int H, int D, void* stream,
-                            void* const* events);
+                            float* delta, void* workspace, size_t workspace_bytes, int B,
+                            int T, int H, int D, void* stream, void* const* events);
 na_status na_attn_decode_timed(const void* q, const void* k_cache, const void* v_cache,
                                const int* seqlens, void* o, float* lse, int B, int H, int D,
                                int T_cap, void* workspace, size_t workspace_bytes, void* stream,

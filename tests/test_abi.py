@@ -32,6 +32,7 @@ def lib():
 def test_header_declares_the_entry_points():
     syms = declared_symbols()
     for s in ("na_attn_fwd", "na_attn_bwd", "na_attn_decode", "na_attn_decode_workspace_bytes",
+              "na_attn_bwd_workspace_bytes", "na_attn_bwd_timed", "na_attn_decode_timed",
               "na_attn_fwd_f32", "na_attn_bwd_f32", "na_status_string", "na_last_error"):
         assert s in syms
 
@@ -76,18 +77,37 @@ def test_fwd_rejects_bad_arguments(lib):
 
 
 def test_bwd_rejects_bad_arguments(lib):
-    p = [A + 0x100 * i for i in range(10)]
+    p = [A + 0x100 * i for i in range(11)]   # q k v o dout lse dq dk dv delta workspace
+    need = lib.na_attn_bwd_workspace_bytes(1, 8, 1, 128)
+
+    def bwd(ptrs, ws_bytes=need, D=128, T=8):
+        return lib.na_attn_bwd(*ptrs[:10], ptrs[10], ws_bytes, 1, T, 1, D, None)
+
     bad = list(p)
     bad[3] = 0                     # o
-    assert lib.na_attn_bwd(*bad[:5], bad[5], *bad[6:9], bad[9], 1, 8, 1, 128, None) == INVALID
+    assert bwd(bad) == INVALID
     bad = list(p)
     bad[7] = bad[6]                # dk == dq
-    assert lib.na_attn_bwd(*bad[:5], bad[5], *bad[6:9], bad[9], 1, 8, 1, 128, None) == INVALID
-    assert b"alias" in lib.na_last_error()
-    assert lib.na_attn_bwd(*p[:5], p[5], *p[6:9], p[9], 1, 8, 1, 96, None) == UNSUPPORTED
+    assert bwd(bad) == INVALID and b"alias" in lib.na_last_error()
     bad = list(p)
+    bad[10] = bad[0]               # workspace == q
+    assert bwd(bad) == INVALID
+    assert bwd(p, ws_bytes=need - 1) == INVALID and b"workspace" in lib.na_last_error()
+    assert bwd(p, D=96) == UNSUPPORTED
+    bad = list(p)
+    bad[10] = 0                    # no workspace: recompute path, still checks the rest
     bad[9] = 0                     # delta scratch
+    assert bwd(bad) == INVALID
     assert lib.na_attn_bwd_f32(*bad[:5], bad[5], *bad[6:9], bad[9], 1, 8, 1, 128, None) == INVALID
+
+
+def test_bwd_workspace_bytes(lib):
+    # lower-triangular 32 x 32 bf16 blocks per (b, h)
+    for B, T, H in ((1, 1, 1), (2, 33, 3), (32, 2048, 10)):
+        nblk = (T + 31) // 32
+        assert lib.na_attn_bwd_workspace_bytes(B, T, H, 128) == B * H * nblk * (nblk + 1) // 2 * 2048
+    assert lib.na_attn_bwd_workspace_bytes(1, 8, 1, 64) == 0
+    assert lib.na_attn_bwd_workspace_bytes(0, 8, 1, 128) == 0
 
 
 def test_decode_workspace_and_checks(lib):

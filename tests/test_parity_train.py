@@ -24,13 +24,13 @@ def _na():
     return na
 
 
-def gpu_fwd_bwd(inp, dev):
+def gpu_fwd_bwd(inp, dev, recompute_dq=False):
     import torch
     na = _na()
     q, k, v, do = (to_device(x, dev) for x in (inp.q_store, inp.k_store, inp.v_store,
                                                inp.do_store))
     o, lse = na.attn_fwd(q, k, v)
-    dq, dk, dv, delta = na.attn_bwd(q, k, v, o, do, lse)
+    dq, dk, dv, delta = na.attn_bwd(q, k, v, o, do, lse, recompute_dq=recompute_dq)
     torch.cuda.synchronize()
     return dict(q=q, k=k, v=v, do=do, o=o, lse=lse, dq=dq, dk=dk, dv=dv, delta=delta)
 
@@ -60,13 +60,31 @@ def test_f32_ragged(dev, B, T, H):
 # ------------------------------------------------------------------ bf16, small
 
 SMALL = [(1, 1, 1), (1, 17, 2), (1, 64, 1), (1, 100, 2), (1, 128, 1), (2, 255, 1),
-         (1, 257, 3), (3, 300, 1), (1, 640, 2), (1, 1000, 1), (1, 2048, 1)]
+         (1, 257, 3), (1, 280, 2), (3, 300, 1), (1, 640, 2), (1, 1000, 1), (1, 2048, 1)]
 
 
 @pytest.mark.parametrize("B,T,H", SMALL)
 def test_bf16_shapes(dev, B, T, H):
     inp = W.make_train_inputs("d20", B=B, T=T, H=H, seed=2000 + 7 * T + H)
     compare_all(inp, gpu_fwd_bwd(inp, dev), BF16_REL_L2, BF16_MAX_ABS)
+
+
+@pytest.mark.parametrize("B,T,H", [(1, 1, 1), (1, 100, 2), (2, 257, 1), (1, 280, 2), (1, 1000, 1)])
+def test_bf16_recompute_dq_path(dev, B, T, H):
+    """The backward without a dS workspace (dq pass recomputes S and dP)."""
+    inp = W.make_train_inputs("d20", B=B, T=T, H=H, seed=3000 + 7 * T + H)
+    compare_all(inp, gpu_fwd_bwd(inp, dev, recompute_dq=True), BF16_REL_L2, BF16_MAX_ABS)
+
+
+def test_dq_paths_agree(dev):
+    """Stored-dS GEMM and recompute give the same dq up to bf16 rounding of dS."""
+    import torch
+    inp = W.make_train_inputs("d20", B=1, T=700, H=2, seed=9)
+    a = gpu_fwd_bwd(inp, dev)
+    b = gpu_fwd_bwd(inp, dev, recompute_dq=True)
+    for n in ("dk", "dv", "delta"):
+        assert torch.equal(a[n], b[n]), n
+    assert_close("dq paths", to_host(a["dq"]), to_host(b["dq"]), 2e-3, 2e-3)
 
 
 def test_bf16_unit_scale_inputs(dev):
@@ -119,11 +137,12 @@ def _sampled_heads(B, H):
     return sorted(pairs)
 
 
-@pytest.mark.parametrize("name", ["d12", "d20", "d26"])
-def test_full_config_sampled_heads(dev, name):
+@pytest.mark.parametrize("name,recompute", [("d12", False), ("d20", False), ("d26", False),
+                                             ("d20", True)])
+def test_full_config_sampled_heads(dev, name, recompute):
     import torch
     inp = W.make_train_inputs(name)
-    res = gpu_fwd_bwd(inp, dev)
+    res = gpu_fwd_bwd(inp, dev, recompute_dq=recompute)
     for n in ("o", "dq", "dk", "dv"):
         assert bool(torch.isfinite(res[n].float()).all()), n
     assert bool(torch.isfinite(res["lse"]).all())
