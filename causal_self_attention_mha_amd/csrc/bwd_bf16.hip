@@ -63,33 +63,79 @@ __global__ __launch_bounds__(256) void delta_kernel(const u16* __restrict__ o,
 
 constexpr int KT_KEYS = 128;  // keys per workgroup (32 per wavefront)
 constexpr int QT_ROWS = 64;   // queries per LDS tile
-constexpr int RS = D + 8;     // row-major tile stride (bf16 elements)
+constexpr int NBUF = 3;       // query tiles resident in LDS at once
+constexpr uint32_t TILE_B = QT_ROWS * D * 2;  // bytes of one 64 x 128 bf16 tile
+constexpr uint32_t BUF_B = 2 * TILE_B;        // one buffer: q tile, then dout tile
+
+// Query tiles are copied straight from HBM into LDS (no register staging, no
+// transposed copy).  A tile is 64 unpadded rows of 256 bytes; the 16-byte
+// chunk c of row r sits at chunk c ^ qswz(r).  qswz is a bijection of r mod 16,
+// so the row reads of an MFMA A operand (16 lanes: one chunk of 16 different
+// rows) touch 16 different chunks; and its top two bits differ between any
+// four consecutive rows, so the transposing reads of a B operand (32 lanes:
+// 64 bytes of 4 consecutive rows) touch 16 different chunks too.  With
+// gfx950's 64 four-byte LDS banks both are free of bank conflicts.
+__device__ __forceinline__ uint32_t qswz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+
+// Per-lane byte offsets, within a query tile, of this lane's operand reads.
+struct QOperandOffsets {
+  uint32_t nat[8];    // A operand: row perm_row(l32), elements 16 kc + 8 half .. + 7
+  uint32_t tr[4][2];  // B operand, d block db: transposing read of rows 4 sub .. 4 sub + 3
+};
+
+__device__ __forceinline__ QOperandOffsets q_operand_offsets(int lane) {
+  QOperandOffsets o;
+  const int half = lane >> 5;
+  const int pr = perm_row(lane & 31);
+#pragma unroll
+  for (int kc = 0; kc < 8; ++kc) o.nat[kc] = pr * 256 + 16 * ((2 * kc + half) ^ qswz(pr));
+  // Lane i of 16-lane group g supplies row 8 (g / 2) + 4 sub + i / 4 and the
+  // columns 32 db + 16 (g % 2) + 4 (i % 4) .. + 3; it then holds column
+  // 32 db + lane % 32 of rows 8 (lane / 32) + 4 sub + 0..3, i.e. half of the
+  // 8 query rows its B operand needs (the other half comes from sub ^ 1).
+  const int g = lane >> 4, i = lane & 15;
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      const int r = 8 * (g >> 1) + 4 * sub + (i >> 2);
+      const int col = 32 * db + 16 * (g & 1) + 4 * (i & 3);
+      o.tr[db][sub] = r * 256 + 16 * ((col >> 3) ^ qswz(r)) + 2 * (col & 7);
+    }
+  return o;
+}
+
+// B operand (8 consecutive query rows of one d column per lane) from a query
+// tile: rows base/256 + 8 (lane / 32) + 0..7 of d block db.
+__device__ __forceinline__ bf16x8 tr_operand(uint32_t base, const uint32_t (&t)[2]) {
+  const uint2 lo = ds_read_tr16_at(base + t[0]);
+  const uint2 hi = ds_read_tr16_at(base + t[1]);
+  return as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+}
 
 // One 32-query block of a dK/dV step for one wavefront (32 keys), in three
 // phases:
 //   scores:  S = Q K^T, dP = dout V^T   (A = Q / dout rows from LDS, B = K / V
 //            in registers; lane: key, element r: query acc_row(lane, r))
-//   probs:   P = exp2(c S - lse2), dS = P (dP - delta), rounded to bf16
+//   probs:   P = exp2(c S - lse log2 e), dS = P (dP - delta), rounded to bf16
 //   accum:   dV += P^T dout, dK += dS^T Q  (A = P^T / dS^T from registers,
-//            B = transposed query tiles)
+//            B = query tiles read transposed)
 // The steady-state loop overlaps the scores MFMAs of block j+1 with the probs
-// VALU work of block j.
-__device__ __forceinline__ void dkdv_scores(const u16* Qs, const u16* Gs, int row0,
+// VALU work of block j.  qtile is the LDS byte address of a buffer's q tile
+// (its dout tile follows at + TILE_B).
+__device__ __forceinline__ void dkdv_scores(uint32_t qtile, int row0, const QOperandOffsets& ofs,
                                             const bf16x8 (&kreg)[8], const bf16x8 (&vreg)[8],
-                                            f32x16& sacc, f32x16& pacc, int lane) {
-  const int half = lane >> 5;
-  const int l32 = lane & 31;
+                                            f32x16& sacc, f32x16& pacc) {
   sacc = f32x16{};
   pacc = f32x16{};
-  const u16* qp = &Qs[(row0 + perm_row(l32)) * RS + 8 * half];
-  const u16* gp = &Gs[(row0 + perm_row(l32)) * RS + 8 * half];
+  const uint32_t a0 = qtile + row0 * 256;
 #pragma unroll
   for (int k4 = 0; k4 < 8; k4 += 4) {
     bf16x8 aq[4], ag[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      aq[i] = as_bf16x8(ld16(qp + 16 * (k4 + i)));
-      ag[i] = as_bf16x8(ld16(gp + 16 * (k4 + i)));
+      aq[i] = as_bf16x8(lds_ld16(a0 + ofs.nat[k4 + i]));
+      ag[i] = as_bf16x8(lds_ld16(a0 + TILE_B + ofs.nat[k4 + i]));
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -101,22 +147,22 @@ __device__ __forceinline__ void dkdv_scores(const u16* Qs, const u16* Gs, int ro
 
 template <bool MASK>
 __device__ __forceinline__ void dkdv_probs(const f32x16& sacc, const f32x16& pacc,
-                                           const float* lse2s, const float* dls, int row0,
+                                           const float* lse_t, const float* dl_t, int row0,
                                            bf16x8 (&pb)[2], bf16x8 (&sb)[2], int lane,
                                            int key_minus_q0, float c_log2) {
   const int r0 = row0 + 8 * (lane >> 5);  // element r: query row r0 + 16 (r/8) + r%8
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    const float4 la = *reinterpret_cast<const float4*>(&lse2s[r0 + 16 * j]);
-    const float4 lb = *reinterpret_cast<const float4*>(&lse2s[r0 + 16 * j + 4]);
-    const float4 da = *reinterpret_cast<const float4*>(&dls[r0 + 16 * j]);
-    const float4 db = *reinterpret_cast<const float4*>(&dls[r0 + 16 * j + 4]);
+    const float4 la = *reinterpret_cast<const float4*>(&lse_t[r0 + 16 * j]);
+    const float4 lb = *reinterpret_cast<const float4*>(&lse_t[r0 + 16 * j + 4]);
+    const float4 da = *reinterpret_cast<const float4*>(&dl_t[r0 + 16 * j]);
+    const float4 db = *reinterpret_cast<const float4*>(&dl_t[r0 + 16 * j + 4]);
     const float l8[8] = {la.x, la.y, la.z, la.w, lb.x, lb.y, lb.z, lb.w};
     const float d8[8] = {da.x, da.y, da.z, da.w, db.x, db.y, db.z, db.w};
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int r = 8 * j + i;
-      float p = fast_exp2(fmaf(sacc[r], c_log2, -l8[i]));
+      float p = fast_exp2(fmaf(sacc[r], c_log2, l8[i] * -kLog2e));
       if (MASK && key_minus_q0 > r0 + 16 * j + i) p = 0.f;  // key after query
       pb[j][i] = to_bf16(p);
       sb[j][i] = to_bf16(p * (pacc[r] - d8[i]));
@@ -125,19 +171,16 @@ __device__ __forceinline__ void dkdv_probs(const f32x16& sacc, const f32x16& pac
 }
 
 __device__ __forceinline__ void dkdv_accum(const bf16x8 (&pb)[2], const bf16x8 (&sb)[2],
-                                           const u16* Qt, const u16* Gt, int row0,
-                                           f32x16 (&dka)[4], f32x16 (&dva)[4], int lane) {
-  const int half = lane >> 5;
-  const int l32 = lane & 31;
+                                           uint32_t qtile, int row0, const QOperandOffsets& ofs,
+                                           f32x16 (&dka)[4], f32x16 (&dva)[4]) {
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    const int cg = row0 / 8 + 2 * j + half;  // queries row0 + 16 j + 8 half + 0..7
+    const uint32_t base = qtile + (row0 + 16 * j) * 256;  // queries row0 + 16 j + 8 half + 0..7
     bf16x8 bg[4], bq[4];
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
-      const int t = toff(db * 32 + l32, cg);
-      bg[db] = as_bf16x8(ld16(&Gt[t]));
-      bq[db] = as_bf16x8(ld16(&Qt[t]));
+      bg[db] = tr_operand(base + TILE_B, ofs.tr[db]);
+      bq[db] = tr_operand(base, ofs.tr[db]);
     }
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
@@ -162,17 +205,17 @@ __device__ __forceinline__ void store_ds(u16* blk, const bf16x8 (&sb)[2], int la
 }
 
 template <bool MASK>
-__device__ __forceinline__ void dkdv_block(const u16* Qs, const u16* Gs, const u16* Qt,
-                                           const u16* Gt, const float* lse2s, const float* dls,
-                                           const bf16x8 (&kreg)[8], const bf16x8 (&vreg)[8],
-                                           f32x16 (&dka)[4], f32x16 (&dva)[4], int qb, int lane,
-                                           int key_minus_q0, float c_log2, u16* ds_blk) {
+__device__ __forceinline__ void dkdv_block(uint32_t qtile, const float* lse_t, const float* dl_t,
+                                           const QOperandOffsets& ofs, const bf16x8 (&kreg)[8],
+                                           const bf16x8 (&vreg)[8], f32x16 (&dka)[4],
+                                           f32x16 (&dva)[4], int qb, int lane, int key_minus_q0,
+                                           float c_log2, u16* ds_blk) {
   f32x16 sacc, pacc;
-  dkdv_scores(Qs, Gs, 32 * qb, kreg, vreg, sacc, pacc, lane);
+  dkdv_scores(qtile, 32 * qb, ofs, kreg, vreg, sacc, pacc);
   bf16x8 pb[2], sb[2];
-  dkdv_probs<MASK>(sacc, pacc, lse2s, dls, 32 * qb, pb, sb, lane, key_minus_q0, c_log2);
+  dkdv_probs<MASK>(sacc, pacc, lse_t, dl_t, 32 * qb, pb, sb, lane, key_minus_q0, c_log2);
   if (ds_blk) store_ds(ds_blk, sb, lane);
-  dkdv_accum(pb, sb, Qt, Gt, 32 * qb, dka, dva, lane);
+  dkdv_accum(pb, sb, qtile, 32 * qb, ofs, dka, dva);
 }
 
 // Steady-state step: probabilities of the current block (held in s_cur,
@@ -181,18 +224,17 @@ __device__ __forceinline__ void dkdv_block(const u16* Qs, const u16* Gs, const u
 // separated by scheduling fences: each round issues the LDS reads two rounds
 // ahead, one score MFMA for S and one for dP, and the probability math of two
 // of this lane's sixteen (key, query) elements, so the VALU work runs while
-// the matrix cores are busy.
-__device__ __forceinline__ void dkdv_step(const u16* QsN, const u16* GsN, int rowN,
-                                          const float* lse2s, const float* dls, const u16* Qt,
-                                          const u16* Gt, int rowC, const bf16x8 (&kreg)[8],
+// the matrix cores are busy.  ntile/rowN locate the next block, ctile/rowC
+// the current one.
+__device__ __forceinline__ void dkdv_step(uint32_t ntile, int rowN, const float* lse_t,
+                                          const float* dl_t, uint32_t ctile, int rowC,
+                                          const QOperandOffsets& ofs, const bf16x8 (&kreg)[8],
                                           const bf16x8 (&vreg)[8], const f32x16& s_cur,
                                           const f32x16& p_cur, f32x16& s_nxt, f32x16& p_nxt,
                                           f32x16 (&dka)[4], f32x16 (&dva)[4], int lane,
                                           float c_log2, u16* ds_blk) {
   const int half = lane >> 5;
-  const int l32 = lane & 31;
-  const u16* qp = &QsN[(rowN + perm_row(l32)) * RS + 8 * half];
-  const u16* gp = &GsN[(rowN + perm_row(l32)) * RS + 8 * half];
+  const uint32_t an = ntile + rowN * 256;
   // element r of the current block: query row r0 + 16 (r/8) + r%8
   const int r0 = rowC + 8 * half;
   float l16[16], d16[16];
@@ -200,18 +242,18 @@ __device__ __forceinline__ void dkdv_step(const u16* QsN, const u16* GsN, int ro
   for (int j = 0; j < 2; ++j)
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
-      const float4 a = *reinterpret_cast<const float4*>(&lse2s[r0 + 16 * j + 4 * k]);
-      const float4 d = *reinterpret_cast<const float4*>(&dls[r0 + 16 * j + 4 * k]);
+      const float4 a = *reinterpret_cast<const float4*>(&lse_t[r0 + 16 * j + 4 * k]);
+      const float4 d = *reinterpret_cast<const float4*>(&dl_t[r0 + 16 * j + 4 * k]);
       l16[8 * j + 4 * k] = a.x; l16[8 * j + 4 * k + 1] = a.y;
       l16[8 * j + 4 * k + 2] = a.z; l16[8 * j + 4 * k + 3] = a.w;
       d16[8 * j + 4 * k] = d.x; d16[8 * j + 4 * k + 1] = d.y;
       d16[8 * j + 4 * k + 2] = d.z; d16[8 * j + 4 * k + 3] = d.w;
     }
   bf16x8 aq[8], ag[8];
-  aq[0] = as_bf16x8(ld16(qp));
-  ag[0] = as_bf16x8(ld16(gp));
-  aq[1] = as_bf16x8(ld16(qp + 16));
-  ag[1] = as_bf16x8(ld16(gp + 16));
+  aq[0] = as_bf16x8(lds_ld16(an + ofs.nat[0]));
+  ag[0] = as_bf16x8(lds_ld16(an + TILE_B + ofs.nat[0]));
+  aq[1] = as_bf16x8(lds_ld16(an + ofs.nat[1]));
+  ag[1] = as_bf16x8(lds_ld16(an + TILE_B + ofs.nat[1]));
   s_nxt = f32x16{};
   p_nxt = f32x16{};
   uint32_t pw[8], sw[8];  // bf16 pairs (elements 2i, 2i+1)
@@ -219,13 +261,13 @@ __device__ __forceinline__ void dkdv_step(const u16* QsN, const u16* GsN, int ro
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     if (i + 2 < 8) {
-      aq[i + 2] = as_bf16x8(ld16(qp + 16 * (i + 2)));
-      ag[i + 2] = as_bf16x8(ld16(gp + 16 * (i + 2)));
+      aq[i + 2] = as_bf16x8(lds_ld16(an + ofs.nat[i + 2]));
+      ag[i + 2] = as_bf16x8(lds_ld16(an + TILE_B + ofs.nat[i + 2]));
     }
     s_nxt = mfma32(aq[i], kreg[i], s_nxt);
     const int r = 2 * i;
-    const float p0 = fast_exp2(fmaf(s_cur[r], c_log2, -l16[r]));
-    const float p1 = fast_exp2(fmaf(s_cur[r + 1], c_log2, -l16[r + 1]));
+    const float p0 = fast_exp2(fmaf(s_cur[r], c_log2, l16[r] * -kLog2e));
+    const float p1 = fast_exp2(fmaf(s_cur[r + 1], c_log2, l16[r + 1] * -kLog2e));
     pw[i] = pack_bf16x2(p0, p1);
     sw[i] = pack_bf16x2(p0 * (p_cur[r] - d16[r]), p1 * (p_cur[r + 1] - d16[r + 1]));
     // keep this round's VALU work in this round (no sinking to the first use)
@@ -241,11 +283,11 @@ __device__ __forceinline__ void dkdv_step(const u16* QsN, const u16* GsN, int ro
   // dV += P^T dout, dK += dS^T Q for the current block: operands of chunk j+1
   // are read while chunk j's MFMAs run
   bf16x8 bg[2][4], bq[2][4];
+  const uint32_t c0 = ctile + rowC * 256;
 #pragma unroll
   for (int db = 0; db < 4; ++db) {
-    const int t = toff(db * 32 + l32, rowC / 8 + half);
-    bg[0][db] = as_bf16x8(ld16(&Gt[t]));
-    bq[0][db] = as_bf16x8(ld16(&Qt[t]));
+    bg[0][db] = tr_operand(c0 + TILE_B, ofs.tr[db]);
+    bq[0][db] = tr_operand(c0, ofs.tr[db]);
   }
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -253,9 +295,8 @@ __device__ __forceinline__ void dkdv_step(const u16* QsN, const u16* GsN, int ro
     if (j == 0) {
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
-        const int t = toff(db * 32 + l32, rowC / 8 + 2 + half);
-        bg[1][db] = as_bf16x8(ld16(&Gt[t]));
-        bq[1][db] = as_bf16x8(ld16(&Qt[t]));
+        bg[1][db] = tr_operand(c0 + 16 * 256 + TILE_B, ofs.tr[db]);
+        bq[1][db] = tr_operand(c0 + 16 * 256, ofs.tr[db]);
       }
     }
 #pragma unroll
@@ -272,13 +313,9 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(
     const u16* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
     u16* __restrict__ dk, u16* __restrict__ dv, u16* __restrict__ dsw, int nbt, int B, int T,
     int H, float c_log2, float scale) {
-  // double-buffered query tiles: Q and dout row-major, and transposed (swizzled)
-  __shared__ __attribute__((aligned(16))) u16 Qs[2][QT_ROWS * RS];
-  __shared__ __attribute__((aligned(16))) u16 Gs[2][QT_ROWS * RS];
-  __shared__ __attribute__((aligned(16))) u16 Qt[2][D * QT_ROWS];
-  __shared__ __attribute__((aligned(16))) u16 Gt[2][D * QT_ROWS];
-  __shared__ __attribute__((aligned(16))) float lse2s[2][QT_ROWS];
-  __shared__ __attribute__((aligned(16))) float dls[2][QT_ROWS];
+  // NBUF query tiles (q and dout, swizzled, see qswz) and their lse, delta rows
+  __shared__ __attribute__((aligned(1024))) char qtiles[NBUF * BUF_B];
+  __shared__ __attribute__((aligned(16))) float lsd[NBUF][2][QT_ROWS];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -318,40 +355,42 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(
     dva[i] = f32x16{};
   }
 
-  const int n_qt = (T + QT_ROWS - 1) / QT_ROWS;
-  const int qt0 = k0 / QT_ROWS;
-  const int lrow = tid >> 4;
-  const int lchunk = tid & 15;
-  // query rows past T: q and dout read row T-1 and lse2 = +inf, so P = 0
-  uint4 xq[4], xg[4];
-  float l2 = 0.f, dl = 0.f;
-  auto gload = [&](int qt) {
-    const int q0 = qt * QT_ROWS;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const size_t off = base + min(q0 + 4 * lrow + i, T - 1) * rs + 8 * lchunk;
-      xq[i] = ld16(q + off);
-      xg[i] = ld16(dout + off);
-    }
-    if (tid < QT_ROWS) {
-      const int r = q0 + tid;
-      l2 = r < T ? lse_bh[r] * kLog2e : INFINITY;
-      dl = r < T ? del_bh[r] : 0.f;
-    }
-  };
+  const QOperandOffsets ofs = q_operand_offsets(lane);
+  const uint32_t qt_lds = lds_addr(qtiles);
+  const uint32_t lsd_lds = lds_addr(&lsd[0][0][0]);
 
-  auto lstore = [&](int buf) {
+  // Tile copies: wavefront w copies rows 4 (w + 4 m) .. + 3, m = 0..3, of the
+  // q and dout tiles (1 KB each: lane i moves 16 bytes of row + i / 16 into
+  // physical chunk i % 16); wavefronts 0 and 1 copy the lse and delta rows.
+  // Rows past T are past the end of the buffer range and arrive as zeros: a
+  // zero query row with zero dout, lse and delta adds nothing to dK or dV.
+  const uint32_t rsb = static_cast<uint32_t>(rs) * 2;  // bytes between rows
+  const int drow = 4 * wave + (lane >> 4);
+  const uint32_t dvoff = drow * rsb + 16 * ((lane & 15) ^ qswz(drow));
+  auto issue = [&](int qt, int u) {  // query tile qt -> buffer u
+    const int q0 = qt * QT_ROWS;
+    const uint32_t nrec = static_cast<uint32_t>(T - q0) * rsb;
+    const size_t off = base + static_cast<size_t>(q0) * rs;
+    const i32x4 rq = buffer_rsrc(q + off, nrec);
+    const i32x4 rg = buffer_rsrc(dout + off, nrec);
+    const uint32_t dst = qt_lds + u * BUF_B + 1024 * wave;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      st16(&Qs[buf][(4 * lrow + i) * RS + 8 * lchunk], xq[i]);
-      st16(&Gs[buf][(4 * lrow + i) * RS + 8 * lchunk], xg[i]);
+    for (int m = 0; m < 4; ++m) {
+      dma16(rq, dvoff + 16 * m * rsb, dst + 4096 * m);
+      dma16(rg, dvoff + 16 * m * rsb, dst + TILE_B + 4096 * m);
     }
-    tstore_4x8(Qt[buf], xq, lrow, lchunk);
-    tstore_4x8(Gt[buf], xg, lrow, lchunk);
-    if (tid < QT_ROWS) {
-      lse2s[buf][tid] = l2;
-      dls[buf][tid] = dl;
-    }
+    if (wave == 0)
+      dma4(buffer_rsrc(lse_bh + q0, static_cast<uint32_t>(T - q0) * 4), 4 * lane,
+           lsd_lds + u * 512);
+    if (wave == 1)
+      dma4(buffer_rsrc(del_bh + q0, static_cast<uint32_t>(T - q0) * 4), 4 * lane,
+           lsd_lds + u * 512 + 256);
+  };
+  // Every copy issued so far has landed and every wavefront is past its
+  // reads of the buffer that the next copy overwrites.
+  auto sync_tiles = [&]() {
+    wait_vmem();
+    __syncthreads();
   };
 
   // dS blocks of this wavefront's 32 keys (when a dS workspace is given).
@@ -363,32 +402,37 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(
     return (dsw && 32 * qblk < T) ? dsw + ds_block_index(bh, nbt, qblk, kblk) : nullptr;
   };
 
-  // Diagonal part: the first two query tiles hold every (query, key) pair of
-  // this workgroup that the causal mask can cut; one barrier per tile.
-  const int qt_diag_end = min(qt0 + 2, n_qt);
-  gload(qt0);
-  for (int qt = qt0; qt < qt_diag_end; ++qt) {
-    const int buf = (qt - qt0) & 1;
-    const int q0 = qt * QT_ROWS;
-    lstore(buf);
-    __syncthreads();  // publishes `buf`; frees buf^1 (see the forward kernel)
-    if (qt + 1 < n_qt) gload(qt + 1);
+  // Query tile qt0 + u lives in buffer u % NBUF.  At the sync before tile u is
+  // processed, tiles up to u + 1 have landed; the copy of tile u + 2 is issued
+  // right after it, into the buffer of tile u - 1.
+  const int n_qt = (T + QT_ROWS - 1) / QT_ROWS;
+  const int qt0 = k0 / QT_ROWS;
+  issue(qt0, 0);
+  if (qt0 + 1 < n_qt) issue(qt0 + 1, 1);
 
+  // Diagonal part: the first two query tiles hold every (query, key) pair of
+  // this workgroup that the causal mask can cut.
+  const int n_diag = min(2, n_qt - qt0);
+  for (int u = 0; u < n_diag; ++u) {
+    sync_tiles();
+    if (qt0 + u + 2 < n_qt) issue(qt0 + u + 2, (u + 2) % NBUF);
+    const int q0 = (qt0 + u) * QT_ROWS;
+    const uint32_t qtile = qt_lds + u * BUF_B;
     if (q0 + QT_ROWS - 1 < kw0) continue;  // every query precedes this wavefront's keys
     const int kq = krow - q0;
     if (q0 < kw0 + 31) {  // tile crosses this wavefront's diagonal
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
         if (q0 + 32 * qb + 31 >= kw0)
-          dkdv_block<true>(Qs[buf], Gs[buf], Qt[buf], Gt[buf], lse2s[buf], dls[buf], kreg, vreg,
-                           dka, dva, qb, lane, kq, c_log2, ds_of(q0 / 32 + qb));
+          dkdv_block<true>(qtile, lsd[u][0], lsd[u][1], ofs, kreg, vreg, dka, dva, qb, lane, kq,
+                           c_log2, ds_of(q0 / 32 + qb));
         __builtin_amdgcn_sched_barrier(0);  // keep the two blocks' live ranges apart
       }
     } else {
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
-        dkdv_block<false>(Qs[buf], Gs[buf], Qt[buf], Gt[buf], lse2s[buf], dls[buf], kreg, vreg,
-                          dka, dva, qb, lane, kq, c_log2, ds_of(q0 / 32 + qb));
+        dkdv_block<false>(qtile, lsd[u][0], lsd[u][1], ofs, kreg, vreg, dka, dva, qb, lane, kq,
+                          c_log2, ds_of(q0 / 32 + qb));
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -397,31 +441,32 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(
   // Steady part: every query follows every key, no mask, no skipped block.
   // Software pipeline over 32-query blocks: the step for block j computes the
   // probabilities of j, the scores of j+1 and the dK/dV update of j.  Block
-  // j+1 may live in the next tile, so each tile takes two barriers: one before
-  // its successor overwrites the buffer of its predecessor, one to publish it.
-  if (qt_diag_end < n_qt) {
-    const int ts = qt_diag_end;
-    int b = (ts - qt0) & 1;  // buffer of tile ts; it last held tile ts-2, long retired
-    lstore(b);
-    __syncthreads();
-    gload(min(ts + 1, n_qt - 1));
+  // j+1 may live in the next tile, which has landed by then; one sync per tile.
+  const int ts = qt0 + 2;
+  if (ts < n_qt) {
+    sync_tiles();
+    if (ts + 2 < n_qt) issue(ts + 2, 1);
+    int u = 2;  // buffer of tile t
     f32x16 s0, p0, s1, p1;
-    dkdv_scores(Qs[b], Gs[b], 0, kreg, vreg, s0, p0, lane);
+    dkdv_scores(qt_lds + 2 * BUF_B, 0, ofs, kreg, vreg, s0, p0);
     // Branch-free body: after the last tile the second step still computes
-    // scores of a block past the end (from a buffer refilled with clamped
-    // rows); they are never used.
+    // scores of a block past the end (from a stale buffer); they are never
+    // used.
     for (int t = ts; t < n_qt; ++t) {
+      const int un = u == NBUF - 1 ? 0 : u + 1;  // buffer of tile t + 1
+      const uint32_t ct = qt_lds + u * BUF_B;
+      const uint32_t nt = qt_lds + un * BUF_B;
       // block 2t (rows 0..31 of tile t) while computing scores of rows 32..63
-      dkdv_step(Qs[b], Gs[b], 32, lse2s[b], dls[b], Qt[b], Gt[b], 0, kreg, vreg, s0, p0,
-                s1, p1, dka, dva, lane, c_log2, ds_of(2 * t));
-      __syncthreads();  // every wavefront is done with tile t-1 (buffer b^1)
-      lstore(b ^ 1);
-      __syncthreads();
-      gload(min(t + 2, n_qt - 1));
+      dkdv_step(ct, 32, lsd[u][0], lsd[u][1], ct, 0, ofs, kreg, vreg, s0, p0, s1, p1, dka, dva,
+                lane, c_log2, ds_of(2 * t));
       // block 2t+1 (rows 32..63 of tile t) while computing scores of tile t+1 rows 0..31
-      dkdv_step(Qs[b ^ 1], Gs[b ^ 1], 0, lse2s[b], dls[b], Qt[b], Gt[b], 32, kreg, vreg,
-                s1, p1, s0, p0, dka, dva, lane, c_log2, ds_of(2 * t + 1));
-      b ^= 1;
+      dkdv_step(nt, 0, lsd[u][0], lsd[u][1], ct, 32, ofs, kreg, vreg, s1, p1, s0, p0, dka, dva,
+                lane, c_log2, ds_of(2 * t + 1));
+      if (t + 1 < n_qt) {
+        sync_tiles();
+        if (t + 3 < n_qt) issue(t + 3, u);
+      }
+      u = un;
     }
   }
 
@@ -442,6 +487,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(
 // ---------------------------------------------------------------- dQ
 
 constexpr int DQ_ROWS = 128;  // queries per workgroup (32 per wavefront)
+constexpr int RS = D + 8;     // row-major tile stride (bf16 elements)
 constexpr int DQ_KEYS = 64;   // keys per LDS tile
 
 // One 32-key block of a dQ step for one wavefront (32 queries), in three
@@ -694,9 +740,6 @@ __global__ __launch_bounds__(256, 1) void dq_kernel(
 // query0 + j of keys key0 .. key0 + 3.
 constexpr int DG_ROWS = 128;  // queries per workgroup (32 per wavefront)
 constexpr int DG_KEYS = 64;   // keys per K tile
-
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 __device__ __forceinline__ uint2 ds_read_tr16(const u16* lds) {
   const lds_i16x4* p =

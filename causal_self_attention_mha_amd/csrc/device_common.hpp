@@ -30,11 +30,13 @@ __device__ __forceinline__ float bf16_to_f32(u16 b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }
 
-// Pack two fp32 values into one dword of two bf16 (lo first).
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Pack two fp32 values into one dword of two bf16 (lo first), round to
+// nearest even: a single v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  __bf16 a = to_bf16(lo), b = to_bf16(hi);
-  u16 ua = __builtin_bit_cast(u16, a), ub = __builtin_bit_cast(u16, b);
-  return static_cast<uint32_t>(ua) | (static_cast<uint32_t>(ub) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
 
 // Sum over all 64 lanes of a wavefront; every lane gets the total.
@@ -82,6 +84,64 @@ __device__ __forceinline__ int perm_row(int m) {
 // score MFMA.
 __device__ __forceinline__ int acc_row(int lane, int r) {
   return 8 * (lane >> 5) + (r & 7) + 16 * (r >> 3);
+}
+
+// ---------------------------------------------------------------------------
+// Direct HBM -> LDS copies (buffer_load ... lds).  A raw buffer resource covers
+// [base, base + bytes); a load at a byte offset >= bytes returns zeros, which
+// the kernels use to pad ragged tiles without branches.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ i32x4 buffer_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  // word1: base[47:32], stride 0; word3: dword data format, no swizzle
+  return i32x4{static_cast<int>(static_cast<uint32_t>(a)), static_cast<int>(a >> 32),
+               static_cast<int>(bytes), 0x00020000};
+}
+
+// LDS byte address of a __shared__ object.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)p));
+}
+
+// Lane i copies the 16 (dma16) or 4 (dma4) bytes at byte offset voff of the
+// buffer into LDS at lds + 16 i (lds + 4 i).  lds must be wave-uniform.  The
+// copy is asynchronous and tracked by vmcnt alone: the compiler does not know
+// about it, so callers order it with wait_vmem() and a barrier.
+__device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :
+               : "v"(voff), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(lds))
+               : "memory");
+}
+__device__ __forceinline__ void dma4(i32x4 rsrc, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds"
+               :
+               : "v"(voff), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(lds))
+               : "memory");
+}
+
+// Waits until every vector memory operation of this wavefront has completed
+// (DMA copies landed in LDS, global stores acknowledged).
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
+// lane j receives element j % 4 of the 4-element (8-byte) rows supplied by
+// lanes 4 e + j / 4, e = 0..3: when lane i supplies the address of
+// M[R + i / 4][C + 4 (i % 4)] of a bf16 matrix M, lane j gets M[R + e][C + j].
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+__device__ __forceinline__ uint2 ds_read_tr16_at(uint32_t lds) {
+  return __builtin_bit_cast(
+      uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<lds_i16x4*>(lds)));
+}
+
+// Sixteen-byte LDS read at an LDS byte address.
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 lds_ld16(uint32_t lds) {
+  const u32x4 v = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(lds);
+  return __builtin_bit_cast(uint4, v);
 }
 
 // Maps workgroup index bid to a (batch*head, tile) pair.  The hardware hands
