@@ -105,11 +105,39 @@ __device__ __forceinline__ QOperandOffsets q_operand_offsets(int lane) {
   return o;
 }
 
-// B operand (8 consecutive query rows of one d column per lane) from a query
-// tile: rows base/256 + 8 (lane / 32) + 0..7 of d block db.
-__device__ __forceinline__ bf16x8 tr_operand(uint32_t base, const uint32_t (&t)[2]) {
-  const uint2 lo = ds_read_tr16_at(base + t[0]);
-  const uint2 hi = ds_read_tr16_at(base + t[1]);
+// Per-lane LDS byte addresses of one query tile's operand reads (tile address
+// plus QOperandOffsets), formed once per tile and kept in registers; the row
+// block and the q / dout choice go into the reads' immediate offsets.
+struct TileAddr {
+  uint32_t nat[8];
+  uint32_t tr[4][2];
+};
+
+__device__ __forceinline__ void nat_addr(uint32_t tile, const QOperandOffsets& o,
+                                         uint32_t (&a)[8]) {
+#pragma unroll
+  for (int kc = 0; kc < 8; ++kc) {
+    a[kc] = tile + o.nat[kc];
+    asm volatile("" : "+v"(a[kc]));  // keep the sum; do not re-add at every read
+  }
+}
+
+__device__ __forceinline__ void tr_addr(uint32_t tile, const QOperandOffsets& o,
+                                        uint32_t (&a)[4][2]) {
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      a[db][sub] = tile + o.tr[db][sub];
+      asm volatile("" : "+v"(a[db][sub]));
+    }
+}
+
+// B operand (8 consecutive query rows of one d column per lane): rows
+// off / 256 + 8 (lane / 32) + 0..7 of d block db of the tile behind t.
+__device__ __forceinline__ bf16x8 tr_operand(const uint32_t (&t)[2], uint32_t off) {
+  const uint2 lo = ds_read_tr16_at(t[0] + off);
+  const uint2 hi = ds_read_tr16_at(t[1] + off);
   return as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
 }
 
@@ -123,19 +151,19 @@ __device__ __forceinline__ bf16x8 tr_operand(uint32_t base, const uint32_t (&t)[
 // The steady-state loop overlaps the scores MFMAs of block j+1 with the probs
 // VALU work of block j.  qtile is the LDS byte address of a buffer's q tile
 // (its dout tile follows at + TILE_B).
-__device__ __forceinline__ void dkdv_scores(uint32_t qtile, int row0, const QOperandOffsets& ofs,
+__device__ __forceinline__ void dkdv_scores(const uint32_t (&na)[8], int row0,
                                             const bf16x8 (&kreg)[8], const bf16x8 (&vreg)[8],
                                             f32x16& sacc, f32x16& pacc) {
   sacc = f32x16{};
   pacc = f32x16{};
-  const uint32_t a0 = qtile + row0 * 256;
+  const uint32_t r = row0 * 256;
 #pragma unroll
   for (int k4 = 0; k4 < 8; k4 += 4) {
     bf16x8 aq[4], ag[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      aq[i] = as_bf16x8(lds_ld16(a0 + ofs.nat[k4 + i]));
-      ag[i] = as_bf16x8(lds_ld16(a0 + TILE_B + ofs.nat[k4 + i]));
+      aq[i] = as_bf16x8(lds_ld16(na[k4 + i] + r));
+      ag[i] = as_bf16x8(lds_ld16(na[k4 + i] + r + TILE_B));
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -171,16 +199,16 @@ __device__ __forceinline__ void dkdv_probs(const f32x16& sacc, const f32x16& pac
 }
 
 __device__ __forceinline__ void dkdv_accum(const bf16x8 (&pb)[2], const bf16x8 (&sb)[2],
-                                           uint32_t qtile, int row0, const QOperandOffsets& ofs,
+                                           const uint32_t (&ta)[4][2], int row0,
                                            f32x16 (&dka)[4], f32x16 (&dva)[4]) {
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    const uint32_t base = qtile + (row0 + 16 * j) * 256;  // queries row0 + 16 j + 8 half + 0..7
+    const uint32_t r = (row0 + 16 * j) * 256;  // queries row0 + 16 j + 8 half + 0..7
     bf16x8 bg[4], bq[4];
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
-      bg[db] = tr_operand(base + TILE_B, ofs.tr[db]);
-      bq[db] = tr_operand(base, ofs.tr[db]);
+      bg[db] = tr_operand(ta[db], r + TILE_B);
+      bq[db] = tr_operand(ta[db], r);
     }
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
@@ -205,17 +233,17 @@ __device__ __forceinline__ void store_ds(u16* blk, const bf16x8 (&sb)[2], int la
 }
 
 template <bool MASK>
-__device__ __forceinline__ void dkdv_block(uint32_t qtile, const float* lse_t, const float* dl_t,
-                                           const QOperandOffsets& ofs, const bf16x8 (&kreg)[8],
+__device__ __forceinline__ void dkdv_block(const TileAddr& ta, const float* lse_t,
+                                           const float* dl_t, const bf16x8 (&kreg)[8],
                                            const bf16x8 (&vreg)[8], f32x16 (&dka)[4],
                                            f32x16 (&dva)[4], int qb, int lane, int key_minus_q0,
                                            float c_log2, u16* ds_blk) {
   f32x16 sacc, pacc;
-  dkdv_scores(qtile, 32 * qb, ofs, kreg, vreg, sacc, pacc);
+  dkdv_scores(ta.nat, 32 * qb, kreg, vreg, sacc, pacc);
   bf16x8 pb[2], sb[2];
   dkdv_probs<MASK>(sacc, pacc, lse_t, dl_t, 32 * qb, pb, sb, lane, key_minus_q0, c_log2);
   if (ds_blk) store_ds(ds_blk, sb, lane);
-  dkdv_accum(pb, sb, qtile, 32 * qb, ofs, dka, dva);
+  dkdv_accum(pb, sb, ta.tr, 32 * qb, dka, dva);
 }
 
 // Steady-state step: probabilities of the current block (held in s_cur,
@@ -224,17 +252,17 @@ __device__ __forceinline__ void dkdv_block(uint32_t qtile, const float* lse_t, c
 // separated by scheduling fences: each round issues the LDS reads two rounds
 // ahead, one score MFMA for S and one for dP, and the probability math of two
 // of this lane's sixteen (key, query) elements, so the VALU work runs while
-// the matrix cores are busy.  ntile/rowN locate the next block, ctile/rowC
-// the current one.
-__device__ __forceinline__ void dkdv_step(uint32_t ntile, int rowN, const float* lse_t,
-                                          const float* dl_t, uint32_t ctile, int rowC,
-                                          const QOperandOffsets& ofs, const bf16x8 (&kreg)[8],
+// the matrix cores are busy.  na/rowN locate the next block (row-wise reads of
+// its tile), ta/rowC the current one (transposed reads).
+__device__ __forceinline__ void dkdv_step(const uint32_t (&na)[8], int rowN, const float* lse_t,
+                                          const float* dl_t, const uint32_t (&ta)[4][2],
+                                          int rowC, const bf16x8 (&kreg)[8],
                                           const bf16x8 (&vreg)[8], const f32x16& s_cur,
                                           const f32x16& p_cur, f32x16& s_nxt, f32x16& p_nxt,
                                           f32x16 (&dka)[4], f32x16 (&dva)[4], int lane,
                                           float c_log2, u16* ds_blk) {
   const int half = lane >> 5;
-  const uint32_t an = ntile + rowN * 256;
+  const uint32_t rn = rowN * 256;
   // element r of the current block: query row r0 + 16 (r/8) + r%8
   const int r0 = rowC + 8 * half;
   float l16[16], d16[16];
@@ -250,10 +278,10 @@ __device__ __forceinline__ void dkdv_step(uint32_t ntile, int rowN, const float*
       d16[8 * j + 4 * k + 2] = d.z; d16[8 * j + 4 * k + 3] = d.w;
     }
   bf16x8 aq[8], ag[8];
-  aq[0] = as_bf16x8(lds_ld16(an + ofs.nat[0]));
-  ag[0] = as_bf16x8(lds_ld16(an + TILE_B + ofs.nat[0]));
-  aq[1] = as_bf16x8(lds_ld16(an + ofs.nat[1]));
-  ag[1] = as_bf16x8(lds_ld16(an + TILE_B + ofs.nat[1]));
+  aq[0] = as_bf16x8(lds_ld16(na[0] + rn));
+  ag[0] = as_bf16x8(lds_ld16(na[0] + rn + TILE_B));
+  aq[1] = as_bf16x8(lds_ld16(na[1] + rn));
+  ag[1] = as_bf16x8(lds_ld16(na[1] + rn + TILE_B));
   s_nxt = f32x16{};
   p_nxt = f32x16{};
   uint32_t pw[8], sw[8];  // bf16 pairs (elements 2i, 2i+1)
@@ -261,8 +289,8 @@ __device__ __forceinline__ void dkdv_step(uint32_t ntile, int rowN, const float*
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     if (i + 2 < 8) {
-      aq[i + 2] = as_bf16x8(lds_ld16(an + ofs.nat[i + 2]));
-      ag[i + 2] = as_bf16x8(lds_ld16(an + TILE_B + ofs.nat[i + 2]));
+      aq[i + 2] = as_bf16x8(lds_ld16(na[i + 2] + rn));
+      ag[i + 2] = as_bf16x8(lds_ld16(na[i + 2] + rn + TILE_B));
     }
     s_nxt = mfma32(aq[i], kreg[i], s_nxt);
     const int r = 2 * i;
@@ -283,11 +311,11 @@ __device__ __forceinline__ void dkdv_step(uint32_t ntile, int rowN, const float*
   // dV += P^T dout, dK += dS^T Q for the current block: operands of chunk j+1
   // are read while chunk j's MFMAs run
   bf16x8 bg[2][4], bq[2][4];
-  const uint32_t c0 = ctile + rowC * 256;
+  const uint32_t rc = rowC * 256;
 #pragma unroll
   for (int db = 0; db < 4; ++db) {
-    bg[0][db] = tr_operand(c0 + TILE_B, ofs.tr[db]);
-    bq[0][db] = tr_operand(c0, ofs.tr[db]);
+    bg[0][db] = tr_operand(ta[db], rc + TILE_B);
+    bq[0][db] = tr_operand(ta[db], rc);
   }
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -295,8 +323,8 @@ __device__ __forceinline__ void dkdv_step(uint32_t ntile, int rowN, const float*
     if (j == 0) {
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
-        bg[1][db] = tr_operand(c0 + 16 * 256 + TILE_B, ofs.tr[db]);
-        bq[1][db] = tr_operand(c0 + 16 * 256, ofs.tr[db]);
+        bg[1][db] = tr_operand(ta[db], rc + 16 * 256 + TILE_B);
+        bq[1][db] = tr_operand(ta[db], rc + 16 * 256);
       }
     }
 #pragma unroll
@@ -417,22 +445,24 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(
     sync_tiles();
     if (qt0 + u + 2 < n_qt) issue(qt0 + u + 2, (u + 2) % NBUF);
     const int q0 = (qt0 + u) * QT_ROWS;
-    const uint32_t qtile = qt_lds + u * BUF_B;
     if (q0 + QT_ROWS - 1 < kw0) continue;  // every query precedes this wavefront's keys
+    TileAddr ta;
+    nat_addr(qt_lds + u * BUF_B, ofs, ta.nat);
+    tr_addr(qt_lds + u * BUF_B, ofs, ta.tr);
     const int kq = krow - q0;
     if (q0 < kw0 + 31) {  // tile crosses this wavefront's diagonal
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
         if (q0 + 32 * qb + 31 >= kw0)
-          dkdv_block<true>(qtile, lsd[u][0], lsd[u][1], ofs, kreg, vreg, dka, dva, qb, lane, kq,
-                           c_log2, ds_of(q0 / 32 + qb));
+          dkdv_block<true>(ta, lsd[u][0], lsd[u][1], kreg, vreg, dka, dva, qb, lane, kq, c_log2,
+                           ds_of(q0 / 32 + qb));
         __builtin_amdgcn_sched_barrier(0);  // keep the two blocks' live ranges apart
       }
     } else {
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
-        dkdv_block<false>(qtile, lsd[u][0], lsd[u][1], ofs, kreg, vreg, dka, dva, qb, lane, kq,
-                          c_log2, ds_of(q0 / 32 + qb));
+        dkdv_block<false>(ta, lsd[u][0], lsd[u][1], kreg, vreg, dka, dva, qb, lane, kq, c_log2,
+                          ds_of(q0 / 32 + qb));
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -447,21 +477,26 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(
     sync_tiles();
     if (ts + 2 < n_qt) issue(ts + 2, 1);
     int u = 2;  // buffer of tile t
+    uint32_t nc[8];  // row-read addresses of tile t
+    nat_addr(qt_lds + 2 * BUF_B, ofs, nc);
     f32x16 s0, p0, s1, p1;
-    dkdv_scores(qt_lds + 2 * BUF_B, 0, ofs, kreg, vreg, s0, p0);
+    dkdv_scores(nc, 0, kreg, vreg, s0, p0);
     // Branch-free body: after the last tile the second step still computes
     // scores of a block past the end (from a stale buffer); they are never
     // used.
     for (int t = ts; t < n_qt; ++t) {
       const int un = u == NBUF - 1 ? 0 : u + 1;  // buffer of tile t + 1
-      const uint32_t ct = qt_lds + u * BUF_B;
-      const uint32_t nt = qt_lds + un * BUF_B;
+      uint32_t tc[4][2], nn[8];
+      tr_addr(qt_lds + u * BUF_B, ofs, tc);
       // block 2t (rows 0..31 of tile t) while computing scores of rows 32..63
-      dkdv_step(ct, 32, lsd[u][0], lsd[u][1], ct, 0, ofs, kreg, vreg, s0, p0, s1, p1, dka, dva,
-                lane, c_log2, ds_of(2 * t));
+      dkdv_step(nc, 32, lsd[u][0], lsd[u][1], tc, 0, kreg, vreg, s0, p0, s1, p1, dka, dva, lane,
+                c_log2, ds_of(2 * t));
+      nat_addr(qt_lds + un * BUF_B, ofs, nn);
       // block 2t+1 (rows 32..63 of tile t) while computing scores of tile t+1 rows 0..31
-      dkdv_step(nt, 0, lsd[u][0], lsd[u][1], ct, 32, ofs, kreg, vreg, s1, p1, s0, p0, dka, dva,
-                lane, c_log2, ds_of(2 * t + 1));
+      dkdv_step(nn, 0, lsd[u][0], lsd[u][1], tc, 32, kreg, vreg, s1, p1, s0, p0, dka, dva, lane,
+                c_log2, ds_of(2 * t + 1));
+#pragma unroll
+      for (int kc = 0; kc < 8; ++kc) nc[kc] = nn[kc];
       if (t + 1 < n_qt) {
         sync_tiles();
         if (t + 3 < n_qt) issue(t + 3, u);
