@@ -64,82 +64,12 @@ __global__ __launch_bounds__(256) void delta_kernel(const u16* __restrict__ o,
 constexpr int KT_KEYS = 128;  // keys per workgroup (32 per wavefront)
 constexpr int QT_ROWS = 64;   // queries per LDS tile
 constexpr int NBUF = 3;       // query tiles resident in LDS at once
-constexpr uint32_t TILE_B = QT_ROWS * D * 2;  // bytes of one 64 x 128 bf16 tile
+constexpr uint32_t TILE_B = kTileBytes;      // one 64 x 128 bf16 tile
 constexpr uint32_t BUF_B = 2 * TILE_B;        // one buffer: q tile, then dout tile
 
 // Query tiles are copied straight from HBM into LDS (no register staging, no
-// transposed copy).  A tile is 64 unpadded rows of 256 bytes; the 16-byte
-// chunk c of row r sits at chunk c ^ qswz(r).  qswz is a bijection of r mod 16,
-// so the row reads of an MFMA A operand (16 lanes: one chunk of 16 different
-// rows) touch 16 different chunks; and its top two bits differ between any
-// four consecutive rows, so the transposing reads of a B operand (32 lanes:
-// 64 bytes of 4 consecutive rows) touch 16 different chunks too.  With
-// gfx950's 64 four-byte LDS banks both are free of bank conflicts.
-__device__ __forceinline__ uint32_t qswz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
-
-// Per-lane byte offsets, within a query tile, of this lane's operand reads.
-struct QOperandOffsets {
-  uint32_t nat[8];    // A operand: row perm_row(l32), elements 16 kc + 8 half .. + 7
-  uint32_t tr[4][2];  // B operand, d block db: transposing read of rows 4 sub .. 4 sub + 3
-};
-
-__device__ __forceinline__ QOperandOffsets q_operand_offsets(int lane) {
-  QOperandOffsets o;
-  const int half = lane >> 5;
-  const int pr = perm_row(lane & 31);
-#pragma unroll
-  for (int kc = 0; kc < 8; ++kc) o.nat[kc] = pr * 256 + 16 * ((2 * kc + half) ^ qswz(pr));
-  // Lane i of 16-lane group g supplies row 8 (g / 2) + 4 sub + i / 4 and the
-  // columns 32 db + 16 (g % 2) + 4 (i % 4) .. + 3; it then holds column
-  // 32 db + lane % 32 of rows 8 (lane / 32) + 4 sub + 0..3, i.e. half of the
-  // 8 query rows its B operand needs (the other half comes from sub ^ 1).
-  const int g = lane >> 4, i = lane & 15;
-#pragma unroll
-  for (int db = 0; db < 4; ++db)
-#pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-      const int r = 8 * (g >> 1) + 4 * sub + (i >> 2);
-      const int col = 32 * db + 16 * (g & 1) + 4 * (i & 3);
-      o.tr[db][sub] = r * 256 + 16 * ((col >> 3) ^ qswz(r)) + 2 * (col & 7);
-    }
-  return o;
-}
-
-// Per-lane LDS byte addresses of one query tile's operand reads (tile address
-// plus QOperandOffsets), formed once per tile and kept in registers; the row
-// block and the q / dout choice go into the reads' immediate offsets.
-struct TileAddr {
-  uint32_t nat[8];
-  uint32_t tr[4][2];
-};
-
-__device__ __forceinline__ void nat_addr(uint32_t tile, const QOperandOffsets& o,
-                                         uint32_t (&a)[8]) {
-#pragma unroll
-  for (int kc = 0; kc < 8; ++kc) {
-    a[kc] = tile + o.nat[kc];
-    asm volatile("" : "+v"(a[kc]));  // keep the sum; do not re-add at every read
-  }
-}
-
-__device__ __forceinline__ void tr_addr(uint32_t tile, const QOperandOffsets& o,
-                                        uint32_t (&a)[4][2]) {
-#pragma unroll
-  for (int db = 0; db < 4; ++db)
-#pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-      a[db][sub] = tile + o.tr[db][sub];
-      asm volatile("" : "+v"(a[db][sub]));
-    }
-}
-
-// B operand (8 consecutive query rows of one d column per lane): rows
-// off / 256 + 8 (lane / 32) + 0..7 of d block db of the tile behind t.
-__device__ __forceinline__ bf16x8 tr_operand(const uint32_t (&t)[2], uint32_t off) {
-  const uint2 lo = ds_read_tr16_at(t[0] + off);
-  const uint2 hi = ds_read_tr16_at(t[1] + off);
-  return as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
-}
+// transposed copy) in the swizzled 64 x 128 layout of tile_swz; Q and dout rows
+// are read row-wise as MFMA A operands and transposed as B operands.
 
 // One 32-query block of a dK/dV step for one wavefront (32 keys), in three
 // phases:
@@ -341,7 +271,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(
     const u16* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
     u16* __restrict__ dk, u16* __restrict__ dv, u16* __restrict__ dsw, int nbt, int B, int T,
     int H, float c_log2, float scale) {
-  // NBUF query tiles (q and dout, swizzled, see qswz) and their lse, delta rows
+  // NBUF query tiles (q and dout, swizzled, see tile_swz) and their lse, delta rows
   __shared__ __attribute__((aligned(1024))) char qtiles[NBUF * BUF_B];
   __shared__ __attribute__((aligned(16))) float lsd[NBUF][2][QT_ROWS];
 
@@ -383,30 +313,22 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(
     dva[i] = f32x16{};
   }
 
-  const QOperandOffsets ofs = q_operand_offsets(lane);
+  const TileOffsets ofs = tile_operand_offsets(lane);
   const uint32_t qt_lds = lds_addr(qtiles);
   const uint32_t lsd_lds = lds_addr(&lsd[0][0][0]);
 
-  // Tile copies: wavefront w copies rows 4 (w + 4 m) .. + 3, m = 0..3, of the
-  // q and dout tiles (1 KB each: lane i moves 16 bytes of row + i / 16 into
-  // physical chunk i % 16); wavefronts 0 and 1 copy the lse and delta rows.
-  // Rows past T are past the end of the buffer range and arrive as zeros: a
-  // zero query row with zero dout, lse and delta adds nothing to dK or dV.
+  // Tile copies (see copy_tile); wavefronts 0 and 1 also copy the lse and
+  // delta rows.  Rows past T are past the end of the buffer range and arrive
+  // as zeros: a zero query row with zero dout, lse and delta adds nothing to
+  // dK or dV.
   const uint32_t rsb = static_cast<uint32_t>(rs) * 2;  // bytes between rows
-  const int drow = 4 * wave + (lane >> 4);
-  const uint32_t dvoff = drow * rsb + 16 * ((lane & 15) ^ qswz(drow));
+  const uint32_t dvoff = tile_copy_offset(wave, lane, rsb);
   auto issue = [&](int qt, int u) {  // query tile qt -> buffer u
     const int q0 = qt * QT_ROWS;
     const uint32_t nrec = static_cast<uint32_t>(T - q0) * rsb;
     const size_t off = base + static_cast<size_t>(q0) * rs;
-    const i32x4 rq = buffer_rsrc(q + off, nrec);
-    const i32x4 rg = buffer_rsrc(dout + off, nrec);
-    const uint32_t dst = qt_lds + u * BUF_B + 1024 * wave;
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      dma16(rq, dvoff + 16 * m * rsb, dst + 4096 * m);
-      dma16(rg, dvoff + 16 * m * rsb, dst + TILE_B + 4096 * m);
-    }
+    copy_tile(buffer_rsrc(q + off, nrec), dvoff, rsb, qt_lds + u * BUF_B, wave);
+    copy_tile(buffer_rsrc(dout + off, nrec), dvoff, rsb, qt_lds + u * BUF_B + TILE_B, wave);
     if (wave == 0)
       dma4(buffer_rsrc(lse_bh + q0, static_cast<uint32_t>(T - q0) * 4), 4 * lane,
            lsd_lds + u * 512);

@@ -144,6 +144,102 @@ __device__ __forceinline__ uint4 lds_ld16(uint32_t lds) {
   return __builtin_bit_cast(uint4, v);
 }
 
+// ---------------------------------------------------------------------------
+// Swizzled 64 x 128 bf16 tiles in LDS (query tiles of the backward, key and
+// value tiles of the forward), filled by dma16 from HBM.  A tile is 64
+// unpadded rows of 256 bytes; the 16-byte chunk c of row r sits at chunk
+// c ^ tile_swz(r).  tile_swz is a bijection of r mod 16, so the row reads of
+// an MFMA operand (16 lanes: one chunk of 16 different rows) touch 16
+// different chunks; and its top two bits differ between any four consecutive
+// rows, so the transposing reads (32 lanes: 64 bytes of 4 consecutive rows)
+// touch 16 different chunks too.  With gfx950's 64 four-byte LDS banks both
+// are free of bank conflicts.
+constexpr uint32_t kTileBytes = 64 * 128 * 2;
+
+__device__ __forceinline__ uint32_t tile_swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+
+// Per-lane byte offsets, within a tile, of this lane's operand reads.
+struct TileOffsets {
+  uint32_t nat[8];    // row read: row perm_row(l32), elements 16 kc + 8 half .. + 7
+  uint32_t tr[4][2];  // transposed read, column block db: rows 4 sub .. 4 sub + 3
+};
+
+__device__ __forceinline__ TileOffsets tile_operand_offsets(int lane) {
+  TileOffsets o;
+  const int half = lane >> 5;
+  const int pr = perm_row(lane & 31);
+#pragma unroll
+  for (int kc = 0; kc < 8; ++kc) o.nat[kc] = pr * 256 + 16 * ((2 * kc + half) ^ tile_swz(pr));
+  // Lane i of 16-lane group g supplies row 8 (g / 2) + 4 sub + i / 4 and the
+  // columns 32 db + 16 (g % 2) + 4 (i % 4) .. + 3; it then holds column
+  // 32 db + lane % 32 of rows 8 (lane / 32) + 4 sub + 0..3, i.e. half of the
+  // 8 rows its MFMA operand needs (the other half comes from sub ^ 1).
+  const int g = lane >> 4, i = lane & 15;
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      const int r = 8 * (g >> 1) + 4 * sub + (i >> 2);
+      const int col = 32 * db + 16 * (g & 1) + 4 * (i & 3);
+      o.tr[db][sub] = r * 256 + 16 * ((col >> 3) ^ tile_swz(r)) + 2 * (col & 7);
+    }
+  return o;
+}
+
+// Per-lane LDS byte addresses of one tile's operand reads (tile address plus
+// TileOffsets), formed once per tile and kept in registers; row blocks and
+// buffer choices go into the reads' immediate offsets.
+struct TileAddr {
+  uint32_t nat[8];
+  uint32_t tr[4][2];
+};
+
+__device__ __forceinline__ void nat_addr(uint32_t tile, const TileOffsets& o, uint32_t (&a)[8]) {
+#pragma unroll
+  for (int kc = 0; kc < 8; ++kc) {
+    a[kc] = tile + o.nat[kc];
+    asm volatile("" : "+v"(a[kc]));  // keep the sum; do not re-add at every read
+  }
+}
+
+__device__ __forceinline__ void tr_addr(uint32_t tile, const TileOffsets& o,
+                                        uint32_t (&a)[4][2]) {
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      a[db][sub] = tile + o.tr[db][sub];
+      asm volatile("" : "+v"(a[db][sub]));
+    }
+}
+
+// Transposed operand (8 consecutive rows of one column per lane): rows
+// off / 256 + 8 (lane / 32) + 0..7, column 32 db + lane % 32 of the tile
+// behind t = a.tr[db].
+__device__ __forceinline__ bf16x8 tr_operand(const uint32_t (&t)[2], uint32_t off) {
+  const uint2 lo = ds_read_tr16_at(t[0] + off);
+  const uint2 hi = ds_read_tr16_at(t[1] + off);
+  return as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+}
+
+// Per-lane source offset of the tile copy: wavefront w of a 256-thread
+// workgroup moves rows 4 (w + 4 m) .. + 3, m = 0..3, one 1-KB dma16 each
+// (lane i: 16 bytes of row + i / 16 into physical chunk i % 16).  rsb is the
+// byte stride between rows in HBM.
+__device__ __forceinline__ uint32_t tile_copy_offset(int wave, int lane, uint32_t rsb) {
+  const int drow = 4 * wave + (lane >> 4);
+  return drow * rsb + 16 * ((lane & 15) ^ tile_swz(drow));
+}
+
+// Copies this wavefront's share of a 64 x 128 tile: rows of the buffer
+// resource (rows past its end arrive as zeros) into the tile at LDS address
+// tile.
+__device__ __forceinline__ void copy_tile(i32x4 rsrc, uint32_t voff, uint32_t rsb, uint32_t tile,
+                                          int wave) {
+#pragma unroll
+  for (int m = 0; m < 4; ++m) dma16(rsrc, voff + 16 * m * rsb, tile + 1024 * wave + 4096 * m);
+}
+
 // Maps workgroup index bid to a (batch*head, tile) pair.  The hardware hands
 // workgroup i to XCD i % 8, and each XCD has its own L2; this order makes the
 // workgroups of one XCD cover one head's tiles back to back (tile 0 first,

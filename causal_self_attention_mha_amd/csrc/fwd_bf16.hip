@@ -9,11 +9,12 @@
 // Design (one workgroup = 4 wavefronts = 128 query rows of one (b, h)):
 //   * each wavefront owns 32 query rows; its Q^T operand (32 x 128 bf16) stays
 //     in registers for the whole key loop;
-//   * K and V tiles of 64 keys are staged through double-buffered LDS, the
-//     next tile's global loads in flight while the current one is computed:
-//     K row-major (padded rows), V transposed (d-major, XOR-swizzled 16-byte
-//     groups) so that the PV MFMA reads 16 contiguous bytes per lane and
-//     neither the stores nor the reads conflict in LDS banks;
+//   * K and V tiles of 64 keys are copied straight from HBM into
+//     double-buffered LDS (buffer loads with the LDS destination; keys past T
+//     arrive as zeros), the next tile's copy in flight while the current one
+//     is computed, one barrier per tile.  Both tiles keep their natural
+//     row-major layout, swizzled (see tile_swz): K is read row-wise, V^T with
+//     the transposing ds_read_b64_tr_b16, both free of bank conflicts;
 //   * scores are computed transposed, S^T = K Q^T (v_mfma_f32_32x32x16_bf16),
 //     so that each lane owns one query row: the online-softmax max and sum are
 //     lane-local apart from one exchange with lane l^32;
@@ -21,10 +22,16 @@
 //     rescale factor is also lane-local;
 //   * the softmax runs in the exp2 domain on raw scores: p = 2^(c z - c m)
 //     with c = s log2(e), one FMA and one v_exp_f32 per score;
+//   * the 32 LDS operand reads of a tile are issued in a fixed order four
+//     operands ahead of the MFMA that consumes them, the last K MFMAs
+//     overlapping the first V reads, which in turn stay in flight during the
+//     softmax;
 //   * key tiles entirely above the diagonal are never visited; only tiles that
 //     cross the diagonal apply the causal select;
 //   * each XCD runs one head's query tiles back to back, heaviest first, so
 //     the head's K and V stay in that XCD's L2.
+#include <type_traits>
+
 #include "device_common.hpp"
 #include "internal.hpp"
 
@@ -34,7 +41,7 @@ namespace {
 constexpr int D = kHeadDim;
 constexpr int BQ = 128;  // query rows per workgroup
 constexpr int BK = 64;   // keys per LDS tile
-constexpr int KS = D + 8;    // K tile row stride in LDS (bf16 elements)
+constexpr uint32_t BUF_B = 2 * kTileBytes;  // one buffer: K tile, then V tile
 // Lazy rescaling: the running max m is only raised (and O, l rescaled) when a
 // new score exceeds it by more than 2^8 in the exp2 domain, so most tiles skip
 // the rescale; probabilities then stay below 256, harmless in fp32 and bf16.
@@ -46,9 +53,8 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const u16* __restrict_
                                                           u16* __restrict__ o,
                                                           float* __restrict__ lse, int B, int T,
                                                           int H, float c_log2, float scale) {
-  // double-buffered K (row-major) and V^T tiles
-  __shared__ __attribute__((aligned(16))) u16 Ks[2][BK * KS];
-  __shared__ __attribute__((aligned(16))) u16 Vt[2][D * BK];  // swizzled, see toff()
+  // two buffers of (K tile, V tile), swizzled (see tile_swz)
+  __shared__ __attribute__((aligned(1024))) char kvs[2 * BUF_B];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -88,53 +94,64 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const u16* __restrict_
   const int last_q = min(q0 + BQ, T) - 1;
   const int n_kt = last_q / BK + 1;  // key tiles at or left of the diagonal
 
-  // cooperative tile loads: K rows (tid>>4) + 16 i, 16-byte chunk tid&15;
-  // V keys 4*(tid>>4) + i, d chunk tid&15, written transposed.  Key rows past
-  // T read row T-1: such keys are always masked (their P is 0), so any finite
-  // value works.
-  const int lrow = tid >> 4;
-  const int lchunk = tid & 15;
-  const u16* kg = k + base + 8 * lchunk;
-  const u16* vg = v + base + 8 * lchunk;
-  uint4 kv[4], vv[4];
-  auto gload = [&](int kt) {
+  // operand read addresses in buffer 0 (buffer 1: + BUF_B, V tile: + kTileBytes)
+  const uint32_t kv_lds = lds_addr(kvs);
+  TileAddr ta;
+  {
+    const TileOffsets ofs = tile_operand_offsets(lane);
+    nat_addr(kv_lds, ofs, ta.nat);
+    tr_addr(kv_lds + kTileBytes, ofs, ta.tr);
+  }
+  const uint32_t rsb = static_cast<uint32_t>(rs) * 2;
+  const uint32_t cvoff = tile_copy_offset(wave, lane, rsb);
+  auto issue = [&](int kt, int buf) {  // K, V tile kt -> buffer buf; keys past T read as 0
     const int k0 = kt * BK;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      kv[i] = ld16(kg + min(k0 + lrow + 16 * i, T - 1) * rs);
-      vv[i] = ld16(vg + min(k0 + 4 * lrow + i, T - 1) * rs);
-    }
-  };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) st16(&Ks[buf][(lrow + 16 * i) * KS + 8 * lchunk], kv[i]);
-    tstore_4x8(Vt[buf], vv, lrow, lchunk);  // V^T: row d, column key
+    const uint32_t nrec = static_cast<uint32_t>(T - k0) * rsb;
+    const size_t off = base + static_cast<size_t>(k0) * rs;
+    copy_tile(buffer_rsrc(k + off, nrec), cvoff, rsb, kv_lds + buf * BUF_B, wave);
+    copy_tile(buffer_rsrc(v + off, nrec), cvoff, rsb, kv_lds + buf * BUF_B + kTileBytes, wave);
   };
 
-  gload(0);
-  for (int kt = 0; kt < n_kt; ++kt) {
-    const int buf = kt & 1;
+  // One key tile; BUF is the buffer it sits in (a compile-time constant, so
+  // that every LDS read address is a register plus an immediate).
+  auto tile = [&](auto bufc, int kt) {
+    constexpr uint32_t BUF = decltype(bufc)::value;
+    constexpr uint32_t KO = BUF * BUF_B;  // K tile offset from buffer 0's
+    constexpr uint32_t VO = BUF * BUF_B;  // V^T reads: ta.tr already points at the V tile
     const int k0 = kt * BK;
-    lstore(buf);
-    // One barrier per tile: it publishes buffer `buf` and, because every
-    // wavefront passed it only after finishing tile kt-1, it also frees
-    // buffer buf^1 for the next store.
+    // One barrier per tile: after it every copy into this buffer has landed
+    // and every wavefront is done with the other buffer (tile kt-1), which the
+    // next copy may then overwrite.
+    wait_vmem();
     __syncthreads();
-    if (kt + 1 < n_kt) gload(kt + 1);  // next tile in flight during this one
+    if (kt + 1 < n_kt) issue(kt + 1, 1 - BUF);
+    if (k0 > qw0 + 31) return;  // whole tile above this wavefront's diagonal
 
-    if (k0 > qw0 + 31) continue;  // whole tile above this wavefront's diagonal
+    // Operand sequence: 16 K operands, n = 2 kc + kb (the two score blocks
+    // alternate, so consecutive MFMAs are independent), then 16 V^T operands,
+    // n = 16 + 4 c + db.
+    bf16x8 opnd[32];
+    auto read = [&](int n) {
+      if (n < 16) {
+        const int kc = n >> 1, kb = n & 1;
+        opnd[n] = as_bf16x8(lds_ld16(ta.nat[kc] + KO + kb * 32 * 256));
+      } else {
+        const int c = (n - 16) >> 2, db = (n - 16) & 3;
+        opnd[n] = tr_operand(ta.tr[db], VO + c * 16 * 256);
+      }
+    };
+    constexpr int AHEAD = 4;
+#pragma unroll
+    for (int n = 0; n < AHEAD; ++n) read(n);
+    __builtin_amdgcn_sched_barrier(0);
 
     // S^T = K Q^T for two 32-key blocks
-    f32x16 sacc[2];
+    f32x16 sacc[2] = {f32x16{}, f32x16{}};
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const u16* kp = &Ks[buf][(kb * 32 + perm_row(l32)) * KS + 8 * half];
-      bf16x8 a[8];
-#pragma unroll
-      for (int kc = 0; kc < 8; ++kc) a[kc] = as_bf16x8(ld16(kp + 16 * kc));
-      sacc[kb] = f32x16{};
-#pragma unroll
-      for (int kc = 0; kc < 8; ++kc) sacc[kb] = mfma32(a[kc], qreg[kc], sacc[kb]);
+    for (int n = 0; n < 16; ++n) {
+      read(n + AHEAD);
+      sacc[n & 1] = mfma32(opnd[n], qreg[n >> 1], sacc[n & 1]);
+      __builtin_amdgcn_sched_barrier(0);
     }
 
     // causal select on tiles that cross the diagonal
@@ -179,17 +196,22 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const u16* __restrict_
       }
     }
     lpart += psum;
+    __builtin_amdgcn_sched_barrier(0);
 
     // O^T += V^T P^T
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      bf16x8 a[4];
-#pragma unroll
-      for (int db = 0; db < 4; ++db)
-        a[db] = as_bf16x8(ld16(&Vt[buf][toff(db * 32 + l32, 2 * c + half)]));
-#pragma unroll
-      for (int db = 0; db < 4; ++db) oacc[db] = mfma32(a[db], pb[c], oacc[db]);
+    for (int n = 16; n < 32; ++n) {
+      if (n + AHEAD < 32) read(n + AHEAD);
+      const int c = (n - 16) >> 2, db = (n - 16) & 3;
+      oacc[db] = mfma32(opnd[n], pb[c], oacc[db]);
+      __builtin_amdgcn_sched_barrier(0);
     }
+  };
+
+  issue(0, 0);
+  for (int kt = 0; kt < n_kt; kt += 2) {
+    tile(std::integral_constant<uint32_t, 0>{}, kt);
+    if (kt + 1 < n_kt) tile(std::integral_constant<uint32_t, 1>{}, kt + 1);
   }
 
   const float l = lpart + __shfl_xor(lpart, 32, 64);
