@@ -222,10 +222,10 @@ __device__ __forceinline__ bf16x8 tr_operand(const uint32_t (&t)[2], uint32_t of
   return as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
 }
 
-// Per-lane source offset of the tile copy: wavefront w of a 256-thread
-// workgroup moves rows 4 (w + 4 m) .. + 3, m = 0..3, one 1-KB dma16 each
-// (lane i: 16 bytes of row + i / 16 into physical chunk i % 16).  rsb is the
-// byte stride between rows in HBM.
+// Per-lane source offset of the tile copy: wavefront w of a workgroup of NW
+// wavefronts moves rows 4 (w + NW m) .. + 3, m = 0 .. 16 / NW - 1, one 1-KB
+// dma16 each (lane i: 16 bytes of row + i / 16 into physical chunk i % 16).
+// rsb is the byte stride between rows in HBM.
 __device__ __forceinline__ uint32_t tile_copy_offset(int wave, int lane, uint32_t rsb) {
   const int drow = 4 * wave + (lane >> 4);
   return drow * rsb + 16 * ((lane & 15) ^ tile_swz(drow));
@@ -233,11 +233,14 @@ __device__ __forceinline__ uint32_t tile_copy_offset(int wave, int lane, uint32_
 
 // Copies this wavefront's share of a 64 x 128 tile: rows of the buffer
 // resource (rows past its end arrive as zeros) into the tile at LDS address
-// tile.
+// tile.  NW (4 or 8) wavefronts share the copy.
+template <int NW = 4>
 __device__ __forceinline__ void copy_tile(i32x4 rsrc, uint32_t voff, uint32_t rsb, uint32_t tile,
                                           int wave) {
+  static_assert(NW == 4 || NW == 8, "16 row groups split evenly");
 #pragma unroll
-  for (int m = 0; m < 4; ++m) dma16(rsrc, voff + 16 * m * rsb, tile + 1024 * wave + 4096 * m);
+  for (int m = 0; m < 16 / NW; ++m)
+    dma16(rsrc, voff + 4 * NW * m * rsb, tile + 1024 * (wave + NW * m));
 }
 
 // Maps workgroup index bid to a (batch*head, tile) pair.  The hardware hands

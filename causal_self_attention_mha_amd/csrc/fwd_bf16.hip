@@ -11,8 +11,9 @@
 //     in registers for the whole key loop;
 //   * K and V tiles of 64 keys are copied straight from HBM into
 //     double-buffered LDS (buffer loads with the LDS destination; keys past T
-//     arrive as zeros), the next tile's copy in flight while the current one
-//     is computed, one barrier per tile.  Both tiles keep their natural
+//     arrive as zeros), the next tile's copy issued after the current tile's
+//     score MFMAs and in flight during its softmax and PV; one barrier per
+//     tile.  Both tiles keep their natural
 //     row-major layout, swizzled (see tile_swz): K is read row-wise, V^T with
 //     the transposing ds_read_b64_tr_b16, both free of bank conflicts;
 //   * scores are computed transposed, S^T = K Q^T (v_mfma_f32_32x32x16_bf16),
@@ -39,7 +40,8 @@ namespace na {
 namespace {
 
 constexpr int D = kHeadDim;
-constexpr int BQ = 128;  // query rows per workgroup
+constexpr int NW = 4;             // wavefronts per workgroup (32 query rows each)
+constexpr int BQ = 32 * NW;       // query rows per workgroup
 constexpr int BK = 64;   // keys per LDS tile
 constexpr uint32_t BUF_B = 2 * kTileBytes;  // one buffer: K tile, then V tile
 // Lazy rescaling: the running max m is only raised (and O, l rescaled) when a
@@ -47,7 +49,7 @@ constexpr uint32_t BUF_B = 2 * kTileBytes;  // one buffer: K tile, then V tile
 // the rescale; probabilities then stay below 256, harmless in fp32 and bf16.
 constexpr float kRescaleLog2 = 8.0f;
 
-__global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const u16* __restrict__ q,
+__global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(const u16* __restrict__ q,
                                                           const u16* __restrict__ k,
                                                           const u16* __restrict__ v,
                                                           u16* __restrict__ o,
@@ -108,8 +110,9 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const u16* __restrict_
     const int k0 = kt * BK;
     const uint32_t nrec = static_cast<uint32_t>(T - k0) * rsb;
     const size_t off = base + static_cast<size_t>(k0) * rs;
-    copy_tile(buffer_rsrc(k + off, nrec), cvoff, rsb, kv_lds + buf * BUF_B, wave);
-    copy_tile(buffer_rsrc(v + off, nrec), cvoff, rsb, kv_lds + buf * BUF_B + kTileBytes, wave);
+    copy_tile<NW>(buffer_rsrc(k + off, nrec), cvoff, rsb, kv_lds + buf * BUF_B, wave);
+    copy_tile<NW>(buffer_rsrc(v + off, nrec), cvoff, rsb, kv_lds + buf * BUF_B + kTileBytes,
+                  wave);
   };
 
   // One key tile; BUF is the buffer it sits in (a compile-time constant, so
@@ -124,8 +127,13 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const u16* __restrict_
     // next copy may then overwrite.
     wait_vmem();
     __syncthreads();
-    if (kt + 1 < n_kt) issue(kt + 1, 1 - BUF);
-    if (k0 > qw0 + 31) return;  // whole tile above this wavefront's diagonal
+    const bool skip = k0 > qw0 + 31;  // whole tile above this wavefront's diagonal
+    // The copy of the next tile is issued once this tile's K reads are done
+    // (measured faster than issuing it at the barrier).
+    if (skip) {
+      if (kt + 1 < n_kt) issue(kt + 1, 1 - BUF);
+      return;
+    }
 
     // Operand sequence: 16 K operands, n = 2 kc + kb (the two score blocks
     // alternate, so consecutive MFMAs are independent), then 16 V^T operands,
@@ -153,6 +161,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const u16* __restrict_
       sacc[n & 1] = mfma32(opnd[n], qreg[n >> 1], sacc[n & 1]);
       __builtin_amdgcn_sched_barrier(0);
     }
+    if (kt + 1 < n_kt) issue(kt + 1, 1 - BUF);
 
     // causal select on tiles that cross the diagonal
     if (k0 + BK - 1 > qw0) {
@@ -239,7 +248,7 @@ hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o,
   const float c_log2 = scale * 1.4426950408889634f;
   const int n_qt = (T + BQ - 1) / BQ;
   const dim3 grid(static_cast<unsigned>(n_qt) * B * H);
-  return launch(fwd_bf16_kernel, grid, dim3(256), 0, s, static_cast<const u16*>(q),
+  return launch(fwd_bf16_kernel, grid, dim3(64 * NW), 0, s, static_cast<const u16*>(q),
                 static_cast<const u16*>(k), static_cast<const u16*>(v), static_cast<u16*>(o),
                 lse, B, T, H, c_log2, scale);
 }
