@@ -76,8 +76,8 @@ constexpr uint32_t BUF_B = 2 * TILE_B;        // one buffer: q tile, then dout t
 //   scores:  S = Q K^T, dP = dout V^T   (A = Q / dout rows from LDS, B = K / V
 //            in registers; lane: key, element r: query acc_row(lane, r))
 //   probs:   P = exp2(c S - lse log2 e), dS = P (dP - delta), rounded to bf16
-//   accum:   dV += P^T dout, dK += dS^T Q  (A = P^T / dS^T from registers,
-//            B = query tiles read transposed)
+//   accum:   dV^T += dout^T P, dK^T += Q^T dS  (A = query tiles read
+//            transposed, B = P / dS from registers; lane: key, element r: d)
 // The steady-state loop overlaps the scores MFMAs of block j+1 with the probs
 // VALU work of block j.  qtile is the LDS byte address of a buffer's q tile
 // (its dout tile follows at + TILE_B).
@@ -142,8 +142,8 @@ __device__ __forceinline__ void dkdv_accum(const bf16x8 (&pb)[2], const bf16x8 (
     }
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
-      dva[db] = mfma32(pb[j], bg[db], dva[db]);
-      dka[db] = mfma32(sb[j], bq[db], dka[db]);
+      dva[db] = mfma32(bg[db], pb[j], dva[db]);
+      dka[db] = mfma32(bq[db], sb[j], dka[db]);
     }
   }
 }
@@ -179,10 +179,11 @@ __device__ __forceinline__ void dkdv_block(const TileAddr& ta, const float* lse_
 // Steady-state step: probabilities of the current block (held in s_cur,
 // p_cur), scores of the next block into s_nxt, p_nxt, then the current
 // block's dK/dV accumulation.  The order is fixed by hand in eight rounds,
-// separated by scheduling fences: each round issues the LDS reads two rounds
-// ahead, one score MFMA for S and one for dP, and the probability math of two
-// of this lane's sixteen (key, query) elements, so the VALU work runs while
-// the matrix cores are busy.  na/rowN locate the next block (row-wise reads of
+// separated by scheduling fences: each round issues the LDS reads (operands,
+// lse and delta) two rounds ahead, one score MFMA for S and one for dP, and
+// the probability math of two of this lane's sixteen (key, query) elements,
+// so the VALU work runs while the matrix cores are busy; the last four rounds
+// also read the transposed operands of the first accumulation chunk.  na/rowN locate the next block (row-wise reads of
 // its tile), ta/rowC the current one (transposed reads).
 __device__ __forceinline__ void dkdv_step(const uint32_t (&na)[8], int rowN, const float* lse_t,
                                           const float* dl_t, const uint32_t (&ta)[4][2],
@@ -193,41 +194,39 @@ __device__ __forceinline__ void dkdv_step(const uint32_t (&na)[8], int rowN, con
                                           float c_log2, u16* ds_blk) {
   const int half = lane >> 5;
   const uint32_t rn = rowN * 256;
-  // element r of the current block: query row r0 + 16 (r/8) + r%8
+  const uint32_t rc = rowC * 256;
+  // element r of the current block: query row r0 + 16 (r/8) + r%8; round i
+  // handles elements 2i, 2i+1 (rows rr(i), rr(i) + 1)
   const int r0 = rowC + 8 * half;
-  float l16[16], d16[16];
-#pragma unroll
-  for (int j = 0; j < 2; ++j)
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const float4 a = *reinterpret_cast<const float4*>(&lse_t[r0 + 16 * j + 4 * k]);
-      const float4 d = *reinterpret_cast<const float4*>(&dl_t[r0 + 16 * j + 4 * k]);
-      l16[8 * j + 4 * k] = a.x; l16[8 * j + 4 * k + 1] = a.y;
-      l16[8 * j + 4 * k + 2] = a.z; l16[8 * j + 4 * k + 3] = a.w;
-      d16[8 * j + 4 * k] = d.x; d16[8 * j + 4 * k + 1] = d.y;
-      d16[8 * j + 4 * k + 2] = d.z; d16[8 * j + 4 * k + 3] = d.w;
-    }
+  auto rr = [&](int i) { return r0 + 16 * (i >> 2) + 2 * (i & 3); };
   bf16x8 aq[8], ag[8];
-  aq[0] = as_bf16x8(lds_ld16(na[0] + rn));
-  ag[0] = as_bf16x8(lds_ld16(na[0] + rn + TILE_B));
-  aq[1] = as_bf16x8(lds_ld16(na[1] + rn));
-  ag[1] = as_bf16x8(lds_ld16(na[1] + rn + TILE_B));
+  float2 lr[8], dr[8];
+  bf16x8 bg[2][4], bq[2][4];
+  auto reads = [&](int i) {
+    aq[i] = as_bf16x8(lds_ld16(na[i] + rn));
+    ag[i] = as_bf16x8(lds_ld16(na[i] + rn + TILE_B));
+    lr[i] = *reinterpret_cast<const float2*>(&lse_t[rr(i)]);
+    dr[i] = *reinterpret_cast<const float2*>(&dl_t[rr(i)]);
+  };
+  reads(0);
+  reads(1);
   s_nxt = f32x16{};
   p_nxt = f32x16{};
   uint32_t pw[8], sw[8];  // bf16 pairs (elements 2i, 2i+1)
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    if (i + 2 < 8) {
-      aq[i + 2] = as_bf16x8(lds_ld16(na[i + 2] + rn));
-      ag[i + 2] = as_bf16x8(lds_ld16(na[i + 2] + rn + TILE_B));
+    if (i + 2 < 8) reads(i + 2);
+    if (i >= 4) {  // transposed operands of the first accumulation chunk
+      bg[0][i - 4] = tr_operand(ta[i - 4], rc + TILE_B);
+      bq[0][i - 4] = tr_operand(ta[i - 4], rc);
     }
     s_nxt = mfma32(aq[i], kreg[i], s_nxt);
     const int r = 2 * i;
-    const float p0 = fast_exp2(fmaf(s_cur[r], c_log2, l16[r] * -kLog2e));
-    const float p1 = fast_exp2(fmaf(s_cur[r + 1], c_log2, l16[r + 1] * -kLog2e));
+    const float p0 = fast_exp2(fmaf(s_cur[r], c_log2, lr[i].x * -kLog2e));
+    const float p1 = fast_exp2(fmaf(s_cur[r + 1], c_log2, lr[i].y * -kLog2e));
     pw[i] = pack_bf16x2(p0, p1);
-    sw[i] = pack_bf16x2(p0 * (p_cur[r] - d16[r]), p1 * (p_cur[r + 1] - d16[r + 1]));
+    sw[i] = pack_bf16x2(p0 * (p_cur[r] - dr[i].x), p1 * (p_cur[r + 1] - dr[i].y));
     // keep this round's VALU work in this round (no sinking to the first use)
     asm volatile("" : "+v"(pw[i]), "+v"(sw[i]));
     p_nxt = mfma32(ag[i], vreg[i], p_nxt);
@@ -238,16 +237,8 @@ __device__ __forceinline__ void dkdv_step(const uint32_t (&na)[8], int rowN, con
   const bf16x8 sb[2] = {as_bf16x8(make_uint4(sw[0], sw[1], sw[2], sw[3])),
                         as_bf16x8(make_uint4(sw[4], sw[5], sw[6], sw[7]))};
   if (ds_blk) store_ds(ds_blk, sb, lane);
-  // dV += P^T dout, dK += dS^T Q for the current block: operands of chunk j+1
-  // are read while chunk j's MFMAs run
-  bf16x8 bg[2][4], bq[2][4];
-  const uint32_t rc = rowC * 256;
-#pragma unroll
-  for (int db = 0; db < 4; ++db) {
-    bg[0][db] = tr_operand(ta[db], rc + TILE_B);
-    bq[0][db] = tr_operand(ta[db], rc);
-  }
-  __builtin_amdgcn_sched_barrier(0);
+  // dV += P^T dout, dK += dS^T Q for the current block: operands of chunk 1
+  // are read while chunk 0's MFMAs run
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     if (j == 0) {
@@ -259,8 +250,8 @@ __device__ __forceinline__ void dkdv_step(const uint32_t (&na)[8], int rowN, con
     }
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
-      dva[db] = mfma32(pb[j], bg[j][db], dva[db]);
-      dka[db] = mfma32(sb[j], bq[j][db], dka[db]);
+      dva[db] = mfma32(bg[j][db], pb[j], dva[db]);
+      dka[db] = mfma32(bq[j][db], sb[j], dka[db]);
     }
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -284,7 +275,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(
   const int BH = B * H;
   const int n_ktiles = (T + KT_KEYS - 1) / KT_KEYS;
   int bh, kt;  // key tile 0 has the most work: first
-  xcd_tile_map(static_cast<int>(blockIdx.x), BH, n_ktiles, bh, kt);
+  xcd_tile_map_grouped(static_cast<int>(blockIdx.x), BH, n_ktiles, 8, bh, kt);
   const int b = bh / H, h = bh % H;
   const int k0 = kt * KT_KEYS;
   const int kw0 = k0 + 32 * wave;
@@ -427,18 +418,24 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(
     }
   }
 
-  // dka[db], dva[db] element r: key kw0 + 8 (r/4) + 4 half + r%4, d = 32 db + l32
+  // dka[db], dva[db] (dK^T, dV^T blocks) element r: key krow = kw0 + l32,
+  // d = 32 db + 8 (r/4) + 4 half + r%4: four consecutive d per 8-byte store
+  if (krow < T) {
+    u16* kp = dk + base + krow * rs + 4 * half;
+    u16* vp = dv + base + krow * rs + 4 * half;
 #pragma unroll
-  for (int db = 0; db < 4; ++db)
+    for (int db = 0; db < 4; ++db)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int key = kw0 + 8 * (r >> 2) + 4 * half + (r & 3);
-      if (key < T) {
-        const size_t off = base + key * rs + 32 * db + l32;
-        dk[off] = __builtin_bit_cast(u16, to_bf16(dka[db][r] * scale));
-        dv[off] = __builtin_bit_cast(u16, to_bf16(dva[db][r]));
+      for (int g = 0; g < 4; ++g) {
+        const int r = 4 * g;
+        *reinterpret_cast<uint2*>(kp + 32 * db + 8 * g) =
+            make_uint2(pack_bf16x2(dka[db][r] * scale, dka[db][r + 1] * scale),
+                       pack_bf16x2(dka[db][r + 2] * scale, dka[db][r + 3] * scale));
+        *reinterpret_cast<uint2*>(vp + 32 * db + 8 * g) =
+            make_uint2(pack_bf16x2(dva[db][r], dva[db][r + 1]),
+                       pack_bf16x2(dva[db][r + 2], dva[db][r + 3]));
       }
-    }
+  }
 }
 
 // ---------------------------------------------------------------- dQ

@@ -293,4 +293,28 @@ __device__ __forceinline__ void tstore_4x8(u16* tile, const uint4 (&x)[4], int l
   }
 }
 
+// Like xcd_tile_map, but within each XCD the heads are taken in groups of up
+// to G and a group's tiles are ordered tile-major (tile 0 of every head of
+// the group, then tile 1, ...).  With tile 0 the heaviest, the hardware's
+// in-order dispatch then starts the heaviest tiles of a group first across
+// the XCD's compute units (a longest-first list schedule), so the last group
+// ends without a long tail; a group's rows still fit the XCD's L2 and the
+// shared last-level cache.
+__device__ __forceinline__ void xcd_tile_map_grouped(int bid, int BH, int n_tiles, int G, int& bh,
+                                                     int& t) {
+  constexpr int kXcds = 8;
+  if (BH % kXcds != 0) {
+    bh = bid % BH;
+    t = bid / BH;
+    return;
+  }
+  const int x = bid % kXcds, w = bid / kXcds;
+  const int hpx = BH / kXcds;  // heads per XCD
+  const int grp = w / (G * n_tiles);
+  const int gsz = min(G, hpx - grp * G);
+  const int i = w - grp * G * n_tiles;
+  t = i / gsz;
+  bh = x + kXcds * (grp * G + i % gsz);
+}
+
 }  // namespace na
