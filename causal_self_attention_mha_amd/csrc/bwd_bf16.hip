@@ -275,7 +275,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(
   const int BH = B * H;
   const int n_ktiles = (T + KT_KEYS - 1) / KT_KEYS;
   int bh, kt;  // key tile 0 has the most work: first
-  xcd_tile_map_grouped(static_cast<int>(blockIdx.x), BH, n_ktiles, 8, bh, kt);
+  xcd_tile_map_grouped(static_cast<int>(blockIdx.x), BH, n_ktiles, kHeadGroup, bh, kt);
   const int b = bh / H, h = bh % H;
   const int k0 = kt * KT_KEYS;
   const int kw0 = k0 + 32 * wave;
@@ -558,7 +558,7 @@ __global__ __launch_bounds__(256, 1) void dq_kernel(
   const int BH = B * H;
   const int n_qt = (T + DQ_ROWS - 1) / DQ_ROWS;
   int bh, t;
-  xcd_tile_map(static_cast<int>(blockIdx.x), BH, n_qt, bh, t);
+  xcd_tile_map_grouped(static_cast<int>(blockIdx.x), BH, n_qt, kHeadGroup, bh, t);
   const int qt = n_qt - 1 - t;  // heaviest (last) query tile first
   const int b = bh / H, h = bh % H;
   const int q0 = qt * DQ_ROWS;
@@ -719,7 +719,7 @@ __global__ __launch_bounds__(256, 2) void dq_gemm_kernel(const u16* __restrict__
   const int BH = B * H;
   const int n_qt = (T + DG_ROWS - 1) / DG_ROWS;
   int bh, t;
-  xcd_tile_map(static_cast<int>(blockIdx.x), BH, n_qt, bh, t);
+  xcd_tile_map_grouped(static_cast<int>(blockIdx.x), BH, n_qt, kHeadGroup, bh, t);
   const int qt = n_qt - 1 - t;  // heaviest (last) query tile first
   const int b = bh / H, h = bh % H;
   const int q0 = qt * DG_ROWS;

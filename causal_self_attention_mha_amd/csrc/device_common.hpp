@@ -243,22 +243,36 @@ __device__ __forceinline__ void copy_tile(i32x4 rsrc, uint32_t voff, uint32_t rs
     dma16(rsrc, voff + 4 * NW * m * rsb, tile + 1024 * (wave + NW * m));
 }
 
-// Maps workgroup index bid to a (batch*head, tile) pair.  The hardware hands
-// workgroup i to XCD i % 8, and each XCD has its own L2; this order makes the
-// workgroups of one XCD cover one head's tiles back to back (tile 0 first,
-// which callers make the heaviest), so the K/V (or Q/dout) rows that all
-// tiles of a head share stay in that XCD's L2.  Falls back to head-fastest
-// order when the head count is not a multiple of 8.
-__device__ __forceinline__ void xcd_tile_map(int bid, int BH, int n_tiles, int& bh, int& t) {
+// Workgroup order.  The hardware hands workgroup i to XCD i % 8, and each XCD
+// has its own L2; the maps below make the workgroups of one XCD cover a few
+// heads' tiles close together in time, so the rows that all tiles of a head
+// share stay in that XCD's L2.  (Falls back to head-fastest order when the
+// head count is not a multiple of 8.)
+//
+// xcd_tile_map_grouped maps workgroup index bid to a (batch*head, tile) pair:
+// within each XCD the heads are taken in groups of up to G and a group's tiles
+// are ordered tile-major (tile 0 of every head of the group, then tile 1,
+// ...).  With tile 0 the heaviest, the hardware's in-order dispatch then
+// starts the heaviest tiles of a group first across the XCD's compute units (a
+// longest-first list schedule), so the last group ends without a long tail; a
+// group's rows still fit the XCD's L2 and the shared last-level cache.
+constexpr int kHeadGroup = 4;  // heads per group (measured best for the d12..d26 shapes)
+
+__device__ __forceinline__ void xcd_tile_map_grouped(int bid, int BH, int n_tiles, int G, int& bh,
+                                                     int& t) {
   constexpr int kXcds = 8;
-  if (BH % kXcds == 0) {
-    const int x = bid % kXcds, w = bid / kXcds;
-    bh = x + kXcds * (w / n_tiles);
-    t = w % n_tiles;
-  } else {
+  if (BH % kXcds != 0) {
     bh = bid % BH;
     t = bid / BH;
+    return;
   }
+  const int x = bid % kXcds, w = bid / kXcds;
+  const int hpx = BH / kXcds;  // heads per XCD
+  const int grp = w / (G * n_tiles);
+  const int gsz = min(G, hpx - grp * G);
+  const int i = w - grp * G * n_tiles;
+  t = i / gsz;
+  bh = x + kXcds * (grp * G + i % gsz);
 }
 
 // ---------------------------------------------------------------------------
@@ -291,30 +305,6 @@ __device__ __forceinline__ void tstore_4x8(u16* tile, const uint4 (&x)[4], int l
     const int d = 8 * lchunk + el;
     *reinterpret_cast<uint2*>(&tile[toff(d, lrow >> 1) + 4 * (lrow & 1)]) = make_uint2(a, b);
   }
-}
-
-// Like xcd_tile_map, but within each XCD the heads are taken in groups of up
-// to G and a group's tiles are ordered tile-major (tile 0 of every head of
-// the group, then tile 1, ...).  With tile 0 the heaviest, the hardware's
-// in-order dispatch then starts the heaviest tiles of a group first across
-// the XCD's compute units (a longest-first list schedule), so the last group
-// ends without a long tail; a group's rows still fit the XCD's L2 and the
-// shared last-level cache.
-__device__ __forceinline__ void xcd_tile_map_grouped(int bid, int BH, int n_tiles, int G, int& bh,
-                                                     int& t) {
-  constexpr int kXcds = 8;
-  if (BH % kXcds != 0) {
-    bh = bid % BH;
-    t = bid / BH;
-    return;
-  }
-  const int x = bid % kXcds, w = bid / kXcds;
-  const int hpx = BH / kXcds;  // heads per XCD
-  const int grp = w / (G * n_tiles);
-  const int gsz = min(G, hpx - grp * G);
-  const int i = w - grp * G * n_tiles;
-  t = i / gsz;
-  bh = x + kXcds * (grp * G + i % gsz);
 }
 
 }  // namespace na

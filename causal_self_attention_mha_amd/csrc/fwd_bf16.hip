@@ -67,7 +67,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(const u16* __
   const int BH = B * H;
   const int n_qt = (T + BQ - 1) / BQ;
   int bh, t;
-  xcd_tile_map(static_cast<int>(blockIdx.x), BH, n_qt, bh, t);
+  xcd_tile_map_grouped(static_cast<int>(blockIdx.x), BH, n_qt, kHeadGroup, bh, t);
   const int qt = n_qt - 1 - t;  // heaviest (last) query tile first
   const int b = bh / H, h = bh % H;
   const int q0 = qt * BQ;
