@@ -108,11 +108,15 @@ def train_flops(B, T, H, D):
 
 
 def train_bytes(B, T, H, D):
-    """Minimum HBM bytes per launch: every input read once, every output written once."""
+    """Minimum HBM bytes per launch: every input read once, every output written
+    once.  The backward runs with the dS workspace: dkdv also writes dS (bf16,
+    lower-triangular 32 x 32 blocks per head) and dq reads it with K."""
     t = B * T * H * D * 2          # one bf16 (B, T, H, D) tensor
     r = B * H * T * 4              # one fp32 (B, H, T) row vector
-    return {"fwd": 3 * t + t + r, "delta": 2 * t + r, "dkdv": 4 * t + 2 * r + 2 * t,
-            "dq": 4 * t + 2 * r + t}
+    nblk = (T + 31) // 32
+    ds = B * H * nblk * (nblk + 1) // 2 * 32 * 32 * 2
+    return {"fwd": 3 * t + t + r, "delta": 2 * t + r, "dkdv": 4 * t + 2 * r + 2 * t + ds,
+            "dq": t + ds + t}
 
 
 def cpu_baseline(inp, n_heads):

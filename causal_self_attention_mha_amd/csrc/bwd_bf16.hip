@@ -10,12 +10,16 @@
 // section 5 "Flash Attention integration").
 //
 // Three kernels on one stream:
-//   delta_kernel  rowsum(dout * o)                        (HBM bound)
-//   dkdv_kernel   one workgroup per 128-key tile; K and V stay in registers
-//                 as MFMA operands, query tiles of 64 stream through LDS in
-//                 both row-major and transposed copies; accumulates dK, dV
-//   dq_kernel     one workgroup per 128-query tile; Q, dout stay in registers,
-//                 key tiles of 64 stream through LDS; accumulates dQ
+//   delta_kernel    rowsum(dout * o)                      (HBM bound)
+//   dkdv_kernel     one workgroup per 128-key tile; K and V stay in registers
+//                   as MFMA operands, query tiles of 64 are copied HBM -> LDS
+//                   (triple-buffered, read row-wise and transposed);
+//                   accumulates dK, dV and, given a workspace, stores dS
+//   dq_gemm_kernel  with the dS workspace: one workgroup per 128-query tile,
+//                   dQ = s dS K over the stored blocks
+//   dq_kernel       without it: one workgroup per 128-query tile; Q, dout stay
+//                   in registers, key tiles of 64 stream through LDS, S and dP
+//                   are recomputed; accumulates dQ
 // P and dS are rounded to bf16 before they enter an MFMA; everything else is
 // fp32.  Each output element is written by exactly one lane, so results are
 // bitwise deterministic.
