@@ -23,6 +23,8 @@
 // P and dS are rounded to bf16 before they enter an MFMA; everything else is
 // fp32.  Each output element is written by exactly one lane, so results are
 // bitwise deterministic.
+#include <type_traits>
+
 #include "device_common.hpp"
 #include "internal.hpp"
 
@@ -689,28 +691,27 @@ __global__ __launch_bounds__(256, 1) void dq_kernel(
 // With a dS workspace the dK/dV kernel keeps dS (bf16, 32 x 32 blocks), and
 // dQ = s dS K is a plain GEMM over the lower-triangular blocks instead of a
 // pass that recomputes S and dP.  Per wavefront (32 queries) and 32-key block:
-//   dQ^T += K^T dS^T   (A = transposed K tile from LDS, B = dS^T)
-// The B operand needs lane = query, eight consecutive keys, while the stored
-// block is [key][query]; each wavefront stages its block in LDS and reads it
-// with ds_read_b64_tr_b16, which within each 16-lane group gives lane j
-// element j&3 of the four-element rows supplied by lanes 4e + (j>>2): lanes
-// supplying rows key0 + i/4 at columns 4 (i%4) leave lane j with the column
-// query0 + j of keys key0 .. key0 + 3.
+//   dQ^T += K^T dS^T   (A = K tile read transposed, B = dS^T)
+// Both operands need eight consecutive keys per lane: K^T comes from the
+// swizzled K tile with ds_read_b64_tr_b16 (as V^T in the forward), and dS^T
+// from the stored [key][query] block, copied as is into LDS and read with the
+// same transposing instruction (lanes supplying rows key0 + i/4 at columns
+// 4 (i%4) leave lane j with column query0 + j of keys key0 .. key0 + 3).  K
+// tiles (by the whole workgroup) and each wavefront's dS blocks (by that
+// wavefront) are copied HBM -> LDS by DMA, one barrier per key tile.  The dS
+// stream is the HBM-bound part (about B*H*T^2 bytes against a few hundred
+// cycles of MFMA per block), so its copies run two tiles ahead (three
+// buffers); K tiles, mostly L2 hits, run one ahead (two buffers).
 constexpr int DG_ROWS = 128;  // queries per workgroup (32 per wavefront)
 constexpr int DG_KEYS = 64;   // keys per K tile
-
-__device__ __forceinline__ uint2 ds_read_tr16(const u16* lds) {
-  const lds_i16x4* p =
-      (const lds_i16x4*)((__attribute__((address_space(3))) const u16*)lds);  // NOLINT
-  return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p));
-}
+constexpr uint32_t DG_DS_B = 2 * 32 * 32 * 2;  // a wavefront's two dS blocks per key tile
 
 __global__ __launch_bounds__(256, 2) void dq_gemm_kernel(const u16* __restrict__ k,
                                                          const u16* __restrict__ dsw,
                                                          u16* __restrict__ dq, int nbt, int B,
                                                          int T, int H, float scale) {
-  __shared__ __attribute__((aligned(16))) u16 Kt[2][D * DG_KEYS];  // transposed, swizzled
-  __shared__ __attribute__((aligned(16))) u16 Sst[4][2][32 * 32];  // per-wavefront dS staging
+  __shared__ __attribute__((aligned(1024))) char ktile[2][kTileBytes];   // swizzled K
+  __shared__ __attribute__((aligned(1024))) char sst[3][4][DG_DS_B];     // dS blocks per wave
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -732,7 +733,8 @@ __global__ __launch_bounds__(256, 2) void dq_gemm_kernel(const u16* __restrict__
   const bool live = qw0 < T;  // wavefront has at least one real query row
   const int rs = H * D;
   const size_t base = static_cast<size_t>(b) * T * rs + static_cast<size_t>(h) * D;
-  const u16* dsh = dsw + ds_block_index(bh, nbt, 0, 0);
+  // this wavefront's row of dS blocks: (qblk, 0 .. qblk), 2 KiB each, contiguous
+  const u16* dsrow = dsw + ds_block_index(bh, nbt, qblk, 0);
 
   f32x16 dqa[4];
 #pragma unroll
@@ -740,67 +742,96 @@ __global__ __launch_bounds__(256, 2) void dq_gemm_kernel(const u16* __restrict__
 
   const int last_q = min(q0 + DG_ROWS, T) - 1;
   const int n_kt = last_q / DG_KEYS + 1;
-  const int lrow = tid >> 4;
-  const int lchunk = tid & 15;
-  uint4 xk[4];
-  auto kload = [&](int kt) {  // key rows past T read row T-1: their dS is 0
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      xk[i] = ld16(k + base + min(kt * DG_KEYS + 4 * lrow + i, T - 1) * rs + 8 * lchunk);
+
+  // K^T read addresses in buffer 0 (buffer 1: + kTileBytes)
+  uint32_t ktr[4][2];
+  {
+    const TileOffsets ofs = tile_operand_offsets(lane);
+    tr_addr(lds_addr(ktile), ofs, ktr);
+  }
+  // dS^T reads: 16-lane group gi supplies keys 16 c + 8 half + 4 sub + i16 / 4,
+  // queries 16 (gi & 1) + 4 (i16 & 3) of a block stored [key][query]
+  const uint32_t st_lds = lds_addr(&sst[0][wave][0]);
+  const uint32_t st_off =
+      ((8 * half + (i16 >> 2)) * 32 + 16 * (gi & 1) + 4 * (i16 & 3)) * 2;
+  const uint32_t rsb = static_cast<uint32_t>(rs) * 2;
+  const uint32_t kvoff = tile_copy_offset(wave, lane, rsb);
+  const uint32_t kt_lds = lds_addr(ktile);
+  // the wavefront's blocks of key tile kt: kblk = 2 kt, 2 kt + 1 (if <= qblk)
+  const uint32_t ds_rows = static_cast<uint32_t>(qblk + 1) * 2048;  // bytes of its row
+  const i32x4 ds_rsrc = buffer_rsrc(dsrow, live ? ds_rows : 0);
+  // Copy j (0..3) of this wavefront's share of K tile kt / of its dS blocks
+  // of key tile kt.  The copies of the next tiles are spread between the
+  // current tile's MFMAs: issued in a burst they stall the issuing wavefront
+  // behind the compute unit's vector-memory queue.
+  auto issue_k = [&](int kt, int buf, int j) {
+    const int k0 = kt * DG_KEYS;
+    const uint32_t nrec = static_cast<uint32_t>(T - k0) * rsb;  // keys past T read as 0
+    dma16(buffer_rsrc(k + base + static_cast<size_t>(k0) * rs, nrec), kvoff + 16 * j * rsb,
+          kt_lds + buf * kTileBytes + 1024 * wave + 4096 * j);
   };
-  // this wavefront's two dS blocks of key tile kt (32 bytes per lane each)
-  uint4 xs[2][2];
-  auto sload = [&](int kt) {
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const int kblk = 2 * kt + kb;
-      if (live && kblk <= qblk) {
-        const u16* p = dsh + (static_cast<size_t>(qblk) * (qblk + 1) / 2 + kblk) * 1024 + 16 * lane;
-        xs[kb][0] = ld16(p);
-        xs[kb][1] = ld16(p + 8);
-      }
-    }
+  auto issue_ds = [&](int kt, int sbuf, int j) {
+    // blocks past qblk are past the resource's end (zeros, never read)
+    dma16(ds_rsrc, kt * 4096 + j * 1024 + 16 * lane, st_lds + sbuf * (4 * DG_DS_B) + j * 1024);
   };
 
-  kload(0);
-  sload(0);
-  for (int kt = 0; kt < n_kt; ++kt) {
-    const int buf = kt & 1;
-    tstore_4x8(Kt[buf], xk, lrow, lchunk);
-    __syncthreads();  // publishes `buf`; frees buf^1 (see the forward kernel)
-    uint4 cur[2][2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      cur[kb][0] = xs[kb][0];
-      cur[kb][1] = xs[kb][1];
-    }
-    if (kt + 1 < n_kt) {
-      kload(kt + 1);
-      sload(kt + 1);
-    }
+  // Copies in issue order: K(0), dS(0), dS(1), then per tile t: K(t+1),
+  // dS(t+2).  At tile t, K(t) and dS(t) must have landed while dS(t+1) (the
+  // last 4 copies issued, if it exists) may still be in flight.
+  auto tile = [&](auto bufc, int kt) {
+    constexpr uint32_t BUF = decltype(bufc)::value;
+    const int sb = kt % 3;
+    if (kt + 1 < n_kt)
+      wait_vmem_but<4>();
+    else
+      wait_vmem();
+    __syncthreads();
+    const bool more_k = kt + 1 < n_kt, more_ds = kt + 2 < n_kt;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const int kblk = 2 * kt + kb;
-      if (!live || kblk > qblk) continue;  // wavefront-uniform
-      u16* st = Sst[wave][kb];
-      st16(st + 16 * lane, cur[kb][0]);
-      st16(st + 16 * lane + 8, cur[kb][1]);
+      const bool act = live && kblk <= qblk;  // wavefront-uniform
+      const uint32_t st = st_lds + sb * (4 * DG_DS_B) + kb * 2048 + st_off;
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-        // keys 16 c + 8 half + 4 r + 0..3 of column (query) l32
-        const int row = 16 * c + 8 * half + (i16 >> 2);
-        const int col = 16 * (gi & 1) + 4 * (i16 & 3);
-        const uint2 r0 = ds_read_tr16(st + row * 32 + col);
-        const uint2 r1 = ds_read_tr16(st + (row + 4) * 32 + col);
+        // all of K(kt+1) before any of dS(kt+2): the wait above relies on
+        // dS(kt+1)'s copies being the last four issued
+        const int j = 2 * kb + c;
+        if (j < 2) {
+          if (more_k) {
+            issue_k(kt + 1, 1 - BUF, 2 * j);
+            issue_k(kt + 1, 1 - BUF, 2 * j + 1);
+          }
+        } else if (more_ds) {
+          issue_ds(kt + 2, (kt + 2) % 3, 2 * (j - 2));
+          issue_ds(kt + 2, (kt + 2) % 3, 2 * (j - 2) + 1);
+        }
+        if (!act) continue;
+        // keys 32 kb + 16 c + 8 half + 0..7 (of this tile), query column l32
+        const uint2 r0 = ds_read_tr16_at(st + c * 16 * 64);
+        const uint2 r1 = ds_read_tr16_at(st + c * 16 * 64 + 4 * 64);
         const bf16x8 bs = as_bf16x8(make_uint4(r0.x, r0.y, r1.x, r1.y));
         bf16x8 a[4];
 #pragma unroll
         for (int db = 0; db < 4; ++db)
-          a[db] = as_bf16x8(ld16(&Kt[buf][toff(db * 32 + l32, 4 * kb + 2 * c + half)]));
+          a[db] = tr_operand(ktr[db], BUF * kTileBytes + (32 * kb + 16 * c) * 256);
 #pragma unroll
         for (int db = 0; db < 4; ++db) dqa[db] = mfma32(a[db], bs, dqa[db]);
       }
     }
+  };
+
+#pragma unroll
+  for (int j = 0; j < 4; ++j) issue_k(0, 0, j);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) issue_ds(0, 0, j);
+  if (n_kt > 1) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) issue_ds(1, 1, j);
+  }
+  for (int kt = 0; kt < n_kt; kt += 2) {
+    tile(std::integral_constant<uint32_t, 0>{}, kt);
+    if (kt + 1 < n_kt) tile(std::integral_constant<uint32_t, 1>{}, kt + 1);
   }
 
   const int qrow = qw0 + l32;

@@ -109,22 +109,35 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // buffer into LDS at lds + 16 i (lds + 4 i).  lds must be wave-uniform.  The
 // copy is asynchronous and tracked by vmcnt alone: the compiler does not know
 // about it, so callers order it with wait_vmem() and a barrier.
+// The resource must be wave-uniform; readfirstlane states that to the compiler
+// (and is free when it already sits in scalar registers).
+__device__ __forceinline__ i32x4 uniform_rsrc(i32x4 r) {
+  return i32x4{__builtin_amdgcn_readfirstlane(r[0]), __builtin_amdgcn_readfirstlane(r[1]),
+               __builtin_amdgcn_readfirstlane(r[2]), __builtin_amdgcn_readfirstlane(r[3])};
+}
+
 __device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t voff, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
                :
-               : "v"(voff), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(lds))
+               : "v"(voff), "s"(uniform_rsrc(rsrc)), "s"(__builtin_amdgcn_readfirstlane(lds))
                : "memory");
 }
 __device__ __forceinline__ void dma4(i32x4 rsrc, uint32_t voff, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds"
                :
-               : "v"(voff), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(lds))
+               : "v"(voff), "s"(uniform_rsrc(rsrc)), "s"(__builtin_amdgcn_readfirstlane(lds))
                : "memory");
 }
 
 // Waits until every vector memory operation of this wavefront has completed
 // (DMA copies landed in LDS, global stores acknowledged).
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// ... all but the N most recently issued ones (they complete in issue order).
+template <int N>
+__device__ __forceinline__ void wait_vmem_but() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 
 // Transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
 // lane j receives element j % 4 of the 4-element (8-byte) rows supplied by
