@@ -424,23 +424,35 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(
     }
   }
 
-  // dka[db], dva[db] (dK^T, dV^T blocks) element r: key krow = kw0 + l32,
-  // d = 32 db + 8 (r/4) + 4 half + r%4: four consecutive d per 8-byte store
-  if (krow < T) {
-    u16* kp = dk + base + krow * rs + 4 * half;
-    u16* vp = dv + base + krow * rs + 4 * half;
+  // dka[db], dva[db] (dK^T, dV^T blocks) element r: key kw0 + l32,
+  // d = 32 db + 8 (r/4) + 4 half + r%4.  The rows leave through LDS so that 16
+  // lanes store one 256-byte row: stored straight from registers, every lane
+  // would write 8 bytes to a different row.  Staging rows are swizzled by
+  // 16-byte chunk (chunk c of row r at c ^ (r mod 16)).
+  __syncthreads();  // every wavefront is done with the query tiles
+  const uint32_t stg = qt_lds + wave * 16384;  // 32 dK rows, then 32 dV rows
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+  for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int r = 4 * g;
-        *reinterpret_cast<uint2*>(kp + 32 * db + 8 * g) =
-            make_uint2(pack_bf16x2(dka[db][r] * scale, dka[db][r + 1] * scale),
-                       pack_bf16x2(dka[db][r + 2] * scale, dka[db][r + 3] * scale));
-        *reinterpret_cast<uint2*>(vp + 32 * db + 8 * g) =
-            make_uint2(pack_bf16x2(dva[db][r], dva[db][r + 1]),
-                       pack_bf16x2(dva[db][r + 2], dva[db][r + 3]));
-      }
+    for (int g = 0; g < 4; ++g) {
+      const int r = 4 * g;
+      const uint32_t off = l32 * 256 + 16 * ((4 * db + g) ^ (l32 & 15)) + 8 * half;
+      lds_st8(stg + off, pack_bf16x2(dka[db][r] * scale, dka[db][r + 1] * scale),
+              pack_bf16x2(dka[db][r + 2] * scale, dka[db][r + 3] * scale));
+      lds_st8(stg + 8192 + off, pack_bf16x2(dva[db][r], dva[db][r + 1]),
+              pack_bf16x2(dva[db][r + 2], dva[db][r + 3]));
+    }
+  // lane i copies chunk i % 16 of rows 4 m + i / 16
+#pragma unroll
+  for (int m = 0; m < 8; ++m) {
+    const int r = 4 * m + (lane >> 4), c = lane & 15;
+    const uint32_t off = r * 256 + 16 * (c ^ (r & 15));
+    const uint4 xk = lds_ld16(stg + off);
+    const uint4 xv = lds_ld16(stg + 8192 + off);
+    if (kw0 + r < T) {
+      st16(dk + base + (kw0 + r) * rs + 8 * c, xk);
+      st16(dv + base + (kw0 + r) * rs + 8 * c, xv);
+    }
   }
 }
 

@@ -150,6 +150,12 @@ __device__ __forceinline__ uint2 ds_read_tr16_at(uint32_t lds) {
       uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<lds_i16x4*>(lds)));
 }
 
+// Eight-byte LDS write at an LDS byte address.
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void lds_st8(uint32_t lds, uint32_t lo, uint32_t hi) {
+  *reinterpret_cast<__attribute__((address_space(3))) u32x2*>(lds) = u32x2{lo, hi};
+}
+
 // Sixteen-byte LDS read at an LDS byte address.
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ uint4 lds_ld16(uint32_t lds) {
