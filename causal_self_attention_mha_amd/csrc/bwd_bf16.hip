@@ -290,18 +290,10 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(
   const float* lse_bh = lse + static_cast<size_t>(bh) * T;
   const float* del_bh = delta + static_cast<size_t>(bh) * T;
 
-  // K^T and V^T operands: lane holds row kw0 + l32 (rows past T read row
-  // T-1; their gradients are never stored), elements 16 kc + 8 half + 0..7.
+  // K^T and V^T operands: lane holds row kw0 + l32 (see below),
+  // elements 16 kc + 8 half + 0..7.
   const int krow = kw0 + l32;
   bf16x8 kreg[8], vreg[8];
-  {
-    const size_t off = base + min(krow, T - 1) * rs + 8 * half;
-#pragma unroll
-    for (int kc = 0; kc < 8; ++kc) {
-      kreg[kc] = as_bf16x8(ld16(k + off + 16 * kc));
-      vreg[kc] = as_bf16x8(ld16(v + off + 16 * kc));
-    }
-  }
 
   f32x16 dka[4], dva[4];
 #pragma unroll
@@ -354,14 +346,44 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(
   // right after it, into the buffer of tile u - 1.
   const int n_qt = (T + QT_ROWS - 1) / QT_ROWS;
   const int qt0 = k0 / QT_ROWS;
+  // The workgroup's 128 K and V rows come through buffers 1 and 2 (K rows
+  // 0..63 in the q slot, 64..127 in the dout slot; V likewise), copied with
+  // 16 lanes per row, together with query tile qt0 into buffer 0; each lane
+  // then reads its row's operands.  Keys past T arrive as zeros: their
+  // gradients are never stored and, since every real query precedes them,
+  // the causal mask removes them from every real query's dS.
+  {
+    const int nk = T - k0;  // >= 1
+    const uint32_t n0 = static_cast<uint32_t>(min(nk, 64)) * rsb;
+    const uint32_t n1 = static_cast<uint32_t>(max(nk - 64, 0)) * rsb;
+    const size_t off0 = base + static_cast<size_t>(k0) * rs;
+    const size_t off1 = off0 + static_cast<size_t>(64) * rs;
+    copy_tile(buffer_rsrc(k + off0, n0), dvoff, rsb, qt_lds + BUF_B, wave);
+    copy_tile(buffer_rsrc(k + off1, n1), dvoff, rsb, qt_lds + BUF_B + TILE_B, wave);
+    copy_tile(buffer_rsrc(v + off0, n0), dvoff, rsb, qt_lds + 2 * BUF_B, wave);
+    copy_tile(buffer_rsrc(v + off1, n1), dvoff, rsb, qt_lds + 2 * BUF_B + TILE_B, wave);
+  }
   issue(qt0, 0);
+  sync_tiles();
+  {
+    const int rr = 32 * (wave & 1) + l32;  // row within the 64-row half
+    const uint32_t kt_row = qt_lds + BUF_B + (wave >> 1) * TILE_B + rr * 256;
+#pragma unroll
+    for (int kc = 0; kc < 8; ++kc) {
+      const uint32_t o = 16 * ((2 * kc + half) ^ tile_swz(rr));
+      kreg[kc] = as_bf16x8(lds_ld16(kt_row + o));
+      vreg[kc] = as_bf16x8(lds_ld16(kt_row + BUF_B + o));
+    }
+  }
+  __syncthreads();  // buffers 1 and 2 are free again
   if (qt0 + 1 < n_qt) issue(qt0 + 1, 1);
 
   // Diagonal part: the first two query tiles hold every (query, key) pair of
-  // this workgroup that the causal mask can cut.
+  // this workgroup that the causal mask can cut.  Tile qt0 has landed (and is
+  // published) already; tile qt0 + 1 is waited for at u = 1.
   const int n_diag = min(2, n_qt - qt0);
   for (int u = 0; u < n_diag; ++u) {
-    sync_tiles();
+    if (u > 0) sync_tiles();
     if (qt0 + u + 2 < n_qt) issue(qt0 + u + 2, (u + 2) % NBUF);
     const int q0 = (qt0 + u) * QT_ROWS;
     if (q0 + QT_ROWS - 1 < kw0) continue;  // every query precedes this wavefront's keys
