@@ -109,51 +109,6 @@ __device__ __forceinline__ void dkdv_scores(const uint32_t (&na)[8], int row0,
   }
 }
 
-template <bool MASK>
-__device__ __forceinline__ void dkdv_probs(const f32x16& sacc, const f32x16& pacc,
-                                           const float* lse_t, const float* dl_t, int row0,
-                                           bf16x8 (&pb)[2], bf16x8 (&sb)[2], int lane,
-                                           int key_minus_q0, float c_log2) {
-  const int r0 = row0 + 8 * (lane >> 5);  // element r: query row r0 + 16 (r/8) + r%8
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const float4 la = *reinterpret_cast<const float4*>(&lse_t[r0 + 16 * j]);
-    const float4 lb = *reinterpret_cast<const float4*>(&lse_t[r0 + 16 * j + 4]);
-    const float4 da = *reinterpret_cast<const float4*>(&dl_t[r0 + 16 * j]);
-    const float4 db = *reinterpret_cast<const float4*>(&dl_t[r0 + 16 * j + 4]);
-    const float l8[8] = {la.x, la.y, la.z, la.w, lb.x, lb.y, lb.z, lb.w};
-    const float d8[8] = {da.x, da.y, da.z, da.w, db.x, db.y, db.z, db.w};
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int r = 8 * j + i;
-      float p = fast_exp2(fmaf(sacc[r], c_log2, l8[i] * -kLog2e));
-      if (MASK && key_minus_q0 > r0 + 16 * j + i) p = 0.f;  // key after query
-      pb[j][i] = to_bf16(p);
-      sb[j][i] = to_bf16(p * (pacc[r] - d8[i]));
-    }
-  }
-}
-
-__device__ __forceinline__ void dkdv_accum(const bf16x8 (&pb)[2], const bf16x8 (&sb)[2],
-                                           const uint32_t (&ta)[4][2], int row0,
-                                           f32x16 (&dka)[4], f32x16 (&dva)[4]) {
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const uint32_t r = (row0 + 16 * j) * 256;  // queries row0 + 16 j + 8 half + 0..7
-    bf16x8 bg[4], bq[4];
-#pragma unroll
-    for (int db = 0; db < 4; ++db) {
-      bg[db] = tr_operand(ta[db], r + TILE_B);
-      bq[db] = tr_operand(ta[db], r);
-    }
-#pragma unroll
-    for (int db = 0; db < 4; ++db) {
-      dva[db] = mfma32(bg[db], pb[j], dva[db]);
-      dka[db] = mfma32(bq[db], sb[j], dka[db]);
-    }
-  }
-}
-
 // dS of one 32-query x 32-key block, kept for the dQ GEMM: stored as a
 // 32 x 32 bf16 matrix [key][query] (row = this lane's key, 8 queries per
 // 16-byte store).  Blocks of a head are packed lower-triangularly: block
@@ -168,20 +123,6 @@ __device__ __forceinline__ void store_ds(u16* blk, const bf16x8 (&sb)[2], int la
   st16(blk + l32 * 32 + 16 + 8 * half, __builtin_bit_cast(uint4, sb[1]));
 }
 
-template <bool MASK>
-__device__ __forceinline__ void dkdv_block(const TileAddr& ta, const float* lse_t,
-                                           const float* dl_t, const bf16x8 (&kreg)[8],
-                                           const bf16x8 (&vreg)[8], f32x16 (&dka)[4],
-                                           f32x16 (&dva)[4], int qb, int lane, int key_minus_q0,
-                                           float c_log2, u16* ds_blk) {
-  f32x16 sacc, pacc;
-  dkdv_scores(ta.nat, 32 * qb, kreg, vreg, sacc, pacc);
-  bf16x8 pb[2], sb[2];
-  dkdv_probs<MASK>(sacc, pacc, lse_t, dl_t, 32 * qb, pb, sb, lane, key_minus_q0, c_log2);
-  if (ds_blk) store_ds(ds_blk, sb, lane);
-  dkdv_accum(pb, sb, ta.tr, 32 * qb, dka, dva);
-}
-
 // Steady-state step: probabilities of the current block (held in s_cur,
 // p_cur), scores of the next block into s_nxt, p_nxt, then the current
 // block's dK/dV accumulation.  The order is fixed by hand in eight rounds,
@@ -191,13 +132,17 @@ __device__ __forceinline__ void dkdv_block(const TileAddr& ta, const float* lse_
 // so the VALU work runs while the matrix cores are busy; the last four rounds
 // also read the transposed operands of the first accumulation chunk.  na/rowN locate the next block (row-wise reads of
 // its tile), ta/rowC the current one (transposed reads).
+// MASK: the current block holds this wavefront's diagonal; kq is its key
+// minus the first query row of the current tile, and P is zeroed where the
+// key follows the query.
+template <bool MASK>
 __device__ __forceinline__ void dkdv_step(const uint32_t (&na)[8], int rowN, const float* lse_t,
                                           const float* dl_t, const uint32_t (&ta)[4][2],
                                           int rowC, const bf16x8 (&kreg)[8],
                                           const bf16x8 (&vreg)[8], const f32x16& s_cur,
                                           const f32x16& p_cur, f32x16& s_nxt, f32x16& p_nxt,
                                           f32x16 (&dka)[4], f32x16 (&dva)[4], int lane,
-                                          float c_log2, u16* ds_blk) {
+                                          float c_log2, int kq, u16* ds_blk) {
   const int half = lane >> 5;
   const uint32_t rn = rowN * 256;
   const uint32_t rc = rowC * 256;
@@ -229,8 +174,12 @@ __device__ __forceinline__ void dkdv_step(const uint32_t (&na)[8], int rowN, con
     }
     s_nxt = mfma32(aq[i], kreg[i], s_nxt);
     const int r = 2 * i;
-    const float p0 = fast_exp2(fmaf(s_cur[r], c_log2, lr[i].x * -kLog2e));
-    const float p1 = fast_exp2(fmaf(s_cur[r + 1], c_log2, lr[i].y * -kLog2e));
+    float p0 = fast_exp2(fmaf(s_cur[r], c_log2, lr[i].x * -kLog2e));
+    float p1 = fast_exp2(fmaf(s_cur[r + 1], c_log2, lr[i].y * -kLog2e));
+    if (MASK) {  // rows rr(i), rr(i) + 1 of the current tile
+      if (kq > rr(i)) p0 = 0.f;
+      if (kq > rr(i) + 1) p1 = 0.f;
+    }
     pw[i] = pack_bf16x2(p0, p1);
     sw[i] = pack_bf16x2(p0 * (p_cur[r] - dr[i].x), p1 * (p_cur[r + 1] - dr[i].y));
     // keep this round's VALU work in this round (no sinking to the first use)
@@ -270,6 +219,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(
     int H, float c_log2, float scale) {
   // NBUF query tiles (q and dout, swizzled, see tile_swz) and their lse, delta rows
   __shared__ __attribute__((aligned(1024))) char qtiles[NBUF * BUF_B];
+  __shared__ __attribute__((aligned(1024))) char kstage[2 * TILE_B];  // K rows at start
   __shared__ __attribute__((aligned(16))) float lsd[NBUF][2][QT_ROWS];
 
   const int tid = threadIdx.x;
@@ -305,6 +255,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(
   const TileOffsets ofs = tile_operand_offsets(lane);
   const uint32_t qt_lds = lds_addr(qtiles);
   const uint32_t lsd_lds = lds_addr(&lsd[0][0][0]);
+  const uint32_t kst_lds = lds_addr(kstage);
 
   // Tile copies (see copy_tile); wavefronts 0 and 1 also copy the lse and
   // delta rows.  Rows past T are past the end of the buffer range and arrive
@@ -341,110 +292,97 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(
     return (dsw && 32 * qblk < T) ? dsw + ds_block_index(bh, nbt, qblk, kblk) : nullptr;
   };
 
-  // Query tile qt0 + u lives in buffer u % NBUF.  At the sync before tile u is
-  // processed, tiles up to u + 1 have landed; the copy of tile u + 2 is issued
-  // right after it, into the buffer of tile u - 1.
+  // Query tile qt0 + u lives in buffer u % NBUF.  The workgroup's 128 K rows
+  // come through the staging region kst and its V rows through buffer 2 (rows
+  // 0..63, then 64..127), copied with 16 lanes per row together with query
+  // tiles qt0 and qt0 + 1; each lane then reads its row's operands.  Keys
+  // past T arrive as zeros: their gradients are never stored and, since every
+  // real query precedes them, the causal mask removes them from every real
+  // query's dS.
   const int n_qt = (T + QT_ROWS - 1) / QT_ROWS;
   const int qt0 = k0 / QT_ROWS;
-  // The workgroup's 128 K and V rows come through buffers 1 and 2 (K rows
-  // 0..63 in the q slot, 64..127 in the dout slot; V likewise), copied with
-  // 16 lanes per row, together with query tile qt0 into buffer 0; each lane
-  // then reads its row's operands.  Keys past T arrive as zeros: their
-  // gradients are never stored and, since every real query precedes them,
-  // the causal mask removes them from every real query's dS.
   {
     const int nk = T - k0;  // >= 1
     const uint32_t n0 = static_cast<uint32_t>(min(nk, 64)) * rsb;
     const uint32_t n1 = static_cast<uint32_t>(max(nk - 64, 0)) * rsb;
     const size_t off0 = base + static_cast<size_t>(k0) * rs;
     const size_t off1 = off0 + static_cast<size_t>(64) * rs;
-    copy_tile(buffer_rsrc(k + off0, n0), dvoff, rsb, qt_lds + BUF_B, wave);
-    copy_tile(buffer_rsrc(k + off1, n1), dvoff, rsb, qt_lds + BUF_B + TILE_B, wave);
+    copy_tile(buffer_rsrc(k + off0, n0), dvoff, rsb, kst_lds, wave);
+    copy_tile(buffer_rsrc(k + off1, n1), dvoff, rsb, kst_lds + TILE_B, wave);
     copy_tile(buffer_rsrc(v + off0, n0), dvoff, rsb, qt_lds + 2 * BUF_B, wave);
     copy_tile(buffer_rsrc(v + off1, n1), dvoff, rsb, qt_lds + 2 * BUF_B + TILE_B, wave);
   }
   issue(qt0, 0);
+  if (qt0 + 1 < n_qt) issue(qt0 + 1, 1);
   sync_tiles();
   {
     const int rr = 32 * (wave & 1) + l32;  // row within the 64-row half
-    const uint32_t kt_row = qt_lds + BUF_B + (wave >> 1) * TILE_B + rr * 256;
+    const uint32_t o_row = (wave >> 1) * TILE_B + rr * 256;
 #pragma unroll
     for (int kc = 0; kc < 8; ++kc) {
-      const uint32_t o = 16 * ((2 * kc + half) ^ tile_swz(rr));
-      kreg[kc] = as_bf16x8(lds_ld16(kt_row + o));
-      vreg[kc] = as_bf16x8(lds_ld16(kt_row + BUF_B + o));
+      const uint32_t o = o_row + 16 * ((2 * kc + half) ^ tile_swz(rr));
+      kreg[kc] = as_bf16x8(lds_ld16(kst_lds + o));
+      vreg[kc] = as_bf16x8(lds_ld16(qt_lds + 2 * BUF_B + o));
     }
   }
-  __syncthreads();  // buffers 1 and 2 are free again
-  if (qt0 + 1 < n_qt) issue(qt0 + 1, 1);
+  __syncthreads();  // buffer 2 is free again
+  if (qt0 + 2 < n_qt) issue(qt0 + 2, 2);
 
-  // Diagonal part: the first two query tiles hold every (query, key) pair of
-  // this workgroup that the causal mask can cut.  Tile qt0 has landed (and is
-  // published) already; tile qt0 + 1 is waited for at u = 1.
-  const int n_diag = min(2, n_qt - qt0);
-  for (int u = 0; u < n_diag; ++u) {
-    if (u > 0) sync_tiles();
-    if (qt0 + u + 2 < n_qt) issue(qt0 + u + 2, (u + 2) % NBUF);
-    const int q0 = (qt0 + u) * QT_ROWS;
-    if (q0 + QT_ROWS - 1 < kw0) continue;  // every query precedes this wavefront's keys
-    TileAddr ta;
-    nat_addr(qt_lds + u * BUF_B, ofs, ta.nat);
-    tr_addr(qt_lds + u * BUF_B, ofs, ta.tr);
-    const int kq = krow - q0;
-    if (q0 < kw0 + 31) {  // tile crosses this wavefront's diagonal
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        if (q0 + 32 * qb + 31 >= kw0)
-          dkdv_block<true>(ta, lsd[u][0], lsd[u][1], kreg, vreg, dka, dva, qb, lane, kq, c_log2,
-                           ds_of(q0 / 32 + qb));
-        __builtin_amdgcn_sched_barrier(0);  // keep the two blocks' live ranges apart
-      }
-    } else {
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        dkdv_block<false>(ta, lsd[u][0], lsd[u][1], kreg, vreg, dka, dva, qb, lane, kq, c_log2,
-                          ds_of(q0 / 32 + qb));
-        __builtin_amdgcn_sched_barrier(0);
-      }
+  // One software pipeline over the 32-query blocks from the diagonal on: the
+  // step for block j computes the probabilities of j, the scores of j+1 and
+  // the dK/dV update of j.  This wavefront's first block is its diagonal
+  // block bw (masked); blocks before it hold no visible (query, key) pair and
+  // are skipped, and the slot of block bw - 1 computes bw's scores.  Tile t
+  // holds blocks 2t, 2t+1; block 2t+1's step reads the scores of block 2t+2
+  // from tile t+1.  At the sync before tile t (t > qt0) tile t+1 has landed
+  // and tile t-1's buffer is free for the copy of tile t+2.  After the last
+  // tile the second step still computes scores of a block past the end (from
+  // a stale buffer); they are never used.
+  const int bw = kw0 / 32;
+  f32x16 s0, p0, s1, p1;  // scores of even blocks in s0/p0, of odd blocks in s1/p1
+  uint32_t nc[8];         // row-read addresses of tile t
+  nat_addr(qt_lds, ofs, nc);
+  if (bw == 2 * qt0) dkdv_scores(nc, 0, kreg, vreg, s0, p0);
+  int u = 0;  // buffer of tile t
+  // The first two tiles (every diagonal block of the workgroup) take the
+  // per-wavefront branches; the rest run one branch-free body.
+  auto tile = [&](int t, auto steady) {
+    constexpr bool STEADY = decltype(steady)::value;
+    const int un = u == NBUF - 1 ? 0 : u + 1;  // buffer of tile t + 1
+    if (t > qt0) {
+      sync_tiles();
+      if (t + 2 < n_qt) issue(t + 2, un == NBUF - 1 ? 0 : un + 1);
     }
-  }
-
-  // Steady part: every query follows every key, no mask, no skipped block.
-  // Software pipeline over 32-query blocks: the step for block j computes the
-  // probabilities of j, the scores of j+1 and the dK/dV update of j.  Block
-  // j+1 may live in the next tile, which has landed by then; one sync per tile.
-  const int ts = qt0 + 2;
-  if (ts < n_qt) {
-    sync_tiles();
-    if (ts + 2 < n_qt) issue(ts + 2, 1);
-    int u = 2;  // buffer of tile t
-    uint32_t nc[8];  // row-read addresses of tile t
-    nat_addr(qt_lds + 2 * BUF_B, ofs, nc);
-    f32x16 s0, p0, s1, p1;
-    dkdv_scores(nc, 0, kreg, vreg, s0, p0);
-    // Branch-free body: after the last tile the second step still computes
-    // scores of a block past the end (from a stale buffer); they are never
-    // used.
-    for (int t = ts; t < n_qt; ++t) {
-      const int un = u == NBUF - 1 ? 0 : u + 1;  // buffer of tile t + 1
-      uint32_t tc[4][2], nn[8];
-      tr_addr(qt_lds + u * BUF_B, ofs, tc);
-      // block 2t (rows 0..31 of tile t) while computing scores of rows 32..63
-      dkdv_step(nc, 32, lsd[u][0], lsd[u][1], tc, 0, kreg, vreg, s0, p0, s1, p1, dka, dva, lane,
-                c_log2, ds_of(2 * t));
-      nat_addr(qt_lds + un * BUF_B, ofs, nn);
-      // block 2t+1 (rows 32..63 of tile t) while computing scores of tile t+1 rows 0..31
-      dkdv_step(nn, 0, lsd[u][0], lsd[u][1], tc, 32, kreg, vreg, s1, p1, s0, p0, dka, dva, lane,
-                c_log2, ds_of(2 * t + 1));
+    uint32_t tc[4][2], nn[8];
+    tr_addr(qt_lds + u * BUF_B, ofs, tc);
+    nat_addr(qt_lds + un * BUF_B, ofs, nn);
+    const int kq = krow - QT_ROWS * t;
+    const int j0 = 2 * t, j1 = 2 * t + 1;
+    // block j0 (rows 0..31 of tile t), scores of rows 32..63
+    if (STEADY || j0 > bw)
+      dkdv_step<false>(nc, 32, lsd[u][0], lsd[u][1], tc, 0, kreg, vreg, s0, p0, s1, p1, dka, dva,
+                       lane, c_log2, kq, ds_of(j0));
+    else if (j0 == bw)
+      dkdv_step<true>(nc, 32, lsd[u][0], lsd[u][1], tc, 0, kreg, vreg, s0, p0, s1, p1, dka, dva,
+                      lane, c_log2, kq, ds_of(j0));
+    else if (j0 == bw - 1)
+      dkdv_scores(nc, 32, kreg, vreg, s1, p1);
+    // block j1 (rows 32..63 of tile t), scores of tile t+1 rows 0..31
+    if (STEADY || j1 > bw)
+      dkdv_step<false>(nn, 0, lsd[u][0], lsd[u][1], tc, 32, kreg, vreg, s1, p1, s0, p0, dka, dva,
+                       lane, c_log2, kq, ds_of(j1));
+    else if (j1 == bw)
+      dkdv_step<true>(nn, 0, lsd[u][0], lsd[u][1], tc, 32, kreg, vreg, s1, p1, s0, p0, dka, dva,
+                      lane, c_log2, kq, ds_of(j1));
+    else if (j1 == bw - 1)
+      dkdv_scores(nn, 0, kreg, vreg, s0, p0);
 #pragma unroll
-      for (int kc = 0; kc < 8; ++kc) nc[kc] = nn[kc];
-      if (t + 1 < n_qt) {
-        sync_tiles();
-        if (t + 3 < n_qt) issue(t + 3, u);
-      }
-      u = un;
-    }
-  }
+    for (int kc = 0; kc < 8; ++kc) nc[kc] = nn[kc];
+    u = un;
+  };
+  const int t_diag_end = min(qt0 + 2, n_qt);
+  for (int t = qt0; t < t_diag_end; ++t) tile(t, std::false_type{});
+  for (int t = t_diag_end; t < n_qt; ++t) tile(t, std::true_type{});
 
   // dka[db], dva[db] (dK^T, dV^T blocks) element r: key kw0 + l32,
   // d = 32 db + 8 (r/4) + 4 half + r%4.  The rows leave through LDS so that 16
