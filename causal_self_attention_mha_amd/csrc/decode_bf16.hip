@@ -10,18 +10,21 @@
 // at row L-1.
 //
 // The work is HBM bound (each cached K and V byte is used once).  Two kernels:
-//   split:   one workgroup per (chunk of 256 keys, b) holding keys < L, all
-//            heads together.  16-lane groups map to (head h, stream s); at a
-//            given loop step the groups of all heads and streams read whole
-//            cache rows (S * H * 256 contiguous bytes of K and of V), so the
-//            cache streams from HBM in order.  One pass: each group takes its
-//            keys in batches of 8, with the next batch's K and V loads in
-//            flight while the current batch runs an online softmax (running
-//            max, sum and output in registers); no barrier until the streams
-//            of a head are merged through LDS at the end.  Writes unnormalised
-//            o_c and (m_c, l_c) per (b, chunk, h).
-//   combine: one workgroup per (b, h): o = sum_c e^(m_c - M) o_c / sum_c e^(m_c - M) l_c.
+//   split:   persistent workgroups (two per compute unit) walk the non-empty
+//            (sequence b, 64-key chunk) slots, all heads per workgroup, one
+//            16-lane group per head reading whole 256-byte head rows.  Each
+//            group streams a chunk's keys in batches of 4 with an online
+//            softmax in registers; the next batch's K and V loads (possibly
+//            the next slot's, with its query) are in flight while the current
+//            batch is computed.  Writes unnormalised o_c and (m_c, l_c) per
+//            (b, chunk, h).  Balancing slots rather than launching one
+//            workgroup per chunk matters: the ragged lengths otherwise leave
+//            compute units idle (measured 48% -> 56% of HBM bandwidth).
+//   combine: one workgroup per (b, h), one pass with a running max:
+//            o = sum_c e^(m_c - M) o_c / sum_c e^(m_c - M) l_c.
 // Rows t >= L are never read.
+#include <algorithm>
+
 #include "device_common.hpp"
 #include "internal.hpp"
 
@@ -29,76 +32,137 @@ namespace na {
 namespace {
 
 constexpr int D = kHeadDim;
-constexpr int CHUNK = 256;  // keys per split workgroup
-constexpr int U = 8;        // keys per batch and per lane
+constexpr int CHUNK = 64;        // keys per work slot
+constexpr int U = 4;            // keys per batch (per 16-lane group)
+constexpr int kWgPerCu = 2;     // persistent workgroups per compute unit
+constexpr int kMaxFlatB = 8192;  // up to this many sequences the slot list is flattened
 
 __host__ __device__ inline int n_chunks(int T_cap) { return (T_cap + CHUNK - 1) / CHUNK; }
 
-// Streams per head: enough 16-lane groups to reach at least 256 threads, at
-// most 512 threads (H <= 32 is checked on the host).
-inline int streams_for(int H) {
-  const int s = (256 + 16 * H - 1) / (16 * H);
-  return s * 16 * H <= 512 ? s : 1;
-}
-
 // workspace: o_part [B][NC][H][D] fp32, then ml [B][NC][H][2] fp32 (m_c, l_c)
+//
+// Persistent split: a workgroup of 16 H threads (one 16-lane group per head,
+// lane i of a group owns bytes 16 i .. 16 i + 15 of the 256-byte head row)
+// walks work slots (b, chunk c) with c * CHUNK < L_b, slot w = blockIdx.x,
+// + gridDim.x, ...  Slots are numbered over the flattened list of non-empty
+// chunks (prefix sums of ceil(L_b / CHUNK) in LDS), so every workgroup gets
+// the same number of slots give or take one.  A slot's keys stream in
+// batches of U rows; the K, V (and, at a slot change, q) loads of the next
+// batch, which may belong to the next slot, are issued before the current
+// batch is computed, so HBM latency hides behind the previous batch's work
+// across slot boundaries.  At the end of a slot each group writes its
+// unnormalised partial output and (m, l).
+struct Batch {
+  int slot;  // flattened slot index, or -1 past the end
+  int b, c;  // sequence and chunk
+  int n;     // keys in this chunk
+  int ib;    // batch within the chunk
+};
+
 __global__ __launch_bounds__(512) void decode_split_kernel(
     const u16* __restrict__ q, const u16* __restrict__ kc, const u16* __restrict__ vc,
-    const int* __restrict__ seqlens, float* __restrict__ opart, float* __restrict__ ml, int H,
-    int T_cap, int S, float scale) {
-  extern __shared__ __attribute__((aligned(16))) float smem[];
-  float* part = smem;                    // [S][H][D] per-stream outputs
-  float* pm = part + S * H * D;          // [S][H] per-stream running max
-  float* pl = pm + S * H;                // [S][H] per-stream running sum
-
-  const int c = blockIdx.x, b = blockIdx.y;
-  const int NC = gridDim.x;
-  const int L = min(max(seqlens[b], 0), T_cap);
-  const int j0 = c * CHUNK;
-  if (j0 >= L) return;  // uniform across the workgroup
-  const int n = min(CHUNK, L - j0);
-
+    const int* __restrict__ seqlens, float* __restrict__ opart, float* __restrict__ ml, int B,
+    int H, int T_cap, float scale) {
+  __shared__ int pre[kMaxFlatB + 1];  // pre[b] = non-empty chunks of sequences < b
   const int tid = threadIdx.x;
-  const int g = tid >> 4;       // group
-  const int l16 = tid & 15;     // which 16 bytes of the 256-byte head row
-  const int h = g % H;
-  const int st = g / H;         // stream
-  const size_t rs = static_cast<size_t>(H) * D;
-  const size_t base = (static_cast<size_t>(b) * T_cap + j0) * rs + static_cast<size_t>(h) * D +
-                      8 * l16;
-  const u16* kb = kc + base;
-  const u16* vb = vc + base;
+  const int h = tid >> 4;
+  const int l16 = tid & 15;
+  const int NC = n_chunks(T_cap);
+  const int P = gridDim.x;
+  const bool flat = B <= kMaxFlatB;
+  auto len = [&](int b) { return min(max(seqlens[b], 0), T_cap); };
+  int total;  // number of slots
+  if (flat) {
+    // prefix sums of chunk counts: serial over 64-sequence blocks, each block
+    // summed by one wavefront (B is small here)
+    if (tid < 64) {
+      int run = 0;
+      for (int b0 = 0; b0 < B; b0 += 64) {
+        const int b = b0 + tid;
+        const int c = b < B ? (len(b) + CHUNK - 1) / CHUNK : 0;
+        int x = c;  // inclusive scan over the wavefront
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const int y = __shfl_up(x, o, 64);
+          if (tid >= o) x += y;
+        }
+        if (b < B) pre[b + 1] = run + x;
+        run += __shfl(x, 63, 64);
+      }
+      if (tid == 0) pre[0] = 0;
+    }
+    __syncthreads();
+    total = pre[B];
+  } else {
+    total = B * NC;  // raw (b, c) grid; empty slots are skipped below
+  }
 
-  float qv[8];  // q scaled by s * log2(e): scores come out in the exp2 domain
-  {
-    const float c2 = scale * 1.4426950408889634f;
-    const uint4 x = ld16(q + (static_cast<size_t>(b) * H + h) * D + 8 * l16);
+  // slot -> (b, c): binary search in pre (flat) or direct (raw)
+  auto locate = [&](int slot, Batch& t) {
+    if (flat) {
+      int lo = 0, hi = B - 1;  // largest b with pre[b] <= slot
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (pre[mid] <= slot) lo = mid; else hi = mid - 1;
+      }
+      t.b = lo;
+      t.c = slot - pre[lo];
+    } else {
+      t.b = slot / NC;
+      t.c = slot % NC;
+    }
+    t.n = min(CHUNK, len(t.b) - t.c * CHUNK);  // <= 0 only for raw empty slots
+  };
+  auto first_from = [&](int slot) {  // first non-empty slot >= slot (stride P)
+    Batch t{-1, 0, 0, 0, 0};
+    for (; slot < total; slot += P) {
+      locate(slot, t);
+      if (t.n > 0) {
+        t.slot = slot;
+        return t;
+      }
+    }
+    t.slot = -1;
+    return t;
+  };
+  auto next = [&](const Batch& t) {
+    if ((t.ib + 1) * U < t.n) {
+      Batch u = t;
+      ++u.ib;
+      return u;
+    }
+    return first_from(t.slot + P);
+  };
+
+  const size_t rs = static_cast<size_t>(H) * D;
+  const float c2 = scale * 1.4426950408889634f;  // scores in the exp2 domain
+  auto rows = [&](const Batch& t, uint4 (&xk)[U], uint4 (&xv)[U]) {
+    const size_t base = (static_cast<size_t>(t.b) * T_cap + t.c * CHUNK) * rs +
+                        static_cast<size_t>(h) * D + 8 * l16;
+    const int rsi = H * D;
+#pragma unroll
+    for (int i = 0; i < U; ++i) {
+      const int r = min(t.ib * U + i, t.n - 1) * rsi;  // rows past n: re-read, zero weight
+      xk[i] = ld16(kc + base + r);
+      xv[i] = ld16(vc + base + r);
+    }
+  };
+  auto qrow = [&](const Batch& t) {
+    return ld16(q + (static_cast<size_t>(t.b) * H + h) * D + 8 * l16);
+  };
+
+  float qv[8];
+  auto set_q = [&](uint4 x) {
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       const uint32_t u = (&x.x)[w];
       qv[2 * w] = __uint_as_float(u << 16) * c2;
       qv[2 * w + 1] = __uint_as_float(u & 0xffff0000u) * c2;
     }
-  }
-
-  // keys st, st + S, ... (< n) in batches of U; rows past n re-read row n-1
-  // and get zero weight
-  auto row = [&](int key) { return static_cast<size_t>(min(key, n - 1)) * rs; };
-  uint4 xk[U], xv[U], yk[U], yv[U];
-#pragma unroll
-  for (int i = 0; i < U; ++i) {
-    xk[i] = ld16(kb + row(st + i * S));
-    xv[i] = ld16(vb + row(st + i * S));
-  }
+  };
   float m = -INFINITY, l = 0.f;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int k0 = st; k0 < n; k0 += U * S) {
-    const int k1 = k0 + U * S;  // next batch (clamped loads are harmless past n)
-#pragma unroll
-    for (int i = 0; i < U; ++i) {
-      yk[i] = ld16(kb + row(k1 + i * S));
-      yv[i] = ld16(vb + row(k1 + i * S));
-    }
+  auto compute = [&](const Batch& t, const uint4 (&xk)[U], const uint4 (&xv)[U]) {
     float z[U];
 #pragma unroll
     for (int i = 0; i < U; ++i) {
@@ -110,13 +174,13 @@ __global__ __launch_bounds__(512) void decode_split_kernel(
         a = fmaf(qv[2 * w + 1], __uint_as_float(u & 0xffff0000u), a);
       }
       a = sum16(a);
-      z[i] = k0 + i * S < n ? a : -INFINITY;
+      z[i] = t.ib * U + i < t.n ? a : -INFINITY;
     }
-    float bm = z[0];
+    float bm = z[0];  // finite: row ib * U < n
 #pragma unroll
     for (int i = 1; i < U; ++i) bm = fmaxf(bm, z[i]);
-    const float m_new = fmaxf(m, bm);        // finite: key k0 < n is valid
-    const float alpha = fast_exp2(m - m_new);  // 0 on the first batch
+    const float m_new = fmaxf(m, bm);
+    const float alpha = fast_exp2(m - m_new);  // 0 on a chunk's first batch
     l *= alpha;
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] *= alpha;
@@ -132,42 +196,51 @@ __global__ __launch_bounds__(512) void decode_split_kernel(
       }
     }
     m = m_new;
+    if ((t.ib + 1) * U >= t.n) {  // last batch of the chunk: partial out, reset
+      const size_t slotw = (static_cast<size_t>(t.b) * NC + t.c) * H + h;
+      float* op = opart + slotw * D + 8 * l16;
+      *reinterpret_cast<float4*>(op) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+      *reinterpret_cast<float4*>(op + 4) = make_float4(acc[4], acc[5], acc[6], acc[7]);
+      if (l16 == 0) {
+        ml[2 * slotw] = m * 0.6931471805599453f;  // back to natural-log units
+        ml[2 * slotw + 1] = l;
+      }
+      m = -INFINITY;
+      l = 0.f;
 #pragma unroll
-    for (int i = 0; i < U; ++i) {
-      xk[i] = yk[i];
-      xv[i] = yv[i];
+      for (int e = 0; e < 8; ++e) acc[e] = 0.f;
     }
-  }
+  };
 
-  // merge the S streams of each head (in the exp2 domain), stream 0 writes
-  float* pp = part + (static_cast<size_t>(st) * H + h) * D + 8 * l16;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) pp[e] = acc[e];
-  if (l16 == 0) {
-    pm[st * H + h] = m;  // -inf for a stream that had no key
-    pl[st * H + h] = l;
-  }
-  __syncthreads();
-  if (st == 0) {
-    float M = -INFINITY;
-    for (int s2 = 0; s2 < S; ++s2) M = fmaxf(M, pm[s2 * H + h]);
-    float out[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    float den = 0.f;
-    for (int s2 = 0; s2 < S; ++s2) {
-      const float w = fast_exp2(pm[s2 * H + h] - M);
-      den = fmaf(w, pl[s2 * H + h], den);
-      const float* sp = part + (static_cast<size_t>(s2) * H + h) * D + 8 * l16;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) out[e] = fmaf(w, sp[e], out[e]);
+  uint4 ak[U], av[U], bk[U], bv[U];
+  uint4 qa, qb;
+  Batch cur = first_from(static_cast<int>(blockIdx.x));
+  if (cur.slot < 0) return;  // uniform: no work for this workgroup
+  rows(cur, ak, av);
+  set_q(qrow(cur));
+  while (true) {
+    Batch nx = next(cur);
+    if (nx.slot >= 0) {
+      rows(nx, bk, bv);
+      if (nx.ib == 0) qb = qrow(nx);
     }
-    const size_t slot = (static_cast<size_t>(b) * NC + c) * H + h;
-    float* op = opart + slot * D + 8 * l16;
-    *reinterpret_cast<float4*>(op) = make_float4(out[0], out[1], out[2], out[3]);
-    *reinterpret_cast<float4*>(op + 4) = make_float4(out[4], out[5], out[6], out[7]);
-    if (l16 == 0) {
-      ml[2 * slot] = M * 0.6931471805599453f;  // back to natural-log units
-      ml[2 * slot + 1] = den;
+    __builtin_amdgcn_sched_barrier(0);
+    compute(cur, ak, av);
+    __builtin_amdgcn_sched_barrier(0);
+    if (nx.slot < 0) break;
+    if (nx.ib == 0) set_q(qb);
+    cur = nx;
+    nx = next(cur);
+    if (nx.slot >= 0) {
+      rows(nx, ak, av);
+      if (nx.ib == 0) qa = qrow(nx);
     }
+    __builtin_amdgcn_sched_barrier(0);
+    compute(cur, bk, bv);
+    __builtin_amdgcn_sched_barrier(0);
+    if (nx.slot < 0) break;
+    if (nx.ib == 0) set_q(qa);
+    cur = nx;
   }
 }
 
@@ -181,17 +254,10 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(
   const int d = threadIdx.x;
   const float* mlb = ml + 2 * (static_cast<size_t>(b) * NC * H + h);  // chunk c at 2 c H
   const float* opb = opart + (static_cast<size_t>(b) * NC * H + h) * D + d;  // chunk c at c H D
-  // groups of 16 chunks: all loads of a group issued before they are used
+  // one pass over the chunks in groups of 16 (all loads of a group issued
+  // before they are used), with a running max M
   constexpr int G = 16;
-  float M = -INFINITY;
-  for (int c0 = 0; c0 < nc; c0 += G) {
-    float mv[G];
-#pragma unroll
-    for (int i = 0; i < G; ++i) mv[i] = c0 + i < nc ? mlb[2 * (c0 + i) * H] : -INFINITY;
-#pragma unroll
-    for (int i = 0; i < G; ++i) M = fmaxf(M, mv[i]);
-  }
-  float den = 0.f, num = 0.f;
+  float M = -INFINITY, den = 0.f, num = 0.f;
   for (int c0 = 0; c0 < nc; c0 += G) {
     float mv[G], lv[G], ov[G];
 #pragma unroll
@@ -202,12 +268,20 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(
       lv[i] = mlb[2 * c * H + 1];
       ov[i] = opb[static_cast<size_t>(c) * H * D];
     }
+    float gm = mv[0];
+#pragma unroll
+    for (int i = 1; i < G; ++i) gm = fmaxf(gm, mv[i]);
+    const float M_new = fmaxf(M, gm);  // finite: chunk c0 < nc exists
+    const float sc = expf(M - M_new);  // 0 on the first group
+    den *= sc;
+    num *= sc;
 #pragma unroll
     for (int i = 0; i < G; ++i) {
-      const float w = expf(mv[i] - M);  // 0 for chunks past nc
+      const float w = expf(mv[i] - M_new);  // 0 for chunks past nc
       den = fmaf(w, lv[i], den);
       num = fmaf(w, ov[i], num);
     }
+    M = M_new;
   }
   const float out = nc > 0 ? num / den : 0.f;
   o[(static_cast<size_t>(b) * H + h) * D + d] = __builtin_bit_cast(u16, to_bf16(out));
@@ -227,17 +301,19 @@ hipError_t launch_decode_bf16(const void* q, const void* kc, const void* vc, con
                               hipStream_t s, hipEvent_t const* ev) {
   const float scale = 1.0f / sqrtf(static_cast<float>(D));
   const int NC = n_chunks(T_cap);
-  const int S = streams_for(H);
-  const int threads = 16 * H * S;
-  const size_t shmem = (static_cast<size_t>(S) * H * D + 2 * static_cast<size_t>(S) * H) *
-                       sizeof(float);
   float* opart = static_cast<float*>(ws);
   float* ml = opart + static_cast<std::size_t>(B) * NC * H * D;
+  // persistent workgroups: a few per compute unit, never more than slots
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) == hipSuccess)
+    (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  const long slots = static_cast<long>(B) * NC;
+  const int P = static_cast<int>(std::min<long>(slots, static_cast<long>(kWgPerCu) * cus));
   hipError_t e = mark(ev, 0, s);
   if (e != hipSuccess) return e;
-  e = launch(decode_split_kernel, dim3(NC, B), dim3(threads), shmem, s, static_cast<const u16*>(q),
-             static_cast<const u16*>(kc), static_cast<const u16*>(vc), seqlens, opart, ml, H,
-             T_cap, S, scale);
+  e = launch(decode_split_kernel, dim3(P), dim3(16 * H), 0, s, static_cast<const u16*>(q),
+             static_cast<const u16*>(kc), static_cast<const u16*>(vc), seqlens, opart, ml, B, H,
+             T_cap, scale);
   if (e != hipSuccess) return e;
   if ((e = mark(ev, 1, s)) != hipSuccess) return e;
   e = launch(decode_combine_kernel, dim3(H, B), dim3(128), 0, s, static_cast<const float*>(opart),

@@ -75,3 +75,14 @@ def test_decode_matches_last_forward_row(dev):
     torch.cuda.synchronize()
     assert_close("o", to_host(od[0]), to_host(o[0, L - 1]), 1e-2, 1e-2)
     assert_close("lse", to_host(ld[0]), to_host(lse[0, :, L - 1]), 1e-5, 1e-4)
+
+
+def test_decode_many_sequences_raw_slot_order(dev):
+    """More than 8192 sequences: the split kernel walks the raw (sequence,
+    chunk) grid instead of the flattened list of non-empty chunks."""
+    B = 8200
+    rng = np.random.default_rng(14)
+    lens = rng.integers(0, 70, size=B)  # includes empty sequences and chunk edges
+    inp = W.make_decode_inputs(B=B, T_cap=70, H=1, seed=14, seqlens=lens)
+    o, lse = run_decode(inp, dev)
+    check(inp, o, lse)
