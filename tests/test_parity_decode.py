@@ -86,3 +86,19 @@ def test_decode_many_sequences_raw_slot_order(dev):
     inp = W.make_decode_inputs(B=B, T_cap=70, H=1, seed=14, seqlens=lens)
     o, lse = run_decode(inp, dev)
     check(inp, o, lse)
+
+
+def test_decode_reuses_workspace(dev):
+    """Calls sharing one workspace (two different inputs, then the first again)
+    each give the oracle's result."""
+    import torch
+    import causal_self_attention_mha_amd as na
+    a = W.make_decode_inputs(B=9, T_cap=400, H=4, seed=15)
+    b = W.make_decode_inputs(B=9, T_cap=400, H=4, seed=16)
+    ws = torch.zeros(na.decode_workspace_bytes(9, 4, 400), dtype=torch.uint8, device=dev)
+    for inp in (a, b, a):
+        lens = torch.from_numpy(inp.seqlens.astype(np.int32)).to(dev)
+        o, lse = na.attn_decode(to_device(inp.q_store, dev), to_device(inp.k_store, dev),
+                                to_device(inp.v_store, dev), lens, workspace=ws)
+        torch.cuda.synchronize()
+        check(inp, o, lse)
