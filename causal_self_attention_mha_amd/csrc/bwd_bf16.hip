@@ -130,13 +130,15 @@ __device__ __forceinline__ void store_ds(u16* blk, const bf16x8 (&sb)[2], int la
 // lse and delta) two rounds ahead, one score MFMA for S and one for dP, and
 // the probability math of two of this lane's sixteen (key, query) elements,
 // so the VALU work runs while the matrix cores are busy; the last four rounds
-// also read the transposed operands of the first accumulation chunk.  na/rowN locate the next block (row-wise reads of
-// its tile), ta/rowC the current one (transposed reads).
+// also read the transposed operands of the first accumulation chunk.  na/rowN
+// locate the next block (row-wise reads of its tile), ta/rowC the current one
+// (transposed reads); nl_t and dl_t are the current tile's rows of -lse log2(e)
+// and of delta.
 // MASK: the current block holds this wavefront's diagonal; kq is its key
 // minus the first query row of the current tile, and P is zeroed where the
 // key follows the query.
 template <bool MASK>
-__device__ __forceinline__ void dkdv_step(const uint32_t (&na)[8], int rowN, const float* lse_t,
+__device__ __forceinline__ void dkdv_step(const uint32_t (&na)[8], int rowN, const float* nl_t,
                                           const float* dl_t, const uint32_t (&ta)[4][2],
                                           int rowC, const bf16x8 (&kreg)[8],
                                           const bf16x8 (&vreg)[8], const f32x16& s_cur,
@@ -156,7 +158,7 @@ __device__ __forceinline__ void dkdv_step(const uint32_t (&na)[8], int rowN, con
   auto reads = [&](int i) {
     aq[i] = as_bf16x8(lds_ld16(na[i] + rn));
     ag[i] = as_bf16x8(lds_ld16(na[i] + rn + TILE_B));
-    lr[i] = *reinterpret_cast<const float2*>(&lse_t[rr(i)]);
+    lr[i] = *reinterpret_cast<const float2*>(&nl_t[rr(i)]);
     dr[i] = *reinterpret_cast<const float2*>(&dl_t[rr(i)]);
   };
   reads(0);
@@ -174,8 +176,8 @@ __device__ __forceinline__ void dkdv_step(const uint32_t (&na)[8], int rowN, con
     }
     s_nxt = mfma32(aq[i], kreg[i], s_nxt);
     const int r = 2 * i;
-    float p0 = fast_exp2(fmaf(s_cur[r], c_log2, lr[i].x * -kLog2e));
-    float p1 = fast_exp2(fmaf(s_cur[r + 1], c_log2, lr[i].y * -kLog2e));
+    float p0 = fast_exp2(fmaf(s_cur[r], c_log2, lr[i].x));
+    float p1 = fast_exp2(fmaf(s_cur[r + 1], c_log2, lr[i].y));
     if (MASK) {  // rows rr(i), rr(i) + 1 of the current tile
       if (kq > rr(i)) p0 = 0.f;
       if (kq > rr(i) + 1) p1 = 0.f;
@@ -210,6 +212,11 @@ __device__ __forceinline__ void dkdv_step(const uint32_t (&na)[8], int rowN, con
     }
     __builtin_amdgcn_sched_barrier(0);
   }
+}
+
+// lse (natural log) -> -lse log2(e), in place, for the 64 rows of a tile.
+__device__ __forceinline__ void to_exp2_offset(float* rows, int lane) {
+  rows[lane] = rows[lane] * -kLog2e;
 }
 
 __global__ __launch_bounds__(256, 1) void dkdv_kernel(
@@ -315,6 +322,10 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(
   issue(qt0, 0);
   if (qt0 + 1 < n_qt) issue(qt0 + 1, 1);
   sync_tiles();
+  // The lse rows are used as -lse log2(e), the exponent offset of P in the
+  // exp2 domain: the wavefront that first sees a tile's rows land rewrites
+  // them in place (the next barrier publishes them).
+  if (wave < 2) to_exp2_offset(lsd[wave][0], lane);
   {
     const int rr = 32 * (wave & 1) + l32;  // row within the 64-row half
     const uint32_t o_row = (wave >> 1) * TILE_B + rr * 256;
@@ -352,6 +363,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(
     if (t > qt0) {
       sync_tiles();
       if (t + 2 < n_qt) issue(t + 2, un == NBUF - 1 ? 0 : un + 1);
+      if (t + 1 < n_qt && wave == 3) to_exp2_offset(lsd[un][0], lane);  // tile t+1
     }
     uint32_t tc[4][2], nn[8];
     tr_addr(qt_lds + u * BUF_B, ofs, tc);
@@ -759,37 +771,41 @@ __global__ __launch_bounds__(256, 2) void dq_gemm_kernel(const u16* __restrict__
       wait_vmem();
     __syncthreads();
     const bool more_k = kt + 1 < n_kt, more_ds = kt + 2 < n_kt;
+    // Four chunks of 16 keys, j = 2 kb + c (keys 32 kb + 16 c .. + 15 of the
+    // tile); chunk j+1's operands are read while chunk j's MFMAs run.
+    bf16x8 a[2][4], bs[2];
+    auto read = [&](int j) {
+      const int kb = j >> 1, c = j & 1;
+      // keys 32 kb + 16 c + 8 half + 0..7, query column l32
+      const uint32_t st = st_lds + sb * (4 * DG_DS_B) + kb * 2048 + st_off + c * 16 * 64;
+      const uint2 r0 = ds_read_tr16_at(st);
+      const uint2 r1 = ds_read_tr16_at(st + 4 * 64);
+      bs[j & 1] = as_bf16x8(make_uint4(r0.x, r0.y, r1.x, r1.y));
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const int kblk = 2 * kt + kb;
-      const bool act = live && kblk <= qblk;  // wavefront-uniform
-      const uint32_t st = st_lds + sb * (4 * DG_DS_B) + kb * 2048 + st_off;
+      for (int db = 0; db < 4; ++db)
+        a[j & 1][db] = tr_operand(ktr[db], BUF * kTileBytes + (32 * kb + 16 * c) * 256);
+    };
+    read(0);
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        // all of K(kt+1) before any of dS(kt+2): the wait above relies on
-        // dS(kt+1)'s copies being the last four issued
-        const int j = 2 * kb + c;
-        if (j < 2) {
-          if (more_k) {
-            issue_k(kt + 1, 1 - BUF, 2 * j);
-            issue_k(kt + 1, 1 - BUF, 2 * j + 1);
-          }
-        } else if (more_ds) {
-          issue_ds(kt + 2, (kt + 2) % 3, 2 * (j - 2));
-          issue_ds(kt + 2, (kt + 2) % 3, 2 * (j - 2) + 1);
+    for (int j = 0; j < 4; ++j) {
+      // all of K(kt+1) before any of dS(kt+2): the wait above relies on
+      // dS(kt+1)'s copies being the last four issued
+      if (j < 2) {
+        if (more_k) {
+          issue_k(kt + 1, 1 - BUF, 2 * j);
+          issue_k(kt + 1, 1 - BUF, 2 * j + 1);
         }
-        if (!act) continue;
-        // keys 32 kb + 16 c + 8 half + 0..7 (of this tile), query column l32
-        const uint2 r0 = ds_read_tr16_at(st + c * 16 * 64);
-        const uint2 r1 = ds_read_tr16_at(st + c * 16 * 64 + 4 * 64);
-        const bf16x8 bs = as_bf16x8(make_uint4(r0.x, r0.y, r1.x, r1.y));
-        bf16x8 a[4];
-#pragma unroll
-        for (int db = 0; db < 4; ++db)
-          a[db] = tr_operand(ktr[db], BUF * kTileBytes + (32 * kb + 16 * c) * 256);
-#pragma unroll
-        for (int db = 0; db < 4; ++db) dqa[db] = mfma32(a[db], bs, dqa[db]);
+      } else if (more_ds) {
+        issue_ds(kt + 2, (kt + 2) % 3, 2 * (j - 2));
+        issue_ds(kt + 2, (kt + 2) % 3, 2 * (j - 2) + 1);
       }
+      if (j + 1 < 4) read(j + 1);
+      // block 2 kt + kb of this wavefront's row exists (wavefront-uniform)
+      if (live && 2 * kt + (j >> 1) <= qblk) {
+#pragma unroll
+        for (int db = 0; db < 4; ++db) dqa[db] = mfma32(a[j & 1][db], bs[j & 1], dqa[db]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
