@@ -11,12 +11,14 @@
 //
 // Three kernels on one stream:
 //   delta_kernel    rowsum(dout * o)                      (HBM bound)
-//   dkdv_kernel     one workgroup per 128-key tile; K and V stay in registers
+//   dkdv_kernel     a 128-key tile per work item; K and V stay in registers
 //                   as MFMA operands, query tiles of 64 are copied HBM -> LDS
 //                   (triple-buffered, read row-wise and transposed);
 //                   accumulates dK, dV and, given a workspace, stores dS
-//   dq_gemm_kernel  with the dS workspace: one workgroup per 128-query tile,
+//   dq_gemm_kernel  with the dS workspace: a 128-query tile per work item,
 //                   dQ = s dS K over the stored blocks
+// Both run persistent workgroups (one / two per compute unit) that walk their
+// work items in a balanced order (persistent_item).
 //   dq_kernel       without it: one workgroup per 128-query tile; Q, dout stay
 //                   in registers, key tiles of 64 stream through LDS, S and dP
 //                   are recomputed; accumulates dQ
@@ -237,193 +239,200 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(
 
   const int BH = B * H;
   const int n_ktiles = (T + KT_KEYS - 1) / KT_KEYS;
-  int bh, kt;  // key tile 0 has the most work: first
-  xcd_tile_map_grouped(static_cast<int>(blockIdx.x), BH, n_ktiles, kHeadGroup, bh, kt);
-  const int b = bh / H, h = bh % H;
-  const int k0 = kt * KT_KEYS;
-  const int kw0 = k0 + 32 * wave;
-  const int rs = H * D;  // 32-bit row offsets within one (b, h) slice
-  const size_t base = static_cast<size_t>(b) * T * rs + static_cast<size_t>(h) * D;
-  const float* lse_bh = lse + static_cast<size_t>(bh) * T;
-  const float* del_bh = delta + static_cast<size_t>(bh) * T;
+  const int n_items = BH * n_ktiles;
+  for (int r = 0;; ++r) {
+    const int item = persistent_item(r);
+    if (item >= n_items) break;
+    // every wavefront is done with the previous item's LDS tiles
+    if (r > 0) __syncthreads();
+    int bh, kt;  // key tile 0 has the most work: first
+    xcd_tile_map_grouped(item, BH, n_ktiles, kHeadGroup, bh, kt);
+    const int b = bh / H, h = bh % H;
+    const int k0 = kt * KT_KEYS;
+    const int kw0 = k0 + 32 * wave;
+    const int rs = H * D;  // 32-bit row offsets within one (b, h) slice
+    const size_t base = static_cast<size_t>(b) * T * rs + static_cast<size_t>(h) * D;
+    const float* lse_bh = lse + static_cast<size_t>(bh) * T;
+    const float* del_bh = delta + static_cast<size_t>(bh) * T;
 
-  // K^T and V^T operands: lane holds row kw0 + l32 (see below),
-  // elements 16 kc + 8 half + 0..7.
-  const int krow = kw0 + l32;
-  bf16x8 kreg[8], vreg[8];
+    // K^T and V^T operands: lane holds row kw0 + l32 (see below),
+    // elements 16 kc + 8 half + 0..7.
+    const int krow = kw0 + l32;
+    bf16x8 kreg[8], vreg[8];
 
-  f32x16 dka[4], dva[4];
+    f32x16 dka[4], dva[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    dka[i] = f32x16{};
-    dva[i] = f32x16{};
-  }
-
-  const TileOffsets ofs = tile_operand_offsets(lane);
-  const uint32_t qt_lds = lds_addr(qtiles);
-  const uint32_t lsd_lds = lds_addr(&lsd[0][0][0]);
-  const uint32_t kst_lds = lds_addr(kstage);
-
-  // Tile copies (see copy_tile); wavefronts 0 and 1 also copy the lse and
-  // delta rows.  Rows past T are past the end of the buffer range and arrive
-  // as zeros: a zero query row with zero dout, lse and delta adds nothing to
-  // dK or dV.
-  const uint32_t rsb = static_cast<uint32_t>(rs) * 2;  // bytes between rows
-  const uint32_t dvoff = tile_copy_offset(wave, lane, rsb);
-  auto issue = [&](int qt, int u) {  // query tile qt -> buffer u
-    const int q0 = qt * QT_ROWS;
-    const uint32_t nrec = static_cast<uint32_t>(T - q0) * rsb;
-    const size_t off = base + static_cast<size_t>(q0) * rs;
-    copy_tile(buffer_rsrc(q + off, nrec), dvoff, rsb, qt_lds + u * BUF_B, wave);
-    copy_tile(buffer_rsrc(dout + off, nrec), dvoff, rsb, qt_lds + u * BUF_B + TILE_B, wave);
-    if (wave == 0)
-      dma4(buffer_rsrc(lse_bh + q0, static_cast<uint32_t>(T - q0) * 4), 4 * lane,
-           lsd_lds + u * 512);
-    if (wave == 1)
-      dma4(buffer_rsrc(del_bh + q0, static_cast<uint32_t>(T - q0) * 4), 4 * lane,
-           lsd_lds + u * 512 + 256);
-  };
-  // Every copy issued so far has landed and every wavefront is past its
-  // reads of the buffer that the next copy overwrites.
-  auto sync_tiles = [&]() {
-    wait_vmem();
-    __syncthreads();
-  };
-
-  // dS blocks of this wavefront's 32 keys (when a dS workspace is given).
-  // Only blocks with a query row < T exist in the packed layout; a block made
-  // of padding rows only (the tail of the last tile) is not stored.  Stored
-  // blocks always have kblk <= qblk.
-  const int kblk = kw0 / 32;
-  auto ds_of = [&](int qblk) -> u16* {
-    return (dsw && 32 * qblk < T) ? dsw + ds_block_index(bh, nbt, qblk, kblk) : nullptr;
-  };
-
-  // Query tile qt0 + u lives in buffer u % NBUF.  The workgroup's 128 K rows
-  // come through the staging region kst and its V rows through buffer 2 (rows
-  // 0..63, then 64..127), copied with 16 lanes per row together with query
-  // tiles qt0 and qt0 + 1; each lane then reads its row's operands.  Keys
-  // past T arrive as zeros: their gradients are never stored and, since every
-  // real query precedes them, the causal mask removes them from every real
-  // query's dS.
-  const int n_qt = (T + QT_ROWS - 1) / QT_ROWS;
-  const int qt0 = k0 / QT_ROWS;
-  {
-    const int nk = T - k0;  // >= 1
-    const uint32_t n0 = static_cast<uint32_t>(min(nk, 64)) * rsb;
-    const uint32_t n1 = static_cast<uint32_t>(max(nk - 64, 0)) * rsb;
-    const size_t off0 = base + static_cast<size_t>(k0) * rs;
-    const size_t off1 = off0 + static_cast<size_t>(64) * rs;
-    copy_tile(buffer_rsrc(k + off0, n0), dvoff, rsb, kst_lds, wave);
-    copy_tile(buffer_rsrc(k + off1, n1), dvoff, rsb, kst_lds + TILE_B, wave);
-    copy_tile(buffer_rsrc(v + off0, n0), dvoff, rsb, qt_lds + 2 * BUF_B, wave);
-    copy_tile(buffer_rsrc(v + off1, n1), dvoff, rsb, qt_lds + 2 * BUF_B + TILE_B, wave);
-  }
-  issue(qt0, 0);
-  if (qt0 + 1 < n_qt) issue(qt0 + 1, 1);
-  sync_tiles();
-  // The lse rows are used as -lse log2(e), the exponent offset of P in the
-  // exp2 domain: the wavefront that first sees a tile's rows land rewrites
-  // them in place (the next barrier publishes them).
-  if (wave < 2) to_exp2_offset(lsd[wave][0], lane);
-  {
-    const int rr = 32 * (wave & 1) + l32;  // row within the 64-row half
-    const uint32_t o_row = (wave >> 1) * TILE_B + rr * 256;
-#pragma unroll
-    for (int kc = 0; kc < 8; ++kc) {
-      const uint32_t o = o_row + 16 * ((2 * kc + half) ^ tile_swz(rr));
-      kreg[kc] = as_bf16x8(lds_ld16(kst_lds + o));
-      vreg[kc] = as_bf16x8(lds_ld16(qt_lds + 2 * BUF_B + o));
+    for (int i = 0; i < 4; ++i) {
+      dka[i] = f32x16{};
+      dva[i] = f32x16{};
     }
-  }
-  __syncthreads();  // buffer 2 is free again
-  if (qt0 + 2 < n_qt) issue(qt0 + 2, 2);
 
-  // One software pipeline over the 32-query blocks from the diagonal on: the
-  // step for block j computes the probabilities of j, the scores of j+1 and
-  // the dK/dV update of j.  This wavefront's first block is its diagonal
-  // block bw (masked); blocks before it hold no visible (query, key) pair and
-  // are skipped, and the slot of block bw - 1 computes bw's scores.  Tile t
-  // holds blocks 2t, 2t+1; block 2t+1's step reads the scores of block 2t+2
-  // from tile t+1.  At the sync before tile t (t > qt0) tile t+1 has landed
-  // and tile t-1's buffer is free for the copy of tile t+2.  After the last
-  // tile the second step still computes scores of a block past the end (from
-  // a stale buffer); they are never used.
-  const int bw = kw0 / 32;
-  f32x16 s0, p0, s1, p1;  // scores of even blocks in s0/p0, of odd blocks in s1/p1
-  uint32_t nc[8];         // row-read addresses of tile t
-  nat_addr(qt_lds, ofs, nc);
-  if (bw == 2 * qt0) dkdv_scores(nc, 0, kreg, vreg, s0, p0);
-  int u = 0;  // buffer of tile t
-  // The first two tiles (every diagonal block of the workgroup) take the
-  // per-wavefront branches; the rest run one branch-free body.
-  auto tile = [&](int t, auto steady) {
-    constexpr bool STEADY = decltype(steady)::value;
-    const int un = u == NBUF - 1 ? 0 : u + 1;  // buffer of tile t + 1
-    if (t > qt0) {
-      sync_tiles();
-      if (t + 2 < n_qt) issue(t + 2, un == NBUF - 1 ? 0 : un + 1);
-      if (t + 1 < n_qt && wave == 3) to_exp2_offset(lsd[un][0], lane);  // tile t+1
-    }
-    uint32_t tc[4][2], nn[8];
-    tr_addr(qt_lds + u * BUF_B, ofs, tc);
-    nat_addr(qt_lds + un * BUF_B, ofs, nn);
-    const int kq = krow - QT_ROWS * t;
-    const int j0 = 2 * t, j1 = 2 * t + 1;
-    // block j0 (rows 0..31 of tile t), scores of rows 32..63
-    if (STEADY || j0 > bw)
-      dkdv_step<false>(nc, 32, lsd[u][0], lsd[u][1], tc, 0, kreg, vreg, s0, p0, s1, p1, dka, dva,
-                       lane, c_log2, kq, ds_of(j0));
-    else if (j0 == bw)
-      dkdv_step<true>(nc, 32, lsd[u][0], lsd[u][1], tc, 0, kreg, vreg, s0, p0, s1, p1, dka, dva,
-                      lane, c_log2, kq, ds_of(j0));
-    else if (j0 == bw - 1)
-      dkdv_scores(nc, 32, kreg, vreg, s1, p1);
-    // block j1 (rows 32..63 of tile t), scores of tile t+1 rows 0..31
-    if (STEADY || j1 > bw)
-      dkdv_step<false>(nn, 0, lsd[u][0], lsd[u][1], tc, 32, kreg, vreg, s1, p1, s0, p0, dka, dva,
-                       lane, c_log2, kq, ds_of(j1));
-    else if (j1 == bw)
-      dkdv_step<true>(nn, 0, lsd[u][0], lsd[u][1], tc, 32, kreg, vreg, s1, p1, s0, p0, dka, dva,
-                      lane, c_log2, kq, ds_of(j1));
-    else if (j1 == bw - 1)
-      dkdv_scores(nn, 0, kreg, vreg, s0, p0);
-#pragma unroll
-    for (int kc = 0; kc < 8; ++kc) nc[kc] = nn[kc];
-    u = un;
-  };
-  const int t_diag_end = min(qt0 + 2, n_qt);
-  for (int t = qt0; t < t_diag_end; ++t) tile(t, std::false_type{});
-  for (int t = t_diag_end; t < n_qt; ++t) tile(t, std::true_type{});
+    const TileOffsets ofs = tile_operand_offsets(lane);
+    const uint32_t qt_lds = lds_addr(qtiles);
+    const uint32_t lsd_lds = lds_addr(&lsd[0][0][0]);
+    const uint32_t kst_lds = lds_addr(kstage);
 
-  // dka[db], dva[db] (dK^T, dV^T blocks) element r: key kw0 + l32,
-  // d = 32 db + 8 (r/4) + 4 half + r%4.  The rows leave through LDS so that 16
-  // lanes store one 256-byte row: stored straight from registers, every lane
-  // would write 8 bytes to a different row.  Staging rows are swizzled by
-  // 16-byte chunk (chunk c of row r at c ^ (r mod 16)).
-  __syncthreads();  // every wavefront is done with the query tiles
-  const uint32_t stg = qt_lds + wave * 16384;  // 32 dK rows, then 32 dV rows
-#pragma unroll
-  for (int db = 0; db < 4; ++db)
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int r = 4 * g;
-      const uint32_t off = l32 * 256 + 16 * ((4 * db + g) ^ (l32 & 15)) + 8 * half;
-      lds_st8(stg + off, pack_bf16x2(dka[db][r] * scale, dka[db][r + 1] * scale),
-              pack_bf16x2(dka[db][r + 2] * scale, dka[db][r + 3] * scale));
-      lds_st8(stg + 8192 + off, pack_bf16x2(dva[db][r], dva[db][r + 1]),
-              pack_bf16x2(dva[db][r + 2], dva[db][r + 3]));
+    // Tile copies (see copy_tile); wavefronts 0 and 1 also copy the lse and
+    // delta rows.  Rows past T are past the end of the buffer range and arrive
+    // as zeros: a zero query row with zero dout, lse and delta adds nothing to
+    // dK or dV.
+    const uint32_t rsb = static_cast<uint32_t>(rs) * 2;  // bytes between rows
+    const uint32_t dvoff = tile_copy_offset(wave, lane, rsb);
+    auto issue = [&](int qt, int u) {  // query tile qt -> buffer u
+      const int q0 = qt * QT_ROWS;
+      const uint32_t nrec = static_cast<uint32_t>(T - q0) * rsb;
+      const size_t off = base + static_cast<size_t>(q0) * rs;
+      copy_tile(buffer_rsrc(q + off, nrec), dvoff, rsb, qt_lds + u * BUF_B, wave);
+      copy_tile(buffer_rsrc(dout + off, nrec), dvoff, rsb, qt_lds + u * BUF_B + TILE_B, wave);
+      if (wave == 0)
+        dma4(buffer_rsrc(lse_bh + q0, static_cast<uint32_t>(T - q0) * 4), 4 * lane,
+             lsd_lds + u * 512);
+      if (wave == 1)
+        dma4(buffer_rsrc(del_bh + q0, static_cast<uint32_t>(T - q0) * 4), 4 * lane,
+             lsd_lds + u * 512 + 256);
+    };
+    // Every copy issued so far has landed and every wavefront is past its
+    // reads of the buffer that the next copy overwrites.
+    auto sync_tiles = [&]() {
+      wait_vmem();
+      __syncthreads();
+    };
+
+    // dS blocks of this wavefront's 32 keys (when a dS workspace is given).
+    // Only blocks with a query row < T exist in the packed layout; a block made
+    // of padding rows only (the tail of the last tile) is not stored.  Stored
+    // blocks always have kblk <= qblk.
+    const int kblk = kw0 / 32;
+    auto ds_of = [&](int qblk) -> u16* {
+      return (dsw && 32 * qblk < T) ? dsw + ds_block_index(bh, nbt, qblk, kblk) : nullptr;
+    };
+
+    // Query tile qt0 + u lives in buffer u % NBUF.  The workgroup's 128 K rows
+    // come through the staging region kst and its V rows through buffer 2 (rows
+    // 0..63, then 64..127), copied with 16 lanes per row together with query
+    // tiles qt0 and qt0 + 1; each lane then reads its row's operands.  Keys
+    // past T arrive as zeros: their gradients are never stored and, since every
+    // real query precedes them, the causal mask removes them from every real
+    // query's dS.
+    const int n_qt = (T + QT_ROWS - 1) / QT_ROWS;
+    const int qt0 = k0 / QT_ROWS;
+    {
+      const int nk = T - k0;  // >= 1
+      const uint32_t n0 = static_cast<uint32_t>(min(nk, 64)) * rsb;
+      const uint32_t n1 = static_cast<uint32_t>(max(nk - 64, 0)) * rsb;
+      const size_t off0 = base + static_cast<size_t>(k0) * rs;
+      const size_t off1 = off0 + static_cast<size_t>(64) * rs;
+      copy_tile(buffer_rsrc(k + off0, n0), dvoff, rsb, kst_lds, wave);
+      copy_tile(buffer_rsrc(k + off1, n1), dvoff, rsb, kst_lds + TILE_B, wave);
+      copy_tile(buffer_rsrc(v + off0, n0), dvoff, rsb, qt_lds + 2 * BUF_B, wave);
+      copy_tile(buffer_rsrc(v + off1, n1), dvoff, rsb, qt_lds + 2 * BUF_B + TILE_B, wave);
     }
-  // lane i copies chunk i % 16 of rows 4 m + i / 16
+    issue(qt0, 0);
+    if (qt0 + 1 < n_qt) issue(qt0 + 1, 1);
+    sync_tiles();
+    // The lse rows are used as -lse log2(e), the exponent offset of P in the
+    // exp2 domain: the wavefront that first sees a tile's rows land rewrites
+    // them in place (the next barrier publishes them).
+    if (wave < 2) to_exp2_offset(lsd[wave][0], lane);
+    {
+      const int rr = 32 * (wave & 1) + l32;  // row within the 64-row half
+      const uint32_t o_row = (wave >> 1) * TILE_B + rr * 256;
 #pragma unroll
-  for (int m = 0; m < 8; ++m) {
-    const int r = 4 * m + (lane >> 4), c = lane & 15;
-    const uint32_t off = r * 256 + 16 * (c ^ (r & 15));
-    const uint4 xk = lds_ld16(stg + off);
-    const uint4 xv = lds_ld16(stg + 8192 + off);
-    if (kw0 + r < T) {
-      st16(dk + base + (kw0 + r) * rs + 8 * c, xk);
-      st16(dv + base + (kw0 + r) * rs + 8 * c, xv);
+      for (int kc = 0; kc < 8; ++kc) {
+        const uint32_t o = o_row + 16 * ((2 * kc + half) ^ tile_swz(rr));
+        kreg[kc] = as_bf16x8(lds_ld16(kst_lds + o));
+        vreg[kc] = as_bf16x8(lds_ld16(qt_lds + 2 * BUF_B + o));
+      }
+    }
+    __syncthreads();  // buffer 2 is free again
+    if (qt0 + 2 < n_qt) issue(qt0 + 2, 2);
+
+    // One software pipeline over the 32-query blocks from the diagonal on: the
+    // step for block j computes the probabilities of j, the scores of j+1 and
+    // the dK/dV update of j.  This wavefront's first block is its diagonal
+    // block bw (masked); blocks before it hold no visible (query, key) pair and
+    // are skipped, and the slot of block bw - 1 computes bw's scores.  Tile t
+    // holds blocks 2t, 2t+1; block 2t+1's step reads the scores of block 2t+2
+    // from tile t+1.  At the sync before tile t (t > qt0) tile t+1 has landed
+    // and tile t-1's buffer is free for the copy of tile t+2.  After the last
+    // tile the second step still computes scores of a block past the end (from
+    // a stale buffer); they are never used.
+    const int bw = kw0 / 32;
+    f32x16 s0, p0, s1, p1;  // scores of even blocks in s0/p0, of odd blocks in s1/p1
+    uint32_t nc[8];         // row-read addresses of tile t
+    nat_addr(qt_lds, ofs, nc);
+    if (bw == 2 * qt0) dkdv_scores(nc, 0, kreg, vreg, s0, p0);
+    int u = 0;  // buffer of tile t
+    // The first two tiles (every diagonal block of the workgroup) take the
+    // per-wavefront branches; the rest run one branch-free body.
+    auto tile = [&](int t, auto steady) {
+      constexpr bool STEADY = decltype(steady)::value;
+      const int un = u == NBUF - 1 ? 0 : u + 1;  // buffer of tile t + 1
+      if (t > qt0) {
+        sync_tiles();
+        if (t + 2 < n_qt) issue(t + 2, un == NBUF - 1 ? 0 : un + 1);
+        if (t + 1 < n_qt && wave == 3) to_exp2_offset(lsd[un][0], lane);  // tile t+1
+      }
+      uint32_t tc[4][2], nn[8];
+      tr_addr(qt_lds + u * BUF_B, ofs, tc);
+      nat_addr(qt_lds + un * BUF_B, ofs, nn);
+      const int kq = krow - QT_ROWS * t;
+      const int j0 = 2 * t, j1 = 2 * t + 1;
+      // block j0 (rows 0..31 of tile t), scores of rows 32..63
+      if (STEADY || j0 > bw)
+        dkdv_step<false>(nc, 32, lsd[u][0], lsd[u][1], tc, 0, kreg, vreg, s0, p0, s1, p1, dka, dva,
+                         lane, c_log2, kq, ds_of(j0));
+      else if (j0 == bw)
+        dkdv_step<true>(nc, 32, lsd[u][0], lsd[u][1], tc, 0, kreg, vreg, s0, p0, s1, p1, dka, dva,
+                        lane, c_log2, kq, ds_of(j0));
+      else if (j0 == bw - 1)
+        dkdv_scores(nc, 32, kreg, vreg, s1, p1);
+      // block j1 (rows 32..63 of tile t), scores of tile t+1 rows 0..31
+      if (STEADY || j1 > bw)
+        dkdv_step<false>(nn, 0, lsd[u][0], lsd[u][1], tc, 32, kreg, vreg, s1, p1, s0, p0, dka, dva,
+                         lane, c_log2, kq, ds_of(j1));
+      else if (j1 == bw)
+        dkdv_step<true>(nn, 0, lsd[u][0], lsd[u][1], tc, 32, kreg, vreg, s1, p1, s0, p0, dka, dva,
+                        lane, c_log2, kq, ds_of(j1));
+      else if (j1 == bw - 1)
+        dkdv_scores(nn, 0, kreg, vreg, s0, p0);
+#pragma unroll
+      for (int kc = 0; kc < 8; ++kc) nc[kc] = nn[kc];
+      u = un;
+    };
+    const int t_diag_end = min(qt0 + 2, n_qt);
+    for (int t = qt0; t < t_diag_end; ++t) tile(t, std::false_type{});
+    for (int t = t_diag_end; t < n_qt; ++t) tile(t, std::true_type{});
+
+    // dka[db], dva[db] (dK^T, dV^T blocks) element r: key kw0 + l32,
+    // d = 32 db + 8 (r/4) + 4 half + r%4.  The rows leave through LDS so that 16
+    // lanes store one 256-byte row: stored straight from registers, every lane
+    // would write 8 bytes to a different row.  Staging rows are swizzled by
+    // 16-byte chunk (chunk c of row r at c ^ (r mod 16)).
+    __syncthreads();  // every wavefront is done with the query tiles
+    const uint32_t stg = qt_lds + wave * 16384;  // 32 dK rows, then 32 dV rows
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int r = 4 * g;
+        const uint32_t off = l32 * 256 + 16 * ((4 * db + g) ^ (l32 & 15)) + 8 * half;
+        lds_st8(stg + off, pack_bf16x2(dka[db][r] * scale, dka[db][r + 1] * scale),
+                pack_bf16x2(dka[db][r + 2] * scale, dka[db][r + 3] * scale));
+        lds_st8(stg + 8192 + off, pack_bf16x2(dva[db][r], dva[db][r + 1]),
+                pack_bf16x2(dva[db][r + 2], dva[db][r + 3]));
+      }
+    // lane i copies chunk i % 16 of rows 4 m + i / 16
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      const int r = 4 * m + (lane >> 4), c = lane & 15;
+      const uint32_t off = r * 256 + 16 * (c ^ (r & 15));
+      const uint4 xk = lds_ld16(stg + off);
+      const uint4 xv = lds_ld16(stg + 8192 + off);
+      if (kw0 + r < T) {
+        st16(dk + base + (kw0 + r) * rs + 8 * c, xk);
+        st16(dv + base + (kw0 + r) * rs + 8 * c, xv);
+      }
     }
   }
 }
@@ -707,132 +716,142 @@ __global__ __launch_bounds__(256, 2) void dq_gemm_kernel(const u16* __restrict__
 
   const int BH = B * H;
   const int n_qt = (T + DG_ROWS - 1) / DG_ROWS;
-  int bh, t;
-  xcd_tile_map_grouped(static_cast<int>(blockIdx.x), BH, n_qt, kHeadGroup, bh, t);
-  const int qt = n_qt - 1 - t;  // heaviest (last) query tile first
-  const int b = bh / H, h = bh % H;
-  const int q0 = qt * DG_ROWS;
-  const int qw0 = q0 + 32 * wave;
-  const int qblk = qw0 / 32;
-  const bool live = qw0 < T;  // wavefront has at least one real query row
-  const int rs = H * D;
-  const size_t base = static_cast<size_t>(b) * T * rs + static_cast<size_t>(h) * D;
-  // this wavefront's row of dS blocks: (qblk, 0 .. qblk), 2 KiB each, contiguous
-  const u16* dsrow = dsw + ds_block_index(bh, nbt, qblk, 0);
+  const int n_items = BH * n_qt;
+  for (int r = 0;; ++r) {
+    const int item = persistent_item(r);
+    if (item >= n_items) break;
+    // every wavefront is done with the previous item's LDS tiles
+    if (r > 0) __syncthreads();
+    int bh, t;
+    // heads last-first: the dK/dV pass stored their dS last, so part of it
+    // may still sit in the last-level cache
+    xcd_tile_map_grouped(item, BH, n_qt, kHeadGroup, bh, t, true);
+    const int qt = n_qt - 1 - t;  // heaviest (last) query tile first
+    const int b = bh / H, h = bh % H;
+    const int q0 = qt * DG_ROWS;
+    const int qw0 = q0 + 32 * wave;
+    const int qblk = qw0 / 32;
+    const bool live = qw0 < T;  // wavefront has at least one real query row
+    const int rs = H * D;
+    const size_t base = static_cast<size_t>(b) * T * rs + static_cast<size_t>(h) * D;
+    // this wavefront's row of dS blocks: (qblk, 0 .. qblk), 2 KiB each, contiguous
+    const u16* dsrow = dsw + ds_block_index(bh, nbt, qblk, 0);
 
-  f32x16 dqa[4];
+    f32x16 dqa[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) dqa[i] = f32x16{};
+    for (int i = 0; i < 4; ++i) dqa[i] = f32x16{};
 
-  const int last_q = min(q0 + DG_ROWS, T) - 1;
-  const int n_kt = last_q / DG_KEYS + 1;
+    const int last_q = min(q0 + DG_ROWS, T) - 1;
+    const int n_kt = last_q / DG_KEYS + 1;
 
-  // K^T read addresses in buffer 0 (buffer 1: + kTileBytes)
-  uint32_t ktr[4][2];
-  {
-    const TileOffsets ofs = tile_operand_offsets(lane);
-    tr_addr(lds_addr(ktile), ofs, ktr);
-  }
-  // dS^T reads: 16-lane group gi supplies keys 16 c + 8 half + 4 sub + i16 / 4,
-  // queries 16 (gi & 1) + 4 (i16 & 3) of a block stored [key][query]
-  const uint32_t st_lds = lds_addr(&sst[0][wave][0]);
-  const uint32_t st_off =
-      ((8 * half + (i16 >> 2)) * 32 + 16 * (gi & 1) + 4 * (i16 & 3)) * 2;
-  const uint32_t rsb = static_cast<uint32_t>(rs) * 2;
-  const uint32_t kvoff = tile_copy_offset(wave, lane, rsb);
-  const uint32_t kt_lds = lds_addr(ktile);
-  // the wavefront's blocks of key tile kt: kblk = 2 kt, 2 kt + 1 (if <= qblk)
-  const uint32_t ds_rows = static_cast<uint32_t>(qblk + 1) * 2048;  // bytes of its row
-  const i32x4 ds_rsrc = buffer_rsrc(dsrow, live ? ds_rows : 0);
-  // Copy j (0..3) of this wavefront's share of K tile kt / of its dS blocks
-  // of key tile kt.  The copies of the next tiles are spread between the
-  // current tile's MFMAs: issued in a burst they stall the issuing wavefront
-  // behind the compute unit's vector-memory queue.
-  auto issue_k = [&](int kt, int buf, int j) {
-    const int k0 = kt * DG_KEYS;
-    const uint32_t nrec = static_cast<uint32_t>(T - k0) * rsb;  // keys past T read as 0
-    dma16(buffer_rsrc(k + base + static_cast<size_t>(k0) * rs, nrec), kvoff + 16 * j * rsb,
-          kt_lds + buf * kTileBytes + 1024 * wave + 4096 * j);
-  };
-  auto issue_ds = [&](int kt, int sbuf, int j) {
-    // blocks past qblk are past the resource's end (zeros, never read)
-    dma16(ds_rsrc, kt * 4096 + j * 1024 + 16 * lane, st_lds + sbuf * (4 * DG_DS_B) + j * 1024);
-  };
+    // K^T read addresses in buffer 0 (buffer 1: + kTileBytes)
+    uint32_t ktr[4][2];
+    {
+      const TileOffsets ofs = tile_operand_offsets(lane);
+      tr_addr(lds_addr(ktile), ofs, ktr);
+    }
+    // dS^T reads: 16-lane group gi supplies keys 16 c + 8 half + 4 sub + i16 / 4,
+    // queries 16 (gi & 1) + 4 (i16 & 3) of a block stored [key][query]
+    const uint32_t st_lds = lds_addr(&sst[0][wave][0]);
+    const uint32_t st_off =
+        ((8 * half + (i16 >> 2)) * 32 + 16 * (gi & 1) + 4 * (i16 & 3)) * 2;
+    const uint32_t rsb = static_cast<uint32_t>(rs) * 2;
+    const uint32_t kvoff = tile_copy_offset(wave, lane, rsb);
+    const uint32_t kt_lds = lds_addr(ktile);
+    // the wavefront's blocks of key tile kt: kblk = 2 kt, 2 kt + 1 (if <= qblk)
+    const uint32_t ds_rows = static_cast<uint32_t>(qblk + 1) * 2048;  // bytes of its row
+    const i32x4 ds_rsrc = buffer_rsrc(dsrow, live ? ds_rows : 0);
+    // Copy j (0..3) of this wavefront's share of K tile kt / of its dS blocks
+    // of key tile kt.  The copies of the next tiles are spread between the
+    // current tile's MFMAs: issued in a burst they stall the issuing wavefront
+    // behind the compute unit's vector-memory queue.
+    auto issue_k = [&](int kt, int buf, int j) {
+      const int k0 = kt * DG_KEYS;
+      const uint32_t nrec = static_cast<uint32_t>(T - k0) * rsb;  // keys past T read as 0
+      dma16(buffer_rsrc(k + base + static_cast<size_t>(k0) * rs, nrec), kvoff + 16 * j * rsb,
+            kt_lds + buf * kTileBytes + 1024 * wave + 4096 * j);
+    };
+    auto issue_ds = [&](int kt, int sbuf, int j) {
+      // blocks past qblk are past the resource's end (zeros, never read)
+      dma16(ds_rsrc, kt * 4096 + j * 1024 + 16 * lane, st_lds + sbuf * (4 * DG_DS_B) + j * 1024);
+    };
 
-  // Copies in issue order: K(0), dS(0), dS(1), then per tile t: K(t+1),
-  // dS(t+2).  At tile t, K(t) and dS(t) must have landed while dS(t+1) (the
-  // last 4 copies issued, if it exists) may still be in flight.
-  auto tile = [&](auto bufc, int kt) {
-    constexpr uint32_t BUF = decltype(bufc)::value;
-    const int sb = kt % 3;
-    if (kt + 1 < n_kt)
-      wait_vmem_but<4>();
-    else
-      wait_vmem();
-    __syncthreads();
-    const bool more_k = kt + 1 < n_kt, more_ds = kt + 2 < n_kt;
-    // Four chunks of 16 keys, j = 2 kb + c (keys 32 kb + 16 c .. + 15 of the
-    // tile); chunk j+1's operands are read while chunk j's MFMAs run.
-    bf16x8 a[2][4], bs[2];
-    auto read = [&](int j) {
-      const int kb = j >> 1, c = j & 1;
-      // keys 32 kb + 16 c + 8 half + 0..7, query column l32
-      const uint32_t st = st_lds + sb * (4 * DG_DS_B) + kb * 2048 + st_off + c * 16 * 64;
-      const uint2 r0 = ds_read_tr16_at(st);
-      const uint2 r1 = ds_read_tr16_at(st + 4 * 64);
-      bs[j & 1] = as_bf16x8(make_uint4(r0.x, r0.y, r1.x, r1.y));
+    // Copies in issue order: K(0), dS(0), dS(1), then per tile t: K(t+1),
+    // dS(t+2).  At tile t, K(t) and dS(t) must have landed while dS(t+1) (the
+    // last 4 copies issued, if it exists) may still be in flight.
+    auto tile = [&](auto bufc, int kt) {
+      constexpr uint32_t BUF = decltype(bufc)::value;
+      const int sb = kt % 3;
+      if (kt + 1 < n_kt)
+        wait_vmem_but<4>();
+      else
+        wait_vmem();
+      __syncthreads();
+      const bool more_k = kt + 1 < n_kt, more_ds = kt + 2 < n_kt;
+      // Four chunks of 16 keys, j = 2 kb + c (keys 32 kb + 16 c .. + 15 of the
+      // tile); chunk j+1's operands are read while chunk j's MFMAs run.
+      bf16x8 a[2][4], bs[2];
+      auto read = [&](int j) {
+        const int kb = j >> 1, c = j & 1;
+        // keys 32 kb + 16 c + 8 half + 0..7, query column l32
+        const uint32_t st = st_lds + sb * (4 * DG_DS_B) + kb * 2048 + st_off + c * 16 * 64;
+        const uint2 r0 = ds_read_tr16_at(st);
+        const uint2 r1 = ds_read_tr16_at(st + 4 * 64);
+        bs[j & 1] = as_bf16x8(make_uint4(r0.x, r0.y, r1.x, r1.y));
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+          a[j & 1][db] = tr_operand(ktr[db], BUF * kTileBytes + (32 * kb + 16 * c) * 256);
+      };
+      read(0);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        // all of K(kt+1) before any of dS(kt+2): the wait above relies on
+        // dS(kt+1)'s copies being the last four issued
+        if (j < 2) {
+          if (more_k) {
+            issue_k(kt + 1, 1 - BUF, 2 * j);
+            issue_k(kt + 1, 1 - BUF, 2 * j + 1);
+          }
+        } else if (more_ds) {
+          issue_ds(kt + 2, (kt + 2) % 3, 2 * (j - 2));
+          issue_ds(kt + 2, (kt + 2) % 3, 2 * (j - 2) + 1);
+        }
+        if (j + 1 < 4) read(j + 1);
+        // block 2 kt + kb of this wavefront's row exists (wavefront-uniform)
+        if (live && 2 * kt + (j >> 1) <= qblk) {
+#pragma unroll
+          for (int db = 0; db < 4; ++db) dqa[db] = mfma32(a[j & 1][db], bs[j & 1], dqa[db]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+
+#pragma unroll
+    for (int j = 0; j < 4; ++j) issue_k(0, 0, j);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) issue_ds(0, 0, j);
+    if (n_kt > 1) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) issue_ds(1, 1, j);
+    }
+    for (int kt = 0; kt < n_kt; kt += 2) {
+      tile(std::integral_constant<uint32_t, 0>{}, kt);
+      if (kt + 1 < n_kt) tile(std::integral_constant<uint32_t, 1>{}, kt + 1);
+    }
+
+    const int qrow = qw0 + l32;
+    if (qrow < T) {
+      u16* qp = dq + base + qrow * rs;
 #pragma unroll
       for (int db = 0; db < 4; ++db)
-        a[j & 1][db] = tr_operand(ktr[db], BUF * kTileBytes + (32 * kb + 16 * c) * 256);
-    };
-    read(0);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      // all of K(kt+1) before any of dS(kt+2): the wait above relies on
-      // dS(kt+1)'s copies being the last four issued
-      if (j < 2) {
-        if (more_k) {
-          issue_k(kt + 1, 1 - BUF, 2 * j);
-          issue_k(kt + 1, 1 - BUF, 2 * j + 1);
+        for (int g = 0; g < 4; ++g) {
+          uint2 pk = make_uint2(
+              pack_bf16x2(dqa[db][4 * g] * scale, dqa[db][4 * g + 1] * scale),
+              pack_bf16x2(dqa[db][4 * g + 2] * scale, dqa[db][4 * g + 3] * scale));
+          *reinterpret_cast<uint2*>(qp + 32 * db + 8 * g + 4 * half) = pk;
         }
-      } else if (more_ds) {
-        issue_ds(kt + 2, (kt + 2) % 3, 2 * (j - 2));
-        issue_ds(kt + 2, (kt + 2) % 3, 2 * (j - 2) + 1);
-      }
-      if (j + 1 < 4) read(j + 1);
-      // block 2 kt + kb of this wavefront's row exists (wavefront-uniform)
-      if (live && 2 * kt + (j >> 1) <= qblk) {
-#pragma unroll
-        for (int db = 0; db < 4; ++db) dqa[db] = mfma32(a[j & 1][db], bs[j & 1], dqa[db]);
-      }
-      __builtin_amdgcn_sched_barrier(0);
     }
-  };
-
-#pragma unroll
-  for (int j = 0; j < 4; ++j) issue_k(0, 0, j);
-#pragma unroll
-  for (int j = 0; j < 4; ++j) issue_ds(0, 0, j);
-  if (n_kt > 1) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) issue_ds(1, 1, j);
-  }
-  for (int kt = 0; kt < n_kt; kt += 2) {
-    tile(std::integral_constant<uint32_t, 0>{}, kt);
-    if (kt + 1 < n_kt) tile(std::integral_constant<uint32_t, 1>{}, kt + 1);
-  }
-
-  const int qrow = qw0 + l32;
-  if (qrow < T) {
-    u16* qp = dq + base + qrow * rs;
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        uint2 pk = make_uint2(pack_bf16x2(dqa[db][4 * g] * scale, dqa[db][4 * g + 1] * scale),
-                              pack_bf16x2(dqa[db][4 * g + 2] * scale, dqa[db][4 * g + 3] * scale));
-        *reinterpret_cast<uint2*>(qp + 32 * db + 8 * g + 4 * half) = pk;
-      }
   }
 }
 
@@ -864,14 +883,16 @@ hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const vo
   if (e != hipSuccess) return e;
   if ((e = mark(ev, 1, s)) != hipSuccess) return e;
   const int n_kt = (T + KT_KEYS - 1) / KT_KEYS;
-  e = launch(dkdv_kernel, dim3(static_cast<unsigned>(n_kt) * B * H), dim3(256), 0, s, q16, k16,
-             v16, g16, lse, static_cast<const float*>(delta), static_cast<u16*>(dk),
-             static_cast<u16*>(dv), dsw, nbt, B, T, H, c_log2, scale);
+  const dim3 kv_grid(persistent_grid(static_cast<long>(n_kt) * B * H, 1));
+  e = launch(dkdv_kernel, kv_grid, dim3(256), 0, s, q16, k16, v16, g16, lse,
+             static_cast<const float*>(delta), static_cast<u16*>(dk), static_cast<u16*>(dv), dsw,
+             nbt, B, T, H, c_log2, scale);
   if (e != hipSuccess) return e;
   if ((e = mark(ev, 2, s)) != hipSuccess) return e;
   if (dsw != nullptr) {
     const int n_qt = (T + DG_ROWS - 1) / DG_ROWS;
-    e = launch(dq_gemm_kernel, dim3(static_cast<unsigned>(n_qt) * B * H), dim3(256), 0, s, k16,
+    e = launch(dq_gemm_kernel, dim3(persistent_grid(static_cast<long>(n_qt) * B * H, 2)),
+               dim3(256), 0, s, k16,
                static_cast<const u16*>(dsw), static_cast<u16*>(dq), nbt, B, T, H, scale);
   } else {
     const int n_qt = (T + DQ_ROWS - 1) / DQ_ROWS;

@@ -277,8 +277,10 @@ __device__ __forceinline__ void copy_tile(i32x4 rsrc, uint32_t voff, uint32_t rs
 // group's rows still fit the XCD's L2 and the shared last-level cache.
 constexpr int kHeadGroup = 4;  // heads per group (measured best for the d12..d26 shapes)
 
+// reverse_heads: an XCD takes its heads last-first (the tile order inside a
+// group is kept), e.g. to read first what a preceding pass wrote last.
 __device__ __forceinline__ void xcd_tile_map_grouped(int bid, int BH, int n_tiles, int G, int& bh,
-                                                     int& t) {
+                                                     int& t, bool reverse_heads = false) {
   constexpr int kXcds = 8;
   if (BH % kXcds != 0) {
     bh = bid % BH;
@@ -291,7 +293,27 @@ __device__ __forceinline__ void xcd_tile_map_grouped(int bid, int BH, int n_tile
   const int gsz = min(G, hpx - grp * G);
   const int i = w - grp * G * n_tiles;
   t = i / gsz;
-  bh = x + kXcds * (grp * G + i % gsz);
+  const int hl = grp * G + i % gsz;  // head of this XCD
+  bh = x + kXcds * (reverse_heads ? hpx - 1 - hl : hl);
+}
+
+// Persistent grids: one workgroup per slot (compute units x workgroups per
+// compute unit), each taking work items round by round until they run out.
+// Round r of workgroup w takes the virtual block index 8 j + w mod 8, so the
+// item stays on the XCD the hardware gives workgroup w (w mod 8) and
+// xcd_tile_map_grouped's order applies; the XCD's local order (heaviest tile
+// first within each group of heads) is dealt to its W = gridDim / 8
+// workgroups boustrophedon, j = r W + (r odd ? W - 1 - l : l) with l = w / 8,
+// so a workgroup that drew a heavy tile in one round draws a light one in the
+// next.  Indices grow with r: the first one past the item count ends the walk.
+// The hardware dispatcher, fed one workgroup per item, leaves a slot idle for
+// microseconds after a short workgroup ends.
+__device__ __forceinline__ int persistent_item(int r) {
+  const int w = static_cast<int>(blockIdx.x), G = static_cast<int>(gridDim.x);
+  if (G % 8 != 0) return w + r * G;
+  const int W = G / 8, l = w / 8;
+  const int j = r * W + ((r & 1) ? W - 1 - l : l);
+  return 8 * j + (w & 7);
 }
 
 // ---------------------------------------------------------------------------

@@ -33,6 +33,29 @@ hipError_t launch_decode_bf16(const void* q, const void* kc, const void* vc, con
                               void* o, float* lse, int B, int H, int T_cap, void* ws,
                               hipStream_t s, hipEvent_t const* ev = nullptr);
 
+// Compute units of the current device (cached per device; 256 if the query
+// fails).  Persistent grids size themselves from it.
+inline int device_cus() {
+  static int cached[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+      cus = 256;
+    cached[dev] = cus;
+  }
+  return cached[dev];
+}
+
+// Grid of a persistent kernel: per_cu workgroups per compute unit, never more
+// than there are items.
+inline unsigned persistent_grid(long items, int per_cu) {
+  const long slots = static_cast<long>(device_cus()) * per_cu;
+  return static_cast<unsigned>(items < slots ? items : slots);
+}
+
 // Records ev[i] on s when timing events were supplied.
 inline hipError_t mark(hipEvent_t const* ev, int i, hipStream_t s) {
   return ev ? hipEventRecord(ev[i], s) : hipSuccess;
