@@ -228,8 +228,9 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(
     int H, float c_log2, float scale) {
   // NBUF query tiles (q and dout, swizzled, see tile_swz) and their lse, delta rows
   __shared__ __attribute__((aligned(1024))) char qtiles[NBUF * BUF_B];
-  __shared__ __attribute__((aligned(1024))) char kstage[2 * TILE_B];  // K rows at start
+  __shared__ __attribute__((aligned(1024))) char kstage[2 * TILE_B];  // K rows of an item
   __shared__ __attribute__((aligned(16))) float lsd[NBUF][2][QT_ROWS];
+  __shared__ __attribute__((aligned(1024))) char estage[4][4096];  // dK, dV rows on the way out
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -240,25 +241,119 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(
   const int BH = B * H;
   const int n_ktiles = (T + KT_KEYS - 1) / KT_KEYS;
   const int n_items = BH * n_ktiles;
-  for (int r = 0;; ++r) {
-    const int item = persistent_item(r);
-    if (item >= n_items) break;
-    // every wavefront is done with the previous item's LDS tiles
-    if (r > 0) __syncthreads();
-    int bh, kt;  // key tile 0 has the most work: first
-    xcd_tile_map_grouped(item, BH, n_ktiles, kHeadGroup, bh, kt);
-    const int b = bh / H, h = bh % H;
-    const int k0 = kt * KT_KEYS;
-    const int kw0 = k0 + 32 * wave;
-    const int rs = H * D;  // 32-bit row offsets within one (b, h) slice
-    const size_t base = static_cast<size_t>(b) * T * rs + static_cast<size_t>(h) * D;
-    const float* lse_bh = lse + static_cast<size_t>(bh) * T;
-    const float* del_bh = delta + static_cast<size_t>(bh) * T;
+  const int n_qt = (T + QT_ROWS - 1) / QT_ROWS;
+  const int rs = H * D;  // 32-bit row offsets within one (b, h) slice
+  const uint32_t rsb = static_cast<uint32_t>(rs) * 2;  // bytes between rows
+  const uint32_t dvoff = tile_copy_offset(wave, lane, rsb);
+  const TileOffsets ofs = tile_operand_offsets(lane);
+  const uint32_t qt_lds = lds_addr(qtiles);
+  const uint32_t lsd_lds = lds_addr(&lsd[0][0][0]);
+  const uint32_t kst_lds = lds_addr(kstage);
+  const uint32_t est_lds = lds_addr(&estage[wave][0]);
 
-    // K^T and V^T operands: lane holds row kw0 + l32 (see below),
-    // elements 16 kc + 8 half + 0..7.
+  // A work item: the 128-key tile k0 / 128 of head bh (xcd_tile_map_grouped
+  // order, key tile 0, the one with the most work, first).
+  struct Item {
+    int bh, k0, qt0;
+    size_t base;
+  };
+  auto item_at = [&](int r, Item& it) -> bool {
+    const int vb = persistent_item(r);
+    if (vb >= n_items) return false;
+    int bh, kt;
+    xcd_tile_map_grouped(vb, BH, n_ktiles, kHeadGroup, bh, kt);
+    it.bh = bh;
+    it.k0 = kt * KT_KEYS;
+    it.qt0 = it.k0 / QT_ROWS;
+    it.base = static_cast<size_t>(bh / H) * T * rs + static_cast<size_t>(bh % H) * D;
+    return true;
+  };
+
+  // Query tile qt of item it -> buffer u (see copy_tile); wavefronts 0 and 1
+  // also copy its lse and delta rows.  Rows past T are past the end of the
+  // buffer range and arrive as zeros: a zero query row with zero dout, lse and
+  // delta adds nothing to dK or dV.
+  auto issue = [&](const Item& it, int qt, int u) {
+    const int q0 = qt * QT_ROWS;
+    const uint32_t nrec = static_cast<uint32_t>(T - q0) * rsb;
+    const size_t off = it.base + static_cast<size_t>(q0) * rs;
+    copy_tile(buffer_rsrc(q + off, nrec), dvoff, rsb, qt_lds + u * BUF_B, wave);
+    copy_tile(buffer_rsrc(dout + off, nrec), dvoff, rsb, qt_lds + u * BUF_B + TILE_B, wave);
+    const size_t row0 = static_cast<size_t>(it.bh) * T + q0;
+    if (wave == 0)
+      dma4(buffer_rsrc(lse + row0, static_cast<uint32_t>(T - q0) * 4), 4 * lane,
+           lsd_lds + u * 512);
+    if (wave == 1)
+      dma4(buffer_rsrc(delta + row0, static_cast<uint32_t>(T - q0) * 4), 4 * lane,
+           lsd_lds + u * 512 + 256);
+  };
+  // The 128 K (or V) rows of item it -> LDS at dst (two swizzled 64-row tiles).
+  // Keys past T arrive as zeros: their gradients are never stored and, since
+  // every real query precedes them, the causal mask removes them from every
+  // real query's dS.
+  auto copy_rows = [&](const Item& it, const u16* src, uint32_t dst) {
+    const int nk = T - it.k0;  // >= 1
+    const uint32_t n0 = static_cast<uint32_t>(min(nk, 64)) * rsb;
+    const uint32_t n1 = static_cast<uint32_t>(max(nk - 64, 0)) * rsb;
+    const size_t off0 = it.base + static_cast<size_t>(it.k0) * rs;
+    copy_tile(buffer_rsrc(src + off0, n0), dvoff, rsb, dst, wave);
+    copy_tile(buffer_rsrc(src + off0 + static_cast<size_t>(64) * rs, n1), dvoff, rsb,
+              dst + TILE_B, wave);
+  };
+  // Every copy issued so far has landed and every wavefront is past its
+  // reads of the buffer that the next copy overwrites.
+  auto sync_tiles = [&]() {
+    wait_vmem();
+    __syncthreads();
+  };
+
+  // The query tiles of the items form one stream through the NBUF buffers:
+  // the item whose first tile sits in buffer gb has tile qt0 + i in buffer
+  // (gb + i) % NBUF, and the next item's first tiles follow on.  The copies
+  // of the next item's K rows, of its first two query tiles and (once the last
+  // tile is done) of its V rows overlap the end of the current item, so only
+  // the register reads of K and V remain between two items.
+  Item cur, nxt;
+  if (!item_at(0, cur)) return;
+  bool has_next = item_at(1, nxt);
+  int gb = 0;
+  copy_rows(cur, k, kst_lds);
+  copy_rows(cur, v, qt_lds + 2 * BUF_B);
+  issue(cur, cur.qt0, 0);
+  if (cur.qt0 + 1 < n_qt) issue(cur, cur.qt0 + 1, 1);
+  sync_tiles();
+
+  for (int r = 0;; ++r) {
+    // K rows in kstage, V rows in buffer (gb + 2) % NBUF, query tiles qt0 and
+    // qt0 + 1 in buffers gb, gb + 1: all landed.
+    const int qt0 = cur.qt0;
+    const int nt = n_qt - qt0;  // query tiles of this item
+    const int kw0 = cur.k0 + 32 * wave;
+    const size_t base = cur.base;
+    const int bh = cur.bh;
+    const int ub2 = gb == 0 ? 2 : gb - 1;  // (gb + 2) % NBUF
+    // The lse rows are used as -lse log2(e), the exponent offset of P in the
+    // exp2 domain: the wavefront that first sees a tile's rows land rewrites
+    // them in place (the next barrier publishes them).
+    if (wave < 2 && wave < nt) to_exp2_offset(lsd[(gb + wave) % NBUF][0], lane);
+    // K^T and V^T operands: lane holds row kw0 + l32, elements 16 kc + 8 half
+    // + 0..7, read from the rows staged with 16 lanes per row.
     const int krow = kw0 + l32;
     bf16x8 kreg[8], vreg[8];
+    {
+      const int rr = 32 * (wave & 1) + l32;  // row within the 64-row half
+      const uint32_t o_row = (wave >> 1) * TILE_B + rr * 256;
+#pragma unroll
+      for (int kc = 0; kc < 8; ++kc) {
+        const uint32_t o = o_row + 16 * ((2 * kc + half) ^ tile_swz(rr));
+        kreg[kc] = as_bf16x8(lds_ld16(kst_lds + o));
+        vreg[kc] = as_bf16x8(lds_ld16(qt_lds + ub2 * BUF_B + o));
+      }
+    }
+    __syncthreads();  // kstage and buffer (gb + 2) % NBUF are free again
+    if (qt0 + 2 < n_qt) issue(cur, qt0 + 2, ub2);
+    int nx = 0;              // leading query tiles of the next item issued
+    bool k_next = false;     // next item's K rows issued
 
     f32x16 dka[4], dva[4];
 #pragma unroll
@@ -267,102 +362,32 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(
       dva[i] = f32x16{};
     }
 
-    const TileOffsets ofs = tile_operand_offsets(lane);
-    const uint32_t qt_lds = lds_addr(qtiles);
-    const uint32_t lsd_lds = lds_addr(&lsd[0][0][0]);
-    const uint32_t kst_lds = lds_addr(kstage);
-
-    // Tile copies (see copy_tile); wavefronts 0 and 1 also copy the lse and
-    // delta rows.  Rows past T are past the end of the buffer range and arrive
-    // as zeros: a zero query row with zero dout, lse and delta adds nothing to
-    // dK or dV.
-    const uint32_t rsb = static_cast<uint32_t>(rs) * 2;  // bytes between rows
-    const uint32_t dvoff = tile_copy_offset(wave, lane, rsb);
-    auto issue = [&](int qt, int u) {  // query tile qt -> buffer u
-      const int q0 = qt * QT_ROWS;
-      const uint32_t nrec = static_cast<uint32_t>(T - q0) * rsb;
-      const size_t off = base + static_cast<size_t>(q0) * rs;
-      copy_tile(buffer_rsrc(q + off, nrec), dvoff, rsb, qt_lds + u * BUF_B, wave);
-      copy_tile(buffer_rsrc(dout + off, nrec), dvoff, rsb, qt_lds + u * BUF_B + TILE_B, wave);
-      if (wave == 0)
-        dma4(buffer_rsrc(lse_bh + q0, static_cast<uint32_t>(T - q0) * 4), 4 * lane,
-             lsd_lds + u * 512);
-      if (wave == 1)
-        dma4(buffer_rsrc(del_bh + q0, static_cast<uint32_t>(T - q0) * 4), 4 * lane,
-             lsd_lds + u * 512 + 256);
-    };
-    // Every copy issued so far has landed and every wavefront is past its
-    // reads of the buffer that the next copy overwrites.
-    auto sync_tiles = [&]() {
-      wait_vmem();
-      __syncthreads();
-    };
-
     // dS blocks of this wavefront's 32 keys (when a dS workspace is given).
-    // Only blocks with a query row < T exist in the packed layout; a block made
-    // of padding rows only (the tail of the last tile) is not stored.  Stored
-    // blocks always have kblk <= qblk.
+    // Only blocks with a query row < T exist in the packed layout; a block
+    // made of padding rows only (the tail of the last tile) is not stored.
+    // Stored blocks always have kblk <= qblk.
     const int kblk = kw0 / 32;
     auto ds_of = [&](int qblk) -> u16* {
       return (dsw && 32 * qblk < T) ? dsw + ds_block_index(bh, nbt, qblk, kblk) : nullptr;
     };
 
-    // Query tile qt0 + u lives in buffer u % NBUF.  The workgroup's 128 K rows
-    // come through the staging region kst and its V rows through buffer 2 (rows
-    // 0..63, then 64..127), copied with 16 lanes per row together with query
-    // tiles qt0 and qt0 + 1; each lane then reads its row's operands.  Keys
-    // past T arrive as zeros: their gradients are never stored and, since every
-    // real query precedes them, the causal mask removes them from every real
-    // query's dS.
-    const int n_qt = (T + QT_ROWS - 1) / QT_ROWS;
-    const int qt0 = k0 / QT_ROWS;
-    {
-      const int nk = T - k0;  // >= 1
-      const uint32_t n0 = static_cast<uint32_t>(min(nk, 64)) * rsb;
-      const uint32_t n1 = static_cast<uint32_t>(max(nk - 64, 0)) * rsb;
-      const size_t off0 = base + static_cast<size_t>(k0) * rs;
-      const size_t off1 = off0 + static_cast<size_t>(64) * rs;
-      copy_tile(buffer_rsrc(k + off0, n0), dvoff, rsb, kst_lds, wave);
-      copy_tile(buffer_rsrc(k + off1, n1), dvoff, rsb, kst_lds + TILE_B, wave);
-      copy_tile(buffer_rsrc(v + off0, n0), dvoff, rsb, qt_lds + 2 * BUF_B, wave);
-      copy_tile(buffer_rsrc(v + off1, n1), dvoff, rsb, qt_lds + 2 * BUF_B + TILE_B, wave);
-    }
-    issue(qt0, 0);
-    if (qt0 + 1 < n_qt) issue(qt0 + 1, 1);
-    sync_tiles();
-    // The lse rows are used as -lse log2(e), the exponent offset of P in the
-    // exp2 domain: the wavefront that first sees a tile's rows land rewrites
-    // them in place (the next barrier publishes them).
-    if (wave < 2) to_exp2_offset(lsd[wave][0], lane);
-    {
-      const int rr = 32 * (wave & 1) + l32;  // row within the 64-row half
-      const uint32_t o_row = (wave >> 1) * TILE_B + rr * 256;
-#pragma unroll
-      for (int kc = 0; kc < 8; ++kc) {
-        const uint32_t o = o_row + 16 * ((2 * kc + half) ^ tile_swz(rr));
-        kreg[kc] = as_bf16x8(lds_ld16(kst_lds + o));
-        vreg[kc] = as_bf16x8(lds_ld16(qt_lds + 2 * BUF_B + o));
-      }
-    }
-    __syncthreads();  // buffer 2 is free again
-    if (qt0 + 2 < n_qt) issue(qt0 + 2, 2);
-
-    // One software pipeline over the 32-query blocks from the diagonal on: the
-    // step for block j computes the probabilities of j, the scores of j+1 and
-    // the dK/dV update of j.  This wavefront's first block is its diagonal
-    // block bw (masked); blocks before it hold no visible (query, key) pair and
-    // are skipped, and the slot of block bw - 1 computes bw's scores.  Tile t
-    // holds blocks 2t, 2t+1; block 2t+1's step reads the scores of block 2t+2
-    // from tile t+1.  At the sync before tile t (t > qt0) tile t+1 has landed
-    // and tile t-1's buffer is free for the copy of tile t+2.  After the last
-    // tile the second step still computes scores of a block past the end (from
-    // a stale buffer); they are never used.
+    // One software pipeline over the 32-query blocks from the diagonal on:
+    // the step for block j computes the probabilities of j, the scores of j+1
+    // and the dK/dV update of j.  This wavefront's first block is its diagonal
+    // block bw (masked); blocks before it hold no visible (query, key) pair
+    // and are skipped, and the slot of block bw - 1 computes bw's scores.  Tile
+    // t holds blocks 2t, 2t+1; block 2t+1's step reads the scores of block
+    // 2t+2 from tile t+1.  At the sync before tile t (t > qt0) tile t+1 has
+    // landed and tile t-1's buffer is free for the copy of stream position
+    // t+2.  After the last tile the second step still computes scores of a
+    // block past the end (from whatever the next buffer holds); they are never
+    // used.
     const int bw = kw0 / 32;
     f32x16 s0, p0, s1, p1;  // scores of even blocks in s0/p0, of odd blocks in s1/p1
     uint32_t nc[8];         // row-read addresses of tile t
-    nat_addr(qt_lds, ofs, nc);
+    nat_addr(qt_lds + gb * BUF_B, ofs, nc);
     if (bw == 2 * qt0) dkdv_scores(nc, 0, kreg, vreg, s0, p0);
-    int u = 0;  // buffer of tile t
+    int u = gb;  // buffer of tile t
     // The first two tiles (every diagonal block of the workgroup) take the
     // per-wavefront branches; the rest run one branch-free body.
     auto tile = [&](int t, auto steady) {
@@ -370,7 +395,18 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(
       const int un = u == NBUF - 1 ? 0 : u + 1;  // buffer of tile t + 1
       if (t > qt0) {
         sync_tiles();
-        if (t + 2 < n_qt) issue(t + 2, un == NBUF - 1 ? 0 : un + 1);
+        const int u2 = un == NBUF - 1 ? 0 : un + 1;
+        const int pos = t + 2;
+        if (pos < n_qt) {
+          issue(cur, pos, u2);
+        } else if (has_next && pos - n_qt == nx && nx < 2 && nxt.qt0 + nx < n_qt) {
+          issue(nxt, nxt.qt0 + nx, u2);  // the next item's tile nx, in stream order
+          ++nx;
+        }
+        if (t == n_qt - 1 && has_next) {
+          copy_rows(nxt, k, kst_lds);
+          k_next = true;
+        }
         if (t + 1 < n_qt && wave == 3) to_exp2_offset(lsd[un][0], lane);  // tile t+1
       }
       uint32_t tc[4][2], nn[8];
@@ -380,20 +416,20 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(
       const int j0 = 2 * t, j1 = 2 * t + 1;
       // block j0 (rows 0..31 of tile t), scores of rows 32..63
       if (STEADY || j0 > bw)
-        dkdv_step<false>(nc, 32, lsd[u][0], lsd[u][1], tc, 0, kreg, vreg, s0, p0, s1, p1, dka, dva,
-                         lane, c_log2, kq, ds_of(j0));
+        dkdv_step<false>(nc, 32, lsd[u][0], lsd[u][1], tc, 0, kreg, vreg, s0, p0, s1, p1, dka,
+                         dva, lane, c_log2, kq, ds_of(j0));
       else if (j0 == bw)
-        dkdv_step<true>(nc, 32, lsd[u][0], lsd[u][1], tc, 0, kreg, vreg, s0, p0, s1, p1, dka, dva,
-                        lane, c_log2, kq, ds_of(j0));
+        dkdv_step<true>(nc, 32, lsd[u][0], lsd[u][1], tc, 0, kreg, vreg, s0, p0, s1, p1, dka,
+                        dva, lane, c_log2, kq, ds_of(j0));
       else if (j0 == bw - 1)
         dkdv_scores(nc, 32, kreg, vreg, s1, p1);
       // block j1 (rows 32..63 of tile t), scores of tile t+1 rows 0..31
       if (STEADY || j1 > bw)
-        dkdv_step<false>(nn, 0, lsd[u][0], lsd[u][1], tc, 32, kreg, vreg, s1, p1, s0, p0, dka, dva,
-                         lane, c_log2, kq, ds_of(j1));
+        dkdv_step<false>(nn, 0, lsd[u][0], lsd[u][1], tc, 32, kreg, vreg, s1, p1, s0, p0, dka,
+                         dva, lane, c_log2, kq, ds_of(j1));
       else if (j1 == bw)
-        dkdv_step<true>(nn, 0, lsd[u][0], lsd[u][1], tc, 32, kreg, vreg, s1, p1, s0, p0, dka, dva,
-                        lane, c_log2, kq, ds_of(j1));
+        dkdv_step<true>(nn, 0, lsd[u][0], lsd[u][1], tc, 32, kreg, vreg, s1, p1, s0, p0, dka,
+                        dva, lane, c_log2, kq, ds_of(j1));
       else if (j1 == bw - 1)
         dkdv_scores(nn, 0, kreg, vreg, s0, p0);
 #pragma unroll
@@ -404,36 +440,60 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(
     for (int t = qt0; t < t_diag_end; ++t) tile(t, std::false_type{});
     for (int t = t_diag_end; t < n_qt; ++t) tile(t, std::true_type{});
 
+    // Every wavefront is done with the last tile's buffer: the next item's V
+    // rows go there, and whatever the stream has not copied yet of its K rows
+    // and first two query tiles follows.
+    __syncthreads();
+    const int ulast = (gb + nt - 1) % NBUF;
+    if (has_next) {
+      if (!k_next) copy_rows(nxt, k, kst_lds);
+      copy_rows(nxt, v, qt_lds + ulast * BUF_B);
+      for (int j = nx; j < 2; ++j)
+        if (nxt.qt0 + j < n_qt) issue(nxt, nxt.qt0 + j, (gb + nt + j) % NBUF);
+    }
+
     // dka[db], dva[db] (dK^T, dV^T blocks) element r: key kw0 + l32,
-    // d = 32 db + 8 (r/4) + 4 half + r%4.  The rows leave through LDS so that 16
-    // lanes store one 256-byte row: stored straight from registers, every lane
-    // would write 8 bytes to a different row.  Staging rows are swizzled by
-    // 16-byte chunk (chunk c of row r at c ^ (r mod 16)).
-    __syncthreads();  // every wavefront is done with the query tiles
-    const uint32_t stg = qt_lds + wave * 16384;  // 32 dK rows, then 32 dV rows
+    // d = 32 db + 8 (r/4) + 4 half + r%4.  The rows leave through this
+    // wavefront's 4 KiB of LDS, 16 rows at a time, so that 16 lanes store one
+    // 256-byte row: stored straight from registers, every lane would write 8
+    // bytes to a different row.  Staging rows are swizzled by 16-byte chunk
+    // (chunk c of row r at c ^ r).  LDS operations of one wavefront complete
+    // in order, so no barrier is needed between the rounds.
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+    for (int tsel = 0; tsel < 2; ++tsel) {  // dK, then dV
+      const f32x16* acc = tsel ? dva : dka;
+      const float sc = tsel ? 1.f : scale;
+      u16* dst = tsel ? dv : dk;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int r = 4 * g;
-        const uint32_t off = l32 * 256 + 16 * ((4 * db + g) ^ (l32 & 15)) + 8 * half;
-        lds_st8(stg + off, pack_bf16x2(dka[db][r] * scale, dka[db][r + 1] * scale),
-                pack_bf16x2(dka[db][r + 2] * scale, dka[db][r + 3] * scale));
-        lds_st8(stg + 8192 + off, pack_bf16x2(dva[db][r], dva[db][r + 1]),
-                pack_bf16x2(dva[db][r + 2], dva[db][r + 3]));
-      }
-    // lane i copies chunk i % 16 of rows 4 m + i / 16
+      for (int sh = 0; sh < 2; ++sh) {  // keys kw0 + 16 sh .. + 15
+        if ((l32 >> 4) == sh) {
+          const int rr = l32 & 15;
 #pragma unroll
-    for (int m = 0; m < 8; ++m) {
-      const int r = 4 * m + (lane >> 4), c = lane & 15;
-      const uint32_t off = r * 256 + 16 * (c ^ (r & 15));
-      const uint4 xk = lds_ld16(stg + off);
-      const uint4 xv = lds_ld16(stg + 8192 + off);
-      if (kw0 + r < T) {
-        st16(dk + base + (kw0 + r) * rs + 8 * c, xk);
-        st16(dv + base + (kw0 + r) * rs + 8 * c, xv);
+          for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              const int e = 4 * g;
+              lds_st8(est_lds + rr * 256 + 16 * ((4 * db + g) ^ rr) + 8 * half,
+                      pack_bf16x2(acc[db][e] * sc, acc[db][e + 1] * sc),
+                      pack_bf16x2(acc[db][e + 2] * sc, acc[db][e + 3] * sc));
+            }
+        }
+        // lane i copies chunk i % 16 of rows 4 m + i / 16
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const int rr = 4 * m + (lane >> 4), c = lane & 15;
+          const uint4 x = lds_ld16(est_lds + rr * 256 + 16 * (c ^ rr));
+          const int key = kw0 + 16 * sh + rr;
+          if (key < T) st16(dst + base + key * rs + 8 * c, x);
+        }
       }
     }
+
+    if (!has_next) break;
+    sync_tiles();  // the next item's K, V rows and first query tiles have landed
+    gb = (gb + nt) % NBUF;
+    cur = nxt;
+    has_next = item_at(r + 2, nxt);
   }
 }
 
