@@ -17,7 +17,12 @@ readings taken here (plainest, all listed in the design notes):
 
   * scaled dot-product attention, softmax over keys, scale s = 1/sqrt(D);
   * causal = top-left aligned with T_q = T_k: key j visible to query i iff j <= i;
-  * full causal window (the long "L" layers of the SSSL pattern);
+  * full causal window by default (the long "L" layers of the SSSL pattern);
+    with a window W (the short "S" layers, same blog, section 1 "GPT model",
+    and the window_size argument of section 5), key j is visible to query i
+    iff i - W <= j <= i: the query itself and the W keys before it.  The blog
+    gives neither W nor the argument's convention; this is flash-attention's
+    (left, right) = (W, 0) band under a causal mask;
   * n_kv_head = n_head (plain multi-head attention);
   * LSE is the natural log of sum_j exp(s * q_i . k_j) over visible keys;
   * the loss depends on O only, so the LSE output receives no gradient;
@@ -45,22 +50,25 @@ def softmax_scale(D: int) -> float:
     return 1.0 / math.sqrt(D)
 
 
-def _scores(Q: np.ndarray, K: np.ndarray) -> np.ndarray:
-    """S_ij = s * <Q_i, K_j>, with S_ij = -inf where j > i (causal mask)."""
+def _scores(Q: np.ndarray, K: np.ndarray, window=None) -> np.ndarray:
+    """S_ij = s * <Q_i, K_j>, with S_ij = -inf where j > i (causal mask) and,
+    given a window W, where j < i - W (the band's lower edge)."""
     T, D = Q.shape
     S = softmax_scale(D) * (Q @ K.T)
     S[np.triu_indices(T, k=1, m=K.shape[0])] = -np.inf
+    if window is not None:
+        S[np.tril_indices(T, k=-int(window) - 1, m=K.shape[0])] = -np.inf
     return S
 
 
-def causal_probabilities(Q, K):
+def causal_probabilities(Q, K, window=None):
     """P = softmax over keys of the masked scaled scores, and LSE per row.
 
     Returns (P, lse) with P (T, T) and lse (T,) in float64.
     """
     Q = np.asarray(Q, dtype=np.float64)
     K = np.asarray(K, dtype=np.float64)
-    S = _scores(Q, K)
+    S = _scores(Q, K, window)
     m = S.max(axis=1)                     # row max over visible keys (finite: j = i)
     E = np.exp(S - m[:, None])            # masked entries give exp(-inf) = 0
     l = E.sum(axis=1)
@@ -69,17 +77,17 @@ def causal_probabilities(Q, K):
     return P, lse
 
 
-def forward_head(Q, K, V):
+def forward_head(Q, K, V, window=None):
     """One (batch, head): O = softmax(s Q K^T + causal mask) V and LSE.
 
     Q, K, V: (T, D).  Returns O (T, D) and lse (T,) in float64.
     """
-    P, lse = causal_probabilities(Q, K)
+    P, lse = causal_probabilities(Q, K, window)
     O = P @ np.asarray(V, dtype=np.float64)
     return O, lse
 
 
-def backward_head(Q, K, V, dO):
+def backward_head(Q, K, V, dO, window=None):
     """Analytic gradients of L = sum(O * dO) for one (batch, head).
 
     With P the attention probabilities (recomputed here), O = P V:
@@ -96,7 +104,7 @@ def backward_head(Q, K, V, dO):
     V = np.asarray(V, dtype=np.float64)
     dO = np.asarray(dO, dtype=np.float64)
     s = softmax_scale(Q.shape[1])
-    P, _ = causal_probabilities(Q, K)
+    P, _ = causal_probabilities(Q, K, window)
     O = P @ V
     dV = P.T @ dO
     dP = dO @ V.T
@@ -115,28 +123,29 @@ def _heads(x):
             yield (b, h), np.asarray(x[b, :, h, :], dtype=np.float64)
 
 
-def forward(q, k, v, heads=None):
+def forward(q, k, v, heads=None, window=None):
     """Batched forward over (B, T, H, D) arrays.
 
     heads: optional iterable of (b, h) pairs; when given, only those heads are
     computed and the result is a dict {(b, h): (O, lse)}.  Otherwise returns
-    o (B, T, H, D) and lse (B, H, T) in float64.
+    o (B, T, H, D) and lse (B, H, T) in float64.  window: None (full causal)
+    or W >= 0 (see the module notes).
     """
     B, T, H, D = q.shape
     if heads is not None:
-        return {(b, h): forward_head(q[b, :, h, :], k[b, :, h, :], v[b, :, h, :])
+        return {(b, h): forward_head(q[b, :, h, :], k[b, :, h, :], v[b, :, h, :], window)
                 for (b, h) in heads}
     o = np.empty((B, T, H, D), dtype=np.float64)
     lse = np.empty((B, H, T), dtype=np.float64)
     for b in range(B):
         for h in range(H):
-            O, L = forward_head(q[b, :, h, :], k[b, :, h, :], v[b, :, h, :])
+            O, L = forward_head(q[b, :, h, :], k[b, :, h, :], v[b, :, h, :], window)
             o[b, :, h, :] = O
             lse[b, h, :] = L
     return o, lse
 
 
-def backward(q, k, v, do, heads=None):
+def backward(q, k, v, do, heads=None, window=None):
     """Batched backward over (B, T, H, D) arrays.
 
     Returns dq, dk, dv (B, T, H, D) and delta (B, H, T) in float64, or, when
@@ -145,7 +154,7 @@ def backward(q, k, v, do, heads=None):
     B, T, H, D = q.shape
     if heads is not None:
         return {(b, h): backward_head(q[b, :, h, :], k[b, :, h, :], v[b, :, h, :],
-                                      do[b, :, h, :]) for (b, h) in heads}
+                                      do[b, :, h, :], window) for (b, h) in heads}
     dq = np.empty((B, T, H, D), dtype=np.float64)
     dk = np.empty_like(dq)
     dv = np.empty_like(dq)
@@ -153,7 +162,7 @@ def backward(q, k, v, do, heads=None):
     for b in range(B):
         for h in range(H):
             gq, gk, gv, dl = backward_head(q[b, :, h, :], k[b, :, h, :], v[b, :, h, :],
-                                           do[b, :, h, :])
+                                           do[b, :, h, :], window)
             dq[b, :, h, :] = gq
             dk[b, :, h, :] = gk
             dv[b, :, h, :] = gv
@@ -161,19 +170,21 @@ def backward(q, k, v, do, heads=None):
     return dq, dk, dv, delta
 
 
-def decode_head(q, K, V, L: int):
+def decode_head(q, K, V, L: int, window=None):
     """Single-query attention over the first L cached keys of one head.
 
     q: (D,), K, V: (T_cap, D).  z_j = s <q, K_j> for j < L; o = softmax(z) V[:L];
     lse = logsumexp(z).  Rows >= L are never read.  L = 0 gives o = 0 and
-    lse = -inf (an empty softmax).
+    lse = -inf (an empty softmax).  The query sits at position L - 1, so a
+    window W keeps keys L - 1 - W .. L - 1 only.
     """
     D = q.shape[0]
     if L <= 0:
         return np.zeros(D), -np.inf
+    j0 = 0 if window is None else max(0, L - 1 - int(window))
     q = np.asarray(q, dtype=np.float64)
-    Kl = np.asarray(K[:L], dtype=np.float64)
-    Vl = np.asarray(V[:L], dtype=np.float64)
+    Kl = np.asarray(K[j0:L], dtype=np.float64)
+    Vl = np.asarray(V[j0:L], dtype=np.float64)
     z = softmax_scale(D) * (Kl @ q)
     m = z.max()
     e = np.exp(z - m)
@@ -181,7 +192,7 @@ def decode_head(q, K, V, L: int):
     return (e / l) @ Vl, m + math.log(l)
 
 
-def decode(q, k_cache, v_cache, seqlens, pairs=None):
+def decode(q, k_cache, v_cache, seqlens, pairs=None, window=None):
     """Batched decode.  q (B, H, D); caches (B, T_cap, H, D); seqlens int [B].
 
     Returns o (B, H, D) and lse (B, H) in float64, or a dict {(b, h): (o, lse)}
@@ -190,13 +201,13 @@ def decode(q, k_cache, v_cache, seqlens, pairs=None):
     B, H, D = q.shape
     if pairs is not None:
         return {(b, h): decode_head(q[b, h], k_cache[b, :, h, :], v_cache[b, :, h, :],
-                                    int(seqlens[b])) for (b, h) in pairs}
+                                    int(seqlens[b]), window) for (b, h) in pairs}
     o = np.empty((B, H, D), dtype=np.float64)
     lse = np.empty((B, H), dtype=np.float64)
     for b in range(B):
         for h in range(H):
             ob, lb = decode_head(q[b, h], k_cache[b, :, h, :], v_cache[b, :, h, :],
-                                 int(seqlens[b]))
+                                 int(seqlens[b]), window)
             o[b, h] = ob
             lse[b, h] = lb
     return o, lse

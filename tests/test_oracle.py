@@ -260,3 +260,126 @@ def test_decode_equals_last_forward_row_and_ignores_tail():
 def test_decode_empty_sequence():
     o, l = oracle.decode_head(np.ones(8), np.ones((4, 8)), np.ones((4, 8)), 0)
     assert np.array_equal(o, np.zeros(8)) and l == -np.inf
+
+
+# ---------------------------------------------------------------- sliding window
+
+def _brute_window_row(q, K, V, i, W):
+    """Row i by pure-Python loops over the keys i - W .. i (no numpy matmul)."""
+    D = len(q)
+    s = 1.0 / math.sqrt(D)
+    js = range(max(0, i - W), i + 1)
+    z = {j: s * sum(q[d] * K[j][d] for d in range(D)) for j in js}
+    m = max(z.values())
+    e = {j: math.exp(z[j] - m) for j in js}
+    l = sum(e.values())
+    o = [sum(e[j] * V[j][d] for j in js) / l for d in range(D)]
+    return o, m + math.log(l)
+
+
+@pytest.mark.parametrize("W", [0, 1, 2, 3, 6, 9])
+def test_window_brute_force_loops(W):
+    """Each row's softmax over exactly the keys i - W .. i, in plain loops."""
+    T, D = 8, 4
+    Q, K, V = (rnd((T, D), s) for s in (301, 302, 303))
+    O, lse = oracle.forward_head(Q, K, V, window=W)
+    for i in range(T):
+        o, l = _brute_window_row(Q[i].tolist(), K.tolist(), V.tolist(), i, W)
+        assert np.allclose(O[i], o, rtol=0, atol=1e-13)
+        assert abs(lse[i] - l) <= 1e-13
+
+
+def test_window_zero_closed_form():
+    """W = 0: every query sees only itself, so O = V, lse = s <q_i, k_i>,
+    dV = dO and the one-key softmax has no gradient: dQ = dK = 0."""
+    T, D = 11, 16
+    Q, K, V, dO = (rnd((T, D), s) for s in (311, 312, 313, 314))
+    O, lse = oracle.forward_head(Q, K, V, window=0)
+    assert np.array_equal(O, V)
+    assert np.allclose(lse, np.sum(Q * K, axis=1) / 4.0, rtol=0, atol=1e-14)
+    dQ, dK, dV, delta = oracle.backward_head(Q, K, V, dO, window=0)
+    assert np.array_equal(dV, dO)
+    assert np.allclose(dQ, 0.0, atol=1e-13) and np.allclose(dK, 0.0, atol=1e-13)
+    assert np.allclose(delta, np.sum(dO * V, axis=1), rtol=0, atol=1e-13)
+
+
+def test_window_covering_the_sequence_is_full_causal():
+    B, T, H, D = 1, 13, 2, 8
+    q, k, v, do = (rnd((B, T, H, D), s) for s in (321, 322, 323, 324))
+    o, lse = oracle.forward(q, k, v)
+    dq, dk, dv, _ = oracle.backward(q, k, v, do)
+    for W in (T - 1, T, 5 * T):
+        ow, lw = oracle.forward(q, k, v, window=W)
+        gw = oracle.backward(q, k, v, do, window=W)
+        assert np.array_equal(o, ow) and np.array_equal(lse, lw)
+        for a, b in zip((dq, dk, dv), gw[:3]):
+            assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("T,D,W", [(6, 4, 1), (7, 4, 2), (9, 8, 4)])
+def test_window_finite_differences(T, D, W):
+    """Banded gradients equal central differences of sum(O * dO)."""
+    B, H = 1, 1
+    q, k, v, do = (rnd((B, T, H, D), s) for s in (331, 332, 333, 334))
+    dq, dk, dv, _ = oracle.backward(q, k, v, do, window=W)
+    loss = lambda a, b, c: float(np.sum(oracle.forward(a, b, c, window=W)[0] * do))  # noqa
+    eps = 1e-6
+    for idx, (x, g) in enumerate(((q, dq), (k, dk), (v, dv))):
+        fd = np.zeros_like(x)
+        for pos in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[pos] += eps
+            xm[pos] -= eps
+            args_p = [q, k, v]
+            args_m = [q, k, v]
+            args_p[idx], args_m[idx] = xp, xm
+            fd[pos] = (loss(*args_p) - loss(*args_m)) / (2 * eps)
+        assert np.allclose(g, fd, rtol=0, atol=2e-8)
+
+
+@pytest.mark.parametrize("T,W", [(37, 5), (64, 16), (20, 0)])
+def test_window_against_torch_sdpa_fp64(T, W):
+    """torch's CPU scaled_dot_product_attention with an explicit boolean band
+    mask (allowed iff i - W <= j <= i), and its autograd, in float64."""
+    torch = pytest.importorskip("torch")
+    B, H, D = 2, 2, 16
+    q, k, v, do = (rnd((B, T, H, D), s) for s in (341, 342, 343, 344))
+    o, lse = oracle.forward(q, k, v, window=W)
+    dq, dk, dv, _ = oracle.backward(q, k, v, do, window=W)
+    i = torch.arange(T)[:, None]
+    j = torch.arange(T)[None, :]
+    allowed = (j <= i) & (j >= i - W)
+    tq, tk, tv = (torch.tensor(x.transpose(0, 2, 1, 3).copy(), dtype=torch.float64,
+                               requires_grad=True) for x in (q, k, v))
+    to = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=allowed)
+    to.backward(torch.tensor(do.transpose(0, 2, 1, 3).copy(), dtype=torch.float64))
+    back = lambda t: t.detach().numpy().transpose(0, 2, 1, 3)  # noqa: E731
+    assert np.allclose(o, back(to), rtol=0, atol=1e-12)
+    assert np.allclose(dq, back(tq.grad), rtol=0, atol=1e-11)
+    assert np.allclose(dk, back(tk.grad), rtol=0, atol=1e-11)
+    assert np.allclose(dv, back(tv.grad), rtol=0, atol=1e-11)
+    S = torch.matmul(tq.detach(), tk.detach().transpose(-1, -2)) / math.sqrt(D)
+    S = S.masked_fill(~allowed, float("-inf"))
+    assert np.allclose(lse, torch.logsumexp(S, dim=-1).numpy(), rtol=0, atol=1e-12)
+
+
+def test_window_decode_equals_last_forward_row_and_ignores_old_keys():
+    B, Tc, H, D, W = 3, 40, 2, 32, 7
+    q = rnd((B, H, D), 351, 0.5)
+    kc, vc = rnd((B, Tc, H, D), 352, 0.5), rnd((B, Tc, H, D), 353, 0.5)
+    lens = np.array([1, 8, 40])
+    kp, vp = kc.copy(), vc.copy()
+    for b, L in enumerate(lens):          # poison rows outside L - 1 - W .. L - 1
+        kp[b, L:] = np.nan
+        vp[b, L:] = np.nan
+        kp[b, :max(0, L - 1 - W)] = np.nan
+        vp[b, :max(0, L - 1 - W)] = np.nan
+    o, lse = oracle.decode(q, kp, vp, lens, window=W)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    for b, L in enumerate(lens):
+        for h in range(H):
+            Qf = kc[b, :L, h, :].copy()
+            Qf[L - 1] = q[b, h]
+            O, l = oracle.forward_head(Qf, kc[b, :L, h, :], vc[b, :L, h, :], window=W)
+            assert np.allclose(o[b, h], O[L - 1], rtol=0, atol=1e-13)
+            assert abs(lse[b, h] - l[L - 1]) <= 1e-13
