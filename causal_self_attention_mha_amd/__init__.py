@@ -12,6 +12,9 @@ Functions (names match the C entry points):
   attn_fwd(q, k, v)                       -> (o, lse)
   attn_bwd(q, k, v, o, dout, lse)         -> (dq, dk, dv, delta)
   attn_decode(q, k_cache, v_cache, seqlens) -> (o, lse)
+Each takes window=W (an int >= 0) for sliding-window attention (key j visible
+to query i iff i - W <= j <= i), which calls the *_window entry point;
+window=None is plain causal attention.
 bf16 tensors use the bf16 kernels, float32 tensors the fp32 kernels
 (forward and backward only).  Layouts: q, k, v, o, dout (B, T, H, 128);
 lse, delta (B, H, T) float32; decode q/o (B, H, 128), caches (B, T_cap, H, 128),
@@ -71,8 +74,12 @@ def load_library():
     lib.na_attn_bwd_f32.argtypes = [vp, vp, vp, vp, vp, f32p, vp, vp, vp, f32p, i, i, i, i, vp]
     lib.na_attn_bwd_timed.argtypes = lib.na_attn_bwd.argtypes + [vp]  # + events
     lib.na_attn_decode_timed.argtypes = lib.na_attn_decode.argtypes + [vp]
+    lib.na_attn_fwd_window.argtypes = [vp, vp, vp, vp, f32p, i, i, i, i, i, vp]
+    lib.na_attn_bwd_window.argtypes = lib.na_attn_bwd.argtypes[:-1] + [i, vp, vp]
+    lib.na_attn_decode_window.argtypes = [vp, vp, vp, vp, vp, f32p, i, i, i, i, i, vp, sz, vp, vp]
     for fn in ("na_attn_fwd", "na_attn_bwd", "na_attn_decode", "na_attn_fwd_f32",
-               "na_attn_bwd_f32", "na_attn_bwd_timed", "na_attn_decode_timed"):
+               "na_attn_bwd_f32", "na_attn_bwd_timed", "na_attn_decode_timed",
+               "na_attn_fwd_window", "na_attn_bwd_window", "na_attn_decode_window"):
         getattr(lib, fn).restype = ctypes.c_int
     lib.na_status_string.argtypes = [ctypes.c_int]
     lib.na_status_string.restype = ctypes.c_char_p
@@ -117,7 +124,14 @@ def _check_train(names, tensors, dtype=None):
     return dtype
 
 
-def attn_fwd(q, k, v, o=None, lse=None):
+def _window(window):
+    if window is None:
+        return None
+    _require(int(window) == window and window >= 0, f"window must be an int >= 0, got {window}")
+    return int(window)
+
+
+def attn_fwd(q, k, v, o=None, lse=None, window=None):
     """Causal attention forward.  Returns (o, lse): o like q, lse float32 (B, H, T)."""
     import torch
     lib = load_library()
@@ -128,6 +142,13 @@ def attn_fwd(q, k, v, o=None, lse=None):
     _check_train(("q", "o"), (q, o), dtype)
     _require(lse.shape == (B, H, T) and lse.dtype == torch.float32 and lse.is_contiguous(),
              "lse must be contiguous float32 (B, H, T)")
+    window = _window(window)
+    if window is not None:
+        _require(dtype == torch.bfloat16, "window: bf16 tensors only")
+        _check(lib, "na_attn_fwd_window",
+               lib.na_attn_fwd_window(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, T, H, D,
+                                      window, _stream(q)))
+        return o, lse
     fn = "na_attn_fwd" if dtype == torch.bfloat16 else "na_attn_fwd_f32"
     _check(lib, fn, getattr(lib, fn)(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, T, H, D,
                                      _stream(q)))
@@ -139,12 +160,13 @@ def bwd_workspace_bytes(B, T, H, D=HEAD_DIM):
 
 
 def attn_bwd(q, k, v, o, dout, lse, dq=None, dk=None, dv=None, delta=None, workspace=None,
-             recompute_dq=False):
+             recompute_dq=False, window=None):
     """Causal attention backward.  Returns (dq, dk, dv, delta).
 
     bf16: by default a dS workspace is allocated (or `workspace` is used) so
     that dq is a GEMM over the stored dS; recompute_dq=True passes no
-    workspace and the dq pass recomputes S and dP.  fp32 has one path."""
+    workspace and the dq pass recomputes S and dP (plain causal only: a
+    window needs the workspace).  fp32 has one path."""
     import torch
     lib = load_library()
     dtype = _check_train(("q", "k", "v", "o", "dout"), (q, k, v, o, dout))
@@ -156,6 +178,8 @@ def attn_bwd(q, k, v, o, dout, lse, dq=None, dk=None, dv=None, delta=None, works
     dv = torch.empty_like(v) if dv is None else dv
     delta = torch.empty((B, H, T), dtype=torch.float32, device=q.device) if delta is None else delta
     _check_train(("q", "dq", "dk", "dv"), (q, dq, dk, dv), dtype)
+    window = _window(window)
+    _require(window is None or dtype == torch.bfloat16, "window: bf16 tensors only")
     if dtype == torch.bfloat16:
         ws_bytes = 0
         if not recompute_dq:
@@ -166,10 +190,17 @@ def attn_bwd(q, k, v, o, dout, lse, dq=None, dk=None, dv=None, delta=None, works
                 ws_bytes = workspace.numel() * workspace.element_size()
         else:
             workspace = None
-        _check(lib, "na_attn_bwd",
-               lib.na_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq),
-                               _ptr(dk), _ptr(dv), _ptr(delta), _ptr(workspace), ws_bytes, B, T,
-                               H, D, _stream(q)))
+        if window is not None:
+            _check(lib, "na_attn_bwd_window",
+                   lib.na_attn_bwd_window(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout),
+                                          _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(delta),
+                                          _ptr(workspace), ws_bytes, B, T, H, D, window,
+                                          _stream(q), None))
+        else:
+            _check(lib, "na_attn_bwd",
+                   lib.na_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse),
+                                   _ptr(dq), _ptr(dk), _ptr(dv), _ptr(delta), _ptr(workspace),
+                                   ws_bytes, B, T, H, D, _stream(q)))
     else:
         _check(lib, "na_attn_bwd_f32",
                lib.na_attn_bwd_f32(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse),
@@ -183,7 +214,7 @@ def decode_workspace_bytes(B, H, T_cap, D=HEAD_DIM):
 
 
 def attn_decode(q, k_cache, v_cache, seqlens, o=None, lse=None, workspace=None,
-                want_lse=True):
+                want_lse=True, window=None):
     """Single-token decode over a padded cache.  Returns (o, lse)."""
     import torch
     lib = load_library()
@@ -205,8 +236,15 @@ def attn_decode(q, k_cache, v_cache, seqlens, o=None, lse=None, workspace=None,
     need = decode_workspace_bytes(B, H, T_cap, D)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    window = _window(window)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    if window is not None:
+        _check(lib, "na_attn_decode_window",
+               lib.na_attn_decode_window(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seqlens),
+                                         _ptr(o), _ptr(lse), B, H, D, T_cap, window,
+                                         _ptr(workspace), ws_bytes, _stream(q), None))
+        return o, lse
     _check(lib, "na_attn_decode",
            lib.na_attn_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seqlens), _ptr(o),
-                              _ptr(lse), B, H, D, T_cap, _ptr(workspace),
-                              workspace.numel() * workspace.element_size(), _stream(q)))
+                              _ptr(lse), B, H, D, T_cap, _ptr(workspace), ws_bytes, _stream(q)))
     return o, lse

@@ -91,14 +91,19 @@ const char* na_status_string(na_status s) {
 
 const char* na_last_error(void) { return g_msg; }
 
-na_status na_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
-                      int T, int H, int D, void* stream) {
+na_status na_attn_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse,
+                             int B, int T, int H, int D, int window, void* stream) {
   na_status st = check_sizes(B, T, H, D);
   if (st) return st;
   st = check_ptrs({{q, "q"}, {k, "k"}, {v, "v"}}, {{o, "o"}, {lse, "lse"}});
   if (st) return st;
-  return hip_status(na::launch_fwd_bf16(q, k, v, o, lse, B, T, H, (hipStream_t)stream),
-                    "na_attn_fwd");
+  return hip_status(
+      na::launch_fwd_bf16(q, k, v, o, lse, B, T, H, window, (hipStream_t)stream), "na_attn_fwd");
+}
+
+na_status na_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                      int T, int H, int D, void* stream) {
+  return na_attn_fwd_window(q, k, v, o, lse, B, T, H, D, -1, stream);
 }
 
 size_t na_attn_bwd_workspace_bytes(int B, int T, int H, int D) {
@@ -106,12 +111,16 @@ size_t na_attn_bwd_workspace_bytes(int B, int T, int H, int D) {
   return na::bwd_workspace_bytes(B, T, H);
 }
 
-na_status na_attn_bwd_timed(const void* q, const void* k, const void* v, const void* o,
-                            const void* dout, const float* lse, void* dq, void* dk, void* dv,
-                            float* delta, void* workspace, size_t workspace_bytes, int B,
-                            int T, int H, int D, void* stream, void* const* events) {
+na_status na_attn_bwd_window(const void* q, const void* k, const void* v, const void* o,
+                             const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                             float* delta, void* workspace, size_t workspace_bytes, int B,
+                             int T, int H, int D, int window, void* stream,
+                             void* const* events) {
   na_status st = check_sizes(B, T, H, D);
   if (st) return st;
+  if (workspace == nullptr && window >= 0 && window < T - 1)
+    return fail(NA_ERR_UNSUPPORTED, "a sliding window (window=%d) needs the dS workspace",
+                window);
   if (workspace != nullptr) {
     st = check_ptrs({{q, "q"}, {k, "k"}, {v, "v"}, {o, "o"}, {dout, "dout"}, {lse, "lse"}},
                     {{dq, "dq"}, {dk, "dk"}, {dv, "dv"}, {delta, "delta"},
@@ -129,9 +138,17 @@ na_status na_attn_bwd_timed(const void* q, const void* k, const void* v, const v
     if (st) return st;
   }
   return hip_status(na::launch_bwd_bf16(q, k, v, o, dout, lse, dq, dk, dv, delta, workspace, B,
-                                        T, H, (hipStream_t)stream,
+                                        T, H, window, (hipStream_t)stream,
                                         reinterpret_cast<hipEvent_t const*>(events)),
                     "na_attn_bwd");
+}
+
+na_status na_attn_bwd_timed(const void* q, const void* k, const void* v, const void* o,
+                            const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                            float* delta, void* workspace, size_t workspace_bytes, int B,
+                            int T, int H, int D, void* stream, void* const* events) {
+  return na_attn_bwd_window(q, k, v, o, dout, lse, dq, dk, dv, delta, workspace,
+                            workspace_bytes, B, T, H, D, -1, stream, events);
 }
 
 na_status na_attn_bwd(const void* q, const void* k, const void* v, const void* o,
@@ -147,10 +164,10 @@ size_t na_attn_decode_workspace_bytes(int B, int H, int D, int T_cap) {
   return na::decode_workspace_bytes(B, H, T_cap);
 }
 
-na_status na_attn_decode_timed(const void* q, const void* k_cache, const void* v_cache,
-                               const int* seqlens, void* o, float* lse, int B, int H, int D,
-                               int T_cap, void* workspace, size_t workspace_bytes, void* stream,
-                               void* const* events) {
+na_status na_attn_decode_window(const void* q, const void* k_cache, const void* v_cache,
+                                const int* seqlens, void* o, float* lse, int B, int H, int D,
+                                int T_cap, int window, void* workspace, size_t workspace_bytes,
+                                void* stream, void* const* events) {
   na_status st = check_sizes(B, T_cap, H, D);
   if (st) return st;
   if (lse != nullptr) {
@@ -167,9 +184,17 @@ na_status na_attn_decode_timed(const void* q, const void* k_cache, const void* v
   if (workspace_bytes < need)
     return fail(NA_ERR_INVALID_ARG, "workspace_bytes %zu < required %zu", workspace_bytes, need);
   return hip_status(na::launch_decode_bf16(q, k_cache, v_cache, seqlens, o, lse, B, H, T_cap,
-                                           workspace, (hipStream_t)stream,
+                                           window, workspace, (hipStream_t)stream,
                                            reinterpret_cast<hipEvent_t const*>(events)),
                     "na_attn_decode");
+}
+
+na_status na_attn_decode_timed(const void* q, const void* k_cache, const void* v_cache,
+                               const int* seqlens, void* o, float* lse, int B, int H, int D,
+                               int T_cap, void* workspace, size_t workspace_bytes, void* stream,
+                               void* const* events) {
+  return na_attn_decode_window(q, k_cache, v_cache, seqlens, o, lse, B, H, D, T_cap, -1,
+                               workspace, workspace_bytes, stream, events);
 }
 
 na_status na_attn_decode(const void* q, const void* k_cache, const void* v_cache,

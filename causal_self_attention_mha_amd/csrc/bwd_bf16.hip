@@ -138,15 +138,16 @@ __device__ __forceinline__ void store_ds(u16* blk, const bf16x8 (&sb)[2], int la
 // and of delta.
 // MASK: the current block holds this wavefront's diagonal; kq is its key
 // minus the first query row of the current tile, and P is zeroed where the
-// key follows the query.
-template <bool MASK>
+// key follows the query.  BAND (with MASK): P is also zeroed where the query
+// lies more than win rows after the key (outside a sliding window).
+template <bool MASK, bool BAND = false>
 __device__ __forceinline__ void dkdv_step(const uint32_t (&na)[8], int rowN, const float* nl_t,
                                           const float* dl_t, const uint32_t (&ta)[4][2],
                                           int rowC, const bf16x8 (&kreg)[8],
                                           const bf16x8 (&vreg)[8], const f32x16& s_cur,
                                           const f32x16& p_cur, f32x16& s_nxt, f32x16& p_nxt,
                                           f32x16 (&dka)[4], f32x16 (&dva)[4], int lane,
-                                          float c_log2, int kq, u16* ds_blk) {
+                                          float c_log2, int kq, u16* ds_blk, int win = 0) {
   const int half = lane >> 5;
   const uint32_t rn = rowN * 256;
   const uint32_t rc = rowC * 256;
@@ -181,8 +182,8 @@ __device__ __forceinline__ void dkdv_step(const uint32_t (&na)[8], int rowN, con
     float p0 = fast_exp2(fmaf(s_cur[r], c_log2, lr[i].x));
     float p1 = fast_exp2(fmaf(s_cur[r + 1], c_log2, lr[i].y));
     if (MASK) {  // rows rr(i), rr(i) + 1 of the current tile
-      if (kq > rr(i)) p0 = 0.f;
-      if (kq > rr(i) + 1) p1 = 0.f;
+      if (kq > rr(i) || (BAND && rr(i) - kq > win)) p0 = 0.f;
+      if (kq > rr(i) + 1 || (BAND && rr(i) + 1 - kq > win)) p1 = 0.f;
     }
     pw[i] = pack_bf16x2(p0, p1);
     sw[i] = pack_bf16x2(p0 * (p_cur[r] - dr[i].x), p1 * (p_cur[r + 1] - dr[i].y));
@@ -221,11 +222,13 @@ __device__ __forceinline__ void to_exp2_offset(float* rows, int lane) {
   rows[lane] = rows[lane] * -kLog2e;
 }
 
+// WIN: sliding window, key j visible to query i iff i - win <= j <= i.
+template <bool WIN>
 __global__ __launch_bounds__(256, 1) void dkdv_kernel(
     const u16* __restrict__ q, const u16* __restrict__ k, const u16* __restrict__ v,
     const u16* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
     u16* __restrict__ dk, u16* __restrict__ dv, u16* __restrict__ dsw, int nbt, int B, int T,
-    int H, float c_log2, float scale) {
+    int H, float c_log2, float scale, int win) {
   // NBUF query tiles (q and dout, swizzled, see tile_swz) and their lse, delta rows
   __shared__ __attribute__((aligned(1024))) char qtiles[NBUF * BUF_B];
   __shared__ __attribute__((aligned(1024))) char kstage[2 * TILE_B];  // K rows of an item
@@ -252,9 +255,10 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(
   const uint32_t est_lds = lds_addr(&estage[wave][0]);
 
   // A work item: the 128-key tile k0 / 128 of head bh (xcd_tile_map_grouped
-  // order, key tile 0, the one with the most work, first).
+  // order, key tile 0, the one with the most work, first), whose keys are
+  // seen by the query tiles qt0 .. qte - 1.
   struct Item {
-    int bh, k0, qt0;
+    int bh, k0, qt0, qte;
     size_t base;
   };
   auto item_at = [&](int r, Item& it) -> bool {
@@ -265,6 +269,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(
     it.bh = bh;
     it.k0 = kt * KT_KEYS;
     it.qt0 = it.k0 / QT_ROWS;
+    it.qte = WIN ? min(n_qt, (it.k0 + KT_KEYS - 1 + win) / QT_ROWS + 1) : n_qt;
     it.base = static_cast<size_t>(bh / H) * T * rs + static_cast<size_t>(bh % H) * D;
     return true;
   };
@@ -320,14 +325,15 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(
   copy_rows(cur, k, kst_lds);
   copy_rows(cur, v, qt_lds + 2 * BUF_B);
   issue(cur, cur.qt0, 0);
-  if (cur.qt0 + 1 < n_qt) issue(cur, cur.qt0 + 1, 1);
+  if (cur.qt0 + 1 < cur.qte) issue(cur, cur.qt0 + 1, 1);
   sync_tiles();
 
   for (int r = 0;; ++r) {
     // K rows in kstage, V rows in buffer (gb + 2) % NBUF, query tiles qt0 and
     // qt0 + 1 in buffers gb, gb + 1: all landed.
     const int qt0 = cur.qt0;
-    const int nt = n_qt - qt0;  // query tiles of this item
+    const int qte = cur.qte;
+    const int nt = qte - qt0;  // query tiles of this item
     const int kw0 = cur.k0 + 32 * wave;
     const size_t base = cur.base;
     const int bh = cur.bh;
@@ -351,7 +357,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(
       }
     }
     __syncthreads();  // kstage and buffer (gb + 2) % NBUF are free again
-    if (qt0 + 2 < n_qt) issue(cur, qt0 + 2, ub2);
+    if (qt0 + 2 < qte) issue(cur, qt0 + 2, ub2);
     int nx = 0;              // leading query tiles of the next item issued
     bool k_next = false;     // next item's K rows issued
 
@@ -397,48 +403,61 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(
         sync_tiles();
         const int u2 = un == NBUF - 1 ? 0 : un + 1;
         const int pos = t + 2;
-        if (pos < n_qt) {
+        if (pos < qte) {
           issue(cur, pos, u2);
-        } else if (has_next && pos - n_qt == nx && nx < 2 && nxt.qt0 + nx < n_qt) {
+        } else if (has_next && pos - qte == nx && nx < 2 && nxt.qt0 + nx < nxt.qte) {
           issue(nxt, nxt.qt0 + nx, u2);  // the next item's tile nx, in stream order
           ++nx;
         }
-        if (t == n_qt - 1 && has_next) {
+        if (t == qte - 1 && has_next) {
           copy_rows(nxt, k, kst_lds);
           k_next = true;
         }
-        if (t + 1 < n_qt && wave == 3) to_exp2_offset(lsd[un][0], lane);  // tile t+1
+        if (t + 1 < qte && wave == 3) to_exp2_offset(lsd[un][0], lane);  // tile t+1
       }
       uint32_t tc[4][2], nn[8];
       tr_addr(qt_lds + u * BUF_B, ofs, tc);
       nat_addr(qt_lds + un * BUF_B, ofs, nn);
       const int kq = krow - QT_ROWS * t;
       const int j0 = 2 * t, j1 = 2 * t + 1;
+      // with a window: some row of tile t lies past the window of this
+      // wavefront's first key, so its steps also take the band select
+      const bool edge = WIN && QT_ROWS * t + QT_ROWS - 1 - kw0 > win;
       // block j0 (rows 0..31 of tile t), scores of rows 32..63
-      if (STEADY || j0 > bw)
-        dkdv_step<false>(nc, 32, lsd[u][0], lsd[u][1], tc, 0, kreg, vreg, s0, p0, s1, p1, dka,
-                         dva, lane, c_log2, kq, ds_of(j0));
-      else if (j0 == bw)
-        dkdv_step<true>(nc, 32, lsd[u][0], lsd[u][1], tc, 0, kreg, vreg, s0, p0, s1, p1, dka,
-                        dva, lane, c_log2, kq, ds_of(j0));
-      else if (j0 == bw - 1)
+      if (STEADY || j0 > bw) {
+        if (WIN && edge)
+          dkdv_step<true, true>(nc, 32, lsd[u][0], lsd[u][1], tc, 0, kreg, vreg, s0, p0, s1, p1,
+                                dka, dva, lane, c_log2, kq, ds_of(j0), win);
+        else
+          dkdv_step<false>(nc, 32, lsd[u][0], lsd[u][1], tc, 0, kreg, vreg, s0, p0, s1, p1, dka,
+                           dva, lane, c_log2, kq, ds_of(j0));
+      } else if (j0 == bw) {
+        dkdv_step<true, WIN>(nc, 32, lsd[u][0], lsd[u][1], tc, 0, kreg, vreg, s0, p0, s1, p1,
+                             dka, dva, lane, c_log2, kq, ds_of(j0), win);
+      } else if (j0 == bw - 1) {
         dkdv_scores(nc, 32, kreg, vreg, s1, p1);
+      }
       // block j1 (rows 32..63 of tile t), scores of tile t+1 rows 0..31
-      if (STEADY || j1 > bw)
-        dkdv_step<false>(nn, 0, lsd[u][0], lsd[u][1], tc, 32, kreg, vreg, s1, p1, s0, p0, dka,
-                         dva, lane, c_log2, kq, ds_of(j1));
-      else if (j1 == bw)
-        dkdv_step<true>(nn, 0, lsd[u][0], lsd[u][1], tc, 32, kreg, vreg, s1, p1, s0, p0, dka,
-                        dva, lane, c_log2, kq, ds_of(j1));
-      else if (j1 == bw - 1)
+      if (STEADY || j1 > bw) {
+        if (WIN && edge)
+          dkdv_step<true, true>(nn, 0, lsd[u][0], lsd[u][1], tc, 32, kreg, vreg, s1, p1, s0, p0,
+                                dka, dva, lane, c_log2, kq, ds_of(j1), win);
+        else
+          dkdv_step<false>(nn, 0, lsd[u][0], lsd[u][1], tc, 32, kreg, vreg, s1, p1, s0, p0, dka,
+                           dva, lane, c_log2, kq, ds_of(j1));
+      } else if (j1 == bw) {
+        dkdv_step<true, WIN>(nn, 0, lsd[u][0], lsd[u][1], tc, 32, kreg, vreg, s1, p1, s0, p0,
+                             dka, dva, lane, c_log2, kq, ds_of(j1), win);
+      } else if (j1 == bw - 1) {
         dkdv_scores(nn, 0, kreg, vreg, s0, p0);
+      }
 #pragma unroll
       for (int kc = 0; kc < 8; ++kc) nc[kc] = nn[kc];
       u = un;
     };
-    const int t_diag_end = min(qt0 + 2, n_qt);
+    const int t_diag_end = min(qt0 + 2, qte);
     for (int t = qt0; t < t_diag_end; ++t) tile(t, std::false_type{});
-    for (int t = t_diag_end; t < n_qt; ++t) tile(t, std::true_type{});
+    for (int t = t_diag_end; t < qte; ++t) tile(t, std::true_type{});
 
     // Every wavefront is done with the last tile's buffer: the next item's V
     // rows go there, and whatever the stream has not copied yet of its K rows
@@ -449,7 +468,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(
       if (!k_next) copy_rows(nxt, k, kst_lds);
       copy_rows(nxt, v, qt_lds + ulast * BUF_B);
       for (int j = nx; j < 2; ++j)
-        if (nxt.qt0 + j < n_qt) issue(nxt, nxt.qt0 + j, (gb + nt + j) % NBUF);
+        if (nxt.qt0 + j < nxt.qte) issue(nxt, nxt.qt0 + j, (gb + nt + j) % NBUF);
     }
 
     // dka[db], dva[db] (dK^T, dV^T blocks) element r: key kw0 + l32,
@@ -759,10 +778,12 @@ constexpr int DG_ROWS = 128;  // queries per workgroup (32 per wavefront)
 constexpr int DG_KEYS = 64;   // keys per K tile
 constexpr uint32_t DG_DS_B = 2 * 32 * 32 * 2;  // a wavefront's two dS blocks per key tile
 
+// WIN: sliding window, key j visible to query i iff i - win <= j <= i.
+template <bool WIN>
 __global__ __launch_bounds__(256, 2) void dq_gemm_kernel(const u16* __restrict__ k,
                                                          const u16* __restrict__ dsw,
                                                          u16* __restrict__ dq, int nbt, int B,
-                                                         int T, int H, float scale) {
+                                                         int T, int H, float scale, int win) {
   __shared__ __attribute__((aligned(1024))) char ktile[2][kTileBytes];   // swizzled K
   __shared__ __attribute__((aligned(1024))) char sst[3][4][DG_DS_B];     // dS blocks per wave
 
@@ -803,6 +824,8 @@ __global__ __launch_bounds__(256, 2) void dq_gemm_kernel(const u16* __restrict__
 
     const int last_q = min(q0 + DG_ROWS, T) - 1;
     const int n_kt = last_q / DG_KEYS + 1;
+    // first key tile that any row of the workgroup sees (0 without a window)
+    const int kt_lo = WIN ? max(q0 - win, 0) / DG_KEYS : 0;
 
     // K^T read addresses in buffer 0 (buffer 1: + kTileBytes)
     uint32_t ktr[4][2];
@@ -877,8 +900,11 @@ __global__ __launch_bounds__(256, 2) void dq_gemm_kernel(const u16* __restrict__
           issue_ds(kt + 2, (kt + 2) % 3, 2 * (j - 2) + 1);
         }
         if (j + 1 < 4) read(j + 1);
-        // block 2 kt + kb of this wavefront's row exists (wavefront-uniform)
-        if (live && 2 * kt + (j >> 1) <= qblk) {
+        // block 2 kt + kb of this wavefront's row exists and, with a window,
+        // holds a visible pair (wavefront-uniform); the dK/dV pass stored
+        // every such block
+        const int kblk = 2 * kt + (j >> 1);
+        if (live && kblk <= qblk && (!WIN || 32 * kblk + 31 >= 32 * qblk - win)) {
 #pragma unroll
           for (int db = 0; db < 4; ++db) dqa[db] = mfma32(a[j & 1][db], bs[j & 1], dqa[db]);
         }
@@ -887,14 +913,14 @@ __global__ __launch_bounds__(256, 2) void dq_gemm_kernel(const u16* __restrict__
     };
 
 #pragma unroll
-    for (int j = 0; j < 4; ++j) issue_k(0, 0, j);
+    for (int j = 0; j < 4; ++j) issue_k(kt_lo, 0, j);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) issue_ds(0, 0, j);
-    if (n_kt > 1) {
+    for (int j = 0; j < 4; ++j) issue_ds(kt_lo, kt_lo % 3, j);
+    if (kt_lo + 1 < n_kt) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) issue_ds(1, 1, j);
+      for (int j = 0; j < 4; ++j) issue_ds(kt_lo + 1, (kt_lo + 1) % 3, j);
     }
-    for (int kt = 0; kt < n_kt; kt += 2) {
+    for (int kt = kt_lo; kt < n_kt; kt += 2) {
       tile(std::integral_constant<uint32_t, 0>{}, kt);
       if (kt + 1 < n_kt) tile(std::integral_constant<uint32_t, 1>{}, kt + 1);
     }
@@ -924,8 +950,8 @@ std::size_t bwd_workspace_bytes(int B, int T, int H) {
 
 hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const void* o,
                            const void* dout, const float* lse, void* dq, void* dk, void* dv,
-                           float* delta, void* ws, int B, int T, int H, hipStream_t s,
-                           hipEvent_t const* ev) {
+                           float* delta, void* ws, int B, int T, int H, int window,
+                           hipStream_t s, hipEvent_t const* ev) {
   const float scale = 1.0f / sqrtf(static_cast<float>(D));
   const float c_log2 = scale * kLog2e;
   const u16* q16 = static_cast<const u16*>(q);
@@ -944,17 +970,21 @@ hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const vo
   if ((e = mark(ev, 1, s)) != hipSuccess) return e;
   const int n_kt = (T + KT_KEYS - 1) / KT_KEYS;
   const dim3 kv_grid(persistent_grid(static_cast<long>(n_kt) * B * H, 1));
-  e = launch(dkdv_kernel, kv_grid, dim3(256), 0, s, q16, k16, v16, g16, lse,
-             static_cast<const float*>(delta), static_cast<u16*>(dk), static_cast<u16*>(dv), dsw,
-             nbt, B, T, H, c_log2, scale);
+  // a window that covers every key of every row is the plain causal case
+  const bool win = window >= 0 && window < T - 1;
+  const int w = win ? window : T;
+  e = launch(win ? dkdv_kernel<true> : dkdv_kernel<false>, kv_grid, dim3(256), 0, s, q16, k16,
+             v16, g16, lse, static_cast<const float*>(delta), static_cast<u16*>(dk),
+             static_cast<u16*>(dv), dsw, nbt, B, T, H, c_log2, scale, w);
   if (e != hipSuccess) return e;
   if ((e = mark(ev, 2, s)) != hipSuccess) return e;
   if (dsw != nullptr) {
     const int n_qt = (T + DG_ROWS - 1) / DG_ROWS;
-    e = launch(dq_gemm_kernel, dim3(persistent_grid(static_cast<long>(n_qt) * B * H, 2)),
-               dim3(256), 0, s, k16,
-               static_cast<const u16*>(dsw), static_cast<u16*>(dq), nbt, B, T, H, scale);
+    e = launch(win ? dq_gemm_kernel<true> : dq_gemm_kernel<false>,
+               dim3(persistent_grid(static_cast<long>(n_qt) * B * H, 2)), dim3(256), 0, s, k16,
+               static_cast<const u16*>(dsw), static_cast<u16*>(dq), nbt, B, T, H, scale, w);
   } else {
+    if (win) return hipErrorInvalidValue;  // the recompute pass has no window (checked on the host)
     const int n_qt = (T + DQ_ROWS - 1) / DQ_ROWS;
     e = launch(dq_kernel, dim3(static_cast<unsigned>(n_qt) * B * H), dim3(256), 0, s, q16, k16,
                v16, g16, lse, static_cast<const float*>(delta), static_cast<u16*>(dq), B, T, H,

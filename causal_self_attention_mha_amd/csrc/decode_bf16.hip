@@ -1,7 +1,8 @@
 // bf16 single-token decode over a ragged, padded KV cache (split-KV).
 //
-// Per (b, h), with L = seqlens[b] clamped to [0, T_cap]:
-//   z_j = s <q_bh, K[b, j, h]>  (j < L),  o = softmax(z) V[b, 0:L, h],
+// Per (b, h), with L = seqlens[b] clamped to [0, T_cap] and j0 = 0 (or, with
+// a sliding window W, j0 = max(0, L - 1 - W): the query sits at row L - 1):
+//   z_j = s <q_bh, K[b, j, h]>  (j0 <= j < L),  o = softmax(z) V[b, j0:L, h],
 //   lse = ln sum_j exp(z_j)
 // i.e. the attention step nanochat's inference engine runs per generated
 // token against its prefilled prompt cache through flash_attn_with_kvcache
@@ -55,14 +56,15 @@ __host__ __device__ inline int n_chunks(int T_cap) { return (T_cap + CHUNK - 1) 
 struct Batch {
   int slot;  // flattened slot index, or -1 past the end
   int b, c;  // sequence and chunk
-  int n;     // keys in this chunk
+  int n;     // keys of the chunk below L (rows c * CHUNK .. c * CHUNK + n - 1)
   int ib;    // batch within the chunk
+  int j0;    // first visible key of the sequence
 };
 
 __global__ __launch_bounds__(512) void decode_split_kernel(
     const u16* __restrict__ q, const u16* __restrict__ kc, const u16* __restrict__ vc,
     const int* __restrict__ seqlens, float* __restrict__ opart, float* __restrict__ ml, int B,
-    int H, int T_cap, float scale) {
+    int H, int T_cap, float scale, int win) {
   __shared__ int pre[kMaxFlatB + 1];  // pre[b] = non-empty chunks of sequences < b
   const int tid = threadIdx.x;
   const int h = tid >> 4;
@@ -71,6 +73,10 @@ __global__ __launch_bounds__(512) void decode_split_kernel(
   const int P = gridDim.x;
   const bool flat = B <= kMaxFlatB;
   auto len = [&](int b) { return min(max(seqlens[b], 0), T_cap); };
+  // first visible key of a sequence of length L (win < 0: no window)
+  auto first_key = [&](int L) { return win < 0 ? 0 : max(0, L - 1 - win); };
+  // chunks holding a visible key: first_key(L) / CHUNK .. (L - 1) / CHUNK
+  auto n_vis = [&](int L) { return L > 0 ? (L - 1) / CHUNK - first_key(L) / CHUNK + 1 : 0; };
   int total;  // number of slots
   if (flat) {
     // prefix sums of chunk counts: serial over 64-sequence blocks, each block
@@ -79,7 +85,7 @@ __global__ __launch_bounds__(512) void decode_split_kernel(
       int run = 0;
       for (int b0 = 0; b0 < B; b0 += 64) {
         const int b = b0 + tid;
-        const int c = b < B ? (len(b) + CHUNK - 1) / CHUNK : 0;
+        const int c = b < B ? n_vis(len(b)) : 0;
         int x = c;  // inclusive scan over the wavefront
 #pragma unroll
         for (int o = 1; o < 64; o <<= 1) {
@@ -106,15 +112,20 @@ __global__ __launch_bounds__(512) void decode_split_kernel(
         if (pre[mid] <= slot) lo = mid; else hi = mid - 1;
       }
       t.b = lo;
-      t.c = slot - pre[lo];
+      t.c = first_key(len(lo)) / CHUNK + slot - pre[lo];
     } else {
       t.b = slot / NC;
       t.c = slot % NC;
     }
-    t.n = min(CHUNK, len(t.b) - t.c * CHUNK);  // <= 0 only for raw empty slots
+    const int L = len(t.b);
+    t.j0 = first_key(L);
+    // <= 0 only for raw slots past L or wholly before the window
+    t.n = t.c < t.j0 / CHUNK ? 0 : min(CHUNK, L - t.c * CHUNK);
+    // batches wholly before j0 are skipped
+    t.ib = t.c == t.j0 / CHUNK ? (t.j0 - t.c * CHUNK) / U : 0;
   };
   auto first_from = [&](int slot) {  // first non-empty slot >= slot (stride P)
-    Batch t{-1, 0, 0, 0, 0};
+    Batch t{-1, 0, 0, 0, 0, 0};
     for (; slot < total; slot += P) {
       locate(slot, t);
       if (t.n > 0) {
@@ -140,9 +151,12 @@ __global__ __launch_bounds__(512) void decode_split_kernel(
     const size_t base = (static_cast<size_t>(t.b) * T_cap + t.c * CHUNK) * rs +
                         static_cast<size_t>(h) * D + 8 * l16;
     const int rsi = H * D;
+    const int r_lo = t.j0 - t.c * CHUNK;  // rows before it lie before the window
 #pragma unroll
     for (int i = 0; i < U; ++i) {
-      const int r = min(t.ib * U + i, t.n - 1) * rsi;  // rows past n: re-read, zero weight
+      // rows past n or before the window: row n-1 / the first visible row is
+      // read again instead (zero weight), so no row outside the window is read
+      const int r = min(max(t.ib * U + i, r_lo), t.n - 1) * rsi;
       xk[i] = ld16(kc + base + r);
       xv[i] = ld16(vc + base + r);
     }
@@ -174,19 +188,23 @@ __global__ __launch_bounds__(512) void decode_split_kernel(
         a = fmaf(qv[2 * w + 1], __uint_as_float(u & 0xffff0000u), a);
       }
       a = sum16(a);
-      z[i] = t.ib * U + i < t.n ? a : -INFINITY;
+      const int row = t.ib * U + i;
+      z[i] = row < t.n && t.c * CHUNK + row >= t.j0 ? a : -INFINITY;
     }
-    float bm = z[0];  // finite: row ib * U < n
+    float bm = z[0];
 #pragma unroll
     for (int i = 1; i < U; ++i) bm = fmaxf(bm, z[i]);
     const float m_new = fmaxf(m, bm);
-    const float alpha = fast_exp2(m - m_new);  // 0 on a chunk's first batch
+    // -inf only while every key so far lies before the window: exponents are
+    // then taken against 0 so that they give 0, not NaN
+    const float mref = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = fast_exp2(m - mref);  // 0 on a chunk's first batch
     l *= alpha;
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] *= alpha;
 #pragma unroll
     for (int i = 0; i < U; ++i) {
-      const float p = fast_exp2(z[i] - m_new);  // 0 for dropped rows
+      const float p = fast_exp2(z[i] - mref);  // 0 for dropped rows
       l += p;
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
@@ -222,24 +240,24 @@ __global__ __launch_bounds__(512) void decode_split_kernel(
     Batch nx = next(cur);
     if (nx.slot >= 0) {
       rows(nx, bk, bv);
-      if (nx.ib == 0) qb = qrow(nx);
+      if (nx.slot != cur.slot) qb = qrow(nx);  // a new slot: its query
     }
     __builtin_amdgcn_sched_barrier(0);
     compute(cur, ak, av);
     __builtin_amdgcn_sched_barrier(0);
     if (nx.slot < 0) break;
-    if (nx.ib == 0) set_q(qb);
+    if (nx.slot != cur.slot) set_q(qb);
     cur = nx;
     nx = next(cur);
     if (nx.slot >= 0) {
       rows(nx, ak, av);
-      if (nx.ib == 0) qa = qrow(nx);
+      if (nx.slot != cur.slot) qa = qrow(nx);
     }
     __builtin_amdgcn_sched_barrier(0);
     compute(cur, bk, bv);
     __builtin_amdgcn_sched_barrier(0);
     if (nx.slot < 0) break;
-    if (nx.ib == 0) set_q(qa);
+    if (nx.slot != cur.slot) set_q(qa);
     cur = nx;
   }
 }
@@ -247,10 +265,11 @@ __global__ __launch_bounds__(512) void decode_split_kernel(
 __global__ __launch_bounds__(128) void decode_combine_kernel(
     const float* __restrict__ opart, const float* __restrict__ ml,
     const int* __restrict__ seqlens, u16* __restrict__ o, float* __restrict__ lse, int H,
-    int T_cap, int NC) {
+    int T_cap, int NC, int win) {
   const int h = blockIdx.x, b = blockIdx.y;
   const int L = min(max(seqlens[b], 0), T_cap);
-  const int nc = (L + CHUNK - 1) / CHUNK;
+  const int nc = (L + CHUNK - 1) / CHUNK;                         // chunks end here
+  const int c_lo = win < 0 || L == 0 ? 0 : max(0, L - 1 - win) / CHUNK;  // and start here
   const int d = threadIdx.x;
   const float* mlb = ml + 2 * (static_cast<size_t>(b) * NC * H + h);  // chunk c at 2 c H
   const float* opb = opart + (static_cast<size_t>(b) * NC * H + h) * D + d;  // chunk c at c H D
@@ -258,7 +277,7 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(
   // before they are used), with a running max M
   constexpr int G = 16;
   float M = -INFINITY, den = 0.f, num = 0.f;
-  for (int c0 = 0; c0 < nc; c0 += G) {
+  for (int c0 = c_lo; c0 < nc; c0 += G) {
     float mv[G], lv[G], ov[G];
 #pragma unroll
     for (int i = 0; i < G; ++i) {
@@ -297,10 +316,12 @@ std::size_t decode_workspace_bytes(int B, int H, int T_cap) {
 }
 
 hipError_t launch_decode_bf16(const void* q, const void* kc, const void* vc, const int* seqlens,
-                              void* o, float* lse, int B, int H, int T_cap, void* ws,
-                              hipStream_t s, hipEvent_t const* ev) {
+                              void* o, float* lse, int B, int H, int T_cap, int window,
+                              void* ws, hipStream_t s, hipEvent_t const* ev) {
   const float scale = 1.0f / sqrtf(static_cast<float>(D));
   const int NC = n_chunks(T_cap);
+  // a window that covers the whole cache is no window
+  const int win = window >= 0 && window < T_cap - 1 ? window : -1;
   float* opart = static_cast<float*>(ws);
   float* ml = opart + static_cast<std::size_t>(B) * NC * H * D;
   // persistent workgroups: a few per compute unit, never more than slots
@@ -313,11 +334,12 @@ hipError_t launch_decode_bf16(const void* q, const void* kc, const void* vc, con
   if (e != hipSuccess) return e;
   e = launch(decode_split_kernel, dim3(P), dim3(16 * H), 0, s, static_cast<const u16*>(q),
              static_cast<const u16*>(kc), static_cast<const u16*>(vc), seqlens, opart, ml, B, H,
-             T_cap, scale);
+             T_cap, scale, win);
   if (e != hipSuccess) return e;
   if ((e = mark(ev, 1, s)) != hipSuccess) return e;
   e = launch(decode_combine_kernel, dim3(H, B), dim3(128), 0, s, static_cast<const float*>(opart),
-             static_cast<const float*>(ml), seqlens, static_cast<u16*>(o), lse, H, T_cap, NC);
+             static_cast<const float*>(ml), seqlens, static_cast<u16*>(o), lse, H, T_cap, NC,
+             win);
   if (e != hipSuccess) return e;
   return mark(ev, 2, s);
 }

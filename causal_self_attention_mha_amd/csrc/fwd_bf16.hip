@@ -49,12 +49,13 @@ constexpr uint32_t BUF_B = 2 * kTileBytes;  // one buffer: K tile, then V tile
 // the rescale; probabilities then stay below 256, harmless in fp32 and bf16.
 constexpr float kRescaleLog2 = 8.0f;
 
-__global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(const u16* __restrict__ q,
-                                                          const u16* __restrict__ k,
-                                                          const u16* __restrict__ v,
-                                                          u16* __restrict__ o,
-                                                          float* __restrict__ lse, int B, int T,
-                                                          int H, float c_log2, float scale) {
+// WIN: sliding window, key j visible to query i iff i - win <= j <= i (the
+// plain causal kernel is WIN = false).
+template <bool WIN>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(
+    const u16* __restrict__ q, const u16* __restrict__ k, const u16* __restrict__ v,
+    u16* __restrict__ o, float* __restrict__ lse, int B, int T, int H, float c_log2, float scale,
+    int win) {
   // two buffers of (K tile, V tile), swizzled (see tile_swz)
   __shared__ __attribute__((aligned(1024))) char kvs[2 * BUF_B];
 
@@ -95,6 +96,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(const u16* __
 
   const int last_q = min(q0 + BQ, T) - 1;
   const int n_kt = last_q / BK + 1;  // key tiles at or left of the diagonal
+  // first key tile that any row of the workgroup sees (0 without a window)
+  const int kt_lo = WIN ? max(q0 - win, 0) / BK : 0;
 
   // operand read addresses in buffer 0 (buffer 1: + BUF_B, V tile: + kTileBytes)
   const uint32_t kv_lds = lds_addr(kvs);
@@ -127,7 +130,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(const u16* __
     // next copy may then overwrite.
     wait_vmem();
     __syncthreads();
-    const bool skip = k0 > qw0 + 31;  // whole tile above this wavefront's diagonal
+    // whole tile above this wavefront's diagonal, or before its rows' windows
+    const bool skip = k0 > qw0 + 31 || (WIN && k0 + BK - 1 < qw0 - win);
     // The copy of the next tile is issued once this tile's K reads are done
     // (measured faster than issuing it at the barrier).
     if (skip) {
@@ -163,14 +167,15 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(const u16* __
     }
     if (kt + 1 < n_kt) issue(kt + 1, 1 - BUF);
 
-    // causal select on tiles that cross the diagonal
-    if (k0 + BK - 1 > qw0) {
+    // causal select on tiles that cross the diagonal (and, with a window, on
+    // tiles that cross the lower edge of some row's window)
+    if (k0 + BK - 1 > qw0 || (WIN && k0 < qw0 + 31 - win)) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = k0 + kb * 32 + acc_row(lane, r);
-          if (key > qrow) sacc[kb][r] = -INFINITY;
+          if (key > qrow || (WIN && key < qrow - win)) sacc[kb][r] = -INFINITY;
         }
     }
 
@@ -182,7 +187,10 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(const u16* __
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
     if (__any(mx > m + thr)) {  // wavefront-uniform
       const float m_new = fmaxf(m, mx);
-      const float alpha = fast_exp2((m - m_new) * c_log2);  // 0 on the first tile
+      // 0 on the first tile; with a window, a row whose keys so far all lie
+      // before its window keeps m = -inf (and l = 0, O = 0): any finite factor
+      const float alpha =
+          (WIN && m_new == -INFINITY) ? 0.f : fast_exp2((m - m_new) * c_log2);
       lpart *= alpha;
 #pragma unroll
       for (int db = 0; db < 4; ++db)
@@ -190,7 +198,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(const u16* __
         for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
       m = m_new;
     }
-    const float neg = -m * c_log2;
+    // a row whose keys so far all lie before its window (WIN only) still has
+    // m = -inf: its probabilities are exp2(-inf) = 0, not exp2(-inf + inf)
+    const float neg = (WIN && m == -INFINITY) ? 0.f : -m * c_log2;
 
     // P^T as bf16 MFMA B operands: chunk c (16 keys) = sacc[c/2][8(c%2) .. +7]
     bf16x8 pb[4];
@@ -217,8 +227,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(const u16* __
     }
   };
 
-  issue(0, 0);
-  for (int kt = 0; kt < n_kt; kt += 2) {
+  issue(kt_lo, 0);
+  for (int kt = kt_lo; kt < n_kt; kt += 2) {
     tile(std::integral_constant<uint32_t, 0>{}, kt);
     if (kt + 1 < n_kt) tile(std::integral_constant<uint32_t, 1>{}, kt + 1);
   }
@@ -243,14 +253,16 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(const u16* __
 }  // namespace
 
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
-                           int B, int T, int H, hipStream_t s) {
+                           int B, int T, int H, int window, hipStream_t s) {
   const float scale = 1.0f / sqrtf(static_cast<float>(D));
   const float c_log2 = scale * 1.4426950408889634f;
   const int n_qt = (T + BQ - 1) / BQ;
   const dim3 grid(static_cast<unsigned>(n_qt) * B * H);
-  return launch(fwd_bf16_kernel, grid, dim3(64 * NW), 0, s, static_cast<const u16*>(q),
-                static_cast<const u16*>(k), static_cast<const u16*>(v), static_cast<u16*>(o),
-                lse, B, T, H, c_log2, scale);
+  const bool win = window >= 0 && window < T - 1;  // else every row sees all its keys
+  return launch(win ? fwd_bf16_kernel<true> : fwd_bf16_kernel<false>, grid, dim3(64 * NW), 0, s,
+                static_cast<const u16*>(q), static_cast<const u16*>(k),
+                static_cast<const u16*>(v), static_cast<u16*>(o), lse, B, T, H, c_log2, scale,
+                win ? window : T);
 }
 
 }  // namespace na

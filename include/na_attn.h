@@ -16,7 +16,8 @@
  * Readings fixed by this library (the pages do not write them out):
  *   - scores z_ij = s <q_i, k_j> with s = 1/sqrt(D); softmax over keys;
  *   - causal: key j is visible to query i iff j <= i (T_q = T_k, top left);
- *   - n_kv_head = n_head, full causal window;
+ *   - n_kv_head = n_head; full causal window (the *_window entry points
+ *     below take a sliding window);
  *   - lse_i = ln sum_j exp(z_ij) over visible keys (natural log, fp32);
  *   - bf16 inputs are rounded values; all accumulation is fp32; fp32 -> bf16
  *     conversions round to nearest even.
@@ -134,6 +135,33 @@ na_status na_attn_decode_timed(const void* q, const void* k_cache, const void* v
                                const int* seqlens, void* o, float* lse, int B, int H, int D,
                                int T_cap, void* workspace, size_t workspace_bytes, void* stream,
                                void* const* events);
+
+/*
+ * Sliding-window (banded causal) variants.  nanochat alternates short- and
+ * long-window layers (the "SSSL" pattern of the blog's section 1 "GPT model")
+ * through flash_attn_func's window_size argument (section 5).  The pages give
+ * neither the window length nor the argument's convention; here, as in
+ * flash-attention's (left, right) = (window, 0) band under a causal mask, key j
+ * is visible to query i iff i - window <= j <= i (the query and the `window`
+ * keys before it).  Decode: the query sits at row L - 1 of a sequence of
+ * length L and sees keys max(0, L - 1 - window) .. L - 1.  window < 0, or a
+ * window that reaches key 0 from every row (window >= T - 1, resp.
+ * T_cap - 1), is exactly the plain entry point.  The windowed backward needs
+ * the dS workspace (NA_ERR_UNSUPPORTED with workspace == NULL).  Arguments,
+ * layouts and errors otherwise as for the plain calls; `events` as for the
+ * _timed entry points (NULL allowed).
+ */
+na_status na_attn_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse,
+                             int B, int T, int H, int D, int window, void* stream);
+na_status na_attn_bwd_window(const void* q, const void* k, const void* v, const void* o,
+                             const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                             float* delta, void* workspace, size_t workspace_bytes, int B,
+                             int T, int H, int D, int window, void* stream,
+                             void* const* events);
+na_status na_attn_decode_window(const void* q, const void* k_cache, const void* v_cache,
+                                const int* seqlens, void* o, float* lse, int B, int H, int D,
+                                int T_cap, int window, void* workspace, size_t workspace_bytes,
+                                void* stream, void* const* events);
 
 /* Static text for a status code. */
 const char* na_status_string(na_status s);

@@ -33,7 +33,8 @@ def test_header_declares_the_entry_points():
     syms = declared_symbols()
     for s in ("na_attn_fwd", "na_attn_bwd", "na_attn_decode", "na_attn_decode_workspace_bytes",
               "na_attn_bwd_workspace_bytes", "na_attn_bwd_timed", "na_attn_decode_timed",
-              "na_attn_fwd_f32", "na_attn_bwd_f32", "na_status_string", "na_last_error"):
+              "na_attn_fwd_f32", "na_attn_bwd_f32", "na_status_string", "na_last_error",
+              "na_attn_fwd_window", "na_attn_bwd_window", "na_attn_decode_window"):
         assert s in syms
 
 
@@ -99,6 +100,29 @@ def test_bwd_rejects_bad_arguments(lib):
     bad[9] = 0                     # delta scratch
     assert bwd(bad) == INVALID
     assert lib.na_attn_bwd_f32(*bad[:5], bad[5], *bad[6:9], bad[9], 1, 8, 1, 128, None) == INVALID
+
+
+def test_window_entry_points_check_their_arguments(lib):
+    assert lib.na_attn_fwd_window(0, A, A + 0x100, A + 0x200, A + 0x300, 1, 8, 1, 128, 3,
+                                  None) == INVALID
+    assert lib.na_attn_fwd_window(A, A + 0x100, A + 0x200, A + 0x300, A + 0x400, 1, 8, 1, 64, 3,
+                                  None) == UNSUPPORTED
+    p = [A + 0x100 * i for i in range(11)]
+    need = lib.na_attn_bwd_workspace_bytes(1, 8, 1, 128)
+    # a real window needs the dS workspace ...
+    assert lib.na_attn_bwd_window(*p[:10], None, 0, 1, 8, 1, 128, 3, None, None) == UNSUPPORTED
+    assert b"workspace" in lib.na_last_error()
+    # ... and the usual checks still apply with one
+    bad = list(p)
+    bad[7] = bad[6]
+    assert lib.na_attn_bwd_window(*bad[:10], bad[10], need, 1, 8, 1, 128, 3, None,
+                                  None) == INVALID
+    d = [A + 0x100 * i for i in range(7)]   # q k v seqlens o lse workspace
+    wneed = lib.na_attn_decode_workspace_bytes(4, 2, 128, 64)
+    assert lib.na_attn_decode_window(d[0], d[1], d[2], 0, d[4], d[5], 4, 2, 128, 64, 5, d[6],
+                                     wneed, None, None) == INVALID
+    assert lib.na_attn_decode_window(*d[:6], 4, 2, 128, 64, 5, d[6], wneed - 1, None,
+                                     None) == INVALID
 
 
 def test_bwd_workspace_bytes(lib):
