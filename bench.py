@@ -14,6 +14,12 @@ uniform in [1, 2048]) is timed in its own loop and reported under "decode";
 it rotates three separately allocated caches so that no call finds its
 cache in the 256 MB Infinity Cache.
 
+The same d20 step with a sliding window (--window, default 1024: the short
+"S" layers of nanochat's SSSL pattern; the pages give no window length, so
+half the context is this benchmark's choice) and the windowed decode are
+timed the same way and reported under "sliding_window" (FLOPs and bytes
+counted over the visible (query, key) pairs only).
+
 The fp64 oracle runs once on a bounded sample of the same workload on the
 host cores and is reported as "cpu_baseline" (a reported baseline, not the
 target).
@@ -119,6 +125,14 @@ def train_bytes(B, T, H, D):
             "dq": t + ds + t}
 
 
+def visible_pairs(T, window):
+    """(query, key) pairs per head with j <= i and, given a window, i - j <= window."""
+    if window is None or window >= T - 1:
+        return T * (T + 1) // 2
+    w = window
+    return (w + 1) * (w + 2) // 2 - (w + 1) + (T - w) * (w + 1) if T > w else T * (T + 1) // 2
+
+
 def cpu_baseline(inp, n_heads):
     """Time the fp64 oracle (as it stands) on the first n_heads (b, h) heads."""
     import oracle
@@ -150,6 +164,8 @@ def main():
     ap.add_argument("--cpu-heads", type=int, default=256,
                     help="(b,h) heads in the oracle CPU-baseline sample (0 = skip)")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--window", type=int, default=1024,
+                    help="sliding-window length for the extra windowed measurement (-1 = skip)")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="first run a plain device copy of this many MiB (a known-size "
                          "kernel that calibrates HBM byte counters in a profiler run)")
@@ -208,15 +224,16 @@ def main():
     evs = [ev.create(5) for _ in range(n_total)]
     ev_arr = [(ctypes.c_void_p * 4)(*[e.value for e in step[1:5]]) for step in evs]
 
-    def step(i):
+    def step(i, window=-1):
         e = evs[i]
         ev.record(e[0], stream)
-        st = lib.na_attn_fwd(ptr(q), ptr(k), ptr(v), ptr(o), ptr(lse), B, T, H, D, P(stream))
+        st = lib.na_attn_fwd_window(ptr(q), ptr(k), ptr(v), ptr(o), ptr(lse), B, T, H, D,
+                                    window, P(stream))
         if st:
             raise RuntimeError(lib.na_last_error().decode())
-        st = lib.na_attn_bwd_timed(ptr(q), ptr(k), ptr(v), ptr(o), ptr(do), ptr(lse), ptr(dq),
-                                   ptr(dk), ptr(dv), ptr(delta), ptr(ws), ws_bytes, B, T, H, D,
-                                   P(stream), ctypes.cast(ev_arr[i], P))
+        st = lib.na_attn_bwd_window(ptr(q), ptr(k), ptr(v), ptr(o), ptr(do), ptr(lse), ptr(dq),
+                                    ptr(dk), ptr(dv), ptr(delta), ptr(ws), ws_bytes, B, T, H, D,
+                                    window, P(stream), ctypes.cast(ev_arr[i], P))
         if st:
             raise RuntimeError(lib.na_last_error().decode())
 
@@ -275,6 +292,39 @@ def main():
         "roofline": roofline,
     }
 
+    # ---------------- the same step with a sliding window
+    wlen = args.window if 0 <= args.window < T - 1 else None
+    if wlen is not None:
+        log(f"sliding window {wlen}: warmup {args.warmup}, timing {args.steps} steps")
+        for i in range(args.warmup):
+            step(i, wlen)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.warmup, n_total):
+            step(i, wlen)
+        torch.cuda.synchronize()
+        wwall = time.perf_counter() - t0
+        wper = {n: [] for n in names}
+        for i in range(args.warmup, n_total):
+            for j, n in enumerate(names):
+                wper[n].append(ev.ms(evs[i][j], evs[i][j + 1]))
+        pairs = visible_pairs(T, wlen)
+        wfl = {"fwd": 2, "delta": 0, "dkdv": 4, "dq": 1}
+        wfl = {n: c * B * H * pairs * 2 * D for n, c in wfl.items()}
+        w_ms = wwall * 1e3 / args.steps
+        wk = {}
+        for n in names:
+            avg = float(np.mean(wper[n]))
+            wk[n] = {"avg_us": round(avg * 1e3, 2),
+                     "tflops": round(wfl[n] / (avg * 1e-3) / 1e12, 2) if wfl[n] else None}
+        w_tf = 7 * B * H * pairs * 2 * D / (w_ms * 1e-3) / 1e12
+        result["sliding_window"] = {
+            "workload": f"d20 causal self-attention fwd+bwd, sliding window {wlen}",
+            "window": wlen, "ms_per_step": round(w_ms, 4), "TFLOP_per_s": round(w_tf, 2),
+            "flops_per_step": 7 * B * H * pairs * 2 * D, "visible_pairs_per_head": pairs,
+            "kernels": wk}
+        log(f"sliding window {wlen}: {w_ms:.3f} ms  {w_tf:.1f} TFLOP/s  kernels {wk}")
+
     del q, k, v, do, o, dq, dk, dv, ws
     torch.cuda.empty_cache()
 
@@ -298,11 +348,11 @@ def main():
         devs = [ev.create(3) for _ in range(nd + 5)]
         darr = [(ctypes.c_void_p * 3)(*[e.value for e in x]) for x in devs]
 
-        def dstep(i):
+        def dstep(i, window=-1):
             kc, vc = caches[i % 3]
-            st = lib.na_attn_decode_timed(ptr(qd), ptr(kc), ptr(vc), ptr(lens), ptr(od), ptr(lsed),
-                                          Bd, Hd, D, Tc, ptr(ws), wsb, P(stream),
-                                          ctypes.cast(darr[i], P))
+            st = lib.na_attn_decode_window(ptr(qd), ptr(kc), ptr(vc), ptr(lens), ptr(od),
+                                           ptr(lsed), Bd, Hd, D, Tc, window, ptr(ws), wsb,
+                                           P(stream), ctypes.cast(darr[i], P))
             if st:
                 raise RuntimeError(lib.na_last_error().decode())
 
@@ -329,6 +379,21 @@ def main():
             "split_GB_per_s": round(split_gbs, 1), "iters": nd, "rotated_caches": 3,
         }
         log(f"decode {result['decode']}")
+        if wlen is not None:
+            for i in range(5):
+                dstep(i, wlen)
+            torch.cuda.synchronize()
+            for i in range(5, nd + 5):
+                dstep(i, wlen)
+            torch.cuda.synchronize()
+            wtot = [ev.ms(devs[i][0], devs[i][2]) for i in range(5, nd + 5)]
+            wkv = int(np.minimum(dinp.seqlens.astype(np.int64), wlen + 1).sum()) * Hd * D * 2 * 2
+            w_ms = float(np.mean(wtot))
+            w_gbs = (wkv + io_bytes) / (w_ms * 1e-3) / 1e9
+            result["sliding_window"]["decode"] = {
+                "us_per_call": round(w_ms * 1e3, 2), "kv_bytes": wkv,
+                "GB_per_s": round(w_gbs, 1), "pct_hbm_peak": round(100 * w_gbs / PEAK_HBM_GBS, 2)}
+            log(f"sliding window decode {result['sliding_window']['decode']}")
         del caches, kc0, vc0
         torch.cuda.empty_cache()
 
