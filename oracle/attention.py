@@ -23,7 +23,12 @@ readings taken here (plainest, all listed in the design notes):
     iff i - W <= j <= i: the query itself and the W keys before it.  The blog
     gives neither W nor the argument's convention; this is flash-attention's
     (left, right) = (W, 0) band under a causal mask;
-  * n_kv_head = n_head (plain multi-head attention);
+  * n_kv_head = n_head (plain multi-head attention) by default; with fewer
+    key/value heads (GQA, same blog, section 1: fewer KV heads than query
+    heads for faster inference), H is a multiple of H_kv and query head h
+    reads key/value head h // (H / H_kv), the grouping of torch's
+    scaled_dot_product_attention(enable_gqa=True); a key/value head's
+    gradient is the sum over the query heads that read it;
   * LSE is the natural log of sum_j exp(s * q_i . k_j) over visible keys;
   * the loss depends on O only, so the LSE output receives no gradient;
   * decode: the single new query is the last cached position and sees all
@@ -40,8 +45,15 @@ import numpy as np
 
 __all__ = [
     "softmax_scale", "forward_head", "backward_head", "forward", "backward",
-    "decode_head", "decode", "causal_probabilities",
+    "decode_head", "decode", "causal_probabilities", "kv_head", "kv_grads",
 ]
+
+
+def kv_head(h: int, H: int, H_kv: int) -> int:
+    """Key/value head read by query head h (H a multiple of H_kv)."""
+    if H % H_kv != 0:
+        raise ValueError(f"H={H} is not a multiple of H_kv={H_kv}")
+    return h // (H // H_kv)
 
 
 def softmax_scale(D: int) -> float:
@@ -132,42 +144,66 @@ def forward(q, k, v, heads=None, window=None):
     or W >= 0 (see the module notes).
     """
     B, T, H, D = q.shape
+    Hk = k.shape[2]
+    kh = lambda h: kv_head(h, H, Hk)  # noqa: E731
     if heads is not None:
-        return {(b, h): forward_head(q[b, :, h, :], k[b, :, h, :], v[b, :, h, :], window)
+        return {(b, h): forward_head(q[b, :, h, :], k[b, :, kh(h), :], v[b, :, kh(h), :], window)
                 for (b, h) in heads}
     o = np.empty((B, T, H, D), dtype=np.float64)
     lse = np.empty((B, H, T), dtype=np.float64)
     for b in range(B):
         for h in range(H):
-            O, L = forward_head(q[b, :, h, :], k[b, :, h, :], v[b, :, h, :], window)
+            O, L = forward_head(q[b, :, h, :], k[b, :, kh(h), :], v[b, :, kh(h), :], window)
             o[b, :, h, :] = O
             lse[b, h, :] = L
     return o, lse
 
 
 def backward(q, k, v, do, heads=None, window=None):
-    """Batched backward over (B, T, H, D) arrays.
+    """Batched backward over (B, T, H, D) arrays (k, v: (B, T, H_kv, D)).
 
-    Returns dq, dk, dv (B, T, H, D) and delta (B, H, T) in float64, or, when
-    `heads` is given, a dict {(b, h): (dQ, dK, dV, delta)} for those heads.
+    Returns dq (B, T, H, D), dk, dv (B, T, H_kv, D) and delta (B, H, T) in
+    float64, or, when `heads` is given, a dict {(b, h): (dQ, dK, dV, delta)}
+    for those query heads, where dK and dV are query head h's share of its
+    key/value head's gradient (see kv_grads for the group sums).
     """
     B, T, H, D = q.shape
+    Hk = k.shape[2]
+    kh = lambda h: kv_head(h, H, Hk)  # noqa: E731
     if heads is not None:
-        return {(b, h): backward_head(q[b, :, h, :], k[b, :, h, :], v[b, :, h, :],
+        return {(b, h): backward_head(q[b, :, h, :], k[b, :, kh(h), :], v[b, :, kh(h), :],
                                       do[b, :, h, :], window) for (b, h) in heads}
     dq = np.empty((B, T, H, D), dtype=np.float64)
-    dk = np.empty_like(dq)
-    dv = np.empty_like(dq)
+    dk = np.zeros((B, T, Hk, D), dtype=np.float64)
+    dv = np.zeros_like(dk)
     delta = np.empty((B, H, T), dtype=np.float64)
     for b in range(B):
         for h in range(H):
-            gq, gk, gv, dl = backward_head(q[b, :, h, :], k[b, :, h, :], v[b, :, h, :],
+            gq, gk, gv, dl = backward_head(q[b, :, h, :], k[b, :, kh(h), :], v[b, :, kh(h), :],
                                            do[b, :, h, :], window)
             dq[b, :, h, :] = gq
-            dk[b, :, h, :] = gk
-            dv[b, :, h, :] = gv
+            dk[b, :, kh(h), :] += gk
+            dv[b, :, kh(h), :] += gv
             delta[b, h, :] = dl
     return dq, dk, dv, delta
+
+
+def kv_grads(q, k, v, do, kv_heads, window=None):
+    """{(b, hk): (dK, dV)} for the listed key/value heads: the sums, over the
+    query heads that read head hk, of their backward_head shares."""
+    H, Hk = q.shape[2], k.shape[2]
+    G = H // Hk
+    out = {}
+    for (b, hk) in kv_heads:
+        dK = np.zeros(k.shape[1:2] + k.shape[3:], dtype=np.float64)
+        dV = np.zeros_like(dK)
+        for h in range(hk * G, hk * G + G):
+            _, gk, gv, _ = backward_head(q[b, :, h, :], k[b, :, hk, :], v[b, :, hk, :],
+                                         do[b, :, h, :], window)
+            dK += gk
+            dV += gv
+        out[(b, hk)] = (dK, dV)
+    return out
 
 
 def decode_head(q, K, V, L: int, window=None):
@@ -193,20 +229,22 @@ def decode_head(q, K, V, L: int, window=None):
 
 
 def decode(q, k_cache, v_cache, seqlens, pairs=None, window=None):
-    """Batched decode.  q (B, H, D); caches (B, T_cap, H, D); seqlens int [B].
+    """Batched decode.  q (B, H, D); caches (B, T_cap, H_kv, D); seqlens int [B].
 
     Returns o (B, H, D) and lse (B, H) in float64, or a dict {(b, h): (o, lse)}
     when `pairs` lists the (b, h) pairs to compute.
     """
     B, H, D = q.shape
+    Hk = k_cache.shape[2]
+    kh = lambda h: kv_head(h, H, Hk)  # noqa: E731
     if pairs is not None:
-        return {(b, h): decode_head(q[b, h], k_cache[b, :, h, :], v_cache[b, :, h, :],
+        return {(b, h): decode_head(q[b, h], k_cache[b, :, kh(h), :], v_cache[b, :, kh(h), :],
                                     int(seqlens[b]), window) for (b, h) in pairs}
     o = np.empty((B, H, D), dtype=np.float64)
     lse = np.empty((B, H), dtype=np.float64)
     for b in range(B):
         for h in range(H):
-            ob, lb = decode_head(q[b, h], k_cache[b, :, h, :], v_cache[b, :, h, :],
+            ob, lb = decode_head(q[b, h], k_cache[b, :, kh(h), :], v_cache[b, :, kh(h), :],
                                  int(seqlens[b]), window)
             o[b, h] = ob
             lse[b, h] = lb

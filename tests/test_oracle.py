@@ -383,3 +383,88 @@ def test_window_decode_equals_last_forward_row_and_ignores_old_keys():
             O, l = oracle.forward_head(Qf, kc[b, :L, h, :], vc[b, :L, h, :], window=W)
             assert np.allclose(o[b, h], O[L - 1], rtol=0, atol=1e-13)
             assert abs(lse[b, h] - l[L - 1]) <= 1e-13
+
+
+# ---------------------------------------------------------------- grouped-query attention
+
+@pytest.mark.parametrize("H,Hk,W", [(4, 2, None), (6, 2, None), (4, 1, None), (4, 2, 5)])
+def test_gqa_against_torch_sdpa_fp64(H, Hk, W):
+    """torch's CPU scaled_dot_product_attention(enable_gqa=True) and its
+    autograd in float64 (query head h reads key/value head h // (H / Hk))."""
+    torch = pytest.importorskip("torch")
+    B, T, D = 2, 29, 16
+    q, do = rnd((B, T, H, D), 401), rnd((B, T, H, D), 404)
+    k, v = rnd((B, T, Hk, D), 402), rnd((B, T, Hk, D), 403)
+    o, lse = oracle.forward(q, k, v, window=W)
+    dq, dk, dv, _ = oracle.backward(q, k, v, do, window=W)
+    assert dk.shape == (B, T, Hk, D)
+    tq, tk, tv = (torch.tensor(x.transpose(0, 2, 1, 3).copy(), dtype=torch.float64,
+                               requires_grad=True) for x in (q, k, v))
+    i = torch.arange(T)[:, None]
+    j = torch.arange(T)[None, :]
+    allowed = (j <= i) if W is None else (j <= i) & (j >= i - W)
+    to = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=allowed,
+                                                          enable_gqa=True)
+    to.backward(torch.tensor(do.transpose(0, 2, 1, 3).copy(), dtype=torch.float64))
+    back = lambda t: t.detach().numpy().transpose(0, 2, 1, 3)  # noqa: E731
+    assert np.allclose(o, back(to), rtol=0, atol=1e-12)
+    assert np.allclose(dq, back(tq.grad), rtol=0, atol=1e-11)
+    assert np.allclose(dk, back(tk.grad), rtol=0, atol=1e-11)
+    assert np.allclose(dv, back(tv.grad), rtol=0, atol=1e-11)
+
+
+def test_gqa_finite_differences():
+    B, T, H, Hk, D = 1, 5, 4, 2, 4
+    q, do = rnd((B, T, H, D), 411), rnd((B, T, H, D), 414)
+    k, v = rnd((B, T, Hk, D), 412), rnd((B, T, Hk, D), 413)
+    dq, dk, dv, _ = oracle.backward(q, k, v, do)
+    loss = lambda a, b, c: float(np.sum(oracle.forward(a, b, c)[0] * do))  # noqa: E731
+    eps = 1e-6
+    for idx, (x, g) in enumerate(((q, dq), (k, dk), (v, dv))):
+        fd = np.zeros_like(x)
+        for pos in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[pos] += eps
+            xm[pos] -= eps
+            args_p, args_m = [q, k, v], [q, k, v]
+            args_p[idx], args_m[idx] = xp, xm
+            fd[pos] = (loss(*args_p) - loss(*args_m)) / (2 * eps)
+        assert np.allclose(g, fd, rtol=0, atol=2e-8)
+
+
+def test_gqa_is_mha_on_repeated_heads():
+    """GQA equals MHA with each key/value head repeated for its query heads
+    (consecutive query heads share one), and the key/value gradients are the
+    group sums of the repeated heads' gradients."""
+    B, T, H, Hk, D = 2, 23, 6, 3, 8
+    G = H // Hk
+    q, do = rnd((B, T, H, D), 421), rnd((B, T, H, D), 424)
+    k, v = rnd((B, T, Hk, D), 422), rnd((B, T, Hk, D), 423)
+    kr, vr = np.repeat(k, G, axis=2), np.repeat(v, G, axis=2)
+    o, lse = oracle.forward(q, k, v)
+    o2, lse2 = oracle.forward(q, kr, vr)
+    assert np.array_equal(o, o2) and np.array_equal(lse, lse2)
+    dq, dk, dv, _ = oracle.backward(q, k, v, do)
+    dq2, dk2, dv2, _ = oracle.backward(q, kr, vr, do)
+    assert np.array_equal(dq, dq2)
+    assert np.allclose(dk, dk2.reshape(B, T, Hk, G, D).sum(axis=3), rtol=0, atol=1e-13)
+    assert np.allclose(dv, dv2.reshape(B, T, Hk, G, D).sum(axis=3), rtol=0, atol=1e-13)
+    got = oracle.kv_grads(q, k, v, do, [(1, 2), (0, 0)])
+    for (b, hk), (gk, gv) in got.items():
+        assert np.allclose(gk, dk[b, :, hk], rtol=0, atol=1e-13)
+        assert np.allclose(gv, dv[b, :, hk], rtol=0, atol=1e-13)
+
+
+def test_gqa_decode_reads_the_group_head():
+    B, Tc, H, Hk, D = 2, 30, 4, 2, 16
+    q = rnd((B, H, D), 431, 0.5)
+    kc, vc = rnd((B, Tc, Hk, D), 432, 0.5), rnd((B, Tc, Hk, D), 433, 0.5)
+    lens = np.array([9, 30])
+    o, lse = oracle.decode(q, kc, vc, lens)
+    for b, L in enumerate(lens):
+        for h in range(H):
+            Qf = kc[b, :L, h // 2, :].copy()
+            Qf[L - 1] = q[b, h]
+            O, l = oracle.forward_head(Qf, kc[b, :L, h // 2, :], vc[b, :L, h // 2, :])
+            assert np.allclose(o[b, h], O[L - 1], rtol=0, atol=1e-13)
+            assert abs(lse[b, h] - l[L - 1]) <= 1e-13
