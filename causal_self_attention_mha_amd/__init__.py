@@ -14,7 +14,9 @@ Functions (names match the C entry points):
   attn_decode(q, k_cache, v_cache, seqlens) -> (o, lse)
 Each takes window=W (an int >= 0) for sliding-window attention (key j visible
 to query i iff i - W <= j <= i), which calls the *_window entry point;
-window=None is plain causal attention.
+window=None is plain causal attention.  k and v (and the decode caches) may
+have fewer heads than q (grouped-query attention, H a multiple of H_kv; the
+*_gqa entry points); dk and dv then have the key/value heads' shape.
 bf16 tensors use the bf16 kernels, float32 tensors the fp32 kernels
 (forward and backward only).  Layouts: q, k, v, o, dout (B, T, H, 128);
 lse, delta (B, H, T) float32; decode q/o (B, H, 128), caches (B, T_cap, H, 128),
@@ -77,9 +79,15 @@ def load_library():
     lib.na_attn_fwd_window.argtypes = [vp, vp, vp, vp, f32p, i, i, i, i, i, vp]
     lib.na_attn_bwd_window.argtypes = lib.na_attn_bwd.argtypes[:-1] + [i, vp, vp]
     lib.na_attn_decode_window.argtypes = [vp, vp, vp, vp, vp, f32p, i, i, i, i, i, vp, sz, vp, vp]
+    lib.na_attn_fwd_gqa.argtypes = [vp, vp, vp, vp, f32p, i, i, i, i, i, i, vp]
+    lib.na_attn_bwd_gqa.argtypes = [vp, vp, vp, vp, vp, f32p, vp, vp, vp, f32p, vp, sz, i, i, i,
+                                    i, i, i, vp, vp]
+    lib.na_attn_decode_gqa.argtypes = [vp, vp, vp, vp, vp, f32p, i, i, i, i, i, i, vp, sz, vp,
+                                       vp]
     for fn in ("na_attn_fwd", "na_attn_bwd", "na_attn_decode", "na_attn_fwd_f32",
                "na_attn_bwd_f32", "na_attn_bwd_timed", "na_attn_decode_timed",
-               "na_attn_fwd_window", "na_attn_bwd_window", "na_attn_decode_window"):
+               "na_attn_fwd_window", "na_attn_bwd_window", "na_attn_decode_window",
+               "na_attn_fwd_gqa", "na_attn_bwd_gqa", "na_attn_decode_gqa"):
         getattr(lib, fn).restype = ctypes.c_int
     lib.na_status_string.argtypes = [ctypes.c_int]
     lib.na_status_string.restype = ctypes.c_char_p
@@ -108,7 +116,9 @@ def _require(cond, msg):
         raise ValueError(msg)
 
 
-def _check_train(names, tensors, dtype=None):
+def _check_train(names, tensors, dtype=None, kv_heads=None):
+    """Same dtype, device, contiguity and (B, T, H, 128) shape as the first
+    tensor; tensors named in kv_heads may instead have H_kv heads."""
     import torch
     ref = tensors[0]
     _require(ref.is_cuda, f"{names[0]} must be a GPU tensor (no CPU path)")
@@ -118,7 +128,10 @@ def _check_train(names, tensors, dtype=None):
     _require(dtype in (torch.bfloat16, torch.float32), f"unsupported dtype {dtype}")
     for n, t in zip(names, tensors):
         _require(t.dtype == dtype, f"{n} has dtype {t.dtype}, expected {dtype}")
-        _require(t.shape == ref.shape, f"{n} has shape {tuple(t.shape)}, expected {tuple(ref.shape)}")
+        want = tuple(ref.shape)
+        if kv_heads is not None and n in kv_heads:
+            want = want[:2] + (kv_heads[n],) + want[3:]
+        _require(tuple(t.shape) == want, f"{n} has shape {tuple(t.shape)}, expected {want}")
         _require(t.device == ref.device, f"{n} is on {t.device}, expected {ref.device}")
         _require(t.is_contiguous(), f"{n} must be contiguous")
     return dtype
@@ -131,11 +144,19 @@ def _window(window):
     return int(window)
 
 
+def _kv_heads(q, k):
+    _require(k.dim() == 4, f"k must be (B, T, H_kv, {HEAD_DIM}), got {tuple(k.shape)}")
+    H, Hk = q.shape[2], k.shape[2]
+    _require(Hk >= 1 and H % Hk == 0, f"q has {H} heads, not a multiple of k's {Hk}")
+    return Hk
+
+
 def attn_fwd(q, k, v, o=None, lse=None, window=None):
     """Causal attention forward.  Returns (o, lse): o like q, lse float32 (B, H, T)."""
     import torch
     lib = load_library()
-    dtype = _check_train(("q", "k", "v"), (q, k, v))
+    Hk = _kv_heads(q, k)
+    dtype = _check_train(("q", "k", "v"), (q, k, v), kv_heads={"k": Hk, "v": Hk})
     B, T, H, D = q.shape
     o = torch.empty_like(q) if o is None else o
     lse = torch.empty((B, H, T), dtype=torch.float32, device=q.device) if lse is None else lse
@@ -143,11 +164,17 @@ def attn_fwd(q, k, v, o=None, lse=None, window=None):
     _require(lse.shape == (B, H, T) and lse.dtype == torch.float32 and lse.is_contiguous(),
              "lse must be contiguous float32 (B, H, T)")
     window = _window(window)
-    if window is not None:
-        _require(dtype == torch.bfloat16, "window: bf16 tensors only")
-        _check(lib, "na_attn_fwd_window",
-               lib.na_attn_fwd_window(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, T, H, D,
-                                      window, _stream(q)))
+    if Hk != H or window is not None:
+        _require(dtype == torch.bfloat16, "window / grouped heads: bf16 tensors only")
+        w = -1 if window is None else window
+        if Hk != H:
+            _check(lib, "na_attn_fwd_gqa",
+                   lib.na_attn_fwd_gqa(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, T, H,
+                                       Hk, D, w, _stream(q)))
+        else:
+            _check(lib, "na_attn_fwd_window",
+                   lib.na_attn_fwd_window(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, T,
+                                          H, D, w, _stream(q)))
         return o, lse
     fn = "na_attn_fwd" if dtype == torch.bfloat16 else "na_attn_fwd_f32"
     _check(lib, fn, getattr(lib, fn)(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, T, H, D,
@@ -169,7 +196,9 @@ def attn_bwd(q, k, v, o, dout, lse, dq=None, dk=None, dv=None, delta=None, works
     window needs the workspace).  fp32 has one path."""
     import torch
     lib = load_library()
-    dtype = _check_train(("q", "k", "v", "o", "dout"), (q, k, v, o, dout))
+    Hk = _kv_heads(q, k)
+    kvh = {"k": Hk, "v": Hk}
+    dtype = _check_train(("q", "k", "v", "o", "dout"), (q, k, v, o, dout), kv_heads=kvh)
     B, T, H, D = q.shape
     _require(lse.shape == (B, H, T) and lse.dtype == torch.float32 and lse.is_contiguous(),
              "lse must be contiguous float32 (B, H, T)")
@@ -177,9 +206,11 @@ def attn_bwd(q, k, v, o, dout, lse, dq=None, dk=None, dv=None, delta=None, works
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
     delta = torch.empty((B, H, T), dtype=torch.float32, device=q.device) if delta is None else delta
-    _check_train(("q", "dq", "dk", "dv"), (q, dq, dk, dv), dtype)
+    _check_train(("q", "dq", "dk", "dv"), (q, dq, dk, dv), dtype,
+                 kv_heads={"dk": Hk, "dv": Hk})
     window = _window(window)
-    _require(window is None or dtype == torch.bfloat16, "window: bf16 tensors only")
+    _require((window is None and Hk == H) or dtype == torch.bfloat16,
+             "window / grouped heads: bf16 tensors only")
     if dtype == torch.bfloat16:
         ws_bytes = 0
         if not recompute_dq:
@@ -190,17 +221,17 @@ def attn_bwd(q, k, v, o, dout, lse, dq=None, dk=None, dv=None, delta=None, works
                 ws_bytes = workspace.numel() * workspace.element_size()
         else:
             workspace = None
-        if window is not None:
+        args = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk),
+                _ptr(dv), _ptr(delta), _ptr(workspace), ws_bytes)
+        w = -1 if window is None else window
+        if Hk != H:
+            _check(lib, "na_attn_bwd_gqa",
+                   lib.na_attn_bwd_gqa(*args, B, T, H, Hk, D, w, _stream(q), None))
+        elif window is not None:
             _check(lib, "na_attn_bwd_window",
-                   lib.na_attn_bwd_window(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout),
-                                          _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(delta),
-                                          _ptr(workspace), ws_bytes, B, T, H, D, window,
-                                          _stream(q), None))
+                   lib.na_attn_bwd_window(*args, B, T, H, D, w, _stream(q), None))
         else:
-            _check(lib, "na_attn_bwd",
-                   lib.na_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse),
-                                   _ptr(dq), _ptr(dk), _ptr(dv), _ptr(delta), _ptr(workspace),
-                                   ws_bytes, B, T, H, D, _stream(q)))
+            _check(lib, "na_attn_bwd", lib.na_attn_bwd(*args, B, T, H, D, _stream(q)))
     else:
         _check(lib, "na_attn_bwd_f32",
                lib.na_attn_bwd_f32(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse),
@@ -221,9 +252,10 @@ def attn_decode(q, k_cache, v_cache, seqlens, o=None, lse=None, workspace=None,
     _require(q.is_cuda and q.dtype == torch.bfloat16 and q.dim() == 3 and q.shape[-1] == HEAD_DIM,
              "q must be a bf16 GPU tensor (B, H, 128)")
     B, H, D = q.shape
-    _require(k_cache.dim() == 4 and k_cache.shape[0] == B and k_cache.shape[2] == H
-             and k_cache.shape[3] == D, "k_cache must be (B, T_cap, H, 128)")
-    T_cap = k_cache.shape[1]
+    _require(k_cache.dim() == 4 and k_cache.shape[0] == B and k_cache.shape[3] == D
+             and k_cache.shape[2] >= 1 and H % k_cache.shape[2] == 0,
+             "k_cache must be (B, T_cap, H_kv, 128) with H a multiple of H_kv")
+    T_cap, Hk = k_cache.shape[1], k_cache.shape[2]
     for n, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
         _require(t.dtype == torch.bfloat16 and t.device == q.device and t.is_contiguous(),
                  f"{n} must be contiguous bf16 on {q.device}")
@@ -238,13 +270,17 @@ def attn_decode(q, k_cache, v_cache, seqlens, o=None, lse=None, workspace=None,
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     window = _window(window)
     ws_bytes = workspace.numel() * workspace.element_size()
-    if window is not None:
+    args = (_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seqlens), _ptr(o), _ptr(lse))
+    w = -1 if window is None else window
+    if Hk != H:
+        _check(lib, "na_attn_decode_gqa",
+               lib.na_attn_decode_gqa(*args, B, H, Hk, D, T_cap, w, _ptr(workspace), ws_bytes,
+                                      _stream(q), None))
+    elif window is not None:
         _check(lib, "na_attn_decode_window",
-               lib.na_attn_decode_window(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seqlens),
-                                         _ptr(o), _ptr(lse), B, H, D, T_cap, window,
-                                         _ptr(workspace), ws_bytes, _stream(q), None))
-        return o, lse
-    _check(lib, "na_attn_decode",
-           lib.na_attn_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seqlens), _ptr(o),
-                              _ptr(lse), B, H, D, T_cap, _ptr(workspace), ws_bytes, _stream(q)))
+               lib.na_attn_decode_window(*args, B, H, D, T_cap, w, _ptr(workspace), ws_bytes,
+                                         _stream(q), None))
+    else:
+        _check(lib, "na_attn_decode",
+               lib.na_attn_decode(*args, B, H, D, T_cap, _ptr(workspace), ws_bytes, _stream(q)))
     return o, lse

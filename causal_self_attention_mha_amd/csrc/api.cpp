@@ -75,6 +75,14 @@ na_status check_sizes(int B, int T, int H, int D) {
   return NA_OK;
 }
 
+// Key/value heads: 1 <= H_kv <= H and H a multiple of H_kv.
+na_status check_kv_heads(int H, int H_kv) {
+  if (H_kv < 1 || H_kv > H || H % H_kv != 0)
+    return fail(NA_ERR_INVALID_ARG, "H=%d is not a multiple of H_kv=%d (1 <= H_kv <= H)", H,
+                H_kv);
+  return NA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -91,14 +99,21 @@ const char* na_status_string(na_status s) {
 
 const char* na_last_error(void) { return g_msg; }
 
-na_status na_attn_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse,
-                             int B, int T, int H, int D, int window, void* stream) {
+na_status na_attn_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
+                          int B, int T, int H, int H_kv, int D, int window, void* stream) {
   na_status st = check_sizes(B, T, H, D);
   if (st) return st;
+  if ((st = check_kv_heads(H, H_kv))) return st;
   st = check_ptrs({{q, "q"}, {k, "k"}, {v, "v"}}, {{o, "o"}, {lse, "lse"}});
   if (st) return st;
   return hip_status(
-      na::launch_fwd_bf16(q, k, v, o, lse, B, T, H, window, (hipStream_t)stream), "na_attn_fwd");
+      na::launch_fwd_bf16(q, k, v, o, lse, B, T, H, H_kv, window, (hipStream_t)stream),
+      "na_attn_fwd");
+}
+
+na_status na_attn_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse,
+                             int B, int T, int H, int D, int window, void* stream) {
+  return na_attn_fwd_gqa(q, k, v, o, lse, B, T, H, H, D, window, stream);
 }
 
 na_status na_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
@@ -111,13 +126,14 @@ size_t na_attn_bwd_workspace_bytes(int B, int T, int H, int D) {
   return na::bwd_workspace_bytes(B, T, H);
 }
 
-na_status na_attn_bwd_window(const void* q, const void* k, const void* v, const void* o,
-                             const void* dout, const float* lse, void* dq, void* dk, void* dv,
-                             float* delta, void* workspace, size_t workspace_bytes, int B,
-                             int T, int H, int D, int window, void* stream,
-                             void* const* events) {
+na_status na_attn_bwd_gqa(const void* q, const void* k, const void* v, const void* o,
+                          const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                          float* delta, void* workspace, size_t workspace_bytes, int B, int T,
+                          int H, int H_kv, int D, int window, void* stream,
+                          void* const* events) {
   na_status st = check_sizes(B, T, H, D);
   if (st) return st;
+  if ((st = check_kv_heads(H, H_kv))) return st;
   if (workspace == nullptr && window >= 0 && window < T - 1)
     return fail(NA_ERR_UNSUPPORTED, "a sliding window (window=%d) needs the dS workspace",
                 window);
@@ -138,9 +154,18 @@ na_status na_attn_bwd_window(const void* q, const void* k, const void* v, const 
     if (st) return st;
   }
   return hip_status(na::launch_bwd_bf16(q, k, v, o, dout, lse, dq, dk, dv, delta, workspace, B,
-                                        T, H, window, (hipStream_t)stream,
+                                        T, H, H_kv, window, (hipStream_t)stream,
                                         reinterpret_cast<hipEvent_t const*>(events)),
                     "na_attn_bwd");
+}
+
+na_status na_attn_bwd_window(const void* q, const void* k, const void* v, const void* o,
+                             const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                             float* delta, void* workspace, size_t workspace_bytes, int B,
+                             int T, int H, int D, int window, void* stream,
+                             void* const* events) {
+  return na_attn_bwd_gqa(q, k, v, o, dout, lse, dq, dk, dv, delta, workspace, workspace_bytes,
+                         B, T, H, H, D, window, stream, events);
 }
 
 na_status na_attn_bwd_timed(const void* q, const void* k, const void* v, const void* o,
@@ -164,12 +189,13 @@ size_t na_attn_decode_workspace_bytes(int B, int H, int D, int T_cap) {
   return na::decode_workspace_bytes(B, H, T_cap);
 }
 
-na_status na_attn_decode_window(const void* q, const void* k_cache, const void* v_cache,
-                                const int* seqlens, void* o, float* lse, int B, int H, int D,
-                                int T_cap, int window, void* workspace, size_t workspace_bytes,
-                                void* stream, void* const* events) {
+na_status na_attn_decode_gqa(const void* q, const void* k_cache, const void* v_cache,
+                             const int* seqlens, void* o, float* lse, int B, int H, int H_kv,
+                             int D, int T_cap, int window, void* workspace,
+                             size_t workspace_bytes, void* stream, void* const* events) {
   na_status st = check_sizes(B, T_cap, H, D);
   if (st) return st;
+  if ((st = check_kv_heads(H, H_kv))) return st;
   if (lse != nullptr) {
     st = check_ptrs({{q, "q"}, {k_cache, "k_cache"}, {v_cache, "v_cache"}, {seqlens, "seqlens"}},
                     {{o, "o"}, {lse, "lse"}, {workspace, "workspace"}});
@@ -183,10 +209,18 @@ na_status na_attn_decode_window(const void* q, const void* k_cache, const void* 
   const size_t need = na::decode_workspace_bytes(B, H, T_cap);
   if (workspace_bytes < need)
     return fail(NA_ERR_INVALID_ARG, "workspace_bytes %zu < required %zu", workspace_bytes, need);
-  return hip_status(na::launch_decode_bf16(q, k_cache, v_cache, seqlens, o, lse, B, H, T_cap,
-                                           window, workspace, (hipStream_t)stream,
+  return hip_status(na::launch_decode_bf16(q, k_cache, v_cache, seqlens, o, lse, B, H, H_kv,
+                                           T_cap, window, workspace, (hipStream_t)stream,
                                            reinterpret_cast<hipEvent_t const*>(events)),
                     "na_attn_decode");
+}
+
+na_status na_attn_decode_window(const void* q, const void* k_cache, const void* v_cache,
+                                const int* seqlens, void* o, float* lse, int B, int H, int D,
+                                int T_cap, int window, void* workspace, size_t workspace_bytes,
+                                void* stream, void* const* events) {
+  return na_attn_decode_gqa(q, k_cache, v_cache, seqlens, o, lse, B, H, H, D, T_cap, window,
+                            workspace, workspace_bytes, stream, events);
 }
 
 na_status na_attn_decode_timed(const void* q, const void* k_cache, const void* v_cache,

@@ -223,12 +223,15 @@ __device__ __forceinline__ void to_exp2_offset(float* rows, int lane) {
 }
 
 // WIN: sliding window, key j visible to query i iff i - win <= j <= i.
+// Hk key/value heads (H a multiple of Hk): a work item holds the keys of one
+// key/value head, and its query tiles run over the G = H / Hk query heads that
+// read it, so that dK and dV sum the group in registers.
 template <bool WIN>
 __global__ __launch_bounds__(256, 1) void dkdv_kernel(
     const u16* __restrict__ q, const u16* __restrict__ k, const u16* __restrict__ v,
     const u16* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
     u16* __restrict__ dk, u16* __restrict__ dv, u16* __restrict__ dsw, int nbt, int B, int T,
-    int H, float c_log2, float scale, int win) {
+    int H, int Hk, float c_log2, float scale, int win) {
   // NBUF query tiles (q and dout, swizzled, see tile_swz) and their lse, delta rows
   __shared__ __attribute__((aligned(1024))) char qtiles[NBUF * BUF_B];
   __shared__ __attribute__((aligned(1024))) char kstage[2 * TILE_B];  // K rows of an item
@@ -241,50 +244,61 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(
   const int half = lane >> 5;
   const int l32 = lane & 31;
 
-  const int BH = B * H;
+  const int G = H / Hk;
   const int n_ktiles = (T + KT_KEYS - 1) / KT_KEYS;
-  const int n_items = BH * n_ktiles;
+  const int n_items = B * Hk * n_ktiles;
   const int n_qt = (T + QT_ROWS - 1) / QT_ROWS;
-  const int rs = H * D;  // 32-bit row offsets within one (b, h) slice
-  const uint32_t rsb = static_cast<uint32_t>(rs) * 2;  // bytes between rows
-  const uint32_t dvoff = tile_copy_offset(wave, lane, rsb);
+  // 32-bit row offsets within one batch (T * H * D < 2^31 is checked on the host)
+  const int rs = H * D;    // q, dout rows
+  const int rsk = Hk * D;  // k, v, dk, dv rows
+  const uint32_t rsb = static_cast<uint32_t>(rs) * 2;    // bytes between rows
+  const uint32_t rsbk = static_cast<uint32_t>(rsk) * 2;
+  const uint32_t qoff = tile_copy_offset(wave, lane, rsb);
+  const uint32_t koff = tile_copy_offset(wave, lane, rsbk);
   const TileOffsets ofs = tile_operand_offsets(lane);
   const uint32_t qt_lds = lds_addr(qtiles);
   const uint32_t lsd_lds = lds_addr(&lsd[0][0][0]);
   const uint32_t kst_lds = lds_addr(kstage);
   const uint32_t est_lds = lds_addr(&estage[wave][0]);
 
-  // A work item: the 128-key tile k0 / 128 of head bh (xcd_tile_map_grouped
-  // order, key tile 0, the one with the most work, first), whose keys are
-  // seen by the query tiles qt0 .. qte - 1.
+  // A work item: the 128-key tile k0 / 128 of key/value head hk of batch b
+  // (xcd_tile_map_grouped order, key tile 0, the one with the most work,
+  // first), whose keys are seen by the query tiles qt0 .. qte - 1 of each of
+  // the G query heads hk G .. hk G + G - 1: N = G (qte - qt0) query tiles,
+  // position n = g (qte - qt0) + (t - qt0) for query head hk G + g, tile t.
   struct Item {
-    int bh, k0, qt0, qte;
-    size_t base;
+    int b, hk, k0, qt0, qte, N;
+    size_t kbase;
   };
   auto item_at = [&](int r, Item& it) -> bool {
     const int vb = persistent_item(r);
     if (vb >= n_items) return false;
-    int bh, kt;
-    xcd_tile_map_grouped(vb, BH, n_ktiles, kHeadGroup, bh, kt);
-    it.bh = bh;
+    int bhk, kt;
+    xcd_tile_map_grouped(vb, B * Hk, n_ktiles, kHeadGroup, bhk, kt);
+    it.b = bhk / Hk;
+    it.hk = bhk % Hk;
     it.k0 = kt * KT_KEYS;
     it.qt0 = it.k0 / QT_ROWS;
     it.qte = WIN ? min(n_qt, (it.k0 + KT_KEYS - 1 + win) / QT_ROWS + 1) : n_qt;
-    it.base = static_cast<size_t>(bh / H) * T * rs + static_cast<size_t>(bh % H) * D;
+    it.N = G * (it.qte - it.qt0);
+    it.kbase = static_cast<size_t>(it.b) * T * rsk + static_cast<size_t>(it.hk) * D;
     return true;
   };
 
-  // Query tile qt of item it -> buffer u (see copy_tile); wavefronts 0 and 1
-  // also copy its lse and delta rows.  Rows past T are past the end of the
-  // buffer range and arrive as zeros: a zero query row with zero dout, lse and
-  // delta adds nothing to dK or dV.
-  auto issue = [&](const Item& it, int qt, int u) {
-    const int q0 = qt * QT_ROWS;
+  // Query tile at position n of item it -> buffer u (see copy_tile);
+  // wavefronts 0 and 1 also copy its lse and delta rows.  Rows past T are past
+  // the end of the buffer range and arrive as zeros: a zero query row with
+  // zero dout, lse and delta adds nothing to dK or dV.
+  auto issue = [&](const Item& it, int n, int u) {
+    const int nt = it.qte - it.qt0;
+    const int h = it.hk * G + n / nt;
+    const int q0 = (it.qt0 + n % nt) * QT_ROWS;
     const uint32_t nrec = static_cast<uint32_t>(T - q0) * rsb;
-    const size_t off = it.base + static_cast<size_t>(q0) * rs;
-    copy_tile(buffer_rsrc(q + off, nrec), dvoff, rsb, qt_lds + u * BUF_B, wave);
-    copy_tile(buffer_rsrc(dout + off, nrec), dvoff, rsb, qt_lds + u * BUF_B + TILE_B, wave);
-    const size_t row0 = static_cast<size_t>(it.bh) * T + q0;
+    const size_t off = static_cast<size_t>(it.b) * T * rs + static_cast<size_t>(h) * D +
+                       static_cast<size_t>(q0) * rs;
+    copy_tile(buffer_rsrc(q + off, nrec), qoff, rsb, qt_lds + u * BUF_B, wave);
+    copy_tile(buffer_rsrc(dout + off, nrec), qoff, rsb, qt_lds + u * BUF_B + TILE_B, wave);
+    const size_t row0 = (static_cast<size_t>(it.b) * H + h) * T + q0;
     if (wave == 0)
       dma4(buffer_rsrc(lse + row0, static_cast<uint32_t>(T - q0) * 4), 4 * lane,
            lsd_lds + u * 512);
@@ -298,11 +312,11 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(
   // real query's dS.
   auto copy_rows = [&](const Item& it, const u16* src, uint32_t dst) {
     const int nk = T - it.k0;  // >= 1
-    const uint32_t n0 = static_cast<uint32_t>(min(nk, 64)) * rsb;
-    const uint32_t n1 = static_cast<uint32_t>(max(nk - 64, 0)) * rsb;
-    const size_t off0 = it.base + static_cast<size_t>(it.k0) * rs;
-    copy_tile(buffer_rsrc(src + off0, n0), dvoff, rsb, dst, wave);
-    copy_tile(buffer_rsrc(src + off0 + static_cast<size_t>(64) * rs, n1), dvoff, rsb,
+    const uint32_t n0 = static_cast<uint32_t>(min(nk, 64)) * rsbk;
+    const uint32_t n1 = static_cast<uint32_t>(max(nk - 64, 0)) * rsbk;
+    const size_t off0 = it.kbase + static_cast<size_t>(it.k0) * rsk;
+    copy_tile(buffer_rsrc(src + off0, n0), koff, rsbk, dst, wave);
+    copy_tile(buffer_rsrc(src + off0 + static_cast<size_t>(64) * rsk, n1), koff, rsbk,
               dst + TILE_B, wave);
   };
   // Every copy issued so far has landed and every wavefront is past its
@@ -313,35 +327,35 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(
   };
 
   // The query tiles of the items form one stream through the NBUF buffers:
-  // the item whose first tile sits in buffer gb has tile qt0 + i in buffer
-  // (gb + i) % NBUF, and the next item's first tiles follow on.  The copies
-  // of the next item's K rows, of its first two query tiles and (once the last
-  // tile is done) of its V rows overlap the end of the current item, so only
-  // the register reads of K and V remain between two items.
+  // the item whose first tile sits in buffer gb has the tile at position n in
+  // buffer (gb + n) % NBUF, and the next item's first tiles follow on.  The
+  // copies of the next item's K rows, of its first two query tiles and (once
+  // the last tile is done) of its V rows overlap the end of the current item,
+  // so only the register reads of K and V remain between two items.
   Item cur, nxt;
   if (!item_at(0, cur)) return;
   bool has_next = item_at(1, nxt);
   int gb = 0;
   copy_rows(cur, k, kst_lds);
   copy_rows(cur, v, qt_lds + 2 * BUF_B);
-  issue(cur, cur.qt0, 0);
-  if (cur.qt0 + 1 < cur.qte) issue(cur, cur.qt0 + 1, 1);
+  issue(cur, 0, 0);
+  if (1 < cur.N) issue(cur, 1, 1);
   sync_tiles();
 
   for (int r = 0;; ++r) {
-    // K rows in kstage, V rows in buffer (gb + 2) % NBUF, query tiles qt0 and
-    // qt0 + 1 in buffers gb, gb + 1: all landed.
+    // K rows in kstage, V rows in buffer (gb + 2) % NBUF, the tiles at
+    // positions 0 and 1 in buffers gb, gb + 1: all landed.
     const int qt0 = cur.qt0;
     const int qte = cur.qte;
-    const int nt = qte - qt0;  // query tiles of this item
+    const int nt = qte - qt0;  // query tiles of this item per query head
+    const int N = cur.N;
     const int kw0 = cur.k0 + 32 * wave;
-    const size_t base = cur.base;
-    const int bh = cur.bh;
+    const size_t kbase = cur.kbase;
     const int ub2 = gb == 0 ? 2 : gb - 1;  // (gb + 2) % NBUF
     // The lse rows are used as -lse log2(e), the exponent offset of P in the
     // exp2 domain: the wavefront that first sees a tile's rows land rewrites
     // them in place (the next barrier publishes them).
-    if (wave < 2 && wave < nt) to_exp2_offset(lsd[(gb + wave) % NBUF][0], lane);
+    if (wave < 2 && wave < N) to_exp2_offset(lsd[(gb + wave) % NBUF][0], lane);
     // K^T and V^T operands: lane holds row kw0 + l32, elements 16 kc + 8 half
     // + 0..7, read from the rows staged with 16 lanes per row.
     const int krow = kw0 + l32;
@@ -357,7 +371,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(
       }
     }
     __syncthreads();  // kstage and buffer (gb + 2) % NBUF are free again
-    if (qt0 + 2 < qte) issue(cur, qt0 + 2, ub2);
+    if (2 < N) issue(cur, 2, ub2);
     int nx = 0;              // leading query tiles of the next item issued
     bool k_next = false;     // next item's K rows issued
 
@@ -368,52 +382,57 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(
       dva[i] = f32x16{};
     }
 
-    // dS blocks of this wavefront's 32 keys (when a dS workspace is given).
-    // Only blocks with a query row < T exist in the packed layout; a block
-    // made of padding rows only (the tail of the last tile) is not stored.
-    // Stored blocks always have kblk <= qblk.
+    // dS blocks of this wavefront's 32 keys for query head h (when a dS
+    // workspace is given).  Only blocks with a query row < T exist in the
+    // packed layout; a block made of padding rows only (the tail of the last
+    // tile) is not stored.  Stored blocks always have kblk <= qblk.
     const int kblk = kw0 / 32;
-    auto ds_of = [&](int qblk) -> u16* {
-      return (dsw && 32 * qblk < T) ? dsw + ds_block_index(bh, nbt, qblk, kblk) : nullptr;
+    auto ds_of = [&](int h, int qblk) -> u16* {
+      return (dsw && 32 * qblk < T)
+                 ? dsw + ds_block_index(cur.b * H + h, nbt, qblk, kblk)
+                 : nullptr;
     };
 
     // One software pipeline over the 32-query blocks from the diagonal on:
     // the step for block j computes the probabilities of j, the scores of j+1
-    // and the dK/dV update of j.  This wavefront's first block is its diagonal
-    // block bw (masked); blocks before it hold no visible (query, key) pair
-    // and are skipped, and the slot of block bw - 1 computes bw's scores.  Tile
-    // t holds blocks 2t, 2t+1; block 2t+1's step reads the scores of block
-    // 2t+2 from tile t+1.  At the sync before tile t (t > qt0) tile t+1 has
-    // landed and tile t-1's buffer is free for the copy of stream position
-    // t+2.  After the last tile the second step still computes scores of a
-    // block past the end (from whatever the next buffer holds); they are never
-    // used.
+    // and the dK/dV update of j.  This wavefront's first block of each query
+    // head is its diagonal block bw (masked); blocks before it hold no visible
+    // (query, key) pair and are skipped, and the slot of block bw - 1 computes
+    // bw's scores.  Tile t holds blocks 2t, 2t+1; block 2t+1's step reads the
+    // scores of the next block from the tile at the next position (the next
+    // query head's first tile after a head's last one, whose scores are the
+    // ones its diagonal block needs).  At the sync before position n (n > 0)
+    // position n+1 has landed and position n-1's buffer is free for the copy
+    // of position n+2.  After the last position the second step still
+    // computes scores of a block past the end (from whatever the next buffer
+    // holds); they are never used.
     const int bw = kw0 / 32;
     f32x16 s0, p0, s1, p1;  // scores of even blocks in s0/p0, of odd blocks in s1/p1
-    uint32_t nc[8];         // row-read addresses of tile t
+    uint32_t nc[8];         // row-read addresses of the current tile
     nat_addr(qt_lds + gb * BUF_B, ofs, nc);
     if (bw == 2 * qt0) dkdv_scores(nc, 0, kreg, vreg, s0, p0);
-    int u = gb;  // buffer of tile t
-    // The first two tiles (every diagonal block of the workgroup) take the
-    // per-wavefront branches; the rest run one branch-free body.
-    auto tile = [&](int t, auto steady) {
+    int u = gb;  // buffer of the current position
+    // The first two tiles of each query head (every diagonal block of the
+    // workgroup) take the per-wavefront branches; the rest run one branch-free
+    // body.
+    auto tile = [&](int h, int n, int t, auto steady) {
       constexpr bool STEADY = decltype(steady)::value;
-      const int un = u == NBUF - 1 ? 0 : u + 1;  // buffer of tile t + 1
-      if (t > qt0) {
+      const int un = u == NBUF - 1 ? 0 : u + 1;  // buffer of position n + 1
+      if (n > 0) {
         sync_tiles();
         const int u2 = un == NBUF - 1 ? 0 : un + 1;
-        const int pos = t + 2;
-        if (pos < qte) {
+        const int pos = n + 2;
+        if (pos < N) {
           issue(cur, pos, u2);
-        } else if (has_next && pos - qte == nx && nx < 2 && nxt.qt0 + nx < nxt.qte) {
-          issue(nxt, nxt.qt0 + nx, u2);  // the next item's tile nx, in stream order
+        } else if (has_next && pos - N == nx && nx < 2 && nx < nxt.N) {
+          issue(nxt, nx, u2);  // the next item's position nx, in stream order
           ++nx;
         }
-        if (t == qte - 1 && has_next) {
+        if (n == N - 1 && has_next) {
           copy_rows(nxt, k, kst_lds);
           k_next = true;
         }
-        if (t + 1 < qte && wave == 3) to_exp2_offset(lsd[un][0], lane);  // tile t+1
+        if (n + 1 < N && wave == 3) to_exp2_offset(lsd[un][0], lane);  // position n+1
       }
       uint32_t tc[4][2], nn[8];
       tr_addr(qt_lds + u * BUF_B, ofs, tc);
@@ -427,27 +446,27 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(
       if (STEADY || j0 > bw) {
         if (WIN && edge)
           dkdv_step<true, true>(nc, 32, lsd[u][0], lsd[u][1], tc, 0, kreg, vreg, s0, p0, s1, p1,
-                                dka, dva, lane, c_log2, kq, ds_of(j0), win);
+                                dka, dva, lane, c_log2, kq, ds_of(h, j0), win);
         else
           dkdv_step<false>(nc, 32, lsd[u][0], lsd[u][1], tc, 0, kreg, vreg, s0, p0, s1, p1, dka,
-                           dva, lane, c_log2, kq, ds_of(j0));
+                           dva, lane, c_log2, kq, ds_of(h, j0));
       } else if (j0 == bw) {
         dkdv_step<true, WIN>(nc, 32, lsd[u][0], lsd[u][1], tc, 0, kreg, vreg, s0, p0, s1, p1,
-                             dka, dva, lane, c_log2, kq, ds_of(j0), win);
+                             dka, dva, lane, c_log2, kq, ds_of(h, j0), win);
       } else if (j0 == bw - 1) {
         dkdv_scores(nc, 32, kreg, vreg, s1, p1);
       }
-      // block j1 (rows 32..63 of tile t), scores of tile t+1 rows 0..31
+      // block j1 (rows 32..63 of tile t), scores of the next position's rows 0..31
       if (STEADY || j1 > bw) {
         if (WIN && edge)
           dkdv_step<true, true>(nn, 0, lsd[u][0], lsd[u][1], tc, 32, kreg, vreg, s1, p1, s0, p0,
-                                dka, dva, lane, c_log2, kq, ds_of(j1), win);
+                                dka, dva, lane, c_log2, kq, ds_of(h, j1), win);
         else
           dkdv_step<false>(nn, 0, lsd[u][0], lsd[u][1], tc, 32, kreg, vreg, s1, p1, s0, p0, dka,
-                           dva, lane, c_log2, kq, ds_of(j1));
+                           dva, lane, c_log2, kq, ds_of(h, j1));
       } else if (j1 == bw) {
         dkdv_step<true, WIN>(nn, 0, lsd[u][0], lsd[u][1], tc, 32, kreg, vreg, s1, p1, s0, p0,
-                             dka, dva, lane, c_log2, kq, ds_of(j1), win);
+                             dka, dva, lane, c_log2, kq, ds_of(h, j1), win);
       } else if (j1 == bw - 1) {
         dkdv_scores(nn, 0, kreg, vreg, s0, p0);
       }
@@ -456,19 +475,23 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(
       u = un;
     };
     const int t_diag_end = min(qt0 + 2, qte);
-    for (int t = qt0; t < t_diag_end; ++t) tile(t, std::false_type{});
-    for (int t = t_diag_end; t < qte; ++t) tile(t, std::true_type{});
+    for (int g = 0; g < G; ++g) {
+      const int h = cur.hk * G + g;
+      const int n0 = g * nt - qt0;  // position of tile t: n0 + t
+      for (int t = qt0; t < t_diag_end; ++t) tile(h, n0 + t, t, std::false_type{});
+      for (int t = t_diag_end; t < qte; ++t) tile(h, n0 + t, t, std::true_type{});
+    }
 
     // Every wavefront is done with the last tile's buffer: the next item's V
     // rows go there, and whatever the stream has not copied yet of its K rows
     // and first two query tiles follows.
     __syncthreads();
-    const int ulast = (gb + nt - 1) % NBUF;
+    const int ulast = (gb + N - 1) % NBUF;
     if (has_next) {
       if (!k_next) copy_rows(nxt, k, kst_lds);
       copy_rows(nxt, v, qt_lds + ulast * BUF_B);
       for (int j = nx; j < 2; ++j)
-        if (nxt.qt0 + j < nxt.qte) issue(nxt, nxt.qt0 + j, (gb + nt + j) % NBUF);
+        if (j < nxt.N) issue(nxt, j, (gb + N + j) % NBUF);
     }
 
     // dka[db], dva[db] (dK^T, dV^T blocks) element r: key kw0 + l32,
@@ -503,14 +526,14 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(
           const int rr = 4 * m + (lane >> 4), c = lane & 15;
           const uint4 x = lds_ld16(est_lds + rr * 256 + 16 * (c ^ rr));
           const int key = kw0 + 16 * sh + rr;
-          if (key < T) st16(dst + base + key * rs + 8 * c, x);
+          if (key < T) st16(dst + kbase + key * rsk + 8 * c, x);
         }
       }
     }
 
     if (!has_next) break;
     sync_tiles();  // the next item's K, V rows and first query tiles have landed
-    gb = (gb + nt) % NBUF;
+    gb = (gb + N) % NBUF;
     cur = nxt;
     has_next = item_at(r + 2, nxt);
   }
@@ -622,7 +645,7 @@ __device__ __forceinline__ void dq_step(const u16* KsN, const u16* VsN, int rowN
 __global__ __launch_bounds__(256, 1) void dq_kernel(
     const u16* __restrict__ q, const u16* __restrict__ k, const u16* __restrict__ v,
     const u16* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
-    u16* __restrict__ dq, int B, int T, int H, float c_log2, float scale) {
+    u16* __restrict__ dq, int B, int T, int H, int Hk, float c_log2, float scale) {
   __shared__ __attribute__((aligned(16))) u16 Ks[2][DQ_KEYS * RS];
   __shared__ __attribute__((aligned(16))) u16 Vs[2][DQ_KEYS * RS];
   __shared__ __attribute__((aligned(16))) u16 Kt[2][D * DQ_KEYS];  // transposed, swizzled
@@ -633,16 +656,20 @@ __global__ __launch_bounds__(256, 1) void dq_kernel(
   const int half = lane >> 5;
   const int l32 = lane & 31;
 
-  const int BH = B * H;
+  const int G = H / Hk;  // query heads per key/value head, grouped on one XCD
   const int n_qt = (T + DQ_ROWS - 1) / DQ_ROWS;
-  int bh, t;
-  xcd_tile_map_grouped(static_cast<int>(blockIdx.x), BH, n_qt, kHeadGroup, bh, t);
-  const int qt = n_qt - 1 - t;  // heaviest (last) query tile first
-  const int b = bh / H, h = bh % H;
+  int bhk, tg;
+  xcd_tile_map_grouped(static_cast<int>(blockIdx.x), B * Hk, n_qt * G, kHeadGroup, bhk, tg);
+  const int qt = n_qt - 1 - tg / G;  // heaviest (last) query tile first
+  const int b = bhk / Hk, hk = bhk % Hk;
+  const int h = hk * G + tg % G;
+  const int bh = b * H + h;
   const int q0 = qt * DQ_ROWS;
   const int qw0 = q0 + 32 * wave;
-  const int rs = H * D;  // 32-bit row offsets within one (b, h) slice
+  const int rs = H * D;    // 32-bit row offsets within one batch: q, dout, dq
+  const int rsk = Hk * D;  // k, v
   const size_t base = static_cast<size_t>(b) * T * rs + static_cast<size_t>(h) * D;
+  const size_t kbase = static_cast<size_t>(b) * T * rsk + static_cast<size_t>(hk) * D;
 
   // rows past T read row T-1 (their dq is never stored)
   const int qrow = qw0 + l32;
@@ -673,7 +700,7 @@ __global__ __launch_bounds__(256, 1) void dq_kernel(
     const int k0 = kt * DQ_KEYS;  // rows clamp to T-1
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const size_t off = base + min(k0 + 4 * lrow + i, T - 1) * rs + 8 * lchunk;
+      const size_t off = kbase + min(k0 + 4 * lrow + i, T - 1) * rsk + 8 * lchunk;
       xk[i] = ld16(k + off);
       xv[i] = ld16(v + off);
     }
@@ -783,7 +810,8 @@ template <bool WIN>
 __global__ __launch_bounds__(256, 2) void dq_gemm_kernel(const u16* __restrict__ k,
                                                          const u16* __restrict__ dsw,
                                                          u16* __restrict__ dq, int nbt, int B,
-                                                         int T, int H, float scale, int win) {
+                                                         int T, int H, int Hk, float scale,
+                                                         int win) {
   __shared__ __attribute__((aligned(1024))) char ktile[2][kTileBytes];   // swizzled K
   __shared__ __attribute__((aligned(1024))) char sst[3][4][DG_DS_B];     // dS blocks per wave
 
@@ -795,26 +823,30 @@ __global__ __launch_bounds__(256, 2) void dq_gemm_kernel(const u16* __restrict__
   const int gi = lane >> 4;   // 16-lane group
   const int i16 = lane & 15;
 
-  const int BH = B * H;
+  const int G = H / Hk;  // query heads per key/value head, grouped on one XCD
   const int n_qt = (T + DG_ROWS - 1) / DG_ROWS;
-  const int n_items = BH * n_qt;
+  const int n_items = B * H * n_qt;
   for (int r = 0;; ++r) {
     const int item = persistent_item(r);
     if (item >= n_items) break;
     // every wavefront is done with the previous item's LDS tiles
     if (r > 0) __syncthreads();
-    int bh, t;
+    int bhk, tg;
     // heads last-first: the dK/dV pass stored their dS last, so part of it
     // may still sit in the last-level cache
-    xcd_tile_map_grouped(item, BH, n_qt, kHeadGroup, bh, t, true);
-    const int qt = n_qt - 1 - t;  // heaviest (last) query tile first
-    const int b = bh / H, h = bh % H;
+    xcd_tile_map_grouped(item, B * Hk, n_qt * G, kHeadGroup, bhk, tg, true);
+    const int qt = n_qt - 1 - tg / G;  // heaviest (last) query tile first
+    const int b = bhk / Hk, hk = bhk % Hk;
+    const int h = hk * G + tg % G;
+    const int bh = b * H + h;
     const int q0 = qt * DG_ROWS;
     const int qw0 = q0 + 32 * wave;
     const int qblk = qw0 / 32;
     const bool live = qw0 < T;  // wavefront has at least one real query row
-    const int rs = H * D;
+    const int rs = H * D;    // dq rows
+    const int rsk = Hk * D;  // k rows
     const size_t base = static_cast<size_t>(b) * T * rs + static_cast<size_t>(h) * D;
+    const size_t kbase = static_cast<size_t>(b) * T * rsk + static_cast<size_t>(hk) * D;
     // this wavefront's row of dS blocks: (qblk, 0 .. qblk), 2 KiB each, contiguous
     const u16* dsrow = dsw + ds_block_index(bh, nbt, qblk, 0);
 
@@ -838,7 +870,7 @@ __global__ __launch_bounds__(256, 2) void dq_gemm_kernel(const u16* __restrict__
     const uint32_t st_lds = lds_addr(&sst[0][wave][0]);
     const uint32_t st_off =
         ((8 * half + (i16 >> 2)) * 32 + 16 * (gi & 1) + 4 * (i16 & 3)) * 2;
-    const uint32_t rsb = static_cast<uint32_t>(rs) * 2;
+    const uint32_t rsb = static_cast<uint32_t>(rsk) * 2;
     const uint32_t kvoff = tile_copy_offset(wave, lane, rsb);
     const uint32_t kt_lds = lds_addr(ktile);
     // the wavefront's blocks of key tile kt: kblk = 2 kt, 2 kt + 1 (if <= qblk)
@@ -851,7 +883,7 @@ __global__ __launch_bounds__(256, 2) void dq_gemm_kernel(const u16* __restrict__
     auto issue_k = [&](int kt, int buf, int j) {
       const int k0 = kt * DG_KEYS;
       const uint32_t nrec = static_cast<uint32_t>(T - k0) * rsb;  // keys past T read as 0
-      dma16(buffer_rsrc(k + base + static_cast<size_t>(k0) * rs, nrec), kvoff + 16 * j * rsb,
+      dma16(buffer_rsrc(k + kbase + static_cast<size_t>(k0) * rsk, nrec), kvoff + 16 * j * rsb,
             kt_lds + buf * kTileBytes + 1024 * wave + 4096 * j);
     };
     auto issue_ds = [&](int kt, int sbuf, int j) {
@@ -950,7 +982,7 @@ std::size_t bwd_workspace_bytes(int B, int T, int H) {
 
 hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const void* o,
                            const void* dout, const float* lse, void* dq, void* dk, void* dv,
-                           float* delta, void* ws, int B, int T, int H, int window,
+                           float* delta, void* ws, int B, int T, int H, int Hk, int window,
                            hipStream_t s, hipEvent_t const* ev) {
   const float scale = 1.0f / sqrtf(static_cast<float>(D));
   const float c_log2 = scale * kLog2e;
@@ -969,26 +1001,27 @@ hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const vo
   if (e != hipSuccess) return e;
   if ((e = mark(ev, 1, s)) != hipSuccess) return e;
   const int n_kt = (T + KT_KEYS - 1) / KT_KEYS;
-  const dim3 kv_grid(persistent_grid(static_cast<long>(n_kt) * B * H, 1));
+  const dim3 kv_grid(persistent_grid(static_cast<long>(n_kt) * B * Hk, 1));
   // a window that covers every key of every row is the plain causal case
   const bool win = window >= 0 && window < T - 1;
   const int w = win ? window : T;
   e = launch(win ? dkdv_kernel<true> : dkdv_kernel<false>, kv_grid, dim3(256), 0, s, q16, k16,
              v16, g16, lse, static_cast<const float*>(delta), static_cast<u16*>(dk),
-             static_cast<u16*>(dv), dsw, nbt, B, T, H, c_log2, scale, w);
+             static_cast<u16*>(dv), dsw, nbt, B, T, H, Hk, c_log2, scale, w);
   if (e != hipSuccess) return e;
   if ((e = mark(ev, 2, s)) != hipSuccess) return e;
   if (dsw != nullptr) {
     const int n_qt = (T + DG_ROWS - 1) / DG_ROWS;
     e = launch(win ? dq_gemm_kernel<true> : dq_gemm_kernel<false>,
                dim3(persistent_grid(static_cast<long>(n_qt) * B * H, 2)), dim3(256), 0, s, k16,
-               static_cast<const u16*>(dsw), static_cast<u16*>(dq), nbt, B, T, H, scale, w);
+               static_cast<const u16*>(dsw), static_cast<u16*>(dq), nbt, B, T, H, Hk, scale,
+               w);
   } else {
     if (win) return hipErrorInvalidValue;  // the recompute pass has no window (checked on the host)
     const int n_qt = (T + DQ_ROWS - 1) / DQ_ROWS;
     e = launch(dq_kernel, dim3(static_cast<unsigned>(n_qt) * B * H), dim3(256), 0, s, q16, k16,
                v16, g16, lse, static_cast<const float*>(delta), static_cast<u16*>(dq), B, T, H,
-               c_log2, scale);
+               Hk, c_log2, scale);
   }
   if (e != hipSuccess) return e;
   return mark(ev, 3, s);

@@ -64,7 +64,7 @@ struct Batch {
 __global__ __launch_bounds__(512) void decode_split_kernel(
     const u16* __restrict__ q, const u16* __restrict__ kc, const u16* __restrict__ vc,
     const int* __restrict__ seqlens, float* __restrict__ opart, float* __restrict__ ml, int B,
-    int H, int T_cap, float scale, int win) {
+    int H, int Hk, int T_cap, float scale, int win) {
   __shared__ int pre[kMaxFlatB + 1];  // pre[b] = non-empty chunks of sequences < b
   const int tid = threadIdx.x;
   const int h = tid >> 4;
@@ -145,12 +145,14 @@ __global__ __launch_bounds__(512) void decode_split_kernel(
     return first_from(t.slot + P);
   };
 
-  const size_t rs = static_cast<size_t>(H) * D;
+  // the cache has Hk key/value heads; query head h reads head h / (H / Hk)
+  const int hk = h / (H / Hk);
+  const size_t rs = static_cast<size_t>(Hk) * D;
   const float c2 = scale * 1.4426950408889634f;  // scores in the exp2 domain
   auto rows = [&](const Batch& t, uint4 (&xk)[U], uint4 (&xv)[U]) {
     const size_t base = (static_cast<size_t>(t.b) * T_cap + t.c * CHUNK) * rs +
-                        static_cast<size_t>(h) * D + 8 * l16;
-    const int rsi = H * D;
+                        static_cast<size_t>(hk) * D + 8 * l16;
+    const int rsi = Hk * D;
     const int r_lo = t.j0 - t.c * CHUNK;  // rows before it lie before the window
 #pragma unroll
     for (int i = 0; i < U; ++i) {
@@ -316,8 +318,8 @@ std::size_t decode_workspace_bytes(int B, int H, int T_cap) {
 }
 
 hipError_t launch_decode_bf16(const void* q, const void* kc, const void* vc, const int* seqlens,
-                              void* o, float* lse, int B, int H, int T_cap, int window,
-                              void* ws, hipStream_t s, hipEvent_t const* ev) {
+                              void* o, float* lse, int B, int H, int Hk, int T_cap,
+                              int window, void* ws, hipStream_t s, hipEvent_t const* ev) {
   const float scale = 1.0f / sqrtf(static_cast<float>(D));
   const int NC = n_chunks(T_cap);
   // a window that covers the whole cache is no window
@@ -334,7 +336,7 @@ hipError_t launch_decode_bf16(const void* q, const void* kc, const void* vc, con
   if (e != hipSuccess) return e;
   e = launch(decode_split_kernel, dim3(P), dim3(16 * H), 0, s, static_cast<const u16*>(q),
              static_cast<const u16*>(kc), static_cast<const u16*>(vc), seqlens, opart, ml, B, H,
-             T_cap, scale, win);
+             Hk, T_cap, scale, win);
   if (e != hipSuccess) return e;
   if ((e = mark(ev, 1, s)) != hipSuccess) return e;
   e = launch(decode_combine_kernel, dim3(H, B), dim3(128), 0, s, static_cast<const float*>(opart),

@@ -54,8 +54,8 @@ constexpr float kRescaleLog2 = 8.0f;
 template <bool WIN>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(
     const u16* __restrict__ q, const u16* __restrict__ k, const u16* __restrict__ v,
-    u16* __restrict__ o, float* __restrict__ lse, int B, int T, int H, float c_log2, float scale,
-    int win) {
+    u16* __restrict__ o, float* __restrict__ lse, int B, int T, int H, int Hk, float c_log2,
+    float scale, int win) {
   // two buffers of (K tile, V tile), swizzled (see tile_swz)
   __shared__ __attribute__((aligned(1024))) char kvs[2 * BUF_B];
 
@@ -65,17 +65,24 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(
   const int half = lane >> 5;   // which 8-wide k half of an MFMA operand
   const int l32 = lane & 31;
 
-  const int BH = B * H;
   const int n_qt = (T + BQ - 1) / BQ;
-  int bh, t;
-  xcd_tile_map_grouped(static_cast<int>(blockIdx.x), BH, n_qt, kHeadGroup, bh, t);
-  const int qt = n_qt - 1 - t;  // heaviest (last) query tile first
-  const int b = bh / H, h = bh % H;
+  // Items are grouped by key/value head: the G = H / Hk query heads that read
+  // one K, V head run on one XCD next to each other (query head fastest), so
+  // its K and V stay in that XCD's L2.
+  const int G = H / Hk;
+  int bhk, tg;
+  xcd_tile_map_grouped(static_cast<int>(blockIdx.x), B * Hk, n_qt * G, kHeadGroup, bhk, tg);
+  const int qt = n_qt - 1 - tg / G;  // heaviest (last) query tile first
+  const int b = bhk / Hk, hk = bhk % Hk;
+  const int h = hk * G + tg % G;
+  const int bh = b * H + h;
   const int q0 = qt * BQ;
   const int qw0 = q0 + wave * 32;
-  // 32-bit row offsets within one (b, h) slice (T * H * D < 2^31 is checked on the host)
-  const int rs = H * D;  // stride between t
+  // 32-bit row offsets within one batch (T * H * D < 2^31 is checked on the host)
+  const int rs = H * D;    // q, o: stride between t
+  const int rsk = Hk * D;  // k, v
   const size_t base = static_cast<size_t>(b) * T * rs + static_cast<size_t>(h) * D;
+  const size_t kbase = static_cast<size_t>(b) * T * rsk + static_cast<size_t>(hk) * D;
 
   // Q^T operand: lane holds q[qw0 + l32][16 kc + 8 half + 0..7], kc = 0..7.
   // Rows past T (their outputs are discarded) read row T-1 instead.
@@ -107,12 +114,12 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(
     nat_addr(kv_lds, ofs, ta.nat);
     tr_addr(kv_lds + kTileBytes, ofs, ta.tr);
   }
-  const uint32_t rsb = static_cast<uint32_t>(rs) * 2;
+  const uint32_t rsb = static_cast<uint32_t>(rsk) * 2;
   const uint32_t cvoff = tile_copy_offset(wave, lane, rsb);
   auto issue = [&](int kt, int buf) {  // K, V tile kt -> buffer buf; keys past T read as 0
     const int k0 = kt * BK;
     const uint32_t nrec = static_cast<uint32_t>(T - k0) * rsb;
-    const size_t off = base + static_cast<size_t>(k0) * rs;
+    const size_t off = kbase + static_cast<size_t>(k0) * rsk;
     copy_tile<NW>(buffer_rsrc(k + off, nrec), cvoff, rsb, kv_lds + buf * BUF_B, wave);
     copy_tile<NW>(buffer_rsrc(v + off, nrec), cvoff, rsb, kv_lds + buf * BUF_B + kTileBytes,
                   wave);
@@ -253,7 +260,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(
 }  // namespace
 
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
-                           int B, int T, int H, int window, hipStream_t s) {
+                           int B, int T, int H, int Hk, int window, hipStream_t s) {
   const float scale = 1.0f / sqrtf(static_cast<float>(D));
   const float c_log2 = scale * 1.4426950408889634f;
   const int n_qt = (T + BQ - 1) / BQ;
@@ -261,8 +268,8 @@ hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o,
   const bool win = window >= 0 && window < T - 1;  // else every row sees all its keys
   return launch(win ? fwd_bf16_kernel<true> : fwd_bf16_kernel<false>, grid, dim3(64 * NW), 0, s,
                 static_cast<const u16*>(q), static_cast<const u16*>(k),
-                static_cast<const u16*>(v), static_cast<u16*>(o), lse, B, T, H, c_log2, scale,
-                win ? window : T);
+                static_cast<const u16*>(v), static_cast<u16*>(o), lse, B, T, H, Hk, c_log2,
+                scale, win ? window : T);
 }
 
 }  // namespace na

@@ -16,10 +16,12 @@ constexpr int kHeadDim = 128;
 
 // Sliding windows: window < 0 (or one that covers every earlier key) is plain
 // causal attention; window W >= 0 keeps keys i - W .. i for query i.
+// Hk: key/value heads (H a multiple of Hk; query head h reads head h / (H / Hk)),
+// Hk = H for plain multi-head attention.
 
 // bf16 forward: o, lse from q, k, v.
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
-                           int B, int T, int H, int window, hipStream_t s);
+                           int B, int T, int H, int Hk, int window, hipStream_t s);
 
 // bf16 backward: delta, then dk/dv, then dq.
 // ws: optional dS workspace of bwd_workspace_bytes(B, T, H) bytes; with it dQ
@@ -27,15 +29,15 @@ hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o,
 // (plain causal only: a window needs the workspace).
 hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const void* o,
                            const void* dout, const float* lse, void* dq, void* dk, void* dv,
-                           float* delta, void* ws, int B, int T, int H, int window,
+                           float* delta, void* ws, int B, int T, int H, int Hk, int window,
                            hipStream_t s, hipEvent_t const* ev = nullptr);
 std::size_t bwd_workspace_bytes(int B, int T, int H);
 
 // Decode workspace layout and size (bytes).
 std::size_t decode_workspace_bytes(int B, int H, int T_cap);
 hipError_t launch_decode_bf16(const void* q, const void* kc, const void* vc, const int* seqlens,
-                              void* o, float* lse, int B, int H, int T_cap, int window, void* ws,
-                              hipStream_t s, hipEvent_t const* ev = nullptr);
+                              void* o, float* lse, int B, int H, int Hk, int T_cap, int window,
+                              void* ws, hipStream_t s, hipEvent_t const* ev = nullptr);
 
 // Compute units of the current device (cached per device; 256 if the query
 // fails).  Persistent grids size themselves from it.

@@ -17,7 +17,7 @@
  *   - scores z_ij = s <q_i, k_j> with s = 1/sqrt(D); softmax over keys;
  *   - causal: key j is visible to query i iff j <= i (T_q = T_k, top left);
  *   - n_kv_head = n_head; full causal window (the *_window entry points
- *     below take a sliding window);
+ *     below take a sliding window, the *_gqa ones fewer key/value heads);
  *   - lse_i = ln sum_j exp(z_ij) over visible keys (natural log, fp32);
  *   - bf16 inputs are rounded values; all accumulation is fp32; fp32 -> bf16
  *     conversions round to nearest even.
@@ -162,6 +162,29 @@ na_status na_attn_decode_window(const void* q, const void* k_cache, const void* 
                                 const int* seqlens, void* o, float* lse, int B, int H, int D,
                                 int T_cap, int window, void* workspace, size_t workspace_bytes,
                                 void* stream, void* const* events);
+
+/*
+ * Grouped-query attention (fewer key/value heads than query heads, the
+ * architecture list of the blog's section 1 "GPT model"): k, v, dk, dv (and
+ * the decode caches) have H_kv heads, (B, T, H_kv, D) contiguous; q, o, dout,
+ * dq have H heads; H must be a multiple of H_kv (else NA_ERR_INVALID_ARG), and
+ * query head h reads key/value head h / (H / H_kv).  dk and dv are the sums
+ * over the query heads that read each key/value head.  lse, delta and the
+ * workspaces are per query head, sized as for the plain calls with H.
+ * H_kv == H is plain multi-head attention; `window` as for the *_window
+ * entry points (< 0: none).  bf16 only.
+ */
+na_status na_attn_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
+                          int B, int T, int H, int H_kv, int D, int window, void* stream);
+na_status na_attn_bwd_gqa(const void* q, const void* k, const void* v, const void* o,
+                          const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                          float* delta, void* workspace, size_t workspace_bytes, int B, int T,
+                          int H, int H_kv, int D, int window, void* stream,
+                          void* const* events);
+na_status na_attn_decode_gqa(const void* q, const void* k_cache, const void* v_cache,
+                             const int* seqlens, void* o, float* lse, int B, int H, int H_kv,
+                             int D, int T_cap, int window, void* workspace,
+                             size_t workspace_bytes, void* stream, void* const* events);
 
 /* Static text for a status code. */
 const char* na_status_string(na_status s);

@@ -34,7 +34,8 @@ def test_header_declares_the_entry_points():
     for s in ("na_attn_fwd", "na_attn_bwd", "na_attn_decode", "na_attn_decode_workspace_bytes",
               "na_attn_bwd_workspace_bytes", "na_attn_bwd_timed", "na_attn_decode_timed",
               "na_attn_fwd_f32", "na_attn_bwd_f32", "na_status_string", "na_last_error",
-              "na_attn_fwd_window", "na_attn_bwd_window", "na_attn_decode_window"):
+              "na_attn_fwd_window", "na_attn_bwd_window", "na_attn_decode_window",
+              "na_attn_fwd_gqa", "na_attn_bwd_gqa", "na_attn_decode_gqa"):
         assert s in syms
 
 
@@ -123,6 +124,25 @@ def test_window_entry_points_check_their_arguments(lib):
                                      wneed, None, None) == INVALID
     assert lib.na_attn_decode_window(*d[:6], 4, 2, 128, 64, 5, d[6], wneed - 1, None,
                                      None) == INVALID
+
+
+def test_gqa_entry_points_check_the_head_counts(lib):
+    f = lambda H, Hk: lib.na_attn_fwd_gqa(A, A + 0x100, A + 0x200, A + 0x300, A + 0x400,  # noqa
+                                          1, 8, H, Hk, 128, -1, None)
+    for H, Hk in ((4, 3), (4, 0), (4, 8), (6, -2)):
+        assert f(H, Hk) == INVALID and b"H_kv" in lib.na_last_error()
+    p = [A + 0x100 * i for i in range(11)]
+    need = lib.na_attn_bwd_workspace_bytes(1, 8, 4, 128)
+    assert lib.na_attn_bwd_gqa(*p[:10], p[10], need, 1, 8, 4, 3, 128, -1, None,
+                               None) == INVALID
+    bad = list(p)
+    bad[7] = bad[6]  # dk aliases dq
+    assert lib.na_attn_bwd_gqa(*bad[:10], bad[10], need, 1, 8, 4, 2, 128, -1, None,
+                               None) == INVALID
+    d = [A + 0x100 * i for i in range(7)]
+    wneed = lib.na_attn_decode_workspace_bytes(4, 6, 128, 64)
+    assert lib.na_attn_decode_gqa(*d[:6], 4, 6, 4, 128, 64, -1, d[6], wneed, None,
+                                  None) == INVALID
 
 
 def test_bwd_workspace_bytes(lib):

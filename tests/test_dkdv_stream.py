@@ -6,8 +6,10 @@ current item's last tiles (K into its own staging region, tiles into the
 buffers those tiles free), and its V rows go into the last tile's buffer once
 that tile is done.  Checks that every tile a step reads has landed in the
 buffer it reads, and that no copy targets a buffer still being read, for
-random item sequences, ragged T and sliding windows (an item's query tiles
-then end at the last tile that sees its keys)."""
+random item sequences, ragged T, sliding windows (an item's query tiles
+then end at the last tile that sees its keys) and grouped key/value heads
+(an item's positions run over the G query heads that read its keys, position
+n = g (qte - qt0) + t - qt0)."""
 import random
 
 import pytest
@@ -15,7 +17,7 @@ import pytest
 QT, KT, NB = 64, 128, 3
 
 
-def run_stream(T, items, W=None):
+def run_stream(T, items, W=None, G=1):
     n_qt = (T + QT - 1) // QT
     qt0 = lambda it: items[it] * KT // QT  # noqa: E731
 
@@ -23,6 +25,9 @@ def run_stream(T, items, W=None):
         if W is None:
             return n_qt
         return min(n_qt, (items[it] * KT + KT - 1 + W) // QT + 1)
+
+    def npos(it):  # positions of an item
+        return G * (qte(it) - qt0(it))
 
     buf = [None] * NB
     state = {"k": None}
@@ -44,50 +49,50 @@ def run_stream(T, items, W=None):
     nxt = 1 if len(items) > 1 else None
     issue("k", ("K", cur), set())
     issue(2, ("V", cur), set())
-    issue(0, ("Q", cur, qt0(cur)), set())
-    if qt0(cur) + 1 < qte(cur):
-        issue(1, ("Q", cur, qt0(cur) + 1), set())
+    issue(0, ("Q", cur, 0), set())
+    if 1 < npos(cur):
+        issue(1, ("Q", cur, 1), set())
     land()
     r = 0
     while True:
-        q0, E = qt0(cur), qte(cur)
-        nt = E - q0
+        N = npos(cur)
         ub2 = (gb + 2) % NB
         assert state["k"] == ("K", cur) and buf[ub2] == ("V", cur)
-        assert buf[gb] == ("Q", cur, q0)
-        if nt > 1:
-            assert buf[(gb + 1) % NB] == ("Q", cur, q0 + 1)
-        if q0 + 2 < E:  # after the barrier that frees the V rows' buffer
-            issue(ub2, ("Q", cur, q0 + 2), {gb, (gb + 1) % NB})
+        assert buf[gb] == ("Q", cur, 0)
+        if N > 1:
+            assert buf[(gb + 1) % NB] == ("Q", cur, 1)
+        if 2 < N:  # after the barrier that frees the V rows' buffer
+            issue(ub2, ("Q", cur, 2), {gb, (gb + 1) % NB})
         nx, u = 0, gb
-        for t in range(q0, E):
+        for n in range(N):
             un = (u + 1) % NB
-            if t > q0:
+            if n > 0:
                 land()
-                u2, pos, busy = (un + 1) % NB, t + 2, {u, un}
-                if pos < E:
+                u2, pos, busy = (un + 1) % NB, n + 2, {u, un}
+                if pos < N:
                     issue(u2, ("Q", cur, pos), busy)
-                elif nxt is not None and pos - E == nx and nx < 2 and qt0(nxt) + nx < qte(nxt):
-                    issue(u2, ("Q", nxt, qt0(nxt) + nx), busy)
+                elif nxt is not None and pos - N == nx and nx < 2 and nx < npos(nxt):
+                    issue(u2, ("Q", nxt, nx), busy)
                     nx += 1
-                if t == E - 1 and nxt is not None:
+                if n == N - 1 and nxt is not None:
                     issue("k", ("K", nxt), busy)
-            # a step reads tile t (buffer u) and rows of tile t + 1 (buffer un)
-            assert buf[u] == ("Q", cur, t), (t, u, buf)
-            if t + 1 < E:
-                assert buf[un] == ("Q", cur, t + 1), (t, un, buf)
+            # a step reads position n (buffer u) and rows of position n + 1
+            # (buffer un; across a query-head boundary too)
+            assert buf[u] == ("Q", cur, n), (n, u, buf)
+            if n + 1 < N:
+                assert buf[un] == ("Q", cur, n + 1), (n, un, buf)
             u = un
-        ulast = (gb + nt - 1) % NB  # barrier: the last tile is done
+        ulast = (gb + N - 1) % NB  # barrier: the last tile is done
         if nxt is None:
             break
-        if nt == 1:
+        if N == 1:
             issue("k", ("K", nxt), set())
         issue(ulast, ("V", nxt), set())
         for j in range(nx, 2):
-            if qt0(nxt) + j < qte(nxt):
-                issue((gb + nt + j) % NB, ("Q", nxt, qt0(nxt) + j), set())
+            if j < npos(nxt):
+                issue((gb + N + j) % NB, ("Q", nxt, j), set())
         land()
-        gb, cur, r = (gb + nt) % NB, nxt, r + 1
+        gb, cur, r = (gb + N) % NB, nxt, r + 1
         nxt = r + 1 if r + 1 < len(items) else None
 
 
@@ -99,4 +104,4 @@ def test_stream_buffers(T, W):
     n_kt = (T + KT - 1) // KT
     for _ in range(40):
         items = [rng.randrange(n_kt) for _ in range(rng.randint(1, 12))]
-        run_stream(T, items, W)
+        run_stream(T, items, W, G=rng.choice([1, 1, 2, 3, 5]))
