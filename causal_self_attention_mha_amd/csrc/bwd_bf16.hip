@@ -223,10 +223,11 @@ __device__ __forceinline__ void to_exp2_offset(float* rows, int lane) {
 }
 
 // WIN: sliding window, key j visible to query i iff i - win <= j <= i.
-// Hk key/value heads (H a multiple of Hk): a work item holds the keys of one
-// key/value head, and its query tiles run over the G = H / Hk query heads that
-// read it, so that dK and dV sum the group in registers.
-template <bool WIN>
+// GRP: Hk key/value heads (H a multiple of Hk): a work item holds the keys of
+// one key/value head, and its query tiles run over the G = H / Hk query heads
+// that read it, so that dK and dV sum the group in registers (GRP = false:
+// Hk = H, G = 1, and the head bookkeeping compiles away).
+template <bool WIN, bool GRP>
 __global__ __launch_bounds__(256, 1) void dkdv_kernel(
     const u16* __restrict__ q, const u16* __restrict__ k, const u16* __restrict__ v,
     const u16* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
@@ -244,7 +245,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(
   const int half = lane >> 5;
   const int l32 = lane & 31;
 
-  const int G = H / Hk;
+  const int G = GRP ? H / Hk : 1;
   const int n_ktiles = (T + KT_KEYS - 1) / KT_KEYS;
   const int n_items = B * Hk * n_ktiles;
   const int n_qt = (T + QT_ROWS - 1) / QT_ROWS;
@@ -268,7 +269,8 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(
   // position n = g (qte - qt0) + (t - qt0) for query head hk G + g, tile t.
   struct Item {
     int b, hk, k0, qt0, qte, N;
-    size_t kbase;
+    size_t kbase, qbase;  // k/v rows of head hk, q/dout rows of head hk G
+    size_t lbase;         // lse/delta row of head hk G
   };
   auto item_at = [&](int r, Item& it) -> bool {
     const int vb = persistent_item(r);
@@ -282,29 +284,39 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(
     it.qte = WIN ? min(n_qt, (it.k0 + KT_KEYS - 1 + win) / QT_ROWS + 1) : n_qt;
     it.N = G * (it.qte - it.qt0);
     it.kbase = static_cast<size_t>(it.b) * T * rsk + static_cast<size_t>(it.hk) * D;
+    it.qbase = static_cast<size_t>(it.b) * T * rs + static_cast<size_t>(it.hk) * G * D;
+    it.lbase = (static_cast<size_t>(it.b) * H + static_cast<size_t>(it.hk) * G) * T;
     return true;
   };
 
-  // Query tile at position n of item it -> buffer u (see copy_tile);
-  // wavefronts 0 and 1 also copy its lse and delta rows.  Rows past T are past
-  // the end of the buffer range and arrive as zeros: a zero query row with
-  // zero dout, lse and delta adds nothing to dK or dV.
-  auto issue = [&](const Item& it, int n, int u) {
-    const int nt = it.qte - it.qt0;
-    const int h = it.hk * G + n / nt;
-    const int q0 = (it.qt0 + n % nt) * QT_ROWS;
+  // Query tile qt of query head h (of item it's batch) -> buffer u (see
+  // copy_tile); wavefronts 0 and 1 also copy its lse and delta rows.  Rows
+  // past T are past the end of the buffer range and arrive as zeros: a zero
+  // query row with zero dout, lse and delta adds nothing to dK or dV.
+  // qh, lh: offsets of the query head's row 0 in q / dout and in lse / delta.
+  auto issue_at = [&](size_t qh, size_t lh, int qt, int u) {
+    const int q0 = qt * QT_ROWS;
     const uint32_t nrec = static_cast<uint32_t>(T - q0) * rsb;
-    const size_t off = static_cast<size_t>(it.b) * T * rs + static_cast<size_t>(h) * D +
-                       static_cast<size_t>(q0) * rs;
+    const size_t off = qh + static_cast<size_t>(q0 * rs);
     copy_tile(buffer_rsrc(q + off, nrec), qoff, rsb, qt_lds + u * BUF_B, wave);
     copy_tile(buffer_rsrc(dout + off, nrec), qoff, rsb, qt_lds + u * BUF_B + TILE_B, wave);
-    const size_t row0 = (static_cast<size_t>(it.b) * H + h) * T + q0;
+    const size_t row0 = lh + static_cast<size_t>(q0);
     if (wave == 0)
       dma4(buffer_rsrc(lse + row0, static_cast<uint32_t>(T - q0) * 4), 4 * lane,
            lsd_lds + u * 512);
     if (wave == 1)
       dma4(buffer_rsrc(delta + row0, static_cast<uint32_t>(T - q0) * 4), 4 * lane,
            lsd_lds + u * 512 + 256);
+  };
+  auto issue_tile = [&](const Item& it, int g, int qt, int u) {  // query head hk G + g
+    issue_at(it.qbase + static_cast<size_t>(g * D), it.lbase + static_cast<size_t>(g * T), qt,
+             u);
+  };
+  // The tile at position n of item it -> buffer u (n < it.N; a division, so
+  // only outside the steady loop).
+  auto issue = [&](const Item& it, int n, int u) {
+    const int nt = it.qte - it.qt0;
+    issue_tile(it, n / nt, it.qt0 + n % nt, u);
   };
   // The 128 K (or V) rows of item it -> LDS at dst (two swizzled 64-row tiles).
   // Keys past T arrive as zeros: their gradients are never stored and, since
@@ -415,7 +427,8 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(
     // The first two tiles of each query head (every diagonal block of the
     // workgroup) take the per-wavefront branches; the rest run one branch-free
     // body.
-    auto tile = [&](int h, int n, int t, auto steady) {
+    auto tile = [&](int g, size_t qh, size_t lh, int n, int t, auto steady) {
+      const int h = cur.hk * G + g;  // query head; qh, lh: its row-0 offsets
       constexpr bool STEADY = decltype(steady)::value;
       const int un = u == NBUF - 1 ? 0 : u + 1;  // buffer of position n + 1
       if (n > 0) {
@@ -423,7 +436,15 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(
         const int u2 = un == NBUF - 1 ? 0 : un + 1;
         const int pos = n + 2;
         if (pos < N) {
-          issue(cur, pos, u2);
+          // position n + 2: tile t + 2 of query head g, else of a later head
+          // (two heads on when a head has a single tile); no division
+          if (!GRP || t + 2 < qte) {
+            issue_at(qh, lh, t + 2, u2);
+          } else {
+            int g2 = g + 1, t2 = t + 2 - nt;
+            if (t2 >= qte) t2 -= nt, ++g2;
+            issue_tile(cur, g2, t2, u2);
+          }
         } else if (has_next && pos - N == nx && nx < 2 && nx < nxt.N) {
           issue(nxt, nx, u2);  // the next item's position nx, in stream order
           ++nx;
@@ -476,10 +497,11 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(
     };
     const int t_diag_end = min(qt0 + 2, qte);
     for (int g = 0; g < G; ++g) {
-      const int h = cur.hk * G + g;
       const int n0 = g * nt - qt0;  // position of tile t: n0 + t
-      for (int t = qt0; t < t_diag_end; ++t) tile(h, n0 + t, t, std::false_type{});
-      for (int t = t_diag_end; t < qte; ++t) tile(h, n0 + t, t, std::true_type{});
+      const size_t qh = cur.qbase + static_cast<size_t>(g * D);
+      const size_t lh = cur.lbase + static_cast<size_t>(g * T);
+      for (int t = qt0; t < t_diag_end; ++t) tile(g, qh, lh, n0 + t, t, std::false_type{});
+      for (int t = t_diag_end; t < qte; ++t) tile(g, qh, lh, n0 + t, t, std::true_type{});
     }
 
     // Every wavefront is done with the last tile's buffer: the next item's V
@@ -1005,7 +1027,10 @@ hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const vo
   // a window that covers every key of every row is the plain causal case
   const bool win = window >= 0 && window < T - 1;
   const int w = win ? window : T;
-  e = launch(win ? dkdv_kernel<true> : dkdv_kernel<false>, kv_grid, dim3(256), 0, s, q16, k16,
+  const bool grp = Hk != H;
+  auto* kv_kernel = win ? (grp ? dkdv_kernel<true, true> : dkdv_kernel<true, false>)
+                        : (grp ? dkdv_kernel<false, true> : dkdv_kernel<false, false>);
+  e = launch(kv_kernel, kv_grid, dim3(256), 0, s, q16, k16,
              v16, g16, lse, static_cast<const float*>(delta), static_cast<u16*>(dk),
              static_cast<u16*>(dv), dsw, nbt, B, T, H, Hk, c_log2, scale, w);
   if (e != hipSuccess) return e;

@@ -105,3 +105,23 @@ def test_stream_buffers(T, W):
     for _ in range(40):
         items = [rng.randrange(n_kt) for _ in range(rng.randint(1, 12))]
         run_stream(T, items, W, G=rng.choice([1, 1, 2, 3, 5]))
+
+
+@pytest.mark.parametrize("nt", [1, 2, 3, 5, 32])
+@pytest.mark.parametrize("G", [1, 2, 3, 4, 8])
+def test_position_two_ahead_without_division(nt, G):
+    """The kernel finds the (query head, tile) of position n + 2 from that of
+    position n by at most two wrap-arounds of t; this equals divmod."""
+    qt0 = 7
+    qte = qt0 + nt
+    for n in range(G * nt):
+        g, t = divmod(n, nt)
+        t += qt0
+        if n + 2 >= G * nt:
+            continue
+        g2, t2 = g, t + 2
+        if t2 >= qte:
+            t2, g2 = t2 - nt, g2 + 1
+        if t2 >= qte:
+            t2, g2 = t2 - nt, g2 + 1
+        assert (g2, t2 - qt0) == divmod(n + 2, nt)
