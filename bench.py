@@ -20,6 +20,10 @@ half the context is this benchmark's choice) and the windowed decode are
 timed the same way and reported under "sliding_window" (FLOPs and bytes
 counted over the visible (query, key) pairs only).
 
+Grouped-query attention (--kv-heads, default 5: two query heads per key/value
+head, a choice of this benchmark; the pages give no key/value head count) is
+timed the same way on the d20 step and the decode and reported under "gqa".
+
 The fp64 oracle runs once on a bounded sample of the same workload on the
 host cores and is reported as "cpu_baseline" (a reported baseline, not the
 target).
@@ -166,6 +170,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--window", type=int, default=1024,
                     help="sliding-window length for the extra windowed measurement (-1 = skip)")
+    ap.add_argument("--kv-heads", type=int, default=5,
+                    help="key/value heads for the extra grouped-query measurement (0 = skip)")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="first run a plain device copy of this many MiB (a known-size "
                          "kernel that calibrates HBM byte counters in a profiler run)")
@@ -325,6 +331,49 @@ def main():
             "kernels": wk}
         log(f"sliding window {wlen}: {w_ms:.3f} ms  {w_tf:.1f} TFLOP/s  kernels {wk}")
 
+    # ---------------- the same step with grouped key/value heads
+    hkv = args.kv_heads if 0 < args.kv_heads < H and H % args.kv_heads == 0 else None
+    if hkv is not None:
+        kg, vg = k[:, :, :hkv].contiguous(), v[:, :, :hkv].contiguous()
+        dkg, dvg = torch.empty_like(kg), torch.empty_like(vg)
+
+        def gstep(i):
+            e = evs[i]
+            ev.record(e[0], stream)
+            st = lib.na_attn_fwd_gqa(ptr(q), ptr(kg), ptr(vg), ptr(o), ptr(lse), B, T, H, hkv, D,
+                                     -1, P(stream))
+            if st:
+                raise RuntimeError(lib.na_last_error().decode())
+            st = lib.na_attn_bwd_gqa(ptr(q), ptr(kg), ptr(vg), ptr(o), ptr(do), ptr(lse),
+                                     ptr(dq), ptr(dkg), ptr(dvg), ptr(delta), ptr(ws), ws_bytes,
+                                     B, T, H, hkv, D, -1, P(stream), ctypes.cast(ev_arr[i], P))
+            if st:
+                raise RuntimeError(lib.na_last_error().decode())
+
+        log(f"gqa {H}/{hkv} heads: warmup {args.warmup}, timing {args.steps} steps")
+        for i in range(args.warmup):
+            gstep(i)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.warmup, n_total):
+            gstep(i)
+        torch.cuda.synchronize()
+        gwall = time.perf_counter() - t0
+        gk = {}
+        for j, n in enumerate(names):
+            avg = float(np.mean([ev.ms(evs[i][j], evs[i][j + 1])
+                                 for i in range(args.warmup, n_total)]))
+            gk[n] = {"avg_us": round(avg * 1e3, 2),
+                     "tflops": round(fl[n] / (avg * 1e-3) / 1e12, 2) if fl[n] else None}
+        g_ms = gwall * 1e3 / args.steps
+        g_tf = fl["fwd+bwd"] / (g_ms * 1e-3) / 1e12
+        result["gqa"] = {"workload": f"d20 causal self-attention fwd+bwd, {H} query heads, "
+                                     f"{hkv} key/value heads", "kv_heads": hkv,
+                         "ms_per_step": round(g_ms, 4), "TFLOP_per_s": round(g_tf, 2),
+                         "kernels": gk}
+        log(f"gqa: {g_ms:.3f} ms  {g_tf:.1f} TFLOP/s  kernels {gk}")
+        del kg, vg, dkg, dvg
+
     del q, k, v, do, o, dq, dk, dv, ws
     torch.cuda.empty_cache()
 
@@ -394,6 +443,33 @@ def main():
                 "us_per_call": round(w_ms * 1e3, 2), "kv_bytes": wkv,
                 "GB_per_s": round(w_gbs, 1), "pct_hbm_peak": round(100 * w_gbs / PEAK_HBM_GBS, 2)}
             log(f"sliding window decode {result['sliding_window']['decode']}")
+        if hkv is not None:
+            gcaches = [(kc[:, :, :hkv].contiguous(), vc[:, :, :hkv].contiguous())
+                       for kc, vc in caches]
+
+            def gdstep(i):
+                kc, vc = gcaches[i % 3]
+                st = lib.na_attn_decode_gqa(ptr(qd), ptr(kc), ptr(vc), ptr(lens), ptr(od),
+                                            ptr(lsed), Bd, Hd, hkv, D, Tc, -1, ptr(ws), wsb,
+                                            P(stream), ctypes.cast(darr[i], P))
+                if st:
+                    raise RuntimeError(lib.na_last_error().decode())
+
+            for i in range(5):
+                gdstep(i)
+            torch.cuda.synchronize()
+            for i in range(5, nd + 5):
+                gdstep(i)
+            torch.cuda.synchronize()
+            gtot = [ev.ms(devs[i][0], devs[i][2]) for i in range(5, nd + 5)]
+            gkv = int(dinp.seqlens.astype(np.int64).sum()) * hkv * D * 2 * 2
+            g_ms = float(np.mean(gtot))
+            g_gbs = (gkv + io_bytes) / (g_ms * 1e-3) / 1e9
+            result.setdefault("gqa", {"kv_heads": hkv})["decode"] = {
+                "us_per_call": round(g_ms * 1e3, 2), "kv_bytes": gkv, "GB_per_s": round(g_gbs, 1),
+                "pct_hbm_peak": round(100 * g_gbs / PEAK_HBM_GBS, 2)}
+            log(f"gqa decode {result['gqa']['decode']}")
+            del gcaches
         del caches, kc0, vc0
         torch.cuda.empty_cache()
 
