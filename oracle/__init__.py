@@ -10,5 +10,5 @@ no function is "parity unpinned".
 """
 from .attention import (  # noqa: F401
     softmax_scale, forward_head, backward_head, forward, backward,
-    decode_head, decode, causal_probabilities, kv_head, kv_grads,
+    decode_head, decode, causal_probabilities, kv_head, kv_grads, prefill_head, prefill,
 )

@@ -32,7 +32,13 @@ readings taken here (plainest, all listed in the design notes):
   * LSE is the natural log of sum_j exp(s * q_i . k_j) over visible keys;
   * the loss depends on O only, so the LSE output receives no gradient;
   * decode: the single new query is the last cached position and sees all
-    L_b cached keys (bottom-right alignment); the cache already holds it.
+    L_b cached keys (bottom-right alignment); the cache already holds it;
+  * prefill over a cache (the engine's prefilled prompt cache, same blog,
+    section 6): a chunk of T_q new tokens of a sequence whose cache holds L
+    rows is appended at rows L .. L + T_q - 1, and its query i sits at
+    position L + i and sees keys 0 .. L + i (bottom-right causal alignment,
+    flash_attn_with_kvcache's convention); with a window W, keys
+    L + i - W .. L + i.
 
 Everything is the plain definition in float64, one (batch, head) at a time,
 with dense T x T matrices; numpy's matmul is the only library primitive.
@@ -46,6 +52,7 @@ import numpy as np
 __all__ = [
     "softmax_scale", "forward_head", "backward_head", "forward", "backward",
     "decode_head", "decode", "causal_probabilities", "kv_head", "kv_grads",
+    "prefill_head", "prefill",
 ]
 
 
@@ -249,3 +256,60 @@ def decode(q, k_cache, v_cache, seqlens, pairs=None, window=None):
             o[b, h] = ob
             lse[b, h] = lb
     return o, lse
+
+
+def prefill_head(q, K_cache, V_cache, k_new, v_new, L: int, window=None):
+    """One (batch, head) of a prefill over a cache holding L rows.
+
+    q, k_new, v_new: (T_q, D); K_cache, V_cache: (T_cap, D), rows < L valid.
+    The keys are K_cache[:L] followed by k_new (likewise the values); query i
+    sees keys j <= L + i (and j >= L + i - window).  Returns O (T_q, D) and
+    lse (T_q,) in float64.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    T_q, D = q.shape
+    K = np.concatenate([np.asarray(K_cache[:L], np.float64), np.asarray(k_new, np.float64)])
+    V = np.concatenate([np.asarray(V_cache[:L], np.float64), np.asarray(v_new, np.float64)])
+    S = softmax_scale(D) * (q @ K.T)                  # (T_q, L + T_q)
+    i = np.arange(T_q)[:, None]
+    j = np.arange(L + T_q)[None, :]
+    hidden = j > L + i
+    if window is not None:
+        hidden |= j < L + i - int(window)
+    S[hidden] = -np.inf
+    m = S.max(axis=1)                                 # finite: key L + i is visible
+    E = np.exp(S - m[:, None])
+    l = E.sum(axis=1)
+    return (E / l[:, None]) @ V, m + np.log(l)
+
+
+def prefill(q, k_new, v_new, k_cache, v_cache, cache_lens, window=None, pairs=None):
+    """Batched prefill.  q (B, T_q, H, D); k_new, v_new (B, T_q, H_kv, D);
+    caches (B, T_cap, H_kv, D); cache_lens int [B] (rows already cached,
+    L_b + T_q <= T_cap).
+
+    Returns o (B, T_q, H, D), lse (B, H, T_q) and the caches after the append
+    (new arrays; the inputs are not modified), or, when `pairs` lists (b, h)
+    query heads, a dict {(b, h): (O, lse)}.
+    """
+    B, T_q, H, D = q.shape
+    Hk = k_new.shape[2]
+    kh = lambda h: kv_head(h, H, Hk)  # noqa: E731
+    if pairs is not None:
+        return {(b, h): prefill_head(q[b, :, h], k_cache[b, :, kh(h)], v_cache[b, :, kh(h)],
+                                     k_new[b, :, kh(h)], v_new[b, :, kh(h)],
+                                     int(cache_lens[b]), window) for (b, h) in pairs}
+    kc = np.array(k_cache, dtype=np.float64)
+    vc = np.array(v_cache, dtype=np.float64)
+    o = np.empty((B, T_q, H, D), dtype=np.float64)
+    lse = np.empty((B, H, T_q), dtype=np.float64)
+    for b in range(B):
+        L = int(cache_lens[b])
+        for h in range(H):
+            O, lv = prefill_head(q[b, :, h], k_cache[b, :, kh(h)], v_cache[b, :, kh(h)],
+                                 k_new[b, :, kh(h)], v_new[b, :, kh(h)], L, window)
+            o[b, :, h] = O
+            lse[b, h] = lv
+        kc[b, L:L + T_q] = k_new[b]
+        vc[b, L:L + T_q] = v_new[b]
+    return o, lse, kc, vc

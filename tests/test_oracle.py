@@ -468,3 +468,63 @@ def test_gqa_decode_reads_the_group_head():
             O, l = oracle.forward_head(Qf, kc[b, :L, h // 2, :], vc[b, :L, h // 2, :])
             assert np.allclose(o[b, h], O[L - 1], rtol=0, atol=1e-13)
             assert abs(lse[b, h] - l[L - 1]) <= 1e-13
+
+
+# ---------------------------------------------------------------- prefill over a cache
+
+def _prefill_case(B, T_q, H, Hk, T_cap, lens, seed, D=16):
+    q = rnd((B, T_q, H, D), seed)
+    kn, vn = rnd((B, T_q, Hk, D), seed + 1), rnd((B, T_q, Hk, D), seed + 2)
+    kc, vc = rnd((B, T_cap, Hk, D), seed + 3), rnd((B, T_cap, Hk, D), seed + 4)
+    return q, kn, vn, kc, vc, np.array(lens)
+
+
+def test_prefill_on_an_empty_cache_is_the_forward():
+    """L = 0: the chunk attends only to itself, top-left causal = the forward."""
+    q, kn, vn, kc, vc, lens = _prefill_case(2, 13, 4, 2, 20, [0, 0], 501)
+    o, lse, kc2, vc2 = oracle.prefill(q, kn, vn, kc, vc, lens)
+    of, lf = oracle.forward(q, kn, vn)
+    assert np.array_equal(o, of) and np.array_equal(lse, lf)
+    assert np.array_equal(kc2[:, :13], kn) and np.array_equal(kc2[:, 13:], kc[:, 13:])
+
+
+def test_prefill_of_one_token_is_decode():
+    """T_q = 1: the query at position L sees keys 0 .. L = decode with L + 1 cached rows."""
+    q, kn, vn, kc, vc, lens = _prefill_case(3, 1, 4, 2, 30, [0, 7, 29], 511)
+    o, lse, kc2, vc2 = oracle.prefill(q, kn, vn, kc, vc, lens)
+    od, ld = oracle.decode(q[:, 0], kc2, vc2, lens + 1)
+    assert np.allclose(o[:, 0], od, rtol=0, atol=1e-13)
+    assert np.allclose(lse[:, :, 0], ld, rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("W", [None, 0, 3])
+def test_prefill_brute_force_loops(W):
+    T_q, L, D = 4, 5, 4
+    q, kn, vn, kc, vc, _ = _prefill_case(1, T_q, 1, 1, 12, [L], 521, D=D)
+    O, lse = oracle.prefill_head(q[0, :, 0], kc[0, :, 0], vc[0, :, 0], kn[0, :, 0], vn[0, :, 0],
+                                 L, W)
+    K = kc[0, :L, 0].tolist() + kn[0, :, 0].tolist()
+    V = vc[0, :L, 0].tolist() + vn[0, :, 0].tolist()
+    Wb = 10 ** 9 if W is None else W
+    for i in range(T_q):
+        o, l = _brute_window_row(q[0, i, 0].tolist(), K, V, L + i, Wb)
+        assert np.allclose(O[i], o, rtol=0, atol=1e-13) and abs(lse[i] - l) <= 1e-13
+
+
+def test_prefill_against_torch_sdpa_fp64():
+    """torch's CPU scaled_dot_product_attention with an explicit bottom-right
+    causal mask over [cache rows, new rows] and enable_gqa, in float64."""
+    torch = pytest.importorskip("torch")
+    B, T_q, H, Hk, T_cap, D = 2, 9, 4, 2, 30, 16
+    q, kn, vn, kc, vc, lens = _prefill_case(B, T_q, H, Hk, T_cap, [6, 17], 531, D=D)
+    o, lse, kc2, vc2 = oracle.prefill(q, kn, vn, kc, vc, lens)
+    for b in range(B):
+        L = int(lens[b])
+        K = torch.tensor(kc2[b, :L + T_q].transpose(1, 0, 2).copy())[None]
+        V = torch.tensor(vc2[b, :L + T_q].transpose(1, 0, 2).copy())[None]
+        Q = torch.tensor(q[b].transpose(1, 0, 2).copy())[None]
+        i = torch.arange(T_q)[:, None]
+        j = torch.arange(L + T_q)[None, :]
+        to = torch.nn.functional.scaled_dot_product_attention(Q, K, V, attn_mask=j <= L + i,
+                                                              enable_gqa=True)
+        assert np.allclose(o[b], to[0].numpy().transpose(1, 0, 2), rtol=0, atol=1e-12)
