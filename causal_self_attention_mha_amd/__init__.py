@@ -12,6 +12,8 @@ Functions (names match the C entry points):
   attn_fwd(q, k, v)                       -> (o, lse)
   attn_bwd(q, k, v, o, dout, lse)         -> (dq, dk, dv, delta)
   attn_decode(q, k_cache, v_cache, seqlens) -> (o, lse)
+  attn_prefill(q, k_new, v_new, k_cache, v_cache, cache_lens) -> (o, lse)
+                                          (appends k_new, v_new to the caches in place)
 Each takes window=W (an int >= 0) for sliding-window attention (key j visible
 to query i iff i - W <= j <= i), which calls the *_window entry point;
 window=None is plain causal attention.  k and v (and the decode caches) may
@@ -27,7 +29,8 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["attn_fwd", "attn_bwd", "attn_decode", "decode_workspace_bytes", "bwd_workspace_bytes",
+__all__ = ["attn_fwd", "attn_bwd", "attn_decode", "attn_prefill", "decode_workspace_bytes",
+           "bwd_workspace_bytes",
            "load_library",
            "library_path", "NAError", "HEAD_DIM"]
 
@@ -84,10 +87,11 @@ def load_library():
                                     i, i, i, vp, vp]
     lib.na_attn_decode_gqa.argtypes = [vp, vp, vp, vp, vp, f32p, i, i, i, i, i, i, vp, sz, vp,
                                        vp]
+    lib.na_attn_prefill.argtypes = [vp, vp, vp, vp, vp, vp, vp, f32p, i, i, i, i, i, i, i, vp]
     for fn in ("na_attn_fwd", "na_attn_bwd", "na_attn_decode", "na_attn_fwd_f32",
                "na_attn_bwd_f32", "na_attn_bwd_timed", "na_attn_decode_timed",
                "na_attn_fwd_window", "na_attn_bwd_window", "na_attn_decode_window",
-               "na_attn_fwd_gqa", "na_attn_bwd_gqa", "na_attn_decode_gqa"):
+               "na_attn_fwd_gqa", "na_attn_bwd_gqa", "na_attn_decode_gqa", "na_attn_prefill"):
         getattr(lib, fn).restype = ctypes.c_int
     lib.na_status_string.argtypes = [ctypes.c_int]
     lib.na_status_string.restype = ctypes.c_char_p
@@ -283,4 +287,41 @@ def attn_decode(q, k_cache, v_cache, seqlens, o=None, lse=None, workspace=None,
     else:
         _check(lib, "na_attn_decode",
                lib.na_attn_decode(*args, B, H, D, T_cap, _ptr(workspace), ws_bytes, _stream(q)))
+    return o, lse
+
+
+def attn_prefill(q, k_new, v_new, k_cache, v_cache, cache_lens, o=None, lse=None,
+                 want_lse=True, window=None):
+    """Prefill a chunk over a KV cache: appends k_new, v_new at rows
+    cache_lens[b] .. of the caches (in place), then the chunk's queries attend
+    bottom-right causally over the cache.  Returns (o, lse); cache_lens is not
+    updated."""
+    import torch
+    lib = load_library()
+    _require(q.is_cuda and q.dtype == torch.bfloat16 and q.dim() == 4 and q.shape[-1] == HEAD_DIM,
+             "q must be a bf16 GPU tensor (B, T_q, H, 128)")
+    B, T_q, H, D = q.shape
+    _require(k_new.dim() == 4 and k_new.shape[:2] == (B, T_q) and k_new.shape[3] == D,
+             "k_new must be (B, T_q, H_kv, 128)")
+    Hk = k_new.shape[2]
+    _require(Hk >= 1 and H % Hk == 0, f"q has {H} heads, not a multiple of k_new's {Hk}")
+    _require(k_cache.dim() == 4 and k_cache.shape[0] == B and k_cache.shape[2:] == (Hk, D)
+             and k_cache.shape[1] >= T_q, "k_cache must be (B, T_cap >= T_q, H_kv, 128)")
+    for n, t, shape in (("q", q, q.shape), ("k_new", k_new, k_new.shape),
+                        ("v_new", v_new, k_new.shape), ("k_cache", k_cache, k_cache.shape),
+                        ("v_cache", v_cache, k_cache.shape)):
+        _require(t.dtype == torch.bfloat16 and t.device == q.device and t.is_contiguous()
+                 and t.shape == shape, f"{n} must be contiguous bf16 {tuple(shape)} on {q.device}")
+    _require(cache_lens.dtype == torch.int32 and cache_lens.shape == (B,)
+             and cache_lens.device == q.device and cache_lens.is_contiguous(),
+             "cache_lens must be int32 [B] on the GPU")
+    T_cap = k_cache.shape[1]
+    o = torch.empty_like(q) if o is None else o
+    if want_lse and lse is None:
+        lse = torch.empty((B, H, T_q), dtype=torch.float32, device=q.device)
+    window = _window(window)
+    _check(lib, "na_attn_prefill",
+           lib.na_attn_prefill(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
+                               _ptr(cache_lens), _ptr(o), _ptr(lse), B, T_q, H, Hk, D, T_cap,
+                               -1 if window is None else window, _stream(q)))
     return o, lse

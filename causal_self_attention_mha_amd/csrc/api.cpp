@@ -121,6 +121,29 @@ na_status na_attn_fwd(const void* q, const void* k, const void* v, void* o, floa
   return na_attn_fwd_window(q, k, v, o, lse, B, T, H, D, -1, stream);
 }
 
+na_status na_attn_prefill(const void* q, const void* k_new, const void* v_new, void* k_cache,
+                          void* v_cache, const int* cache_lens, void* o, float* lse, int B,
+                          int T_q, int H, int H_kv, int D, int T_cap, int window,
+                          void* stream) {
+  na_status st = check_sizes(B, T_q, H, D);
+  if (st) return st;
+  if ((st = check_kv_heads(H, H_kv))) return st;
+  if (T_cap < T_q)
+    return fail(NA_ERR_INVALID_ARG, "T_cap=%d is smaller than the chunk T_q=%d", T_cap, T_q);
+  if ((st = check_sizes(B, T_cap, H, D))) return st;  // the caches' extent
+  if (lse != nullptr)
+    st = check_ptrs({{q, "q"}, {k_new, "k_new"}, {v_new, "v_new"}, {cache_lens, "cache_lens"}},
+                    {{k_cache, "k_cache"}, {v_cache, "v_cache"}, {o, "o"}, {lse, "lse"}});
+  else
+    st = check_ptrs({{q, "q"}, {k_new, "k_new"}, {v_new, "v_new"}, {cache_lens, "cache_lens"}},
+                    {{k_cache, "k_cache"}, {v_cache, "v_cache"}, {o, "o"}});
+  if (st) return st;
+  return hip_status(na::launch_prefill_bf16(q, k_new, v_new, k_cache, v_cache, cache_lens, o, lse,
+                                            B, T_q, H, H_kv, T_cap, window,
+                                            (hipStream_t)stream),
+                    "na_attn_prefill");
+}
+
 size_t na_attn_bwd_workspace_bytes(int B, int T, int H, int D) {
   if (B < 1 || T < 1 || H < 1 || D != na::kHeadDim || T > 1048576) return 0;
   return na::bwd_workspace_bytes(B, T, H);

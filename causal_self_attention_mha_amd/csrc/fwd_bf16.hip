@@ -51,11 +51,16 @@ constexpr float kRescaleLog2 = 8.0f;
 
 // WIN: sliding window, key j visible to query i iff i - win <= j <= i (the
 // plain causal kernel is WIN = false).
-template <bool WIN>
+// PRE: prefill over a KV cache.  q, o hold T query rows per sequence, k, v are
+// caches of Tc rows per sequence, and the query rows sit at positions
+// L .. L + T - 1 with L = lens[b] (clamped to [0, Tc - T]): query row r sees
+// cache rows 0 .. L + r.  Without PRE, Tc = T and L = 0 (training).  Masks and
+// tile ranges below compare key rows with query positions L + r.
+template <bool WIN, bool PRE>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(
     const u16* __restrict__ q, const u16* __restrict__ k, const u16* __restrict__ v,
-    u16* __restrict__ o, float* __restrict__ lse, int B, int T, int H, int Hk, float c_log2,
-    float scale, int win) {
+    u16* __restrict__ o, float* __restrict__ lse, int B, int T, int Tc, int H, int Hk,
+    const int* __restrict__ lens, float c_log2, float scale, int win) {
   // two buffers of (K tile, V tile), swizzled (see tile_swz)
   __shared__ __attribute__((aligned(1024))) char kvs[2 * BUF_B];
 
@@ -78,11 +83,14 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(
   const int bh = b * H + h;
   const int q0 = qt * BQ;
   const int qw0 = q0 + wave * 32;
+  const int L = PRE ? min(max(lens[b], 0), Tc - T) : 0;  // position of query row 0
+  const int nk = PRE ? L + T : T;                          // key rows that exist
   // 32-bit row offsets within one batch (T * H * D < 2^31 is checked on the host)
   const int rs = H * D;    // q, o: stride between t
   const int rsk = Hk * D;  // k, v
   const size_t base = static_cast<size_t>(b) * T * rs + static_cast<size_t>(h) * D;
-  const size_t kbase = static_cast<size_t>(b) * T * rsk + static_cast<size_t>(hk) * D;
+  const size_t kbase =
+      static_cast<size_t>(b) * (PRE ? Tc : T) * rsk + static_cast<size_t>(hk) * D;
 
   // Q^T operand: lane holds q[qw0 + l32][16 kc + 8 half + 0..7], kc = 0..7.
   // Rows past T (their outputs are discarded) read row T-1 instead.
@@ -101,10 +109,10 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(
   float lpart = 0.f;    // running sum over this lane's half of the keys
   const float thr = kRescaleLog2 / c_log2;
 
-  const int last_q = min(q0 + BQ, T) - 1;
+  const int last_q = L + min(q0 + BQ, T) - 1;  // position of the last query row
   const int n_kt = last_q / BK + 1;  // key tiles at or left of the diagonal
   // first key tile that any row of the workgroup sees (0 without a window)
-  const int kt_lo = WIN ? max(q0 - win, 0) / BK : 0;
+  const int kt_lo = WIN ? max(L + q0 - win, 0) / BK : 0;
 
   // operand read addresses in buffer 0 (buffer 1: + BUF_B, V tile: + kTileBytes)
   const uint32_t kv_lds = lds_addr(kvs);
@@ -116,9 +124,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(
   }
   const uint32_t rsb = static_cast<uint32_t>(rsk) * 2;
   const uint32_t cvoff = tile_copy_offset(wave, lane, rsb);
-  auto issue = [&](int kt, int buf) {  // K, V tile kt -> buffer buf; keys past T read as 0
+  auto issue = [&](int kt, int buf) {  // K, V tile kt -> buffer buf; keys past nk read as 0
     const int k0 = kt * BK;
-    const uint32_t nrec = static_cast<uint32_t>(T - k0) * rsb;
+    const uint32_t nrec = static_cast<uint32_t>(nk - k0) * rsb;
     const size_t off = kbase + static_cast<size_t>(k0) * rsk;
     copy_tile<NW>(buffer_rsrc(k + off, nrec), cvoff, rsb, kv_lds + buf * BUF_B, wave);
     copy_tile<NW>(buffer_rsrc(v + off, nrec), cvoff, rsb, kv_lds + buf * BUF_B + kTileBytes,
@@ -138,7 +146,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(
     wait_vmem();
     __syncthreads();
     // whole tile above this wavefront's diagonal, or before its rows' windows
-    const bool skip = k0 > qw0 + 31 || (WIN && k0 + BK - 1 < qw0 - win);
+    const bool skip = k0 > L + qw0 + 31 || (WIN && k0 + BK - 1 < L + qw0 - win);
     // The copy of the next tile is issued once this tile's K reads are done
     // (measured faster than issuing it at the barrier).
     if (skip) {
@@ -176,13 +184,14 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(
 
     // causal select on tiles that cross the diagonal (and, with a window, on
     // tiles that cross the lower edge of some row's window)
-    if (k0 + BK - 1 > qw0 || (WIN && k0 < qw0 + 31 - win)) {
+    if (k0 + BK - 1 > L + qw0 || (WIN && k0 < L + qw0 + 31 - win)) {
+      const int qpos = L + qrow;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = k0 + kb * 32 + acc_row(lane, r);
-          if (key > qrow || (WIN && key < qrow - win)) sacc[kb][r] = -INFINITY;
+          if (key > qpos || (WIN && key < qpos - win)) sacc[kb][r] = -INFINITY;
         }
     }
 
@@ -253,7 +262,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(
                               pack_bf16x2(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv));
         *reinterpret_cast<uint2*>(op + 32 * db + 8 * g + 4 * half) = pk;
       }
-    if (half == 0) lse[static_cast<size_t>(bh) * T + qrow] = m * scale + logf(l);
+    if (half == 0 && (!PRE || lse != nullptr))
+      lse[static_cast<size_t>(bh) * T + qrow] = m * scale + logf(l);
   }
 }
 
@@ -266,10 +276,51 @@ hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o,
   const int n_qt = (T + BQ - 1) / BQ;
   const dim3 grid(static_cast<unsigned>(n_qt) * B * H);
   const bool win = window >= 0 && window < T - 1;  // else every row sees all its keys
-  return launch(win ? fwd_bf16_kernel<true> : fwd_bf16_kernel<false>, grid, dim3(64 * NW), 0, s,
-                static_cast<const u16*>(q), static_cast<const u16*>(k),
-                static_cast<const u16*>(v), static_cast<u16*>(o), lse, B, T, H, Hk, c_log2,
-                scale, win ? window : T);
+  return launch(win ? fwd_bf16_kernel<true, false> : fwd_bf16_kernel<false, false>, grid,
+                dim3(64 * NW), 0, s, static_cast<const u16*>(q), static_cast<const u16*>(k),
+                static_cast<const u16*>(v), static_cast<u16*>(o), lse, B, T, T, H, Hk,
+                static_cast<const int*>(nullptr), c_log2, scale, win ? window : T);
+}
+
+// Prefill: the T new rows of k_new, v_new go to cache rows L .. L + T - 1
+// (L = lens[b] clamped to [0, Tc - T]), one 16-byte chunk per thread; the
+// rows of one (b, t) are contiguous (H_kv D elements) in both tensors.
+__global__ __launch_bounds__(256) void kv_append_kernel(const u16* __restrict__ k_new,
+                                                        const u16* __restrict__ v_new,
+                                                        u16* __restrict__ kc, u16* __restrict__ vc,
+                                                        const int* __restrict__ lens, int T,
+                                                        int Tc, int Hk, long chunks) {
+  const long i = static_cast<long>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= chunks) return;
+  const int per_row = Hk * D / 8;  // 16-byte chunks per (b, t) row
+  const long row = i / per_row;    // b * T + t
+  const int c = static_cast<int>(i - row * per_row);
+  const int b = static_cast<int>(row / T), t = static_cast<int>(row - static_cast<long>(b) * T);
+  const int L = min(max(lens[b], 0), Tc - T);
+  const size_t dst = (static_cast<size_t>(b) * Tc + L + t) * Hk * D + 8 * c;
+  const size_t src = static_cast<size_t>(row) * Hk * D + 8 * c;
+  st16(kc + dst, ld16(k_new + src));
+  st16(vc + dst, ld16(v_new + src));
+}
+
+hipError_t launch_prefill_bf16(const void* q, const void* k_new, const void* v_new, void* kc,
+                               void* vc, const int* lens, void* o, float* lse, int B, int T,
+                               int H, int Hk, int Tc, int window, hipStream_t s) {
+  const long chunks = static_cast<long>(B) * T * Hk * D / 8;
+  hipError_t e = launch(kv_append_kernel, dim3(static_cast<unsigned>((chunks + 255) / 256)),
+                        dim3(256), 0, s, static_cast<const u16*>(k_new),
+                        static_cast<const u16*>(v_new), static_cast<u16*>(kc),
+                        static_cast<u16*>(vc), lens, T, Tc, Hk, chunks);
+  if (e != hipSuccess) return e;
+  const float scale = 1.0f / sqrtf(static_cast<float>(D));
+  const float c_log2 = scale * 1.4426950408889634f;
+  const int n_qt = (T + BQ - 1) / BQ;
+  const dim3 grid(static_cast<unsigned>(n_qt) * B * H);
+  const bool win = window >= 0 && window < Tc - 1;  // else every row sees all its keys
+  return launch(win ? fwd_bf16_kernel<true, true> : fwd_bf16_kernel<false, true>, grid,
+                dim3(64 * NW), 0, s, static_cast<const u16*>(q), static_cast<const u16*>(kc),
+                static_cast<const u16*>(vc), static_cast<u16*>(o), lse, B, T, Tc, H, Hk, lens,
+                c_log2, scale, win ? window : Tc);
 }
 
 }  // namespace na

@@ -23,6 +23,14 @@ constexpr int kHeadDim = 128;
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
                            int B, int T, int H, int Hk, int window, hipStream_t s);
 
+// bf16 prefill over a KV cache: k_new, v_new (B, T, Hk, D) appended at cache
+// rows lens[b] .. lens[b] + T - 1 (lens clamped to [0, Tc - T] on the device),
+// then the T queries attend bottom-right causally over rows 0 .. lens[b] + r.
+// lse may be null.
+hipError_t launch_prefill_bf16(const void* q, const void* k_new, const void* v_new, void* kc,
+                               void* vc, const int* lens, void* o, float* lse, int B, int T,
+                               int H, int Hk, int Tc, int window, hipStream_t s);
+
 // bf16 backward: delta, then dk/dv, then dq.
 // ws: optional dS workspace of bwd_workspace_bytes(B, T, H) bytes; with it dQ
 // is a GEMM over the stored dS, without it the dQ pass recomputes S and dP

@@ -186,6 +186,28 @@ na_status na_attn_decode_gqa(const void* q, const void* k_cache, const void* v_c
                              int D, int T_cap, int window, void* workspace,
                              size_t workspace_bytes, void* stream, void* const* events);
 
+/*
+ * Prefill over a KV cache (the inference engine's prefilled prompt cache,
+ * flash_attn_with_kvcache, blog section 6): for each sequence b whose caches
+ * hold L = cache_lens[b] rows, the T_q new key/value rows k_new[b], v_new[b]
+ * are written to cache rows L .. L + T_q - 1, then query row r of q[b] (at
+ * position L + r) attends over cache rows 0 .. L + r (with a window, rows
+ * L + r - window .. L + r).  The pages do not spell out the alignment; this is
+ * flash_attn_with_kvcache's bottom-right causal convention, which reduces to
+ * the decode call for T_q = 1 and to the training forward for L = 0.
+ * q: bf16 (B, T_q, H, D); k_new, v_new: bf16 (B, T_q, H_kv, D); k_cache,
+ * v_cache: bf16 (B, T_cap, H_kv, D), read and written (rows other than
+ * L .. L + T_q - 1 are left as they are); cache_lens: DEVICE int32[B], clamped
+ * to [0, T_cap - T_q] on the device and not updated (the caller adds T_q).
+ * o: bf16 (B, T_q, H, D) output; lse: fp32 (B, H, T_q) output, or NULL.
+ * H a multiple of H_kv; T_cap >= T_q.  Enqueues two kernels: the append, then
+ * the attention.  bf16 only.
+ */
+na_status na_attn_prefill(const void* q, const void* k_new, const void* v_new, void* k_cache,
+                          void* v_cache, const int* cache_lens, void* o, float* lse, int B,
+                          int T_q, int H, int H_kv, int D, int T_cap, int window,
+                          void* stream);
+
 /* Static text for a status code. */
 const char* na_status_string(na_status s);
 

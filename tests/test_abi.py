@@ -35,7 +35,7 @@ def test_header_declares_the_entry_points():
               "na_attn_bwd_workspace_bytes", "na_attn_bwd_timed", "na_attn_decode_timed",
               "na_attn_fwd_f32", "na_attn_bwd_f32", "na_status_string", "na_last_error",
               "na_attn_fwd_window", "na_attn_bwd_window", "na_attn_decode_window",
-              "na_attn_fwd_gqa", "na_attn_bwd_gqa", "na_attn_decode_gqa"):
+              "na_attn_fwd_gqa", "na_attn_bwd_gqa", "na_attn_decode_gqa", "na_attn_prefill"):
         assert s in syms
 
 
@@ -143,6 +143,20 @@ def test_gqa_entry_points_check_the_head_counts(lib):
     wneed = lib.na_attn_decode_workspace_bytes(4, 6, 128, 64)
     assert lib.na_attn_decode_gqa(*d[:6], 4, 6, 4, 128, 64, -1, d[6], wneed, None,
                                   None) == INVALID
+
+
+def test_prefill_checks_its_arguments(lib):
+    p = [A + 0x100 * i for i in range(8)]  # q k_new v_new k_cache v_cache lens o lse
+    call = lambda ptrs, T_q=8, H=2, Hk=2, T_cap=64: lib.na_attn_prefill(  # noqa: E731
+        *ptrs, 1, T_q, H, Hk, 128, T_cap, -1, None)
+    assert call(p, T_cap=4) == INVALID and b"T_cap" in lib.na_last_error()
+    assert call(p, H=4, Hk=3) == INVALID
+    bad = list(p)
+    bad[6] = bad[0]              # o aliases q
+    assert call(bad) == INVALID
+    bad = list(p)
+    bad[5] = 0                   # no cache_lens
+    assert call(bad) == INVALID
 
 
 def test_bwd_workspace_bytes(lib):
