@@ -20,6 +20,11 @@ half the context is this benchmark's choice) and the windowed decode are
 timed the same way and reported under "sliding_window" (FLOPs and bytes
 counted over the visible (query, key) pairs only).
 
+Prefill over a KV cache (16 sequences, a 512-token chunk each over caches of
+U[0, 1536] rows, T_cap 2048, d20 heads; the chat-prefill shape of the
+inference engine, sizes chosen here) is timed and reported under "prefill"
+(append + attention, FLOPs over the visible pairs).
+
 Grouped-query attention (--kv-heads, default 5: two query heads per key/value
 head, a choice of this benchmark; the pages give no key/value head count) is
 timed the same way on the d20 step and the decode and reported under "gqa".
@@ -170,6 +175,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--window", type=int, default=1024,
                     help="sliding-window length for the extra windowed measurement (-1 = skip)")
+    ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--kv-heads", type=int, default=5,
                     help="key/value heads for the extra grouped-query measurement (0 = skip)")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
@@ -472,6 +478,44 @@ def main():
             del gcaches
         del caches, kc0, vc0
         torch.cuda.empty_cache()
+
+    # ---------------- prefill over a KV cache
+    if not args.no_prefill:
+        Bp, Tq, Tcp = 16, 512, 2048
+        rng = np.random.default_rng(W.CONFIGS[W.DECODE].seed + 100)
+        plens = rng.integers(0, Tcp - Tq + 1, size=Bp).astype(np.int32)
+        pin = W.make_train_inputs(cfg, B=Bp, T=Tq)
+        pq, pk, pv = (dev_t(x) for x in (pin.q_store, pin.k_store, pin.v_store))
+        pkc = torch.zeros((Bp, Tcp, H, D), dtype=torch.bfloat16, device=dev)
+        pvc = torch.zeros_like(pkc)
+        pl = torch.from_numpy(plens).to(dev)
+        po = torch.empty_like(pq)
+        plse = torch.empty((Bp, H, Tq), dtype=torch.float32, device=dev)
+        pev = ev.create(2)
+
+        def pstep():
+            st = lib.na_attn_prefill(ptr(pq), ptr(pk), ptr(pv), ptr(pkc), ptr(pvc), ptr(pl),
+                                     ptr(po), ptr(plse), Bp, Tq, H, H, D, Tcp, -1, P(stream))
+            if st:
+                raise RuntimeError(lib.na_last_error().decode())
+
+        for _ in range(args.warmup):
+            pstep()
+        torch.cuda.synchronize()
+        ev.record(pev[0], stream)
+        for _ in range(args.steps):
+            pstep()
+        ev.record(pev[1], stream)
+        p_ms = ev.ms(pev[0], pev[1]) / args.steps
+        pairs = int(sum(Tq * int(L) + Tq * (Tq + 1) // 2 for L in plens))
+        pfl = 4 * D * H * pairs  # QK^T and PV, 2 FLOP per multiply-add
+        result["prefill"] = {
+            "workload": f"prefill over a KV cache: B={Bp} chunks of {Tq} tokens, cache lengths "
+                        f"U[0,{Tcp - Tq}], T_cap={Tcp}, H={H}, D={D}, bf16 (append + attention)",
+            "ms_per_call": round(p_ms, 4), "TFLOP_per_s": round(pfl / (p_ms * 1e-3) / 1e12, 2),
+            "visible_pairs": pairs, "calls": args.steps}
+        log(f"prefill {result['prefill']}")
+        del pq, pk, pv, pkc, pvc, po
 
     # ---------------- CPU baseline: the oracle on a bounded sample
     if args.cpu_heads > 0:
