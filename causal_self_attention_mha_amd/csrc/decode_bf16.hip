@@ -23,7 +23,9 @@
 //            compute units idle (measured 48% -> 56% of HBM bandwidth).
 //   combine: one workgroup per (b, h), one pass with a running max:
 //            o = sum_c e^(m_c - M) o_c / sum_c e^(m_c - M) l_c.
-// Rows t >= L are never read.
+// Rows t >= L (and, with a window, rows before j0) are never read.  With H_kv
+// key/value heads the cache is (B, T_cap, H_kv, D) and query head h's group
+// reads head h / (H / H_kv).
 #include <algorithm>
 
 #include "device_common.hpp"

@@ -13,9 +13,9 @@
 //     double-buffered LDS (buffer loads with the LDS destination; keys past T
 //     arrive as zeros), the next tile's copy issued after the current tile's
 //     score MFMAs and in flight during its softmax and PV; one barrier per
-//     tile.  Both tiles keep their natural
-//     row-major layout, swizzled (see tile_swz): K is read row-wise, V^T with
-//     the transposing ds_read_b64_tr_b16, both free of bank conflicts;
+//     tile.  Both tiles keep their natural row-major layout, swizzled (see
+//     tile_swz): K is read row-wise, V^T with the transposing
+//     ds_read_b64_tr_b16, both free of bank conflicts;
 //   * scores are computed transposed, S^T = K Q^T (v_mfma_f32_32x32x16_bf16),
 //     so that each lane owns one query row: the online-softmax max and sum are
 //     lane-local apart from one exchange with lane l^32;
@@ -29,8 +29,11 @@
 //     softmax;
 //   * key tiles entirely above the diagonal are never visited; only tiles that
 //     cross the diagonal apply the causal select;
-//   * each XCD runs one head's query tiles back to back, heaviest first, so
-//     the head's K and V stay in that XCD's L2.
+//   * each XCD runs a group of heads' query tiles together, heaviest first
+//     (the query heads that share a key/value head next to each other), so
+//     their K and V stay in that XCD's L2.
+// The same kernel, instantiated with WIN and PRE, serves sliding windows and
+// the prefill of a chunk over a KV cache (see the template's notes).
 #include <type_traits>
 
 #include "device_common.hpp"
