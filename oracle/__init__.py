@@ -12,3 +12,6 @@ from .attention import (  # noqa: F401
     softmax_scale, forward_head, backward_head, forward, backward,
     decode_head, decode, causal_probabilities, kv_head, kv_grads, prefill_head, prefill,
 )
+from .prologue import (  # noqa: F401
+    rope_tables, qk_norm_rope_forward, qk_norm_rope_backward,
+)

@@ -528,3 +528,58 @@ def test_prefill_against_torch_sdpa_fp64():
         to = torch.nn.functional.scaled_dot_product_attention(Q, K, V, attn_mask=j <= L + i,
                                                               enable_gqa=True)
         assert np.allclose(o[b], to[0].numpy().transpose(1, 0, 2), rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------- prologue: QK norm + RoPE
+
+def test_prologue_position_zero_is_rms_norm():
+    """cos = 1, sin = 0: the output is torch's F.rms_norm (float64, no weight)."""
+    torch = pytest.importorskip("torch")
+    x = rnd((2, 5, 3, 16), 601)
+    c, s = np.ones((5, 8)), np.zeros((5, 8))
+    y = oracle.qk_norm_rope_forward(x, c, s, eps=1e-6)
+    ref = torch.nn.functional.rms_norm(torch.tensor(x), (16,), eps=1e-6).numpy()
+    assert np.allclose(y, ref, rtol=0, atol=1e-14)
+
+
+def test_prologue_rotation_keeps_the_rms_and_shifts_relative_positions():
+    """Each row's squared norm is D mean(x^2) / (mean(x^2) + eps); the dot
+    product of a rotated query at t1 and key at t2 depends on t1 - t2 only."""
+    D, T = 16, 12
+    x = rnd((1, T, 1, D), 611)
+    c, s = oracle.rope_tables(T, D)
+    y = oracle.qk_norm_rope_forward(x, c, s, eps=1e-6)
+    ms = np.mean(x * x, axis=-1)
+    assert np.allclose(np.sum(y * y, axis=-1), D * ms / (ms + 1e-6), rtol=1e-13, atol=0)
+    qv, kv = rnd((D,), 612), rnd((D,), 613)
+    Q = oracle.qk_norm_rope_forward(np.tile(qv, (1, T, 1, 1)), c, s)[0, :, 0]
+    K = oracle.qk_norm_rope_forward(np.tile(kv, (1, T, 1, 1)), c, s)[0, :, 0]
+    for t1, t2, u1, u2 in ((5, 2, 9, 6), (7, 7, 0, 0), (3, 8, 4, 9)):
+        assert abs(Q[t1] @ K[t2] - Q[u1] @ K[u2]) < 1e-12
+
+
+def test_prologue_rotation_angle_closed_form():
+    """Dimension pair i of row t turns by theta = t * 10000^(-2 i / D)."""
+    D, T = 8, 6
+    x = np.zeros((1, T, 1, D))
+    x[..., 1] = 1.0                 # z = e_1 * sqrt(D) (up to eps)
+    c, s = oracle.rope_tables(T, D)
+    y = oracle.qk_norm_rope_forward(x, c, s, eps=0.0)
+    th = np.arange(T) * 10000.0 ** (-2.0 / D)
+    assert np.allclose(y[0, :, 0, 1], np.sqrt(D) * np.cos(th), atol=1e-13)
+    assert np.allclose(y[0, :, 0, 1 + D // 2], np.sqrt(D) * np.sin(th), atol=1e-13)
+
+
+def test_prologue_backward_finite_differences():
+    x, dy = rnd((1, 4, 2, 8), 621), rnd((1, 4, 2, 8), 622)
+    c, s = oracle.rope_tables(4, 8)
+    g = oracle.qk_norm_rope_backward(x, dy, c, s, eps=1e-6)
+    eps = 1e-6
+    fd = np.zeros_like(x)
+    for pos in np.ndindex(x.shape):
+        xp, xm = x.copy(), x.copy()
+        xp[pos] += eps
+        xm[pos] -= eps
+        fd[pos] = (np.sum(oracle.qk_norm_rope_forward(xp, c, s) * dy)
+                   - np.sum(oracle.qk_norm_rope_forward(xm, c, s) * dy)) / (2 * eps)
+    assert np.allclose(g, fd, rtol=0, atol=1e-8)
