@@ -25,6 +25,11 @@ U[0, 1536] rows, T_cap 2048, d20 heads; the chat-prefill shape of the
 inference engine, sizes chosen here) is timed and reported under "prefill"
 (append + attention, FLOPs over the visible pairs).
 
+The attention prologue (RMS normalisation + rotary embedding of q and k at
+the d20 shape, forward and backward) is timed and reported under "prologue"
+(algorithmic bytes: q and k read and written once, plus the gradients read in
+the backward, plus the cos/sin tables).
+
 Grouped-query attention (--kv-heads, default 5: two query heads per key/value
 head, a choice of this benchmark; the pages give no key/value head count) is
 timed the same way on the d20 step and the decode and reported under "gqa".
@@ -176,6 +181,7 @@ def main():
     ap.add_argument("--window", type=int, default=1024,
                     help="sliding-window length for the extra windowed measurement (-1 = skip)")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-prologue", action="store_true")
     ap.add_argument("--kv-heads", type=int, default=5,
                     help="key/value heads for the extra grouped-query measurement (0 = skip)")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
@@ -379,6 +385,55 @@ def main():
                          "kernels": gk}
         log(f"gqa: {g_ms:.3f} ms  {g_tf:.1f} TFLOP/s  kernels {gk}")
         del kg, vg, dkg, dvg
+
+    # ---------------- prologue: QK norm + rotary embedding of q and k
+    if not args.no_prologue:
+        # any angle table serves for timing: seeded random angles
+        ct, sn = (torch.from_numpy(a).to(dev) for a in W.make_angle_tables(T, D // 2, seed=1))
+        yq, yk, rgq, rgk = (torch.empty_like(q) for _ in range(4))
+        rev = ev.create(4)
+        eps = ctypes.c_float(1e-6)
+
+        def rfwd():
+            st = lib.na_qk_norm_rope_fwd(ptr(q), ptr(k), ptr(yq), ptr(yk), ptr(ct), ptr(sn), None,
+                                         B, T, H, H, D, T, eps, P(stream))
+            if st:
+                raise RuntimeError(lib.na_last_error().decode())
+
+        def rbwd():  # do and v stand in for the gradients of the rotated q and k
+            st = lib.na_qk_norm_rope_bwd(ptr(q), ptr(k), ptr(do), ptr(v), ptr(rgq), ptr(rgk),
+                                         ptr(ct), ptr(sn), None, B, T, H, H, D, T, eps,
+                                         P(stream))
+            if st:
+                raise RuntimeError(lib.na_last_error().decode())
+
+        for _ in range(args.warmup):
+            rfwd()
+            rbwd()
+        torch.cuda.synchronize()
+        ev.record(rev[0], stream)
+        for _ in range(args.steps):
+            rfwd()
+        ev.record(rev[1], stream)
+        for _ in range(args.steps):
+            rbwd()
+        ev.record(rev[2], stream)
+        f_ms = ev.ms(rev[0], rev[1]) / args.steps
+        b_ms = ev.ms(rev[1], rev[2]) / args.steps
+        row_bytes = B * T * 2 * H * D * 2          # q and k, bf16
+        tab_bytes = 2 * T * (D // 2) * 4
+        fb, bb = 2 * row_bytes + tab_bytes, 3 * row_bytes + tab_bytes
+        result["prologue"] = {
+            "workload": f"QK norm + rotary embedding of q and k: B={B}, T={T}, H={H}, D={D}, "
+                        "bf16, fp32 (T, 64) cos/sin tables",
+            "fwd_ms": round(f_ms, 4), "bwd_ms": round(b_ms, 4),
+            "fwd_GB_per_s": round(fb / (f_ms * 1e-3) / 1e9, 1),
+            "bwd_GB_per_s": round(bb / (b_ms * 1e-3) / 1e9, 1),
+            "fwd_frac_hbm": round(fb / (f_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "bwd_frac_hbm": round(bb / (b_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "bytes_fwd": fb, "bytes_bwd": bb, "calls": args.steps}
+        log(f"prologue {result['prologue']}")
+        del yq, yk, rgq, rgk
 
     del q, k, v, do, o, dq, dk, dv, ws
     torch.cuda.empty_cache()

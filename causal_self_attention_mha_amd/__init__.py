@@ -14,6 +14,9 @@ Functions (names match the C entry points):
   attn_decode(q, k_cache, v_cache, seqlens) -> (o, lse)
   attn_prefill(q, k_new, v_new, k_cache, v_cache, cache_lens) -> (o, lse)
                                           (appends k_new, v_new to the caches in place)
+  qk_norm_rope_fwd(q, k, cos, sin)        -> (q_out, k_out)   (the prologue: RMS
+                                          norm + rotary embedding of q and k)
+  qk_norm_rope_bwd(q, k, dq_rot, dk_rot, cos, sin) -> (dq, dk)
 Each takes window=W (an int >= 0) for sliding-window attention (key j visible
 to query i iff i - W <= j <= i), which calls the *_window entry point;
 window=None is plain causal attention.  k and v (and the decode caches) may
@@ -29,7 +32,8 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["attn_fwd", "attn_bwd", "attn_decode", "attn_prefill", "decode_workspace_bytes",
+__all__ = ["attn_fwd", "attn_bwd", "attn_decode", "attn_prefill", "qk_norm_rope_fwd",
+           "qk_norm_rope_bwd", "decode_workspace_bytes",
            "bwd_workspace_bytes",
            "load_library",
            "library_path", "NAError", "HEAD_DIM"]
@@ -88,10 +92,15 @@ def load_library():
     lib.na_attn_decode_gqa.argtypes = [vp, vp, vp, vp, vp, f32p, i, i, i, i, i, i, vp, sz, vp,
                                        vp]
     lib.na_attn_prefill.argtypes = [vp, vp, vp, vp, vp, vp, vp, f32p, i, i, i, i, i, i, i, vp]
+    lib.na_qk_norm_rope_fwd.argtypes = [vp, vp, vp, vp, f32p, f32p, vp, i, i, i, i, i, i,
+                                        ctypes.c_float, vp]
+    lib.na_qk_norm_rope_bwd.argtypes = [vp, vp, vp, vp, vp, vp, f32p, f32p, vp, i, i, i, i, i,
+                                        i, ctypes.c_float, vp]
     for fn in ("na_attn_fwd", "na_attn_bwd", "na_attn_decode", "na_attn_fwd_f32",
                "na_attn_bwd_f32", "na_attn_bwd_timed", "na_attn_decode_timed",
                "na_attn_fwd_window", "na_attn_bwd_window", "na_attn_decode_window",
-               "na_attn_fwd_gqa", "na_attn_bwd_gqa", "na_attn_decode_gqa", "na_attn_prefill"):
+               "na_attn_fwd_gqa", "na_attn_bwd_gqa", "na_attn_decode_gqa", "na_attn_prefill",
+               "na_qk_norm_rope_fwd", "na_qk_norm_rope_bwd"):
         getattr(lib, fn).restype = ctypes.c_int
     lib.na_status_string.argtypes = [ctypes.c_int]
     lib.na_status_string.restype = ctypes.c_char_p
@@ -325,3 +334,59 @@ def attn_prefill(q, k_new, v_new, k_cache, v_cache, cache_lens, o=None, lse=None
                                _ptr(cache_lens), _ptr(o), _ptr(lse), B, T_q, H, Hk, D, T_cap,
                                -1 if window is None else window, _stream(q)))
     return o, lse
+
+
+def _check_prologue(q, k, cos, sin, pos_offset, extra=()):
+    import torch
+    _require(q.is_cuda and q.dtype == torch.bfloat16 and q.dim() == 4 and q.shape[-1] == HEAD_DIM,
+             "q must be a bf16 GPU tensor (B, T, H, 128)")
+    B, T, H, D = q.shape
+    _require(k.dim() == 4 and k.shape[:2] == (B, T) and k.shape[3] == D,
+             "k must be (B, T, H_kv, 128)")
+    for n, t, shape in (("q", q, q.shape), ("k", k, k.shape)) + tuple(extra):
+        _require(t.dtype == torch.bfloat16 and t.device == q.device and t.is_contiguous()
+                 and t.shape == shape, f"{n} must be contiguous bf16 {tuple(shape)} on {q.device}")
+    _require(cos.dim() == 2 and cos.shape[1] == D // 2 and cos.shape[0] >= T,
+             "cos must be (T_tab >= T, 64)")
+    for n, t in (("cos", cos), ("sin", sin)):
+        _require(t.dtype == torch.float32 and t.device == q.device and t.is_contiguous()
+                 and t.shape == cos.shape, f"{n} must be contiguous float32 {tuple(cos.shape)}")
+    if pos_offset is not None:
+        _require(pos_offset.dtype == torch.int32 and pos_offset.shape == (B,)
+                 and pos_offset.device == q.device and pos_offset.is_contiguous(),
+                 "pos_offset must be int32 [B] on the GPU")
+    return B, T, H, k.shape[2], D, cos.shape[0]
+
+
+def qk_norm_rope_fwd(q, k, cos, sin, pos_offset=None, eps=1e-6, q_out=None, k_out=None):
+    """RMS-normalise each head row of q and k, then rotate the pairs (i, i + 64)
+    by the angles whose cos/sin tables (T_tab, 64) float32 are given, at
+    positions t + pos_offset[b] (pos_offset int32 [B], clamped on the device
+    to [0, T_tab - T]; None for positions t).  Returns (q_out, k_out)."""
+    import torch
+    lib = load_library()
+    B, T, H, Hk, D, T_tab = _check_prologue(q, k, cos, sin, pos_offset)
+    q_out = torch.empty_like(q) if q_out is None else q_out
+    k_out = torch.empty_like(k) if k_out is None else k_out
+    _check(lib, "na_qk_norm_rope_fwd",
+           lib.na_qk_norm_rope_fwd(_ptr(q), _ptr(k), _ptr(q_out), _ptr(k_out), _ptr(cos), _ptr(sin),
+                                   _ptr(pos_offset), B, T, H, Hk, D, T_tab, float(eps),
+                                   _stream(q)))
+    return q_out, k_out
+
+
+def qk_norm_rope_bwd(q, k, dq_rot, dk_rot, cos, sin, pos_offset=None, eps=1e-6, dq=None,
+                     dk=None):
+    """Gradients of q and k through qk_norm_rope_fwd, given the gradients
+    dq_rot, dk_rot of its outputs.  Returns (dq, dk)."""
+    import torch
+    lib = load_library()
+    B, T, H, Hk, D, T_tab = _check_prologue(
+        q, k, cos, sin, pos_offset, (("dq_rot", dq_rot, q.shape), ("dk_rot", dk_rot, k.shape)))
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    _check(lib, "na_qk_norm_rope_bwd",
+           lib.na_qk_norm_rope_bwd(_ptr(q), _ptr(k), _ptr(dq_rot), _ptr(dk_rot), _ptr(dq), _ptr(dk),
+                                   _ptr(cos), _ptr(sin), _ptr(pos_offset), B, T, H, Hk, D, T_tab,
+                                   float(eps), _stream(q)))
+    return dq, dk

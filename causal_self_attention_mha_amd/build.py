@@ -32,7 +32,8 @@ COMMON = [
     "-I", os.path.join(ROOT, "include"),
 ]
 
-SOURCES = ["api.cpp", "fwd_bf16.hip", "bwd_bf16.hip", "decode_bf16.hip", "attn_f32.hip"]
+SOURCES = ["api.cpp", "fwd_bf16.hip", "bwd_bf16.hip", "decode_bf16.hip", "attn_f32.hip",
+           "prologue_bf16.hip"]
 
 
 def _compile(src: str, extra: list[str]) -> str:

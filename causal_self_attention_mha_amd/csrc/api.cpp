@@ -285,3 +285,64 @@ na_status na_attn_bwd_f32(const float* q, const float* k, const float* v, const 
 }
 
 }  // extern "C"
+
+namespace {
+
+na_status check_prologue(int B, int T, int H, int H_kv, int D, int T_tab, float eps) {
+  na_status st = check_sizes(B, T, H, D);
+  if (st) return st;
+  if ((st = check_sizes(B, T, H_kv, D))) return st;
+  if (T_tab < T) return fail(NA_ERR_INVALID_ARG, "T_tab=%d is smaller than T=%d", T_tab, T);
+  if ((long double)T_tab * D > 2147483647.0L)
+    return fail(NA_ERR_UNSUPPORTED, "the rotary tables (T_tab=%d) exceed 2^31-1 elements", T_tab);
+  if (!(eps >= 0.f) || eps > 3.0e38f)
+    return fail(NA_ERR_INVALID_ARG, "eps must be finite and >= 0");
+  return NA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+na_status na_qk_norm_rope_fwd(const void* q, const void* k, void* q_out, void* k_out,
+                              const float* cos_tab, const float* sin_tab, const int* pos_offset,
+                              int B, int T, int H, int H_kv, int D, int T_tab, float eps,
+                              void* stream) {
+  na_status st = check_prologue(B, T, H, H_kv, D, T_tab, eps);
+  if (st) return st;
+  if (pos_offset != nullptr)
+    st = check_ptrs({{q, "q"}, {k, "k"}, {cos_tab, "cos_tab"}, {sin_tab, "sin_tab"},
+                     {pos_offset, "pos_offset"}},
+                    {{q_out, "q_out"}, {k_out, "k_out"}});
+  else
+    st = check_ptrs({{q, "q"}, {k, "k"}, {cos_tab, "cos_tab"}, {sin_tab, "sin_tab"}},
+                    {{q_out, "q_out"}, {k_out, "k_out"}});
+  if (st) return st;
+  return hip_status(na::launch_qk_norm_rope_bf16(q, k, nullptr, nullptr, q_out, k_out, cos_tab,
+                                                 sin_tab, pos_offset, B, T, H, H_kv, T_tab, eps,
+                                                 false, (hipStream_t)stream),
+                    "na_qk_norm_rope_fwd");
+}
+
+na_status na_qk_norm_rope_bwd(const void* q, const void* k, const void* dq_rot,
+                              const void* dk_rot, void* dq, void* dk, const float* cos_tab,
+                              const float* sin_tab, const int* pos_offset, int B, int T, int H,
+                              int H_kv, int D, int T_tab, float eps, void* stream) {
+  na_status st = check_prologue(B, T, H, H_kv, D, T_tab, eps);
+  if (st) return st;
+  if (pos_offset != nullptr)
+    st = check_ptrs({{q, "q"}, {k, "k"}, {dq_rot, "dq_rot"}, {dk_rot, "dk_rot"},
+                     {cos_tab, "cos_tab"}, {sin_tab, "sin_tab"}, {pos_offset, "pos_offset"}},
+                    {{dq, "dq"}, {dk, "dk"}});
+  else
+    st = check_ptrs({{q, "q"}, {k, "k"}, {dq_rot, "dq_rot"}, {dk_rot, "dk_rot"},
+                     {cos_tab, "cos_tab"}, {sin_tab, "sin_tab"}},
+                    {{dq, "dq"}, {dk, "dk"}});
+  if (st) return st;
+  return hip_status(na::launch_qk_norm_rope_bf16(q, k, dq_rot, dk_rot, dq, dk, cos_tab, sin_tab,
+                                                 pos_offset, B, T, H, H_kv, T_tab, eps, true,
+                                                 (hipStream_t)stream),
+                    "na_qk_norm_rope_bwd");
+}
+
+}  // extern "C"

@@ -47,6 +47,16 @@ hipError_t launch_decode_bf16(const void* q, const void* kc, const void* vc, con
                               void* o, float* lse, int B, int H, int Hk, int T_cap, int window,
                               void* ws, hipStream_t s, hipEvent_t const* ev = nullptr);
 
+// bf16 QK normalisation + rotary embedding of q (B, T, H, D) and k (B, T, Hk, D)
+// at positions t + clamp(off[b], 0, T_tab - T) (off may be null: positions t)
+// of the fp32 (T_tab, D/2) cos/sin tables.  Forward: outq, outk = y(q), y(k)
+// (dyq, dyk unused).  Backward: outq, outk = gradients of the inputs given
+// dyq, dyk, the gradients of the outputs.
+hipError_t launch_qk_norm_rope_bf16(const void* q, const void* k, const void* dyq,
+                                    const void* dyk, void* outq, void* outk, const float* cos_t,
+                                    const float* sin_t, const int* off, int B, int T, int H,
+                                    int Hk, int T_tab, float eps, bool backward, hipStream_t s);
+
 // Compute units of the current device (cached per device; 256 if the query
 // fails).  Persistent grids size themselves from it.
 inline int device_cus() {

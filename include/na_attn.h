@@ -208,6 +208,41 @@ na_status na_attn_prefill(const void* q, const void* k_new, const void* v_new, v
                           int T_q, int H, int H_kv, int D, int T_cap, int window,
                           void* stream);
 
+/*
+ * Attention prologue: QK normalisation and rotary position embedding of the
+ * query and key heads, the two steps nanochat applies to q and k before
+ * attention (blog section 1 "GPT model", architecture features; the blog gives
+ * no formula).  Readings: for each head row x of D elements,
+ *   z = x / sqrt(mean(x^2) + eps)                  (RMS norm, no learned scale)
+ *   y_i      = z_i cos(th_{p,i}) - z_{i+D/2} sin(th_{p,i})
+ *   y_{i+D/2} = z_i sin(th_{p,i}) + z_{i+D/2} cos(th_{p,i}),  i < D/2,
+ * at position p = t + clamp(pos_offset[b], 0, T_tab - T) (p = t when
+ * pos_offset is NULL).  The angles come in as tables: cos_tab, sin_tab fp32
+ * (T_tab, D/2) contiguous, element p*(D/2) + i (the usual choice is
+ * th_{p,i} = p * 10000^(-2i/D)); the clamp matches na_attn_prefill's, so a
+ * prefill chunk is rotated at its cache positions by passing cache_lens.
+ * q: bf16 (B, T, H, D); k: bf16 (B, T, H_kv, D); q_out, k_out: bf16 outputs of
+ * the same shapes.  H, H_kv >= 1; T_tab >= T; eps >= 0 and finite.  One
+ * kernel; fp32 arithmetic, outputs rounded to nearest even.
+ */
+na_status na_qk_norm_rope_fwd(const void* q, const void* k, void* q_out, void* k_out,
+                              const float* cos_tab, const float* sin_tab, const int* pos_offset,
+                              int B, int T, int H, int H_kv, int D, int T_tab, float eps,
+                              void* stream);
+
+/*
+ * Backward of na_qk_norm_rope_fwd: given q, k (the forward's inputs) and
+ * dq_rot, dk_rot (the gradients of q_out, k_out, e.g. what na_attn_bwd
+ * returns), writes dq, dk (the gradients of q, k):
+ *   dz = R^T dy (the rotation by -th),  dx = r (dz - z mean(dz z)),
+ *   r = 1 / sqrt(mean(x^2) + eps), recomputed from x.
+ * Shapes, tables and checks as in the forward; dq, dk are bf16 outputs.
+ */
+na_status na_qk_norm_rope_bwd(const void* q, const void* k, const void* dq_rot,
+                              const void* dk_rot, void* dq, void* dk, const float* cos_tab,
+                              const float* sin_tab, const int* pos_offset, int B, int T, int H,
+                              int H_kv, int D, int T_tab, float eps, void* stream);
+
 /* Static text for a status code. */
 const char* na_status_string(na_status s);
 

@@ -35,7 +35,8 @@ def test_header_declares_the_entry_points():
               "na_attn_bwd_workspace_bytes", "na_attn_bwd_timed", "na_attn_decode_timed",
               "na_attn_fwd_f32", "na_attn_bwd_f32", "na_status_string", "na_last_error",
               "na_attn_fwd_window", "na_attn_bwd_window", "na_attn_decode_window",
-              "na_attn_fwd_gqa", "na_attn_bwd_gqa", "na_attn_decode_gqa", "na_attn_prefill"):
+              "na_attn_fwd_gqa", "na_attn_bwd_gqa", "na_attn_decode_gqa", "na_attn_prefill",
+              "na_qk_norm_rope_fwd", "na_qk_norm_rope_bwd"):
         assert s in syms
 
 
@@ -157,6 +158,30 @@ def test_prefill_checks_its_arguments(lib):
     bad = list(p)
     bad[5] = 0                   # no cache_lens
     assert call(bad) == INVALID
+
+
+def test_prologue_checks_its_arguments(lib):
+    p = [A + 0x100 * i for i in range(7)]  # q k q_out k_out cos sin pos_offset
+    fwd = lambda ptrs, T=8, H=2, Hk=2, D=128, T_tab=16, eps=1e-6: lib.na_qk_norm_rope_fwd(  # noqa
+        *ptrs, 1, T, H, Hk, D, T_tab, eps, None)
+    assert fwd(p, T_tab=4) == INVALID and b"T_tab" in lib.na_last_error()
+    assert fwd(p, D=64) == UNSUPPORTED
+    assert fwd(p, Hk=0) == INVALID
+    assert fwd(p, eps=-1.0) == INVALID and b"eps" in lib.na_last_error()
+    assert fwd(p, eps=float("nan")) == INVALID
+    bad = list(p)
+    bad[2] = bad[0]              # q_out aliases q
+    assert fwd(bad) == INVALID
+    bad = list(p)
+    bad[4] = 0                   # no cos table
+    assert fwd(bad) == INVALID
+    bad = list(p)
+    bad[5] = A + 8               # sin table not 16-byte aligned
+    assert fwd(bad) == INVALID
+    g = [A + 0x100 * i for i in range(9)]  # q k dq_rot dk_rot dq dk cos sin pos_offset
+    assert lib.na_qk_norm_rope_bwd(*g, 1, 8, 2, 2, 128, 4, 1e-6, None) == INVALID
+    g[4] = g[2]                  # dq aliases dq_rot
+    assert lib.na_qk_norm_rope_bwd(*g, 1, 8, 2, 2, 128, 16, 1e-6, None) == INVALID
 
 
 def test_bwd_workspace_bytes(lib):

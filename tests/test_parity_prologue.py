@@ -1,0 +1,173 @@
+"""GPU parity of the attention prologue (RMS normalisation + rotary embedding
+of the query and key heads, forward and backward) against the fp64 oracle,
+through the C ABI.  Cases: a single row, ragged T, grouped key heads, per
+sequence position offsets (clamped into the table), tables of standard
+RoPE angles and of random angles, all-zero rows, large magnitudes, the d20
+training shape on sampled positions, and the prologue chained with the
+attention forward and backward."""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from parity_util import BF16_MAX_ABS, BF16_REL_L2, assert_close, to_device, to_host
+
+pytestmark = pytest.mark.gpu
+
+EPS = 1e-6
+
+
+def tables(kind, T_tab, seed):
+    if kind == "rope":
+        c, s = oracle.rope_tables(T_tab, 128)
+        return c.astype(np.float32), s.astype(np.float32)
+    return W.make_angle_tables(T_tab, 64, seed)
+
+
+def positions(B, T, T_tab, offs):
+    if offs is None:
+        return [0] * B
+    return [min(max(int(o), 0), T_tab - T) for o in offs]
+
+
+def oracle_pair(xq, xk, gq, gk, c, s, starts, eps=EPS):
+    """Oracle forward and backward of q and k, sequence b at positions
+    starts[b] .. starts[b] + T - 1 of the tables."""
+    T = xq.shape[1]
+    out = {n: [] for n in ("yq", "yk", "dq", "dk")}
+    for b, p0 in enumerate(starts):
+        cb, sb = c[p0:p0 + T].astype(np.float64), s[p0:p0 + T].astype(np.float64)
+        out["yq"].append(oracle.qk_norm_rope_forward(xq[b:b + 1], cb, sb, eps))
+        out["yk"].append(oracle.qk_norm_rope_forward(xk[b:b + 1], cb, sb, eps))
+        out["dq"].append(oracle.qk_norm_rope_backward(xq[b:b + 1], gq[b:b + 1], cb, sb, eps))
+        out["dk"].append(oracle.qk_norm_rope_backward(xk[b:b + 1], gk[b:b + 1], cb, sb, eps))
+    return {n: np.concatenate(v, axis=0) for n, v in out.items()}
+
+
+def make_case(B, T, H, Hk, seed, scale=1.0, zero_rows=0):
+    tr = W.make_train_inputs("d20", B=B, T=T, H=H, seed=seed)
+    st = {"q": tr.q_store, "k": np.ascontiguousarray(tr.k_store[:, :, :Hk]),
+          "gq": tr.do_store, "gk": np.ascontiguousarray(tr.v_store[:, :, :Hk])}
+    val = {"q": tr.q.astype(np.float64), "k": tr.k[:, :, :Hk].astype(np.float64),
+           "gq": tr.do.astype(np.float64), "gk": tr.v[:, :, :Hk].astype(np.float64)}
+    if scale != 1.0:   # a power of two keeps the bf16 values exact
+        for n in ("q", "k"):
+            val[n] = val[n] * scale
+            st[n] = W.f32_to_bf16_bits(val[n].astype(np.float32))
+    if zero_rows:
+        rng = np.random.default_rng(seed + 7)
+        for n in ("q", "k"):
+            flat_v = val[n].reshape(-1, 128)
+            flat_s = st[n].reshape(-1, 128)
+            idx = rng.choice(flat_v.shape[0], size=zero_rows, replace=False)
+            flat_v[idx] = 0.0
+            flat_s[idx] = 0
+    return st, val
+
+
+def run_gpu(st, c, s, offs, dev, eps=EPS, host=True):
+    import torch
+    import causal_self_attention_mha_amd as na
+    q, k, gq, gk = (to_device(st[n], dev) for n in ("q", "k", "gq", "gk"))
+    ct, sn = torch.from_numpy(c).to(dev), torch.from_numpy(s).to(dev)
+    po = None if offs is None else torch.tensor(offs, dtype=torch.int32, device=dev)
+    yq, yk = na.qk_norm_rope_fwd(q, k, ct, sn, pos_offset=po, eps=eps)
+    dq, dk = na.qk_norm_rope_bwd(q, k, gq, gk, ct, sn, pos_offset=po, eps=eps)
+    torch.cuda.synchronize()
+    out = {"yq": yq, "yk": yk, "dq": dq, "dk": dk}
+    return {n: to_host(t) for n, t in out.items()} if host else out
+
+
+CASES = [  # B, T, H, Hk, T_tab, offsets, table kind
+    (1, 1, 1, 1, 1, None, "rope"),
+    (2, 37, 3, 1, 64, None, "rope"),
+    (2, 100, 10, 10, 100, None, "rope"),
+    (3, 50, 4, 2, 300, [0, 17, 290], "rope"),
+    (2, 64, 2, 2, 64, [-5, 10], "random"),
+    (4, 129, 6, 3, 2048, [1919, 0, 1000, 5000], "random"),
+]
+
+
+@pytest.mark.parametrize("B,T,H,Hk,T_tab,offs,kind", CASES)
+def test_prologue_shapes(dev, B, T, H, Hk, T_tab, offs, kind):
+    st, val = make_case(B, T, H, Hk, seed=7000 + T + H)
+    c, s = tables(kind, T_tab, seed=T_tab)
+    got = run_gpu(st, c, s, offs, dev)
+    ref = oracle_pair(val["q"], val["k"], val["gq"], val["gk"], c, s, positions(B, T, T_tab, offs))
+    for n in ("yq", "yk", "dq", "dk"):
+        assert_close(n, got[n], ref[n], BF16_REL_L2, BF16_MAX_ABS)
+
+
+def test_prologue_zero_rows_and_large_values(dev):
+    """All-zero head rows: zero outputs, and the gradient R^T dy / sqrt(eps)
+    (the normalisation's slope at zero, values near 1000 |dy|, so compared by
+    relative L2 only); rows scaled by 64 normalise like unscaled ones."""
+    c, s = tables("rope", 80, 0)
+    st, val = make_case(2, 80, 4, 2, seed=71, zero_rows=40)
+    got = run_gpu(st, c, s, None, dev)
+    ref = oracle_pair(val["q"], val["k"], val["gq"], val["gk"], c, s, [0, 0])
+    for y, d, x in (("yq", "dq", "q"), ("yk", "dk", "k")):
+        z = np.all(val[x] == 0, axis=-1)
+        assert z.sum() > 0 and np.all(got[y][z] == 0)
+        assert_close(f"{d} zero rows", got[d][z], ref[d][z], BF16_REL_L2)
+        assert_close(y, got[y], ref[y], BF16_REL_L2, BF16_MAX_ABS)
+        assert_close(f"{d} other rows", got[d][~z], ref[d][~z], BF16_REL_L2, BF16_MAX_ABS)
+    st2, val2 = make_case(2, 80, 4, 2, seed=72, scale=64.0)
+    got2 = run_gpu(st2, c, s, None, dev)
+    ref2 = oracle_pair(val2["q"], val2["k"], val2["gq"], val2["gk"], c, s, [0, 0])
+    for n in ("yq", "yk", "dq", "dk"):
+        assert_close(n, got2[n], ref2[n], BF16_REL_L2, BF16_MAX_ABS)
+
+
+def test_prologue_d20_sampled(dev):
+    """The d20 training shape (B=32, T=2048, H=10, D=128) with standard RoPE
+    tables, in the launch the benchmark times; the oracle checks 96 sampled
+    (b, t) positions, every head of each."""
+    B, T, H = 32, 2048, 10
+    tr = W.make_train_inputs("d20", seed=20)
+    assert tr.q.shape == (B, T, H, 128)
+    c, s = tables("rope", T, 0)
+    st = {"q": tr.q_store, "k": tr.k_store, "gq": tr.do_store, "gk": tr.v_store}
+    got = run_gpu(st, c, s, None, dev, host=False)
+    rng = np.random.default_rng(5)
+    bs, ts = rng.integers(0, B, 96), rng.integers(0, T, 96)
+    ts[:4] = [0, 1, T - 1, T // 2]
+    for b, t in zip(bs, ts):
+        sl = (slice(b, b + 1), slice(t, t + 1))
+        ref = oracle_pair(tr.q[sl].astype(np.float64), tr.k[sl].astype(np.float64),
+                          tr.do[sl].astype(np.float64), tr.v[sl].astype(np.float64),
+                          c[t:t + 1], s[t:t + 1], [0])
+        for n in ("yq", "yk", "dq", "dk"):
+            assert_close(f"{n}[{b},{t}]", to_host(got[n][sl]), ref[n], BF16_REL_L2,
+                         BF16_MAX_ABS)
+
+
+def test_prologue_chained_with_attention(dev):
+    """prologue -> attention forward -> attention backward -> prologue backward
+    on the GPU against the same chain through the oracle: o and the gradients
+    of the pre-normalisation q and k."""
+    import torch
+    import causal_self_attention_mha_amd as na
+    B, T, H = 2, 96, 2
+    tr = W.make_train_inputs("d20", B=B, T=T, H=H, seed=77)
+    c, s = tables("rope", T, 0)
+    q, k, v, do = (to_device(a, dev) for a in (tr.q_store, tr.k_store, tr.v_store, tr.do_store))
+    ct, sn = torch.from_numpy(c).to(dev), torch.from_numpy(s).to(dev)
+    qr, kr = na.qk_norm_rope_fwd(q, k, ct, sn)
+    o, lse = na.attn_fwd(qr, kr, v)
+    dqr, dkr, dv, _ = na.attn_bwd(qr, kr, v, o, do, lse)
+    dq, dk = na.qk_norm_rope_bwd(q, k, dqr, dkr, ct, sn)
+    torch.cuda.synchronize()
+    c64, s64 = c.astype(np.float64), s.astype(np.float64)
+    rq = oracle.qk_norm_rope_forward(tr.q.astype(np.float64), c64, s64, EPS)
+    rk = oracle.qk_norm_rope_forward(tr.k.astype(np.float64), c64, s64, EPS)
+    ro, rl = oracle.forward(rq, rk, tr.v)
+    rdq, rdk, rdv, _ = oracle.backward(rq, rk, tr.v, tr.do)
+    assert_close("o", to_host(o), ro, BF16_REL_L2, BF16_MAX_ABS)
+    assert_close("dv", to_host(dv), rdv, BF16_REL_L2, BF16_MAX_ABS)
+    assert_close("dq", to_host(dq),
+                 oracle.qk_norm_rope_backward(tr.q.astype(np.float64), rdq, c64, s64, EPS),
+                 BF16_REL_L2, BF16_MAX_ABS)
+    assert_close("dk", to_host(dk),
+                 oracle.qk_norm_rope_backward(tr.k.astype(np.float64), rdk, c64, s64, EPS),
+                 BF16_REL_L2, BF16_MAX_ABS)

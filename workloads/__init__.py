@@ -33,6 +33,7 @@ __all__ = [
     "Config", "CONFIGS", "HEADLINE", "DECODE",
     "f32_to_bf16_bits", "bf16_bits_to_f32",
     "TrainInputs", "DecodeInputs", "make_train_inputs", "make_decode_inputs",
+    "make_angle_tables",
 ]
 
 
@@ -179,3 +180,12 @@ def make_decode_inputs(cfg: Config | str = DECODE, *, B: int | None = None,
     k, ks = _draw(rng, (B, T_cap, H, cfg.D), cfg.qkv_scale, cfg.dtype)
     v, vs = _draw(rng, (B, T_cap, H, cfg.D), cfg.qkv_scale, cfg.dtype)
     return DecodeInputs(cfg, lens, q, k, v, qs, ks, vs)
+
+
+def make_angle_tables(T_tab: int, half: int = 64, seed: int = 0):
+    """cos and sin (T_tab, half) float32 of angles drawn uniformly from
+    [-pi, pi): arbitrary rotation tables for the QK-norm + rotary prologue,
+    whose kernels take the tables as inputs.  Returns (cos, sin) float32."""
+    rng = np.random.default_rng(seed)
+    a = rng.uniform(-np.pi, np.pi, size=(T_tab, half))
+    return np.cos(a).astype(np.float32), np.sin(a).astype(np.float32)
