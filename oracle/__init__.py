@@ -13,5 +13,6 @@ from .attention import (  # noqa: F401
     decode_head, decode, causal_probabilities, kv_head, kv_grads, prefill_head, prefill,
 )
 from .prologue import (  # noqa: F401
-    rope_tables, qk_norm_rope_forward, qk_norm_rope_backward,
+    rope_tables, qk_norm_rope_forward, qk_norm_rope_backward, value_gate_forward,
+    value_gate_backward,
 )

@@ -19,13 +19,22 @@ taken here are the plainest ones:
     t * base^(-2 i / D) with base 10000 in the tests and the benchmark);
   * the rotation keeps the RMS, so normalising before or after it is the same.
 
+The value-embedding gate (ResFormer value residual, same blog and section,
+"value embeddings"): on the layers that carry one, a learned value embedding
+ve of each key/value head is mixed into v with a per-head gate that depends
+on the input: v' = v + 3 sigmoid(g) ve, where g (B, T, H_kv) is the output
+of the small ve_gate projection of the first input channels (that projection
+is an ordinary matrix product upstream; the gate logits g are taken as an
+input here).
+
 Plain float64 numpy, one formula per step.
 """
 from __future__ import annotations
 
 import numpy as np
 
-__all__ = ["rope_tables", "qk_norm_rope_forward", "qk_norm_rope_backward"]
+__all__ = ["rope_tables", "qk_norm_rope_forward", "qk_norm_rope_backward",
+           "value_gate_forward", "value_gate_backward"]
 
 
 def rope_tables(T: int, D: int, base: float = 10000.0, pos0: int = 0):
@@ -63,3 +72,23 @@ def qk_norm_rope_backward(x, dy, cos, sin, eps: float = 1e-6):
     d1, d2 = dy[..., :D // 2], dy[..., D // 2:]
     dz = np.concatenate([d1 * c + d2 * s, -d1 * s + d2 * c], axis=-1)
     return r * (dz - z * np.mean(dz * z, axis=-1, keepdims=True))
+
+
+def _sigmoid(g):
+    return 1.0 / (1.0 + np.exp(-np.asarray(g, dtype=np.float64)))
+
+
+def value_gate_forward(v, ve, g):
+    """v, ve (B, T, H_kv, D); g (B, T, H_kv).  v + 3 sigmoid(g) ve, float64."""
+    return np.asarray(v, np.float64) + 3.0 * _sigmoid(g)[..., None] * np.asarray(ve, np.float64)
+
+
+def value_gate_backward(ve, g, dv_out):
+    """Gradients of sum(v' * dv_out): dv = dv_out, dve = 3 sigmoid(g) dv_out,
+    dg = 3 sigmoid(g) (1 - sigmoid(g)) <ve, dv_out> over D.  Returns
+    (dve, dg)."""
+    sg = _sigmoid(g)
+    dv_out = np.asarray(dv_out, np.float64)
+    dve = 3.0 * sg[..., None] * dv_out
+    dg = 3.0 * sg * (1.0 - sg) * np.sum(np.asarray(ve, np.float64) * dv_out, axis=-1)
+    return dve, dg

@@ -583,3 +583,42 @@ def test_prologue_backward_finite_differences():
         fd[pos] = (np.sum(oracle.qk_norm_rope_forward(xp, c, s) * dy)
                    - np.sum(oracle.qk_norm_rope_forward(xm, c, s) * dy)) / (2 * eps)
     assert np.allclose(g, fd, rtol=0, atol=1e-8)
+
+
+def test_value_gate_limits_and_midpoint():
+    """g -> -inf leaves v; g -> +inf adds 3 ve; g = 0 adds 1.5 ve exactly."""
+    v, ve = rnd((2, 3, 2, 8), 631), rnd((2, 3, 2, 8), 632)
+    assert np.array_equal(oracle.value_gate_forward(v, ve, np.full((2, 3, 2), -800.0)), v)
+    assert np.allclose(oracle.value_gate_forward(v, ve, np.full((2, 3, 2), 800.0)), v + 3 * ve,
+                       rtol=0, atol=1e-15)
+    assert np.array_equal(oracle.value_gate_forward(v, ve, np.zeros((2, 3, 2))), v + 1.5 * ve)
+
+
+def test_value_gate_backward_matches_torch_autograd():
+    """An independent routine: torch's sigmoid and autograd in float64."""
+    torch = pytest.importorskip("torch")
+    v, ve = rnd((2, 5, 3, 16), 641), rnd((2, 5, 3, 16), 642)
+    g, dy = rnd((2, 5, 3), 643, 2.0), rnd((2, 5, 3, 16), 644)
+    tv, tve, tg = (torch.tensor(a, requires_grad=True) for a in (v, ve, g))
+    out = tv + 3 * torch.sigmoid(tg).unsqueeze(-1) * tve
+    out.backward(torch.tensor(dy))
+    assert np.allclose(oracle.value_gate_forward(v, ve, g), out.detach().numpy(), rtol=0,
+                       atol=1e-14)
+    dve, dg = oracle.value_gate_backward(ve, g, dy)
+    assert np.allclose(tv.grad.numpy(), dy)   # dv is dv_out itself
+    assert np.allclose(dve, tve.grad.numpy(), rtol=0, atol=1e-14)
+    assert np.allclose(dg, tg.grad.numpy(), rtol=0, atol=1e-13)
+
+
+def test_value_gate_backward_finite_differences():
+    ve, g, dy = rnd((1, 3, 2, 4), 651), rnd((1, 3, 2), 652), rnd((1, 3, 2, 4), 653)
+    v = rnd((1, 3, 2, 4), 654)
+    _, dg = oracle.value_gate_backward(ve, g, dy)
+    eps = 1e-6
+    for pos in np.ndindex(g.shape):
+        gp, gm = g.copy(), g.copy()
+        gp[pos] += eps
+        gm[pos] -= eps
+        fd = (np.sum(oracle.value_gate_forward(v, ve, gp) * dy)
+              - np.sum(oracle.value_gate_forward(v, ve, gm) * dy)) / (2 * eps)
+        assert abs(fd - dg[pos]) < 1e-8
