@@ -26,9 +26,9 @@ inference engine, sizes chosen here) is timed and reported under "prefill"
 (append + attention, FLOPs over the visible pairs).
 
 The attention prologue (RMS normalisation + rotary embedding of q and k at
-the d20 shape, forward and backward) is timed and reported under "prologue"
-(algorithmic bytes: q and k read and written once, plus the gradients read in
-the backward, plus the cos/sin tables).
+the d20 shape, forward and backward, and the value-embedding gate on the d20
+key/value heads) is timed and reported under "prologue" (algorithmic bytes:
+every tensor read or written once, plus the cos/sin tables).
 
 Grouped-query attention (--kv-heads, default 5: two query heads per key/value
 head, a choice of this benchmark; the pages give no key/value head count) is
@@ -420,6 +420,36 @@ def main():
         ev.record(rev[2], stream)
         f_ms = ev.ms(rev[0], rev[1]) / args.steps
         b_ms = ev.ms(rev[1], rev[2]) / args.steps
+        # value-embedding gate on the d20 key/value heads: v, ve = q, k stand-ins
+        gt = dev_t(W.make_gate_logits(B, T, H, seed=2)[1])
+
+        def gfwd():
+            st = lib.na_value_gate_fwd(ptr(v), ptr(k), ptr(gt), ptr(yq), B, T, H, D, P(stream))
+            if st:
+                raise RuntimeError(lib.na_last_error().decode())
+
+        def gbwd():
+            st = lib.na_value_gate_bwd(ptr(k), ptr(gt), ptr(do), ptr(rgq), ptr(yk), B, T, H, D,
+                                       P(stream))
+            if st:
+                raise RuntimeError(lib.na_last_error().decode())
+
+        for _ in range(args.warmup):
+            gfwd()
+            gbwd()
+        ev.record(rev[0], stream)
+        for _ in range(args.steps):
+            gfwd()
+        ev.record(rev[1], stream)
+        for _ in range(args.steps):
+            gbwd()
+        ev.record(rev[2], stream)
+        torch.cuda.synchronize()
+        gf_ms = ev.ms(rev[0], rev[1]) / args.steps
+        gb_ms = ev.ms(rev[1], rev[2]) / args.steps
+        vrow = B * T * H * D * 2
+        gbytes = B * T * H * 2
+        gfb, gbb = 3 * vrow + gbytes, 3 * vrow + 2 * gbytes
         row_bytes = B * T * 2 * H * D * 2          # q and k, bf16
         tab_bytes = 2 * T * (D // 2) * 4
         fb, bb = 2 * row_bytes + tab_bytes, 3 * row_bytes + tab_bytes
@@ -431,9 +461,14 @@ def main():
             "bwd_GB_per_s": round(bb / (b_ms * 1e-3) / 1e9, 1),
             "fwd_frac_hbm": round(fb / (f_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
             "bwd_frac_hbm": round(bb / (b_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-            "bytes_fwd": fb, "bytes_bwd": bb, "calls": args.steps}
+            "bytes_fwd": fb, "bytes_bwd": bb,
+            "value_gate": {"fwd_ms": round(gf_ms, 4), "bwd_ms": round(gb_ms, 4),
+                           "fwd_GB_per_s": round(gfb / (gf_ms * 1e-3) / 1e9, 1),
+                           "bwd_GB_per_s": round(gbb / (gb_ms * 1e-3) / 1e9, 1),
+                           "bytes_fwd": gfb, "bytes_bwd": gbb},
+            "calls": args.steps}
         log(f"prologue {result['prologue']}")
-        del yq, yk, rgq, rgk
+        del yq, yk, rgq, rgk, gt
 
     del q, k, v, do, o, dq, dk, dv, ws
     torch.cuda.empty_cache()

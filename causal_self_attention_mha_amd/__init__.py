@@ -17,6 +17,8 @@ Functions (names match the C entry points):
   qk_norm_rope_fwd(q, k, cos, sin)        -> (q_out, k_out)   (the prologue: RMS
                                           norm + rotary embedding of q and k)
   qk_norm_rope_bwd(q, k, dq_rot, dk_rot, cos, sin) -> (dq, dk)
+  value_gate_fwd(v, ve, gate)             -> v + 3 sigmoid(gate) ve
+  value_gate_bwd(ve, gate, dv_out)        -> (dve, dgate)   (dv is dv_out)
 Each takes window=W (an int >= 0) for sliding-window attention (key j visible
 to query i iff i - W <= j <= i), which calls the *_window entry point;
 window=None is plain causal attention.  k and v (and the decode caches) may
@@ -33,7 +35,7 @@ import ctypes
 import os
 
 __all__ = ["attn_fwd", "attn_bwd", "attn_decode", "attn_prefill", "qk_norm_rope_fwd",
-           "qk_norm_rope_bwd", "decode_workspace_bytes",
+           "qk_norm_rope_bwd", "value_gate_fwd", "value_gate_bwd", "decode_workspace_bytes",
            "bwd_workspace_bytes",
            "load_library",
            "library_path", "NAError", "HEAD_DIM"]
@@ -94,13 +96,16 @@ def load_library():
     lib.na_attn_prefill.argtypes = [vp, vp, vp, vp, vp, vp, vp, f32p, i, i, i, i, i, i, i, vp]
     lib.na_qk_norm_rope_fwd.argtypes = [vp, vp, vp, vp, f32p, f32p, vp, i, i, i, i, i, i,
                                         ctypes.c_float, vp]
+    lib.na_value_gate_fwd.argtypes = [vp, vp, vp, vp, i, i, i, i, vp]
+    lib.na_value_gate_bwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, vp]
     lib.na_qk_norm_rope_bwd.argtypes = [vp, vp, vp, vp, vp, vp, f32p, f32p, vp, i, i, i, i, i,
                                         i, ctypes.c_float, vp]
     for fn in ("na_attn_fwd", "na_attn_bwd", "na_attn_decode", "na_attn_fwd_f32",
                "na_attn_bwd_f32", "na_attn_bwd_timed", "na_attn_decode_timed",
                "na_attn_fwd_window", "na_attn_bwd_window", "na_attn_decode_window",
                "na_attn_fwd_gqa", "na_attn_bwd_gqa", "na_attn_decode_gqa", "na_attn_prefill",
-               "na_qk_norm_rope_fwd", "na_qk_norm_rope_bwd"):
+               "na_qk_norm_rope_fwd", "na_qk_norm_rope_bwd", "na_value_gate_fwd",
+               "na_value_gate_bwd"):
         getattr(lib, fn).restype = ctypes.c_int
     lib.na_status_string.argtypes = [ctypes.c_int]
     lib.na_status_string.restype = ctypes.c_char_p
@@ -390,3 +395,45 @@ def qk_norm_rope_bwd(q, k, dq_rot, dk_rot, cos, sin, pos_offset=None, eps=1e-6, 
                                    _ptr(cos), _ptr(sin), _ptr(pos_offset), B, T, H, Hk, D, T_tab,
                                    float(eps), _stream(q)))
     return dq, dk
+
+
+def _check_value_gate(names, rows, gate):
+    import torch
+    ref = rows[0]
+    _require(ref.is_cuda and ref.dtype == torch.bfloat16 and ref.dim() == 4
+             and ref.shape[-1] == HEAD_DIM, f"{names[0]} must be a bf16 GPU tensor "
+             "(B, T, H_kv, 128)")
+    for n, t in zip(names, rows):
+        _require(t.dtype == torch.bfloat16 and t.device == ref.device and t.is_contiguous()
+                 and t.shape == ref.shape, f"{n} must be contiguous bf16 {tuple(ref.shape)}")
+    _require(gate.dtype == torch.bfloat16 and gate.device == ref.device and gate.is_contiguous()
+             and tuple(gate.shape) == tuple(ref.shape[:3]),
+             f"gate must be contiguous bf16 {tuple(ref.shape[:3])}")
+    return tuple(ref.shape)
+
+
+def value_gate_fwd(v, ve, gate, v_out=None):
+    """v + 3 sigmoid(gate) ve for v, ve (B, T, H_kv, 128) bf16 and gate
+    logits (B, T, H_kv) bf16."""
+    import torch
+    lib = load_library()
+    B, T, Hk, D = _check_value_gate(("v", "ve"), (v, ve), gate)
+    v_out = torch.empty_like(v) if v_out is None else v_out
+    _check(lib, "na_value_gate_fwd",
+           lib.na_value_gate_fwd(_ptr(v), _ptr(ve), _ptr(gate), _ptr(v_out), B, T, Hk, D,
+                                 _stream(v)))
+    return v_out
+
+
+def value_gate_bwd(ve, gate, dv_out, dve=None, dgate=None):
+    """Gradients through value_gate_fwd given dv_out: returns (dve, dgate); the
+    gradient of v is dv_out itself."""
+    import torch
+    lib = load_library()
+    B, T, Hk, D = _check_value_gate(("ve", "dv_out"), (ve, dv_out), gate)
+    dve = torch.empty_like(ve) if dve is None else dve
+    dgate = torch.empty_like(gate) if dgate is None else dgate
+    _check(lib, "na_value_gate_bwd",
+           lib.na_value_gate_bwd(_ptr(ve), _ptr(gate), _ptr(dv_out), _ptr(dve), _ptr(dgate), B, T,
+                                 Hk, D, _stream(ve)))
+    return dve, dgate

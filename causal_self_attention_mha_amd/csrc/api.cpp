@@ -345,4 +345,27 @@ na_status na_qk_norm_rope_bwd(const void* q, const void* k, const void* dq_rot,
                     "na_qk_norm_rope_bwd");
 }
 
+na_status na_value_gate_fwd(const void* v, const void* ve, const void* gate, void* v_out, int B,
+                            int T, int H_kv, int D, void* stream) {
+  na_status st = check_sizes(B, T, H_kv, D);
+  if (st) return st;
+  st = check_ptrs({{v, "v"}, {ve, "ve"}, {gate, "gate"}}, {{v_out, "v_out"}});
+  if (st) return st;
+  return hip_status(na::launch_value_gate_bf16(v, ve, gate, v_out, nullptr, B, T, H_kv, false,
+                                               (hipStream_t)stream),
+                    "na_value_gate_fwd");
+}
+
+na_status na_value_gate_bwd(const void* ve, const void* gate, const void* dv_out, void* dve,
+                            void* dgate, int B, int T, int H_kv, int D, void* stream) {
+  na_status st = check_sizes(B, T, H_kv, D);
+  if (st) return st;
+  st = check_ptrs({{ve, "ve"}, {gate, "gate"}, {dv_out, "dv_out"}},
+                  {{dve, "dve"}, {dgate, "dgate"}});
+  if (st) return st;
+  return hip_status(na::launch_value_gate_bf16(dv_out, ve, gate, dve, dgate, B, T, H_kv, true,
+                                               (hipStream_t)stream),
+                    "na_value_gate_bwd");
+}
+
 }  // extern "C"

@@ -57,6 +57,13 @@ hipError_t launch_qk_norm_rope_bf16(const void* q, const void* k, const void* dy
                                     const float* sin_t, const int* off, int B, int T, int H,
                                     int Hk, int T_tab, float eps, bool backward, hipStream_t s);
 
+// bf16 value-embedding gate over (B, T, Hk, D) rows with gate logits g (B, T, Hk).
+// Forward (a = v): out = v + 3 sigmoid(g) ve.  Backward (a = dv'):
+// out = dve = 3 sigmoid(g) dv', dgate = 3 sigmoid(g) (1 - sigmoid(g)) <ve, dv'>.
+hipError_t launch_value_gate_bf16(const void* a, const void* ve, const void* gate, void* out,
+                                  void* dgate, int B, int T, int Hk, bool backward,
+                                  hipStream_t s);
+
 // Compute units of the current device (cached per device; 256 if the query
 // fails).  Persistent grids size themselves from it.
 inline int device_cus() {

@@ -133,7 +133,71 @@ __global__ __launch_bounds__(256) void qk_norm_rope_kernel(
   }
 }
 
+// Value-embedding gate (ResFormer value residual, same blog and section):
+// v' = v + 3 sigmoid(g) ve per key/value head row, g (B, T, Hk) the gate
+// logits.  Backward: dv = dv' (the caller reuses it, nothing is written),
+// dve = 3 sigmoid(g) dv', dg = 3 sigmoid(g) (1 - sigmoid(g)) <ve, dv'>.
+// 16 lanes per row as above, kRowsAhead consecutive rows per 16-lane group.
+template <bool BWD>
+__global__ __launch_bounds__(256) void value_gate_kernel(const u16* __restrict__ a,
+                                                         const u16* __restrict__ ve,
+                                                         const u16* __restrict__ gate,
+                                                         u16* __restrict__ out,
+                                                         u16* __restrict__ dgate, long rows) {
+  const int lane = threadIdx.x & 15;
+  const long r0 = ((long)blockIdx.x * (blockDim.x >> 4) + (threadIdx.x >> 4)) * kRowsAhead;
+  uint4 av[kRowsAhead], ev[kRowsAhead];
+  float gv[kRowsAhead];
+#pragma unroll
+  for (int u = 0; u < kRowsAhead; ++u)
+    if (r0 + u < rows) {
+      const size_t o = (size_t)(r0 + u) * kHeadDim + lane * 8;
+      av[u] = ld16(a + o);
+      ev[u] = ld16(ve + o);
+      gv[u] = bf16_to_f32(gate[r0 + u]);
+    }
+#pragma unroll
+  for (int u = 0; u < kRowsAhead; ++u) {
+    if (r0 + u >= rows) break;
+    const float sg = __builtin_amdgcn_rcpf(1.f + fast_exp2(-gv[u] * 1.4426950408889634f));
+    float x[8], e[8], y[8];
+    unpack8(av[u], x);
+    unpack8(ev[u], e);
+    if (!BWD) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) y[i] = fmaf(3.f * sg, e[i], x[i]);
+    } else {
+      float dot = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        y[i] = 3.f * sg * x[i];
+        dot = fmaf(e[i], x[i], dot);
+      }
+      dot = sum16(dot);
+      if (lane == 0) dgate[r0 + u] = __builtin_bit_cast(u16, to_bf16(3.f * sg * (1.f - sg) * dot));
+    }
+    st16_stream(out + (size_t)(r0 + u) * kHeadDim + lane * 8, pack8(y));
+  }
+}
+
 }  // namespace
+
+hipError_t launch_value_gate_bf16(const void* a, const void* ve, const void* gate, void* out,
+                                  void* dgate, int B, int T, int Hk, bool backward,
+                                  hipStream_t s) {
+  const long rows = (long)B * T * Hk;
+  const long per_wg = 16 * kRowsAhead;
+  const dim3 grid((unsigned)((rows + per_wg - 1) / per_wg)), block(256);
+  auto ca = static_cast<const u16*>(a), cv = static_cast<const u16*>(ve),
+       cg = static_cast<const u16*>(gate);
+  if (backward)
+    hipLaunchKernelGGL(value_gate_kernel<true>, grid, block, 0, s, ca, cv, cg,
+                       static_cast<u16*>(out), static_cast<u16*>(dgate), rows);
+  else
+    hipLaunchKernelGGL(value_gate_kernel<false>, grid, block, 0, s, ca, cv, cg,
+                       static_cast<u16*>(out), nullptr, rows);
+  return hipGetLastError();
+}
 
 hipError_t launch_qk_norm_rope_bf16(const void* q, const void* k, const void* dyq,
                                     const void* dyk, void* outq, void* outk, const float* cos_t,

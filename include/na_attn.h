@@ -243,6 +243,30 @@ na_status na_qk_norm_rope_bwd(const void* q, const void* k, const void* dq_rot,
                               const float* sin_tab, const int* pos_offset, int B, int T, int H,
                               int H_kv, int D, int T_tab, float eps, void* stream);
 
+/*
+ * Value-embedding gate (ResFormer value residual; blog section 1 "GPT model",
+ * value embeddings): on the layers that carry a value embedding, each
+ * key/value head's v is mixed with the embedding ve through a per-head gate
+ * that depends on the input,
+ *   v_out = v + 3 sigmoid(gate) ve,
+ * where gate (B, T, H_kv) holds the logits of the small ve_gate projection
+ * (an ordinary matrix product upstream, not part of this call).
+ * v, ve, v_out: bf16 (B, T, H_kv, D); gate: bf16 (B, T, H_kv).  One kernel,
+ * fp32 arithmetic.
+ */
+na_status na_value_gate_fwd(const void* v, const void* ve, const void* gate, void* v_out, int B,
+                            int T, int H_kv, int D, void* stream);
+
+/*
+ * Backward of na_value_gate_fwd given dv_out, the gradient of v_out (e.g. the
+ * dv that na_attn_bwd returns): the gradient of v is dv_out itself (nothing is
+ * written for it); dve = 3 sigmoid(gate) dv_out (bf16 (B, T, H_kv, D)) and
+ * dgate = 3 sigmoid(gate) (1 - sigmoid(gate)) sum_d ve dv_out (bf16
+ * (B, T, H_kv)).  One kernel.
+ */
+na_status na_value_gate_bwd(const void* ve, const void* gate, const void* dv_out, void* dve,
+                            void* dgate, int B, int T, int H_kv, int D, void* stream);
+
 /* Static text for a status code. */
 const char* na_status_string(na_status s);
 

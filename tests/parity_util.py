@@ -7,6 +7,10 @@ import numpy as np
 F32_REL_L2 = 1e-5
 BF16_REL_L2 = 1e-2
 BF16_MAX_ABS = 2e-2
+# For bf16 outputs whose magnitude reaches past 4 (where one bf16 step is
+# 2^-5 or more, so rounding alone exceeds BF16_MAX_ABS), the element bound
+# is max(BF16_MAX_ABS, BF16_STEP_REL * |ref|): one bf16 step at |ref|.
+BF16_STEP_REL = 2.0 ** -7
 
 
 def to_device(store, dev):
@@ -45,3 +49,18 @@ def assert_close(name, x, ref, rel, mabs=None):
     if mabs is not None:
         assert a <= mabs, msg
     return r, a
+
+
+def assert_close_scaled(name, x, ref, rel):
+    """rel-L2 <= rel and, element by element,
+    |x - ref| <= max(BF16_MAX_ABS, BF16_STEP_REL * |ref|)."""
+    assert np.all(np.isfinite(x)), f"{name}: non-finite values"
+    x = np.asarray(x, np.float64)
+    ref = np.asarray(ref, np.float64)
+    r = rel_l2(x, ref)
+    excess = np.abs(x - ref) - np.maximum(BF16_MAX_ABS, BF16_STEP_REL * np.abs(ref))
+    msg = f"{name}: rel_l2={r:.3e} (<= {rel:g}) worst element excess={excess.max():.3e} (<= 0)"
+    print(msg)
+    assert r <= rel, msg
+    assert excess.max() <= 0, msg
+    return r

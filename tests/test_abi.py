@@ -36,7 +36,8 @@ def test_header_declares_the_entry_points():
               "na_attn_fwd_f32", "na_attn_bwd_f32", "na_status_string", "na_last_error",
               "na_attn_fwd_window", "na_attn_bwd_window", "na_attn_decode_window",
               "na_attn_fwd_gqa", "na_attn_bwd_gqa", "na_attn_decode_gqa", "na_attn_prefill",
-              "na_qk_norm_rope_fwd", "na_qk_norm_rope_bwd"):
+              "na_qk_norm_rope_fwd", "na_qk_norm_rope_bwd", "na_value_gate_fwd",
+              "na_value_gate_bwd"):
         assert s in syms
 
 
@@ -182,6 +183,16 @@ def test_prologue_checks_its_arguments(lib):
     assert lib.na_qk_norm_rope_bwd(*g, 1, 8, 2, 2, 128, 4, 1e-6, None) == INVALID
     g[4] = g[2]                  # dq aliases dq_rot
     assert lib.na_qk_norm_rope_bwd(*g, 1, 8, 2, 2, 128, 16, 1e-6, None) == INVALID
+
+
+def test_value_gate_checks_its_arguments(lib):
+    p = [A + 0x100 * i for i in range(5)]
+    assert lib.na_value_gate_fwd(*p[:4], 1, 8, 2, 64, None) == UNSUPPORTED
+    assert lib.na_value_gate_fwd(*p[:4], 1, 8, 0, 128, None) == INVALID
+    assert lib.na_value_gate_fwd(p[0], p[1], p[2], p[0], 1, 8, 2, 128, None) == INVALID  # alias
+    assert lib.na_value_gate_fwd(p[0], p[1], 0, p[3], 1, 8, 2, 128, None) == INVALID
+    assert lib.na_value_gate_bwd(p[0], p[1], p[2], p[3], p[3], 1, 8, 2, 128, None) == INVALID
+    assert lib.na_value_gate_bwd(p[0], p[1], p[2], p[3], A + 2, 1, 8, 2, 128, None) == INVALID
 
 
 def test_bwd_workspace_bytes(lib):

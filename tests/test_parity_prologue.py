@@ -1,6 +1,6 @@
 """GPU parity of the attention prologue (RMS normalisation + rotary embedding
-of the query and key heads, forward and backward) against the fp64 oracle,
-through the C ABI.  Cases: a single row, ragged T, grouped key heads, per
+of the query and key heads, and the value-embedding gate, forward and
+backward) against the fp64 oracle, through the C ABI.  Cases: a single row, ragged T, grouped key heads, per
 sequence position offsets (clamped into the table), tables of standard
 RoPE angles and of random angles, all-zero rows, large magnitudes, the d20
 training shape on sampled positions, and the prologue chained with the
@@ -10,7 +10,8 @@ import pytest
 
 import oracle
 import workloads as W
-from parity_util import BF16_MAX_ABS, BF16_REL_L2, assert_close, to_device, to_host
+from parity_util import (BF16_MAX_ABS, BF16_REL_L2, assert_close, assert_close_scaled, to_device,
+                         to_host)
 
 pytestmark = pytest.mark.gpu
 
@@ -171,3 +172,50 @@ def test_prologue_chained_with_attention(dev):
     assert_close("dk", to_host(dk),
                  oracle.qk_norm_rope_backward(tr.k.astype(np.float64), rdk, c64, s64, EPS),
                  BF16_REL_L2, BF16_MAX_ABS)
+
+
+def run_value_gate(v_st, ve_st, g_st, dy_st, dev):
+    import torch
+    import causal_self_attention_mha_amd as na
+    v, ve, dy = (to_device(a, dev) for a in (v_st, ve_st, dy_st))
+    g = to_device(g_st, dev)
+    out = na.value_gate_fwd(v, ve, g)
+    dve, dg = na.value_gate_bwd(ve, g, dy)
+    torch.cuda.synchronize()
+    return to_host(out), to_host(dve), to_host(dg)
+
+
+@pytest.mark.parametrize("B,T,Hk", [(1, 1, 1), (2, 37, 3), (3, 100, 5), (2, 65, 10)])
+def test_value_gate_shapes(dev, B, T, Hk):
+    """v_out reaches |v| + 3 |ve| (past 8 at these scales), so its element bound
+    grows with the magnitude (one bf16 step); dve and dgate stay small."""
+    tr = W.make_train_inputs("d20", B=B, T=T, H=Hk, seed=8000 + T)
+    g, g_st = W.make_gate_logits(B, T, Hk, seed=T)
+    out, dve, dg = run_value_gate(tr.v_store, tr.k_store, g_st, tr.do_store, dev)
+    v, ve, dy = (a.astype(np.float64) for a in (tr.v, tr.k, tr.do))
+    assert_close_scaled("v_out", out, oracle.value_gate_forward(v, ve, g), BF16_REL_L2)
+    rdve, rdg = oracle.value_gate_backward(ve, g, dy)
+    assert_close("dve", dve, rdve, BF16_REL_L2, BF16_MAX_ABS)
+    assert_close("dgate", dg, rdg, BF16_REL_L2, BF16_MAX_ABS)
+
+
+def test_value_gate_saturated_logits_and_d20(dev):
+    """Logits of +-60 saturate the gate at 0 and 3 (finite, gate gradient 0);
+    then the d20 key/value shape (B=32, T=2048, H_kv=10), compared whole."""
+    B, T, Hk = 2, 40, 2
+    tr = W.make_train_inputs("d20", B=B, T=T, H=Hk, seed=81)
+    g = np.where(np.arange(B * T * Hk).reshape(B, T, Hk) % 2 == 0, 60.0, -60.0).astype(np.float32)
+    g_st = W.f32_to_bf16_bits(g)
+    out, dve, dg = run_value_gate(tr.v_store, tr.k_store, g_st, tr.do_store, dev)
+    v, ve, dy = (a.astype(np.float64) for a in (tr.v, tr.k, tr.do))
+    assert_close_scaled("v_out", out, oracle.value_gate_forward(v, ve, g), BF16_REL_L2)
+    assert np.all(np.abs(dg) < 1e-20)
+    tr = W.make_train_inputs("d20", seed=82)
+    B, T, Hk = tr.q.shape[:3]
+    g, g_st = W.make_gate_logits(B, T, Hk, seed=83)
+    out, dve, dg = run_value_gate(tr.v_store, tr.k_store, g_st, tr.do_store, dev)
+    v, ve, dy = (a.astype(np.float64) for a in (tr.v, tr.k, tr.do))
+    assert_close_scaled("v_out d20", out, oracle.value_gate_forward(v, ve, g), BF16_REL_L2)
+    rdve, rdg = oracle.value_gate_backward(ve, g, dy)
+    assert_close("dve d20", dve, rdve, BF16_REL_L2, BF16_MAX_ABS)
+    assert_close("dgate d20", dg, rdg, BF16_REL_L2, BF16_MAX_ABS)

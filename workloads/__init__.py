@@ -33,7 +33,7 @@ __all__ = [
     "Config", "CONFIGS", "HEADLINE", "DECODE",
     "f32_to_bf16_bits", "bf16_bits_to_f32",
     "TrainInputs", "DecodeInputs", "make_train_inputs", "make_decode_inputs",
-    "make_angle_tables",
+    "make_angle_tables", "make_gate_logits",
 ]
 
 
@@ -189,3 +189,9 @@ def make_angle_tables(T_tab: int, half: int = 64, seed: int = 0):
     rng = np.random.default_rng(seed)
     a = rng.uniform(-np.pi, np.pi, size=(T_tab, half))
     return np.cos(a).astype(np.float32), np.sin(a).astype(np.float32)
+
+
+def make_gate_logits(B: int, T: int, H: int, seed: int = 0, scale: float = 2.0):
+    """Per-head gate logits (B, T, H) for the value-embedding gate:
+    standard normal * scale, rounded to bf16.  Returns (values_f32, bf16 bits)."""
+    return _draw(np.random.default_rng(seed), (B, T, H), scale, "bf16")
