@@ -96,6 +96,10 @@ KERNEL_SOURCES = {  # the sources whose text determines each kernel's code
     "fwd": ["fwd_bf16.hip", "device_common.hpp", "internal.hpp"],
     "dkdv": ["bwd_bf16.hip", "device_common.hpp", "internal.hpp"],
     "dq": ["bwd_bf16.hip", "device_common.hpp", "internal.hpp"],
+    "qk_norm_rope_fwd": ["prologue_bf16.hip", "device_common.hpp", "internal.hpp"],
+    "qk_norm_rope_bwd": ["prologue_bf16.hip", "device_common.hpp", "internal.hpp"],
+    "value_gate_fwd": ["prologue_bf16.hip", "device_common.hpp", "internal.hpp"],
+    "value_gate_bwd": ["prologue_bf16.hip", "device_common.hpp", "internal.hpp"],
 }
 
 
@@ -462,10 +466,14 @@ def main():
             "fwd_frac_hbm": round(fb / (f_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
             "bwd_frac_hbm": round(bb / (b_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
             "bytes_fwd": fb, "bytes_bwd": bb,
+            "traffic_fwd": recorded_traffic("qk_norm_rope_fwd"),
+            "traffic_bwd": recorded_traffic("qk_norm_rope_bwd"),
             "value_gate": {"fwd_ms": round(gf_ms, 4), "bwd_ms": round(gb_ms, 4),
                            "fwd_GB_per_s": round(gfb / (gf_ms * 1e-3) / 1e9, 1),
                            "bwd_GB_per_s": round(gbb / (gb_ms * 1e-3) / 1e9, 1),
-                           "bytes_fwd": gfb, "bytes_bwd": gbb},
+                           "bytes_fwd": gfb, "bytes_bwd": gbb,
+                           "traffic_fwd": recorded_traffic("value_gate_fwd"),
+                           "traffic_bwd": recorded_traffic("value_gate_bwd")},
             "calls": args.steps}
         log(f"prologue {result['prologue']}")
         del yq, yk, rgq, rgk, gt
