@@ -12,7 +12,9 @@ recorded on the launch stream around every kernel.
 The single-token decode over the ragged d20 cache (B=64, H=10, lengths
 uniform in [1, 2048]) is timed in its own loop and reported under "decode";
 it rotates three separately allocated caches so that no call finds its
-cache in the 256 MB Infinity Cache.
+cache in the 256 MB Infinity Cache.  The call time comes from HIP events
+around each call; the split/combine breakdown from a second loop that also
+records an event between the two kernels (which adds a gap of its own).
 
 The same d20 step with a sliding window (--window, default 1024: the short
 "S" layers of nanochat's SSSL pattern; the pages give no window length, so
@@ -501,22 +503,37 @@ def main():
         devs = [ev.create(3) for _ in range(nd + 5)]
         darr = [(ctypes.c_void_p * 3)(*[e.value for e in x]) for x in devs]
 
-        def dstep(i, window=-1):
+        def dstep(i, window=-1, per_kernel=False):
+            # per_kernel: the _timed entry records an event between the two
+            # kernels (for the split/combine breakdown); otherwise events sit
+            # only around the call, so the call time has no event inside it
             kc, vc = caches[i % 3]
+            e = devs[i]
+            if not per_kernel:
+                ev.record(e[0], stream)
             st = lib.na_attn_decode_window(ptr(qd), ptr(kc), ptr(vc), ptr(lens), ptr(od),
                                            ptr(lsed), Bd, Hd, D, Tc, window, ptr(ws), wsb,
-                                           P(stream), ctypes.cast(darr[i], P))
+                                           P(stream),
+                                           ctypes.cast(darr[i], P) if per_kernel else None)
             if st:
                 raise RuntimeError(lib.na_last_error().decode())
+            if not per_kernel:
+                ev.record(e[2], stream)
 
+        for i in range(5):
+            dstep(i, per_kernel=True)
+        torch.cuda.synchronize()
+        for i in range(5, nd + 5):
+            dstep(i, per_kernel=True)
+        torch.cuda.synchronize()
+        split = [ev.ms(devs[i][0], devs[i][1]) for i in range(5, nd + 5)]
+        comb = [ev.ms(devs[i][1], devs[i][2]) for i in range(5, nd + 5)]
         for i in range(5):
             dstep(i)
         torch.cuda.synchronize()
         for i in range(5, nd + 5):
             dstep(i)
         torch.cuda.synchronize()
-        split = [ev.ms(devs[i][0], devs[i][1]) for i in range(5, nd + 5)]
-        comb = [ev.ms(devs[i][1], devs[i][2]) for i in range(5, nd + 5)]
         tot = [ev.ms(devs[i][0], devs[i][2]) for i in range(5, nd + 5)]
         kv_bytes = int(dinp.seqlens.astype(np.int64).sum()) * Hd * D * 2 * 2
         io_bytes = Bd * Hd * D * 2 * 2
@@ -553,11 +570,13 @@ def main():
 
             def gdstep(i):
                 kc, vc = gcaches[i % 3]
+                ev.record(devs[i][0], stream)
                 st = lib.na_attn_decode_gqa(ptr(qd), ptr(kc), ptr(vc), ptr(lens), ptr(od),
                                             ptr(lsed), Bd, Hd, hkv, D, Tc, -1, ptr(ws), wsb,
-                                            P(stream), ctypes.cast(darr[i], P))
+                                            P(stream), None)
                 if st:
                     raise RuntimeError(lib.na_last_error().decode())
+                ev.record(devs[i][2], stream)
 
             for i in range(5):
                 gdstep(i)
