@@ -15,9 +15,9 @@
 //                   as MFMA operands, query tiles of 64 are copied HBM -> LDS
 //                   (triple-buffered, read row-wise and transposed);
 //                   accumulates dK, dV and, given a workspace, stores dS
-//   dq_gemm_kernel  with the dS workspace: a 128-query tile per work item,
+//   dq_gemm_kernel  with the dS workspace: a 256-query tile per work item,
 //                   dQ = s dS K over the stored blocks
-// Both run persistent workgroups (one / two per compute unit) that walk their
+// Both run persistent workgroups (one per compute unit) that walk their
 // work items in a balanced order (persistent_item).
 //   dq_kernel       without it: one workgroup per 128-query tile; Q, dout stay
 //                   in registers, key tiles of 64 stream through LDS, S and dP
@@ -822,20 +822,25 @@ __global__ __launch_bounds__(256, 1) void dq_kernel(
 // wavefront) are copied HBM -> LDS by DMA, one barrier per key tile.  The dS
 // stream is the HBM-bound part (about B*H*T^2 bytes against a few hundred
 // cycles of MFMA per block), so its copies run two tiles ahead (three
-// buffers); K tiles, mostly L2 hits, run one ahead (two buffers).
-constexpr int DG_ROWS = 128;  // queries per workgroup (32 per wavefront)
+// buffers); K tiles, mostly L2 hits, run one ahead (two buffers).  Eight
+// wavefronts share each K tile: every byte through the compute unit's
+// vector-memory path counts here, and the K copies are a third of it at four
+// wavefronts (measured: 379 -> 356 us at d20 going from four to eight).
+constexpr int DG_WAVES = 8;                // wavefronts per workgroup
+constexpr int DG_ROWS = 32 * DG_WAVES;     // queries per workgroup (32 per wavefront)
+constexpr int DG_KCOPY = 16 / DG_WAVES;    // 1-KB copies per wavefront of each K tile
 constexpr int DG_KEYS = 64;   // keys per K tile
 constexpr uint32_t DG_DS_B = 2 * 32 * 32 * 2;  // a wavefront's two dS blocks per key tile
 
 // WIN: sliding window, key j visible to query i iff i - win <= j <= i.
 template <bool WIN>
-__global__ __launch_bounds__(256, 2) void dq_gemm_kernel(const u16* __restrict__ k,
+__global__ __launch_bounds__(64 * DG_WAVES, 8 / DG_WAVES) void dq_gemm_kernel(const u16* __restrict__ k,
                                                          const u16* __restrict__ dsw,
                                                          u16* __restrict__ dq, int nbt, int B,
                                                          int T, int H, int Hk, float scale,
                                                          int win) {
   __shared__ __attribute__((aligned(1024))) char ktile[2][kTileBytes];   // swizzled K
-  __shared__ __attribute__((aligned(1024))) char sst[3][4][DG_DS_B];     // dS blocks per wave
+  __shared__ __attribute__((aligned(1024))) char sst[3][DG_WAVES][DG_DS_B];  // dS blocks per wave
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -898,19 +903,20 @@ __global__ __launch_bounds__(256, 2) void dq_gemm_kernel(const u16* __restrict__
     // the wavefront's blocks of key tile kt: kblk = 2 kt, 2 kt + 1 (if <= qblk)
     const uint32_t ds_rows = static_cast<uint32_t>(qblk + 1) * 2048;  // bytes of its row
     const i32x4 ds_rsrc = buffer_rsrc(dsrow, live ? ds_rows : 0);
-    // Copy j (0..3) of this wavefront's share of K tile kt / of its dS blocks
-    // of key tile kt.  The copies of the next tiles are spread between the
+    // Copy j (0 .. DG_KCOPY - 1) of this wavefront's share of K tile kt / copy
+    // j (0..3) of its dS blocks of key tile kt.  The copies of the next tiles are spread between the
     // current tile's MFMAs: issued in a burst they stall the issuing wavefront
     // behind the compute unit's vector-memory queue.
     auto issue_k = [&](int kt, int buf, int j) {
       const int k0 = kt * DG_KEYS;
       const uint32_t nrec = static_cast<uint32_t>(T - k0) * rsb;  // keys past T read as 0
-      dma16(buffer_rsrc(k + kbase + static_cast<size_t>(k0) * rsk, nrec), kvoff + 16 * j * rsb,
-            kt_lds + buf * kTileBytes + 1024 * wave + 4096 * j);
+      dma16(buffer_rsrc(k + kbase + static_cast<size_t>(k0) * rsk, nrec),
+            kvoff + 4 * DG_WAVES * j * rsb,
+            kt_lds + buf * kTileBytes + 1024 * (wave + DG_WAVES * j));
     };
     auto issue_ds = [&](int kt, int sbuf, int j) {
       // blocks past qblk are past the resource's end (zeros, never read)
-      dma16(ds_rsrc, kt * 4096 + j * 1024 + 16 * lane, st_lds + sbuf * (4 * DG_DS_B) + j * 1024);
+      dma16(ds_rsrc, kt * 4096 + j * 1024 + 16 * lane, st_lds + sbuf * (DG_WAVES * DG_DS_B) + j * 1024);
     };
 
     // Copies in issue order: K(0), dS(0), dS(1), then per tile t: K(t+1),
@@ -931,7 +937,7 @@ __global__ __launch_bounds__(256, 2) void dq_gemm_kernel(const u16* __restrict__
       auto read = [&](int j) {
         const int kb = j >> 1, c = j & 1;
         // keys 32 kb + 16 c + 8 half + 0..7, query column l32
-        const uint32_t st = st_lds + sb * (4 * DG_DS_B) + kb * 2048 + st_off + c * 16 * 64;
+        const uint32_t st = st_lds + sb * (DG_WAVES * DG_DS_B) + kb * 2048 + st_off + c * 16 * 64;
         const uint2 r0 = ds_read_tr16_at(st);
         const uint2 r1 = ds_read_tr16_at(st + 4 * 64);
         bs[j & 1] = as_bf16x8(make_uint4(r0.x, r0.y, r1.x, r1.y));
@@ -946,8 +952,9 @@ __global__ __launch_bounds__(256, 2) void dq_gemm_kernel(const u16* __restrict__
         // dS(kt+1)'s copies being the last four issued
         if (j < 2) {
           if (more_k) {
-            issue_k(kt + 1, 1 - BUF, 2 * j);
-            issue_k(kt + 1, 1 - BUF, 2 * j + 1);
+#pragma unroll
+            for (int c = j * DG_KCOPY / 2; c < (j + 1) * DG_KCOPY / 2; ++c)
+              issue_k(kt + 1, 1 - BUF, c);
           }
         } else if (more_ds) {
           issue_ds(kt + 2, (kt + 2) % 3, 2 * (j - 2));
@@ -967,7 +974,7 @@ __global__ __launch_bounds__(256, 2) void dq_gemm_kernel(const u16* __restrict__
     };
 
 #pragma unroll
-    for (int j = 0; j < 4; ++j) issue_k(kt_lo, 0, j);
+    for (int j = 0; j < DG_KCOPY; ++j) issue_k(kt_lo, 0, j);
 #pragma unroll
     for (int j = 0; j < 4; ++j) issue_ds(kt_lo, kt_lo % 3, j);
     if (kt_lo + 1 < n_kt) {
@@ -1038,7 +1045,8 @@ hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const vo
   if (dsw != nullptr) {
     const int n_qt = (T + DG_ROWS - 1) / DG_ROWS;
     e = launch(win ? dq_gemm_kernel<true> : dq_gemm_kernel<false>,
-               dim3(persistent_grid(static_cast<long>(n_qt) * B * H, 2)), dim3(256), 0, s, k16,
+               dim3(persistent_grid(static_cast<long>(n_qt) * B * H, 8 / DG_WAVES)),
+               dim3(64 * DG_WAVES), 0, s, k16,
                static_cast<const u16*>(dsw), static_cast<u16*>(dq), nbt, B, T, H, Hk, scale,
                w);
   } else {
