@@ -72,3 +72,17 @@ def test_decode_inputs():
     assert full.seqlens.shape == (64,)
     rng = np.random.default_rng(W.CONFIGS["decode_d20"].seed)
     assert np.array_equal(full.seqlens, rng.integers(1, 2049, size=64))
+
+
+def test_prologue_inputs_are_seeded_and_well_formed():
+    c1, s1 = W.make_angle_tables(17, 64, seed=3)
+    c2, s2 = W.make_angle_tables(17, 64, seed=3)
+    assert c1.dtype == np.float32 and c1.shape == (17, 64) and s1.shape == (17, 64)
+    assert np.array_equal(c1, c2) and np.array_equal(s1, s2)
+    # cos^2 + sin^2 = 1 up to the fp32 rounding of each
+    assert np.allclose(c1.astype(np.float64) ** 2 + s1.astype(np.float64) ** 2, 1.0, atol=1e-6)
+    assert not np.array_equal(W.make_angle_tables(17, 64, seed=4)[0], c1)
+    g, bits = W.make_gate_logits(2, 5, 3, seed=7)
+    assert g.shape == (2, 5, 3) and bits.dtype == np.uint16
+    assert np.array_equal(W.bf16_bits_to_f32(bits), g)      # values are the stored bf16
+    assert np.array_equal(W.make_gate_logits(2, 5, 3, seed=7)[1], bits)
