@@ -102,3 +102,15 @@ def test_decode_reuses_workspace(dev):
                                 to_device(inp.v_store, dev), lens, workspace=ws)
         torch.cuda.synchronize()
         check(inp, o, lse)
+
+
+@pytest.mark.parametrize("H,B", [(1, 100), (2, 70), (3, 60)])
+def test_decode_few_heads_many_sequences(dev, H, B):
+    """Workgroups of 16 H threads (fewer than a wavefront) with more sequences
+    than threads: the prefix sum over the sequences' chunk counts runs in
+    blocks of 16 or 32 lanes."""
+    rng = np.random.default_rng(15 + H)
+    lens = rng.integers(0, 300, size=B)
+    inp = W.make_decode_inputs(B=B, T_cap=300, H=H, seed=15 + H, seqlens=lens)
+    o, lse = run_decode(inp, dev)
+    check(inp, o, lse)

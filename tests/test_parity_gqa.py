@@ -119,3 +119,32 @@ def test_gqa_decode(dev, H, Hk, Wn):
     live = inp.seqlens > 0
     assert_close("o", to_host(o)[live], ro[live], BF16_REL_L2, BF16_MAX_ABS)
     assert_close("lse", to_host(lse)[live], rl[live], BF16_REL_L2, BF16_MAX_ABS)
+
+
+@pytest.mark.parametrize("H,Hk,B,T_cap", [(4, 1, 40, 300), (2, 1, 37, 300), (10, 5, 64, 2048),
+                                          (12, 3, 20, 500)])
+def test_gqa_decode_many_sequences(dev, H, Hk, B, T_cap):
+    """Grouped decode (one 16-lane group per key/value head serving 2 or 4
+    query heads; other ratios one group per query head), ragged lengths
+    U[0, T_cap], rows past each length NaN; (10, 5, 64, 2048) is the d20
+    decode workload with five key/value heads."""
+    import torch
+    import causal_self_attention_mha_amd as na
+    rng = np.random.default_rng(90 + H + Hk)
+    lens = rng.integers(0, T_cap + 1, size=B)
+    inp = W.make_decode_inputs(B=B, T_cap=T_cap, H=H, seed=91 + H, seqlens=lens)
+    for n in ("k_cache", "v_cache", "k_store", "v_store"):
+        setattr(inp, n, np.ascontiguousarray(getattr(inp, n)[:, :, :Hk]))
+    q = to_device(inp.q_store, dev)
+    kc, vc = to_device(inp.k_store, dev), to_device(inp.v_store, dev)
+    for b, L in enumerate(inp.seqlens):
+        kc[b, int(L):] = float("nan")
+        vc[b, int(L):] = float("nan")
+    lensd = torch.from_numpy(inp.seqlens.astype(np.int32)).to(dev)
+    o, lse = na.attn_decode(q, kc, vc, lensd)
+    torch.cuda.synchronize()
+    ro, rl = oracle.decode(inp.q, inp.k_cache, inp.v_cache, inp.seqlens)
+    live = inp.seqlens > 0
+    assert_close("o", to_host(o)[live], ro[live], BF16_REL_L2, BF16_MAX_ABS)
+    assert_close("lse", to_host(lse)[live], rl[live], BF16_REL_L2, BF16_MAX_ABS)
+    assert np.all(to_host(o)[~live] == 0.0) and np.all(np.isneginf(to_host(lse)[~live]))
