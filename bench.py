@@ -25,7 +25,9 @@ counted over the visible (query, key) pairs only).
 Prefill over a KV cache (16 sequences, a 512-token chunk each over caches of
 U[0, 1536] rows, T_cap 2048, d20 heads; the chat-prefill shape of the
 inference engine, sizes chosen here) is timed and reported under "prefill"
-(append + attention, FLOPs over the visible pairs).
+(append + attention, FLOPs over the visible pairs), and again with the QK norm
+and rotary embedding folded in, next to the prologue kernel followed by the
+prefill ("with_qk_norm_rope").
 
 The attention prologue (RMS normalisation + rotary embedding of q and k at
 the d20 shape, forward and backward, and the value-embedding gate on the d20
@@ -626,13 +628,49 @@ def main():
         p_ms = ev.ms(pev[0], pev[1]) / args.steps
         pairs = int(sum(Tq * int(L) + Tq * (Tq + 1) // 2 for L in plens))
         pfl = 4 * D * H * pairs  # QK^T and PV, 2 FLOP per multiply-add
+        # the same call with the QK-norm + rotary prologue folded in, and the
+        # two-step path it replaces (prologue kernel, then the prefill)
+        pct, pst = (torch.from_numpy(a).to(dev) for a in W.make_angle_tables(Tcp, D // 2, seed=3))
+        pqr, pkr = torch.empty_like(pq), torch.empty_like(pk)
+        peps = ctypes.c_float(1e-6)
+
+        def prstep():
+            st = lib.na_attn_prefill_rope(ptr(pq), ptr(pk), ptr(pv), ptr(pkc), ptr(pvc), ptr(pl),
+                                          ptr(pct), ptr(pst), Tcp, peps, ptr(po), ptr(plse), Bp,
+                                          Tq, H, H, D, Tcp, -1, P(stream))
+            if st:
+                raise RuntimeError(lib.na_last_error().decode())
+
+        def p2step():
+            st = lib.na_qk_norm_rope_fwd(ptr(pq), ptr(pk), ptr(pqr), ptr(pkr), ptr(pct), ptr(pst),
+                                         ptr(pl), Bp, Tq, H, H, D, Tcp, peps, P(stream))
+            if st:
+                raise RuntimeError(lib.na_last_error().decode())
+            st = lib.na_attn_prefill(ptr(pqr), ptr(pkr), ptr(pv), ptr(pkc), ptr(pvc), ptr(pl),
+                                     ptr(po), ptr(plse), Bp, Tq, H, H, D, Tcp, -1, P(stream))
+            if st:
+                raise RuntimeError(lib.na_last_error().decode())
+
+        rope_ms = {}
+        for name, fn in (("fused", prstep), ("two_step", p2step)):
+            for _ in range(args.warmup):
+                fn()
+            torch.cuda.synchronize()
+            ev.record(pev[0], stream)
+            for _ in range(args.steps):
+                fn()
+            ev.record(pev[1], stream)
+            torch.cuda.synchronize()
+            rope_ms[name] = ev.ms(pev[0], pev[1]) / args.steps
         result["prefill"] = {
             "workload": f"prefill over a KV cache: B={Bp} chunks of {Tq} tokens, cache lengths "
                         f"U[0,{Tcp - Tq}], T_cap={Tcp}, H={H}, D={D}, bf16 (append + attention)",
             "ms_per_call": round(p_ms, 4), "TFLOP_per_s": round(pfl / (p_ms * 1e-3) / 1e12, 2),
-            "visible_pairs": pairs, "calls": args.steps}
+            "visible_pairs": pairs, "calls": args.steps,
+            "with_qk_norm_rope": {"fused_ms": round(rope_ms["fused"], 4),
+                                  "two_step_ms": round(rope_ms["two_step"], 4)}}
         log(f"prefill {result['prefill']}")
-        del pq, pk, pv, pkc, pvc, po
+        del pq, pk, pv, pkc, pvc, po, pqr, pkr
 
     # ---------------- CPU baseline: the oracle on a bounded sample
     if args.cpu_heads > 0:

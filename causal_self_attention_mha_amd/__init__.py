@@ -96,6 +96,8 @@ def load_library():
     lib.na_attn_prefill.argtypes = [vp, vp, vp, vp, vp, vp, vp, f32p, i, i, i, i, i, i, i, vp]
     lib.na_qk_norm_rope_fwd.argtypes = [vp, vp, vp, vp, f32p, f32p, vp, i, i, i, i, i, i,
                                         ctypes.c_float, vp]
+    lib.na_attn_prefill_rope.argtypes = [vp, vp, vp, vp, vp, vp, f32p, f32p, i, ctypes.c_float,
+                                         vp, f32p, i, i, i, i, i, i, i, vp]
     lib.na_value_gate_fwd.argtypes = [vp, vp, vp, vp, i, i, i, i, vp]
     lib.na_value_gate_bwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, vp]
     lib.na_qk_norm_rope_bwd.argtypes = [vp, vp, vp, vp, vp, vp, f32p, f32p, vp, i, i, i, i, i,
@@ -105,7 +107,7 @@ def load_library():
                "na_attn_fwd_window", "na_attn_bwd_window", "na_attn_decode_window",
                "na_attn_fwd_gqa", "na_attn_bwd_gqa", "na_attn_decode_gqa", "na_attn_prefill",
                "na_qk_norm_rope_fwd", "na_qk_norm_rope_bwd", "na_value_gate_fwd",
-               "na_value_gate_bwd"):
+               "na_value_gate_bwd", "na_attn_prefill_rope"):
         getattr(lib, fn).restype = ctypes.c_int
     lib.na_status_string.argtypes = [ctypes.c_int]
     lib.na_status_string.restype = ctypes.c_char_p
@@ -305,11 +307,13 @@ def attn_decode(q, k_cache, v_cache, seqlens, o=None, lse=None, workspace=None,
 
 
 def attn_prefill(q, k_new, v_new, k_cache, v_cache, cache_lens, o=None, lse=None,
-                 want_lse=True, window=None):
+                 want_lse=True, window=None, rope=None, eps=1e-6):
     """Prefill a chunk over a KV cache: appends k_new, v_new at rows
     cache_lens[b] .. of the caches (in place), then the chunk's queries attend
     bottom-right causally over the cache.  Returns (o, lse); cache_lens is not
-    updated."""
+    updated.  rope=(cos, sin), float32 (T_tab >= T_cap, 64) tables: q and
+    k_new are raw heads, RMS-normalised and rotated at their cache positions
+    inside the call (na_attn_prefill_rope)."""
     import torch
     lib = load_library()
     _require(q.is_cuda and q.dtype == torch.bfloat16 and q.dim() == 4 and q.shape[-1] == HEAD_DIM,
@@ -334,10 +338,23 @@ def attn_prefill(q, k_new, v_new, k_cache, v_cache, cache_lens, o=None, lse=None
     if want_lse and lse is None:
         lse = torch.empty((B, H, T_q), dtype=torch.float32, device=q.device)
     window = _window(window)
+    w = -1 if window is None else window
+    if rope is not None:
+        cos, sin = rope
+        for n, t in (("cos", cos), ("sin", sin)):
+            _require(t.dtype == torch.float32 and t.device == q.device and t.is_contiguous()
+                     and t.dim() == 2 and t.shape[1] == D // 2 and t.shape == cos.shape
+                     and t.shape[0] >= T_cap, f"{n} must be contiguous float32 (T_tab >= T_cap, 64)")
+        _check(lib, "na_attn_prefill_rope",
+               lib.na_attn_prefill_rope(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache),
+                                        _ptr(v_cache), _ptr(cache_lens), _ptr(cos), _ptr(sin),
+                                        cos.shape[0], float(eps), _ptr(o), _ptr(lse), B, T_q, H,
+                                        Hk, D, T_cap, w, _stream(q)))
+        return o, lse
     _check(lib, "na_attn_prefill",
            lib.na_attn_prefill(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
                                _ptr(cache_lens), _ptr(o), _ptr(lse), B, T_q, H, Hk, D, T_cap,
-                               -1 if window is None else window, _stream(q)))
+                               w, _stream(q)))
     return o, lse
 
 

@@ -144,6 +144,37 @@ na_status na_attn_prefill(const void* q, const void* k_new, const void* v_new, v
                     "na_attn_prefill");
 }
 
+na_status na_attn_prefill_rope(const void* q, const void* k_new, const void* v_new,
+                               void* k_cache, void* v_cache, const int* cache_lens,
+                               const float* cos_tab, const float* sin_tab, int T_tab, float eps,
+                               void* o, float* lse, int B, int T_q, int H, int H_kv, int D,
+                               int T_cap, int window, void* stream) {
+  na_status st = check_sizes(B, T_q, H, D);
+  if (st) return st;
+  if ((st = check_kv_heads(H, H_kv))) return st;
+  if (T_cap < T_q)
+    return fail(NA_ERR_INVALID_ARG, "T_cap=%d is smaller than the chunk T_q=%d", T_cap, T_q);
+  if ((st = check_sizes(B, T_cap, H, D))) return st;
+  if (T_tab < T_cap)
+    return fail(NA_ERR_INVALID_ARG, "T_tab=%d is smaller than T_cap=%d", T_tab, T_cap);
+  if ((long double)T_tab * D > 2147483647.0L)
+    return fail(NA_ERR_UNSUPPORTED, "the rotary tables (T_tab=%d) exceed 2^31-1 elements", T_tab);
+  if (!(eps >= 0.f) || eps > 3.0e38f) return fail(NA_ERR_INVALID_ARG, "eps must be finite and >= 0");
+  if (lse != nullptr)
+    st = check_ptrs({{q, "q"}, {k_new, "k_new"}, {v_new, "v_new"}, {cache_lens, "cache_lens"},
+                     {cos_tab, "cos_tab"}, {sin_tab, "sin_tab"}},
+                    {{k_cache, "k_cache"}, {v_cache, "v_cache"}, {o, "o"}, {lse, "lse"}});
+  else
+    st = check_ptrs({{q, "q"}, {k_new, "k_new"}, {v_new, "v_new"}, {cache_lens, "cache_lens"},
+                     {cos_tab, "cos_tab"}, {sin_tab, "sin_tab"}},
+                    {{k_cache, "k_cache"}, {v_cache, "v_cache"}, {o, "o"}});
+  if (st) return st;
+  return hip_status(na::launch_prefill_bf16(q, k_new, v_new, k_cache, v_cache, cache_lens, o, lse,
+                                            B, T_q, H, H_kv, T_cap, window, (hipStream_t)stream,
+                                            cos_tab, sin_tab, eps),
+                    "na_attn_prefill_rope");
+}
+
 size_t na_attn_bwd_workspace_bytes(int B, int T, int H, int D) {
   if (B < 1 || T < 1 || H < 1 || D != na::kHeadDim || T > 1048576) return 0;
   return na::bwd_workspace_bytes(B, T, H);

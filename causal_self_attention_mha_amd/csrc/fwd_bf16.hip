@@ -59,11 +59,15 @@ constexpr float kRescaleLog2 = 8.0f;
 // L .. L + T - 1 with L = lens[b] (clamped to [0, Tc - T]): query row r sees
 // cache rows 0 .. L + r.  Without PRE, Tc = T and L = 0 (training).  Masks and
 // tile ranges below compare key rows with query positions L + r.
-template <bool WIN, bool PRE>
+// ROPE (prefill only): q holds the raw query heads; each row is RMS-normalised
+// and rotated by the angles of its position (fp32 (T_tab, 64) cos/sin tables)
+// as it is loaded, then rounded to bf16 like any query operand.
+template <bool WIN, bool PRE, bool ROPE = false>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(
     const u16* __restrict__ q, const u16* __restrict__ k, const u16* __restrict__ v,
     u16* __restrict__ o, float* __restrict__ lse, int B, int T, int Tc, int H, int Hk,
-    const int* __restrict__ lens, float c_log2, float scale, int win) {
+    const int* __restrict__ lens, float c_log2, float scale, int win,
+    const float* __restrict__ cos_t, const float* __restrict__ sin_t, float eps) {
   // two buffers of (K tile, V tile), swizzled (see tile_swz)
   __shared__ __attribute__((aligned(1024))) char kvs[2 * BUF_B];
 
@@ -103,6 +107,40 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(
     const u16* qp = q + base + min(qrow, T - 1) * rs + 8 * half;
 #pragma unroll
     for (int kc = 0; kc < 8; ++kc) qreg[kc] = as_bf16x8(ld16(qp + 16 * kc));
+  }
+  if constexpr (ROPE) {
+    // the lane holds elements 16 kc + 8 half + e of its row; element i < 64
+    // (kc < 4) pairs with i + 64, the same e of qreg[kc + 4]; the other half
+    // of the row sits in lane l ^ 32
+    float x[8][8];
+    float ss = 0.f;
+#pragma unroll
+    for (int kc = 0; kc < 8; ++kc)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        x[kc][e] = static_cast<float>(qreg[kc][e]);
+        ss = fmaf(x[kc][e], x[kc][e], ss);
+      }
+    ss += __shfl_xor(ss, 32, 64);
+    const float r = __builtin_amdgcn_rsqf(ss * (1.f / D) + eps);
+    const int p = L + min(qrow, T - 1);  // the row's position in the cache
+    const float* cp = cos_t + static_cast<size_t>(p) * (D / 2) + 8 * half;
+    const float* sp = sin_t + static_cast<size_t>(p) * (D / 2) + 8 * half;
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) {
+      const float4 c0 = *reinterpret_cast<const float4*>(cp + 16 * kc);
+      const float4 c1 = *reinterpret_cast<const float4*>(cp + 16 * kc + 4);
+      const float4 s0 = *reinterpret_cast<const float4*>(sp + 16 * kc);
+      const float4 s1 = *reinterpret_cast<const float4*>(sp + 16 * kc + 4);
+      const float cs[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+      const float sn[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float z1 = x[kc][e] * r, z2 = x[kc + 4][e] * r;
+        qreg[kc][e] = to_bf16(fmaf(z1, cs[e], -z2 * sn[e]));
+        qreg[kc + 4][e] = to_bf16(fmaf(z1, sn[e], z2 * cs[e]));
+      }
+    }
   }
 
   f32x16 oacc[4];
@@ -282,19 +320,27 @@ hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o,
   return launch(win ? fwd_bf16_kernel<true, false> : fwd_bf16_kernel<false, false>, grid,
                 dim3(64 * NW), 0, s, static_cast<const u16*>(q), static_cast<const u16*>(k),
                 static_cast<const u16*>(v), static_cast<u16*>(o), lse, B, T, T, H, Hk,
-                static_cast<const int*>(nullptr), c_log2, scale, win ? window : T);
+                static_cast<const int*>(nullptr), c_log2, scale, win ? window : T,
+                static_cast<const float*>(nullptr), static_cast<const float*>(nullptr), 0.f);
 }
 
 // Prefill: the T new rows of k_new, v_new go to cache rows L .. L + T - 1
 // (L = lens[b] clamped to [0, Tc - T]), one 16-byte chunk per thread; the
 // rows of one (b, t) are contiguous (H_kv D elements) in both tensors.
+// ROPE: each key head row is RMS-normalised and rotated by the angles of its
+// position L + t on the way (16 lanes per head row: the pair partner of
+// element i < 64 is 8 lanes away, the sum of squares a 16-lane sum).
+template <bool ROPE>
 __global__ __launch_bounds__(256) void kv_append_kernel(const u16* __restrict__ k_new,
                                                         const u16* __restrict__ v_new,
                                                         u16* __restrict__ kc, u16* __restrict__ vc,
                                                         const int* __restrict__ lens, int T,
-                                                        int Tc, int Hk, long chunks) {
+                                                        int Tc, int Hk, long chunks,
+                                                        const float* __restrict__ cos_t,
+                                                        const float* __restrict__ sin_t,
+                                                        float eps) {
   const long i = static_cast<long>(blockIdx.x) * 256 + threadIdx.x;
-  if (i >= chunks) return;
+  if (i >= chunks) return;  // chunks is a multiple of 16: whole head rows drop out
   const int per_row = Hk * D / 8;  // 16-byte chunks per (b, t) row
   const long row = i / per_row;    // b * T + t
   const int c = static_cast<int>(i - row * per_row);
@@ -302,28 +348,57 @@ __global__ __launch_bounds__(256) void kv_append_kernel(const u16* __restrict__ 
   const int L = min(max(lens[b], 0), Tc - T);
   const size_t dst = (static_cast<size_t>(b) * Tc + L + t) * Hk * D + 8 * c;
   const size_t src = static_cast<size_t>(row) * Hk * D + 8 * c;
-  st16(kc + dst, ld16(k_new + src));
+  uint4 kv = ld16(k_new + src);
+  if constexpr (ROPE) {
+    const int sub = c & 15;  // elements 8 sub .. 8 sub + 7 of the head row
+    const uint32_t w[4] = {kv.x, kv.y, kv.z, kv.w};
+    float x[8];
+    float ss = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      x[2 * j] = __uint_as_float(w[j] << 16);
+      x[2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u);
+      ss = fmaf(x[2 * j], x[2 * j], fmaf(x[2 * j + 1], x[2 * j + 1], ss));
+    }
+    const float r = __builtin_amdgcn_rsqf(sum16(ss) * (1.f / D) + eps);
+    const size_t tp = static_cast<size_t>(L + t) * (D / 2) + 8 * (sub & 7);
+    const float sg = sub < 8 ? -1.f : 1.f;  // y_i = z_i c - z_{i+64} s, y_{i+64} = z_i s + z_{i+64} c
+    float y[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float z = x[e] * r;
+      const float zp = dpp<0x128>(z);  // the partner lane's element (row_ror:8)
+      y[e] = fmaf(z, cos_t[tp + e], sg * sin_t[tp + e] * zp);
+    }
+    kv = make_uint4(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]), pack_bf16x2(y[4], y[5]),
+                    pack_bf16x2(y[6], y[7]));
+  }
+  st16(kc + dst, kv);
   st16(vc + dst, ld16(v_new + src));
 }
 
 hipError_t launch_prefill_bf16(const void* q, const void* k_new, const void* v_new, void* kc,
                                void* vc, const int* lens, void* o, float* lse, int B, int T,
-                               int H, int Hk, int Tc, int window, hipStream_t s) {
+                               int H, int Hk, int Tc, int window, hipStream_t s,
+                               const float* cos_t, const float* sin_t, float eps) {
+  const bool rope = cos_t != nullptr;
   const long chunks = static_cast<long>(B) * T * Hk * D / 8;
-  hipError_t e = launch(kv_append_kernel, dim3(static_cast<unsigned>((chunks + 255) / 256)),
-                        dim3(256), 0, s, static_cast<const u16*>(k_new),
-                        static_cast<const u16*>(v_new), static_cast<u16*>(kc),
-                        static_cast<u16*>(vc), lens, T, Tc, Hk, chunks);
+  hipError_t e = launch(rope ? kv_append_kernel<true> : kv_append_kernel<false>,
+                        dim3(static_cast<unsigned>((chunks + 255) / 256)), dim3(256), 0, s,
+                        static_cast<const u16*>(k_new), static_cast<const u16*>(v_new),
+                        static_cast<u16*>(kc), static_cast<u16*>(vc), lens, T, Tc, Hk, chunks,
+                        cos_t, sin_t, eps);
   if (e != hipSuccess) return e;
   const float scale = 1.0f / sqrtf(static_cast<float>(D));
   const float c_log2 = scale * 1.4426950408889634f;
   const int n_qt = (T + BQ - 1) / BQ;
   const dim3 grid(static_cast<unsigned>(n_qt) * B * H);
   const bool win = window >= 0 && window < Tc - 1;  // else every row sees all its keys
-  return launch(win ? fwd_bf16_kernel<true, true> : fwd_bf16_kernel<false, true>, grid,
-                dim3(64 * NW), 0, s, static_cast<const u16*>(q), static_cast<const u16*>(kc),
-                static_cast<const u16*>(vc), static_cast<u16*>(o), lse, B, T, Tc, H, Hk, lens,
-                c_log2, scale, win ? window : Tc);
+  auto* kern = rope ? (win ? fwd_bf16_kernel<true, true, true> : fwd_bf16_kernel<false, true, true>)
+                    : (win ? fwd_bf16_kernel<true, true> : fwd_bf16_kernel<false, true>);
+  return launch(kern, grid, dim3(64 * NW), 0, s, static_cast<const u16*>(q),
+                static_cast<const u16*>(kc), static_cast<const u16*>(vc), static_cast<u16*>(o),
+                lse, B, T, Tc, H, Hk, lens, c_log2, scale, win ? window : Tc, cos_t, sin_t, eps);
 }
 
 }  // namespace na

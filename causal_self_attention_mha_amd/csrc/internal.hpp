@@ -27,9 +27,14 @@ hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o,
 // rows lens[b] .. lens[b] + T - 1 (lens clamped to [0, Tc - T] on the device),
 // then the T queries attend bottom-right causally over rows 0 .. lens[b] + r.
 // lse may be null.
+// With cos_t non-null, q and k_new hold raw heads that are RMS-normalised (eps)
+// and rotated by the fp32 (>= Tc, D/2) cos/sin tables at their cache positions
+// on the way (k_new in the append, q as the forward loads it).
 hipError_t launch_prefill_bf16(const void* q, const void* k_new, const void* v_new, void* kc,
                                void* vc, const int* lens, void* o, float* lse, int B, int T,
-                               int H, int Hk, int Tc, int window, hipStream_t s);
+                               int H, int Hk, int Tc, int window, hipStream_t s,
+                               const float* cos_t = nullptr, const float* sin_t = nullptr,
+                               float eps = 0.f);
 
 // bf16 backward: delta, then dk/dv, then dq.
 // ws: optional dS workspace of bwd_workspace_bytes(B, T, H) bytes; with it dQ

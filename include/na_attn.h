@@ -267,6 +267,25 @@ na_status na_value_gate_fwd(const void* v, const void* ve, const void* gate, voi
 na_status na_value_gate_bwd(const void* ve, const void* gate, const void* dv_out, void* dve,
                             void* dgate, int B, int T, int H_kv, int D, void* stream);
 
+/*
+ * Prefill with the prologue folded in: as na_attn_prefill, but q and k_new
+ * hold the raw query and key heads, and each head row is RMS-normalised and
+ * rotated (the readings of na_qk_norm_rope_fwd) at its cache position on the
+ * way: key row t of sequence b at position L + t as it is appended (the cache
+ * receives the rotated bf16 row), query row r at position L + r as the
+ * attention loads it, with L = cache_lens[b] clamped to [0, T_cap - T_q].
+ * Equal, up to rounding, to na_qk_norm_rope_fwd on q and k_new with
+ * pos_offset = cache_lens followed by na_attn_prefill, without the round trip
+ * of the rotated q and k_new through memory.  cos_tab, sin_tab: fp32
+ * (T_tab, D/2), T_tab >= T_cap; eps >= 0 and finite.  v_new is appended as
+ * is.  Other arguments, checks and outputs as in na_attn_prefill.
+ */
+na_status na_attn_prefill_rope(const void* q, const void* k_new, const void* v_new,
+                               void* k_cache, void* v_cache, const int* cache_lens,
+                               const float* cos_tab, const float* sin_tab, int T_tab, float eps,
+                               void* o, float* lse, int B, int T_q, int H, int H_kv, int D,
+                               int T_cap, int window, void* stream);
+
 /* Static text for a status code. */
 const char* na_status_string(na_status s);
 

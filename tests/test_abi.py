@@ -37,7 +37,7 @@ def test_header_declares_the_entry_points():
               "na_attn_fwd_window", "na_attn_bwd_window", "na_attn_decode_window",
               "na_attn_fwd_gqa", "na_attn_bwd_gqa", "na_attn_decode_gqa", "na_attn_prefill",
               "na_qk_norm_rope_fwd", "na_qk_norm_rope_bwd", "na_value_gate_fwd",
-              "na_value_gate_bwd"):
+              "na_value_gate_bwd", "na_attn_prefill_rope"):
         assert s in syms
 
 
@@ -183,6 +183,20 @@ def test_prologue_checks_its_arguments(lib):
     assert lib.na_qk_norm_rope_bwd(*g, 1, 8, 2, 2, 128, 4, 1e-6, None) == INVALID
     g[4] = g[2]                  # dq aliases dq_rot
     assert lib.na_qk_norm_rope_bwd(*g, 1, 8, 2, 2, 128, 16, 1e-6, None) == INVALID
+
+
+def test_prefill_rope_checks_its_arguments(lib):
+    p = [A + 0x100 * i for i in range(10)]  # q k_new v_new k_cache v_cache lens cos sin o lse
+    call = lambda ptrs, T_tab=64, eps=1e-6, T_cap=64: lib.na_attn_prefill_rope(  # noqa: E731
+        *ptrs[:8], T_tab, eps, ptrs[8], ptrs[9], 1, 8, 2, 2, 128, T_cap, -1, None)
+    assert call(p, T_tab=32) == INVALID and b"T_tab" in lib.na_last_error()
+    assert call(p, eps=-1.0) == INVALID
+    bad = list(p)
+    bad[6] = 0                   # no cos table
+    assert call(bad) == INVALID
+    bad = list(p)
+    bad[8] = bad[0]              # o aliases q
+    assert call(bad) == INVALID
 
 
 def test_value_gate_checks_its_arguments(lib):

@@ -93,3 +93,72 @@ def test_prefill_chat_workload_sampled_heads(dev):
     for (b, h), (O, L) in got.items():
         assert_close(f"[b={b},h={h}].o", to_host(o[b, :, h]), O, BF16_REL_L2, BF16_MAX_ABS)
         assert_close(f"[b={b},h={h}].lse", to_host(lse[b, h]), L, BF16_REL_L2, BF16_MAX_ABS)
+
+
+# ---------------------------------------------------------------- prefill with the prologue folded in
+
+ROPE_CASES = [(2, 17, 2, 2, 300, [0, 100], None), (3, 300, 2, 1, 1024, [0, 63, 700], None),
+              (2, 65, 6, 3, 500, [64, 129], 200), (1, 1, 4, 2, 2048, [2047], None),
+              (2, 128, 4, 2, 600, [1, 5000], None)]
+
+
+@pytest.mark.parametrize("B,T_q,H,Hk,T_cap,lens,Wn", ROPE_CASES)
+def test_prefill_rope_shapes(dev, B, T_q, H, Hk, T_cap, lens, Wn):
+    """na_attn_prefill_rope on raw q and k_new against the oracle chain: QK norm
+    + rotary embedding of q and k_new at their cache positions, then the
+    prefill.  The appended key rows hold the rotated keys (bf16 tolerance),
+    the value rows are copies, every other cache row is left as it was."""
+    import torch
+    import causal_self_attention_mha_amd as na
+    case = make_case(B, T_q, H, Hk, T_cap, lens, seed=6500 + T_q + T_cap)
+    c, s = oracle.rope_tables(T_cap, 128)
+    c, s = c.astype(np.float32), s.astype(np.float32)
+    q, kn, vn, kc, vc = (to_device(case[n], dev) for n in ("q", "kn", "vn", "kc", "vc"))
+    kc0 = to_host(kc)
+    lensd = torch.from_numpy(case["lens"]).to(dev)
+    o, lse = na.attn_prefill(q, kn, vn, kc, vc, lensd, window=Wn,
+                             rope=(torch.from_numpy(c).to(dev), torch.from_numpy(s).to(dev)))
+    torch.cuda.synchronize()
+    starts = [min(max(int(x), 0), T_cap - T_q) for x in case["lens"]]
+    c64, s64 = c.astype(np.float64), s.astype(np.float64)
+    qr = np.concatenate([oracle.qk_norm_rope_forward(case["qf"][b:b + 1], c64[L:L + T_q],
+                                                     s64[L:L + T_q]) for b, L in enumerate(starts)])
+    kr = np.concatenate([oracle.qk_norm_rope_forward(case["knf"][b:b + 1], c64[L:L + T_q],
+                                                     s64[L:L + T_q]) for b, L in enumerate(starts)])
+    # the device clamps cache_lens to [0, T_cap - T_q]; the oracle takes the clamped rows
+    ro, rl, rkc, rvc = oracle.prefill(qr, kr, case["vnf"], case["kcf"], case["vcf"],
+                                      np.array(starts), window=Wn)
+    assert_close("o", to_host(o), ro, BF16_REL_L2, BF16_MAX_ABS)
+    assert_close("lse", to_host(lse), rl, BF16_REL_L2, BF16_MAX_ABS)
+    gk, gv = to_host(kc), to_host(vc)
+    assert np.array_equal(gv, rvc)
+    for b, L in enumerate(starts):
+        assert_close(f"k_cache[{b}] appended", gk[b, L:L + T_q], rkc[b, L:L + T_q], BF16_REL_L2,
+                     BF16_MAX_ABS)
+        assert np.array_equal(gk[b, :L], kc0[b, :L]) and np.array_equal(gk[b, L + T_q:],
+                                                                        kc0[b, L + T_q:])
+
+
+def test_prefill_rope_matches_prologue_then_prefill(dev):
+    """The folded call against the two-step path on the GPU (na_qk_norm_rope_fwd
+    with pos_offset = cache_lens, then na_attn_prefill): the same results up to
+    the rounding order of the normalisation's sum (a consistency check; parity
+    with the oracle is the test above)."""
+    import torch
+    import causal_self_attention_mha_amd as na
+    case = make_case(3, 200, 4, 2, 800, [0, 350, 9999], seed=64)
+    c, s = (torch.from_numpy(a.astype(np.float32)).to(dev) for a in oracle.rope_tables(800, 128))
+    lensd = torch.from_numpy(case["lens"]).to(dev)
+    q, kn, vn = (to_device(case[n], dev) for n in ("q", "kn", "vn"))
+    kc1, vc1 = to_device(case["kc"], dev), to_device(case["vc"], dev)
+    kc2, vc2 = kc1.clone(), vc1.clone()
+    o1, l1 = na.attn_prefill(q, kn, vn, kc1, vc1, lensd, rope=(c, s))
+    qr, kr = na.qk_norm_rope_fwd(q, kn, c, s, pos_offset=lensd)
+    o2, l2 = na.attn_prefill(qr, kr, vn, kc2, vc2, lensd)
+    torch.cuda.synchronize()
+    # the two paths may round an element of the rotated q or k to different
+    # bf16 neighbours, so they are compared to the bf16 bound
+    assert_close("o", to_host(o1), to_host(o2), BF16_REL_L2, BF16_MAX_ABS)
+    assert_close("lse", to_host(l1), to_host(l2), BF16_REL_L2, BF16_MAX_ABS)
+    assert_close("k_cache", to_host(kc1), to_host(kc2), BF16_REL_L2, BF16_MAX_ABS)
+    assert torch.equal(vc1, vc2)
