@@ -636,8 +636,8 @@ def main():
 
         def prstep():
             st = lib.na_attn_prefill_rope(ptr(pq), ptr(pk), ptr(pv), ptr(pkc), ptr(pvc), ptr(pl),
-                                          ptr(pct), ptr(pst), Tcp, peps, ptr(po), ptr(plse), Bp,
-                                          Tq, H, H, D, Tcp, -1, P(stream))
+                                          ptr(pct), ptr(pst), Tcp, peps, None, None, ptr(po),
+                                          ptr(plse), Bp, Tq, H, H, D, Tcp, -1, P(stream))
             if st:
                 raise RuntimeError(lib.na_last_error().decode())
 

@@ -97,7 +97,7 @@ def load_library():
     lib.na_qk_norm_rope_fwd.argtypes = [vp, vp, vp, vp, f32p, f32p, vp, i, i, i, i, i, i,
                                         ctypes.c_float, vp]
     lib.na_attn_prefill_rope.argtypes = [vp, vp, vp, vp, vp, vp, f32p, f32p, i, ctypes.c_float,
-                                         vp, f32p, i, i, i, i, i, i, i, vp]
+                                         vp, vp, vp, f32p, i, i, i, i, i, i, i, vp]
     lib.na_value_gate_fwd.argtypes = [vp, vp, vp, vp, i, i, i, i, vp]
     lib.na_value_gate_bwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, vp]
     lib.na_qk_norm_rope_bwd.argtypes = [vp, vp, vp, vp, vp, vp, f32p, f32p, vp, i, i, i, i, i,
@@ -307,13 +307,15 @@ def attn_decode(q, k_cache, v_cache, seqlens, o=None, lse=None, workspace=None,
 
 
 def attn_prefill(q, k_new, v_new, k_cache, v_cache, cache_lens, o=None, lse=None,
-                 want_lse=True, window=None, rope=None, eps=1e-6):
+                 want_lse=True, window=None, rope=None, eps=1e-6, value_gate=None):
     """Prefill a chunk over a KV cache: appends k_new, v_new at rows
     cache_lens[b] .. of the caches (in place), then the chunk's queries attend
     bottom-right causally over the cache.  Returns (o, lse); cache_lens is not
     updated.  rope=(cos, sin), float32 (T_tab >= T_cap, 64) tables: q and
     k_new are raw heads, RMS-normalised and rotated at their cache positions
-    inside the call (na_attn_prefill_rope)."""
+    inside the call (na_attn_prefill_rope); with it, value_gate=(ve, gate)
+    (bf16 (B, T_q, H_kv, 128) and (B, T_q, H_kv)) appends
+    v_new + 3 sigmoid(gate) ve instead of v_new."""
     import torch
     lib = load_library()
     _require(q.is_cuda and q.dtype == torch.bfloat16 and q.dim() == 4 and q.shape[-1] == HEAD_DIM,
@@ -339,17 +341,26 @@ def attn_prefill(q, k_new, v_new, k_cache, v_cache, cache_lens, o=None, lse=None
         lse = torch.empty((B, H, T_q), dtype=torch.float32, device=q.device)
     window = _window(window)
     w = -1 if window is None else window
+    _require(value_gate is None or rope is not None, "value_gate is taken with rope only")
     if rope is not None:
         cos, sin = rope
         for n, t in (("cos", cos), ("sin", sin)):
             _require(t.dtype == torch.float32 and t.device == q.device and t.is_contiguous()
                      and t.dim() == 2 and t.shape[1] == D // 2 and t.shape == cos.shape
                      and t.shape[0] >= T_cap, f"{n} must be contiguous float32 (T_tab >= T_cap, 64)")
+        ve = gate = None
+        if value_gate is not None:
+            ve, gate = value_gate
+            _require(ve.dtype == torch.bfloat16 and ve.shape == k_new.shape and ve.is_contiguous()
+                     and ve.device == q.device, "ve must be contiguous bf16 like k_new")
+            _require(gate.dtype == torch.bfloat16 and tuple(gate.shape) == tuple(k_new.shape[:3])
+                     and gate.is_contiguous() and gate.device == q.device,
+                     "gate must be contiguous bf16 (B, T_q, H_kv)")
         _check(lib, "na_attn_prefill_rope",
                lib.na_attn_prefill_rope(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache),
                                         _ptr(v_cache), _ptr(cache_lens), _ptr(cos), _ptr(sin),
-                                        cos.shape[0], float(eps), _ptr(o), _ptr(lse), B, T_q, H,
-                                        Hk, D, T_cap, w, _stream(q)))
+                                        cos.shape[0], float(eps), _ptr(ve), _ptr(gate), _ptr(o),
+                                        _ptr(lse), B, T_q, H, Hk, D, T_cap, w, _stream(q)))
         return o, lse
     _check(lib, "na_attn_prefill",
            lib.na_attn_prefill(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),

@@ -147,8 +147,9 @@ na_status na_attn_prefill(const void* q, const void* k_new, const void* v_new, v
 na_status na_attn_prefill_rope(const void* q, const void* k_new, const void* v_new,
                                void* k_cache, void* v_cache, const int* cache_lens,
                                const float* cos_tab, const float* sin_tab, int T_tab, float eps,
-                               void* o, float* lse, int B, int T_q, int H, int H_kv, int D,
-                               int T_cap, int window, void* stream) {
+                               const void* ve, const void* gate, void* o, float* lse, int B,
+                               int T_q, int H, int H_kv, int D, int T_cap, int window,
+                               void* stream) {
   na_status st = check_sizes(B, T_q, H, D);
   if (st) return st;
   if ((st = check_kv_heads(H, H_kv))) return st;
@@ -160,6 +161,13 @@ na_status na_attn_prefill_rope(const void* q, const void* k_new, const void* v_n
   if ((long double)T_tab * D > 2147483647.0L)
     return fail(NA_ERR_UNSUPPORTED, "the rotary tables (T_tab=%d) exceed 2^31-1 elements", T_tab);
   if (!(eps >= 0.f) || eps > 3.0e38f) return fail(NA_ERR_INVALID_ARG, "eps must be finite and >= 0");
+  if ((ve == nullptr) != (gate == nullptr))
+    return fail(NA_ERR_INVALID_ARG, "ve and gate are given together or not at all");
+  if (ve != nullptr) {
+    st = check_ptrs({{ve, "ve"}, {gate, "gate"}}, {{k_cache, "k_cache"}, {v_cache, "v_cache"},
+                                                   {o, "o"}});
+    if (st) return st;
+  }
   if (lse != nullptr)
     st = check_ptrs({{q, "q"}, {k_new, "k_new"}, {v_new, "v_new"}, {cache_lens, "cache_lens"},
                      {cos_tab, "cos_tab"}, {sin_tab, "sin_tab"}},
@@ -171,7 +179,7 @@ na_status na_attn_prefill_rope(const void* q, const void* k_new, const void* v_n
   if (st) return st;
   return hip_status(na::launch_prefill_bf16(q, k_new, v_new, k_cache, v_cache, cache_lens, o, lse,
                                             B, T_q, H, H_kv, T_cap, window, (hipStream_t)stream,
-                                            cos_tab, sin_tab, eps),
+                                            cos_tab, sin_tab, eps, ve, gate),
                     "na_attn_prefill_rope");
 }
 

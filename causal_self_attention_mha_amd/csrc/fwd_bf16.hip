@@ -330,7 +330,9 @@ hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o,
 // ROPE: each key head row is RMS-normalised and rotated by the angles of its
 // position L + t on the way (16 lanes per head row: the pair partner of
 // element i < 64 is 8 lanes away, the sum of squares a 16-lane sum).
-template <bool ROPE>
+// GATE: each value head row gets the value-embedding gate on the way,
+// v + 3 sigmoid(g) ve, with ve (B, T, Hk, D) and the logits g (B, T, Hk) bf16.
+template <bool ROPE, bool GATE>
 __global__ __launch_bounds__(256) void kv_append_kernel(const u16* __restrict__ k_new,
                                                         const u16* __restrict__ v_new,
                                                         u16* __restrict__ kc, u16* __restrict__ vc,
@@ -338,7 +340,8 @@ __global__ __launch_bounds__(256) void kv_append_kernel(const u16* __restrict__ 
                                                         int Tc, int Hk, long chunks,
                                                         const float* __restrict__ cos_t,
                                                         const float* __restrict__ sin_t,
-                                                        float eps) {
+                                                        float eps, const u16* __restrict__ ve,
+                                                        const u16* __restrict__ gate) {
   const long i = static_cast<long>(blockIdx.x) * 256 + threadIdx.x;
   if (i >= chunks) return;  // chunks is a multiple of 16: whole head rows drop out
   const int per_row = Hk * D / 8;  // 16-byte chunks per (b, t) row
@@ -374,20 +377,37 @@ __global__ __launch_bounds__(256) void kv_append_kernel(const u16* __restrict__ 
                     pack_bf16x2(y[6], y[7]));
   }
   st16(kc + dst, kv);
-  st16(vc + dst, ld16(v_new + src));
+  uint4 vv = ld16(v_new + src);
+  if constexpr (GATE) {
+    const float g = bf16_to_f32(gate[row * Hk + c / 16]);
+    const float w3 = 3.f * __builtin_amdgcn_rcpf(1.f + fast_exp2(-g * 1.4426950408889634f));
+    const uint4 ev = ld16(ve + src);
+    const uint32_t a[4] = {vv.x, vv.y, vv.z, vv.w}, b4[4] = {ev.x, ev.y, ev.z, ev.w};
+    uint32_t r4[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      r4[j] = pack_bf16x2(fmaf(w3, __uint_as_float(b4[j] << 16), __uint_as_float(a[j] << 16)),
+                          fmaf(w3, __uint_as_float(b4[j] & 0xffff0000u),
+                               __uint_as_float(a[j] & 0xffff0000u)));
+    vv = make_uint4(r4[0], r4[1], r4[2], r4[3]);
+  }
+  st16(vc + dst, vv);
 }
 
 hipError_t launch_prefill_bf16(const void* q, const void* k_new, const void* v_new, void* kc,
                                void* vc, const int* lens, void* o, float* lse, int B, int T,
                                int H, int Hk, int Tc, int window, hipStream_t s,
-                               const float* cos_t, const float* sin_t, float eps) {
-  const bool rope = cos_t != nullptr;
+                               const float* cos_t, const float* sin_t, float eps,
+                               const void* ve, const void* gate) {
+  const bool rope = cos_t != nullptr, gated = ve != nullptr;
   const long chunks = static_cast<long>(B) * T * Hk * D / 8;
-  hipError_t e = launch(rope ? kv_append_kernel<true> : kv_append_kernel<false>,
-                        dim3(static_cast<unsigned>((chunks + 255) / 256)), dim3(256), 0, s,
-                        static_cast<const u16*>(k_new), static_cast<const u16*>(v_new),
+  auto* append = rope ? (gated ? kv_append_kernel<true, true> : kv_append_kernel<true, false>)
+                      : (gated ? kv_append_kernel<false, true> : kv_append_kernel<false, false>);
+  hipError_t e = launch(append, dim3(static_cast<unsigned>((chunks + 255) / 256)), dim3(256), 0,
+                        s, static_cast<const u16*>(k_new), static_cast<const u16*>(v_new),
                         static_cast<u16*>(kc), static_cast<u16*>(vc), lens, T, Tc, Hk, chunks,
-                        cos_t, sin_t, eps);
+                        cos_t, sin_t, eps, static_cast<const u16*>(ve),
+                        static_cast<const u16*>(gate));
   if (e != hipSuccess) return e;
   const float scale = 1.0f / sqrtf(static_cast<float>(D));
   const float c_log2 = scale * 1.4426950408889634f;

@@ -29,12 +29,15 @@ hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o,
 // lse may be null.
 // With cos_t non-null, q and k_new hold raw heads that are RMS-normalised (eps)
 // and rotated by the fp32 (>= Tc, D/2) cos/sin tables at their cache positions
-// on the way (k_new in the append, q as the forward loads it).
+// on the way (k_new in the append, q as the forward loads it).  With ve
+// non-null, v_new gets the value-embedding gate v + 3 sigmoid(gate) ve in the
+// append (ve (B, T, Hk, D), gate (B, T, Hk), bf16).
 hipError_t launch_prefill_bf16(const void* q, const void* k_new, const void* v_new, void* kc,
                                void* vc, const int* lens, void* o, float* lse, int B, int T,
                                int H, int Hk, int Tc, int window, hipStream_t s,
                                const float* cos_t = nullptr, const float* sin_t = nullptr,
-                               float eps = 0.f);
+                               float eps = 0.f, const void* ve = nullptr,
+                               const void* gate = nullptr);
 
 // bf16 backward: delta, then dk/dv, then dq.
 // ws: optional dS workspace of bwd_workspace_bytes(B, T, H) bytes; with it dQ

@@ -277,14 +277,20 @@ na_status na_value_gate_bwd(const void* ve, const void* gate, const void* dv_out
  * Equal, up to rounding, to na_qk_norm_rope_fwd on q and k_new with
  * pos_offset = cache_lens followed by na_attn_prefill, without the round trip
  * of the rotated q and k_new through memory.  cos_tab, sin_tab: fp32
- * (T_tab, D/2), T_tab >= T_cap; eps >= 0 and finite.  v_new is appended as
- * is.  Other arguments, checks and outputs as in na_attn_prefill.
+ * (T_tab, D/2), T_tab >= T_cap; eps >= 0 and finite.
+ * ve, gate: the value-embedding gate (blog section 1, value embeddings), both
+ * or neither: with them each value row is appended as
+ * v_new + 3 sigmoid(gate) ve (ve bf16 (B, T_q, H_kv, D), gate bf16 logits
+ * (B, T_q, H_kv), as in na_value_gate_fwd); without them (NULL) v_new is
+ * appended as is.  Other arguments, checks and outputs as in
+ * na_attn_prefill.
  */
 na_status na_attn_prefill_rope(const void* q, const void* k_new, const void* v_new,
                                void* k_cache, void* v_cache, const int* cache_lens,
                                const float* cos_tab, const float* sin_tab, int T_tab, float eps,
-                               void* o, float* lse, int B, int T_q, int H, int H_kv, int D,
-                               int T_cap, int window, void* stream);
+                               const void* ve, const void* gate, void* o, float* lse, int B,
+                               int T_q, int H, int H_kv, int D, int T_cap, int window,
+                               void* stream);
 
 /* Static text for a status code. */
 const char* na_status_string(na_status s);

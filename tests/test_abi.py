@@ -186,9 +186,12 @@ def test_prologue_checks_its_arguments(lib):
 
 
 def test_prefill_rope_checks_its_arguments(lib):
-    p = [A + 0x100 * i for i in range(10)]  # q k_new v_new k_cache v_cache lens cos sin o lse
-    call = lambda ptrs, T_tab=64, eps=1e-6, T_cap=64: lib.na_attn_prefill_rope(  # noqa: E731
-        *ptrs[:8], T_tab, eps, ptrs[8], ptrs[9], 1, 8, 2, 2, 128, T_cap, -1, None)
+    p = [A + 0x100 * i for i in range(12)]  # q k_new v_new k_cache v_cache lens cos sin o lse ve g
+    call = lambda ptrs, T_tab=64, eps=1e-6, T_cap=64, ve=None, g=None: (  # noqa: E731
+        lib.na_attn_prefill_rope(*ptrs[:8], T_tab, eps, ve, g, ptrs[8], ptrs[9], 1, 8, 2, 2, 128,
+                                 T_cap, -1, None))
+    assert call(p, ve=p[10]) == INVALID and b"together" in lib.na_last_error()
+    assert call(p, ve=p[10], g=A + 2) == INVALID       # misaligned gate
     assert call(p, T_tab=32) == INVALID and b"T_tab" in lib.na_last_error()
     assert call(p, eps=-1.0) == INVALID
     bad = list(p)

@@ -162,3 +162,40 @@ def test_prefill_rope_matches_prologue_then_prefill(dev):
     assert_close("lse", to_host(l1), to_host(l2), BF16_REL_L2, BF16_MAX_ABS)
     assert_close("k_cache", to_host(kc1), to_host(kc2), BF16_REL_L2, BF16_MAX_ABS)
     assert torch.equal(vc1, vc2)
+
+
+@pytest.mark.parametrize("B,T_q,H,Hk,T_cap,lens", [(2, 70, 4, 2, 400, [0, 250]),
+                                                   (3, 129, 2, 2, 700, [5, 300, 571])])
+def test_prefill_rope_value_gate(dev, B, T_q, H, Hk, T_cap, lens):
+    """na_attn_prefill_rope with the value-embedding gate: the appended value
+    rows are v_new + 3 sigmoid(g) ve (they reach past 8, so the scaled bf16
+    bound), and attention uses them."""
+    import torch
+    import causal_self_attention_mha_amd as na
+    from parity_util import assert_close_scaled
+    case = make_case(B, T_q, H, Hk, T_cap, lens, seed=6600 + T_q)
+    ve_in = W.make_train_inputs("d20", B=B, T=T_q, H=Hk, seed=6601 + T_q)
+    g, g_st = W.make_gate_logits(B, T_q, Hk, seed=6602 + T_q)
+    c, s = (a.astype(np.float32) for a in oracle.rope_tables(T_cap, 128))
+    q, kn, vn, kc, vc = (to_device(case[n], dev) for n in ("q", "kn", "vn", "kc", "vc"))
+    ve, gt = to_device(ve_in.k_store, dev), to_device(g_st, dev)
+    lensd = torch.from_numpy(case["lens"]).to(dev)
+    o, lse = na.attn_prefill(q, kn, vn, kc, vc, lensd, rope=(torch.from_numpy(c).to(dev),
+                                                               torch.from_numpy(s).to(dev)),
+                             value_gate=(ve, gt))
+    torch.cuda.synchronize()
+    starts = [min(max(int(x), 0), T_cap - T_q) for x in case["lens"]]
+    c64, s64 = c.astype(np.float64), s.astype(np.float64)
+    qr = np.concatenate([oracle.qk_norm_rope_forward(case["qf"][b:b + 1], c64[L:L + T_q],
+                                                     s64[L:L + T_q]) for b, L in enumerate(starts)])
+    kr = np.concatenate([oracle.qk_norm_rope_forward(case["knf"][b:b + 1], c64[L:L + T_q],
+                                                     s64[L:L + T_q]) for b, L in enumerate(starts)])
+    vg = oracle.value_gate_forward(case["vnf"], ve_in.k.astype(np.float64), g)
+    ro, rl, rkc, rvc = oracle.prefill(qr, kr, vg, case["kcf"], case["vcf"], np.array(starts))
+    assert_close("o", to_host(o), ro, BF16_REL_L2, BF16_MAX_ABS)
+    assert_close("lse", to_host(lse), rl, BF16_REL_L2, BF16_MAX_ABS)
+    gv = to_host(vc)
+    for b, L in enumerate(starts):
+        assert_close_scaled(f"v_cache[{b}] appended", gv[b, L:L + T_q], rvc[b, L:L + T_q],
+                            BF16_REL_L2)
+        assert np.array_equal(gv[b, :L], case["vcf"][b, :L])
