@@ -12,7 +12,9 @@ recorded on the launch stream around every kernel.
 The single-token decode over the ragged d20 cache (B=64, H=10, lengths
 uniform in [1, 2048]) is timed in its own loop and reported under "decode";
 it rotates three separately allocated caches so that no call finds its
-cache in the 256 MB Infinity Cache.  The call time comes from HIP events
+cache in the 256 MB Infinity Cache; the same step with the new token's
+append and the QK norm + rotary embedding folded in is reported beside it
+("with_append_rope_us").  The call time comes from HIP events
 around each call; the split/combine breakdown from a second loop that also
 records an event between the two kernels (which adds a gap of its own).
 
@@ -550,6 +552,35 @@ def main():
             "combine_avg_us": round(float(np.mean(comb)) * 1e3, 2),
             "split_GB_per_s": round(split_gbs, 1), "iters": nd, "rotated_caches": 3,
         }
+        # the engine's per-token step: append the new token's rows (QK norm and
+        # rotary embedding folded in), then attend over them with the cache
+        act, ast = (torch.from_numpy(a).to(dev) for a in W.make_angle_tables(Tc, D // 2, seed=4))
+        dnew = W.make_train_inputs(cfg, B=Bd, T=1, H=Hd, seed=7)
+        kn_d, vn_d = dev_t(dnew.k_store), dev_t(dnew.v_store)
+        lens_app = torch.from_numpy(np.minimum(dinp.seqlens, Tc - 1).astype(np.int32)).to(dev)
+        deps = ctypes.c_float(1e-6)
+
+        def astep(i):
+            kc, vc = caches[i % 3]
+            e = devs[i]
+            ev.record(e[0], stream)
+            st = lib.na_attn_decode_append(ptr(qd), ptr(kn_d), ptr(vn_d), ptr(kc), ptr(vc),
+                                           ptr(lens_app), ptr(act), ptr(ast), Tc, deps, None,
+                                           None, ptr(od), ptr(lsed), Bd, Hd, Hd, D, Tc, -1,
+                                           ptr(ws), wsb, P(stream))
+            if st:
+                raise RuntimeError(lib.na_last_error().decode())
+            ev.record(e[2], stream)
+
+        for i in range(5):
+            astep(i)
+        torch.cuda.synchronize()
+        for i in range(5, nd + 5):
+            astep(i)
+        torch.cuda.synchronize()
+        a_ms = float(np.mean([ev.ms(devs[i][0], devs[i][2]) for i in range(5, nd + 5)]))
+        result["decode"]["with_append_rope_us"] = round(a_ms * 1e3, 2)
+        del kn_d, vn_d
         log(f"decode {result['decode']}")
         if wlen is not None:
             for i in range(5):

@@ -12,6 +12,8 @@ Functions (names match the C entry points):
   attn_fwd(q, k, v)                       -> (o, lse)
   attn_bwd(q, k, v, o, dout, lse)         -> (dq, dk, dv, delta)
   attn_decode(q, k_cache, v_cache, seqlens) -> (o, lse)
+  attn_decode_append(q, k_new, v_new, k_cache, v_cache, seqlens) -> (o, lse)
+                                          (appends the new token's key/value rows first)
   attn_prefill(q, k_new, v_new, k_cache, v_cache, cache_lens) -> (o, lse)
                                           (appends k_new, v_new to the caches in place)
   qk_norm_rope_fwd(q, k, cos, sin)        -> (q_out, k_out)   (the prologue: RMS
@@ -34,7 +36,8 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["attn_fwd", "attn_bwd", "attn_decode", "attn_prefill", "qk_norm_rope_fwd",
+__all__ = ["attn_fwd", "attn_bwd", "attn_decode", "attn_decode_append", "attn_prefill",
+           "qk_norm_rope_fwd",
            "qk_norm_rope_bwd", "value_gate_fwd", "value_gate_bwd", "decode_workspace_bytes",
            "bwd_workspace_bytes",
            "load_library",
@@ -98,6 +101,8 @@ def load_library():
                                         ctypes.c_float, vp]
     lib.na_attn_prefill_rope.argtypes = [vp, vp, vp, vp, vp, vp, f32p, f32p, i, ctypes.c_float,
                                          vp, vp, vp, f32p, i, i, i, i, i, i, i, vp]
+    lib.na_attn_decode_append.argtypes = [vp, vp, vp, vp, vp, vp, f32p, f32p, i, ctypes.c_float,
+                                          vp, vp, vp, f32p, i, i, i, i, i, i, vp, sz, vp]
     lib.na_value_gate_fwd.argtypes = [vp, vp, vp, vp, i, i, i, i, vp]
     lib.na_value_gate_bwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, vp]
     lib.na_qk_norm_rope_bwd.argtypes = [vp, vp, vp, vp, vp, vp, f32p, f32p, vp, i, i, i, i, i,
@@ -107,7 +112,7 @@ def load_library():
                "na_attn_fwd_window", "na_attn_bwd_window", "na_attn_decode_window",
                "na_attn_fwd_gqa", "na_attn_bwd_gqa", "na_attn_decode_gqa", "na_attn_prefill",
                "na_qk_norm_rope_fwd", "na_qk_norm_rope_bwd", "na_value_gate_fwd",
-               "na_value_gate_bwd", "na_attn_prefill_rope"):
+               "na_value_gate_bwd", "na_attn_prefill_rope", "na_attn_decode_append"):
         getattr(lib, fn).restype = ctypes.c_int
     lib.na_status_string.argtypes = [ctypes.c_int]
     lib.na_status_string.restype = ctypes.c_char_p
@@ -303,6 +308,61 @@ def attn_decode(q, k_cache, v_cache, seqlens, o=None, lse=None, workspace=None,
     else:
         _check(lib, "na_attn_decode",
                lib.na_attn_decode(*args, B, H, D, T_cap, _ptr(workspace), ws_bytes, _stream(q)))
+    return o, lse
+
+
+def attn_decode_append(q, k_new, v_new, k_cache, v_cache, seqlens, o=None, lse=None,
+                       workspace=None, want_lse=True, window=None, rope=None, eps=1e-6,
+                       value_gate=None):
+    """Decode step with the append: writes k_new, v_new (B, H_kv, 128) at row
+    seqlens[b] of the caches (in place; seqlens is not updated), then the
+    query attends over rows 0 .. seqlens[b].  rope=(cos, sin) float32
+    (T_tab >= T_cap, 64): q and k_new are raw heads, normalised and rotated
+    at that position; value_gate=(ve, gate): the appended value row is
+    v_new + 3 sigmoid(gate) ve.  Returns (o, lse)."""
+    import torch
+    lib = load_library()
+    _require(q.is_cuda and q.dtype == torch.bfloat16 and q.dim() == 3 and q.shape[-1] == HEAD_DIM,
+             "q must be a bf16 GPU tensor (B, H, 128)")
+    B, H, D = q.shape
+    _require(k_cache.dim() == 4 and k_cache.shape[0] == B and k_cache.shape[3] == D
+             and k_cache.shape[2] >= 1 and H % k_cache.shape[2] == 0,
+             "k_cache must be (B, T_cap, H_kv, 128) with H a multiple of H_kv")
+    T_cap, Hk = k_cache.shape[1], k_cache.shape[2]
+    for n, t, shape in (("q", q, q.shape), ("k_new", k_new, (B, Hk, D)),
+                        ("v_new", v_new, (B, Hk, D)), ("k_cache", k_cache, k_cache.shape),
+                        ("v_cache", v_cache, k_cache.shape)):
+        _require(t.dtype == torch.bfloat16 and t.device == q.device and t.is_contiguous()
+                 and tuple(t.shape) == tuple(shape), f"{n} must be contiguous bf16 {tuple(shape)}")
+    _require(seqlens.dtype == torch.int32 and seqlens.shape == (B,) and seqlens.device == q.device
+             and seqlens.is_contiguous(), "seqlens must be int32 [B] on the GPU")
+    cos = sin = ve = gate = None
+    if rope is not None:
+        cos, sin = rope
+        for n, t in (("cos", cos), ("sin", sin)):
+            _require(t.dtype == torch.float32 and t.device == q.device and t.is_contiguous()
+                     and t.dim() == 2 and t.shape[1] == D // 2 and t.shape == cos.shape
+                     and t.shape[0] >= T_cap, f"{n} must be contiguous float32 (T_tab >= T_cap, 64)")
+    if value_gate is not None:
+        ve, gate = value_gate
+        _require(ve.dtype == torch.bfloat16 and tuple(ve.shape) == (B, Hk, D)
+                 and ve.is_contiguous() and ve.device == q.device, "ve must be bf16 (B, H_kv, 128)")
+        _require(gate.dtype == torch.bfloat16 and tuple(gate.shape) == (B, Hk)
+                 and gate.is_contiguous() and gate.device == q.device, "gate must be bf16 (B, H_kv)")
+    o = torch.empty_like(q) if o is None else o
+    if want_lse and lse is None:
+        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    need = decode_workspace_bytes(B, H, T_cap, D)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    window = _window(window)
+    _check(lib, "na_attn_decode_append",
+           lib.na_attn_decode_append(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache),
+                                     _ptr(v_cache), _ptr(seqlens), _ptr(cos), _ptr(sin),
+                                     0 if cos is None else cos.shape[0], float(eps), _ptr(ve),
+                                     _ptr(gate), _ptr(o), _ptr(lse), B, H, Hk, D, T_cap,
+                                     -1 if window is None else window, _ptr(workspace),
+                                     workspace.numel() * workspace.element_size(), _stream(q)))
     return o, lse
 
 

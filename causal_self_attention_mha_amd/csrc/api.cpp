@@ -277,6 +277,50 @@ na_status na_attn_decode_gqa(const void* q, const void* k_cache, const void* v_c
                     "na_attn_decode");
 }
 
+na_status na_attn_decode_append(const void* q, const void* k_new, const void* v_new,
+                                void* k_cache, void* v_cache, const int* seqlens,
+                                const float* cos_tab, const float* sin_tab, int T_tab, float eps,
+                                const void* ve, const void* gate, void* o, float* lse, int B,
+                                int H, int H_kv, int D, int T_cap, int window, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  na_status st = check_sizes(B, T_cap, H, D);
+  if (st) return st;
+  if ((st = check_kv_heads(H, H_kv))) return st;
+  if (lse != nullptr)
+    st = check_ptrs({{q, "q"}, {k_new, "k_new"}, {v_new, "v_new"}, {seqlens, "seqlens"}},
+                    {{k_cache, "k_cache"}, {v_cache, "v_cache"}, {o, "o"}, {lse, "lse"},
+                     {workspace, "workspace"}});
+  else
+    st = check_ptrs({{q, "q"}, {k_new, "k_new"}, {v_new, "v_new"}, {seqlens, "seqlens"}},
+                    {{k_cache, "k_cache"}, {v_cache, "v_cache"}, {o, "o"},
+                     {workspace, "workspace"}});
+  if (st) return st;
+  if ((cos_tab == nullptr) != (sin_tab == nullptr))
+    return fail(NA_ERR_INVALID_ARG, "cos_tab and sin_tab are given together or not at all");
+  if (cos_tab != nullptr) {
+    if ((st = check_ptrs({{cos_tab, "cos_tab"}, {sin_tab, "sin_tab"}}, {{o, "o"}}))) return st;
+    if (T_tab < T_cap)
+      return fail(NA_ERR_INVALID_ARG, "T_tab=%d is smaller than T_cap=%d", T_tab, T_cap);
+    if ((long double)T_tab * D > 2147483647.0L)
+      return fail(NA_ERR_UNSUPPORTED, "the rotary tables (T_tab=%d) exceed 2^31-1 elements",
+                  T_tab);
+    if (!(eps >= 0.f) || eps > 3.0e38f)
+      return fail(NA_ERR_INVALID_ARG, "eps must be finite and >= 0");
+  }
+  if ((ve == nullptr) != (gate == nullptr))
+    return fail(NA_ERR_INVALID_ARG, "ve and gate are given together or not at all");
+  if (ve != nullptr && (st = check_ptrs({{ve, "ve"}, {gate, "gate"}}, {{o, "o"}}))) return st;
+  if (B > 65535) return fail(NA_ERR_INVALID_ARG, "decode supports B <= 65535 (B=%d)", B);
+  if (H > 32) return fail(NA_ERR_UNSUPPORTED, "decode supports H <= 32 (H=%d)", H);
+  const size_t need = na::decode_workspace_bytes(B, H, T_cap);
+  if (workspace_bytes < need)
+    return fail(NA_ERR_INVALID_ARG, "workspace_bytes %zu < required %zu", workspace_bytes, need);
+  return hip_status(na::launch_decode_bf16(q, k_cache, v_cache, seqlens, o, lse, B, H, H_kv,
+                                           T_cap, window, workspace, (hipStream_t)stream, nullptr,
+                                           k_new, v_new, cos_tab, sin_tab, eps, ve, gate),
+                    "na_attn_decode_append");
+}
+
 na_status na_attn_decode_window(const void* q, const void* k_cache, const void* v_cache,
                                 const int* seqlens, void* o, float* lse, int B, int H, int D,
                                 int T_cap, int window, void* workspace, size_t workspace_bytes,

@@ -74,7 +74,8 @@ template <int GQ>
 __global__ __launch_bounds__(512) void decode_split_kernel(
     const u16* __restrict__ q, const u16* __restrict__ kc, const u16* __restrict__ vc,
     const int* __restrict__ seqlens, float* __restrict__ opart, float* __restrict__ ml, int B,
-    int H, int Hk, int T_cap, float scale, int win) {
+    int H, int Hk, int T_cap, float scale, int win, int app, const float* __restrict__ cos_t,
+    const float* __restrict__ sin_t, float eps) {
   __shared__ int pre[kMaxFlatB + 1];  // pre[b] = non-empty chunks of sequences < b
   const int tid = threadIdx.x;
   const int gi = tid >> 4;  // 16-lane group
@@ -82,7 +83,9 @@ __global__ __launch_bounds__(512) void decode_split_kernel(
   const int NC = n_chunks(T_cap);
   const int P = gridDim.x;
   const bool flat = B <= kMaxFlatB;
-  auto len = [&](int b) { return min(max(seqlens[b], 0), T_cap); };
+  // app = 1: the new token was just appended at row seqlens[b] (clamped to
+  // T_cap - 1), which the sequence now includes
+  auto len = [&](int b) { return min(max(seqlens[b], 0), T_cap - app) + app; };
   // first visible key of a sequence of length L (win < 0: no window)
   auto first_key = [&](int L) { return win < 0 ? 0 : max(0, L - 1 - win); };
   // chunks holding a visible key: first_key(L) / CHUNK .. (L - 1) / CHUNK
@@ -188,15 +191,41 @@ __global__ __launch_bounds__(512) void decode_split_kernel(
   };
 
   float qv[GQ][8];
-  auto set_q = [&](const QRows& r) {
+  // cos_t non-null: the query rows are raw heads, RMS-normalised and rotated
+  // at the query's position L - 1 here (the lane holds elements 8 l16 .. + 7;
+  // the pair partner of element i < 64 is 8 lanes away)
+  auto set_q = [&](const QRows& r, int b) {
 #pragma unroll
-    for (int g = 0; g < GQ; ++g)
+    for (int g = 0; g < GQ; ++g) {
+      float x[8];
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
         const uint32_t u = (&r.x[g].x)[w];
-        qv[g][2 * w] = __uint_as_float(u << 16) * c2;
-        qv[g][2 * w + 1] = __uint_as_float(u & 0xffff0000u) * c2;
+        x[2 * w] = __uint_as_float(u << 16);
+        x[2 * w + 1] = __uint_as_float(u & 0xffff0000u);
       }
+      if (cos_t != nullptr) {  // workgroup-uniform
+        float ss = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ss = fmaf(x[e], x[e], ss);
+        const float rn = __builtin_amdgcn_rsqf(sum16(ss) * (1.f / D) + eps);
+        const size_t tp = static_cast<size_t>(max(len(b) - 1, 0)) * (D / 2) + 8 * (l16 & 7);
+        const float sg = l16 < 8 ? -1.f : 1.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float z = x[e] * rn;
+          x[e] = z;
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float zp = dpp<0x128>(x[e]);  // row_ror:8, the partner lane's element
+          qv[g][e] = fmaf(x[e], cos_t[tp + e], sg * sin_t[tp + e] * zp) * c2;
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qv[g][e] = x[e] * c2;
+      }
+    }
   };
   float m[GQ], l[GQ], acc[GQ][8];
 #pragma unroll
@@ -273,7 +302,7 @@ __global__ __launch_bounds__(512) void decode_split_kernel(
   Batch cur = first_from(static_cast<int>(blockIdx.x));
   if (cur.slot < 0) return;  // uniform: no work for this workgroup
   rows(cur, ak, av);
-  set_q(qrow(cur));
+  set_q(qrow(cur), cur.b);
   while (true) {
     Batch nx = next(cur);
     if (nx.slot >= 0) {
@@ -284,7 +313,7 @@ __global__ __launch_bounds__(512) void decode_split_kernel(
     compute(cur, ak, av);
     __builtin_amdgcn_sched_barrier(0);
     if (nx.slot < 0) break;
-    if (nx.slot != cur.slot) set_q(qb);
+    if (nx.slot != cur.slot) set_q(qb, nx.b);
     cur = nx;
     nx = next(cur);
     if (nx.slot >= 0) {
@@ -295,7 +324,7 @@ __global__ __launch_bounds__(512) void decode_split_kernel(
     compute(cur, bk, bv);
     __builtin_amdgcn_sched_barrier(0);
     if (nx.slot < 0) break;
-    if (nx.slot != cur.slot) set_q(qa);
+    if (nx.slot != cur.slot) set_q(qa, nx.b);
     cur = nx;
   }
 }
@@ -303,9 +332,9 @@ __global__ __launch_bounds__(512) void decode_split_kernel(
 __global__ __launch_bounds__(128) void decode_combine_kernel(
     const float* __restrict__ opart, const float* __restrict__ ml,
     const int* __restrict__ seqlens, u16* __restrict__ o, float* __restrict__ lse, int H,
-    int T_cap, int NC, int win) {
+    int T_cap, int NC, int win, int app) {
   const int h = blockIdx.x, b = blockIdx.y;
-  const int L = min(max(seqlens[b], 0), T_cap);
+  const int L = min(max(seqlens[b], 0), T_cap - app) + app;
   const int nc = (L + CHUNK - 1) / CHUNK;                         // chunks end here
   const int c_lo = win < 0 || L == 0 ? 0 : max(0, L - 1 - win) / CHUNK;  // and start here
   const int d = threadIdx.x;
@@ -355,7 +384,9 @@ std::size_t decode_workspace_bytes(int B, int H, int T_cap) {
 
 hipError_t launch_decode_bf16(const void* q, const void* kc, const void* vc, const int* seqlens,
                               void* o, float* lse, int B, int H, int Hk, int T_cap,
-                              int window, void* ws, hipStream_t s, hipEvent_t const* ev) {
+                              int window, void* ws, hipStream_t s, hipEvent_t const* ev,
+                              const void* k_new, const void* v_new, const float* cos_t,
+                              const float* sin_t, float eps, const void* ve, const void* gate) {
   const float scale = 1.0f / sqrtf(static_cast<float>(D));
   const int NC = n_chunks(T_cap);
   // a window that covers the whole cache is no window
@@ -376,17 +407,23 @@ hipError_t launch_decode_bf16(const void* q, const void* kc, const void* vc, con
   const int P = static_cast<int>(std::min<long>(slots, static_cast<long>(per_cu) * cus));
   hipError_t e = mark(ev, 0, s);
   if (e != hipSuccess) return e;
+  const int app = k_new != nullptr ? 1 : 0;
+  if (app) {
+    e = launch_kv_append_bf16(k_new, v_new, const_cast<void*>(kc), const_cast<void*>(vc),
+                              seqlens, B, 1, Hk, T_cap, cos_t, sin_t, eps, ve, gate, s);
+    if (e != hipSuccess) return e;
+  }
   auto* split = gq == 4   ? decode_split_kernel<4>
                 : gq == 2 ? decode_split_kernel<2>
                           : decode_split_kernel<1>;
   e = launch(split, dim3(P), dim3(16 * (H / gq)), 0, s, static_cast<const u16*>(q),
              static_cast<const u16*>(kc), static_cast<const u16*>(vc), seqlens, opart, ml, B, H,
-             Hk, T_cap, scale, win);
+             Hk, T_cap, scale, win, app, cos_t, sin_t, eps);
   if (e != hipSuccess) return e;
   if ((e = mark(ev, 1, s)) != hipSuccess) return e;
   e = launch(decode_combine_kernel, dim3(H, B), dim3(128), 0, s, static_cast<const float*>(opart),
              static_cast<const float*>(ml), seqlens, static_cast<u16*>(o), lse, H, T_cap, NC,
-             win);
+             win, app);
   if (e != hipSuccess) return e;
   return mark(ev, 2, s);
 }

@@ -394,20 +394,28 @@ __global__ __launch_bounds__(256) void kv_append_kernel(const u16* __restrict__ 
   st16(vc + dst, vv);
 }
 
+hipError_t launch_kv_append_bf16(const void* k_new, const void* v_new, void* kc, void* vc,
+                                 const int* lens, int B, int T, int Hk, int Tc,
+                                 const float* cos_t, const float* sin_t, float eps,
+                                 const void* ve, const void* gate, hipStream_t s) {
+  const bool rope = cos_t != nullptr, gated = ve != nullptr;
+  const long chunks = static_cast<long>(B) * T * Hk * D / 8;
+  auto* append = rope ? (gated ? kv_append_kernel<true, true> : kv_append_kernel<true, false>)
+                      : (gated ? kv_append_kernel<false, true> : kv_append_kernel<false, false>);
+  return launch(append, dim3(static_cast<unsigned>((chunks + 255) / 256)), dim3(256), 0, s,
+                static_cast<const u16*>(k_new), static_cast<const u16*>(v_new),
+                static_cast<u16*>(kc), static_cast<u16*>(vc), lens, T, Tc, Hk, chunks, cos_t,
+                sin_t, eps, static_cast<const u16*>(ve), static_cast<const u16*>(gate));
+}
+
 hipError_t launch_prefill_bf16(const void* q, const void* k_new, const void* v_new, void* kc,
                                void* vc, const int* lens, void* o, float* lse, int B, int T,
                                int H, int Hk, int Tc, int window, hipStream_t s,
                                const float* cos_t, const float* sin_t, float eps,
                                const void* ve, const void* gate) {
-  const bool rope = cos_t != nullptr, gated = ve != nullptr;
-  const long chunks = static_cast<long>(B) * T * Hk * D / 8;
-  auto* append = rope ? (gated ? kv_append_kernel<true, true> : kv_append_kernel<true, false>)
-                      : (gated ? kv_append_kernel<false, true> : kv_append_kernel<false, false>);
-  hipError_t e = launch(append, dim3(static_cast<unsigned>((chunks + 255) / 256)), dim3(256), 0,
-                        s, static_cast<const u16*>(k_new), static_cast<const u16*>(v_new),
-                        static_cast<u16*>(kc), static_cast<u16*>(vc), lens, T, Tc, Hk, chunks,
-                        cos_t, sin_t, eps, static_cast<const u16*>(ve),
-                        static_cast<const u16*>(gate));
+  const bool rope = cos_t != nullptr;
+  hipError_t e = launch_kv_append_bf16(k_new, v_new, kc, vc, lens, B, T, Hk, Tc, cos_t, sin_t,
+                                       eps, ve, gate, s);
   if (e != hipSuccess) return e;
   const float scale = 1.0f / sqrtf(static_cast<float>(D));
   const float c_log2 = scale * 1.4426950408889634f;

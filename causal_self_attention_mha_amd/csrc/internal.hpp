@@ -49,11 +49,29 @@ hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const vo
                            hipStream_t s, hipEvent_t const* ev = nullptr);
 std::size_t bwd_workspace_bytes(int B, int T, int H);
 
+// bf16 append of T new key/value rows per sequence at cache rows
+// clamp(lens[b], 0, Tc - T) .. + T - 1, with the optional QK norm + rotary
+// embedding of the key rows (cos_t non-null) and value-embedding gate (ve
+// non-null) on the way.
+hipError_t launch_kv_append_bf16(const void* k_new, const void* v_new, void* kc, void* vc,
+                                 const int* lens, int B, int T, int Hk, int Tc,
+                                 const float* cos_t, const float* sin_t, float eps,
+                                 const void* ve, const void* gate, hipStream_t s);
+
 // Decode workspace layout and size (bytes).
 std::size_t decode_workspace_bytes(int B, int H, int T_cap);
+// With k_new non-null, the new token's key/value rows (B, Hk, D) are first
+// appended at row clamp(seqlens[b], 0, T_cap - 1) (launch_kv_append_bf16 with
+// T = 1, rotated / gated as given) and the sequence then includes it; with
+// cos_t non-null the query rows are raw heads, normalised and rotated at the
+// query's position.
 hipError_t launch_decode_bf16(const void* q, const void* kc, const void* vc, const int* seqlens,
                               void* o, float* lse, int B, int H, int Hk, int T_cap, int window,
-                              void* ws, hipStream_t s, hipEvent_t const* ev = nullptr);
+                              void* ws, hipStream_t s, hipEvent_t const* ev = nullptr,
+                              const void* k_new = nullptr, const void* v_new = nullptr,
+                              const float* cos_t = nullptr, const float* sin_t = nullptr,
+                              float eps = 0.f, const void* ve = nullptr,
+                              const void* gate = nullptr);
 
 // bf16 QK normalisation + rotary embedding of q (B, T, H, D) and k (B, T, Hk, D)
 // at positions t + clamp(off[b], 0, T_tab - T) (off may be null: positions t)

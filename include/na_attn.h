@@ -292,6 +292,31 @@ na_status na_attn_prefill_rope(const void* q, const void* k_new, const void* v_n
                                int T_q, int H, int H_kv, int D, int T_cap, int window,
                                void* stream);
 
+/*
+ * Decode step with the append (the inference engine's per-token call of
+ * flash_attn_with_kvcache with the new key and value, blog section 6): for
+ * each sequence b, the new token's key/value rows k_new[b], v_new[b] are
+ * written to cache row L = seqlens[b] (rows already cached; clamped to
+ * [0, T_cap - 1] on the device, not updated: the caller adds 1), then the
+ * query attends over rows 0 .. L (with a window, L - window .. L) exactly as
+ * na_attn_decode_gqa over L + 1 rows.
+ * Optional prologue, as in na_attn_prefill_rope: with cos_tab, sin_tab (fp32
+ * (T_tab, D/2), T_tab >= T_cap; both or neither) q and k_new are raw heads,
+ * RMS-normalised (eps) and rotated at position L (k_new in the append, q as
+ * the decode loads it); with ve, gate (bf16 (B, H_kv, D) and (B, H_kv); both
+ * or neither) the value row is appended as v_new + 3 sigmoid(gate) ve.
+ * q: bf16 (B, H, D); k_new, v_new: bf16 (B, H_kv, D); caches bf16
+ * (B, T_cap, H_kv, D), read and written (only row L changes).  o, lse,
+ * workspace and the limits as in na_attn_decode.  Enqueues three kernels:
+ * the append, the split and the combine.
+ */
+na_status na_attn_decode_append(const void* q, const void* k_new, const void* v_new,
+                                void* k_cache, void* v_cache, const int* seqlens,
+                                const float* cos_tab, const float* sin_tab, int T_tab, float eps,
+                                const void* ve, const void* gate, void* o, float* lse, int B,
+                                int H, int H_kv, int D, int T_cap, int window, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
 /* Static text for a status code. */
 const char* na_status_string(na_status s);
 

@@ -37,7 +37,7 @@ def test_header_declares_the_entry_points():
               "na_attn_fwd_window", "na_attn_bwd_window", "na_attn_decode_window",
               "na_attn_fwd_gqa", "na_attn_bwd_gqa", "na_attn_decode_gqa", "na_attn_prefill",
               "na_qk_norm_rope_fwd", "na_qk_norm_rope_bwd", "na_value_gate_fwd",
-              "na_value_gate_bwd", "na_attn_prefill_rope"):
+              "na_value_gate_bwd", "na_attn_prefill_rope", "na_attn_decode_append"):
         assert s in syms
 
 
@@ -200,6 +200,22 @@ def test_prefill_rope_checks_its_arguments(lib):
     bad = list(p)
     bad[8] = bad[0]              # o aliases q
     assert call(bad) == INVALID
+
+
+def test_decode_append_checks_its_arguments(lib):
+    p = [A + 0x100 * i for i in range(14)]
+    need = lib.na_attn_decode_workspace_bytes(4, 6, 128, 64)
+    # q k_new v_new k_cache v_cache seqlens cos sin T_tab eps ve gate o lse ... ws
+    call = lambda cos=p[6], sin=p[7], T_tab=64, ve=None, g=None, ws=need: (  # noqa: E731
+        lib.na_attn_decode_append(p[0], p[1], p[2], p[3], p[4], p[5], cos, sin, T_tab, 1e-6, ve, g,
+                                  p[8], p[9], 4, 6, 3, 128, 64, -1, p[13], ws, None))
+    assert call(T_tab=32) == INVALID and b"T_tab" in lib.na_last_error()
+    assert call(sin=None) == INVALID and b"together" in lib.na_last_error()
+    assert call(ve=p[10]) == INVALID
+    assert call(ws=need - 4) == INVALID and b"workspace" in lib.na_last_error()
+    assert lib.na_attn_decode_append(p[0], p[1], p[2], p[3], p[4], p[5], None, None, 0, 0.0, None,
+                                     None, p[8], p[9], 4, 6, 4, 128, 64, -1, p[13], need,
+                                     None) == INVALID  # H not a multiple of H_kv
 
 
 def test_value_gate_checks_its_arguments(lib):

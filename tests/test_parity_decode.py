@@ -114,3 +114,85 @@ def test_decode_few_heads_many_sequences(dev, H, B):
     inp = W.make_decode_inputs(B=B, T_cap=300, H=H, seed=15 + H, seqlens=lens)
     o, lse = run_decode(inp, dev)
     check(inp, o, lse)
+
+
+# ---------------------------------------------------------------- decode step with the append
+
+APPEND_CASES = [  # B, H, Hk, T_cap, window, rope, gate
+    (16, 4, 4, 300, None, False, False),
+    (10, 8, 2, 500, 100, True, True),
+    (64, 10, 10, 2048, None, True, False),
+    (12, 6, 3, 256, None, False, True),
+]
+
+
+@pytest.mark.parametrize("B,H,Hk,T_cap,Wn,rope,gate", APPEND_CASES)
+def test_decode_append(dev, B, H, Hk, T_cap, Wn, rope, gate):
+    """na_attn_decode_append: the new token's key/value rows go to row
+    L = clamp(seqlens[b], 0, T_cap - 1) (optionally normalised and rotated,
+    and gated), then the query (optionally normalised and rotated at L)
+    attends over rows 0 .. L; against the oracle on the cache with that row
+    written.  Every other cache row is left as it was."""
+    import torch
+    import causal_self_attention_mha_amd as na
+    from parity_util import assert_close_scaled
+    rng = np.random.default_rng(500 + B + T_cap)
+    lens = rng.integers(0, T_cap, size=B)
+    lens[:3] = [0, T_cap - 1, T_cap + 50]              # empty, last row, clamped
+    cache = W.make_decode_inputs(B=B, T_cap=T_cap, H=Hk, seed=501 + B,
+                                 seqlens=np.minimum(np.maximum(lens, 1), T_cap))
+    qin = W.make_decode_inputs(B=B, T_cap=1, H=H, seed=502 + B, seqlens=[1] * B)
+    new = W.make_train_inputs("d20", B=B, T=1, H=Hk, seed=503 + B)
+    kn_st, vn_st = new.k_store.reshape(B, Hk, 128), new.v_store.reshape(B, Hk, 128)
+    kn, vn = new.k.reshape(B, Hk, 128).astype(np.float64), new.v.reshape(B, Hk, 128).astype(np.float64)
+    L = np.minimum(np.maximum(lens, 0), T_cap - 1)
+    c = s = None
+    if rope:
+        c, s = (a.astype(np.float32) for a in oracle.rope_tables(T_cap, 128))
+    ve_st = g_st = None
+    if gate:
+        vein = W.make_train_inputs("d20", B=B, T=1, H=Hk, seed=504 + B)
+        ve_st, ve = vein.k_store.reshape(B, Hk, 128), vein.k.reshape(B, Hk, 128).astype(np.float64)
+        g, g_st = W.make_gate_logits(B, 1, Hk, seed=505 + B)
+        g_st, g = g_st.reshape(B, Hk), g.reshape(B, Hk)
+    q, kc, vc = (to_device(a, dev) for a in (qin.q_store, cache.k_store, cache.v_store))
+    kc0, vc0 = to_host(kc), to_host(vc)
+    args = dict(window=Wn)
+    if rope:
+        args["rope"] = (torch.from_numpy(c).to(dev), torch.from_numpy(s).to(dev))
+    if gate:
+        args["value_gate"] = (to_device(ve_st, dev), to_device(g_st, dev))
+    o, lse = na.attn_decode_append(q, to_device(kn_st, dev), to_device(vn_st, dev), kc, vc,
+                                   torch.from_numpy(lens.astype(np.int32)).to(dev), **args)
+    torch.cuda.synchronize()
+    # the oracle: the same rows through the oracle's prologue, written into the cache
+    qf = qin.q.astype(np.float64)
+    kr, vr = kn.copy(), vn.copy()
+    if rope:
+        c64, s64 = c.astype(np.float64), s.astype(np.float64)
+        for b in range(B):
+            p = int(L[b])
+            qf[b] = oracle.qk_norm_rope_forward(qf[b][None, None], c64[p:p + 1], s64[p:p + 1])[0, 0]
+            kr[b] = oracle.qk_norm_rope_forward(kn[b][None, None], c64[p:p + 1], s64[p:p + 1])[0, 0]
+    if gate:
+        vr = oracle.value_gate_forward(vn, ve, g)
+    kcr, vcr = cache.k_cache.astype(np.float64).copy(), cache.v_cache.astype(np.float64).copy()
+    for b in range(B):
+        kcr[b, L[b]] = kr[b]
+        vcr[b, L[b]] = vr[b]
+    ro, rl = oracle.decode(qf, kcr, vcr, L + 1, window=Wn)
+    assert_close("o", to_host(o), ro, BF16_REL_L2, BF16_MAX_ABS)
+    assert_close("lse", to_host(lse), rl, BF16_REL_L2, BF16_MAX_ABS)
+    gk, gv = to_host(kc), to_host(vc)
+    rows = (np.arange(B), L)
+    if rope:
+        assert_close("k row", gk[rows], kr, BF16_REL_L2, BF16_MAX_ABS)
+    else:
+        assert np.array_equal(gk[rows], kn)
+    if gate:
+        assert_close_scaled("v row", gv[rows], vr, BF16_REL_L2)
+    else:
+        assert np.array_equal(gv[rows], vn)
+    keep = np.ones((B, T_cap), dtype=bool)
+    keep[rows] = False
+    assert np.array_equal(gk[keep], kc0[keep]) and np.array_equal(gv[keep], vc0[keep])
