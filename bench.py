@@ -482,7 +482,46 @@ def main():
                            "traffic_bwd": recorded_traffic("value_gate_bwd")},
             "calls": args.steps}
         log(f"prologue {result['prologue']}")
-        del yq, yk, rgq, rgk, gt
+        # the d20 step with the prologue: prologue forward, attention forward and
+        # backward, prologue backward as its own kernel or folded into the
+        # attention backward's epilogues (na_attn_bwd_rope)
+        tdq, tdk, tdv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+
+        def pro_step(folded):
+            rfwd()  # yq, yk = rotated q, k
+            st = lib.na_attn_fwd(ptr(yq), ptr(yk), ptr(v), ptr(o), ptr(lse), B, T, H, D,
+                                 P(stream))
+            if st:
+                raise RuntimeError(lib.na_last_error().decode())
+            if folded:
+                st = lib.na_attn_bwd_rope(ptr(yq), ptr(yk), ptr(v), ptr(o), ptr(do), ptr(lse),
+                                          ptr(q), ptr(k), ptr(ct), ptr(sn), T, eps, ptr(tdq),
+                                          ptr(tdk), ptr(tdv), ptr(delta), ptr(ws), ws_bytes, B, T,
+                                          H, H, D, -1, P(stream))
+            else:
+                st = lib.na_attn_bwd(ptr(yq), ptr(yk), ptr(v), ptr(o), ptr(do), ptr(lse),
+                                     ptr(rgq), ptr(rgk), ptr(tdv), ptr(delta), ptr(ws), ws_bytes,
+                                     B, T, H, D, P(stream))
+                if not st:
+                    st = lib.na_qk_norm_rope_bwd(ptr(q), ptr(k), ptr(rgq), ptr(rgk), ptr(tdq),
+                                                 ptr(tdk), ptr(ct), ptr(sn), None, B, T, H, H, D,
+                                                 T, eps, P(stream))
+            if st:
+                raise RuntimeError(lib.na_last_error().decode())
+
+        step_ms = {}
+        for name, folded in (("folded_bwd", True), ("separate_bwd", False)):
+            for _ in range(args.warmup):
+                pro_step(folded)
+            torch.cuda.synchronize()
+            ev.record(rev[0], stream)
+            for _ in range(args.steps):
+                pro_step(folded)
+            ev.record(rev[1], stream)
+            torch.cuda.synchronize()
+            step_ms[name] = round(ev.ms(rev[0], rev[1]) / args.steps, 4)
+        result["prologue"]["d20_step_with_prologue_ms"] = step_ms
+        del yq, yk, rgq, rgk, gt, tdq, tdk, tdv
 
     del q, k, v, do, o, dq, dk, dv, ws
     torch.cuda.empty_cache()

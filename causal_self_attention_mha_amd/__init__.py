@@ -103,6 +103,9 @@ def load_library():
                                          vp, vp, vp, f32p, i, i, i, i, i, i, i, vp]
     lib.na_attn_decode_append.argtypes = [vp, vp, vp, vp, vp, vp, f32p, f32p, i, ctypes.c_float,
                                           vp, vp, vp, f32p, i, i, i, i, i, i, vp, sz, vp]
+    lib.na_attn_bwd_rope.argtypes = [vp, vp, vp, vp, vp, f32p, vp, vp, f32p, f32p, i,
+                                     ctypes.c_float, vp, vp, vp, f32p, vp, sz, i, i, i, i, i, i,
+                                     vp]
     lib.na_value_gate_fwd.argtypes = [vp, vp, vp, vp, i, i, i, i, vp]
     lib.na_value_gate_bwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, vp]
     lib.na_qk_norm_rope_bwd.argtypes = [vp, vp, vp, vp, vp, vp, f32p, f32p, vp, i, i, i, i, i,
@@ -112,7 +115,8 @@ def load_library():
                "na_attn_fwd_window", "na_attn_bwd_window", "na_attn_decode_window",
                "na_attn_fwd_gqa", "na_attn_bwd_gqa", "na_attn_decode_gqa", "na_attn_prefill",
                "na_qk_norm_rope_fwd", "na_qk_norm_rope_bwd", "na_value_gate_fwd",
-               "na_value_gate_bwd", "na_attn_prefill_rope", "na_attn_decode_append"):
+               "na_value_gate_bwd", "na_attn_prefill_rope", "na_attn_decode_append",
+               "na_attn_bwd_rope"):
         getattr(lib, fn).restype = ctypes.c_int
     lib.na_status_string.argtypes = [ctypes.c_int]
     lib.na_status_string.restype = ctypes.c_char_p
@@ -212,13 +216,17 @@ def bwd_workspace_bytes(B, T, H, D=HEAD_DIM):
 
 
 def attn_bwd(q, k, v, o, dout, lse, dq=None, dk=None, dv=None, delta=None, workspace=None,
-             recompute_dq=False, window=None):
+             recompute_dq=False, window=None, rope=None, eps=1e-6):
     """Causal attention backward.  Returns (dq, dk, dv, delta).
 
     bf16: by default a dS workspace is allocated (or `workspace` is used) so
     that dq is a GEMM over the stored dS; recompute_dq=True passes no
     workspace and the dq pass recomputes S and dP (plain causal only: a
-    window needs the workspace).  fp32 has one path."""
+    window needs the workspace).  fp32 has one path.
+    rope=(q_raw, k_raw, cos, sin): q and k are the outputs of
+    qk_norm_rope_fwd(q_raw, k_raw, cos, sin); dq and dk are returned as the
+    gradients of q_raw and k_raw, the prologue's backward done in the same
+    kernels (na_attn_bwd_rope)."""
     import torch
     lib = load_library()
     Hk = _kv_heads(q, k)
@@ -249,7 +257,21 @@ def attn_bwd(q, k, v, o, dout, lse, dq=None, dk=None, dv=None, delta=None, works
         args = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk),
                 _ptr(dv), _ptr(delta), _ptr(workspace), ws_bytes)
         w = -1 if window is None else window
-        if Hk != H:
+        if rope is not None:
+            q_raw, k_raw, cos, sin = rope
+            _require(workspace is not None, "rope needs the dS workspace (recompute_dq=False)")
+            _check_train(("q", "q_raw", "k_raw"), (q, q_raw, k_raw), dtype, kv_heads={"k_raw": Hk})
+            for n, t in (("cos", cos), ("sin", sin)):
+                _require(t.dtype == torch.float32 and t.device == q.device and t.is_contiguous()
+                         and t.dim() == 2 and t.shape[1] == D // 2 and t.shape == cos.shape
+                         and t.shape[0] >= T, f"{n} must be contiguous float32 (T_tab >= T, 64)")
+            _check(lib, "na_attn_bwd_rope",
+                   lib.na_attn_bwd_rope(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse),
+                                        _ptr(q_raw), _ptr(k_raw), _ptr(cos), _ptr(sin),
+                                        cos.shape[0], float(eps), _ptr(dq), _ptr(dk), _ptr(dv),
+                                        _ptr(delta), _ptr(workspace), ws_bytes, B, T, H, Hk, D, w,
+                                        _stream(q)))
+        elif Hk != H:
             _check(lib, "na_attn_bwd_gqa",
                    lib.na_attn_bwd_gqa(*args, B, T, H, Hk, D, w, _stream(q), None))
         elif window is not None:

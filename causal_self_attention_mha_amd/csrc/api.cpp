@@ -277,6 +277,36 @@ na_status na_attn_decode_gqa(const void* q, const void* k_cache, const void* v_c
                     "na_attn_decode");
 }
 
+na_status na_attn_bwd_rope(const void* q, const void* k, const void* v, const void* o,
+                           const void* dout, const float* lse, const void* q_raw,
+                           const void* k_raw, const float* cos_tab, const float* sin_tab,
+                           int T_tab, float eps, void* dq, void* dk, void* dv, float* delta,
+                           void* workspace, size_t workspace_bytes, int B, int T, int H,
+                           int H_kv, int D, int window, void* stream) {
+  na_status st = check_sizes(B, T, H, D);
+  if (st) return st;
+  if ((st = check_kv_heads(H, H_kv))) return st;
+  st = check_ptrs({{q, "q"}, {k, "k"}, {v, "v"}, {o, "o"}, {dout, "dout"}, {lse, "lse"},
+                   {q_raw, "q_raw"}, {k_raw, "k_raw"}, {cos_tab, "cos_tab"},
+                   {sin_tab, "sin_tab"}},
+                  {{dq, "dq"}, {dk, "dk"}, {dv, "dv"}, {delta, "delta"},
+                   {workspace, "workspace"}});
+  if (st) return st;
+  if (T_tab < T) return fail(NA_ERR_INVALID_ARG, "T_tab=%d is smaller than T=%d", T_tab, T);
+  if ((long double)T_tab * D > 2147483647.0L)
+    return fail(NA_ERR_UNSUPPORTED, "the rotary tables (T_tab=%d) exceed 2^31-1 elements", T_tab);
+  if (!(eps >= 0.f) || eps > 3.0e38f) return fail(NA_ERR_INVALID_ARG, "eps must be finite and >= 0");
+  if (T > 1048576)
+    return fail(NA_ERR_UNSUPPORTED, "the dS workspace path needs T <= 1048576 (T=%d)", T);
+  const size_t need = na::bwd_workspace_bytes(B, T, H);
+  if (workspace_bytes < need)
+    return fail(NA_ERR_INVALID_ARG, "workspace_bytes %zu < required %zu", workspace_bytes, need);
+  return hip_status(na::launch_bwd_bf16(q, k, v, o, dout, lse, dq, dk, dv, delta, workspace, B, T,
+                                        H, H_kv, window, (hipStream_t)stream, nullptr, q_raw,
+                                        k_raw, cos_tab, sin_tab, eps),
+                    "na_attn_bwd_rope");
+}
+
 na_status na_attn_decode_append(const void* q, const void* k_new, const void* v_new,
                                 void* k_cache, void* v_cache, const int* seqlens,
                                 const float* cos_tab, const float* sin_tab, int T_tab, float eps,

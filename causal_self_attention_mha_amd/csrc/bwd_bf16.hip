@@ -67,6 +67,61 @@ __global__ __launch_bounds__(256) void delta_kernel(const u16* __restrict__ o,
   if (chunk == 0) delta[row] = acc;  // row == (b * H + h) * T + t
 }
 
+// ---------------------------------------------------------------- prologue backward
+
+// With the QK-norm + rotary prologue folded into the backward, the kernels that
+// write dq and dk turn the gradient g of a rotated row into the gradient of
+// the raw row x (readings of the prologue: z = x r, r = 1 / sqrt(mean(x^2) +
+// eps), y = R z with pairs (i, i + 64) turned by +theta):
+//   dz = R^T g,  dx = r (dz - z mean(dz z)).
+struct RopeBwd {
+  const u16* raw;  // the raw q or k, same layout as the gradient
+  const float* cos_t;
+  const float* sin_t;  // fp32 (>= T, 64) tables, row = position
+  float eps;
+};
+
+// 16 lanes per 256-byte row, lane c holding elements 8 c .. 8 c + 7: gradient
+// chunk g16 of the rotated row at position pos, raw chunk x16; returns the
+// raw row's gradient chunk.  Every lane of the 16-lane group takes part.
+__device__ __forceinline__ uint4 rope_bwd_chunk(uint4 g16, uint4 x16, const RopeBwd& ra, int pos,
+                                                int c) {
+  float g[8], x[8];
+  const uint32_t gw[4] = {g16.x, g16.y, g16.z, g16.w}, xw[4] = {x16.x, x16.y, x16.z, x16.w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    g[2 * j] = __uint_as_float(gw[j] << 16);
+    g[2 * j + 1] = __uint_as_float(gw[j] & 0xffff0000u);
+    x[2 * j] = __uint_as_float(xw[j] << 16);
+    x[2 * j + 1] = __uint_as_float(xw[j] & 0xffff0000u);
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ss = fmaf(x[e], x[e], ss);
+  const float r = __builtin_amdgcn_rsqf(sum16(ss) * (1.f / D) + ra.eps);
+  const size_t tp = static_cast<size_t>(pos) * (D / 2) + 8 * (c & 7);
+  const float4 c0 = *reinterpret_cast<const float4*>(ra.cos_t + tp);
+  const float4 c1 = *reinterpret_cast<const float4*>(ra.cos_t + tp + 4);
+  const float4 s0 = *reinterpret_cast<const float4*>(ra.sin_t + tp);
+  const float4 s1 = *reinterpret_cast<const float4*>(ra.sin_t + tp + 4);
+  const float cs[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+  const float sn[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+  const float sg = c < 8 ? 1.f : -1.f;  // dz_i = g_i c + g_{i+64} s, dz_{i+64} = g_{i+64} c - g_i s
+  float dz[8], dot = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float gp = dpp<0x128>(g[e]);  // the partner lane's element (row_ror:8)
+    dz[e] = fmaf(g[e], cs[e], sg * sn[e] * gp);
+    dot = fmaf(dz[e], x[e], dot);
+  }
+  const float m = sum16(dot) * r * (1.f / D);  // mean(dz z)
+  float y[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) y[e] = r * fmaf(-x[e] * r, m, dz[e]);
+  return make_uint4(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]), pack_bf16x2(y[4], y[5]),
+                    pack_bf16x2(y[6], y[7]));
+}
+
 // ---------------------------------------------------------------- dK, dV
 
 constexpr int KT_KEYS = 128;  // keys per workgroup (32 per wavefront)
@@ -227,12 +282,13 @@ __device__ __forceinline__ void to_exp2_offset(float* rows, int lane) {
 // one key/value head, and its query tiles run over the G = H / Hk query heads
 // that read it, so that dK and dV sum the group in registers (GRP = false:
 // Hk = H, G = 1, and the head bookkeeping compiles away).
-template <bool WIN, bool GRP>
+// ROPE: dk is written as the gradient of the raw keys (RopeBwd).
+template <bool WIN, bool GRP, bool ROPE>
 __global__ __launch_bounds__(256, 1) void dkdv_kernel(
     const u16* __restrict__ q, const u16* __restrict__ k, const u16* __restrict__ v,
     const u16* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
     u16* __restrict__ dk, u16* __restrict__ dv, u16* __restrict__ dsw, int nbt, int B, int T,
-    int H, int Hk, float c_log2, float scale, int win) {
+    int H, int Hk, float c_log2, float scale, int win, RopeBwd ra) {
   // NBUF query tiles (q and dout, swizzled, see tile_swz) and their lse, delta rows
   __shared__ __attribute__((aligned(1024))) char qtiles[NBUF * BUF_B];
   __shared__ __attribute__((aligned(1024))) char kstage[2 * TILE_B];  // K rows of an item
@@ -521,8 +577,12 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(
     // wavefront's 4 KiB of LDS, 16 rows at a time, so that 16 lanes store one
     // 256-byte row: stored straight from registers, every lane would write 8
     // bytes to a different row.  Staging rows are swizzled by 16-byte chunk
-    // (chunk c of row r at c ^ r).  LDS operations of one wavefront complete
-    // in order, so no barrier is needed between the rounds.
+    // (chunk c of row r at c ^ r).  Only this wavefront touches its staging
+    // area, so no barrier is needed between the rounds; but the previous
+    // round's reads must be done before a round overwrites the rows, which the
+    // compiler does not see (it may sink a read into the conditional store
+    // that uses it, past the next round's writes): each round starts with an
+    // LDS wait that is also a compiler memory barrier.
 #pragma unroll
     for (int tsel = 0; tsel < 2; ++tsel) {  // dK, then dV
       const f32x16* acc = tsel ? dva : dka;
@@ -530,6 +590,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(
       u16* dst = tsel ? dv : dk;
 #pragma unroll
       for (int sh = 0; sh < 2; ++sh) {  // keys kw0 + 16 sh .. + 15
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         if ((l32 >> 4) == sh) {
           const int rr = l32 & 15;
 #pragma unroll
@@ -546,8 +607,12 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
           const int rr = 4 * m + (lane >> 4), c = lane & 15;
-          const uint4 x = lds_ld16(est_lds + rr * 256 + 16 * (c ^ rr));
+          uint4 x = lds_ld16(est_lds + rr * 256 + 16 * (c ^ rr));
           const int key = kw0 + 16 * sh + rr;
+          if (ROPE && tsel == 0) {  // whole 16-lane groups: key is uniform over one
+            const int kr = min(key, T - 1);
+            x = rope_bwd_chunk(x, ld16(ra.raw + kbase + kr * rsk + 8 * c), ra, kr, c);
+          }
           if (key < T) st16(dst + kbase + key * rsk + 8 * c, x);
         }
       }
@@ -833,12 +898,13 @@ constexpr int DG_KEYS = 64;   // keys per K tile
 constexpr uint32_t DG_DS_B = 2 * 32 * 32 * 2;  // a wavefront's two dS blocks per key tile
 
 // WIN: sliding window, key j visible to query i iff i - win <= j <= i.
-template <bool WIN>
+// ROPE: dq is written as the gradient of the raw queries (RopeBwd).
+template <bool WIN, bool ROPE>
 __global__ __launch_bounds__(64 * DG_WAVES, 8 / DG_WAVES) void dq_gemm_kernel(const u16* __restrict__ k,
                                                          const u16* __restrict__ dsw,
                                                          u16* __restrict__ dq, int nbt, int B,
                                                          int T, int H, int Hk, float scale,
-                                                         int win) {
+                                                         int win, RopeBwd ra) {
   __shared__ __attribute__((aligned(1024))) char ktile[2][kTileBytes];   // swizzled K
   __shared__ __attribute__((aligned(1024))) char sst[3][DG_WAVES][DG_DS_B];  // dS blocks per wave
 
@@ -987,15 +1053,67 @@ __global__ __launch_bounds__(64 * DG_WAVES, 8 / DG_WAVES) void dq_gemm_kernel(co
     }
 
     const int qrow = qw0 + l32;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) dqa[db][e] *= scale;
+    if constexpr (ROPE) {
+      // the lane holds elements d = 32 db + 8 g + 4 half + j of its row (the
+      // other half in lane l ^ 32); d < 64 (db < 2) pairs with d + 64 (db + 2)
+      const int pr = min(qrow, T - 1);
+      const u16* xp = ra.raw + base + static_cast<size_t>(pr) * rs + 4 * half;
+      float x[4][16];
+      float ss = 0.f;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const uint2 w = *reinterpret_cast<const uint2*>(xp + 32 * db + 8 * g);
+          x[db][4 * g] = __uint_as_float(w.x << 16);
+          x[db][4 * g + 1] = __uint_as_float(w.x & 0xffff0000u);
+          x[db][4 * g + 2] = __uint_as_float(w.y << 16);
+          x[db][4 * g + 3] = __uint_as_float(w.y & 0xffff0000u);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) ss = fmaf(x[db][4 * g + j], x[db][4 * g + j], ss);
+        }
+      ss += __shfl_xor(ss, 32, 64);
+      const float rn = __builtin_amdgcn_rsqf(ss * (1.f / D) + ra.eps);
+      const float* cp = ra.cos_t + static_cast<size_t>(pr) * (D / 2) + 4 * half;
+      const float* sp = ra.sin_t + static_cast<size_t>(pr) * (D / 2) + 4 * half;
+      float dot = 0.f;
+#pragma unroll
+      for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const float4 c4 = *reinterpret_cast<const float4*>(cp + 32 * db + 8 * g);
+          const float4 s4 = *reinterpret_cast<const float4*>(sp + 32 * db + 8 * g);
+          const float cs[4] = {c4.x, c4.y, c4.z, c4.w}, sn[4] = {s4.x, s4.y, s4.z, s4.w};
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float g1 = dqa[db][4 * g + j], g2 = dqa[db + 2][4 * g + j];
+            const float d1 = fmaf(g1, cs[j], g2 * sn[j]);    // R^T g, first half
+            const float d2 = fmaf(g2, cs[j], -g1 * sn[j]);   // second half
+            dqa[db][4 * g + j] = d1;
+            dqa[db + 2][4 * g + j] = d2;
+            dot = fmaf(d1, x[db][4 * g + j], fmaf(d2, x[db + 2][4 * g + j], dot));
+          }
+        }
+      dot += __shfl_xor(dot, 32, 64);
+      const float m = dot * rn * (1.f / D);  // mean(dz z)
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          dqa[db][e] = rn * fmaf(-x[db][e] * rn, m, dqa[db][e]);
+    }
     if (qrow < T) {
       u16* qp = dq + base + qrow * rs;
 #pragma unroll
       for (int db = 0; db < 4; ++db)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          uint2 pk = make_uint2(
-              pack_bf16x2(dqa[db][4 * g] * scale, dqa[db][4 * g + 1] * scale),
-              pack_bf16x2(dqa[db][4 * g + 2] * scale, dqa[db][4 * g + 3] * scale));
+          uint2 pk = make_uint2(pack_bf16x2(dqa[db][4 * g], dqa[db][4 * g + 1]),
+                                pack_bf16x2(dqa[db][4 * g + 2], dqa[db][4 * g + 3]));
           *reinterpret_cast<uint2*>(qp + 32 * db + 8 * g + 4 * half) = pk;
         }
     }
@@ -1012,7 +1130,12 @@ std::size_t bwd_workspace_bytes(int B, int T, int H) {
 hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const void* o,
                            const void* dout, const float* lse, void* dq, void* dk, void* dv,
                            float* delta, void* ws, int B, int T, int H, int Hk, int window,
-                           hipStream_t s, hipEvent_t const* ev) {
+                           hipStream_t s, hipEvent_t const* ev, const void* q_raw,
+                           const void* k_raw, const float* cos_t, const float* sin_t, float eps) {
+  const bool rope = q_raw != nullptr;
+  if (rope && ws == nullptr) return hipErrorInvalidValue;  // checked on the host
+  const RopeBwd rq{static_cast<const u16*>(q_raw), cos_t, sin_t, eps};
+  const RopeBwd rk{static_cast<const u16*>(k_raw), cos_t, sin_t, eps};
   const float scale = 1.0f / sqrtf(static_cast<float>(D));
   const float c_log2 = scale * kLog2e;
   const u16* q16 = static_cast<const u16*>(q);
@@ -1035,20 +1158,23 @@ hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const vo
   const bool win = window >= 0 && window < T - 1;
   const int w = win ? window : T;
   const bool grp = Hk != H;
-  auto* kv_kernel = win ? (grp ? dkdv_kernel<true, true> : dkdv_kernel<true, false>)
-                        : (grp ? dkdv_kernel<false, true> : dkdv_kernel<false, false>);
+  auto* kv_kernel =
+      rope ? (win ? (grp ? dkdv_kernel<true, true, true> : dkdv_kernel<true, false, true>)
+                  : (grp ? dkdv_kernel<false, true, true> : dkdv_kernel<false, false, true>))
+           : (win ? (grp ? dkdv_kernel<true, true, false> : dkdv_kernel<true, false, false>)
+                  : (grp ? dkdv_kernel<false, true, false> : dkdv_kernel<false, false, false>));
   e = launch(kv_kernel, kv_grid, dim3(256), 0, s, q16, k16,
              v16, g16, lse, static_cast<const float*>(delta), static_cast<u16*>(dk),
-             static_cast<u16*>(dv), dsw, nbt, B, T, H, Hk, c_log2, scale, w);
+             static_cast<u16*>(dv), dsw, nbt, B, T, H, Hk, c_log2, scale, w, rk);
   if (e != hipSuccess) return e;
   if ((e = mark(ev, 2, s)) != hipSuccess) return e;
   if (dsw != nullptr) {
     const int n_qt = (T + DG_ROWS - 1) / DG_ROWS;
-    e = launch(win ? dq_gemm_kernel<true> : dq_gemm_kernel<false>,
-               dim3(persistent_grid(static_cast<long>(n_qt) * B * H, 8 / DG_WAVES)),
-               dim3(64 * DG_WAVES), 0, s, k16,
-               static_cast<const u16*>(dsw), static_cast<u16*>(dq), nbt, B, T, H, Hk, scale,
-               w);
+    auto* dq_kern = rope ? (win ? dq_gemm_kernel<true, true> : dq_gemm_kernel<false, true>)
+                         : (win ? dq_gemm_kernel<true, false> : dq_gemm_kernel<false, false>);
+    e = launch(dq_kern, dim3(persistent_grid(static_cast<long>(n_qt) * B * H, 8 / DG_WAVES)),
+               dim3(64 * DG_WAVES), 0, s, k16, static_cast<const u16*>(dsw),
+               static_cast<u16*>(dq), nbt, B, T, H, Hk, scale, w, rq);
   } else {
     if (win) return hipErrorInvalidValue;  // the recompute pass has no window (checked on the host)
     const int n_qt = (T + DQ_ROWS - 1) / DQ_ROWS;

@@ -43,10 +43,17 @@ hipError_t launch_prefill_bf16(const void* q, const void* k_new, const void* v_n
 // ws: optional dS workspace of bwd_workspace_bytes(B, T, H) bytes; with it dQ
 // is a GEMM over the stored dS, without it the dQ pass recomputes S and dP
 // (plain causal only: a window needs the workspace).
+// With q_raw non-null (the workspace path only), q and k are the rotated heads
+// of the QK-norm + rotary prologue, q_raw and k_raw its inputs, and dq, dk are
+// written as the gradients of q_raw and k_raw (the prologue's backward in the
+// dQ GEMM's and the dK/dV pass's epilogues; tables fp32 (>= T, D/2)).
 hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const void* o,
                            const void* dout, const float* lse, void* dq, void* dk, void* dv,
                            float* delta, void* ws, int B, int T, int H, int Hk, int window,
-                           hipStream_t s, hipEvent_t const* ev = nullptr);
+                           hipStream_t s, hipEvent_t const* ev = nullptr,
+                           const void* q_raw = nullptr, const void* k_raw = nullptr,
+                           const float* cos_t = nullptr, const float* sin_t = nullptr,
+                           float eps = 0.f);
 std::size_t bwd_workspace_bytes(int B, int T, int H);
 
 // bf16 append of T new key/value rows per sequence at cache rows

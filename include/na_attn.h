@@ -268,6 +268,25 @@ na_status na_value_gate_bwd(const void* ve, const void* gate, const void* dv_out
                             void* dgate, int B, int T, int H_kv, int D, void* stream);
 
 /*
+ * Backward with the prologue's backward folded in (the training step with QK
+ * norm and rotary embedding: na_qk_norm_rope_fwd made q, k from q_raw, k_raw,
+ * and na_attn_fwd_gqa ran on q, k, v).  Computes what na_attn_bwd_gqa
+ * followed by na_qk_norm_rope_bwd computes, in one pass: dv as in
+ * na_attn_bwd_gqa, and dq, dk as the gradients of q_raw and k_raw (each
+ * row's dz = R^T g, dx = r (dz - z mean(dz z)) applied in the epilogues that
+ * write dq and dk, with positions t, tables fp32 (T_tab >= T, D/2)).
+ * q, k: the rotated heads (the forward's inputs); q_raw, k_raw: the
+ * prologue's inputs, same layouts.  The dS workspace is required.  Other
+ * arguments as in na_attn_bwd_gqa.
+ */
+na_status na_attn_bwd_rope(const void* q, const void* k, const void* v, const void* o,
+                           const void* dout, const float* lse, const void* q_raw,
+                           const void* k_raw, const float* cos_tab, const float* sin_tab,
+                           int T_tab, float eps, void* dq, void* dk, void* dv, float* delta,
+                           void* workspace, size_t workspace_bytes, int B, int T, int H,
+                           int H_kv, int D, int window, void* stream);
+
+/*
  * Prefill with the prologue folded in: as na_attn_prefill, but q and k_new
  * hold the raw query and key heads, and each head row is RMS-normalised and
  * rotated (the readings of na_qk_norm_rope_fwd) at its cache position on the

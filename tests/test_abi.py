@@ -37,7 +37,8 @@ def test_header_declares_the_entry_points():
               "na_attn_fwd_window", "na_attn_bwd_window", "na_attn_decode_window",
               "na_attn_fwd_gqa", "na_attn_bwd_gqa", "na_attn_decode_gqa", "na_attn_prefill",
               "na_qk_norm_rope_fwd", "na_qk_norm_rope_bwd", "na_value_gate_fwd",
-              "na_value_gate_bwd", "na_attn_prefill_rope", "na_attn_decode_append"):
+              "na_value_gate_bwd", "na_attn_prefill_rope", "na_attn_decode_append",
+              "na_attn_bwd_rope"):
         assert s in syms
 
 
@@ -216,6 +217,24 @@ def test_decode_append_checks_its_arguments(lib):
     assert lib.na_attn_decode_append(p[0], p[1], p[2], p[3], p[4], p[5], None, None, 0, 0.0, None,
                                      None, p[8], p[9], 4, 6, 4, 128, 64, -1, p[13], need,
                                      None) == INVALID  # H not a multiple of H_kv
+
+
+def test_bwd_rope_checks_its_arguments(lib):
+    p = [A + 0x100 * i for i in range(17)]
+    need = lib.na_attn_bwd_workspace_bytes(1, 64, 2, 128)
+    # q k v o dout lse q_raw k_raw cos sin | dq dk dv delta ws
+    call = lambda ptrs=p, T_tab=64, ws=need, Hk=2: lib.na_attn_bwd_rope(  # noqa: E731
+        *ptrs[:10], T_tab, 1e-6, ptrs[10], ptrs[11], ptrs[12], ptrs[13], ptrs[14], ws, 1, 64, 2,
+        Hk, 128, -1, None)
+    assert call(T_tab=32) == INVALID and b"T_tab" in lib.na_last_error()
+    assert call(ws=need - 1) == INVALID and b"workspace" in lib.na_last_error()
+    bad = list(p)
+    bad[14] = 0                  # no workspace
+    assert call(bad) == INVALID
+    bad = list(p)
+    bad[10] = bad[6]             # dq aliases q_raw
+    assert call(bad) == INVALID
+    assert call(Hk=3) == INVALID
 
 
 def test_value_gate_checks_its_arguments(lib):

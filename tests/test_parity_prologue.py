@@ -219,3 +219,68 @@ def test_value_gate_saturated_logits_and_d20(dev):
     rdve, rdg = oracle.value_gate_backward(ve, g, dy)
     assert_close("dve d20", dve, rdve, BF16_REL_L2, BF16_MAX_ABS)
     assert_close("dgate d20", dg, rdg, BF16_REL_L2, BF16_MAX_ABS)
+
+
+@pytest.mark.parametrize("B,T,H,Hk,Wn", [(2, 96, 2, 2, None), (2, 300, 4, 2, None),
+                                         (1, 257, 2, 2, 64), (3, 130, 6, 3, 40)])
+def test_bwd_with_prologue_folded_in(dev, B, T, H, Hk, Wn):
+    """na_attn_bwd_rope (the prologue's backward in the dQ and dK/dV epilogues)
+    against the oracle chain: prologue -> attention forward -> attention
+    backward -> prologue backward; dv unchanged by the prologue."""
+    import torch
+    import causal_self_attention_mha_amd as na
+    tr = W.make_train_inputs("d20", B=B, T=T, H=H, seed=770 + T)
+    kv = lambda a: np.ascontiguousarray(a[:, :, :Hk])  # noqa: E731
+    c, s = tables("rope", T, 0)
+    q_raw, k_raw = to_device(tr.q_store, dev), to_device(kv(tr.k_store), dev)
+    v, do = to_device(kv(tr.v_store), dev), to_device(tr.do_store, dev)
+    ct, sn = torch.from_numpy(c).to(dev), torch.from_numpy(s).to(dev)
+    qr, kr = na.qk_norm_rope_fwd(q_raw, k_raw, ct, sn)
+    o, lse = na.attn_fwd(qr, kr, v, window=Wn)
+    dq, dk, dv, _ = na.attn_bwd(qr, kr, v, o, do, lse, window=Wn, rope=(q_raw, k_raw, ct, sn))
+    torch.cuda.synchronize()
+    c64, s64 = c.astype(np.float64), s.astype(np.float64)
+    xq, xk = tr.q.astype(np.float64), kv(tr.k).astype(np.float64)
+    rq = oracle.qk_norm_rope_forward(xq, c64, s64, EPS)
+    rk = oracle.qk_norm_rope_forward(xk, c64, s64, EPS)
+    rdq, rdk, rdv, _ = oracle.backward(rq, rk, kv(tr.v), tr.do, window=Wn)
+    assert_close("dv", to_host(dv), rdv, BF16_REL_L2, BF16_MAX_ABS)
+    assert_close("dq", to_host(dq), oracle.qk_norm_rope_backward(xq, rdq, c64, s64, EPS),
+                 BF16_REL_L2, BF16_MAX_ABS)
+    assert_close("dk", to_host(dk), oracle.qk_norm_rope_backward(xk, rdk, c64, s64, EPS),
+                 BF16_REL_L2, BF16_MAX_ABS)
+
+
+def test_bwd_with_prologue_folded_in_d20_sampled(dev):
+    """The d20 shape: the folded backward against the two-step GPU path (full
+    tensors, bf16 bound) and against the oracle chain on sampled heads."""
+    import torch
+    import causal_self_attention_mha_amd as na
+    tr = W.make_train_inputs("d20", seed=21)
+    B, T, H = tr.q.shape[:3]
+    c, s = tables("rope", T, 0)
+    q_raw, k_raw, v, do = (to_device(a, dev) for a in (tr.q_store, tr.k_store, tr.v_store,
+                                                       tr.do_store))
+    ct, sn = torch.from_numpy(c).to(dev), torch.from_numpy(s).to(dev)
+    qr, kr = na.qk_norm_rope_fwd(q_raw, k_raw, ct, sn)
+    o, lse = na.attn_fwd(qr, kr, v)
+    dq, dk, dv, _ = na.attn_bwd(qr, kr, v, o, do, lse, rope=(q_raw, k_raw, ct, sn))
+    dq2r, dk2r, _, _ = na.attn_bwd(qr, kr, v, o, do, lse)
+    dq2, dk2 = na.qk_norm_rope_bwd(q_raw, k_raw, dq2r, dk2r, ct, sn)
+    torch.cuda.synchronize()
+    assert_close("dq vs two-step", to_host(dq), to_host(dq2), BF16_REL_L2, BF16_MAX_ABS)
+    assert_close("dk vs two-step", to_host(dk), to_host(dk2), BF16_REL_L2, BF16_MAX_ABS)
+    c64, s64 = c.astype(np.float64), s.astype(np.float64)
+    for b, h in ((0, 0), (31, 9), (13, 4)):
+        xq = tr.q[b:b + 1, :, h:h + 1].astype(np.float64)
+        xk = tr.k[b:b + 1, :, h:h + 1].astype(np.float64)
+        rq = oracle.qk_norm_rope_forward(xq, c64, s64, EPS)
+        rk = oracle.qk_norm_rope_forward(xk, c64, s64, EPS)
+        rdq, rdk, _, _ = oracle.backward(rq, rk, tr.v[b:b + 1, :, h:h + 1],
+                                         tr.do[b:b + 1, :, h:h + 1])
+        assert_close(f"dq[{b},{h}]", to_host(dq[b:b + 1, :, h:h + 1]),
+                     oracle.qk_norm_rope_backward(xq, rdq, c64, s64, EPS), BF16_REL_L2,
+                     BF16_MAX_ABS)
+        assert_close(f"dk[{b},{h}]", to_host(dk[b:b + 1, :, h:h + 1]),
+                     oracle.qk_norm_rope_backward(xk, rdk, c64, s64, EPS), BF16_REL_L2,
+                     BF16_MAX_ABS)
