@@ -18,6 +18,12 @@
  *   - causal: key j is visible to query i iff j <= i (T_q = T_k, top left);
  *   - n_kv_head = n_head; full causal window (the *_window entry points
  *     below take a sliding window, the *_gqa ones fewer key/value heads);
+ *   - KV caches: na_attn_decode reads a cache that already holds the new
+ *     token; na_attn_prefill and na_attn_decode_append write the new rows
+ *     first (bottom-right causal alignment for a chunk);
+ *   - the prologue (QK norm, rotary embedding, value-embedding gate) has
+ *     entry points of its own and is folded into the prefill, the decode
+ *     step and, optionally, the backward (na_attn_*_rope, *_append);
  *   - lse_i = ln sum_j exp(z_ij) over visible keys (natural log, fp32);
  *   - bf16 inputs are rounded values; all accumulation is fp32; fp32 -> bf16
  *     conversions round to nearest even.
@@ -25,8 +31,9 @@
  * Conventions for every entry point:
  *   - All tensor pointers are DEVICE pointers owned by the caller.  The library
  *     never allocates device memory; scratch space (delta, the decode
- *     workspace) is passed in.  Inputs are only read; outputs are fully
- *     overwritten (no need to zero them).
+ *     workspace) is passed in.  Inputs are only read (the caches of the
+ *     appending calls are read and written); outputs are fully overwritten
+ *     (no need to zero them).
  *   - bf16 tensors are stored as 16-bit bfloat16.  Layout of q, k, v, o, dout,
  *     dq, dk, dv: (B, T, H, D) contiguous, element ((b*T + t)*H + h)*D + d.
  *     lse and delta: fp32 (B, H, T) contiguous, element (b*H + h)*T + t.
