@@ -196,3 +196,27 @@ def test_decode_append(dev, B, H, Hk, T_cap, Wn, rope, gate):
     keep = np.ones((B, T_cap), dtype=bool)
     keep[rows] = False
     assert np.array_equal(gk[keep], kc0[keep]) and np.array_equal(gv[keep], vc0[keep])
+
+
+def test_decode_append_many_sequences_raw_slot_order(dev):
+    """The appending decode with more than 8192 sequences (the split kernel's
+    raw slot order) and short caches: every sequence, including ones whose
+    cache was empty, sees exactly the rows before the new one plus it."""
+    import torch
+    import causal_self_attention_mha_amd as na
+    B, H, T_cap = 8200, 1, 40
+    rng = np.random.default_rng(16)
+    lens = rng.integers(0, T_cap, size=B)
+    cache = W.make_decode_inputs(B=B, T_cap=T_cap, H=H, seed=16, seqlens=np.maximum(lens, 1))
+    new = W.make_decode_inputs(B=B, T_cap=1, H=H, seed=17, seqlens=[1] * B)
+    kn, vn = to_device(new.k_store[:, 0], dev), to_device(new.v_store[:, 0], dev)
+    q, kc, vc = (to_device(a, dev) for a in (cache.q_store, cache.k_store, cache.v_store))
+    o, lse = na.attn_decode_append(q, kn, vn, kc, vc,
+                                   torch.from_numpy(lens.astype(np.int32)).to(dev))
+    torch.cuda.synchronize()
+    kcr, vcr = cache.k_cache.astype(np.float64).copy(), cache.v_cache.astype(np.float64).copy()
+    kcr[np.arange(B), lens] = new.k_cache[:, 0]
+    vcr[np.arange(B), lens] = new.v_cache[:, 0]
+    ro, rl = oracle.decode(cache.q.astype(np.float64), kcr, vcr, lens + 1)
+    assert_close("o", to_host(o), ro, BF16_REL_L2, BF16_MAX_ABS)
+    assert_close("lse", to_host(lse), rl, BF16_REL_L2, BF16_MAX_ABS)
