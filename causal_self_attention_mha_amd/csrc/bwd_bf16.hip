@@ -81,11 +81,30 @@ struct RopeBwd {
   float eps;
 };
 
+// The inputs of rope_bwd_chunk that come from memory: the raw chunk and the
+// lane's eight cos and sin values, loaded ahead of the gradient they meet.
+struct RopeRow {
+  uint4 x16;
+  float4 c0, c1, s0, s1;
+};
+__device__ __forceinline__ RopeRow rope_row_load(const u16* raw_chunk, const RopeBwd& ra, int pos,
+                                                 int c) {
+  const size_t tp = static_cast<size_t>(pos) * (D / 2) + 8 * (c & 7);
+  RopeRow r;
+  r.x16 = raw_chunk != nullptr ? ld16(raw_chunk) : make_uint4(0, 0, 0, 0);
+  r.c0 = *reinterpret_cast<const float4*>(ra.cos_t + tp);
+  r.c1 = *reinterpret_cast<const float4*>(ra.cos_t + tp + 4);
+  r.s0 = *reinterpret_cast<const float4*>(ra.sin_t + tp);
+  r.s1 = *reinterpret_cast<const float4*>(ra.sin_t + tp + 4);
+  return r;
+}
+
 // 16 lanes per 256-byte row, lane c holding elements 8 c .. 8 c + 7: gradient
-// chunk g16 of the rotated row at position pos, raw chunk x16; returns the
-// raw row's gradient chunk.  Every lane of the 16-lane group takes part.
-__device__ __forceinline__ uint4 rope_bwd_chunk(uint4 g16, uint4 x16, const RopeBwd& ra, int pos,
-                                                int c) {
+// chunk g16 of the rotated row, and the raw chunk with the angles of its
+// position (RopeRow); returns the raw row's gradient chunk.  Every lane of
+// the 16-lane group takes part.
+__device__ __forceinline__ uint4 rope_bwd_chunk(uint4 g16, const RopeRow& rw, float eps, int c) {
+  const uint4 x16 = rw.x16;
   float g[8], x[8];
   const uint32_t gw[4] = {g16.x, g16.y, g16.z, g16.w}, xw[4] = {x16.x, x16.y, x16.z, x16.w};
 #pragma unroll
@@ -98,14 +117,9 @@ __device__ __forceinline__ uint4 rope_bwd_chunk(uint4 g16, uint4 x16, const Rope
   float ss = 0.f;
 #pragma unroll
   for (int e = 0; e < 8; ++e) ss = fmaf(x[e], x[e], ss);
-  const float r = __builtin_amdgcn_rsqf(sum16(ss) * (1.f / D) + ra.eps);
-  const size_t tp = static_cast<size_t>(pos) * (D / 2) + 8 * (c & 7);
-  const float4 c0 = *reinterpret_cast<const float4*>(ra.cos_t + tp);
-  const float4 c1 = *reinterpret_cast<const float4*>(ra.cos_t + tp + 4);
-  const float4 s0 = *reinterpret_cast<const float4*>(ra.sin_t + tp);
-  const float4 s1 = *reinterpret_cast<const float4*>(ra.sin_t + tp + 4);
-  const float cs[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
-  const float sn[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+  const float r = __builtin_amdgcn_rsqf(sum16(ss) * (1.f / D) + eps);
+  const float cs[8] = {rw.c0.x, rw.c0.y, rw.c0.z, rw.c0.w, rw.c1.x, rw.c1.y, rw.c1.z, rw.c1.w};
+  const float sn[8] = {rw.s0.x, rw.s0.y, rw.s0.z, rw.s0.w, rw.s1.x, rw.s1.y, rw.s1.z, rw.s1.w};
   const float sg = c < 8 ? 1.f : -1.f;  // dz_i = g_i c + g_{i+64} s, dz_{i+64} = g_{i+64} c - g_i s
   float dz[8], dot = 0.f;
 #pragma unroll
@@ -583,6 +597,18 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(
     // compiler does not see (it may sink a read into the conditional store
     // that uses it, past the next round's writes): each round starts with an
     // LDS wait that is also a compiler memory barrier.
+    // ROPE: the raw key chunks of the 8 rows this lane finishes, loaded before
+    // the rounds so that their latency overlaps the staging (the angles, L2
+    // hits, are loaded where they are used: all of it at once would not fit
+    // the register budget)
+    uint4 xraw[ROPE ? 8 : 1];
+    if constexpr (ROPE) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int kr = min(kw0 + 16 * (i >> 2) + 4 * (i & 3) + (lane >> 4), T - 1);
+        xraw[i] = ld16(ra.raw + kbase + kr * rsk + 8 * (lane & 15));
+      }
+    }
 #pragma unroll
     for (int tsel = 0; tsel < 2; ++tsel) {  // dK, then dV
       const f32x16* acc = tsel ? dva : dka;
@@ -609,9 +635,13 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(
           const int rr = 4 * m + (lane >> 4), c = lane & 15;
           uint4 x = lds_ld16(est_lds + rr * 256 + 16 * (c ^ rr));
           const int key = kw0 + 16 * sh + rr;
-          if (ROPE && tsel == 0) {  // whole 16-lane groups: key is uniform over one
-            const int kr = min(key, T - 1);
-            x = rope_bwd_chunk(x, ld16(ra.raw + kbase + kr * rsk + 8 * c), ra, kr, c);
+          if constexpr (ROPE) {  // whole 16-lane groups: key is uniform over one
+            if (tsel == 0) {
+              const int kr = min(key, T - 1);
+              RopeRow rw = rope_row_load(nullptr, ra, kr, c);
+              rw.x16 = xraw[ROPE ? 4 * sh + m : 0];
+              x = rope_bwd_chunk(x, rw, ra.eps, c);
+            }
           }
           if (key < T) st16(dst + kbase + key * rsk + 8 * c, x);
         }
@@ -1062,13 +1092,31 @@ __global__ __launch_bounds__(64 * DG_WAVES, 8 / DG_WAVES) void dq_gemm_kernel(co
       // other half in lane l ^ 32); d < 64 (db < 2) pairs with d + 64 (db + 2)
       const int pr = min(qrow, T - 1);
       const u16* xp = ra.raw + base + static_cast<size_t>(pr) * rs + 4 * half;
+      const float* cp = ra.cos_t + static_cast<size_t>(pr) * (D / 2) + 4 * half;
+      const float* sp = ra.sin_t + static_cast<size_t>(pr) * (D / 2) + 4 * half;
+      // every load first (one round of latency), then the arithmetic
+      uint2 xw[4][4];
+      float4 c4[2][4], s4[2][4];
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          xw[db][g] = *reinterpret_cast<const uint2*>(xp + 32 * db + 8 * g);
+#pragma unroll
+      for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          c4[db][g] = *reinterpret_cast<const float4*>(cp + 32 * db + 8 * g);
+          s4[db][g] = *reinterpret_cast<const float4*>(sp + 32 * db + 8 * g);
+        }
+      __builtin_amdgcn_sched_barrier(0);
       float x[4][16];
       float ss = 0.f;
 #pragma unroll
       for (int db = 0; db < 4; ++db)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const uint2 w = *reinterpret_cast<const uint2*>(xp + 32 * db + 8 * g);
+          const uint2 w = xw[db][g];
           x[db][4 * g] = __uint_as_float(w.x << 16);
           x[db][4 * g + 1] = __uint_as_float(w.x & 0xffff0000u);
           x[db][4 * g + 2] = __uint_as_float(w.y << 16);
@@ -1078,16 +1126,13 @@ __global__ __launch_bounds__(64 * DG_WAVES, 8 / DG_WAVES) void dq_gemm_kernel(co
         }
       ss += __shfl_xor(ss, 32, 64);
       const float rn = __builtin_amdgcn_rsqf(ss * (1.f / D) + ra.eps);
-      const float* cp = ra.cos_t + static_cast<size_t>(pr) * (D / 2) + 4 * half;
-      const float* sp = ra.sin_t + static_cast<size_t>(pr) * (D / 2) + 4 * half;
       float dot = 0.f;
 #pragma unroll
       for (int db = 0; db < 2; ++db)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const float4 c4 = *reinterpret_cast<const float4*>(cp + 32 * db + 8 * g);
-          const float4 s4 = *reinterpret_cast<const float4*>(sp + 32 * db + 8 * g);
-          const float cs[4] = {c4.x, c4.y, c4.z, c4.w}, sn[4] = {s4.x, s4.y, s4.z, s4.w};
+          const float4 cv = c4[db][g], sv = s4[db][g];
+          const float cs[4] = {cv.x, cv.y, cv.z, cv.w}, sn[4] = {sv.x, sv.y, sv.z, sv.w};
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const float g1 = dqa[db][4 * g + j], g2 = dqa[db + 2][4 * g + j];
