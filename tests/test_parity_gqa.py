@@ -148,3 +148,36 @@ def test_gqa_decode_many_sequences(dev, H, Hk, B, T_cap):
     assert_close("o", to_host(o)[live], ro[live], BF16_REL_L2, BF16_MAX_ABS)
     assert_close("lse", to_host(lse)[live], rl[live], BF16_REL_L2, BF16_MAX_ABS)
     assert np.all(to_host(o)[~live] == 0.0) and np.all(np.isneginf(to_host(lse)[~live]))
+
+
+@pytest.mark.parametrize("cfg,B,H,Hk,Wn", [("d26", 16, 13, 1, 1024), ("d12", 16, 6, 2, 300)])
+def test_gqa_window_full_shapes_sampled_heads(dev, cfg, B, H, Hk, Wn):
+    """The d26 shape (13 query heads) with one key/value head and a window of
+    1024, and the d12 shape with 2 key/value heads and a window of 300, at
+    full size in the launch configuration the benchmark uses, on sampled
+    heads."""
+    import torch
+    T = 2048
+    inp = gqa_inputs(B, T, H, Hk, seed=None, cfg=cfg)
+    res = gpu_fwd_bwd(inp, dev, window=Wn)
+    for n in ("o", "dq", "dk", "dv"):
+        assert bool(torch.isfinite(res[n].float()).all()), n
+    heads = [(0, 0), (B - 1, H - 1), (B // 2, H // 2)]
+    fw = oracle.forward(inp.q, inp.k, inp.v, heads=heads, window=Wn)
+    bw = oracle.backward(inp.q, inp.k, inp.v, inp.do, heads=heads, window=Wn)
+    for (b, h) in heads:
+        O, L = fw[(b, h)]
+        assert_close(f"{cfg} [b={b},h={h}].o", to_host(res["o"][b, :, h]), O, BF16_REL_L2,
+                     BF16_MAX_ABS)
+        assert_close(f"{cfg} [b={b},h={h}].lse", to_host(res["lse"][b, h]), L, BF16_REL_L2,
+                     BF16_MAX_ABS)
+        assert_close(f"{cfg} [b={b},h={h}].dq", to_host(res["dq"][b, :, h]), bw[(b, h)][0],
+                     BF16_REL_L2, BF16_MAX_ABS)
+    # a key/value head's gradient sums H / Hk query heads (13 at d26): one sample there
+    kv_heads = [(0, 0)] if Hk == 1 else [(0, 0), (B - 1, Hk - 1)]
+    kv = oracle.kv_grads(inp.q, inp.k, inp.v, inp.do, kv_heads, window=Wn)
+    for (b, hk), (gK, gV) in kv.items():
+        assert_close(f"{cfg} [b={b},hk={hk}].dk", to_host(res["dk"][b, :, hk]), gK,
+                     BF16_REL_L2, BF16_MAX_ABS)
+        assert_close(f"{cfg} [b={b},hk={hk}].dv", to_host(res["dv"][b, :, hk]), gV,
+                     BF16_REL_L2, BF16_MAX_ABS)
