@@ -300,3 +300,33 @@ def test_product_and_oracle_share_no_code():
             src = open(os.path.join(ROOT, "oracle", f), encoding="utf-8").read()
             assert "causal_self_attention_mha_amd" not in src
             assert not re.search(r"^\s*(from|import)\s+workloads\b", src, re.M)
+
+
+def _p(i):
+    return A + 0x100 * i
+
+
+# entry point, argument list builder (pointers by index), indices of required pointers
+_NULL_CASES = [
+    ("na_attn_fwd", lambda p: (*p[:4], p[4], 1, 8, 2, 128, None), range(5)),
+    ("na_attn_bwd", lambda p: (*p[:10], p[10], 1 << 20, 1, 8, 2, 128, None), range(10)),
+    ("na_attn_prefill", lambda p: (*p[:8], 1, 8, 2, 2, 128, 64, -1, None), range(7)),
+    ("na_qk_norm_rope_fwd", lambda p: (*p[:6], None, 1, 8, 2, 2, 128, 16, 1e-6, None), range(6)),
+    ("na_qk_norm_rope_bwd", lambda p: (*p[:8], None, 1, 8, 2, 2, 128, 16, 1e-6, None), range(8)),
+    ("na_value_gate_fwd", lambda p: (*p[:4], 1, 8, 2, 128, None), range(4)),
+    ("na_value_gate_bwd", lambda p: (*p[:5], 1, 8, 2, 128, None), range(5)),
+    ("na_attn_bwd_rope", lambda p: (*p[:10], 64, 1e-6, *p[10:15], 1 << 26, 1, 64, 2, 2, 128, -1,
+                                    None), range(15)),
+]
+
+
+@pytest.mark.parametrize("name,args,required", _NULL_CASES, ids=[c[0] for c in _NULL_CASES])
+def test_every_required_pointer_is_checked(lib, name, args, required):
+    """Each required pointer, set to NULL alone, is rejected on the host (so
+    no kernel ever sees it)."""
+    fn = getattr(lib, name)
+    for i in required:
+        p = [_p(j) for j in range(16)]
+        p[i] = 0
+        assert fn(*args(p)) == INVALID, (name, i)
+        assert b"NULL" in lib.na_last_error(), (name, i, lib.na_last_error())
