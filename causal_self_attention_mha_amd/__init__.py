@@ -21,9 +21,11 @@ Functions (names match the C entry points):
   qk_norm_rope_bwd(q, k, dq_rot, dk_rot, cos, sin) -> (dq, dk)
   value_gate_fwd(v, ve, gate)             -> v + 3 sigmoid(gate) ve
   value_gate_bwd(ve, gate, dv_out)        -> (dve, dgate)   (dv is dv_out)
-Each takes window=W (an int >= 0) for sliding-window attention (key j visible
-to query i iff i - W <= j <= i), which calls the *_window entry point;
-window=None is plain causal attention.  k and v (and the decode caches) may
+The attention calls take window=W (an int >= 0) for sliding-window attention
+(key j visible to query i iff i - W <= j <= i), which calls the *_window entry
+point; window=None is plain causal attention.  The prologue folds into
+attn_prefill and attn_decode_append (rope=(cos, sin), value_gate=(ve, gate))
+and into attn_bwd (rope=(q_raw, k_raw, cos, sin): dq, dk of the raw heads).  k and v (and the decode caches) may
 have fewer heads than q (grouped-query attention, H a multiple of H_kv; the
 *_gqa entry points); dk and dv then have the key/value heads' shape.
 bf16 tensors use the bf16 kernels, float32 tensors the fp32 kernels
