@@ -7,7 +7,9 @@ One step = one pass of the training hot path at the d20 shape
 tensors of the `workloads` module, resident in HBM before timing starts.
 W untimed warmup steps, then exactly K timed steps between
 torch.cuda.synchronize() calls; per-kernel durations come from HIP events
-recorded on the launch stream around every kernel.
+recorded on the launch stream around every kernel of every fourth timed step
+(--kernel-events-every: an event between two kernels adds a few
+microseconds, about 1% of the step when every step carries them).
 
 The single-token decode over the ragged d20 cache (B=64, H=10, lengths
 uniform in [1, 2048]) is timed in its own loop and reported under "decode";
@@ -192,6 +194,9 @@ def main():
                     help="sliding-window length for the extra windowed measurement (-1 = skip)")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-prologue", action="store_true")
+    ap.add_argument("--kernel-events-every", type=int, default=4,
+                    help="record the per-kernel HIP events on every N-th timed step (each "
+                         "event between two kernels adds a few microseconds to the step)")
     ap.add_argument("--kv-heads", type=int, default=5,
                     help="key/value heads for the extra grouped-query measurement (0 = skip)")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
@@ -252,16 +257,25 @@ def main():
     evs = [ev.create(5) for _ in range(n_total)]
     ev_arr = [(ctypes.c_void_p * 4)(*[e.value for e in step[1:5]]) for step in evs]
 
+    every = max(1, args.kernel_events_every)
+
+    def instrumented(i):  # timed steps that carry the per-kernel events
+        return (i - args.warmup) % every == 0
+
+    timed_ev = [i for i in range(args.warmup, n_total) if instrumented(i)]
+
     def step(i, window=-1):
         e = evs[i]
-        ev.record(e[0], stream)
+        if instrumented(i):
+            ev.record(e[0], stream)
         st = lib.na_attn_fwd_window(ptr(q), ptr(k), ptr(v), ptr(o), ptr(lse), B, T, H, D,
                                     window, P(stream))
         if st:
             raise RuntimeError(lib.na_last_error().decode())
         st = lib.na_attn_bwd_window(ptr(q), ptr(k), ptr(v), ptr(o), ptr(do), ptr(lse), ptr(dq),
                                     ptr(dk), ptr(dv), ptr(delta), ptr(ws), ws_bytes, B, T, H, D,
-                                    window, P(stream), ctypes.cast(ev_arr[i], P))
+                                    window, P(stream),
+                                    ctypes.cast(ev_arr[i], P) if instrumented(i) else None)
         if st:
             raise RuntimeError(lib.na_last_error().decode())
 
@@ -278,7 +292,7 @@ def main():
     names = ["fwd", "delta", "dkdv", "dq"]
     per = {n: [] for n in names}
     step_ms = []
-    for i in range(args.warmup, n_total):
+    for i in timed_ev:
         e = evs[i]
         for j, n in enumerate(names):
             per[n].append(ev.ms(e[j], e[j + 1]))
@@ -316,6 +330,7 @@ def main():
         "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
         "wall_s_timed": round(wall, 4),
         "gpu_ms_per_step_events": round(gpu_ms_per_step, 4),
+        "kernel_event_steps": len(timed_ev),
         "kernels": kern,
         "roofline": roofline,
     }
@@ -333,7 +348,7 @@ def main():
         torch.cuda.synchronize()
         wwall = time.perf_counter() - t0
         wper = {n: [] for n in names}
-        for i in range(args.warmup, n_total):
+        for i in timed_ev:
             for j, n in enumerate(names):
                 wper[n].append(ev.ms(evs[i][j], evs[i][j + 1]))
         pairs = visible_pairs(T, wlen)
@@ -361,14 +376,16 @@ def main():
 
         def gstep(i):
             e = evs[i]
-            ev.record(e[0], stream)
+            if instrumented(i):
+                ev.record(e[0], stream)
             st = lib.na_attn_fwd_gqa(ptr(q), ptr(kg), ptr(vg), ptr(o), ptr(lse), B, T, H, hkv, D,
                                      -1, P(stream))
             if st:
                 raise RuntimeError(lib.na_last_error().decode())
             st = lib.na_attn_bwd_gqa(ptr(q), ptr(kg), ptr(vg), ptr(o), ptr(do), ptr(lse),
                                      ptr(dq), ptr(dkg), ptr(dvg), ptr(delta), ptr(ws), ws_bytes,
-                                     B, T, H, hkv, D, -1, P(stream), ctypes.cast(ev_arr[i], P))
+                                     B, T, H, hkv, D, -1, P(stream),
+                                     ctypes.cast(ev_arr[i], P) if instrumented(i) else None)
             if st:
                 raise RuntimeError(lib.na_last_error().decode())
 
@@ -383,8 +400,7 @@ def main():
         gwall = time.perf_counter() - t0
         gk = {}
         for j, n in enumerate(names):
-            avg = float(np.mean([ev.ms(evs[i][j], evs[i][j + 1])
-                                 for i in range(args.warmup, n_total)]))
+            avg = float(np.mean([ev.ms(evs[i][j], evs[i][j + 1]) for i in timed_ev]))
             gk[n] = {"avg_us": round(avg * 1e3, 2),
                      "tflops": round(fl[n] / (avg * 1e-3) / 1e12, 2) if fl[n] else None}
         g_ms = gwall * 1e3 / args.steps
