@@ -21,7 +21,8 @@
 //            (b, chunk, h).  Balancing slots rather than launching one
 //            workgroup per chunk matters: the ragged lengths otherwise leave
 //            compute units idle (measured 48% -> 56% of HBM bandwidth).
-//   combine: one workgroup per (b, h), one pass with a running max:
+//   combine: one 64-thread workgroup per (b, h) (two elements per thread), one
+//            pass with a running max:
 //            o = sum_c e^(m_c - M) o_c / sum_c e^(m_c - M) l_c.
 // Rows t >= L (and, with a window, rows before j0) are never read.  With H_kv
 // key/value heads the cache is (B, T_cap, H_kv, D) and query head h reads head
@@ -329,7 +330,7 @@ __global__ __launch_bounds__(512) void decode_split_kernel(
   }
 }
 
-__global__ __launch_bounds__(128) void decode_combine_kernel(
+__global__ __launch_bounds__(64) void decode_combine_kernel(
     const float* __restrict__ opart, const float* __restrict__ ml,
     const int* __restrict__ seqlens, u16* __restrict__ o, float* __restrict__ lse, int H,
     int T_cap, int NC, int win, int app) {
@@ -337,15 +338,16 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(
   const int L = min(max(seqlens[b], 0), T_cap - app) + app;
   const int nc = (L + CHUNK - 1) / CHUNK;                         // chunks end here
   const int c_lo = win < 0 || L == 0 ? 0 : max(0, L - 1 - win) / CHUNK;  // and start here
-  const int d = threadIdx.x;
+  const int d = threadIdx.x;  // elements d and d + 64
   const float* mlb = ml + 2 * (static_cast<size_t>(b) * NC * H + h);  // chunk c at 2 c H
   const float* opb = opart + (static_cast<size_t>(b) * NC * H + h) * D + d;  // chunk c at c H D
+  float num2 = 0.f;
   // one pass over the chunks in groups of 16 (all loads of a group issued
   // before they are used), with a running max M
   constexpr int G = 16;
   float M = -INFINITY, den = 0.f, num = 0.f;
   for (int c0 = c_lo; c0 < nc; c0 += G) {
-    float mv[G], lv[G], ov[G];
+    float mv[G], lv[G], ov[G], ov2[G];
 #pragma unroll
     for (int i = 0; i < G; ++i) {
       const bool ok = c0 + i < nc;
@@ -353,6 +355,7 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(
       mv[i] = ok ? mlb[2 * c * H] : -INFINITY;
       lv[i] = mlb[2 * c * H + 1];
       ov[i] = opb[static_cast<size_t>(c) * H * D];
+      ov2[i] = opb[static_cast<size_t>(c) * H * D + 64];
     }
     float gm = mv[0];
 #pragma unroll
@@ -361,16 +364,19 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(
     const float sc = expf(M - M_new);  // 0 on the first group
     den *= sc;
     num *= sc;
+    num2 *= sc;
 #pragma unroll
     for (int i = 0; i < G; ++i) {
       const float w = expf(mv[i] - M_new);  // 0 for chunks past nc
       den = fmaf(w, lv[i], den);
       num = fmaf(w, ov[i], num);
+      num2 = fmaf(w, ov2[i], num2);
     }
     M = M_new;
   }
-  const float out = nc > 0 ? num / den : 0.f;
+  const float out = nc > 0 ? num / den : 0.f, out2 = nc > 0 ? num2 / den : 0.f;
   o[(static_cast<size_t>(b) * H + h) * D + d] = __builtin_bit_cast(u16, to_bf16(out));
+  o[(static_cast<size_t>(b) * H + h) * D + d + 64] = __builtin_bit_cast(u16, to_bf16(out2));
   if (lse != nullptr && d == 0)
     lse[static_cast<size_t>(b) * H + h] = nc > 0 ? M + logf(den) : -INFINITY;
 }
@@ -421,7 +427,7 @@ hipError_t launch_decode_bf16(const void* q, const void* kc, const void* vc, con
              Hk, T_cap, scale, win, app, cos_t, sin_t, eps);
   if (e != hipSuccess) return e;
   if ((e = mark(ev, 1, s)) != hipSuccess) return e;
-  e = launch(decode_combine_kernel, dim3(H, B), dim3(128), 0, s, static_cast<const float*>(opart),
+  e = launch(decode_combine_kernel, dim3(H, B), dim3(64), 0, s, static_cast<const float*>(opart),
              static_cast<const float*>(ml), seqlens, static_cast<u16*>(o), lse, H, T_cap, NC,
              win, app);
   if (e != hipSuccess) return e;
