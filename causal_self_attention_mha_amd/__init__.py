@@ -168,6 +168,27 @@ def _check_train(names, tensors, dtype=None, kv_heads=None):
     return dtype
 
 
+def _check_buf(name, t, dtype, shape, device):
+    """A caller-supplied output or scratch tensor: exact dtype, shape and
+    device, contiguous.  Anything else would hand the kernels a host pointer
+    or a buffer of the wrong size."""
+    _require(t.device == device, f"{name} is on {t.device}, expected {device}")
+    _require(t.dtype == dtype, f"{name} has dtype {t.dtype}, expected {dtype}")
+    _require(tuple(t.shape) == tuple(shape), f"{name} has shape {tuple(t.shape)}, "
+             f"expected {tuple(shape)}")
+    _require(t.is_contiguous(), f"{name} must be contiguous")
+
+
+def _check_workspace(t, need, device):
+    """A caller-supplied byte workspace: contiguous, on the device, at least
+    `need` bytes.  Returns its size in bytes."""
+    _require(t.device == device, f"workspace is on {t.device}, expected {device}")
+    _require(t.is_contiguous(), "workspace must be contiguous")
+    nbytes = t.numel() * t.element_size()
+    _require(nbytes >= need, f"workspace has {nbytes} bytes, needs {need}")
+    return nbytes
+
+
 def _window(window):
     if window is None:
         return None
@@ -192,8 +213,7 @@ def attn_fwd(q, k, v, o=None, lse=None, window=None):
     o = torch.empty_like(q) if o is None else o
     lse = torch.empty((B, H, T), dtype=torch.float32, device=q.device) if lse is None else lse
     _check_train(("q", "o"), (q, o), dtype)
-    _require(lse.shape == (B, H, T) and lse.dtype == torch.float32 and lse.is_contiguous(),
-             "lse must be contiguous float32 (B, H, T)")
+    _check_buf("lse", lse, torch.float32, (B, H, T), q.device)
     window = _window(window)
     if Hk != H or window is not None:
         _require(dtype == torch.bfloat16, "window / grouped heads: bf16 tensors only")
@@ -235,14 +255,14 @@ def attn_bwd(q, k, v, o, dout, lse, dq=None, dk=None, dv=None, delta=None, works
     kvh = {"k": Hk, "v": Hk}
     dtype = _check_train(("q", "k", "v", "o", "dout"), (q, k, v, o, dout), kv_heads=kvh)
     B, T, H, D = q.shape
-    _require(lse.shape == (B, H, T) and lse.dtype == torch.float32 and lse.is_contiguous(),
-             "lse must be contiguous float32 (B, H, T)")
+    _check_buf("lse", lse, torch.float32, (B, H, T), q.device)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
     delta = torch.empty((B, H, T), dtype=torch.float32, device=q.device) if delta is None else delta
     _check_train(("q", "dq", "dk", "dv"), (q, dq, dk, dv), dtype,
                  kv_heads={"dk": Hk, "dv": Hk})
+    _check_buf("delta", delta, torch.float32, (B, H, T), q.device)
     window = _window(window)
     _require((window is None and Hk == H) or dtype == torch.bfloat16,
              "window / grouped heads: bf16 tensors only")
@@ -253,7 +273,7 @@ def attn_bwd(q, k, v, o, dout, lse, dq=None, dk=None, dv=None, delta=None, works
             if workspace is None:
                 workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
             else:
-                ws_bytes = workspace.numel() * workspace.element_size()
+                ws_bytes = _check_workspace(workspace, ws_bytes, q.device)
         else:
             workspace = None
         args = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk),
@@ -314,11 +334,14 @@ def attn_decode(q, k_cache, v_cache, seqlens, o=None, lse=None, workspace=None,
     o = torch.empty_like(q) if o is None else o
     if want_lse and lse is None:
         lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    _check_buf("o", o, torch.bfloat16, (B, H, D), q.device)
+    if lse is not None:
+        _check_buf("lse", lse, torch.float32, (B, H), q.device)
     need = decode_workspace_bytes(B, H, T_cap, D)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     window = _window(window)
-    ws_bytes = workspace.numel() * workspace.element_size()
+    ws_bytes = _check_workspace(workspace, need, q.device)
     args = (_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seqlens), _ptr(o), _ptr(lse))
     w = -1 if window is None else window
     if Hk != H:
@@ -376,9 +399,13 @@ def attn_decode_append(q, k_new, v_new, k_cache, v_cache, seqlens, o=None, lse=N
     o = torch.empty_like(q) if o is None else o
     if want_lse and lse is None:
         lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    _check_buf("o", o, torch.bfloat16, (B, H, D), q.device)
+    if lse is not None:
+        _check_buf("lse", lse, torch.float32, (B, H), q.device)
     need = decode_workspace_bytes(B, H, T_cap, D)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    _check_workspace(workspace, need, q.device)
     window = _window(window)
     _check(lib, "na_attn_decode_append",
            lib.na_attn_decode_append(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache),
@@ -423,6 +450,9 @@ def attn_prefill(q, k_new, v_new, k_cache, v_cache, cache_lens, o=None, lse=None
     o = torch.empty_like(q) if o is None else o
     if want_lse and lse is None:
         lse = torch.empty((B, H, T_q), dtype=torch.float32, device=q.device)
+    _check_buf("o", o, torch.bfloat16, (B, T_q, H, D), q.device)
+    if lse is not None:
+        _check_buf("lse", lse, torch.float32, (B, H, T_q), q.device)
     window = _window(window)
     w = -1 if window is None else window
     _require(value_gate is None or rope is not None, "value_gate is taken with rope only")
@@ -485,6 +515,8 @@ def qk_norm_rope_fwd(q, k, cos, sin, pos_offset=None, eps=1e-6, q_out=None, k_ou
     B, T, H, Hk, D, T_tab = _check_prologue(q, k, cos, sin, pos_offset)
     q_out = torch.empty_like(q) if q_out is None else q_out
     k_out = torch.empty_like(k) if k_out is None else k_out
+    _check_buf("q_out", q_out, torch.bfloat16, q.shape, q.device)
+    _check_buf("k_out", k_out, torch.bfloat16, k.shape, q.device)
     _check(lib, "na_qk_norm_rope_fwd",
            lib.na_qk_norm_rope_fwd(_ptr(q), _ptr(k), _ptr(q_out), _ptr(k_out), _ptr(cos), _ptr(sin),
                                    _ptr(pos_offset), B, T, H, Hk, D, T_tab, float(eps),
@@ -502,6 +534,8 @@ def qk_norm_rope_bwd(q, k, dq_rot, dk_rot, cos, sin, pos_offset=None, eps=1e-6, 
         q, k, cos, sin, pos_offset, (("dq_rot", dq_rot, q.shape), ("dk_rot", dk_rot, k.shape)))
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
+    _check_buf("dq", dq, torch.bfloat16, q.shape, q.device)
+    _check_buf("dk", dk, torch.bfloat16, k.shape, q.device)
     _check(lib, "na_qk_norm_rope_bwd",
            lib.na_qk_norm_rope_bwd(_ptr(q), _ptr(k), _ptr(dq_rot), _ptr(dk_rot), _ptr(dq), _ptr(dk),
                                    _ptr(cos), _ptr(sin), _ptr(pos_offset), B, T, H, Hk, D, T_tab,
@@ -531,6 +565,7 @@ def value_gate_fwd(v, ve, gate, v_out=None):
     lib = load_library()
     B, T, Hk, D = _check_value_gate(("v", "ve"), (v, ve), gate)
     v_out = torch.empty_like(v) if v_out is None else v_out
+    _check_buf("v_out", v_out, torch.bfloat16, v.shape, v.device)
     _check(lib, "na_value_gate_fwd",
            lib.na_value_gate_fwd(_ptr(v), _ptr(ve), _ptr(gate), _ptr(v_out), B, T, Hk, D,
                                  _stream(v)))
@@ -545,6 +580,8 @@ def value_gate_bwd(ve, gate, dv_out, dve=None, dgate=None):
     B, T, Hk, D = _check_value_gate(("ve", "dv_out"), (ve, dv_out), gate)
     dve = torch.empty_like(ve) if dve is None else dve
     dgate = torch.empty_like(gate) if dgate is None else dgate
+    _check_buf("dve", dve, torch.bfloat16, ve.shape, ve.device)
+    _check_buf("dgate", dgate, torch.bfloat16, gate.shape, ve.device)
     _check(lib, "na_value_gate_bwd",
            lib.na_value_gate_bwd(_ptr(ve), _ptr(gate), _ptr(dv_out), _ptr(dve), _ptr(dgate), B, T,
                                  Hk, D, _stream(ve)))

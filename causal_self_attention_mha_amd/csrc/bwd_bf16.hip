@@ -148,36 +148,126 @@ constexpr uint32_t BUF_B = 2 * TILE_B;        // one buffer: q tile, then dout t
 // transposed copy) in the swizzled 64 x 128 layout of tile_swz; Q and dout rows
 // are read row-wise as MFMA A operands and transposed as B operands.
 
+// The dK/dV pass writes its MFMAs as inline assembly so that each value sits in
+// the register file its users need: the score chains (S, dP) accumulate in
+// VGPRs, where the softmax VALU work reads them, while the dK and dV
+// accumulators and the K, V operands stay in AGPRs.  (With the compiler's
+// builtins the choice is one form for the whole kernel, and the scores then
+// came out in AGPRs and were copied back, 32 copies per 64-query tile.)  The
+// compiler neither knows these are MFMAs nor inserts their hazard wait states,
+// so the wrappers and the code around them keep gfx950's rules for
+// v_mfma_f32_32x32x16_bf16 (the same numbers the compiler inserts around its
+// builtins): a VALU write of an operand needs 2 wait states before the MFMA
+// reads it (the "s_nop 1" below; a copy the compiler might place right before
+// the statement is such a write), a VALU read of the result needs 12 after the
+// MFMA issues (every score chain is read one pipeline step later, after at
+// least 16 other MFMAs, or behind an explicit s_nop), back-to-back MFMAs that
+// accumulate into the same registers need none, and a read of the dK/dV
+// accumulators by VALU code waits behind mfma_drain().
+//
+// Score chain link: d (VGPR) += a (VGPR) * b (AGPR).
+__device__ __forceinline__ void mfma_chain(f32x16& d, bf16x8 a, bf16x8 b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "a"(b));
+}
+// First link of a score chain: d holds the chain's initial value (LDS reads,
+// or a copy the compiler may have placed just before).
+__device__ __forceinline__ void mfma_chain_first(f32x16& d, bf16x8 a, bf16x8 b) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "a"(b));
+}
+// dK/dV accumulation: acc (AGPR) += a (VGPR) * b (VGPR, written by VALU).
+__device__ __forceinline__ void mfma_acc(f32x16& acc, bf16x8 a, bf16x8 b) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+// Wait states between the last accumulation and any read of the accumulators
+// (they are read back through v_accvgpr_read by the epilogue).
+__device__ __forceinline__ void mfma_drain(f32x16 (&dka)[4], f32x16 (&dva)[4]) {
+  asm volatile("s_nop 15\n\ts_nop 7" : "+a"(dka[0]), "+a"(dka[1]), "+a"(dka[2]), "+a"(dka[3]));
+  asm volatile("" : "+a"(dva[0]), "+a"(dva[1]), "+a"(dva[2]), "+a"(dva[3]));
+}
+
+// Initial values of one 32-query block's score chains, for this lane's
+// accumulator elements (element r: query row row0 + acc_row(lane, r), see
+// dkdv_scores): the S chain starts at -lse log2(e) and the dP chain at -delta,
+// so that the finished chains hold the exponent of P and dP - delta.  ini is
+// the LDS byte address of the wavefront's rewritten rows of the block's tile
+// (-lse log2 e at +0, -delta at +256); rows row0 + 8 half + 0..7 and
+// row0 + 16 + 8 half + 0..7 are two runs of 32 bytes.
+__device__ __forceinline__ void load_chain_init(uint32_t ini, int row0, int lane, f32x16& s,
+                                                f32x16& p) {
+  const uint32_t a = ini + 4 * (row0 + 8 * (lane >> 5));
+  const uint4 s0 = lds_ld16(a), s1 = lds_ld16(a + 16), s2 = lds_ld16(a + 64), s3 = lds_ld16(a + 80);
+  const uint4 d0 = lds_ld16(a + 256), d1 = lds_ld16(a + 272), d2 = lds_ld16(a + 320),
+              d3 = lds_ld16(a + 336);
+  s = __builtin_bit_cast(f32x16, (u32x16{s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w, s2.x,
+                                          s2.y, s2.z, s2.w, s3.x, s3.y, s3.z, s3.w}));
+  p = __builtin_bit_cast(f32x16, (u32x16{d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w, d2.x,
+                                          d2.y, d2.z, d2.w, d3.x, d3.y, d3.z, d3.w}));
+}
+
+// Link i of a score chain (the first one waits out a VALU write of the
+// chain's initial value).
+__device__ __forceinline__ void mfma_chain_first_or_next(int i, f32x16& d, bf16x8 a, bf16x8 b) {
+  if (i == 0)
+    mfma_chain_first(d, a, b);
+  else
+    mfma_chain(d, a, b);
+}
+
 // One 32-query block of a dK/dV step for one wavefront (32 keys), in three
 // phases:
-//   scores:  S = Q K^T, dP = dout V^T   (A = Q / dout rows from LDS, B = K / V
-//            in registers; lane: key, element r: query acc_row(lane, r))
-//   probs:   P = exp2(c S - lse log2 e), dS = P (dP - delta), rounded to bf16
+//   scores:  S' = Q K'^T - lse log2 e, dP' = dout V^T - delta (A = Q / dout
+//            rows from LDS, B = K' / V in AGPRs, K' = s log2(e) K rounded to
+//            bf16; the chains start from load_chain_init; lane: key, element
+//            r: query acc_row(lane, r))
+//   probs:   P = exp2(S'), dS = P dP', rounded to bf16
 //   accum:   dV^T += dout^T P, dK^T += Q^T dS  (A = query tiles read
 //            transposed, B = P / dS from registers; lane: key, element r: d)
-// The steady-state loop overlaps the scores MFMAs of block j+1 with the probs
-// VALU work of block j.  qtile is the LDS byte address of a buffer's q tile
-// (its dout tile follows at + TILE_B).
-__device__ __forceinline__ void dkdv_scores(const uint32_t (&na)[8], int row0,
+// Every MFMA here takes one 1 KB operand from LDS, so the compute unit's LDS
+// read bandwidth (about 4 KB per MFMA time with four wavefronts, close to what
+// it delivers) bounds the pass: the reads are spread evenly over the step's 32
+// MFMAs, and each is issued several MFMAs before its use (a single wavefront
+// per SIMD has no other wavefront to hide LDS latency).
+//
+// Row operands of a block's score chains: rows row0 + perm rows of the tile
+// behind na, 16-element chunks kc; Q at +0, dout at + TILE_B.
+__device__ __forceinline__ void read_rows(const uint32_t (&na)[8], int row0, int kc, bf16x8& q,
+                                          bf16x8& g) {
+  q = as_bf16x8(lds_ld16(na[kc] + row0 * 256));
+  g = as_bf16x8(lds_ld16(na[kc] + row0 * 256 + TILE_B));
+}
+
+// Scores of one block without a preceding step (the first block of a
+// wavefront's diagonal): its chains (init from ini, rows of na at row0) into
+// sacc, pacc, and, for the step that follows, the initial values of the next
+// block's chains (ini1 at row1) and its first row operands (na1 at row1).
+// On return sacc, pacc hold finished chains (16 wait states after the last
+// MFMA; see mfma_chain).
+__device__ __forceinline__ void dkdv_scores(const uint32_t (&na)[8], int row0, uint32_t ini,
+                                            const uint32_t (&na1)[8], int row1, uint32_t ini1,
                                             const bf16x8 (&kreg)[8], const bf16x8 (&vreg)[8],
-                                            f32x16& sacc, f32x16& pacc) {
-  sacc = f32x16{};
-  pacc = f32x16{};
-  const uint32_t r = row0 * 256;
+                                            f32x16& sacc, f32x16& pacc, f32x16& s1, f32x16& p1,
+                                            bf16x8 (&pre)[8], int lane) {
+  load_chain_init(ini, row0, lane, sacc, pacc);
 #pragma unroll
   for (int k4 = 0; k4 < 8; k4 += 4) {
     bf16x8 aq[4], ag[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      aq[i] = as_bf16x8(lds_ld16(na[k4 + i] + r));
-      ag[i] = as_bf16x8(lds_ld16(na[k4 + i] + r + TILE_B));
-    }
+    for (int i = 0; i < 4; ++i) read_rows(na, row0, k4 + i, aq[i], ag[i]);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      sacc = mfma32(aq[i], kreg[k4 + i], sacc);
-      pacc = mfma32(ag[i], vreg[k4 + i], pacc);
+      if (k4 + i == 0) {
+        mfma_chain_first(sacc, aq[i], kreg[k4 + i]);
+        mfma_chain_first(pacc, ag[i], vreg[k4 + i]);
+      } else {
+        mfma_chain(sacc, aq[i], kreg[k4 + i]);
+        mfma_chain(pacc, ag[i], vreg[k4 + i]);
+      }
     }
   }
+  load_chain_init(ini1, row1, lane, s1, p1);
+#pragma unroll
+  for (int kc = 0; kc < 4; ++kc) read_rows(na1, row1, kc, pre[kc], pre[4 + kc]);
+  asm volatile("s_nop 15" : "+v"(sacc), "+v"(pacc));
 }
 
 // dS of one 32-query x 32-key block, kept for the dQ GEMM: stored as a
@@ -194,71 +284,67 @@ __device__ __forceinline__ void store_ds(u16* blk, const bf16x8 (&sb)[2], int la
   st16(blk + l32 * 32 + 16 + 8 * half, __builtin_bit_cast(uint4, sb[1]));
 }
 
-// Steady-state step: probabilities of the current block (held in s_cur,
-// p_cur), scores of the next block into s_nxt, p_nxt, then the current
-// block's dK/dV accumulation.  The order is fixed by hand in eight rounds,
-// separated by scheduling fences: each round issues the LDS reads (operands,
-// lse and delta) two rounds ahead, one score MFMA for S and one for dP, and
-// the probability math of two of this lane's sixteen (key, query) elements,
-// so the VALU work runs while the matrix cores are busy; the last four rounds
-// also read the transposed operands of the first accumulation chunk.  na/rowN
-// locate the next block (row-wise reads of its tile), ta/rowC the current one
-// (transposed reads); nl_t and dl_t are the current tile's rows of -lse log2(e)
-// and of delta.
+// Steady-state step: probabilities of the current block (finished chains in
+// s_cur, p_cur), score chains of the next block (s_nxt, p_nxt hold their
+// initial values and pre[] its first four row operand pairs on entry), then
+// the current block's dK/dV accumulation.  The order is fixed by hand,
+// separated by scheduling fences: eight rounds, each with one S and one dP
+// MFMA, the probability math of two of this lane's sixteen (key, query)
+// elements, the row reads of round i + 4 (rounds 0..3) and one transposed
+// operand of the accumulation's first chunk; then sixteen accumulation
+// MFMAs, during which the second chunk's transposed operands are read (eight
+// MFMAs ahead of use) and, for the step after next, the block two ahead's
+// initial values (into s_cur, p_cur, dead by then) and first row operands
+// (into pre).  The block two ahead sits at the same rows (rowC) of the next
+// position's tile: nn, ini_nn.  na/rowN locate the next block, ta/rowC the
+// current one.
 // MASK: the current block holds this wavefront's diagonal; kq is its key
 // minus the first query row of the current tile, and P is zeroed where the
 // key follows the query.  BAND (with MASK): P is also zeroed where the query
 // lies more than win rows after the key (outside a sliding window).
 template <bool MASK, bool BAND = false>
-__device__ __forceinline__ void dkdv_step(const uint32_t (&na)[8], int rowN, const float* nl_t,
-                                          const float* dl_t, const uint32_t (&ta)[4][2],
-                                          int rowC, const bf16x8 (&kreg)[8],
-                                          const bf16x8 (&vreg)[8], const f32x16& s_cur,
-                                          const f32x16& p_cur, f32x16& s_nxt, f32x16& p_nxt,
-                                          f32x16 (&dka)[4], f32x16 (&dva)[4], int lane,
-                                          float c_log2, int kq, u16* ds_blk, int win = 0) {
+__device__ __forceinline__ void dkdv_step(const uint32_t (&na)[8], int rowN,
+                                          const uint32_t (&ta)[4][2], int rowC,
+                                          const uint32_t (&nn)[8], uint32_t ini_nn,
+                                          const bf16x8 (&kreg)[8], const bf16x8 (&vreg)[8],
+                                          bf16x8 (&pre)[8], f32x16& s_cur, f32x16& p_cur,
+                                          f32x16& s_nxt, f32x16& p_nxt, f32x16 (&dka)[4],
+                                          f32x16 (&dva)[4], int lane, int kq, u16* ds_blk,
+                                          int win = 0) {
   const int half = lane >> 5;
-  const uint32_t rn = rowN * 256;
   const uint32_t rc = rowC * 256;
   // element r of the current block: query row r0 + 16 (r/8) + r%8; round i
   // handles elements 2i, 2i+1 (rows rr(i), rr(i) + 1)
   const int r0 = rowC + 8 * half;
   auto rr = [&](int i) { return r0 + 16 * (i >> 2) + 2 * (i & 3); };
-  bf16x8 aq[8], ag[8];
-  float2 lr[8], dr[8];
+  bf16x8 aq[4], ag[4];  // row operands of rounds 4..7
   bf16x8 bg[2][4], bq[2][4];
-  auto reads = [&](int i) {
-    aq[i] = as_bf16x8(lds_ld16(na[i] + rn));
-    ag[i] = as_bf16x8(lds_ld16(na[i] + rn + TILE_B));
-    lr[i] = *reinterpret_cast<const float2*>(&nl_t[rr(i)]);
-    dr[i] = *reinterpret_cast<const float2*>(&dl_t[rr(i)]);
+  // transposed operands of chunk j, block db: dout^T (bg) and Q^T (bq)
+  auto tr_read = [&](int j, int db, bool dq) {
+    if (dq)
+      bq[j][db] = tr_operand(ta[db], rc + j * 16 * 256);
+    else
+      bg[j][db] = tr_operand(ta[db], rc + j * 16 * 256 + TILE_B);
   };
-  reads(0);
-  reads(1);
-  s_nxt = f32x16{};
-  p_nxt = f32x16{};
   uint32_t pw[8], sw[8];  // bf16 pairs (elements 2i, 2i+1)
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    if (i + 2 < 8) reads(i + 2);
-    if (i >= 4) {  // transposed operands of the first accumulation chunk
-      bg[0][i - 4] = tr_operand(ta[i - 4], rc + TILE_B);
-      bq[0][i - 4] = tr_operand(ta[i - 4], rc);
-    }
-    s_nxt = mfma32(aq[i], kreg[i], s_nxt);
+    if (i < 4) read_rows(na, rowN, i + 4, aq[i], ag[i]);
+    tr_read(0, i >> 1, i & 1);
+    mfma_chain_first_or_next(i, s_nxt, i < 4 ? pre[i] : aq[i - 4], kreg[i]);
     const int r = 2 * i;
-    float p0 = fast_exp2(fmaf(s_cur[r], c_log2, lr[i].x));
-    float p1 = fast_exp2(fmaf(s_cur[r + 1], c_log2, lr[i].y));
+    float p0 = fast_exp2(s_cur[r]);
+    float p1 = fast_exp2(s_cur[r + 1]);
     if (MASK) {  // rows rr(i), rr(i) + 1 of the current tile
       if (kq > rr(i) || (BAND && rr(i) - kq > win)) p0 = 0.f;
       if (kq > rr(i) + 1 || (BAND && rr(i) + 1 - kq > win)) p1 = 0.f;
     }
     pw[i] = pack_bf16x2(p0, p1);
-    sw[i] = pack_bf16x2(p0 * (p_cur[r] - dr[i].x), p1 * (p_cur[r + 1] - dr[i].y));
+    sw[i] = pack_bf16x2(p0 * p_cur[r], p1 * p_cur[r + 1]);
     // keep this round's VALU work in this round (no sinking to the first use)
     asm volatile("" : "+v"(pw[i]), "+v"(sw[i]));
-    p_nxt = mfma32(ag[i], vreg[i], p_nxt);
+    mfma_chain_first_or_next(i, p_nxt, i < 4 ? pre[4 + i] : ag[i - 4], vreg[i]);
     __builtin_amdgcn_sched_barrier(0);
   }
   const bf16x8 pb[2] = {as_bf16x8(make_uint4(pw[0], pw[1], pw[2], pw[3])),
@@ -266,29 +352,43 @@ __device__ __forceinline__ void dkdv_step(const uint32_t (&na)[8], int rowN, con
   const bf16x8 sb[2] = {as_bf16x8(make_uint4(sw[0], sw[1], sw[2], sw[3])),
                         as_bf16x8(make_uint4(sw[4], sw[5], sw[6], sw[7]))};
   if (ds_blk) store_ds(ds_blk, sb, lane);
-  // dV += P^T dout, dK += dS^T Q for the current block: operands of chunk 1
-  // are read while chunk 0's MFMAs run
+  // dV += P^T dout, dK += dS^T Q for the current block
+  const uint32_t ia = ini_nn + 4 * (rowC + 8 * half);  // load_chain_init's rows
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    if (j == 0) {
+  for (int m = 0; m < 16; ++m) {
+    const int j = m >> 3, db = (m >> 1) & 3;
+    if (m & 1)
+      mfma_acc(dka[db], bq[j][db], sb[j]);
+    else
+      mfma_acc(dva[db], bg[j][db], pb[j]);
+    if (m < 8) {
+      tr_read(1, m >> 1, m & 1);  // chunk 1, eight MFMAs ahead
+    } else {
+      // the block two ahead: initial values first (needed by its first MFMA)
+      const int x = m - 8;
+      if (x < 4) {
+        const uint32_t o = (x & 1) * 16 + (x >> 1) * 64;
+        const uint4 sv = lds_ld16(ia + o), pv = lds_ld16(ia + o + 256);
 #pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        bg[1][db] = tr_operand(ta[db], rc + 16 * 256 + TILE_B);
-        bq[1][db] = tr_operand(ta[db], rc + 16 * 256);
+        for (int e = 0; e < 4; ++e) {
+          s_cur[4 * x + e] = __uint_as_float((&sv.x)[e]);
+          p_cur[4 * x + e] = __uint_as_float((&pv.x)[e]);
+        }
+      } else {
+        read_rows(nn, rowC, x - 4, pre[x - 4], pre[x]);
       }
-    }
-#pragma unroll
-    for (int db = 0; db < 4; ++db) {
-      dva[db] = mfma32(bg[j][db], pb[j], dva[db]);
-      dka[db] = mfma32(bq[j][db], sb[j], dka[db]);
     }
     __builtin_amdgcn_sched_barrier(0);
   }
 }
 
-// lse (natural log) -> -lse log2(e), in place, for the 64 rows of a tile.
-__device__ __forceinline__ void to_exp2_offset(float* rows, int lane) {
-  rows[lane] = rows[lane] * -kLog2e;
+// The rows of a tile's lse and delta (raw, in the shared buffer) rewritten
+// into this wavefront's own copy as -lse log2(e) and -delta: the initial
+// values of the score chains.  Each wavefront reads only its own copy, so no
+// barrier is needed between the rewrite and the reads.
+__device__ __forceinline__ void rewrite_rows(const float* raw, float* own, int lane) {
+  own[lane] = raw[lane] * -kLog2e;
+  own[64 + lane] = -raw[64 + lane];
 }
 
 // WIN: sliding window, key j visible to query i iff i - win <= j <= i.
@@ -307,6 +407,8 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(
   __shared__ __attribute__((aligned(1024))) char qtiles[NBUF * BUF_B];
   __shared__ __attribute__((aligned(1024))) char kstage[2 * TILE_B];  // K rows of an item
   __shared__ __attribute__((aligned(16))) float lsd[NBUF][2][QT_ROWS];
+  // each wavefront's rewritten lse, delta rows (rewrite_rows) per buffer
+  __shared__ __attribute__((aligned(16))) float lsw[4][NBUF][2][QT_ROWS];
   __shared__ __attribute__((aligned(1024))) char estage[4][4096];  // dK, dV rows on the way out
 
   const int tid = threadIdx.x;
@@ -331,6 +433,10 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(
   const uint32_t lsd_lds = lds_addr(&lsd[0][0][0]);
   const uint32_t kst_lds = lds_addr(kstage);
   const uint32_t est_lds = lds_addr(&estage[wave][0]);
+  // init rows of the score chains for buffer u (load_chain_init)
+  const uint32_t lsw_lds = lds_addr(&lsw[wave][0][0][0]);
+  auto ini = [&](int u) { return lsw_lds + static_cast<uint32_t>(u) * 2 * QT_ROWS * 4; };
+  auto rewrite = [&](int u) { rewrite_rows(&lsd[u][0][0], &lsw[wave][u][0][0], lane); };
 
   // A work item: the 128-key tile k0 / 128 of key/value head hk of batch b
   // (xcd_tile_map_grouped order, key tile 0, the one with the most work,
@@ -434,10 +540,11 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(
     const int kw0 = cur.k0 + 32 * wave;
     const size_t kbase = cur.kbase;
     const int ub2 = gb == 0 ? 2 : gb - 1;  // (gb + 2) % NBUF
-    // The lse rows are used as -lse log2(e), the exponent offset of P in the
-    // exp2 domain: the wavefront that first sees a tile's rows land rewrites
-    // them in place (the next barrier publishes them).
-    if (wave < 2 && wave < N) to_exp2_offset(lsd[(gb + wave) % NBUF][0], lane);
+    // The score chains start from -lse log2(e) and -delta: every wavefront
+    // rewrites the rows of the tiles at positions 0 and 1 into its own copy
+    // (and of position n + 1 at each later tile's barrier).
+    rewrite(gb);
+    if (1 < N) rewrite((gb + 1) % NBUF);
     // K^T and V^T operands: lane holds row kw0 + l32, elements 16 kc + 8 half
     // + 0..7, read from the rows staged with 16 lanes per row.
     const int krow = kw0 + l32;
@@ -448,7 +555,18 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(
 #pragma unroll
       for (int kc = 0; kc < 8; ++kc) {
         const uint32_t o = o_row + 16 * ((2 * kc + half) ^ tile_swz(rr));
-        kreg[kc] = as_bf16x8(lds_ld16(kst_lds + o));
+        // K' = s log2(e) K, rounded to bf16: the S chain then holds the
+        // exponent of P in the exp2 domain directly
+        const uint4 kw = lds_ld16(kst_lds + o);
+        const uint32_t w[4] = {kw.x, kw.y, kw.z, kw.w};
+        uint32_t ks[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          ks[j] = pack_bf16x2(__uint_as_float(w[j] << 16) * c_log2,
+                              __uint_as_float(w[j] & 0xffff0000u) * c_log2);
+        // moved into AGPRs here, once per item (defined by this asm in the
+        // AGPR class, so the MFMAs find it there without a copy per use)
+        asm volatile("" : "=a"(kreg[kc]) : "0"(as_bf16x8(make_uint4(ks[0], ks[1], ks[2], ks[3]))));
         vreg[kc] = as_bf16x8(lds_ld16(qt_lds + ub2 * BUF_B + o));
       }
     }
@@ -492,7 +610,9 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(
     f32x16 s0, p0, s1, p1;  // scores of even blocks in s0/p0, of odd blocks in s1/p1
     uint32_t nc[8];         // row-read addresses of the current tile
     nat_addr(qt_lds + gb * BUF_B, ofs, nc);
-    if (bw == 2 * qt0) dkdv_scores(nc, 0, kreg, vreg, s0, p0);
+    bf16x8 pre[8];          // first row operands of the next block's chains
+    if (bw == 2 * qt0)  // block 0 of position 0 is the diagonal
+      dkdv_scores(nc, 0, ini(gb), nc, 32, ini(gb), kreg, vreg, s0, p0, s1, p1, pre, lane);
     int u = gb;  // buffer of the current position
     // The first two tiles of each query head (every diagonal block of the
     // workgroup) take the per-wavefront branches; the rest run one branch-free
@@ -523,7 +643,8 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(
           copy_rows(nxt, k, kst_lds);
           k_next = true;
         }
-        if (n + 1 < N && wave == 3) to_exp2_offset(lsd[un][0], lane);  // position n+1
+        if (n + 1 < N) rewrite(un);  // position n+1 (landed at this barrier)
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       }
       uint32_t tc[4][2], nn[8];
       tr_addr(qt_lds + u * BUF_B, ofs, tc);
@@ -533,33 +654,35 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(
       // with a window: some row of tile t lies past the window of this
       // wavefront's first key, so its steps also take the band select
       const bool edge = WIN && QT_ROWS * t + QT_ROWS - 1 - kw0 > win;
+      // the block two ahead of each step: the same rows of the next position
+      const uint32_t inn = ini(un);
       // block j0 (rows 0..31 of tile t), scores of rows 32..63
       if (STEADY || j0 > bw) {
         if (WIN && edge)
-          dkdv_step<true, true>(nc, 32, lsd[u][0], lsd[u][1], tc, 0, kreg, vreg, s0, p0, s1, p1,
-                                dka, dva, lane, c_log2, kq, ds_of(h, j0), win);
+          dkdv_step<true, true>(nc, 32, tc, 0, nn, inn, kreg, vreg, pre, s0, p0, s1, p1, dka, dva,
+                                lane, kq, ds_of(h, j0), win);
         else
-          dkdv_step<false>(nc, 32, lsd[u][0], lsd[u][1], tc, 0, kreg, vreg, s0, p0, s1, p1, dka,
-                           dva, lane, c_log2, kq, ds_of(h, j0));
+          dkdv_step<false>(nc, 32, tc, 0, nn, inn, kreg, vreg, pre, s0, p0, s1, p1, dka, dva, lane,
+                           kq, ds_of(h, j0));
       } else if (j0 == bw) {
-        dkdv_step<true, WIN>(nc, 32, lsd[u][0], lsd[u][1], tc, 0, kreg, vreg, s0, p0, s1, p1,
-                             dka, dva, lane, c_log2, kq, ds_of(h, j0), win);
-      } else if (j0 == bw - 1) {
-        dkdv_scores(nc, 32, kreg, vreg, s1, p1);
+        dkdv_step<true, WIN>(nc, 32, tc, 0, nn, inn, kreg, vreg, pre, s0, p0, s1, p1, dka, dva,
+                             lane, kq, ds_of(h, j0), win);
+      } else if (j0 == bw - 1) {  // rows 32..63 hold the diagonal
+        dkdv_scores(nc, 32, ini(u), nn, 0, inn, kreg, vreg, s1, p1, s0, p0, pre, lane);
       }
       // block j1 (rows 32..63 of tile t), scores of the next position's rows 0..31
       if (STEADY || j1 > bw) {
         if (WIN && edge)
-          dkdv_step<true, true>(nn, 0, lsd[u][0], lsd[u][1], tc, 32, kreg, vreg, s1, p1, s0, p0,
-                                dka, dva, lane, c_log2, kq, ds_of(h, j1), win);
+          dkdv_step<true, true>(nn, 0, tc, 32, nn, inn, kreg, vreg, pre, s1, p1, s0, p0, dka, dva,
+                                lane, kq, ds_of(h, j1), win);
         else
-          dkdv_step<false>(nn, 0, lsd[u][0], lsd[u][1], tc, 32, kreg, vreg, s1, p1, s0, p0, dka,
-                           dva, lane, c_log2, kq, ds_of(h, j1));
+          dkdv_step<false>(nn, 0, tc, 32, nn, inn, kreg, vreg, pre, s1, p1, s0, p0, dka, dva, lane,
+                           kq, ds_of(h, j1));
       } else if (j1 == bw) {
-        dkdv_step<true, WIN>(nn, 0, lsd[u][0], lsd[u][1], tc, 32, kreg, vreg, s1, p1, s0, p0,
-                             dka, dva, lane, c_log2, kq, ds_of(h, j1), win);
-      } else if (j1 == bw - 1) {
-        dkdv_scores(nn, 0, kreg, vreg, s0, p0);
+        dkdv_step<true, WIN>(nn, 0, tc, 32, nn, inn, kreg, vreg, pre, s1, p1, s0, p0, dka, dva,
+                             lane, kq, ds_of(h, j1), win);
+      } else if (j1 == bw - 1) {  // the next position's rows 0..31 hold the diagonal
+        dkdv_scores(nn, 0, inn, nn, 32, inn, kreg, vreg, s0, p0, s1, p1, pre, lane);
       }
 #pragma unroll
       for (int kc = 0; kc < 8; ++kc) nc[kc] = nn[kc];
@@ -577,6 +700,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(
     // Every wavefront is done with the last tile's buffer: the next item's V
     // rows go there, and whatever the stream has not copied yet of its K rows
     // and first two query tiles follows.
+    mfma_drain(dka, dva);
     __syncthreads();
     const int ulast = (gb + N - 1) % NBUF;
     if (has_next) {

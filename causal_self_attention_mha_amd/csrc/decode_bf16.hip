@@ -400,9 +400,7 @@ hipError_t launch_decode_bf16(const void* q, const void* kc, const void* vc, con
   float* opart = static_cast<float*>(ws);
   float* ml = opart + static_cast<std::size_t>(B) * NC * H * D;
   // persistent workgroups: a few per compute unit, never more than slots
-  int dev = 0, cus = 256;
-  if (hipGetDevice(&dev) == hipSuccess)
-    (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  const int cus = device_cus();
   // grouped query heads: one 16-lane group per key/value head serves its 2 or
   // 4 query heads (each cached row loaded once); other ratios use one group
   // per query head

@@ -158,6 +158,7 @@ __device__ __forceinline__ void lds_st8(uint32_t lds, uint32_t lo, uint32_t hi) 
 
 // Sixteen-byte LDS read at an LDS byte address.
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x16 __attribute__((ext_vector_type(16)));
 __device__ __forceinline__ uint4 lds_ld16(uint32_t lds) {
   const u32x4 v = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(lds);
   return __builtin_bit_cast(uint4, v);

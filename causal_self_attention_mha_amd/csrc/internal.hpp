@@ -5,6 +5,8 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+
+#include <atomic>
 #include <cstddef>
 #include <cstdint>
 #include <tuple>
@@ -98,19 +100,21 @@ hipError_t launch_value_gate_bf16(const void* a, const void* ve, const void* gat
                                   hipStream_t s);
 
 // Compute units of the current device (cached per device; 256 if the query
-// fails).  Persistent grids size themselves from it.
+// fails).  Persistent grids size themselves from it.  Safe to call from several
+// threads: each cache slot is an atomic, and two threads that race on a slot's
+// first query store the same value.
 inline int device_cus() {
-  static int cached[64] = {};
+  static std::atomic<int> cached[64] = {};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int cus = 0;
+  int cus = cached[dev].load(std::memory_order_relaxed);
+  if (cus == 0) {
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         cus <= 0)
       cus = 256;
-    cached[dev] = cus;
+    cached[dev].store(cus, std::memory_order_relaxed);
   }
-  return cached[dev];
+  return cus;
 }
 
 // Grid of a persistent kernel: per_cu workgroups per compute unit, never more

@@ -191,12 +191,10 @@ hipError_t launch_value_gate_bf16(const void* a, const void* ve, const void* gat
   auto ca = static_cast<const u16*>(a), cv = static_cast<const u16*>(ve),
        cg = static_cast<const u16*>(gate);
   if (backward)
-    hipLaunchKernelGGL(value_gate_kernel<true>, grid, block, 0, s, ca, cv, cg,
-                       static_cast<u16*>(out), static_cast<u16*>(dgate), rows);
-  else
-    hipLaunchKernelGGL(value_gate_kernel<false>, grid, block, 0, s, ca, cv, cg,
-                       static_cast<u16*>(out), nullptr, rows);
-  return hipGetLastError();
+    return launch(value_gate_kernel<true>, grid, block, 0, s, ca, cv, cg, static_cast<u16*>(out),
+                  static_cast<u16*>(dgate), rows);
+  return launch(value_gate_kernel<false>, grid, block, 0, s, ca, cv, cg, static_cast<u16*>(out),
+                static_cast<u16*>(nullptr), rows);
 }
 
 hipError_t launch_qk_norm_rope_bf16(const void* q, const void* k, const void* dyq,
@@ -208,13 +206,12 @@ hipError_t launch_qk_norm_rope_bf16(const void* q, const void* k, const void* dy
   auto cq = static_cast<const u16*>(q), ck = static_cast<const u16*>(k);
   auto oq = static_cast<u16*>(outq), ok = static_cast<u16*>(outk);
   if (backward)
-    hipLaunchKernelGGL(qk_norm_rope_kernel<true>, grid, block, 0, s, cq, ck,
-                       static_cast<const u16*>(dyq), static_cast<const u16*>(dyk), oq, ok, cos_t,
-                       sin_t, off, B, T, H, Hk, T_tab, eps);
-  else
-    hipLaunchKernelGGL(qk_norm_rope_kernel<false>, grid, block, 0, s, cq, ck, nullptr, nullptr,
-                       oq, ok, cos_t, sin_t, off, B, T, H, Hk, T_tab, eps);
-  return hipGetLastError();
+    return launch(qk_norm_rope_kernel<true>, grid, block, 0, s, cq, ck,
+                  static_cast<const u16*>(dyq), static_cast<const u16*>(dyk), oq, ok, cos_t, sin_t,
+                  off, B, T, H, Hk, T_tab, eps);
+  return launch(qk_norm_rope_kernel<false>, grid, block, 0, s, cq, ck,
+                static_cast<const u16*>(nullptr), static_cast<const u16*>(nullptr), oq, ok, cos_t,
+                sin_t, off, B, T, H, Hk, T_tab, eps);
 }
 
 }  // namespace na
