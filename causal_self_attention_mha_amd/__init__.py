@@ -12,6 +12,8 @@ Functions (names match the C entry points):
   attn_fwd(q, k, v)                       -> (o, lse)
   attn_bwd(q, k, v, o, dout, lse)         -> (dq, dk, dv, delta)
   attn_decode(q, k_cache, v_cache, seqlens) -> (o, lse)
+  attn_decode_noalloc(q, k_cache, v_cache, seqlens) -> (o, lse)
+                                          (no workspace: the library's fixed scratch)
   attn_decode_append(q, k_new, v_new, k_cache, v_cache, seqlens) -> (o, lse)
                                           (appends the new token's key/value rows first)
   attn_prefill(q, k_new, v_new, k_cache, v_cache, cache_lens) -> (o, lse)
@@ -38,7 +40,8 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["attn_fwd", "attn_bwd", "attn_decode", "attn_decode_append", "attn_prefill",
+__all__ = ["attn_fwd", "attn_bwd", "attn_decode", "attn_decode_noalloc", "attn_decode_append",
+           "attn_prefill",
            "qk_norm_rope_fwd",
            "qk_norm_rope_bwd", "value_gate_fwd", "value_gate_bwd", "decode_workspace_bytes",
            "bwd_workspace_bytes",
@@ -84,6 +87,7 @@ def load_library():
     lib.na_attn_bwd_workspace_bytes.argtypes = [i, i, i, i]
     lib.na_attn_bwd_workspace_bytes.restype = sz
     lib.na_attn_decode.argtypes = [vp, vp, vp, vp, vp, f32p, i, i, i, i, vp, sz, vp]
+    lib.na_attn_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, f32p, i, i, i, i, vp]
     lib.na_attn_decode_workspace_bytes.argtypes = [i, i, i, i]
     lib.na_attn_decode_workspace_bytes.restype = sz
     lib.na_attn_fwd_f32.argtypes = [vp, vp, vp, vp, f32p, i, i, i, i, vp]
@@ -118,7 +122,7 @@ def load_library():
                "na_attn_fwd_gqa", "na_attn_bwd_gqa", "na_attn_decode_gqa", "na_attn_prefill",
                "na_qk_norm_rope_fwd", "na_qk_norm_rope_bwd", "na_value_gate_fwd",
                "na_value_gate_bwd", "na_attn_prefill_rope", "na_attn_decode_append",
-               "na_attn_bwd_rope"):
+               "na_attn_bwd_rope", "na_attn_decode_noalloc"):
         getattr(lib, fn).restype = ctypes.c_int
     lib.na_status_string.argtypes = [ctypes.c_int]
     lib.na_status_string.restype = ctypes.c_char_p
@@ -355,6 +359,37 @@ def attn_decode(q, k_cache, v_cache, seqlens, o=None, lse=None, workspace=None,
     else:
         _check(lib, "na_attn_decode",
                lib.na_attn_decode(*args, B, H, D, T_cap, _ptr(workspace), ws_bytes, _stream(q)))
+    return o, lse
+
+
+def attn_decode_noalloc(q, k_cache, v_cache, seqlens, o=None, lse=None, want_lse=True):
+    """attn_decode through na_attn_decode_noalloc: no workspace, the split-KV
+    partials go to the library's fixed 16 MiB per-device scratch (sizes that
+    need more raise NAError).  Calls on one device share that scratch, so
+    calls that may overlap on different streams race.  Returns (o, lse)."""
+    import torch
+    lib = load_library()
+    _require(q.is_cuda and q.dtype == torch.bfloat16 and q.dim() == 3 and q.shape[-1] == HEAD_DIM,
+             "q must be a bf16 GPU tensor (B, H, 128)")
+    B, H, D = q.shape
+    _require(k_cache.dim() == 4 and tuple(k_cache.shape[2:]) == (H, D) and k_cache.shape[0] == B,
+             "k_cache must be (B, T_cap, H, 128)")
+    T_cap = k_cache.shape[1]
+    for n, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
+        _require(t.dtype == torch.bfloat16 and t.device == q.device and t.is_contiguous(),
+                 f"{n} must be contiguous bf16 on {q.device}")
+    _require(v_cache.shape == k_cache.shape, "v_cache must match k_cache")
+    _require(seqlens.dtype == torch.int32 and seqlens.shape == (B,) and seqlens.device == q.device
+             and seqlens.is_contiguous(), "seqlens must be int32 [B] on the GPU")
+    o = torch.empty_like(q) if o is None else o
+    if want_lse and lse is None:
+        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    _check_buf("o", o, torch.bfloat16, (B, H, D), q.device)
+    if lse is not None:
+        _check_buf("lse", lse, torch.float32, (B, H), q.device)
+    _check(lib, "na_attn_decode_noalloc",
+           lib.na_attn_decode_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seqlens),
+                                      _ptr(o), _ptr(lse), B, H, D, T_cap, _stream(q)))
     return o, lse
 
 

@@ -374,6 +374,35 @@ na_status na_attn_decode(const void* q, const void* k_cache, const void* v_cache
                               workspace_bytes, stream, nullptr);
 }
 
+na_status na_attn_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                 const int* seqlens, void* o, float* lse, int B, int H, int D,
+                                 int T_cap, void* stream) {
+  na_status st = check_sizes(B, T_cap, H, D);
+  if (st) return st;
+  if (lse != nullptr) {
+    st = check_ptrs({{q, "q"}, {k_cache, "k_cache"}, {v_cache, "v_cache"}, {seqlens, "seqlens"}},
+                    {{o, "o"}, {lse, "lse"}});
+  } else {
+    st = check_ptrs({{q, "q"}, {k_cache, "k_cache"}, {v_cache, "v_cache"}, {seqlens, "seqlens"}},
+                    {{o, "o"}});
+  }
+  if (st) return st;
+  if (B > 65535) return fail(NA_ERR_INVALID_ARG, "decode supports B <= 65535 (B=%d)", B);
+  if (H > 32) return fail(NA_ERR_UNSUPPORTED, "decode supports H <= 32 (H=%d)", H);
+  const size_t need = na::decode_workspace_bytes(B, H, T_cap);
+  if (need > na::kDecodeScratchBytes)
+    return fail(NA_ERR_INVALID_ARG,
+                "these sizes need %zu bytes of decode scratch; the library's own scratch holds "
+                "%zu (pass a workspace to na_attn_decode instead)",
+                need, na::kDecodeScratchBytes);
+  void* ws = nullptr;
+  if (hipError_t e = na::decode_scratch(&ws); e != hipSuccess)
+    return hip_status(e, "na_attn_decode_noalloc (scratch lookup)");
+  return hip_status(na::launch_decode_bf16(q, k_cache, v_cache, seqlens, o, lse, B, H, H, T_cap,
+                                           -1, ws, (hipStream_t)stream, nullptr),
+                    "na_attn_decode_noalloc");
+}
+
 na_status na_attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
                           int B, int T, int H, int D, void* stream) {
   na_status st = check_sizes(B, T, H, D);

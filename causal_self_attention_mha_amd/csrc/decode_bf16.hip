@@ -31,6 +31,7 @@
 // them (d20 with 5 key/value heads: 48.7 -> 42 us, with four workgroups per
 // compute unit instead of two).
 #include <algorithm>
+#include <mutex>
 
 #include "device_common.hpp"
 #include "internal.hpp"
@@ -382,6 +383,35 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(
 }
 
 }  // namespace
+
+// Scratch for callers that cannot allocate (na_attn_decode_noalloc): a fixed
+// array in every device's global memory, which holds the split-KV partials in
+// place of a caller workspace.  Host code never uses the array's name as an
+// address (on the host it is a stand-in, not a device pointer): the device
+// address comes from hipGetSymbolAddress, looked up once per device with that
+// device current and cached.  Every call on a device shares its array, so
+// calls that overlap on one device race; nothing needs clearing between calls
+// (the combine reads only the partials the split kernel of the same call
+// wrote).
+static __device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
+
+hipError_t decode_scratch(void** ptr) {
+  static std::mutex mu;
+  static void* cached[64] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (cached[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    cached[dev] = p;
+  }
+  *ptr = cached[dev];
+  return hipSuccess;
+}
 
 std::size_t decode_workspace_bytes(int B, int H, int T_cap) {
   const std::size_t slots = static_cast<std::size_t>(B) * n_chunks(T_cap) * H;

@@ -69,6 +69,11 @@ hipError_t launch_kv_append_bf16(const void* k_new, const void* v_new, void* kc,
 
 // Decode workspace layout and size (bytes).
 std::size_t decode_workspace_bytes(int B, int H, int T_cap);
+// The library's own decode scratch (na_attn_decode_noalloc): kDecodeScratchBytes
+// of device memory per device; decode_scratch returns the current device's
+// address of it (looked up once per device).
+constexpr std::size_t kDecodeScratchBytes = std::size_t(16) << 20;
+hipError_t decode_scratch(void** ptr);
 // With k_new non-null, the new token's key/value rows (B, Hk, D) are first
 // appended at row clamp(seqlens[b], 0, T_cap - 1) (launch_kv_append_bf16 with
 // T = 1, rotated / gated as given) and the sequence then includes it; with

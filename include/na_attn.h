@@ -116,6 +116,26 @@ na_status na_attn_decode(const void* q, const void* k_cache, const void* v_cache
 size_t na_attn_decode_workspace_bytes(int B, int H, int D, int T_cap);
 
 /*
+ * na_attn_decode without a workspace argument, for callers that cannot
+ * allocate device memory: code being captured into a HIP graph, tight serving
+ * loops, harnesses that forbid hipMalloc.  Same arguments (minus workspace),
+ * layouts, results and errors as na_attn_decode, and the same kernels; the
+ * split-KV partials go to a fixed scratch array of 16 MiB that the library
+ * holds in each device's memory until the process ends.  Sizes whose
+ * na_attn_decode_workspace_bytes exceed 16 MiB are rejected with
+ * NA_ERR_INVALID_ARG before anything is enqueued (the d20 decode shape, B = 64,
+ * H = 10, T_cap = 2048, needs 10.6 MB).  Allocates nothing: the first call on
+ * a device looks up the scratch's device address (hipGetSymbolAddress) and
+ * caches it.  All calls on one device share the scratch: calls that may
+ * overlap on one device (different streams without ordering) race and must
+ * be serialised by the caller.  Nothing in the scratch needs clearing between
+ * calls.
+ */
+na_status na_attn_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                 const int* seqlens, void* o, float* lse, int B, int H, int D,
+                                 int T_cap, void* stream);
+
+/*
  * fp32 twins of the forward and backward (fp32 storage and arithmetic
  * throughout, no bf16 rounding anywhere); same layouts, same conventions.
  * For correctness at fp32 tolerances, not speed.

@@ -336,3 +336,16 @@ def test_every_required_pointer_is_checked(lib, name, args, required):
         p[i] = 0
         assert fn(*args(p)) == INVALID, (name, i)
         assert b"NULL" in lib.na_last_error(), (name, i, lib.na_last_error())
+
+
+def test_decode_noalloc_rejects_sizes_beyond_its_scratch(lib):
+    """na_attn_decode_noalloc refuses, on the host, sizes whose split-KV
+    partials would not fit its fixed 16 MiB scratch."""
+    need = lib.na_attn_decode_workspace_bytes(512, 16, 128, 4096)
+    assert need > 16 << 20
+    st = lib.na_attn_decode_noalloc(A, A + 0x100, A + 0x200, A + 0x300, A + 0x400, A + 0x500,
+                                    512, 16, 128, 4096, None)
+    assert st == INVALID and b"scratch" in lib.na_last_error()
+    assert lib.na_attn_decode_noalloc(0, A, A, A, A, A, 4, 2, 128, 64, None) == INVALID
+    assert lib.na_attn_decode_noalloc(A, A + 0x100, A + 0x200, A + 0x300, A + 0x400, A + 0x500,
+                                      4, 2, 64, 64, None) == UNSUPPORTED
