@@ -148,43 +148,6 @@ constexpr uint32_t BUF_B = 2 * TILE_B;        // one buffer: q tile, then dout t
 // transposed copy) in the swizzled 64 x 128 layout of tile_swz; Q and dout rows
 // are read row-wise as MFMA A operands and transposed as B operands.
 
-// The dK/dV pass writes its MFMAs as inline assembly so that each value sits in
-// the register file its users need: the score chains (S, dP) accumulate in
-// VGPRs, where the softmax VALU work reads them, while the dK and dV
-// accumulators and the K, V operands stay in AGPRs.  (With the compiler's
-// builtins the choice is one form for the whole kernel, and the scores then
-// came out in AGPRs and were copied back, 32 copies per 64-query tile.)  The
-// compiler neither knows these are MFMAs nor inserts their hazard wait states,
-// so the wrappers and the code around them keep gfx950's rules for
-// v_mfma_f32_32x32x16_bf16 (the same numbers the compiler inserts around its
-// builtins): a VALU write of an operand needs 2 wait states before the MFMA
-// reads it (the "s_nop 1" below; a copy the compiler might place right before
-// the statement is such a write), a VALU read of the result needs 12 after the
-// MFMA issues (every score chain is read one pipeline step later, after at
-// least 16 other MFMAs, or behind an explicit s_nop), back-to-back MFMAs that
-// accumulate into the same registers need none, and a read of the dK/dV
-// accumulators by VALU code waits behind mfma_drain().
-//
-// Score chain link: d (VGPR) += a (VGPR) * b (AGPR).
-__device__ __forceinline__ void mfma_chain(f32x16& d, bf16x8 a, bf16x8 b) {
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "a"(b));
-}
-// First link of a score chain: d holds the chain's initial value (LDS reads,
-// or a copy the compiler may have placed just before).
-__device__ __forceinline__ void mfma_chain_first(f32x16& d, bf16x8 a, bf16x8 b) {
-  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "a"(b));
-}
-// dK/dV accumulation: acc (AGPR) += a (VGPR) * b (VGPR, written by VALU).
-__device__ __forceinline__ void mfma_acc(f32x16& acc, bf16x8 a, bf16x8 b) {
-  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
-}
-// Wait states between the last accumulation and any read of the accumulators
-// (they are read back through v_accvgpr_read by the epilogue).
-__device__ __forceinline__ void mfma_drain(f32x16 (&dka)[4], f32x16 (&dva)[4]) {
-  asm volatile("s_nop 15\n\ts_nop 7" : "+a"(dka[0]), "+a"(dka[1]), "+a"(dka[2]), "+a"(dka[3]));
-  asm volatile("" : "+a"(dva[0]), "+a"(dva[1]), "+a"(dva[2]), "+a"(dva[3]));
-}
-
 // Initial values of one 32-query block's score chains, for this lane's
 // accumulator elements (element r: query row row0 + acc_row(lane, r), see
 // dkdv_scores): the S chain starts at -lse log2(e) and the dP chain at -delta,

@@ -349,4 +349,49 @@ __device__ __forceinline__ void tstore_4x8(u16* tile, const uint4 (&x)[4], int l
   }
 }
 
+// ---------------------------------------------------------------------------
+// MFMAs written as inline assembly, so that each value sits in the register
+// file its users need: score chains accumulate in VGPRs, where the softmax
+// VALU work reads them, while long-lived accumulators (dK, dV, O) and
+// resident operands (K, V, Q) stay in AGPRs.  (With the compiler's builtins
+// the choice is one form for the whole kernel, and with more than 256
+// registers per lane the scores then come out in AGPRs and are copied back.)
+// The compiler neither knows these are MFMAs nor inserts their hazard wait
+// states, so the wrappers and the code around them keep gfx950's rules for
+// v_mfma_f32_32x32x16_bf16 (the same numbers the compiler inserts around its
+// builtins): a VALU write of an operand needs 2 wait states before the MFMA
+// reads it (the "s_nop 1" below; a copy the compiler might place right before
+// the statement is such a write), a VALU read of the result needs 12 after the
+// MFMA issues (callers read a chain only after at least one further MFMA has
+// issued behind it, or behind an explicit s_nop), back-to-back MFMAs that
+// accumulate into the same registers need none, and VALU code that reads
+// AGPR accumulators first waits behind a drain (s_nop 15, s_nop 7).
+//
+// Score chain link: d (VGPR) += a (VGPR) * b (AGPR).
+__device__ __forceinline__ void mfma_chain(f32x16& d, bf16x8 a, bf16x8 b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "a"(b));
+}
+// First link of a score chain: d holds the chain's initial value (LDS reads,
+// or a copy the compiler may have placed just before).
+__device__ __forceinline__ void mfma_chain_first(f32x16& d, bf16x8 a, bf16x8 b) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "a"(b));
+}
+// dK/dV accumulation: acc (AGPR) += a (VGPR) * b (VGPR, written by VALU).
+__device__ __forceinline__ void mfma_acc(f32x16& acc, bf16x8 a, bf16x8 b) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+// First link of a chain with a separate initial value: d (VGPR) = a * b + c,
+// c left intact (a persistent offset vector); d must not overlap the inputs.
+__device__ __forceinline__ void mfma_chain_init(f32x16& d, bf16x8 a, bf16x8 b, const f32x16& c) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %3"
+               : "=&v"(d)
+               : "v"(a), "a"(b), "v"(c));
+}
+// Wait states between the last accumulation into eight AGPR accumulators and
+// any read of them (VALU code reads them back through v_accvgpr_read).
+__device__ __forceinline__ void mfma_drain(f32x16 (&x)[4], f32x16 (&y)[4]) {
+  asm volatile("s_nop 15\n\ts_nop 7" : "+a"(x[0]), "+a"(x[1]), "+a"(x[2]), "+a"(x[3]));
+  asm volatile("" : "+a"(y[0]), "+a"(y[1]), "+a"(y[2]), "+a"(y[3]));
+}
+
 }  // namespace na

@@ -76,14 +76,18 @@ def test_bf16_recompute_dq_path(dev, B, T, H):
 
 
 def test_dq_paths_agree(dev):
-    """Stored-dS GEMM and recompute give the same dq up to bf16 rounding of dS."""
+    """Stored-dS GEMM and recompute give the same dq up to rounding: the dK/dV
+    pass that writes dS rounds dS to bf16 and scores against s log2(e) K
+    rounded to bf16, where the recompute pass scales the scores in fp32, so
+    P (and dS) differ by about 2^-9 relative per element; both paths are
+    compared with the oracle at the bf16 tolerances elsewhere."""
     import torch
     inp = W.make_train_inputs("d20", B=1, T=700, H=2, seed=9)
     a = gpu_fwd_bwd(inp, dev)
     b = gpu_fwd_bwd(inp, dev, recompute_dq=True)
     for n in ("dk", "dv", "delta"):
         assert torch.equal(a[n], b[n]), n
-    assert_close("dq paths", to_host(a["dq"]), to_host(b["dq"]), 2e-3, 2e-3)
+    assert_close("dq paths", to_host(a["dq"]), to_host(b["dq"]), 5e-3, 2e-3)
 
 
 def test_bf16_unit_scale_inputs(dev):
