@@ -139,16 +139,30 @@ def train_flops(B, T, H, D):
     return {"fwd": 2 * unit, "delta": 0, "dkdv": 4 * unit, "dq": 1 * unit, "fwd+bwd": 7 * unit}
 
 
-def train_bytes(B, T, H, D):
-    """Minimum HBM bytes per launch: every input read once, every output written
-    once.  The backward runs with the dS workspace: dkdv also writes dS (bf16,
-    lower-triangular 32 x 32 blocks per head) and dq reads it with K."""
+def design_bytes(B, T, H, D):
+    """HBM bytes per launch of the design as built: every operand read once,
+    every result written once, including the dS workspace the backward streams
+    (dkdv writes dS, bf16 lower-triangular 32 x 32 blocks per head, and dq reads
+    it back with K)."""
     t = B * T * H * D * 2          # one bf16 (B, T, H, D) tensor
     r = B * H * T * 4              # one fp32 (B, H, T) row vector
     nblk = (T + 31) // 32
     ds = B * H * nblk * (nblk + 1) // 2 * 32 * 32 * 2
     return {"fwd": 3 * t + t + r, "delta": 2 * t + r, "dkdv": 4 * t + 2 * r + 2 * t + ds,
             "dq": t + ds + t}
+
+
+def method_bytes(B, T, H, D):
+    """HBM bytes per launch of the split-pass method itself (no dS workspace):
+    each pass reads its own operands once and writes its results once.
+    fwd: q, k, v -> o, lse.  delta: o, dO -> delta.  dkdv: q, k, v, dO, lse,
+    delta -> dk, dv.  dq: q, k, v, dO, lse, delta -> dq.  The step-level
+    minimum (every tensor of the layer moved once) is under "fwd_min" and
+    "bwd_min": q, k, v, o, dO, lse read and dq, dk, dv written."""
+    t = B * T * H * D * 2
+    r = B * H * T * 4
+    return {"fwd": 4 * t + r, "delta": 2 * t + r, "dkdv": 6 * t + 2 * r, "dq": 5 * t + 2 * r,
+            "fwd_min": 4 * t + r, "bwd_min": 8 * t + r}
 
 
 def visible_pairs(T, window):
@@ -159,26 +173,48 @@ def visible_pairs(T, window):
     return (w + 1) * (w + 2) // 2 - (w + 1) + (T - w) * (w + 1) if T > w else T * (T + 1) // 2
 
 
-def cpu_baseline(inp, n_heads):
-    """Time the fp64 oracle (as it stands) on the first n_heads (b, h) heads."""
+def cpu_baseline(inp, n_heads, dinp=None, n_seqs=0):
+    """Time the fp64 oracle (as it stands) on the first n_heads (b, h) heads of
+    the training workload, forward and backward separately, and on the first
+    n_seqs sequences of the decode workload."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
-        threads = max(i.get("num_threads", 1) for i in threadpool_info()) or 1
+        blas = max(i.get("num_threads", 1) for i in threadpool_info()
+                   if i.get("user_api") == "blas") or 1
     except Exception:  # pragma: no cover
-        threads = os.cpu_count()
+        blas = None
     B, T, H, D = inp.shape
     heads = [(b, h) for b in range(B) for h in range(H)][:n_heads]
     t0 = time.perf_counter()
     oracle.forward(inp.q, inp.k, inp.v, heads=heads)
+    t1 = time.perf_counter()
     oracle.backward(inp.q, inp.k, inp.v, inp.do, heads=heads)
-    dt = time.perf_counter() - t0
-    flops = 7 * len(heads) * T * T * D
-    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
-            "kind": "oracle",
-            "sample": (f"fp64 numpy oracle fwd+bwd on {len(heads)} of {B * H} (b,h) heads of the "
-                       f"d20 workload (T={T}), {dt:.1f} s wall, algorithmic FLOPs as the GPU"),
-            "seconds": round(dt, 3)}
+    t2 = time.perf_counter()
+    unit = len(heads) * T * T * D    # one causal matmul over the sampled heads
+    fwd_s, bwd_s = t1 - t0, t2 - t1
+    res = {"value": round(7 * unit / (t2 - t0) / 1e12, 6), "unit": "TFLOP/s",
+           "cores": int(blas or os.cpu_count()), "kind": "oracle",
+           "sample": (f"fp64 numpy oracle fwd then bwd on {len(heads)} of {B * H} (b,h) heads "
+                      f"of the d20 workload (T={T}), {t2 - t0:.1f} s wall, algorithmic FLOPs "
+                      "as the GPU (fwd 2, bwd 5 causal matmuls)"),
+           "seconds": round(t2 - t0, 3), "os_cpu_count": os.cpu_count(), "blas_threads": blas,
+           "fwd": {"seconds": round(fwd_s, 3), "TFLOP_per_s": round(2 * unit / fwd_s / 1e12, 6)},
+           "bwd": {"seconds": round(bwd_s, 3),
+                   "TFLOP_per_s": round(5 * unit / bwd_s / 1e12, 6)}}
+    if dinp is not None and n_seqs > 0:
+        sl = dinp.seqlens[:n_seqs]
+        Hd = dinp.q.shape[1]
+        t0 = time.perf_counter()
+        oracle.decode(dinp.q[:n_seqs], dinp.k_cache[:n_seqs], dinp.v_cache[:n_seqs], sl)
+        dt = time.perf_counter() - t0
+        nbytes = int(sl.astype(np.int64).sum()) * Hd * D * 2 * 2
+        res["decode"] = {"seconds": round(dt, 3), "sequences": int(n_seqs),
+                         "GB_per_s": round(nbytes / dt / 1e9, 3),
+                         "sample": f"fp64 oracle decode of {n_seqs} of {len(dinp.seqlens)} "
+                                   "sequences of the d20 decode workload, bytes counted as "
+                                   "the bf16 cache rows the GPU reads"}
+    return res
 
 
 def main():
@@ -199,6 +235,8 @@ def main():
                          "event between two kernels adds a few microseconds to the step)")
     ap.add_argument("--kv-heads", type=int, default=5,
                     help="key/value heads for the extra grouped-query measurement (0 = skip)")
+    ap.add_argument("--depths", default="d12,d26",
+                    help="other model depths whose fwd+bwd step is timed as well ('' = none)")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="first run a plain device copy of this many MiB (a known-size "
                          "kernel that calibrates HBM byte counters in a profiler run)")
@@ -318,7 +356,8 @@ def main():
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": recorded_traffic(dom),
                 "flops_per_launch": fl[dom],
-                "algorithmic_bytes_per_launch": train_bytes(B, T, H, D)[dom]}
+                "design_bytes_per_launch": design_bytes(B, T, H, D)[dom],
+                "method_bytes_per_launch": method_bytes(B, T, H, D)[dom]}
 
     result = {
         "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
@@ -411,6 +450,68 @@ def main():
                          "kernels": gk}
         log(f"gqa: {g_ms:.3f} ms  {g_tf:.1f} TFLOP/s  kernels {gk}")
         del kg, vg, dkg, dvg
+
+    # ---------------- the other depths of the model family (d12, d26)
+    depths = [d for d in args.depths.split(",") if d] if args.depths else []
+    if depths:
+        result["depths"] = {}
+    for dname in depths:
+        c = W.CONFIGS[dname]
+        dB, dT, dH, dD = c.B, c.T, c.H, c.D
+        log(f"{dname}: B={dB} T={dT} H={dH} D={dD}: warmup {args.warmup}, timing {args.steps}")
+        din = W.make_train_inputs(c)
+        xq, xk, xv, xdo = (dev_t(x) for x in (din.q_store, din.k_store, din.v_store,
+                                              din.do_store))
+        del din
+        xo, xdq, xdk, xdv = (torch.empty_like(xq) for _ in range(4))
+        xlse = torch.empty((dB, dH, dT), dtype=torch.float32, device=dev)
+        xdelta = torch.empty_like(xlse)
+        xwsb = na.bwd_workspace_bytes(dB, dT, dH)
+        xws = torch.empty(xwsb, dtype=torch.uint8, device=dev)
+
+        def xstep(i):
+            e = evs[i]
+            if instrumented(i):
+                ev.record(e[0], stream)
+            st = lib.na_attn_fwd(ptr(xq), ptr(xk), ptr(xv), ptr(xo), ptr(xlse), dB, dT, dH, dD,
+                                 P(stream))
+            if st:
+                raise RuntimeError(lib.na_last_error().decode())
+            st = lib.na_attn_bwd_timed(ptr(xq), ptr(xk), ptr(xv), ptr(xo), ptr(xdo), ptr(xlse),
+                                       ptr(xdq), ptr(xdk), ptr(xdv), ptr(xdelta), ptr(xws), xwsb,
+                                       dB, dT, dH, dD, P(stream),
+                                       ctypes.cast(ev_arr[i], P) if instrumented(i) else None)
+            if st:
+                raise RuntimeError(lib.na_last_error().decode())
+
+        for i in range(args.warmup):
+            xstep(i)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.warmup, n_total):
+            xstep(i)
+        torch.cuda.synchronize()
+        xwall = time.perf_counter() - t0
+        xfl = train_flops(dB, dT, dH, dD)
+        xk_ = {}
+        for j, n in enumerate(names):
+            avg = float(np.mean([ev.ms(evs[i][j], evs[i][j + 1]) for i in timed_ev]))
+            xk_[n] = {"avg_us": round(avg * 1e3, 2),
+                      "tflops": round(xfl[n] / (avg * 1e-3) / 1e12, 2) if xfl[n] else None}
+        bwd_us = sum(xk_[n]["avg_us"] for n in ("delta", "dkdv", "dq"))
+        x_ms = xwall * 1e3 / args.steps
+        x_tf = xfl["fwd+bwd"] / (x_ms * 1e-3) / 1e12
+        result["depths"][dname] = {
+            "workload": f"{dname} causal self-attention fwd+bwd", "B": dB, "T": dT, "H": dH,
+            "D": dD, "ms_per_step": round(x_ms, 4), "TFLOP_per_s": round(x_tf, 2),
+            "pct_bf16_peak": round(100 * x_tf / PEAK_BF16_TFLOPS, 2),
+            "fwd_us": xk_["fwd"]["avg_us"], "bwd_us": round(bwd_us, 2),
+            "fwd_TFLOP_per_s": xk_["fwd"]["tflops"],
+            "bwd_TFLOP_per_s": round(5 * xfl["dq"] / (bwd_us * 1e-6) / 1e12, 2),
+            "kernels": xk_}
+        log(f"{dname}: {x_ms:.3f} ms  {x_tf:.1f} TFLOP/s  kernels {xk_}")
+        del xq, xk, xv, xdo, xo, xdq, xdk, xdv, xlse, xdelta, xws
+        torch.cuda.empty_cache()
 
     # ---------------- prologue: QK norm + rotary embedding of q and k
     if not args.no_prologue:
@@ -543,10 +644,11 @@ def main():
     torch.cuda.empty_cache()
 
     # ---------------- decode
+    dinp_cpu = None
     if not args.no_decode:
         dcfg = W.CONFIGS[W.DECODE]
         log("generating decode inputs")
-        dinp = W.make_decode_inputs(dcfg)
+        dinp = dinp_cpu = W.make_decode_inputs(dcfg)
         Bd, Hd, Tc = dcfg.B, dcfg.H, dcfg.T_cap
         qd = dev_t(dinp.q_store)
         caches = []
@@ -761,7 +863,8 @@ def main():
     # ---------------- CPU baseline: the oracle on a bounded sample
     if args.cpu_heads > 0:
         log(f"cpu baseline on {args.cpu_heads} heads")
-        result["cpu_baseline"] = cpu_baseline(inp, args.cpu_heads)
+        result["cpu_baseline"] = cpu_baseline(inp, args.cpu_heads, dinp_cpu,
+                                              64 if dinp_cpu is not None else 0)
     else:
         result["cpu_baseline"] = None
 

@@ -106,7 +106,9 @@ size_t na_attn_bwd_workspace_bytes(int B, int T, int H, int D);
  * o = 0 and lse = -inf.  workspace: device scratch of at least
  * na_attn_decode_workspace_bytes(B, H, D, T_cap) bytes (NA_ERR_INVALID_ARG if
  * smaller).  H <= 32 (else NA_ERR_UNSUPPORTED), B <= 65535.  Enqueues two
- * kernels: split-KV partials, then their combine.
+ * kernels per batch of up to 4096 sequences: split-KV partials over equal
+ * ranges of the visible keys, then their combine (the batches reuse the
+ * workspace in stream order).
  */
 na_status na_attn_decode(const void* q, const void* k_cache, const void* v_cache,
                          const int* seqlens, void* o, float* lse, int B, int H, int D,
@@ -124,7 +126,7 @@ size_t na_attn_decode_workspace_bytes(int B, int H, int D, int T_cap);
  * holds in each device's memory until the process ends.  Sizes whose
  * na_attn_decode_workspace_bytes exceed 16 MiB are rejected with
  * NA_ERR_INVALID_ARG before anything is enqueued (the d20 decode shape, B = 64,
- * H = 10, T_cap = 2048, needs 10.6 MB).  Allocates nothing: the first call on
+ * H = 10, T_cap = 2048, needs 11.0 MB).  Allocates nothing: the first call on
  * a device looks up the scratch's device address (hipGetSymbolAddress) and
  * caches it.  All calls on one device share the scratch: calls that may
  * overlap on one device (different streams without ordering) race and must

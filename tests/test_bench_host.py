@@ -25,12 +25,18 @@ def test_flop_and_byte_counts_at_d20():
     assert unit == 171798691840                      # causal: half of 2 T^2 D per head
     assert fl["fwd"] == 2 * unit and fl["dkdv"] == 4 * unit and fl["dq"] == unit
     assert fl["fwd+bwd"] == 7 * unit
-    by = bench.train_bytes(B, T, H, D)
+    by = bench.design_bytes(B, T, H, D)
     t = B * T * H * D * 2
-    assert by["fwd"] == 4 * t + B * H * T * 4       # q, k, v read, o written, lse written
-    assert by["delta"] == 2 * t + B * H * T * 4
+    r = B * H * T * 4
+    assert by["fwd"] == 4 * t + r                   # q, k, v read, o written, lse written
+    assert by["delta"] == 2 * t + r
     nblk = T // 32
     assert by["dq"] == 2 * t + B * H * nblk * (nblk + 1) // 2 * 2048
+    mb = bench.method_bytes(B, T, H, D)
+    assert mb["dkdv"] == 6 * t + 2 * r              # q, k, v, dO, lse, delta in; dk, dv out
+    assert mb["dq"] == 5 * t + 2 * r                # q, k, v, dO, lse, delta in; dq out
+    # the step minimum quoted for d20: 674 MB forward, 1345 MB backward
+    assert mb["fwd_min"] == 673710080 and mb["bwd_min"] == 1344798720
 
 
 @pytest.mark.parametrize("T,W,expect", [(4, None, 10), (4, 0, 4), (4, 1, 7), (4, 10, 10),

@@ -77,12 +77,12 @@ def test_decode_matches_last_forward_row(dev):
     assert_close("lse", to_host(ld[0]), to_host(lse[0, :, L - 1]), 1e-5, 1e-4)
 
 
-def test_decode_many_sequences_raw_slot_order(dev):
-    """More than 8192 sequences: the split kernel walks the raw (sequence,
-    chunk) grid instead of the flattened list of non-empty chunks."""
+def test_decode_many_sequences_in_launch_batches(dev):
+    """More than 4096 sequences: the library runs them as consecutive batches
+    of split + combine launches that reuse one workspace."""
     B = 8200
     rng = np.random.default_rng(14)
-    lens = rng.integers(0, 70, size=B)  # includes empty sequences and chunk edges
+    lens = rng.integers(0, 70, size=B)  # includes empty sequences and range edges
     inp = W.make_decode_inputs(B=B, T_cap=70, H=1, seed=14, seqlens=lens)
     o, lse = run_decode(inp, dev)
     check(inp, o, lse)
@@ -107,7 +107,7 @@ def test_decode_reuses_workspace(dev):
 @pytest.mark.parametrize("H,B", [(1, 100), (2, 70), (3, 60)])
 def test_decode_few_heads_many_sequences(dev, H, B):
     """Workgroups of 16 H threads (fewer than a wavefront) with more sequences
-    than threads: the prefix sum over the sequences' chunk counts runs in
+    than threads: the prefix sum over the sequences' visible key counts runs in
     blocks of 16 or 32 lanes."""
     rng = np.random.default_rng(15 + H)
     lens = rng.integers(0, 300, size=B)
@@ -198,10 +198,10 @@ def test_decode_append(dev, B, H, Hk, T_cap, Wn, rope, gate):
     assert np.array_equal(gk[keep], kc0[keep]) and np.array_equal(gv[keep], vc0[keep])
 
 
-def test_decode_append_many_sequences_raw_slot_order(dev):
-    """The appending decode with more than 8192 sequences (the split kernel's
-    raw slot order) and short caches: every sequence, including ones whose
-    cache was empty, sees exactly the rows before the new one plus it."""
+def test_decode_append_many_sequences_in_launch_batches(dev):
+    """The appending decode with more than 4096 sequences (several batches of
+    split + combine launches) and short caches: every sequence, including ones
+    whose cache was empty, sees exactly the rows before the new one plus it."""
     import torch
     import causal_self_attention_mha_amd as na
     B, H, T_cap = 8200, 1, 40

@@ -37,7 +37,7 @@ def test_noalloc_decode_matches_workspace_decode(dev):
     import torch
 
     import causal_self_attention_mha_amd as na
-    big = W.make_decode_inputs("decode_d20")  # B = 64, H = 10, T_cap = 2048: 10.6 MB of scratch
+    big = W.make_decode_inputs("decode_d20")  # B = 64, H = 10, T_cap = 2048: 11.0 MB of scratch
     small = W.make_decode_inputs(B=8, T_cap=700, H=4, seed=71)
     for dinp in (big, small):
         o, lse, o_ref, lse_ref = _decode_both(na, dinp, dev)
