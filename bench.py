@@ -108,6 +108,8 @@ KERNEL_SOURCES = {  # the sources whose text determines each kernel's code
     "qk_norm_rope_bwd": ["prologue_bf16.hip", "device_common.hpp", "internal.hpp"],
     "value_gate_fwd": ["prologue_bf16.hip", "device_common.hpp", "internal.hpp"],
     "value_gate_bwd": ["prologue_bf16.hip", "device_common.hpp", "internal.hpp"],
+    "decode_split": ["decode_bf16.hip", "device_common.hpp", "internal.hpp"],
+    "decode_combine": ["decode_bf16.hip", "device_common.hpp", "internal.hpp"],
 }
 
 
@@ -217,6 +219,50 @@ def cpu_baseline(inp, n_heads, dinp=None, n_seqs=0):
     return res
 
 
+def sample_sclk(run_load, seconds, period=0.002):
+    """Sample the current shader clock (the starred line of the amdgpu driver's
+    pp_dpm_sclk file) while run_load(stop_event) keeps the GPU busy."""
+    import glob
+    import re
+    import threading
+    paths = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+    if not paths:
+        return {"source": None, "note": "no pp_dpm_sclk file readable"}
+    samples = {p: [] for p in paths}
+    stop = threading.Event()
+
+    def sampler():
+        while not stop.is_set():
+            for p in paths:
+                try:
+                    with open(p) as fh:
+                        for line in fh:
+                            if line.rstrip().endswith("*"):
+                                m = re.search(r"(\d+)\s*[Mm][Hh]z", line)
+                                if m:
+                                    samples[p].append(int(m.group(1)))
+                except OSError:
+                    pass
+            time.sleep(period)
+
+    th = threading.Thread(target=sampler, daemon=True)
+    th.start()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        run_load()
+    stop.set()
+    th.join()
+    # the busiest card is the one under load (other cards idle at a low clock)
+    p = max(paths, key=lambda q: (np.median(samples[q]) if samples[q] else -1))
+    v = np.array(samples[p], dtype=np.float64)
+    if v.size == 0:
+        return {"source": p, "note": "no samples"}
+    return {"source": p, "samples": int(v.size), "seconds": seconds,
+            "median_MHz": float(np.median(v)), "mean_MHz": round(float(v.mean()), 1),
+            "min_MHz": float(v.min()), "max_MHz": float(v.max()),
+            "p10_MHz": float(np.percentile(v, 10)), "p90_MHz": float(np.percentile(v, 90))}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -235,6 +281,9 @@ def main():
                          "event between two kernels adds a few microseconds to the step)")
     ap.add_argument("--kv-heads", type=int, default=5,
                     help="key/value heads for the extra grouped-query measurement (0 = skip)")
+    ap.add_argument("--sclk-seconds", type=float, default=1.5,
+                    help="seconds of back-to-back d20 steps during which the shader clock "
+                         "is sampled from sysfs (0 = skip)")
     ap.add_argument("--depths", default="d12,d26",
                     help="other model depths whose fwd+bwd step is timed as well ('' = none)")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
@@ -373,6 +422,16 @@ def main():
         "kernels": kern,
         "roofline": roofline,
     }
+
+    # ---------------- shader clock under the d20 step load
+    if args.sclk_seconds > 0:
+        def load():
+            for i in range(args.warmup, args.warmup + 8):
+                step(i)
+            torch.cuda.synchronize()
+        log(f"sampling the shader clock for {args.sclk_seconds} s of d20 steps")
+        result["sclk_under_load"] = sample_sclk(load, args.sclk_seconds)
+        log(f"sclk {result['sclk_under_load']}")
 
     # ---------------- the same step with a sliding window
     wlen = args.window if 0 <= args.window < T - 1 else None
