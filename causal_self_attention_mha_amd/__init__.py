@@ -64,7 +64,9 @@ class NAError(RuntimeError):
 
 
 def library_path() -> str:
-    return os.path.join(_HERE, "lib", "libna_attn.so")
+    """The in-tree libna_attn.so, or the build named by NA_ATTN_LIBRARY (the
+    C-ABI tests use it to load the host-sanitized twin)."""
+    return os.environ.get("NA_ATTN_LIBRARY") or os.path.join(_HERE, "lib", "libna_attn.so")
 
 
 def load_library():

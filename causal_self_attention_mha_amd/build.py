@@ -69,5 +69,42 @@ def build(verbose: bool = False, extra: list[str] | None = None) -> str:
     return LIB
 
 
+SAN_DIR = os.path.join(BUILD, "asan")
+SAN_LIB = os.path.join(SAN_DIR, "libna_attn_asan.so")
+
+
+def build_sanitized(verbose: bool = False) -> str:
+    """A host-sanitized twin of the library for the C-ABI tests: api.cpp (the
+    host-side argument checks and launch code) compiled by the host compiler
+    with AddressSanitizer and UndefinedBehaviorSanitizer, linked with the
+    regular device objects of the last build().  Loading it needs the
+    sanitizer runtimes preloaded (LD_PRELOAD); it runs the host checks only,
+    never on a GPU."""
+    gxx = shutil.which("g++")
+    if gxx is None:
+        raise RuntimeError("g++ not found")
+    os.makedirs(SAN_DIR, exist_ok=True)
+    obj = os.path.join(SAN_DIR, "api.o")
+    san = ["-fsanitize=address,undefined", "-fno-omit-frame-pointer", "-fno-sanitize-recover=all"]
+    cmd = [gxx, "-std=c++17", "-O1", "-g", "-fPIC", "-D__HIP_PLATFORM_AMD__",
+           "-I", "/opt/rocm/include", "-I", os.path.join(ROOT, "include"), *san, "-c",
+           os.path.join(CSRC, "api.cpp"), "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"compile failed\n{' '.join(cmd)}\n{r.stderr}")
+    dev_objs = [os.path.join(BUILD, s + ".o") for s in SOURCES if s != "api.cpp"]
+    missing = [o for o in dev_objs if not os.path.exists(o)]
+    if missing:
+        raise RuntimeError(f"device objects missing (run build() first): {missing}")
+    cmd = [gxx, "-shared", *san, obj, *dev_objs, "-L", "/opt/rocm/lib",
+           "-Wl,-rpath,/opt/rocm/lib", "-lamdhip64", "-o", SAN_LIB]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed\n{' '.join(cmd)}\n{r.stderr}")
+    if verbose:
+        print(f"built {SAN_LIB}")
+    return SAN_LIB
+
+
 if __name__ == "__main__":
     build(verbose=True)

@@ -67,6 +67,11 @@ __device__ __forceinline__ float sum16(float x) {
 // Sixteen-byte global/LDS load and store through a 4 x dword vector.
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 __device__ __forceinline__ void st16(void* p, uint4 v) { *reinterpret_cast<uint4*>(p) = v; }
+// st16 for data not read again soon: a non-temporal store
+__device__ __forceinline__ void st16_nt(void* p, uint4 v) {
+  typedef unsigned v4u __attribute__((ext_vector_type(4)));
+  __builtin_nontemporal_store(v4u{v.x, v.y, v.z, v.w}, reinterpret_cast<v4u*>(p));
+}
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 
@@ -122,6 +127,13 @@ __device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t voff, uint32_t lds) {
                : "v"(voff), "s"(uniform_rsrc(rsrc)), "s"(__builtin_amdgcn_readfirstlane(lds))
                : "memory");
 }
+// dma16 for data read once: the non-temporal policy streams it past the caches.
+__device__ __forceinline__ void dma16_nt(i32x4 rsrc, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen nt lds"
+               :
+               : "v"(voff), "s"(uniform_rsrc(rsrc)), "s"(__builtin_amdgcn_readfirstlane(lds))
+               : "memory");
+}
 __device__ __forceinline__ void dma4(i32x4 rsrc, uint32_t voff, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds"
                :
@@ -132,6 +144,13 @@ __device__ __forceinline__ void dma4(i32x4 rsrc, uint32_t voff, uint32_t lds) {
 // Waits until every vector memory operation of this wavefront has completed
 // (DMA copies landed in LDS, global stores acknowledged).
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Waits until every LDS read of this wavefront has returned its data.  Placed
+// before each barrier after which a DMA copy may overwrite an LDS buffer that
+// was read before it: the copies are asm the compiler does not see as LDS
+// writes, so the read's completion is made explicit rather than left to the
+// barrier's lowering; the "memory" clobber also keeps the compiler from
+// moving any LDS access across it.
+__device__ __forceinline__ void wait_lds() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 // ... all but the N most recently issued ones (they complete in issue order).
 template <int N>
 __device__ __forceinline__ void wait_vmem_but() {

@@ -185,6 +185,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(
     // and every wavefront is done with the other buffer (tile kt-1), which the
     // next copy may then overwrite.
     wait_vmem();
+    wait_lds();
     __syncthreads();
     // whole tile above this wavefront's diagonal, or before its rows' windows
     const bool skip = k0 > L + qw0 + 31 || (WIN && k0 + BK - 1 < L + qw0 - win);
