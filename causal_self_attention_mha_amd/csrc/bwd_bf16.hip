@@ -30,6 +30,17 @@
 #include "device_common.hpp"
 #include "internal.hpp"
 
+// o and dout are read once by the delta kernel and dk, dv written once by
+// the dK/dV pass: non-temporal policy for both (bit 1: delta's loads,
+// 66.9 -> 55.5 us at d20; bit 4: the dK/dV stores, which leaves the caches
+// to the dQ GEMM's K and dS: dq 341.6 -> 332.3 us).  Bit 8 (the dK/dV
+// pass's copies of an item's K and V rows, also read once) measured no gain
+// (dq 331 -> 335 us) and is off.  The forward's O stores (8 bytes per lane)
+// became much slower with it (410 -> 582 us) and keep the default policy.
+#ifndef NA_NT_EXTRA
+#define NA_NT_EXTRA 5
+#endif
+
 namespace na {
 namespace {
 
@@ -54,8 +65,13 @@ __global__ __launch_bounds__(256) void delta_kernel(const u16* __restrict__ o,
   const int h = static_cast<int>(bh % H);
   const int b = static_cast<int>(bh / H);
   const size_t off = ((static_cast<size_t>(b) * T + t) * H + h) * D + 8 * chunk;
+#if NA_NT_EXTRA & 1
+  const uint4 a = ld16_nt(o + off);
+  const uint4 g = ld16_nt(dout + off);
+#else
   const uint4 a = ld16(o + off);
   const uint4 g = ld16(dout + off);
+#endif
   float acc = 0.f;
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
@@ -478,9 +494,10 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(
     const uint32_t n0 = static_cast<uint32_t>(min(nk, 64)) * rsbk;
     const uint32_t n1 = static_cast<uint32_t>(max(nk - 64, 0)) * rsbk;
     const size_t off0 = it.kbase + static_cast<size_t>(it.k0) * rsk;
-    copy_tile(buffer_rsrc(src + off0, n0), koff, rsbk, dst, wave);
-    copy_tile(buffer_rsrc(src + off0 + static_cast<size_t>(64) * rsk, n1), koff, rsbk,
-              dst + TILE_B, wave);
+    copy_tile<4, (NA_NT_EXTRA & 8) != 0>(buffer_rsrc(src + off0, n0), koff, rsbk, dst, wave);
+    copy_tile<4, (NA_NT_EXTRA & 8) != 0>(
+        buffer_rsrc(src + off0 + static_cast<size_t>(64) * rsk, n1), koff, rsbk, dst + TILE_B,
+        wave);
   };
   // Every copy issued so far has landed and every wavefront is past its
   // reads of the buffer that the next copy overwrites.
@@ -745,7 +762,11 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(
               x = rope_bwd_chunk(x, rw, ra.eps, c);
             }
           }
+#if NA_NT_EXTRA & 4
+          if (key < T) st16_nt(dst + kbase + key * rsk + 8 * c, x);
+#else
           if (key < T) st16(dst + kbase + key * rsk + 8 * c, x);
+#endif
         }
       }
     }

@@ -66,6 +66,12 @@ __device__ __forceinline__ float sum16(float x) {
 
 // Sixteen-byte global/LDS load and store through a 4 x dword vector.
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+// ld16 for data read once: a non-temporal load
+__device__ __forceinline__ uint4 ld16_nt(const void* p) {
+  typedef unsigned v4u __attribute__((ext_vector_type(4)));
+  const v4u v = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
 __device__ __forceinline__ void st16(void* p, uint4 v) { *reinterpret_cast<uint4*>(p) = v; }
 // st16 for data not read again soon: a non-temporal store
 __device__ __forceinline__ void st16_nt(void* p, uint4 v) {
@@ -273,13 +279,18 @@ __device__ __forceinline__ uint32_t tile_copy_offset(int wave, int lane, uint32_
 // Copies this wavefront's share of a 64 x 128 tile: rows of the buffer
 // resource (rows past its end arrive as zeros) into the tile at LDS address
 // tile.  NW (4 or 8) wavefronts share the copy.
-template <int NW = 4>
+// NT: the rows are read once (non-temporal copies).
+template <int NW = 4, bool NT = false>
 __device__ __forceinline__ void copy_tile(i32x4 rsrc, uint32_t voff, uint32_t rsb, uint32_t tile,
                                           int wave) {
   static_assert(NW == 4 || NW == 8, "16 row groups split evenly");
 #pragma unroll
-  for (int m = 0; m < 16 / NW; ++m)
-    dma16(rsrc, voff + 4 * NW * m * rsb, tile + 1024 * (wave + NW * m));
+  for (int m = 0; m < 16 / NW; ++m) {
+    if constexpr (NT)
+      dma16_nt(rsrc, voff + 4 * NW * m * rsb, tile + 1024 * (wave + NW * m));
+    else
+      dma16(rsrc, voff + 4 * NW * m * rsb, tile + 1024 * (wave + NW * m));
+  }
 }
 
 // Workgroup order.  The hardware hands workgroup i to XCD i % 8, and each XCD
