@@ -1104,6 +1104,31 @@ __global__ __launch_bounds__(64 * DG_WAVES, 8 / DG_WAVES) void dq_gemm_kernel(co
 #pragma unroll
     for (int i = 0; i < 4; ++i) dqa[i] = f32x16{};
 
+    // ROPE: the raw row and its angles, loaded at the start of the item so
+    // that their latency hides behind the key loop.  The lane holds elements
+    // d = 32 db + 8 g + 4 half + j of its row (the other half in lane l ^ 32);
+    // d < 64 (db < 2) pairs with d + 64 (db + 2).
+    uint2 xw[ROPE ? 4 : 1][4];
+    float4 c4[ROPE ? 2 : 1][4], s4[ROPE ? 2 : 1][4];
+    if constexpr (ROPE) {
+      const int pr = min(qw0 + l32, T - 1);
+      const u16* xp = ra.raw + base + static_cast<size_t>(pr) * rs + 4 * half;
+      const float* cp = ra.cos_t + static_cast<size_t>(pr) * (D / 2) + 4 * half;
+      const float* sp = ra.sin_t + static_cast<size_t>(pr) * (D / 2) + 4 * half;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          xw[db][g] = *reinterpret_cast<const uint2*>(xp + 32 * db + 8 * g);
+#pragma unroll
+      for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          c4[db][g] = *reinterpret_cast<const float4*>(cp + 32 * db + 8 * g);
+          s4[db][g] = *reinterpret_cast<const float4*>(sp + 32 * db + 8 * g);
+        }
+    }
+
     const int last_q = min(q0 + DG_ROWS, T) - 1;
     const int n_kt = last_q / DG_KEYS + 1;
     // first key tile that any row of the workgroup sees (0 without a window)
@@ -1221,28 +1246,6 @@ __global__ __launch_bounds__(64 * DG_WAVES, 8 / DG_WAVES) void dq_gemm_kernel(co
 #pragma unroll
       for (int e = 0; e < 16; ++e) dqa[db][e] *= scale;
     if constexpr (ROPE) {
-      // the lane holds elements d = 32 db + 8 g + 4 half + j of its row (the
-      // other half in lane l ^ 32); d < 64 (db < 2) pairs with d + 64 (db + 2)
-      const int pr = min(qrow, T - 1);
-      const u16* xp = ra.raw + base + static_cast<size_t>(pr) * rs + 4 * half;
-      const float* cp = ra.cos_t + static_cast<size_t>(pr) * (D / 2) + 4 * half;
-      const float* sp = ra.sin_t + static_cast<size_t>(pr) * (D / 2) + 4 * half;
-      // every load first (one round of latency), then the arithmetic
-      uint2 xw[4][4];
-      float4 c4[2][4], s4[2][4];
-#pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int g = 0; g < 4; ++g)
-          xw[db][g] = *reinterpret_cast<const uint2*>(xp + 32 * db + 8 * g);
-#pragma unroll
-      for (int db = 0; db < 2; ++db)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          c4[db][g] = *reinterpret_cast<const float4*>(cp + 32 * db + 8 * g);
-          s4[db][g] = *reinterpret_cast<const float4*>(sp + 32 * db + 8 * g);
-        }
-      __builtin_amdgcn_sched_barrier(0);
       float x[4][16];
       float ss = 0.f;
 #pragma unroll
