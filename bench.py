@@ -42,6 +42,11 @@ Grouped-query attention (--kv-heads, default 5: two query heads per key/value
 head, a choice of this benchmark; the pages give no key/value head count) is
 timed the same way on the d20 step and the decode and reported under "gqa".
 
+The same K-step loop then runs --trials more times (default 5); their
+per-step times, median and spread are reported under "trials" (the headline
+value stays the first timed run), and each kernel's event times carry their
+median and range beside the mean.
+
 The fp64 oracle runs once on a bounded sample of the same workload on the
 host cores and is reported as "cpu_baseline" (a reported baseline, not the
 target).
@@ -281,6 +286,9 @@ def main():
                          "event between two kernels adds a few microseconds to the step)")
     ap.add_argument("--kv-heads", type=int, default=5,
                     help="key/value heads for the extra grouped-query measurement (0 = skip)")
+    ap.add_argument("--trials", type=int, default=5,
+                    help="further runs of the same K timed steps, reported as their spread "
+                         "and median (the headline value is the first run)")
     ap.add_argument("--sclk-seconds", type=float, default=1.5,
                     help="seconds of back-to-back d20 steps during which the shader clock "
                          "is sampled from sysfs (0 = skip)")
@@ -394,6 +402,8 @@ def main():
     for n in names:
         avg = float(np.mean(per[n]))
         kern[n] = {"avg_us": round(avg * 1e3, 2), "min_us": round(min(per[n]) * 1e3, 2),
+                   "median_us": round(float(np.median(per[n])) * 1e3, 2),
+                   "max_us": round(max(per[n]) * 1e3, 2),
                    "tflops": round(fl[n] / (avg * 1e-3) / 1e12, 2) if fl[n] else None}
     log(f"step {ms_per_step:.3f} ms  {tflops:.1f} TFLOP/s  kernels {kern}")
 
@@ -422,6 +432,25 @@ def main():
         "kernels": kern,
         "roofline": roofline,
     }
+
+    # ---------------- repeated trials of the same K-step loop (spread, median)
+    if args.trials > 0:
+        tr_ms = []
+        for _ in range(args.trials):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for i in range(args.warmup, n_total):
+                step(i)
+            torch.cuda.synchronize()
+            tr_ms.append((time.perf_counter() - t0) * 1e3 / args.steps)
+        result["trials"] = {
+            "count": args.trials, "steps_each": args.steps,
+            "ms_per_step": [round(x, 4) for x in tr_ms],
+            "median_ms_per_step": round(float(np.median(tr_ms)), 4),
+            "min_ms_per_step": round(min(tr_ms), 4), "max_ms_per_step": round(max(tr_ms), 4),
+            "median_TFLOP_per_s": round(fl["fwd+bwd"] / (float(np.median(tr_ms)) * 1e-3) / 1e12,
+                                        2)}
+        log(f"trials {result['trials']}")
 
     # ---------------- shader clock under the d20 step load
     if args.sclk_seconds > 0:

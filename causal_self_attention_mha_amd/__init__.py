@@ -249,8 +249,8 @@ def attn_bwd(q, k, v, o, dout, lse, dq=None, dk=None, dv=None, delta=None, works
 
     bf16: by default a dS workspace is allocated (or `workspace` is used) so
     that dq is a GEMM over the stored dS; recompute_dq=True passes no
-    workspace and the dq pass recomputes S and dP (plain causal only: a
-    window needs the workspace).  fp32 has one path.
+    workspace and the dq pass recomputes S and dP (with or without a
+    window).  fp32 has one path.
     rope=(q_raw, k_raw, cos, sin): q and k are the outputs of
     qk_norm_rope_fwd(q_raw, k_raw, cos, sin); dq and dk are returned as the
     gradients of q_raw and k_raw, the prologue's backward done in the same

@@ -196,9 +196,6 @@ na_status na_attn_bwd_gqa(const void* q, const void* k, const void* v, const voi
   na_status st = check_sizes(B, T, H, D);
   if (st) return st;
   if ((st = check_kv_heads(H, H_kv))) return st;
-  if (workspace == nullptr && window >= 0 && window < T - 1)
-    return fail(NA_ERR_UNSUPPORTED, "a sliding window (window=%d) needs the dS workspace",
-                window);
   if (workspace != nullptr) {
     st = check_ptrs({{q, "q"}, {k, "k"}, {v, "v"}, {o, "o"}, {dout, "dout"}, {lse, "lse"}},
                     {{dq, "dq"}, {dk, "dk"}, {dv, "dv"}, {delta, "delta"},

@@ -816,14 +816,18 @@ __device__ __forceinline__ void dq_scores(const u16* Ks, const u16* Vs, int row0
   }
 }
 
-template <bool MASK>
+// MASK: keys after the query are dropped; BAND: so are keys more than win
+// before it (sliding window).
+template <bool MASK, bool BAND = false>
 __device__ __forceinline__ void dq_probs(const f32x16& sacc, const f32x16& pacc, bf16x8 (&sb)[2],
                                          int lane, int qrow_minus_k0, int row0, float lse2,
-                                         float dl, float c_log2) {
+                                         float dl, float c_log2, int win = 0) {
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     float p = fast_exp2(fmaf(sacc[r], c_log2, -lse2));
-    if (MASK && row0 + acc_row(lane, r) > qrow_minus_k0) p = 0.f;  // key after query
+    const int d = qrow_minus_k0 - (row0 + acc_row(lane, r));  // query - key
+    if (MASK && d < 0) p = 0.f;                               // key after query
+    if (BAND && d > win) p = 0.f;                             // key before the window
     sb[r >> 3][r & 7] = to_bf16(p * (pacc[r] - dl));
   }
 }
@@ -843,15 +847,15 @@ __device__ __forceinline__ void dq_accum(const bf16x8 (&sb)[2], const u16* Kt, i
   }
 }
 
-template <bool MASK>
+template <bool MASK, bool BAND = false>
 __device__ __forceinline__ void dq_block(const u16* Ks, const u16* Vs, const u16* Kt,
                                          const bf16x8 (&qreg)[8], const bf16x8 (&greg)[8],
                                          f32x16 (&dqa)[4], int kb, int lane, int qrow_minus_k0,
-                                         float lse2, float dl, float c_log2) {
+                                         float lse2, float dl, float c_log2, int win = 0) {
   f32x16 sacc, pacc;
   dq_scores(Ks, Vs, 32 * kb, qreg, greg, sacc, pacc, lane);
   bf16x8 sb[2];
-  dq_probs<MASK>(sacc, pacc, sb, lane, qrow_minus_k0, 32 * kb, lse2, dl, c_log2);
+  dq_probs<MASK, BAND>(sacc, pacc, sb, lane, qrow_minus_k0, 32 * kb, lse2, dl, c_log2, win);
   dq_accum(sb, Kt, 32 * kb, dqa, lane);
 }
 
@@ -882,10 +886,16 @@ __device__ __forceinline__ void dq_step(const u16* KsN, const u16* VsN, int rowN
   }
 }
 
+// WIN: sliding window (key j visible to query i iff i - win <= j <= i).  The
+// windowed pass skips the pipelined steady part and runs every key tile from
+// the first one any row of the workgroup sees through the per-tile loop, each
+// block with the causal and band selects (this is the path for callers
+// without a dS workspace; the GEMM over stored dS is the fast one).
+template <bool WIN>
 __global__ __launch_bounds__(256, 1) void dq_kernel(
     const u16* __restrict__ q, const u16* __restrict__ k, const u16* __restrict__ v,
     const u16* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
-    u16* __restrict__ dq, int B, int T, int H, int Hk, float c_log2, float scale) {
+    u16* __restrict__ dq, int B, int T, int H, int Hk, float c_log2, float scale, int win) {
   __shared__ __attribute__((aligned(16))) u16 Ks[2][DQ_KEYS * RS];
   __shared__ __attribute__((aligned(16))) u16 Vs[2][DQ_KEYS * RS];
   __shared__ __attribute__((aligned(16))) u16 Kt[2][D * DQ_KEYS];  // transposed, swizzled
@@ -959,8 +969,8 @@ __global__ __launch_bounds__(256, 1) void dq_kernel(
   // (no mask, no skipped block), software-pipelined over 32-key blocks as in
   // the dK/dV kernel.  The last step computes scores of one block past the
   // steady range; they are never used.
-  const int ns = q0 / DQ_KEYS;
-  if (ns > 0) {
+  const int ns = WIN ? max(q0 - win, 0) / DQ_KEYS : q0 / DQ_KEYS;
+  if (!WIN && ns > 0) {
     int b = 0;
     gload(0);
     lstore(b);
@@ -994,7 +1004,18 @@ __global__ __launch_bounds__(256, 1) void dq_kernel(
 
     if (k0 > qw0 + 31) continue;  // whole tile after this wavefront's queries
     const int qk = qrow - k0;
-    if (k0 + DQ_KEYS - 1 > qw0) {  // tile crosses the diagonal
+    if constexpr (WIN) {
+      // blocks holding a visible pair of some row of this wavefront, both
+      // selects applied
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const int kk = k0 + 32 * kb;
+        if (kk <= qw0 + 31 && kk + 31 >= qw0 - win)
+          dq_block<true, true>(Ks[buf], Vs[buf], Kt[buf], qreg, greg, dqa, kb, lane, qk, lse2,
+                               dl, c_log2, win);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else if (k0 + DQ_KEYS - 1 > qw0) {  // tile crosses the diagonal
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         if (k0 + 32 * kb <= qw0 + 31)
@@ -1357,11 +1378,10 @@ hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const vo
                dim3(64 * DG_WAVES), 0, s, k16, static_cast<const u16*>(dsw),
                static_cast<u16*>(dq), nbt, B, T, H, Hk, scale, w, rq);
   } else {
-    if (win) return hipErrorInvalidValue;  // the recompute pass has no window (checked on the host)
     const int n_qt = (T + DQ_ROWS - 1) / DQ_ROWS;
-    e = launch(dq_kernel, dim3(static_cast<unsigned>(n_qt) * B * H), dim3(256), 0, s, q16, k16,
-               v16, g16, lse, static_cast<const float*>(delta), static_cast<u16*>(dq), B, T, H,
-               Hk, c_log2, scale);
+    e = launch(win ? dq_kernel<true> : dq_kernel<false>, dim3(static_cast<unsigned>(n_qt) * B * H),
+               dim3(256), 0, s, q16, k16, v16, g16, lse, static_cast<const float*>(delta),
+               static_cast<u16*>(dq), B, T, H, Hk, c_log2, scale, w);
   }
   if (e != hipSuccess) return e;
   return mark(ev, 3, s);

@@ -175,8 +175,9 @@ na_status na_attn_decode_timed(const void* q, const void* k_cache, const void* v
  * keys before it).  Decode: the query sits at row L - 1 of a sequence of
  * length L and sees keys max(0, L - 1 - window) .. L - 1.  window < 0, or a
  * window that reaches key 0 from every row (window >= T - 1, resp.
- * T_cap - 1), is exactly the plain entry point.  The windowed backward needs
- * the dS workspace (NA_ERR_UNSUPPORTED with workspace == NULL).  Arguments,
+ * T_cap - 1), is exactly the plain entry point.  The windowed backward runs
+ * with or without the dS workspace, as the plain one (without it the dq pass
+ * recomputes S and dP over the band).  Arguments,
  * layouts and errors otherwise as for the plain calls; `events` as for the
  * _timed entry points (NULL allowed).
  */

@@ -119,10 +119,12 @@ def test_window_entry_points_check_their_arguments(lib):
                                   None) == UNSUPPORTED
     p = [A + 0x100 * i for i in range(11)]
     need = lib.na_attn_bwd_workspace_bytes(1, 8, 1, 128)
-    # a real window needs the dS workspace ...
-    assert lib.na_attn_bwd_window(*p[:10], None, 0, 1, 8, 1, 128, 3, None, None) == UNSUPPORTED
-    assert b"workspace" in lib.na_last_error()
-    # ... and the usual checks still apply with one
+    # without a workspace (the recompute path) the usual checks apply ...
+    bad = list(p)
+    bad[9] = bad[0]                # delta == q
+    assert lib.na_attn_bwd_window(*bad[:10], None, 0, 1, 8, 1, 128, 3, None, None) == INVALID
+    assert lib.na_attn_bwd_window(*p[:10], None, 0, 1, 8, 1, 96, 3, None, None) == UNSUPPORTED
+    # ... and with one
     bad = list(p)
     bad[7] = bad[6]
     assert lib.na_attn_bwd_window(*bad[:10], bad[10], need, 1, 8, 1, 128, 3, None,

@@ -21,13 +21,13 @@ def _na():
     return na
 
 
-def gpu_fwd_bwd(inp, dev, window):
+def gpu_fwd_bwd(inp, dev, window, recompute_dq=False):
     import torch
     na = _na()
     q, k, v, do = (to_device(x, dev) for x in (inp.q_store, inp.k_store, inp.v_store,
                                                inp.do_store))
     o, lse = na.attn_fwd(q, k, v, window=window)
-    dq, dk, dv, delta = na.attn_bwd(q, k, v, o, do, lse, window=window)
+    dq, dk, dv, delta = na.attn_bwd(q, k, v, o, do, lse, window=window, recompute_dq=recompute_dq)
     torch.cuda.synchronize()
     return dict(q=q, k=k, v=v, do=do, o=o, lse=lse, dq=dq, dk=dk, dv=dv, delta=delta)
 
@@ -46,6 +46,45 @@ def test_window_bf16_shapes(dev, B, T, H, Wn):
     for name, ref in (("o", o), ("lse", lse), ("dq", dq), ("dk", dk), ("dv", dv),
                       ("delta", delta)):
         assert_close(f"W={Wn} {name}", to_host(res[name]), ref, BF16_REL_L2, BF16_MAX_ABS)
+
+
+@pytest.mark.parametrize("B,T,H,Wn", [(1, 100, 2, 0), (1, 333, 2, 31), (2, 257, 1, 32),
+                                      (1, 300, 1, 64), (1, 700, 2, 100), (2, 500, 1, 128),
+                                      (1, 2048, 1, 1024), (1, 333, 2, 331)])
+def test_window_recompute_dq(dev, B, T, H, Wn):
+    """The windowed backward without a dS workspace: the dq pass recomputes S
+    and dP over the band (both selects in every block); dk, dv, delta are the
+    same pass as with the workspace."""
+    import torch
+    inp = W.make_train_inputs("d20", B=B, T=T, H=H, seed=4500 + 7 * T + H + Wn)
+    res = gpu_fwd_bwd(inp, dev, Wn, recompute_dq=True)
+    dq, dk, dv, delta = oracle.backward(inp.q, inp.k, inp.v, inp.do, window=Wn)
+    for name, ref in (("dq", dq), ("dk", dk), ("dv", dv), ("delta", delta)):
+        assert_close(f"W={Wn} {name}", to_host(res[name]), ref, BF16_REL_L2, BF16_MAX_ABS)
+    ws = gpu_fwd_bwd(inp, dev, Wn)
+    for n in ("dk", "dv", "delta"):
+        assert torch.equal(res[n], ws[n]), n
+
+
+def test_window_recompute_dq_grouped(dev):
+    """The same with grouped key/value heads (4 query heads, 2 key/value heads)."""
+    import torch
+    na = _na()
+    inp = W.make_train_inputs("d20", B=1, T=400, H=4, seed=4601)
+    q, k, v, do = (to_device(x, dev) for x in (inp.q_store, inp.k_store, inp.v_store,
+                                               inp.do_store))
+    k2, v2 = k[:, :, :2].contiguous(), v[:, :, :2].contiguous()
+    o, lse = na.attn_fwd(q, k2, v2, window=90)
+    dq, dk, dv, _ = na.attn_bwd(q, k2, v2, o, do, lse, window=90, recompute_dq=True)
+    dq_ws, dk_ws, dv_ws, _ = na.attn_bwd(q, k2, v2, o, do, lse, window=90)
+    torch.cuda.synchronize()
+    assert torch.equal(dk, dk_ws) and torch.equal(dv, dv_ws)
+    kk = inp.k[:, :, :2]
+    vv = inp.v[:, :, :2]
+    rdq, _, _, _ = oracle.backward(inp.q, np.repeat(kk, 2, axis=2), np.repeat(vv, 2, axis=2),
+                                   inp.do, window=90)
+    assert_close("dq", to_host(dq), rdq, BF16_REL_L2, BF16_MAX_ABS)
+    assert_close("dq paths", to_host(dq), to_host(dq_ws), 5e-3, 2e-3)
 
 
 def test_window_covering_every_key_is_the_plain_call(dev):
@@ -152,7 +191,7 @@ def test_window_decode_full_workload(dev):
 
 
 def test_window_decode_many_sequences_raw_slot_order(dev):
-    """More than 8192 sequences (the raw (sequence, chunk) slot walk) with a window."""
+    """More than 4096 sequences (several split/combine launch pairs) with a window."""
     B = 8200
     rng = np.random.default_rng(51)
     lens = rng.integers(0, 200, size=B)
