@@ -650,8 +650,16 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(
       const bool edge = WIN && QT_ROWS * t + QT_ROWS - 1 - kw0 > win;
       // the block two ahead of each step: the same rows of the next position
       const uint32_t inn = ini(un);
+      // with a window, a block whose first query row is more than win past
+      // this wavefront's last key holds no visible pair, nor does any later
+      // block of the item: the wavefront skips their steps (and their dS
+      // blocks, which the dQ GEMM never reads) but keeps taking part in the
+      // copies and barriers
+      const bool gone0 = WIN && 32 * j0 - (kw0 + 31) > win;
+      const bool gone1 = WIN && 32 * j1 - (kw0 + 31) > win;
       // block j0 (rows 0..31 of tile t), scores of rows 32..63
-      if (STEADY || j0 > bw) {
+      if (gone0) {
+      } else if (STEADY || j0 > bw) {
         if (WIN && edge)
           dkdv_step<true, true>(nc, 32, tc, 0, nn, inn, kreg, vreg, pre, s0, p0, s1, p1, dka, dva,
                                 lane, kq, ds_of(h, j0), win);
@@ -665,7 +673,12 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(
         dkdv_scores(nc, 32, ini(u), nn, 0, inn, kreg, vreg, s1, p1, s0, p0, pre, lane);
       }
       // block j1 (rows 32..63 of tile t), scores of the next position's rows 0..31
-      if (STEADY || j1 > bw) {
+      if (gone1) {
+        // the next query head's first block is this wavefront's diagonal
+        // (wavefront 0): its scores come from this slot, as in the step
+        if (GRP && t == qte - 1 && g + 1 < G && bw == 2 * qt0)
+          dkdv_scores(nn, 0, inn, nn, 32, inn, kreg, vreg, s0, p0, s1, p1, pre, lane);
+      } else if (STEADY || j1 > bw) {
         if (WIN && edge)
           dkdv_step<true, true>(nn, 0, tc, 32, nn, inn, kreg, vreg, pre, s1, p1, s0, p0, dka, dva,
                                 lane, kq, ds_of(h, j1), win);
