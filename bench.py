@@ -107,6 +107,7 @@ class HipEvents:
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_d20.json")
 KERNEL_SOURCES = {  # the sources whose text determines each kernel's code
     "fwd": ["fwd_bf16.hip", "device_common.hpp", "internal.hpp"],
+    "delta": ["bwd_bf16.hip", "device_common.hpp", "internal.hpp"],
     "dkdv": ["bwd_bf16.hip", "device_common.hpp", "internal.hpp"],
     "dq": ["bwd_bf16.hip", "device_common.hpp", "internal.hpp"],
     "qk_norm_rope_fwd": ["prologue_bf16.hip", "device_common.hpp", "internal.hpp"],
@@ -796,6 +797,8 @@ def main():
             "split_avg_us": round(float(np.mean(split)) * 1e3, 2),
             "combine_avg_us": round(float(np.mean(comb)) * 1e3, 2),
             "split_GB_per_s": round(split_gbs, 1), "iters": nd, "rotated_caches": 3,
+            "traffic_split": recorded_traffic("decode_split"),
+            "traffic_combine": recorded_traffic("decode_combine"),
         }
         # the engine's per-token step: append the new token's rows (QK norm and
         # rotary embedding folded in), then attend over them with the cache
