@@ -43,7 +43,10 @@ namespace na {
 namespace {
 
 constexpr int D = kHeadDim;
-constexpr int NW = 4;             // wavefronts per workgroup (32 query rows each)
+#ifndef NA_FWD_NW
+#define NA_FWD_NW 4
+#endif
+constexpr int NW = NA_FWD_NW;     // wavefronts per workgroup (32 query rows each)
 constexpr int BQ = 32 * NW;       // query rows per workgroup
 constexpr int BK = 64;   // keys per LDS tile
 constexpr uint32_t BUF_B = 2 * kTileBytes;  // one buffer: K tile, then V tile
