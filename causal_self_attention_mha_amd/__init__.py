@@ -10,7 +10,8 @@ point raises if the library is not built or no GPU is present.
 
 Functions (names match the C entry points):
   attn_fwd(q, k, v)                       -> (o, lse)
-  attn_bwd(q, k, v, o, dout, lse)         -> (dq, dk, dv, delta)
+  attn_bwd(q, k, v, o, dout, lse)         -> (dq, dk, dv)
+                                          (return_delta=True: (dq, dk, dv, delta))
   attn_decode(q, k_cache, v_cache, seqlens) -> (o, lse)
   attn_decode_noalloc(q, k_cache, v_cache, seqlens) -> (o, lse)
                                           (no workspace: the library's fixed scratch)
@@ -244,8 +245,10 @@ def bwd_workspace_bytes(B, T, H, D=HEAD_DIM):
 
 
 def attn_bwd(q, k, v, o, dout, lse, dq=None, dk=None, dv=None, delta=None, workspace=None,
-             recompute_dq=False, window=None, rope=None, eps=1e-6):
-    """Causal attention backward.  Returns (dq, dk, dv, delta).
+             recompute_dq=False, window=None, rope=None, eps=1e-6, return_delta=False):
+    """Causal attention backward.  Returns (dq, dk, dv), or (dq, dk, dv, delta)
+    with return_delta=True (delta = rowsum(dout * o), the preprocess's (B, H, T)
+    fp32 output, allocated here unless given).
 
     bf16: by default a dS workspace is allocated (or `workspace` is used) so
     that dq is a GEMM over the stored dS; recompute_dq=True passes no
@@ -312,7 +315,7 @@ def attn_bwd(q, k, v, o, dout, lse, dq=None, dk=None, dv=None, delta=None, works
                lib.na_attn_bwd_f32(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse),
                                    _ptr(dq), _ptr(dk), _ptr(dv), _ptr(delta), B, T, H, D,
                                    _stream(q)))
-    return dq, dk, dv, delta
+    return (dq, dk, dv, delta) if return_delta else (dq, dk, dv)
 
 
 def decode_workspace_bytes(B, H, T_cap, D=HEAD_DIM):

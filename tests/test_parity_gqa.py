@@ -29,7 +29,7 @@ def gpu_fwd_bwd(inp, dev, window=None):
     q, k, v, do = (to_device(x, dev) for x in (inp.q_store, inp.k_store, inp.v_store,
                                                inp.do_store))
     o, lse = na.attn_fwd(q, k, v, window=window)
-    dq, dk, dv, delta = na.attn_bwd(q, k, v, o, do, lse, window=window)
+    dq, dk, dv, delta = na.attn_bwd(q, k, v, o, do, lse, window=window, return_delta=True)
     torch.cuda.synchronize()
     return dict(o=o, lse=lse, dq=dq, dk=dk, dv=dv, delta=delta)
 

@@ -32,7 +32,7 @@ def run_train(q_st, k_st, v_st, do_st, dev):
     import causal_self_attention_mha_amd as na
     q, k, v, do = (to_device(x, dev) for x in (q_st, k_st, v_st, do_st))
     o, lse = na.attn_fwd(q, k, v)
-    dq, dk, dv, _ = na.attn_bwd(q, k, v, o, do, lse)
+    dq, dk, dv = na.attn_bwd(q, k, v, o, do, lse)
     torch.cuda.synchronize()
     return {n: to_host(t) for n, t in (("o", o), ("lse", lse), ("dq", dq), ("dk", dk),
                                        ("dv", dv))}

@@ -156,7 +156,7 @@ def test_prologue_chained_with_attention(dev):
     ct, sn = torch.from_numpy(c).to(dev), torch.from_numpy(s).to(dev)
     qr, kr = na.qk_norm_rope_fwd(q, k, ct, sn)
     o, lse = na.attn_fwd(qr, kr, v)
-    dqr, dkr, dv, _ = na.attn_bwd(qr, kr, v, o, do, lse)
+    dqr, dkr, dv = na.attn_bwd(qr, kr, v, o, do, lse)
     dq, dk = na.qk_norm_rope_bwd(q, k, dqr, dkr, ct, sn)
     torch.cuda.synchronize()
     c64, s64 = c.astype(np.float64), s.astype(np.float64)
@@ -237,7 +237,7 @@ def test_bwd_with_prologue_folded_in(dev, B, T, H, Hk, Wn):
     ct, sn = torch.from_numpy(c).to(dev), torch.from_numpy(s).to(dev)
     qr, kr = na.qk_norm_rope_fwd(q_raw, k_raw, ct, sn)
     o, lse = na.attn_fwd(qr, kr, v, window=Wn)
-    dq, dk, dv, _ = na.attn_bwd(qr, kr, v, o, do, lse, window=Wn, rope=(q_raw, k_raw, ct, sn))
+    dq, dk, dv = na.attn_bwd(qr, kr, v, o, do, lse, window=Wn, rope=(q_raw, k_raw, ct, sn))
     torch.cuda.synchronize()
     c64, s64 = c.astype(np.float64), s.astype(np.float64)
     xq, xk = tr.q.astype(np.float64), kv(tr.k).astype(np.float64)
@@ -264,8 +264,8 @@ def test_bwd_with_prologue_folded_in_d20_sampled(dev):
     ct, sn = torch.from_numpy(c).to(dev), torch.from_numpy(s).to(dev)
     qr, kr = na.qk_norm_rope_fwd(q_raw, k_raw, ct, sn)
     o, lse = na.attn_fwd(qr, kr, v)
-    dq, dk, dv, _ = na.attn_bwd(qr, kr, v, o, do, lse, rope=(q_raw, k_raw, ct, sn))
-    dq2r, dk2r, _, _ = na.attn_bwd(qr, kr, v, o, do, lse)
+    dq, dk, dv = na.attn_bwd(qr, kr, v, o, do, lse, rope=(q_raw, k_raw, ct, sn))
+    dq2r, dk2r, _ = na.attn_bwd(qr, kr, v, o, do, lse)
     dq2, dk2 = na.qk_norm_rope_bwd(q_raw, k_raw, dq2r, dk2r, ct, sn)
     torch.cuda.synchronize()
     assert_close("dq vs two-step", to_host(dq), to_host(dq2), BF16_REL_L2, BF16_MAX_ABS)

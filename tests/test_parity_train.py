@@ -29,7 +29,8 @@ def gpu_fwd_bwd(inp, dev, recompute_dq=False):
     q, k, v, do = (to_device(x, dev) for x in (inp.q_store, inp.k_store, inp.v_store,
                                                inp.do_store))
     o, lse = na.attn_fwd(q, k, v)
-    dq, dk, dv, delta = na.attn_bwd(q, k, v, o, do, lse, recompute_dq=recompute_dq)
+    dq, dk, dv, delta = na.attn_bwd(q, k, v, o, do, lse, recompute_dq=recompute_dq,
+                                    return_delta=True)
     torch.cuda.synchronize()
     return dict(q=q, k=k, v=v, do=do, o=o, lse=lse, dq=dq, dk=dk, dv=dv, delta=delta)
 
@@ -115,7 +116,7 @@ def test_causal_independence_bitwise(dev):
     k2[:, t + 1:] = torch.randn_like(k2[:, t + 1:], dtype=torch.float32).to(torch.bfloat16)
     v2[:, t + 1:] = torch.randn_like(v2[:, t + 1:], dtype=torch.float32).to(torch.bfloat16)
     o2, lse2 = na.attn_fwd(r1["q"], k2, v2)
-    dq2, _, _, _ = na.attn_bwd(r1["q"], k2, v2, o2, r1["do"], lse2)
+    dq2, _, _ = na.attn_bwd(r1["q"], k2, v2, o2, r1["do"], lse2)
     torch.cuda.synchronize()
     assert torch.equal(r1["o"][:, :t + 1], o2[:, :t + 1])
     assert torch.equal(r1["lse"][:, :, :t + 1], lse2[:, :, :t + 1])

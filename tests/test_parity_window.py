@@ -27,7 +27,8 @@ def gpu_fwd_bwd(inp, dev, window, recompute_dq=False):
     q, k, v, do = (to_device(x, dev) for x in (inp.q_store, inp.k_store, inp.v_store,
                                                inp.do_store))
     o, lse = na.attn_fwd(q, k, v, window=window)
-    dq, dk, dv, delta = na.attn_bwd(q, k, v, o, do, lse, window=window, recompute_dq=recompute_dq)
+    dq, dk, dv, delta = na.attn_bwd(q, k, v, o, do, lse, window=window, recompute_dq=recompute_dq,
+                                    return_delta=True)
     torch.cuda.synchronize()
     return dict(q=q, k=k, v=v, do=do, o=o, lse=lse, dq=dq, dk=dk, dv=dv, delta=delta)
 
@@ -75,8 +76,8 @@ def test_window_recompute_dq_grouped(dev):
                                                inp.do_store))
     k2, v2 = k[:, :, :2].contiguous(), v[:, :, :2].contiguous()
     o, lse = na.attn_fwd(q, k2, v2, window=90)
-    dq, dk, dv, _ = na.attn_bwd(q, k2, v2, o, do, lse, window=90, recompute_dq=True)
-    dq_ws, dk_ws, dv_ws, _ = na.attn_bwd(q, k2, v2, o, do, lse, window=90)
+    dq, dk, dv = na.attn_bwd(q, k2, v2, o, do, lse, window=90, recompute_dq=True)
+    dq_ws, dk_ws, dv_ws = na.attn_bwd(q, k2, v2, o, do, lse, window=90)
     torch.cuda.synchronize()
     assert torch.equal(dk, dk_ws) and torch.equal(dv, dv_ws)
     kk = inp.k[:, :, :2]
@@ -95,7 +96,7 @@ def test_window_covering_every_key_is_the_plain_call(dev):
     a = gpu_fwd_bwd(inp, dev, 299)
     q, k, v, do = a["q"], a["k"], a["v"], a["do"]
     o, lse = na.attn_fwd(q, k, v)
-    dq, dk, dv, delta = na.attn_bwd(q, k, v, o, do, lse)
+    dq, dk, dv, delta = na.attn_bwd(q, k, v, o, do, lse, return_delta=True)
     torch.cuda.synchronize()
     for n, x in (("o", o), ("lse", lse), ("dq", dq), ("dk", dk), ("dv", dv)):
         assert torch.equal(a[n], x), n
