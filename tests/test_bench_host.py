@@ -48,3 +48,20 @@ def test_visible_pairs(T, W, expect):
     if T <= 16:
         brute = sum(1 for i in range(T) for j in range(i + 1) if W is None or i - j <= W)
         assert brute == expect
+
+
+def test_sclk_sampler_reads_the_starred_level(tmp_path, monkeypatch):
+    """The clock sampler takes the starred line of pp_dpm_sclk (the driver's
+    current level) and reports the busiest card's distribution."""
+    import glob
+    busy = tmp_path / "busy"
+    idle = tmp_path / "idle"
+    busy.write_text("0: 500Mhz\n1: 2024Mhz *\n2: 2400Mhz\n")
+    idle.write_text("S: 113Mhz *\n0: 500Mhz\n1: 2400Mhz\n")
+    monkeypatch.setattr(glob, "glob", lambda pattern: [str(idle), str(busy)])
+    calls = []
+    res = bench.sample_sclk(lambda: calls.append(1) or __import__("time").sleep(0.005), 0.05)
+    assert calls and res["source"] == str(busy)
+    assert res["median_MHz"] == 2024.0 and res["min_MHz"] == res["max_MHz"] == 2024.0
+    monkeypatch.setattr(glob, "glob", lambda pattern: [])
+    assert bench.sample_sclk(lambda: None, 0.01)["source"] is None
