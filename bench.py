@@ -5,7 +5,12 @@ One step = one pass of the training hot path at the d20 shape
 (B=32, T=2048, H=10, D=128, bf16): the forward (o, lse) and the backward
 (delta, dk/dv, dq) through the C ABI.  Inputs are the seeded synthetic
 tensors of the `workloads` module, resident in HBM before timing starts.
-W untimed warmup steps, then exactly K timed steps between
+Each measured section first runs its call back to back, untimed, for
+--ramp-seconds (default 0.3 s; reported as "clock_ramp_s"): after the
+host-side input setup the GPU has idled and its clocks are down, and a K-step
+run that starts after an idle gap of 10 ms or more measures about 8% slower
+than the same steps back to back, which is the state of a training loop.
+Then W untimed warmup steps, then exactly K timed steps between
 torch.cuda.synchronize() calls; per-kernel durations come from HIP events
 recorded on the launch stream around every kernel of every fourth timed step
 (--kernel-events-every: an event between two kernels adds a few
@@ -287,6 +292,9 @@ def main():
                          "event between two kernels adds a few microseconds to the step)")
     ap.add_argument("--kv-heads", type=int, default=5,
                     help="key/value heads for the extra grouped-query measurement (0 = skip)")
+    ap.add_argument("--ramp-seconds", type=float, default=0.3,
+                    help="untimed back-to-back calls before each section's warmup, so that "
+                         "the GPU's clocks are up after the host-side setup (0 = none)")
     ap.add_argument("--trials", type=int, default=5,
                     help="further runs of the same K timed steps, reported as their spread "
                          "and median (the headline value is the first run)")
@@ -318,6 +326,20 @@ def main():
 
     def log(msg):
         print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+    def ramp(fn):
+        """Untimed back-to-back calls of fn for --ramp-seconds before a section's
+        warmup: after the host-side input setup the GPU has been idle and its
+        clocks are down; a short warmup does not bring them back (a K-step run
+        after a >= 10 ms idle gap measured about 8% slower than back to back)."""
+        t_end = time.perf_counter() + args.ramp_seconds
+        n = 0
+        while time.perf_counter() < t_end:
+            for _ in range(4):
+                fn()
+            n += 4
+            torch.cuda.synchronize()
+        log(f"ramp: {n} calls")
 
     if args.copy_probe_mb > 0:
         n = args.copy_probe_mb << 20
@@ -375,6 +397,7 @@ def main():
         if st:
             raise RuntimeError(lib.na_last_error().decode())
 
+    ramp(lambda: step(0))
     log(f"warmup {args.warmup} steps")
     for i in range(args.warmup):
         step(i)
@@ -427,6 +450,7 @@ def main():
         "config": {"workload": "d20 causal self-attention fwd+bwd", "B": B, "T": T, "H": H,
                    "D": D, "causal": True, "parallelism": "single GPU"},
         "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
+        "clock_ramp_s": args.ramp_seconds,
         "wall_s_timed": round(wall, 4),
         "gpu_ms_per_step_events": round(gpu_ms_per_step, 4),
         "kernel_event_steps": len(timed_ev),
@@ -436,6 +460,7 @@ def main():
 
     # ---------------- repeated trials of the same K-step loop (spread, median)
     if args.trials > 0:
+        ramp(lambda: step(0))
         tr_ms = []
         for _ in range(args.trials):
             torch.cuda.synchronize()
@@ -467,6 +492,7 @@ def main():
     wlen = args.window if 0 <= args.window < T - 1 else None
     if wlen is not None:
         log(f"sliding window {wlen}: warmup {args.warmup}, timing {args.steps} steps")
+        ramp(lambda: step(0, wlen))
         for i in range(args.warmup):
             step(i, wlen)
         torch.cuda.synchronize()
@@ -518,6 +544,7 @@ def main():
                 raise RuntimeError(lib.na_last_error().decode())
 
         log(f"gqa {H}/{hkv} heads: warmup {args.warmup}, timing {args.steps} steps")
+        ramp(lambda: gstep(0))
         for i in range(args.warmup):
             gstep(i)
         torch.cuda.synchronize()
@@ -573,6 +600,7 @@ def main():
             if st:
                 raise RuntimeError(lib.na_last_error().decode())
 
+        ramp(lambda: xstep(0))
         for i in range(args.warmup):
             xstep(i)
         torch.cuda.synchronize()
@@ -623,6 +651,7 @@ def main():
             if st:
                 raise RuntimeError(lib.na_last_error().decode())
 
+        ramp(lambda: (rfwd(), rbwd()))
         for _ in range(args.warmup):
             rfwd()
             rbwd()
@@ -650,6 +679,7 @@ def main():
             if st:
                 raise RuntimeError(lib.na_last_error().decode())
 
+        ramp(lambda: (gfwd(), gbwd()))
         for _ in range(args.warmup):
             gfwd()
             gbwd()
@@ -717,6 +747,7 @@ def main():
 
         step_ms = {}
         for name, folded in (("folded_bwd", True), ("separate_bwd", False)):
+            ramp(lambda: pro_step(folded))
             for _ in range(args.warmup):
                 pro_step(folded)
             torch.cuda.synchronize()
@@ -770,6 +801,7 @@ def main():
             if not per_kernel:
                 ev.record(e[2], stream)
 
+        ramp(lambda: dstep(0, per_kernel=True))
         for i in range(5):
             dstep(i, per_kernel=True)
         torch.cuda.synchronize()
@@ -897,6 +929,7 @@ def main():
             if st:
                 raise RuntimeError(lib.na_last_error().decode())
 
+        ramp(pstep)
         for _ in range(args.warmup):
             pstep()
         torch.cuda.synchronize()
@@ -932,6 +965,7 @@ def main():
 
         rope_ms = {}
         for name, fn in (("fused", prstep), ("two_step", p2step)):
+            ramp(fn)
             for _ in range(args.warmup):
                 fn()
             torch.cuda.synchronize()
