@@ -1138,30 +1138,13 @@ __global__ __launch_bounds__(64 * DG_WAVES, 8 / DG_WAVES) void dq_gemm_kernel(co
 #pragma unroll
     for (int i = 0; i < 4; ++i) dqa[i] = f32x16{};
 
-    // ROPE: the raw row and its angles, loaded at the start of the item so
-    // that their latency hides behind the key loop.  The lane holds elements
-    // d = 32 db + 8 g + 4 half + j of its row (the other half in lane l ^ 32);
-    // d < 64 (db < 2) pairs with d + 64 (db + 2).
-    uint2 xw[ROPE ? 4 : 1][4];
-    float4 c4[ROPE ? 2 : 1][4], s4[ROPE ? 2 : 1][4];
-    if constexpr (ROPE) {
-      const int pr = min(qw0 + l32, T - 1);
-      const u16* xp = ra.raw + base + static_cast<size_t>(pr) * rs + 4 * half;
-      const float* cp = ra.cos_t + static_cast<size_t>(pr) * (D / 2) + 4 * half;
-      const float* sp = ra.sin_t + static_cast<size_t>(pr) * (D / 2) + 4 * half;
-#pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int g = 0; g < 4; ++g)
-          xw[db][g] = *reinterpret_cast<const uint2*>(xp + 32 * db + 8 * g);
-#pragma unroll
-      for (int db = 0; db < 2; ++db)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          c4[db][g] = *reinterpret_cast<const float4*>(cp + 32 * db + 8 * g);
-          s4[db][g] = *reinterpret_cast<const float4*>(sp + 32 * db + 8 * g);
-        }
-    }
+    // ROPE: raw chunk and angles of the row that lane group gi finishes in
+    // round sh, step m of the epilogue: query qw0 + 16 sh + 4 m + gi
+    auto rope_load = [&](int sh, int m) {
+      const int qr = min(qw0 + 16 * sh + 4 * m + gi, T - 1);
+      return rope_row_load(ra.raw + base + static_cast<size_t>(qr) * rs + 8 * i16, ra, qr, i16);
+    };
+    RopeRow rrow[ROPE ? 4 : 1];
 
     const int last_q = min(q0 + DG_ROWS, T) - 1;
     const int n_kt = last_q / DG_KEYS + 1;
@@ -1274,63 +1257,48 @@ __global__ __launch_bounds__(64 * DG_WAVES, 8 / DG_WAVES) void dq_gemm_kernel(co
       if (kt + 1 < n_kt) tile(std::integral_constant<uint32_t, 1>{}, kt + 1);
     }
 
-    const int qrow = qw0 + l32;
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) dqa[db][e] *= scale;
+    // dqa[db] element r: query qw0 + l32, d = 32 db + 8 (r / 4) + 4 half + r % 4.
+    // The rows leave through this wavefront's own dS buffers of stages 0 and 1
+    // (rows 0..15 and 16..31; free once its own reads of them are done, which
+    // the LDS wait first establishes, also as a compiler fence), so that 16
+    // lanes store one 256-byte row (chunk c of staged row r at c ^ r).
+    // ROPE: the raw query rows' gradient is formed from the staged bf16
+    // gradient chunk (rope_bwd_chunk); the raw chunk and angles of the first
+    // four rows a lane group finishes are loaded before the staging, each of
+    // the next four as soon as its registers are free.
     if constexpr (ROPE) {
-      float x[4][16];
-      float ss = 0.f;
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const uint2 w = xw[db][g];
-          x[db][4 * g] = __uint_as_float(w.x << 16);
-          x[db][4 * g + 1] = __uint_as_float(w.x & 0xffff0000u);
-          x[db][4 * g + 2] = __uint_as_float(w.y << 16);
-          x[db][4 * g + 3] = __uint_as_float(w.y & 0xffff0000u);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) ss = fmaf(x[db][4 * g + j], x[db][4 * g + j], ss);
-        }
-      ss += __shfl_xor(ss, 32, 64);
-      const float rn = __builtin_amdgcn_rsqf(ss * (1.f / D) + ra.eps);
-      float dot = 0.f;
-#pragma unroll
-      for (int db = 0; db < 2; ++db)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const float4 cv = c4[db][g], sv = s4[db][g];
-          const float cs[4] = {cv.x, cv.y, cv.z, cv.w}, sn[4] = {sv.x, sv.y, sv.z, sv.w};
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const float g1 = dqa[db][4 * g + j], g2 = dqa[db + 2][4 * g + j];
-            const float d1 = fmaf(g1, cs[j], g2 * sn[j]);    // R^T g, first half
-            const float d2 = fmaf(g2, cs[j], -g1 * sn[j]);   // second half
-            dqa[db][4 * g + j] = d1;
-            dqa[db + 2][4 * g + j] = d2;
-            dot = fmaf(d1, x[db][4 * g + j], fmaf(d2, x[db + 2][4 * g + j], dot));
-          }
-        }
-      dot += __shfl_xor(dot, 32, 64);
-      const float m = dot * rn * (1.f / D);  // mean(dz z)
-#pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int e = 0; e < 16; ++e)
-          dqa[db][e] = rn * fmaf(-x[db][e] * rn, m, dqa[db][e]);
+      for (int m = 0; m < 4; ++m) rrow[m] = rope_load(0, m);
     }
-    if (qrow < T) {
-      u16* qp = dq + base + qrow * rs;
+    constexpr uint32_t kStage = DG_WAVES * DG_DS_B;  // bytes between a wavefront's stages
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    {
+      const int rr = l32 & 15;
+      const uint32_t row = st_lds + (l32 >> 4) * kStage + rr * 256 + 8 * half;
 #pragma unroll
       for (int db = 0; db < 4; ++db)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          uint2 pk = make_uint2(pack_bf16x2(dqa[db][4 * g], dqa[db][4 * g + 1]),
-                                pack_bf16x2(dqa[db][4 * g + 2], dqa[db][4 * g + 3]));
-          *reinterpret_cast<uint2*>(qp + 32 * db + 8 * g + 4 * half) = pk;
+          const int e = 4 * g;
+          lds_st8(row + 16 * ((4 * db + g) ^ rr),
+                  pack_bf16x2(dqa[db][e] * scale, dqa[db][e + 1] * scale),
+                  pack_bf16x2(dqa[db][e + 2] * scale, dqa[db][e + 3] * scale));
         }
+    }
+    asm volatile("" ::: "memory");  // the reads below follow the writes above
+#pragma unroll
+    for (int sh = 0; sh < 2; ++sh) {  // queries qw0 + 16 sh .. + 15
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {  // lane i: chunk i % 16 of row 4 m + i / 16
+        const int rr = 4 * m + gi, c = i16;
+        uint4 x = lds_ld16(st_lds + sh * kStage + rr * 256 + 16 * (c ^ rr));
+        const int qr = qw0 + 16 * sh + rr;
+        if constexpr (ROPE) {  // whole 16-lane groups: qr is uniform over one
+          x = rope_bwd_chunk(x, rrow[ROPE ? m : 0], ra.eps, c);
+          if (sh == 0) rrow[ROPE ? m : 0] = rope_load(1, m);
+        }
+        if (qr < T) st16(dq + base + static_cast<size_t>(qr) * rs + 8 * c, x);
+      }
     }
   }
 }
