@@ -41,7 +41,10 @@ prefill ("with_qk_norm_rope").
 The attention prologue (RMS normalisation + rotary embedding of q and k at
 the d20 shape, forward and backward, and the value-embedding gate on the d20
 key/value heads) is timed and reported under "prologue" (algorithmic bytes:
-every tensor read or written once, plus the cos/sin tables).
+every tensor read or written once, plus the cos/sin tables), and so is the
+d20 step with the whole prologue (its forward kernels, the attention forward
+and backward, and the prologue's backward either as its own two kernels or
+folded into the attention backward: "d20_step_with_prologue_ms").
 
 Grouped-query attention (--kv-heads, default 5: two query heads per key/value
 head, a choice of this benchmark; the pages give no key/value head count) is
@@ -718,30 +721,39 @@ def main():
                            "traffic_bwd": recorded_traffic("value_gate_bwd")},
             "calls": args.steps}
         log(f"prologue {result['prologue']}")
-        # the d20 step with the prologue: prologue forward, attention forward and
-        # backward, prologue backward as its own kernel or folded into the
-        # attention backward's epilogues (na_attn_bwd_rope)
+        # the d20 step with the prologue: prologue forward (QK norm + rotary
+        # embedding of q and k, value-embedding gate of v; k stands in for ve),
+        # attention forward and backward, prologue backward as its own kernels
+        # or folded into the attention backward's epilogues (na_attn_bwd_rope
+        # with the gate)
         tdq, tdk, tdv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        vg, tdve, tdg = torch.empty_like(v), torch.empty_like(v), torch.empty_like(gt)
 
         def pro_step(folded):
             rfwd()  # yq, yk = rotated q, k
-            st = lib.na_attn_fwd(ptr(yq), ptr(yk), ptr(v), ptr(o), ptr(lse), B, T, H, D,
-                                 P(stream))
+            st = lib.na_value_gate_fwd(ptr(v), ptr(k), ptr(gt), ptr(vg), B, T, H, D, P(stream))
+            if not st:
+                st = lib.na_attn_fwd(ptr(yq), ptr(yk), ptr(vg), ptr(o), ptr(lse), B, T, H, D,
+                                     P(stream))
             if st:
                 raise RuntimeError(lib.na_last_error().decode())
             if folded:
-                st = lib.na_attn_bwd_rope(ptr(yq), ptr(yk), ptr(v), ptr(o), ptr(do), ptr(lse),
-                                          ptr(q), ptr(k), ptr(ct), ptr(sn), T, eps, ptr(tdq),
-                                          ptr(tdk), ptr(tdv), ptr(delta), ptr(ws), ws_bytes, B, T,
-                                          H, H, D, -1, P(stream))
+                st = lib.na_attn_bwd_rope(ptr(yq), ptr(yk), ptr(vg), ptr(o), ptr(do), ptr(lse),
+                                          ptr(q), ptr(k), ptr(ct), ptr(sn), T, eps, ptr(k),
+                                          ptr(gt), ptr(tdq), ptr(tdk), ptr(tdv), ptr(tdve),
+                                          ptr(tdg), ptr(delta), ptr(ws), ws_bytes, B, T, H, H, D,
+                                          -1, P(stream))
             else:
-                st = lib.na_attn_bwd(ptr(yq), ptr(yk), ptr(v), ptr(o), ptr(do), ptr(lse),
+                st = lib.na_attn_bwd(ptr(yq), ptr(yk), ptr(vg), ptr(o), ptr(do), ptr(lse),
                                      ptr(rgq), ptr(rgk), ptr(tdv), ptr(delta), ptr(ws), ws_bytes,
                                      B, T, H, D, P(stream))
                 if not st:
                     st = lib.na_qk_norm_rope_bwd(ptr(q), ptr(k), ptr(rgq), ptr(rgk), ptr(tdq),
                                                  ptr(tdk), ptr(ct), ptr(sn), None, B, T, H, H, D,
                                                  T, eps, P(stream))
+                if not st:
+                    st = lib.na_value_gate_bwd(ptr(k), ptr(gt), ptr(tdv), ptr(tdve), ptr(tdg), B,
+                                               T, H, D, P(stream))
             if st:
                 raise RuntimeError(lib.na_last_error().decode())
 
@@ -758,7 +770,7 @@ def main():
             torch.cuda.synchronize()
             step_ms[name] = round(ev.ms(rev[0], rev[1]) / args.steps, 4)
         result["prologue"]["d20_step_with_prologue_ms"] = step_ms
-        del yq, yk, rgq, rgk, gt, tdq, tdk, tdv
+        del yq, yk, rgq, rgk, gt, tdq, tdk, tdv, vg, tdve, tdg
 
     del q, k, v, do, o, dq, dk, dv, ws
     torch.cuda.empty_cache()

@@ -113,8 +113,8 @@ def load_library():
     lib.na_attn_decode_append.argtypes = [vp, vp, vp, vp, vp, vp, f32p, f32p, i, ctypes.c_float,
                                           vp, vp, vp, f32p, i, i, i, i, i, i, vp, sz, vp]
     lib.na_attn_bwd_rope.argtypes = [vp, vp, vp, vp, vp, f32p, vp, vp, f32p, f32p, i,
-                                     ctypes.c_float, vp, vp, vp, f32p, vp, sz, i, i, i, i, i, i,
-                                     vp]
+                                     ctypes.c_float, vp, vp, vp, vp, vp, vp, vp, f32p, vp, sz, i,
+                                     i, i, i, i, i, vp]
     lib.na_value_gate_fwd.argtypes = [vp, vp, vp, vp, i, i, i, i, vp]
     lib.na_value_gate_bwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, vp]
     lib.na_qk_norm_rope_bwd.argtypes = [vp, vp, vp, vp, vp, vp, f32p, f32p, vp, i, i, i, i, i,
@@ -245,7 +245,8 @@ def bwd_workspace_bytes(B, T, H, D=HEAD_DIM):
 
 
 def attn_bwd(q, k, v, o, dout, lse, dq=None, dk=None, dv=None, delta=None, workspace=None,
-             recompute_dq=False, window=None, rope=None, eps=1e-6, return_delta=False):
+             recompute_dq=False, window=None, rope=None, eps=1e-6, return_delta=False,
+             value_gate=None):
     """Causal attention backward.  Returns (dq, dk, dv), or (dq, dk, dv, delta)
     with return_delta=True (delta = rowsum(dout * o), the preprocess's (B, H, T)
     fp32 output, allocated here unless given).
@@ -257,7 +258,10 @@ def attn_bwd(q, k, v, o, dout, lse, dq=None, dk=None, dv=None, delta=None, works
     rope=(q_raw, k_raw, cos, sin): q and k are the outputs of
     qk_norm_rope_fwd(q_raw, k_raw, cos, sin); dq and dk are returned as the
     gradients of q_raw and k_raw, the prologue's backward done in the same
-    kernels (na_attn_bwd_rope)."""
+    kernels (na_attn_bwd_rope).
+    value_gate=(ve, gate) (with rope): v is value_gate_fwd(v_in, ve, gate); the
+    kernel that writes dv also writes the gate's gradients, and (dve, dgate)
+    follow dv in the result (dv is the gradient of v_in as well)."""
     import torch
     lib = load_library()
     Hk = _kv_heads(q, k)
@@ -288,9 +292,15 @@ def attn_bwd(q, k, v, o, dout, lse, dq=None, dk=None, dv=None, delta=None, works
         args = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk),
                 _ptr(dv), _ptr(delta), _ptr(workspace), ws_bytes)
         w = -1 if window is None else window
+        _require(value_gate is None or rope is not None, "value_gate folds in with rope only")
         if rope is not None:
             q_raw, k_raw, cos, sin = rope
             _require(workspace is not None, "rope needs the dS workspace (recompute_dq=False)")
+            ve = gate = dve = dgate = None
+            if value_gate is not None:
+                ve, gate = value_gate
+                _check_value_gate(("v", "ve"), (v, ve), gate)
+                dve, dgate = torch.empty_like(ve), torch.empty_like(gate)
             _check_train(("q", "q_raw", "k_raw"), (q, q_raw, k_raw), dtype, kv_heads={"k_raw": Hk})
             for n, t in (("cos", cos), ("sin", sin)):
                 _require(t.dtype == torch.float32 and t.device == q.device and t.is_contiguous()
@@ -299,9 +309,12 @@ def attn_bwd(q, k, v, o, dout, lse, dq=None, dk=None, dv=None, delta=None, works
             _check(lib, "na_attn_bwd_rope",
                    lib.na_attn_bwd_rope(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse),
                                         _ptr(q_raw), _ptr(k_raw), _ptr(cos), _ptr(sin),
-                                        cos.shape[0], float(eps), _ptr(dq), _ptr(dk), _ptr(dv),
-                                        _ptr(delta), _ptr(workspace), ws_bytes, B, T, H, Hk, D, w,
-                                        _stream(q)))
+                                        cos.shape[0], float(eps), _ptr(ve), _ptr(gate), _ptr(dq),
+                                        _ptr(dk), _ptr(dv), _ptr(dve), _ptr(dgate), _ptr(delta),
+                                        _ptr(workspace), ws_bytes, B, T, H, Hk, D, w, _stream(q)))
+            if value_gate is not None:
+                out = (dq, dk, dv, dve, dgate)
+                return out + (delta,) if return_delta else out
         elif Hk != H:
             _check(lib, "na_attn_bwd_gqa",
                    lib.na_attn_bwd_gqa(*args, B, T, H, Hk, D, w, _stream(q), None))

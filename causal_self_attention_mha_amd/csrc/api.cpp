@@ -277,7 +277,8 @@ na_status na_attn_decode_gqa(const void* q, const void* k_cache, const void* v_c
 na_status na_attn_bwd_rope(const void* q, const void* k, const void* v, const void* o,
                            const void* dout, const float* lse, const void* q_raw,
                            const void* k_raw, const float* cos_tab, const float* sin_tab,
-                           int T_tab, float eps, void* dq, void* dk, void* dv, float* delta,
+                           int T_tab, float eps, const void* ve, const void* gate, void* dq,
+                           void* dk, void* dv, void* dve, void* dgate, float* delta,
                            void* workspace, size_t workspace_bytes, int B, int T, int H,
                            int H_kv, int D, int window, void* stream) {
   na_status st = check_sizes(B, T, H, D);
@@ -289,6 +290,11 @@ na_status na_attn_bwd_rope(const void* q, const void* k, const void* v, const vo
                   {{dq, "dq"}, {dk, "dk"}, {dv, "dv"}, {delta, "delta"},
                    {workspace, "workspace"}});
   if (st) return st;
+  const int n_gate = (ve != nullptr) + (gate != nullptr) + (dve != nullptr) + (dgate != nullptr);
+  if (n_gate != 0 && n_gate != 4)
+    return fail(NA_ERR_INVALID_ARG, "ve, gate, dve, dgate: give all four or none");
+  if (n_gate == 4 && (dve == dv || dve == dk || dve == dq || dgate == dv || dgate == dve))
+    return fail(NA_ERR_INVALID_ARG, "dve and dgate must not alias another output");
   if (T_tab < T) return fail(NA_ERR_INVALID_ARG, "T_tab=%d is smaller than T=%d", T_tab, T);
   if ((long double)T_tab * D > 2147483647.0L)
     return fail(NA_ERR_UNSUPPORTED, "the rotary tables (T_tab=%d) exceed 2^31-1 elements", T_tab);
@@ -300,7 +306,7 @@ na_status na_attn_bwd_rope(const void* q, const void* k, const void* v, const vo
     return fail(NA_ERR_INVALID_ARG, "workspace_bytes %zu < required %zu", workspace_bytes, need);
   return hip_status(na::launch_bwd_bf16(q, k, v, o, dout, lse, dq, dk, dv, delta, workspace, B, T,
                                         H, H_kv, window, (hipStream_t)stream, nullptr, q_raw,
-                                        k_raw, cos_tab, sin_tab, eps),
+                                        k_raw, cos_tab, sin_tab, eps, ve, gate, dve, dgate),
                     "na_attn_bwd_rope");
 }
 

@@ -152,6 +152,18 @@ __device__ __forceinline__ uint4 rope_bwd_chunk(uint4 g16, const RopeRow& rw, fl
                     pack_bf16x2(y[6], y[7]));
 }
 
+// With the value-embedding gate's backward folded in as well (v' = v + 3
+// sigmoid(g) ve fed the attention as its values), the kernel that writes dv
+// (= dv') also writes dve = 3 sigmoid(g) dv' and dg = 3 sigmoid(g)
+// (1 - sigmoid(g)) <ve, dv'>, from the bf16 dv' it stores, with the
+// arithmetic of the separate value-gate backward.
+struct GateBwd {
+  const u16* ve;    // (B, T, Hk, D), as v
+  const u16* gate;  // (B, T, Hk) logits
+  u16* dve;         // as ve
+  u16* dgate;       // as gate
+};
+
 // ---------------------------------------------------------------- dK, dV
 
 constexpr int KT_KEYS = 128;  // keys per workgroup (32 per wavefront)
@@ -388,12 +400,13 @@ __device__ __forceinline__ void rewrite_rows(const float* raw, float* own, int l
 // that read it, so that dK and dV sum the group in registers (GRP = false:
 // Hk = H, G = 1, and the head bookkeeping compiles away).
 // ROPE: dk is written as the gradient of the raw keys (RopeBwd).
-template <bool WIN, bool GRP, bool ROPE>
+// GATE: dve and dg are written next to dv (GateBwd).
+template <bool WIN, bool GRP, bool ROPE, bool GATE = false>
 __global__ __launch_bounds__(256, 1) void dkdv_kernel(
     const u16* __restrict__ q, const u16* __restrict__ k, const u16* __restrict__ v,
     const u16* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
     u16* __restrict__ dk, u16* __restrict__ dv, u16* __restrict__ dsw, int nbt, int B, int T,
-    int H, int Hk, float c_log2, float scale, int win, RopeBwd ra) {
+    int H, int Hk, float c_log2, float scale, int win, RopeBwd ra, GateBwd gt) {
   // NBUF query tiles (q and dout, swizzled, see tile_swz) and their lse, delta rows
   __shared__ __attribute__((aligned(1024))) char qtiles[NBUF * BUF_B];
   __shared__ __attribute__((aligned(1024))) char kstage[2 * TILE_B];  // K rows of an item
@@ -706,17 +719,19 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(
 
     // Every wavefront is done with the last tile's buffer: the next item's V
     // rows go there, and whatever the stream has not copied yet of its K rows
-    // and first two query tiles follows.
+    // and first two query tiles follows (issue_next).
     mfma_drain(dka, dva);
     wait_lds();
     __syncthreads();
     const int ulast = (gb + N - 1) % NBUF;
-    if (has_next) {
-      if (!k_next) copy_rows(nxt, k, kst_lds);
-      copy_rows(nxt, v, qt_lds + ulast * BUF_B);
-      for (int j = nx; j < 2; ++j)
-        if (j < nxt.N) issue(nxt, j, (gb + N + j) % NBUF);
-    }
+    auto issue_next = [&]() {
+      if (has_next) {
+        if (!k_next) copy_rows(nxt, k, kst_lds);
+        copy_rows(nxt, v, qt_lds + ulast * BUF_B);
+        for (int j = nx; j < 2; ++j)
+          if (j < nxt.N) issue(nxt, j, (gb + N + j) % NBUF);
+      }
+    };
 
     // dka[db], dva[db] (dK^T, dV^T blocks) element r: key kw0 + l32,
     // d = 32 db + 8 (r/4) + 4 half + r%4.  The rows leave through this
@@ -729,57 +744,124 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(
     // compiler does not see (it may sink a read into the conditional store
     // that uses it, past the next round's writes): each round starts with an
     // LDS wait that is also a compiler memory barrier.
-    // ROPE: the raw key chunks of the 8 rows this lane finishes, loaded before
-    // the rounds so that their latency overlaps the staging (the angles, L2
-    // hits, are loaded where they are used: all of it at once would not fit
-    // the register budget)
-    uint4 xraw[ROPE ? 8 : 1];
-    if constexpr (ROPE) {
+    // Round sh of acc (scaled by sc): lane i gets chunk c = i % 16 of the row
+    // of key key_of(sh, m) in x[m].  (The lane index is passed through an
+    // empty asm so that what derives from it is computed here, not kept live
+    // through the loop above, which needs every register.)
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int c = ln & 15;
+    auto key_of = [&](int sh, int m) { return kw0 + 16 * sh + 4 * m + (ln >> 4); };
+    auto stage_round = [&](const f32x16* acc, float sc, int sh, uint4 (&x)[4]) {
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      if (((ln & 31) >> 4) == sh) {
+        const int rr = ln & 15;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int kr = min(kw0 + 16 * (i >> 2) + 4 * (i & 3) + (lane >> 4), T - 1);
-        xraw[i] = ld16(ra.raw + kbase + kr * rsk + 8 * (lane & 15));
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int e = 4 * g;
+            lds_st8(est_lds + rr * 256 + 16 * ((4 * db + g) ^ rr) + 8 * (ln >> 5),
+                    pack_bf16x2(acc[db][e] * sc, acc[db][e + 1] * sc),
+                    pack_bf16x2(acc[db][e + 2] * sc, acc[db][e + 3] * sc));
+          }
       }
-    }
 #pragma unroll
-    for (int tsel = 0; tsel < 2; ++tsel) {  // dK, then dV
-      const f32x16* acc = tsel ? dva : dka;
-      const float sc = tsel ? 1.f : scale;
-      u16* dst = tsel ? dv : dk;
+      for (int m = 0; m < 4; ++m) {
+        const int rr = 4 * m + (ln >> 4);
+        x[m] = lds_ld16(est_lds + rr * 256 + 16 * (c ^ rr));
+      }
+    };
+    auto store_round = [&](u16* dst, int sh, const uint4 (&x)[4]) {
 #pragma unroll
-      for (int sh = 0; sh < 2; ++sh) {  // keys kw0 + 16 sh .. + 15
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        if ((l32 >> 4) == sh) {
-          const int rr = l32 & 15;
+      for (int m = 0; m < 4; ++m) {
+        const int key = key_of(sh, m);
+#if NA_NT_EXTRA & 4
+        if (key < T) st16_nt(dst + kbase + key * rsk + 8 * c, x[m]);
+#else
+        if (key < T) st16(dst + kbase + key * rsk + 8 * c, x[m]);
+#endif
+      }
+    };
+
+    if constexpr (!ROPE) {
+      issue_next();
 #pragma unroll
-          for (int db = 0; db < 4; ++db)
+      for (int tsel = 0; tsel < 2; ++tsel)  // dK, then dV
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-              const int e = 4 * g;
-              lds_st8(est_lds + rr * 256 + 16 * ((4 * db + g) ^ rr) + 8 * half,
-                      pack_bf16x2(acc[db][e] * sc, acc[db][e + 1] * sc),
-                      pack_bf16x2(acc[db][e + 2] * sc, acc[db][e + 3] * sc));
-            }
+        for (int sh = 0; sh < 2; ++sh) {
+          uint4 x[4];
+          stage_round(tsel ? dva : dka, tsel ? 1.f : scale, sh, x);
+          store_round(tsel ? dv : dk, sh, x);
         }
-        // lane i copies chunk i % 16 of rows 4 m + i / 16
+    } else {
+      // ROPE (and GATE): the rounds need global loads (raw key chunks with
+      // their angles; ve chunks and gate logits).  Vector memory operations
+      // retire in issue order, and the copies of issue_next are asm the
+      // compiler does not count, so a load issued behind a store or a copy
+      // would wait for them as well: each round's loads are issued before the
+      // previous round's stores, and issue_next follows the last of them.
+      auto rope_load = [&](int sh, int m) {
+        const int kr = min(key_of(sh, m), T - 1);
+        return rope_row_load(ra.raw + kbase + kr * rsk + 8 * c, ra, kr, c);
+      };
+      RopeRow rrow[4];
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const int rr = 4 * m + (lane >> 4), c = lane & 15;
-          uint4 x = lds_ld16(est_lds + rr * 256 + 16 * (c ^ rr));
-          const int key = kw0 + 16 * sh + rr;
-          if constexpr (ROPE) {  // whole 16-lane groups: key is uniform over one
-            if (tsel == 0) {
-              const int kr = min(key, T - 1);
-              RopeRow rw = rope_row_load(nullptr, ra, kr, c);
-              rw.x16 = xraw[ROPE ? 4 * sh + m : 0];
-              x = rope_bwd_chunk(x, rw, ra.eps, c);
+      for (int m = 0; m < 4; ++m) rrow[m] = rope_load(0, m);
+      uint4 x0[4], x1[4];
+      stage_round(dka, scale, 0, x0);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) x0[m] = rope_bwd_chunk(x0[m], rrow[m], ra.eps, c);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) rrow[m] = rope_load(1, m);
+      store_round(dk, 0, x0);
+      stage_round(dka, scale, 1, x1);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) x1[m] = rope_bwd_chunk(x1[m], rrow[m], ra.eps, c);
+      // GATE: the ve chunks and gate logits of the dV rows, loaded once the
+      // angles' registers are free; waited for (all but the 4 stores behind
+      // them) before the copies, which the wait would otherwise include
+      const size_t gbase = static_cast<size_t>(cur.b) * T * Hk + cur.hk;  // gate row of key 0
+      uint4 vev[GATE ? 8 : 1];
+      float glv[GATE ? 8 : 1];
+      if constexpr (GATE) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int kr = min(key_of(i >> 2, i & 3), T - 1);
+          vev[i] = ld16(gt.ve + kbase + kr * rsk + 8 * c);
+          glv[i] = bf16_to_f32(gt.gate[gbase + static_cast<size_t>(kr) * Hk]);
+        }
+      }
+      store_round(dk, 1, x1);
+      if constexpr (GATE) wait_vmem_but<4>();
+      issue_next();
+#pragma unroll
+      for (int sh = 0; sh < 2; ++sh) {
+        uint4 x[4];
+        stage_round(dva, 1.f, sh, x);
+        store_round(dv, sh, x);
+        if constexpr (GATE) {  // dv' chunks -> dve chunks and (lane c = 0) dg
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            const int key = key_of(sh, m), i = GATE ? 4 * sh + m : 0;
+            const float sg = __builtin_amdgcn_rcpf(1.f + fast_exp2(-glv[i] * kLog2e));
+            float xv[8], ev[8], y[8];
+            unpack8(x[m], xv);
+            unpack8(vev[i], ev);
+            float dot = 0.f;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+              y[j] = 3.f * sg * xv[j];
+              dot = fmaf(ev[j], xv[j], dot);
+            }
+            dot = sum16(dot);
+            if (key < T) {
+              st16(gt.dve + kbase + key * rsk + 8 * c, pack8(y));
+              if (c == 0)
+                gt.dgate[gbase + static_cast<size_t>(key) * Hk] =
+                    __builtin_bit_cast(u16, to_bf16(3.f * sg * (1.f - sg) * dot));
             }
           }
-#if NA_NT_EXTRA & 4
-          if (key < T) st16_nt(dst + kbase + key * rsk + 8 * c, x);
-#else
-          if (key < T) st16(dst + kbase + key * rsk + 8 * c, x);
-#endif
         }
       }
     }
@@ -1314,9 +1396,14 @@ hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const vo
                            const void* dout, const float* lse, void* dq, void* dk, void* dv,
                            float* delta, void* ws, int B, int T, int H, int Hk, int window,
                            hipStream_t s, hipEvent_t const* ev, const void* q_raw,
-                           const void* k_raw, const float* cos_t, const float* sin_t, float eps) {
+                           const void* k_raw, const float* cos_t, const float* sin_t, float eps,
+                           const void* ve, const void* gate, void* dve, void* dgate) {
   const bool rope = q_raw != nullptr;
+  const bool gated = ve != nullptr;
   if (rope && ws == nullptr) return hipErrorInvalidValue;  // checked on the host
+  if (gated && !rope) return hipErrorInvalidValue;         // the gate folds with the rope only
+  const GateBwd gt{static_cast<const u16*>(ve), static_cast<const u16*>(gate),
+                   static_cast<u16*>(dve), static_cast<u16*>(dgate)};
   const RopeBwd rq{static_cast<const u16*>(q_raw), cos_t, sin_t, eps};
   const RopeBwd rk{static_cast<const u16*>(k_raw), cos_t, sin_t, eps};
   const float scale = 1.0f / sqrtf(static_cast<float>(D));
@@ -1342,13 +1429,17 @@ hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const vo
   const int w = win ? window : T;
   const bool grp = Hk != H;
   auto* kv_kernel =
-      rope ? (win ? (grp ? dkdv_kernel<true, true, true> : dkdv_kernel<true, false, true>)
-                  : (grp ? dkdv_kernel<false, true, true> : dkdv_kernel<false, false, true>))
-           : (win ? (grp ? dkdv_kernel<true, true, false> : dkdv_kernel<true, false, false>)
-                  : (grp ? dkdv_kernel<false, true, false> : dkdv_kernel<false, false, false>));
+      gated
+          ? (win ? (grp ? dkdv_kernel<true, true, true, true> : dkdv_kernel<true, false, true, true>)
+                 : (grp ? dkdv_kernel<false, true, true, true>
+                        : dkdv_kernel<false, false, true, true>))
+      : rope ? (win ? (grp ? dkdv_kernel<true, true, true> : dkdv_kernel<true, false, true>)
+                    : (grp ? dkdv_kernel<false, true, true> : dkdv_kernel<false, false, true>))
+             : (win ? (grp ? dkdv_kernel<true, true, false> : dkdv_kernel<true, false, false>)
+                    : (grp ? dkdv_kernel<false, true, false> : dkdv_kernel<false, false, false>));
   e = launch(kv_kernel, kv_grid, dim3(256), 0, s, q16, k16,
              v16, g16, lse, static_cast<const float*>(delta), static_cast<u16*>(dk),
-             static_cast<u16*>(dv), dsw, nbt, B, T, H, Hk, c_log2, scale, w, rk);
+             static_cast<u16*>(dv), dsw, nbt, B, T, H, Hk, c_log2, scale, w, rk, gt);
   if (e != hipSuccess) return e;
   if ((e = mark(ev, 2, s)) != hipSuccess) return e;
   if (dsw != nullptr) {

@@ -81,6 +81,21 @@ __device__ __forceinline__ void st16_nt(void* p, uint4 v) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 
+// Eight bf16 values (16 bytes, element 2i in the low half of dword i) to fp32
+// and back (round to nearest even).
+__device__ __forceinline__ void unpack8(uint4 v, float (&x)[8]) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = __uint_as_float(w[i] << 16);
+    x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+__device__ __forceinline__ uint4 pack8(const float (&y)[8]) {
+  return make_uint4(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]), pack_bf16x2(y[4], y[5]),
+                    pack_bf16x2(y[6], y[7]));
+}
+
 // The row of a 32-key (or 32-query) block that lane l (mod 32) loads as the
 // A operand of the score MFMA, chosen so that accumulator element r of lane l
 // ends up holding block row 8*(l/32) + (r%8) + 16*(r/8).  That makes each

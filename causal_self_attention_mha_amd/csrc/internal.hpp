@@ -55,7 +55,9 @@ hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const vo
                            hipStream_t s, hipEvent_t const* ev = nullptr,
                            const void* q_raw = nullptr, const void* k_raw = nullptr,
                            const float* cos_t = nullptr, const float* sin_t = nullptr,
-                           float eps = 0.f);
+                           float eps = 0.f, const void* ve = nullptr,
+                           const void* gate = nullptr, void* dve = nullptr,
+                           void* dgate = nullptr);
 std::size_t bwd_workspace_bytes(int B, int T, int H);
 
 // bf16 append of T new key/value rows per sequence at cache rows

@@ -49,24 +49,10 @@ constexpr int kRowsAhead = 8;
 // Value of x in the lane 8 apart within the same 16-lane row (DPP row_ror:8).
 __device__ __forceinline__ float pair_lane(float x) { return dpp<0x128>(x); }
 
-__device__ __forceinline__ void unpack8(uint4 v, float (&x)[8]) {
-  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    x[2 * i] = __uint_as_float(w[i] << 16);
-    x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
-  }
-}
-
 // Sixteen-byte store that streams past the caches: the outputs are not read
 // again by this kernel (measured 4% faster than a plain store at d20).
 __device__ __forceinline__ void st16_stream(u16* p, uint4 v) {
   __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4*>(p));
-}
-
-__device__ __forceinline__ uint4 pack8(const float (&y)[8]) {
-  return make_uint4(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]), pack_bf16x2(y[4], y[5]),
-                    pack_bf16x2(y[6], y[7]));
 }
 
 // BWD = false: x -> y.  BWD = true: (x, dy) -> dx.  Rows r < H come from the

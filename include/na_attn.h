@@ -306,13 +306,19 @@ na_status na_value_gate_bwd(const void* ve, const void* gate, const void* dv_out
  * row's dz = R^T g, dx = r (dz - z mean(dz z)) applied in the epilogues that
  * write dq and dk, with positions t, tables fp32 (T_tab >= T, D/2)).
  * q, k: the rotated heads (the forward's inputs); q_raw, k_raw: the
- * prologue's inputs, same layouts.  The dS workspace is required.  Other
+ * prologue's inputs, same layouts.  The dS workspace is required.
+ * ve, gate, dve, dgate: all NULL, or all given when v is the value-embedding
+ * gate's output v' = v + 3 sigmoid(gate) ve (na_value_gate_fwd; blog
+ * section 1, value embeddings): then the kernel that writes dv (= dv') also
+ * writes dve and dgate, exactly what na_value_gate_bwd(ve, gate, dv) writes
+ * (ve, dve bf16 (B, T, H_kv, D); gate, dgate bf16 (B, T, H_kv)).  Other
  * arguments as in na_attn_bwd_gqa.
  */
 na_status na_attn_bwd_rope(const void* q, const void* k, const void* v, const void* o,
                            const void* dout, const float* lse, const void* q_raw,
                            const void* k_raw, const float* cos_tab, const float* sin_tab,
-                           int T_tab, float eps, void* dq, void* dk, void* dv, float* delta,
+                           int T_tab, float eps, const void* ve, const void* gate, void* dq,
+                           void* dk, void* dv, void* dve, void* dgate, float* delta,
                            void* workspace, size_t workspace_bytes, int B, int T, int H,
                            int H_kv, int D, int window, void* stream);
 

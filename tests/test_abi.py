@@ -230,10 +230,10 @@ def test_decode_append_checks_its_arguments(lib):
 def test_bwd_rope_checks_its_arguments(lib):
     p = [A + 0x100 * i for i in range(17)]
     need = lib.na_attn_bwd_workspace_bytes(1, 64, 2, 128)
-    # q k v o dout lse q_raw k_raw cos sin | dq dk dv delta ws
-    call = lambda ptrs=p, T_tab=64, ws=need, Hk=2: lib.na_attn_bwd_rope(  # noqa: E731
-        *ptrs[:10], T_tab, 1e-6, ptrs[10], ptrs[11], ptrs[12], ptrs[13], ptrs[14], ws, 1, 64, 2,
-        Hk, 128, -1, None)
+    # q k v o dout lse q_raw k_raw cos sin | dq dk dv delta ws | ve gate dve dgate
+    call = lambda ptrs=p, T_tab=64, ws=need, Hk=2, g=(None,) * 4: lib.na_attn_bwd_rope(  # noqa
+        *ptrs[:10], T_tab, 1e-6, g[0], g[1], ptrs[10], ptrs[11], ptrs[12], g[2], g[3], ptrs[13],
+        ptrs[14], ws, 1, 64, 2, Hk, 128, -1, None)
     assert call(T_tab=32) == INVALID and b"T_tab" in lib.na_last_error()
     assert call(ws=need - 1) == INVALID and b"workspace" in lib.na_last_error()
     bad = list(p)
@@ -243,6 +243,13 @@ def test_bwd_rope_checks_its_arguments(lib):
     bad[10] = bad[6]             # dq aliases q_raw
     assert call(bad) == INVALID
     assert call(Hk=3) == INVALID
+    gate = (A + 0x3000, A + 0x3100, A + 0x3200, A + 0x3300)
+    for j in range(4):           # the gate's four pointers: all or none
+        part = list(gate)
+        part[j] = None
+        assert call(g=tuple(part)) == INVALID and b"all four" in lib.na_last_error()
+    assert call(g=gate[:2] + (p[12], gate[3])) == INVALID  # dve aliases dv
+    assert call(g=gate[:3] + (gate[2],)) == INVALID       # dgate aliases dve
 
 
 def test_value_gate_checks_its_arguments(lib):
@@ -323,8 +330,8 @@ _NULL_CASES = [
     ("na_qk_norm_rope_bwd", lambda p: (*p[:8], None, 1, 8, 2, 2, 128, 16, 1e-6, None), range(8)),
     ("na_value_gate_fwd", lambda p: (*p[:4], 1, 8, 2, 128, None), range(4)),
     ("na_value_gate_bwd", lambda p: (*p[:5], 1, 8, 2, 128, None), range(5)),
-    ("na_attn_bwd_rope", lambda p: (*p[:10], 64, 1e-6, *p[10:15], 1 << 26, 1, 64, 2, 2, 128, -1,
-                                    None), range(15)),
+    ("na_attn_bwd_rope", lambda p: (*p[:10], 64, 1e-6, None, None, *p[10:13], None, None,
+                                    *p[13:15], 1 << 26, 1, 64, 2, 2, 128, -1, None), range(15)),
 ]
 
 

@@ -251,6 +251,50 @@ def test_bwd_with_prologue_folded_in(dev, B, T, H, Hk, Wn):
                  BF16_REL_L2, BF16_MAX_ABS)
 
 
+@pytest.mark.parametrize("B,T,H,Hk,Wn", [(2, 96, 2, 2, None), (2, 300, 4, 2, None),
+                                         (1, 257, 2, 2, 64)])
+def test_bwd_with_prologue_and_gate_folded_in(dev, B, T, H, Hk, Wn):
+    """na_attn_bwd_rope with the value-embedding gate folded in as well: the
+    attention ran on v' = v + 3 sigmoid(g) ve.  dq, dk, dv against the oracle
+    chain (prologue, gate -> attention -> backward -> prologue backward), dve
+    and dgate against the oracle's gate backward of the oracle dv, and bit for
+    bit against the separate gate backward kernel run on the folded dv (the
+    same bf16 dv, the same arithmetic)."""
+    import torch
+    import causal_self_attention_mha_amd as na
+    tr = W.make_train_inputs("d20", B=B, T=T, H=H, seed=990 + T)
+    kv = lambda a: np.ascontiguousarray(a[:, :, :Hk])  # noqa: E731
+    g, g_st = W.make_gate_logits(B, T, Hk, seed=91 + T)
+    c, s = tables("rope", T, 0)
+    q_raw, k_raw = to_device(tr.q_store, dev), to_device(kv(tr.k_store), dev)
+    v_in, do = to_device(kv(tr.v_store), dev), to_device(tr.do_store, dev)
+    ve, gd = to_device(kv(tr.k_store[:, ::-1]), dev), to_device(g_st, dev)
+    ct, sn = torch.from_numpy(c).to(dev), torch.from_numpy(s).to(dev)
+    qr, kr = na.qk_norm_rope_fwd(q_raw, k_raw, ct, sn)
+    v = na.value_gate_fwd(v_in, ve, gd)
+    o, lse = na.attn_fwd(qr, kr, v, window=Wn)
+    dq, dk, dv, dve, dg = na.attn_bwd(qr, kr, v, o, do, lse, window=Wn,
+                                      rope=(q_raw, k_raw, ct, sn), value_gate=(ve, gd))
+    dve2, dg2 = na.value_gate_bwd(ve, gd, dv)
+    torch.cuda.synchronize()
+    assert torch.equal(dve, dve2) and torch.equal(dg, dg2)
+    c64, s64 = c.astype(np.float64), s.astype(np.float64)
+    xq, xk = tr.q.astype(np.float64), kv(tr.k).astype(np.float64)
+    ve64 = kv(tr.k[:, ::-1]).astype(np.float64)
+    rq = oracle.qk_norm_rope_forward(xq, c64, s64, EPS)
+    rk = oracle.qk_norm_rope_forward(xk, c64, s64, EPS)
+    rv = oracle.value_gate_forward(kv(tr.v), ve64, g)
+    rdq, rdk, rdv, _ = oracle.backward(rq, rk, rv, tr.do, window=Wn)
+    assert_close("dv", to_host(dv), rdv, BF16_REL_L2, BF16_MAX_ABS)
+    assert_close("dq", to_host(dq), oracle.qk_norm_rope_backward(xq, rdq, c64, s64, EPS),
+                 BF16_REL_L2, BF16_MAX_ABS)
+    assert_close("dk", to_host(dk), oracle.qk_norm_rope_backward(xk, rdk, c64, s64, EPS),
+                 BF16_REL_L2, BF16_MAX_ABS)
+    rdve, rdg = oracle.value_gate_backward(ve64, g, rdv)
+    assert_close("dve", to_host(dve), rdve, BF16_REL_L2, BF16_MAX_ABS)
+    assert_close("dgate", to_host(dg), rdg, BF16_REL_L2, BF16_MAX_ABS)
+
+
 def test_bwd_with_prologue_folded_in_d20_sampled(dev):
     """The d20 shape: the folded backward against the two-step GPU path (full
     tensors, bf16 bound) and against the oracle chain on sampled heads."""
@@ -267,7 +311,16 @@ def test_bwd_with_prologue_folded_in_d20_sampled(dev):
     dq, dk, dv = na.attn_bwd(qr, kr, v, o, do, lse, rope=(q_raw, k_raw, ct, sn))
     dq2r, dk2r, _ = na.attn_bwd(qr, kr, v, o, do, lse)
     dq2, dk2 = na.qk_norm_rope_bwd(q_raw, k_raw, dq2r, dk2r, ct, sn)
+    # the value gate folded in too (v standing in for the gate's output): the
+    # same dq, dk, dv, and the separate gate backward's dve, dgate bit for bit
+    ve = torch.flip(k_raw, dims=(1,)).contiguous()
+    gd = to_device(W.make_gate_logits(B, T, H, seed=22)[1], dev)
+    dq3, dk3, dv3, dve3, dg3 = na.attn_bwd(qr, kr, v, o, do, lse, rope=(q_raw, k_raw, ct, sn),
+                                           value_gate=(ve, gd))
+    dve4, dg4 = na.value_gate_bwd(ve, gd, dv)
     torch.cuda.synchronize()
+    assert torch.equal(dq3, dq) and torch.equal(dk3, dk) and torch.equal(dv3, dv)
+    assert torch.equal(dve3, dve4) and torch.equal(dg3, dg4)
     assert_close("dq vs two-step", to_host(dq), to_host(dq2), BF16_REL_L2, BF16_MAX_ABS)
     assert_close("dk vs two-step", to_host(dk), to_host(dk2), BF16_REL_L2, BF16_MAX_ABS)
     c64, s64 = c.astype(np.float64), s.astype(np.float64)
