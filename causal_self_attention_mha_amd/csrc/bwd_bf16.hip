@@ -1346,8 +1346,8 @@ __global__ __launch_bounds__(64 * DG_WAVES, 8 / DG_WAVES) void dq_gemm_kernel(co
     // lanes store one 256-byte row (chunk c of staged row r at c ^ r).
     // ROPE: the raw query rows' gradient is formed from the staged bf16
     // gradient chunk (rope_bwd_chunk); the raw chunk and angles of the first
-    // four rows a lane group finishes are loaded before the staging, each of
-    // the next four as soon as its registers are free.
+    // four rows a lane group finishes are loaded before the staging, those of
+    // the next four once the first four are used.
     if constexpr (ROPE) {
 #pragma unroll
       for (int m = 0; m < 4; ++m) rrow[m] = rope_load(0, m);
@@ -1368,18 +1368,29 @@ __global__ __launch_bounds__(64 * DG_WAVES, 8 / DG_WAVES) void dq_gemm_kernel(co
         }
     }
     asm volatile("" ::: "memory");  // the reads below follow the writes above
+    // Round sh: lane i holds chunk i % 16 of row 4 m + i / 16 in x[m].  Vector
+    // memory operations retire in issue order, so round 1's loads go out
+    // before round 0's stores (a load behind a store would wait for it).
 #pragma unroll
     for (int sh = 0; sh < 2; ++sh) {  // queries qw0 + 16 sh .. + 15
+      uint4 x[4];
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {  // lane i: chunk i % 16 of row 4 m + i / 16
-        const int rr = 4 * m + gi, c = i16;
-        uint4 x = lds_ld16(st_lds + sh * kStage + rr * 256 + 16 * (c ^ rr));
-        const int qr = qw0 + 16 * sh + rr;
-        if constexpr (ROPE) {  // whole 16-lane groups: qr is uniform over one
-          x = rope_bwd_chunk(x, rrow[ROPE ? m : 0], ra.eps, c);
-          if (sh == 0) rrow[ROPE ? m : 0] = rope_load(1, m);
+      for (int m = 0; m < 4; ++m) {
+        const int rr = 4 * m + gi;
+        x[m] = lds_ld16(st_lds + sh * kStage + rr * 256 + 16 * (i16 ^ rr));
+        if constexpr (ROPE)  // whole 16-lane groups: the row is uniform over one
+          x[m] = rope_bwd_chunk(x[m], rrow[ROPE ? m : 0], ra.eps, i16);
+      }
+      if constexpr (ROPE) {
+        if (sh == 0) {
+#pragma unroll
+          for (int m = 0; m < 4; ++m) rrow[m] = rope_load(1, m);
         }
-        if (qr < T) st16(dq + base + static_cast<size_t>(qr) * rs + 8 * c, x);
+      }
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const int qr = qw0 + 16 * sh + 4 * m + gi;
+        if (qr < T) st16(dq + base + static_cast<size_t>(qr) * rs + 8 * i16, x[m]);
       }
     }
   }
