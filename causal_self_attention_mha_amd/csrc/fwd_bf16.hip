@@ -21,8 +21,14 @@
 //     lane-local apart from one exchange with lane l^32;
 //   * the output is accumulated transposed too, O^T += V^T P^T, so the per-row
 //     rescale factor is also lane-local;
-//   * the softmax runs in the exp2 domain on raw scores: p = 2^(c z - c m)
-//     with c = s log2(e), one FMA and one v_exp_f32 per score;
+//   * the softmax runs in the exp2 domain: p = 2^(c z - c m) with c =
+//     s log2(e).  In the training forward (no window, no prefill) Q is
+//     pre-scaled by c and rounded to bf16 (as the dK/dV pass does with K) and
+//     the score chains start from -m (the MFMA's accumulator input), so a
+//     score costs one v_exp_f32 and nothing else: m is set by a wavefront's
+//     first tile and raised only when a lane's probability sum over a tile
+//     reaches 2^31; the other instantiations take one FMA per score against
+//     a running max raised lazily;
 //   * the 32 LDS operand reads of a tile are issued in a fixed order four
 //     operands ahead of the MFMA that consumes them, the last K MFMAs
 //     overlapping the first V reads, which in turn stay in flight during the
@@ -54,6 +60,9 @@ constexpr uint32_t BUF_B = 2 * kTileBytes;  // one buffer: K tile, then V tile
 // new score exceeds it by more than 2^8 in the exp2 domain, so most tiles skip
 // the rescale; probabilities then stay below 256, harmless in fp32 and bf16.
 constexpr float kRescaleLog2 = 8.0f;
+// The training forward's offset m is raised only when a lane's probability
+// sum over one tile reaches this (every probability then stays below it).
+constexpr float kSumLimit = 2147483648.0f;  // 2^31
 
 // WIN: sliding window, key j visible to query i iff i - win <= j <= i (the
 // plain causal kernel is WIN = false).
@@ -105,11 +114,19 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(
   // Q^T operand: lane holds q[qw0 + l32][16 kc + 8 half + 0..7], kc = 0..7.
   // Rows past T (their outputs are discarded) read row T-1 instead.
   const int qrow = qw0 + l32;
+  // the training forward: Q pre-scaled, score chains seeded with -m (see above)
+  constexpr bool DIET = !WIN && !PRE;
   bf16x8 qreg[8];
   {
     const u16* qp = q + base + min(qrow, T - 1) * rs + 8 * half;
 #pragma unroll
     for (int kc = 0; kc < 8; ++kc) qreg[kc] = as_bf16x8(ld16(qp + 16 * kc));
+  }
+  if constexpr (DIET) {
+#pragma unroll
+    for (int kc = 0; kc < 8; ++kc)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qreg[kc][e] = to_bf16(static_cast<float>(qreg[kc][e]) * c_log2);
   }
   if constexpr (ROPE) {
     // the lane holds elements 16 kc + 8 half + e of its row; element i < 64
@@ -149,9 +166,14 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(
   f32x16 oacc[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) oacc[i] = f32x16{};
-  float m = -INFINITY;  // running max of raw scores for row qrow
+  float m = -INFINITY;  // running max of raw scores for row qrow (DIET: the
+                        // offset of the scaled scores, set by the first tile)
   float lpart = 0.f;    // running sum over this lane's half of the keys
   const float thr = kRescaleLog2 / c_log2;
+  f32x16 ofs;  // DIET: -m in every element, the score chains' initial value
+#pragma unroll
+  for (int e = 0; e < 16; ++e) ofs[e] = 0.f;
+  bool mset = false;  // DIET: m set (wavefront-uniform: a wavefront's rows share their tiles)
 
   const int last_q = L + min(q0 + BQ, T) - 1;  // position of the last query row
   const int n_kt = last_q / BK + 1;  // key tiles at or left of the diagonal
@@ -222,7 +244,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(
 #pragma unroll
     for (int n = 0; n < 16; ++n) {
       read(n + AHEAD);
-      sacc[n & 1] = mfma32(opnd[n], qreg[n >> 1], sacc[n & 1]);
+      sacc[n & 1] = mfma32(opnd[n], qreg[n >> 1], (DIET && n < 2) ? ofs : sacc[n & 1]);
       __builtin_amdgcn_sched_barrier(0);
     }
     if (kt + 1 < n_kt) issue(kt + 1, 1 - BUF);
@@ -240,39 +262,88 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(
         }
     }
 
-    float mx = -INFINITY;
+    // the largest of this lane's scores, shared with lane l ^ 32 (same row)
+    auto tile_max = [&]() {
+      float mx = -INFINITY;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    if (__any(mx > m + thr)) {  // wavefront-uniform
-      const float m_new = fmaxf(m, mx);
-      // 0 on the first tile; with a window, a row whose keys so far all lie
-      // before its window keeps m = -inf (and l = 0, O = 0): any finite factor
-      const float alpha =
-          (WIN && m_new == -INFINITY) ? 0.f : fast_exp2((m - m_new) * c_log2);
-      lpart *= alpha;
-#pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-      m = m_new;
-    }
-    // a row whose keys so far all lie before its window (WIN only) still has
-    // m = -inf: its probabilities are exp2(-inf) = 0, not exp2(-inf + inf)
-    const float neg = (WIN && m == -INFINITY) ? 0.f : -m * c_log2;
-
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
+      return fmaxf(mx, __shfl_xor(mx, 32, 64));
+    };
     // P^T as bf16 MFMA B operands: chunk c (16 keys) = sacc[c/2][8(c%2) .. +7]
     bf16x8 pb[4];
     float psum = 0.f;
+    if constexpr (DIET) {
+      // sacc holds c z - m (c z on the wavefront's first tile, which sets m)
+      if (!mset) {
+        m = tile_max();  // finite: every row sees key 0 in its first tile
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float p = fast_exp2(fmaf(sacc[c >> 1][8 * (c & 1) + i], c_log2, neg));
-        psum += p;
-        pb[c][i] = to_bf16(p);
+          for (int r = 0; r < 16; ++r) sacc[kb][r] -= m;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) ofs[e] = -m;
+        mset = true;
+      }
+      auto probs = [&](float sh) {  // p = 2^(sacc - sh)
+        psum = 0.f;
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const float p = fast_exp2(sacc[c >> 1][8 * (c & 1) + i] - sh);
+            psum += p;
+            pb[c][i] = to_bf16(p);
+          }
+      };
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float p = fast_exp2(sacc[c >> 1][8 * (c & 1) + i]);
+          psum += p;
+          pb[c][i] = to_bf16(p);
+        }
+      if (__any(!(psum < kSumLimit))) {  // rare: scores far above m (wavefront-uniform)
+        const float dm = fmaxf(tile_max(), 0.f);
+        const float alpha = fast_exp2(-dm);
+        lpart *= alpha;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+        m += dm;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) ofs[e] = -m;
+        probs(dm);
+      }
+    } else {
+      const float mx = tile_max();
+      if (__any(mx > m + thr)) {  // wavefront-uniform
+        const float m_new = fmaxf(m, mx);
+        // 0 on the first tile; with a window, a row whose keys so far all lie
+        // before its window keeps m = -inf (and l = 0, O = 0): any finite factor
+        const float alpha =
+            (WIN && m_new == -INFINITY) ? 0.f : fast_exp2((m - m_new) * c_log2);
+        lpart *= alpha;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+        m = m_new;
+      }
+      // a row whose keys so far all lie before its window (WIN only) still has
+      // m = -inf: its probabilities are exp2(-inf) = 0, not exp2(-inf + inf)
+      const float neg = (WIN && m == -INFINITY) ? 0.f : -m * c_log2;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float p = fast_exp2(fmaf(sacc[c >> 1][8 * (c & 1) + i], c_log2, neg));
+          psum += p;
+          pb[c][i] = to_bf16(p);
+        }
       }
     }
     lpart += psum;
@@ -308,7 +379,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(
         *reinterpret_cast<uint2*>(op + 32 * db + 8 * g + 4 * half) = pk;
       }
     if (half == 0 && (!PRE || lse != nullptr))
-      lse[static_cast<size_t>(bh) * T + qrow] = m * scale + logf(l);
+      lse[static_cast<size_t>(bh) * T + qrow] =
+          DIET ? (m + __log2f(l)) * 0.6931471805599453f : m * scale + logf(l);
   }
 }
 
