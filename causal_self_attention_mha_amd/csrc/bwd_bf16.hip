@@ -261,10 +261,15 @@ __device__ __forceinline__ void dkdv_scores(const uint32_t (&na)[8], int row0, u
   asm volatile("s_nop 15" : "+v"(sacc), "+v"(pacc));
 }
 
-// dS of one 32-query x 32-key block, kept for the dQ GEMM: stored as a
-// 32 x 32 bf16 matrix [key][query] (row = this lane's key, 8 queries per
-// 16-byte store).  Blocks of a head are packed lower-triangularly: block
-// (qblk, kblk), kblk <= qblk, at index qblk (qblk + 1) / 2 + kblk.
+// dS of one 32-query x 32-key block, kept for the dQ GEMM: 1024 bf16, the
+// element of key k and query q = 16 j + 8 h + e (e < 8) at 512 j + 16 k + 8 h
+// + e, so that a lane's two 16-byte stores (its key, 8 queries each) go to two
+// contiguous KiB, one per store instruction.  Stored as a [key][query] matrix,
+// each instruction wrote 32-byte pieces 64 bytes apart; the contiguous order
+// took the d20 dK/dV pass from 877 to 864 us, and the dQ GEMM, whose copies
+// gather each block back into [key][query] order in LDS from two 512-byte
+// runs, from 318 to 322 us.  Blocks of a head are packed lower-triangularly:
+// block (qblk, kblk), kblk <= qblk, at index qblk (qblk + 1) / 2 + kblk.
 __device__ __forceinline__ size_t ds_block_index(int bh, int nbt, int qblk, int kblk) {
   return (static_cast<size_t>(bh) * nbt + qblk * (qblk + 1) / 2 + kblk) * 1024;
 }
@@ -278,12 +283,13 @@ __device__ __forceinline__ size_t ds_block_index(int bh, int nbt, int qblk, int 
 #endif
 __device__ __forceinline__ void store_ds(u16* blk, const bf16x8 (&sb)[2], int lane) {
   const int l32 = lane & 31, half = lane >> 5;
+  // lane: key l32; sb[j]: queries 16 j + 8 half + 0..7
   if constexpr ((NA_DS_NT & 2) != 0) {
-    st16_nt(blk + l32 * 32 + 8 * half, __builtin_bit_cast(uint4, sb[0]));
-    st16_nt(blk + l32 * 32 + 16 + 8 * half, __builtin_bit_cast(uint4, sb[1]));
+    st16_nt(blk + 16 * l32 + 8 * half, __builtin_bit_cast(uint4, sb[0]));
+    st16_nt(blk + 512 + 16 * l32 + 8 * half, __builtin_bit_cast(uint4, sb[1]));
   } else {
-    st16(blk + l32 * 32 + 8 * half, __builtin_bit_cast(uint4, sb[0]));
-    st16(blk + l32 * 32 + 16 + 8 * half, __builtin_bit_cast(uint4, sb[1]));
+    st16(blk + 8 * (32 * half + l32), __builtin_bit_cast(uint4, sb[0]));
+    st16(blk + 512 + 8 * (32 * half + l32), __builtin_bit_cast(uint4, sb[1]));
   }
 }
 
@@ -1149,8 +1155,8 @@ __global__ __launch_bounds__(256, 1) void dq_kernel(
 //   dQ^T += K^T dS^T   (A = K tile read transposed, B = dS^T)
 // Both operands need eight consecutive keys per lane: K^T comes from the
 // swizzled K tile with ds_read_b64_tr_b16 (as V^T in the forward), and dS^T
-// from the stored [key][query] block, copied as is into LDS and read with the
-// same transposing instruction (lanes supplying rows key0 + i/4 at columns
+// from the stored block, gathered into [key][query] order in LDS by the copies
+// (store_ds) and read with the same transposing instruction (lanes supplying rows key0 + i/4 at columns
 // 4 (i%4) leave lane j with column query0 + j of keys key0 .. key0 + 3).  K
 // tiles (by the whole workgroup) and each wavefront's dS blocks (by that
 // wavefront) are copied HBM -> LDS by DMA, one barrier per key tile.  The dS
@@ -1240,7 +1246,7 @@ __global__ __launch_bounds__(64 * DG_WAVES, 8 / DG_WAVES) void dq_gemm_kernel(co
       tr_addr(lds_addr(ktile), ofs, ktr);
     }
     // dS^T reads: 16-lane group gi supplies keys 16 c + 8 half + 4 sub + i16 / 4,
-    // queries 16 (gi & 1) + 4 (i16 & 3) of a block stored [key][query]
+    // queries 16 (gi & 1) + 4 (i16 & 3) of a block in [key][query] order
     const uint32_t st_lds = lds_addr(&sst[0][wave][0]);
     const uint32_t st_off =
         ((8 * half + (i16 >> 2)) * 32 + 16 * (gi & 1) + 4 * (i16 & 3)) * 2;
@@ -1261,14 +1267,18 @@ __global__ __launch_bounds__(64 * DG_WAVES, 8 / DG_WAVES) void dq_gemm_kernel(co
             kvoff + 4 * DG_WAVES * j * rsb,
             kt_lds + buf * kTileBytes + 1024 * (wave + DG_WAVES * j));
     };
+    // LDS chunk j (0..3) of a key tile's dS: block kb = j / 2 as a [key][query]
+    // matrix, keys 16 (j % 2) .. + 15; lane L writes key 16 (j % 2) + L / 4,
+    // queries 8 (L % 4) .. + 7, which it gathers from the stored order
+    // (store_ds: query chunk (L % 4) / 2 at 1024 bytes apart, half L % 2)
+    const uint32_t ds_gather = 1024 * ((lane & 3) >> 1) + 32 * (lane >> 2) + 16 * (lane & 1);
     auto issue_ds = [&](int kt, int sbuf, int j) {
       // blocks past qblk are past the resource's end (zeros, never read)
+      const uint32_t src = kt * 4096 + (j >> 1) * 2048 + (j & 1) * 512 + ds_gather;
       if constexpr ((NA_DS_NT & 1) != 0)
-        dma16_nt(ds_rsrc, kt * 4096 + j * 1024 + 16 * lane,
-                 st_lds + sbuf * (DG_WAVES * DG_DS_B) + j * 1024);
+        dma16_nt(ds_rsrc, src, st_lds + sbuf * (DG_WAVES * DG_DS_B) + j * 1024);
       else
-        dma16(ds_rsrc, kt * 4096 + j * 1024 + 16 * lane,
-              st_lds + sbuf * (DG_WAVES * DG_DS_B) + j * 1024);
+        dma16(ds_rsrc, src, st_lds + sbuf * (DG_WAVES * DG_DS_B) + j * 1024);
     };
 
     // Copies in issue order: K(0), dS(0), dS(1), then per tile t: K(t+1),
