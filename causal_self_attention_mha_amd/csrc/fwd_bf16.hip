@@ -366,18 +366,34 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(
   }
 
   const float l = lpart + __shfl_xor(lpart, 32, 64);
-  if (qrow < T) {
+  // The rows leave through this wavefront's 8 KiB of the K/V buffers (free
+  // once every wavefront is past its last tile), so that 16 lanes store one
+  // 256-byte row (chunk c of row r at c ^ (r % 16)); stored straight from the
+  // accumulators, every lane wrote 8 bytes to a different row (d20 forward
+  // 394 -> 388 us).
+  wait_lds();
+  __syncthreads();
+  {
     const float inv = 1.f / l;
-    u16* op = o + base + qrow * rs;
+    const uint32_t stg = kv_lds + wave * 8192;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         // elements 4g..4g+3 are d = 32 db + 8 g + 4 half + 0..3
-        uint2 pk = make_uint2(pack_bf16x2(oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv),
-                              pack_bf16x2(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv));
-        *reinterpret_cast<uint2*>(op + 32 * db + 8 * g + 4 * half) = pk;
+        lds_st8(stg + l32 * 256 + 16 * ((4 * db + g) ^ (l32 & 15)) + 8 * half,
+                pack_bf16x2(oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv),
+                pack_bf16x2(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv));
       }
+    asm volatile("" ::: "memory");  // the reads below follow the writes above
+#pragma unroll
+    for (int mm = 0; mm < 8; ++mm) {  // lane i: chunk i % 16 of row 4 mm + i / 16
+      const int rr = 4 * mm + (lane >> 4), c = lane & 15;
+      const uint4 x = lds_ld16(stg + rr * 256 + 16 * (c ^ (rr & 15)));
+      if (qw0 + rr < T) st16(o + base + static_cast<size_t>(qw0 + rr) * rs + 8 * c, x);
+    }
+  }
+  if (qrow < T) {
     if (half == 0 && (!PRE || lse != nullptr))
       lse[static_cast<size_t>(bh) * T + qrow] =
           DIET ? (m + __log2f(l)) * 0.6931471805599453f : m * scale + logf(l);
