@@ -111,6 +111,25 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(
   const size_t kbase =
       static_cast<size_t>(b) * (PRE ? Tc : T) * rsk + static_cast<size_t>(hk) * D;
 
+  const int last_q = L + min(q0 + BQ, T) - 1;  // position of the last query row
+  const int n_kt = last_q / BK + 1;  // key tiles at or left of the diagonal
+  // first key tile that any row of the workgroup sees (0 without a window)
+  const int kt_lo = WIN ? max(L + q0 - win, 0) / BK : 0;
+  const uint32_t kv_lds = lds_addr(kvs);
+  const uint32_t rsb = static_cast<uint32_t>(rsk) * 2;
+  const uint32_t cvoff = tile_copy_offset(wave, lane, rsb);
+  auto issue = [&](int kt, int buf) {  // K, V tile kt -> buffer buf; keys past nk read as 0
+    const int k0 = kt * BK;
+    const uint32_t nrec = static_cast<uint32_t>(nk - k0) * rsb;
+    const size_t off = kbase + static_cast<size_t>(k0) * rsk;
+    copy_tile<NW>(buffer_rsrc(k + off, nrec), cvoff, rsb, kv_lds + buf * BUF_B, wave);
+    copy_tile<NW>(buffer_rsrc(v + off, nrec), cvoff, rsb, kv_lds + buf * BUF_B + kTileBytes,
+                  wave);
+  };
+  // the first K/V tile's copy goes out before the Q loads, whose use (the
+  // pre-scale, the prologue) would otherwise hold it back
+  issue(kt_lo, 0);
+
   // Q^T operand: lane holds q[qw0 + l32][16 kc + 8 half + 0..7], kc = 0..7.
   // Rows past T (their outputs are discarded) read row T-1 instead.
   const int qrow = qw0 + l32;
@@ -175,29 +194,14 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(
   for (int e = 0; e < 16; ++e) ofs[e] = 0.f;
   bool mset = false;  // DIET: m set (wavefront-uniform: a wavefront's rows share their tiles)
 
-  const int last_q = L + min(q0 + BQ, T) - 1;  // position of the last query row
-  const int n_kt = last_q / BK + 1;  // key tiles at or left of the diagonal
-  // first key tile that any row of the workgroup sees (0 without a window)
-  const int kt_lo = WIN ? max(L + q0 - win, 0) / BK : 0;
 
   // operand read addresses in buffer 0 (buffer 1: + BUF_B, V tile: + kTileBytes)
-  const uint32_t kv_lds = lds_addr(kvs);
   TileAddr ta;
   {
     const TileOffsets ofs = tile_operand_offsets(lane);
     nat_addr(kv_lds, ofs, ta.nat);
     tr_addr(kv_lds + kTileBytes, ofs, ta.tr);
   }
-  const uint32_t rsb = static_cast<uint32_t>(rsk) * 2;
-  const uint32_t cvoff = tile_copy_offset(wave, lane, rsb);
-  auto issue = [&](int kt, int buf) {  // K, V tile kt -> buffer buf; keys past nk read as 0
-    const int k0 = kt * BK;
-    const uint32_t nrec = static_cast<uint32_t>(nk - k0) * rsb;
-    const size_t off = kbase + static_cast<size_t>(k0) * rsk;
-    copy_tile<NW>(buffer_rsrc(k + off, nrec), cvoff, rsb, kv_lds + buf * BUF_B, wave);
-    copy_tile<NW>(buffer_rsrc(v + off, nrec), cvoff, rsb, kv_lds + buf * BUF_B + kTileBytes,
-                  wave);
-  };
 
   // One key tile; BUF is the buffer it sits in (a compile-time constant, so
   // that every LDS read address is a register plus an immediate).
@@ -359,7 +363,6 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(
     }
   };
 
-  issue(kt_lo, 0);
   for (int kt = kt_lo; kt < n_kt; kt += 2) {
     tile(std::integral_constant<uint32_t, 0>{}, kt);
     if (kt + 1 < n_kt) tile(std::integral_constant<uint32_t, 1>{}, kt + 1);
