@@ -235,7 +235,8 @@ def cpu_baseline(inp, n_heads, dinp=None, n_seqs=0):
 
 def sample_sclk(run_load, seconds, period=0.002):
     """Sample the current shader clock (the starred line of the amdgpu driver's
-    pp_dpm_sclk file) while run_load(stop_event) keeps the GPU busy."""
+    pp_dpm_sclk file) and the board power (its hwmon power1_input, microwatts,
+    beside the power1_cap limit) while run_load() keeps the GPU busy."""
     import glob
     import re
     import threading
@@ -243,11 +244,29 @@ def sample_sclk(run_load, seconds, period=0.002):
     if not paths:
         return {"source": None, "note": "no pp_dpm_sclk file readable"}
     samples = {p: [] for p in paths}
+    power = {p: [] for p in paths}
+
+    def hwmon_file(p, name):
+        found = sorted(glob.glob(os.path.join(os.path.dirname(p), "hwmon", "hwmon*", name)))
+        return found[0] if found else None
+
+    pin = {p: hwmon_file(p, "power1_input") for p in paths}
     stop = threading.Event()
+
+    def read_int(path):
+        try:
+            with open(path) as fh:
+                return int(fh.read().strip())
+        except (OSError, ValueError):
+            return None
 
     def sampler():
         while not stop.is_set():
             for p in paths:
+                if pin[p]:
+                    w = read_int(pin[p])
+                    if w is not None:
+                        power[p].append(w / 1e6)
                 try:
                     with open(p) as fh:
                         for line in fh:
@@ -271,10 +290,21 @@ def sample_sclk(run_load, seconds, period=0.002):
     v = np.array(samples[p], dtype=np.float64)
     if v.size == 0:
         return {"source": p, "note": "no samples"}
-    return {"source": p, "samples": int(v.size), "seconds": seconds,
-            "median_MHz": float(np.median(v)), "mean_MHz": round(float(v.mean()), 1),
-            "min_MHz": float(v.min()), "max_MHz": float(v.max()),
-            "p10_MHz": float(np.percentile(v, 10)), "p90_MHz": float(np.percentile(v, 90))}
+    res = {"source": p, "samples": int(v.size), "seconds": seconds,
+           "median_MHz": float(np.median(v)), "mean_MHz": round(float(v.mean()), 1),
+           "min_MHz": float(v.min()), "max_MHz": float(v.max()),
+           "p10_MHz": float(np.percentile(v, 10)), "p90_MHz": float(np.percentile(v, 90))}
+    if power[p]:
+        w = np.array(power[p], dtype=np.float64)
+        cap = hwmon_file(p, "power1_cap")
+        cap_w = read_int(cap) if cap else None
+        res["power"] = {"source": pin[p], "samples": int(w.size),
+                        "median_W": round(float(np.median(w)), 1),
+                        "p10_W": round(float(np.percentile(w, 10)), 1),
+                        "p90_W": round(float(np.percentile(w, 90)), 1),
+                        "max_W": round(float(w.max()), 1),
+                        "cap_W": round(cap_w / 1e6, 1) if cap_w else None}
+    return res
 
 
 def main():

@@ -65,3 +65,23 @@ def test_sclk_sampler_reads_the_starred_level(tmp_path, monkeypatch):
     assert res["median_MHz"] == 2024.0 and res["min_MHz"] == res["max_MHz"] == 2024.0
     monkeypatch.setattr(glob, "glob", lambda pattern: [])
     assert bench.sample_sclk(lambda: None, 0.01)["source"] is None
+
+
+def test_sclk_sampler_reports_board_power_and_cap(tmp_path, monkeypatch):
+    """Beside the clock, the sampler reads the card's hwmon power1_input
+    (microwatts) and reports it in watts with the power1_cap limit."""
+    import glob
+    real_glob = glob.glob
+    dev = tmp_path / "card0" / "device"
+    hw = dev / "hwmon" / "hwmon3"
+    hw.mkdir(parents=True)
+    (dev / "pp_dpm_sclk").write_text("0: 500Mhz\n1: 2100Mhz *\n")
+    (hw / "power1_input").write_text("1350000000\n")
+    (hw / "power1_cap").write_text("1400000000\n")
+    monkeypatch.setattr(glob, "glob", lambda pattern: [str(dev / "pp_dpm_sclk")]
+                        if pattern.startswith("/sys/class/drm") else real_glob(pattern))
+    res = bench.sample_sclk(lambda: __import__("time").sleep(0.005), 0.05)
+    assert res["median_MHz"] == 2100.0
+    pw = res["power"]
+    assert pw["source"] == str(hw / "power1_input") and pw["samples"] >= 1
+    assert pw["median_W"] == pw["max_W"] == 1350.0 and pw["cap_W"] == 1400.0
