@@ -44,7 +44,9 @@ key/value heads) is timed and reported under "prologue" (algorithmic bytes:
 every tensor read or written once, plus the cos/sin tables), and so is the
 d20 step with the whole prologue (its forward kernels, the attention forward
 and backward, and the prologue's backward either as its own two kernels or
-folded into the attention backward: "d20_step_with_prologue_ms").
+folded into the attention backward; and with the query rows' normalisation
+and rotation folded into the attention forward as well, "folded_fwd_bwd":
+"d20_step_with_prologue_ms").
 
 Grouped-query attention (--kv-heads, default 5: two query heads per key/value
 head, a choice of this benchmark; the pages give no key/value head count) is
@@ -759,10 +761,16 @@ def main():
         tdq, tdk, tdv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
         vg, tdve, tdg = torch.empty_like(v), torch.empty_like(v), torch.empty_like(gt)
 
-        def pro_step(folded):
-            rfwd()  # yq, yk = rotated q, k
+        def pro_step(folded, folded_fwd=False):
             st = lib.na_value_gate_fwd(ptr(v), ptr(k), ptr(gt), ptr(vg), B, T, H, D, P(stream))
-            if not st:
+            if st:
+                raise RuntimeError(lib.na_last_error().decode())
+            if folded_fwd:  # keys by the prologue kernel, queries rotated in the forward
+                st = lib.na_attn_fwd_rope(ptr(q), ptr(k), ptr(vg), ptr(ct), ptr(sn), T, eps,
+                                          ptr(yq), ptr(yk), ptr(o), ptr(lse), B, T, H, H, D, -1,
+                                          P(stream))
+            else:
+                rfwd()  # yq, yk = rotated q, k
                 st = lib.na_attn_fwd(ptr(yq), ptr(yk), ptr(vg), ptr(o), ptr(lse), B, T, H, D,
                                      P(stream))
             if st:
@@ -788,14 +796,15 @@ def main():
                 raise RuntimeError(lib.na_last_error().decode())
 
         step_ms = {}
-        for name, folded in (("folded_bwd", True), ("separate_bwd", False)):
-            ramp(lambda: pro_step(folded))
+        for name, folded, ffwd in (("folded_bwd", True, False), ("separate_bwd", False, False),
+                                   ("folded_fwd_bwd", True, True)):
+            ramp(lambda: pro_step(folded, ffwd))
             for _ in range(args.warmup):
-                pro_step(folded)
+                pro_step(folded, ffwd)
             torch.cuda.synchronize()
             ev.record(rev[0], stream)
             for _ in range(args.steps):
-                pro_step(folded)
+                pro_step(folded, ffwd)
             ev.record(rev[1], stream)
             torch.cuda.synchronize()
             step_ms[name] = round(ev.ms(rev[0], rev[1]) / args.steps, 4)

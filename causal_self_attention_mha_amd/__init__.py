@@ -27,8 +27,10 @@ Functions (names match the C entry points):
 The attention calls take window=W (an int >= 0) for sliding-window attention
 (key j visible to query i iff i - W <= j <= i), which calls the *_window entry
 point; window=None is plain causal attention.  The prologue folds into
-attn_prefill and attn_decode_append (rope=(cos, sin), value_gate=(ve, gate))
-and into attn_bwd (rope=(q_raw, k_raw, cos, sin): dq, dk of the raw heads).  k and v (and the decode caches) may
+attn_prefill and attn_decode_append (rope=(cos, sin), value_gate=(ve, gate)),
+into attn_fwd (rope=(cos, sin): q, k raw; returns o, lse and the rotated
+q_rot, k_rot) and into attn_bwd (rope=(q_raw, k_raw, cos, sin): dq, dk of the
+raw heads).  k and v (and the decode caches) may
 have fewer heads than q (grouped-query attention, H a multiple of H_kv; the
 *_gqa entry points); dk and dv then have the key/value heads' shape.
 bf16 tensors use the bf16 kernels, float32 tensors the fp32 kernels
@@ -115,6 +117,8 @@ def load_library():
     lib.na_attn_bwd_rope.argtypes = [vp, vp, vp, vp, vp, f32p, vp, vp, f32p, f32p, i,
                                      ctypes.c_float, vp, vp, vp, vp, vp, vp, vp, f32p, vp, sz, i,
                                      i, i, i, i, i, vp]
+    lib.na_attn_fwd_rope.argtypes = [vp, vp, vp, f32p, f32p, i, ctypes.c_float, vp, vp, vp,
+                                     f32p, i, i, i, i, i, i, vp]
     lib.na_value_gate_fwd.argtypes = [vp, vp, vp, vp, i, i, i, i, vp]
     lib.na_value_gate_bwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, vp]
     lib.na_qk_norm_rope_bwd.argtypes = [vp, vp, vp, vp, vp, vp, f32p, f32p, vp, i, i, i, i, i,
@@ -125,7 +129,7 @@ def load_library():
                "na_attn_fwd_gqa", "na_attn_bwd_gqa", "na_attn_decode_gqa", "na_attn_prefill",
                "na_qk_norm_rope_fwd", "na_qk_norm_rope_bwd", "na_value_gate_fwd",
                "na_value_gate_bwd", "na_attn_prefill_rope", "na_attn_decode_append",
-               "na_attn_bwd_rope", "na_attn_decode_noalloc"):
+               "na_attn_bwd_rope", "na_attn_decode_noalloc", "na_attn_fwd_rope"):
         getattr(lib, fn).restype = ctypes.c_int
     lib.na_status_string.argtypes = [ctypes.c_int]
     lib.na_status_string.restype = ctypes.c_char_p
@@ -210,8 +214,15 @@ def _kv_heads(q, k):
     return Hk
 
 
-def attn_fwd(q, k, v, o=None, lse=None, window=None):
-    """Causal attention forward.  Returns (o, lse): o like q, lse float32 (B, H, T)."""
+def attn_fwd(q, k, v, o=None, lse=None, window=None, rope=None, eps=1e-6, q_rot=None,
+             k_rot=None):
+    """Causal attention forward.  Returns (o, lse): o like q, lse float32 (B, H, T).
+
+    rope=(cos, sin), float32 (T_tab >= T, 64) tables: q and k are the raw
+    query and key heads, normalised and rotated inside the call
+    (na_attn_fwd_rope: the keys by the prologue kernel, the queries as the
+    forward loads them); returns (o, lse, q_rot, k_rot), the rotated heads
+    being the q and k that attn_bwd takes (with rope=(q, k, cos, sin))."""
     import torch
     lib = load_library()
     Hk = _kv_heads(q, k)
@@ -222,6 +233,20 @@ def attn_fwd(q, k, v, o=None, lse=None, window=None):
     _check_train(("q", "o"), (q, o), dtype)
     _check_buf("lse", lse, torch.float32, (B, H, T), q.device)
     window = _window(window)
+    if rope is not None:
+        cos, sin = rope
+        _require(dtype == torch.bfloat16, "rope: bf16 tensors only")
+        _check_prologue(q, k, cos, sin, None)
+        q_rot = torch.empty_like(q) if q_rot is None else q_rot
+        k_rot = torch.empty_like(k) if k_rot is None else k_rot
+        _check_buf("q_rot", q_rot, torch.bfloat16, q.shape, q.device)
+        _check_buf("k_rot", k_rot, torch.bfloat16, k.shape, q.device)
+        _check(lib, "na_attn_fwd_rope",
+               lib.na_attn_fwd_rope(_ptr(q), _ptr(k), _ptr(v), _ptr(cos), _ptr(sin),
+                                    cos.shape[0], float(eps), _ptr(q_rot), _ptr(k_rot), _ptr(o),
+                                    _ptr(lse), B, T, H, Hk, D,
+                                    -1 if window is None else window, _stream(q)))
+        return o, lse, q_rot, k_rot
     if Hk != H or window is not None:
         _require(dtype == torch.bfloat16, "window / grouped heads: bf16 tensors only")
         w = -1 if window is None else window

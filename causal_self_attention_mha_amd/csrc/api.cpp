@@ -469,6 +469,26 @@ na_status na_qk_norm_rope_fwd(const void* q, const void* k, void* q_out, void* k
                     "na_qk_norm_rope_fwd");
 }
 
+na_status na_attn_fwd_rope(const void* q_raw, const void* k_raw, const void* v,
+                           const float* cos_tab, const float* sin_tab, int T_tab, float eps,
+                           void* q_rot, void* k_rot, void* o, float* lse, int B, int T, int H,
+                           int H_kv, int D, int window, void* stream) {
+  na_status st = check_prologue(B, T, H, H_kv, D, T_tab, eps);
+  if (st) return st;
+  if ((st = check_kv_heads(H, H_kv))) return st;
+  st = check_ptrs({{q_raw, "q_raw"}, {k_raw, "k_raw"}, {v, "v"}, {cos_tab, "cos_tab"},
+                   {sin_tab, "sin_tab"}},
+                  {{q_rot, "q_rot"}, {k_rot, "k_rot"}, {o, "o"}, {lse, "lse"}});
+  if (st) return st;
+  hipError_t e = na::launch_qk_norm_rope_bf16(nullptr, k_raw, nullptr, nullptr, nullptr, k_rot,
+                                              cos_tab, sin_tab, nullptr, B, T, H, H_kv, T_tab,
+                                              eps, false, (hipStream_t)stream);
+  if (e == hipSuccess)
+    e = na::launch_fwd_bf16(q_raw, k_rot, v, o, lse, B, T, H, H_kv, window, (hipStream_t)stream,
+                            cos_tab, sin_tab, eps, q_rot);
+  return hip_status(e, "na_attn_fwd_rope");
+}
+
 na_status na_qk_norm_rope_bwd(const void* q, const void* k, const void* dq_rot,
                               const void* dk_rot, void* dq, void* dk, const float* cos_tab,
                               const float* sin_tab, const int* pos_offset, int B, int T, int H,

@@ -71,15 +71,18 @@ constexpr float kSumLimit = 2147483648.0f;  // 2^31
 // L .. L + T - 1 with L = lens[b] (clamped to [0, Tc - T]): query row r sees
 // cache rows 0 .. L + r.  Without PRE, Tc = T and L = 0 (training).  Masks and
 // tile ranges below compare key rows with query positions L + r.
-// ROPE (prefill only): q holds the raw query heads; each row is RMS-normalised
-// and rotated by the angles of its position (fp32 (T_tab, 64) cos/sin tables)
-// as it is loaded, then rounded to bf16 like any query operand.
+// ROPE: q holds the raw query heads; each row is RMS-normalised and rotated by
+// the angles of its position (fp32 (T_tab, 64) cos/sin tables) as it is
+// loaded, then rounded to bf16 like any query operand.  In the training
+// forward (no PRE) the rotated bf16 rows are also written to qo, the query
+// operand of the backward.
 template <bool WIN, bool PRE, bool ROPE = false>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(
     const u16* __restrict__ q, const u16* __restrict__ k, const u16* __restrict__ v,
     u16* __restrict__ o, float* __restrict__ lse, int B, int T, int Tc, int H, int Hk,
     const int* __restrict__ lens, float c_log2, float scale, int win,
-    const float* __restrict__ cos_t, const float* __restrict__ sin_t, float eps) {
+    const float* __restrict__ cos_t, const float* __restrict__ sin_t, float eps,
+    u16* __restrict__ qo) {
   // two buffers of (K tile, V tile), swizzled (see tile_swz)
   __shared__ __attribute__((aligned(1024))) char kvs[2 * BUF_B];
 
@@ -141,16 +144,22 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(
 #pragma unroll
     for (int kc = 0; kc < 8; ++kc) qreg[kc] = as_bf16x8(ld16(qp + 16 * kc));
   }
-  if constexpr (DIET) {
-#pragma unroll
-    for (int kc = 0; kc < 8; ++kc)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) qreg[kc][e] = to_bf16(static_cast<float>(qreg[kc][e]) * c_log2);
-  }
   if constexpr (ROPE) {
     // the lane holds elements 16 kc + 8 half + e of its row; element i < 64
     // (kc < 4) pairs with i + 64, the same e of qreg[kc + 4]; the other half
     // of the row sits in lane l ^ 32
+    // the angles are loaded first, so that they are in flight with the rows
+    const int p = L + min(qrow, T - 1);  // the row's position in the cache
+    const float* cp = cos_t + static_cast<size_t>(p) * (D / 2) + 8 * half;
+    const float* sp = sin_t + static_cast<size_t>(p) * (D / 2) + 8 * half;
+    float4 ang[4][4];
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) {
+      ang[kc][0] = *reinterpret_cast<const float4*>(cp + 16 * kc);
+      ang[kc][1] = *reinterpret_cast<const float4*>(cp + 16 * kc + 4);
+      ang[kc][2] = *reinterpret_cast<const float4*>(sp + 16 * kc);
+      ang[kc][3] = *reinterpret_cast<const float4*>(sp + 16 * kc + 4);
+    }
     float x[8][8];
     float ss = 0.f;
 #pragma unroll
@@ -162,15 +171,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(
       }
     ss += __shfl_xor(ss, 32, 64);
     const float r = __builtin_amdgcn_rsqf(ss * (1.f / D) + eps);
-    const int p = L + min(qrow, T - 1);  // the row's position in the cache
-    const float* cp = cos_t + static_cast<size_t>(p) * (D / 2) + 8 * half;
-    const float* sp = sin_t + static_cast<size_t>(p) * (D / 2) + 8 * half;
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc) {
-      const float4 c0 = *reinterpret_cast<const float4*>(cp + 16 * kc);
-      const float4 c1 = *reinterpret_cast<const float4*>(cp + 16 * kc + 4);
-      const float4 s0 = *reinterpret_cast<const float4*>(sp + 16 * kc);
-      const float4 s1 = *reinterpret_cast<const float4*>(sp + 16 * kc + 4);
+      const float4 c0 = ang[kc][0], c1 = ang[kc][1], s0 = ang[kc][2], s1 = ang[kc][3];
       const float cs[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
       const float sn[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
 #pragma unroll
@@ -180,6 +183,19 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(
         qreg[kc + 4][e] = to_bf16(fmaf(z1, sn[e], z2 * cs[e]));
       }
     }
+    if constexpr (!PRE) {  // the rotated rows: the backward's q operand
+      if (qrow < T) {
+        u16* op = qo + base + static_cast<size_t>(qrow) * rs + 8 * half;
+#pragma unroll
+        for (int kc = 0; kc < 8; ++kc) st16(op + 16 * kc, __builtin_bit_cast(uint4, qreg[kc]));
+      }
+    }
+  }
+  if constexpr (DIET) {
+#pragma unroll
+    for (int kc = 0; kc < 8; ++kc)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qreg[kc][e] = to_bf16(static_cast<float>(qreg[kc][e]) * c_log2);
   }
 
   f32x16 oacc[4];
@@ -213,7 +229,18 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(
     // One barrier per tile: after it every copy into this buffer has landed
     // and every wavefront is done with the other buffer (tile kt-1), which the
     // next copy may then overwrite.
-    wait_vmem();
+    if constexpr (ROPE && !PRE) {
+      // first tile: the 8 stores of the rotated query rows went out after its
+      // copy (all 8 whenever the wavefront's first row is below T); vector
+      // memory operations retire in issue order, so the copy has landed once
+      // at most those 8 are outstanding, and the stores need not be waited for
+      if (kt == kt_lo && qw0 < T)
+        wait_vmem_but<8>();
+      else
+        wait_vmem();
+    } else {
+      wait_vmem();
+    }
     wait_lds();
     __syncthreads();
     // whole tile above this wavefront's diagonal, or before its rows' windows
@@ -406,17 +433,20 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(
 }  // namespace
 
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
-                           int B, int T, int H, int Hk, int window, hipStream_t s) {
+                           int B, int T, int H, int Hk, int window, hipStream_t s,
+                           const float* cos_t, const float* sin_t, float eps, void* q_rot) {
   const float scale = 1.0f / sqrtf(static_cast<float>(D));
   const float c_log2 = scale * 1.4426950408889634f;
   const int n_qt = (T + BQ - 1) / BQ;
   const dim3 grid(static_cast<unsigned>(n_qt) * B * H);
   const bool win = window >= 0 && window < T - 1;  // else every row sees all its keys
-  return launch(win ? fwd_bf16_kernel<true, false> : fwd_bf16_kernel<false, false>, grid,
-                dim3(64 * NW), 0, s, static_cast<const u16*>(q), static_cast<const u16*>(k),
-                static_cast<const u16*>(v), static_cast<u16*>(o), lse, B, T, T, H, Hk,
-                static_cast<const int*>(nullptr), c_log2, scale, win ? window : T,
-                static_cast<const float*>(nullptr), static_cast<const float*>(nullptr), 0.f);
+  const bool rope = cos_t != nullptr;
+  auto* kern = rope ? (win ? fwd_bf16_kernel<true, false, true> : fwd_bf16_kernel<false, false, true>)
+                    : (win ? fwd_bf16_kernel<true, false> : fwd_bf16_kernel<false, false>);
+  return launch(kern, grid, dim3(64 * NW), 0, s, static_cast<const u16*>(q),
+                static_cast<const u16*>(k), static_cast<const u16*>(v), static_cast<u16*>(o), lse,
+                B, T, T, H, Hk, static_cast<const int*>(nullptr), c_log2, scale,
+                win ? window : T, cos_t, sin_t, eps, static_cast<u16*>(q_rot));
 }
 
 // Prefill: the T new rows of k_new, v_new go to cache rows L .. L + T - 1
@@ -521,7 +551,8 @@ hipError_t launch_prefill_bf16(const void* q, const void* k_new, const void* v_n
                     : (win ? fwd_bf16_kernel<true, true> : fwd_bf16_kernel<false, true>);
   return launch(kern, grid, dim3(64 * NW), 0, s, static_cast<const u16*>(q),
                 static_cast<const u16*>(kc), static_cast<const u16*>(vc), static_cast<u16*>(o),
-                lse, B, T, Tc, H, Hk, lens, c_log2, scale, win ? window : Tc, cos_t, sin_t, eps);
+                lse, B, T, Tc, H, Hk, lens, c_log2, scale, win ? window : Tc, cos_t, sin_t, eps,
+                static_cast<u16*>(nullptr));
 }
 
 }  // namespace na

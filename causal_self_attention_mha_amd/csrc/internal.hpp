@@ -21,9 +21,14 @@ constexpr int kHeadDim = 128;
 // Hk: key/value heads (H a multiple of Hk; query head h reads head h / (H / Hk)),
 // Hk = H for plain multi-head attention.
 
-// bf16 forward: o, lse from q, k, v.
+// bf16 forward: o, lse from q, k, v.  With cos_t non-null, q holds the raw
+// query heads, RMS-normalised (eps) and rotated at positions t by the fp32
+// (>= T, D/2) cos/sin tables as the forward loads them; the rotated bf16 rows
+// are written to q_rot (B, T, H, D).
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
-                           int B, int T, int H, int Hk, int window, hipStream_t s);
+                           int B, int T, int H, int Hk, int window, hipStream_t s,
+                           const float* cos_t = nullptr, const float* sin_t = nullptr,
+                           float eps = 0.f, void* q_rot = nullptr);
 
 // bf16 prefill over a KV cache: k_new, v_new (B, T, Hk, D) appended at cache
 // rows lens[b] .. lens[b] + T - 1 (lens clamped to [0, Tc - T] on the device),
@@ -93,7 +98,7 @@ hipError_t launch_decode_bf16(const void* q, const void* kc, const void* vc, con
 // at positions t + clamp(off[b], 0, T_tab - T) (off may be null: positions t)
 // of the fp32 (T_tab, D/2) cos/sin tables.  Forward: outq, outk = y(q), y(k)
 // (dyq, dyk unused).  Backward: outq, outk = gradients of the inputs given
-// dyq, dyk, the gradients of the outputs.
+// dyq, dyk, the gradients of the outputs.  q == nullptr: the key rows only.
 hipError_t launch_qk_norm_rope_bf16(const void* q, const void* k, const void* dyq,
                                     const void* dyk, void* outq, void* outk, const float* cos_t,
                                     const float* sin_t, const int* off, int B, int T, int H,

@@ -56,7 +56,9 @@ __device__ __forceinline__ void st16_stream(u16* p, uint4 v) {
 }
 
 // BWD = false: x -> y.  BWD = true: (x, dy) -> dx.  Rows r < H come from the
-// query tensors, rows H .. H + Hk - 1 from the key tensors.
+// query tensors, rows H .. H + Hk - 1 from the key tensors; with xq == nullptr
+// only the key rows are processed (the training forward then normalises and
+// rotates the query rows itself, as it loads them).
 template <bool BWD>
 __global__ __launch_bounds__(256) void qk_norm_rope_kernel(
     const u16* __restrict__ xq, const u16* __restrict__ xk, const u16* __restrict__ gq,
@@ -87,7 +89,7 @@ __global__ __launch_bounds__(256) void qk_norm_rope_kernel(
     return r < H ? ((size_t)pos * H + r) * kHeadDim + lane * 8
                  : ((size_t)pos * Hk + (r - H)) * kHeadDim + lane * 8;
   };
-  for (int r0 = 0; r0 < R; r0 += kRowsAhead) {
+  for (int r0 = xq != nullptr ? 0 : H; r0 < R; r0 += kRowsAhead) {
     uint4 xv[kRowsAhead], gv[kRowsAhead];
 #pragma unroll
     for (int u = 0; u < kRowsAhead; ++u) {

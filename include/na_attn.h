@@ -261,6 +261,27 @@ na_status na_qk_norm_rope_fwd(const void* q, const void* k, void* q_out, void* k
                               void* stream);
 
 /*
+ * Training forward with the QK prologue folded in (blog section 1 "GPT model":
+ * QK norm and rotary embedding ahead of attention; section 5: the attention
+ * call): the readings of na_qk_norm_rope_fwd at positions p = t, then the
+ * causal attention of na_attn_fwd_gqa (window as there).  q_raw: bf16
+ * (B, T, H, D) raw query heads; k_raw: bf16 (B, T, H_kv, D) raw key heads;
+ * v: bf16 (B, T, H_kv, D) (the value gate's output where the layer has one).
+ * Outputs: q_rot, k_rot, bf16 of the shapes of q_raw, k_raw, the rotated heads
+ * (what na_qk_norm_rope_fwd writes as q_out, k_out, up to the rounding of the
+ * row's mean square: the operands the backward takes as q, k, e.g. in
+ * na_attn_bwd_rope); o, lse as in na_attn_fwd_gqa.  cos_tab, sin_tab: fp32
+ * (T_tab, D/2), T_tab >= T; eps >= 0 and finite.  Enqueues two kernels: the
+ * key rows' prologue, then the forward, which normalises and rotates each
+ * query row as it loads it and writes it to q_rot, so the rotated queries
+ * are not read back.  All buffers distinct.
+ */
+na_status na_attn_fwd_rope(const void* q_raw, const void* k_raw, const void* v,
+                           const float* cos_tab, const float* sin_tab, int T_tab, float eps,
+                           void* q_rot, void* k_rot, void* o, float* lse, int B, int T, int H,
+                           int H_kv, int D, int window, void* stream);
+
+/*
  * Backward of na_qk_norm_rope_fwd: given q, k (the forward's inputs) and
  * dq_rot, dk_rot (the gradients of q_out, k_out, e.g. what na_attn_bwd
  * returns), writes dq, dk (the gradients of q, k):

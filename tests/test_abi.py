@@ -44,7 +44,7 @@ def test_header_declares_the_entry_points():
               "na_attn_fwd_gqa", "na_attn_bwd_gqa", "na_attn_decode_gqa", "na_attn_prefill",
               "na_qk_norm_rope_fwd", "na_qk_norm_rope_bwd", "na_value_gate_fwd",
               "na_value_gate_bwd", "na_attn_prefill_rope", "na_attn_decode_append",
-              "na_attn_bwd_rope"):
+              "na_attn_bwd_rope", "na_attn_fwd_rope"):
         assert s in syms
 
 
@@ -252,6 +252,27 @@ def test_bwd_rope_checks_its_arguments(lib):
     assert call(g=gate[:3] + (gate[2],)) == INVALID       # dgate aliases dve
 
 
+def test_fwd_rope_checks_its_arguments(lib):
+    p = [A + 0x100 * i for i in range(9)]  # q_raw k_raw v cos sin | q_rot k_rot o lse
+    call = lambda ptrs=p, T_tab=64, eps=1e-6, H=2, Hk=2, D=128, win=-1: (  # noqa: E731
+        lib.na_attn_fwd_rope(*ptrs[:5], T_tab, eps, *ptrs[5:], 1, 64, H, Hk, D, win, None))
+    assert call(T_tab=32) == INVALID and b"T_tab" in lib.na_last_error()
+    assert call(eps=-1.0) == INVALID and b"eps" in lib.na_last_error()
+    assert call(eps=float("inf")) == INVALID
+    assert call(D=64) == UNSUPPORTED
+    assert call(Hk=3) == INVALID
+    assert call(H=4, Hk=3) == INVALID
+    bad = list(p)
+    bad[5] = bad[0]              # q_rot aliases q_raw
+    assert call(bad) == INVALID and b"alias" in lib.na_last_error()
+    bad = list(p)
+    bad[6] = bad[7]              # k_rot aliases o
+    assert call(bad) == INVALID
+    bad = list(p)
+    bad[8] = A + 4               # lse not 16-byte aligned
+    assert call(bad) == INVALID
+
+
 def test_value_gate_checks_its_arguments(lib):
     p = [A + 0x100 * i for i in range(5)]
     assert lib.na_value_gate_fwd(*p[:4], 1, 8, 2, 64, None) == UNSUPPORTED
@@ -332,6 +353,8 @@ _NULL_CASES = [
     ("na_value_gate_bwd", lambda p: (*p[:5], 1, 8, 2, 128, None), range(5)),
     ("na_attn_bwd_rope", lambda p: (*p[:10], 64, 1e-6, None, None, *p[10:13], None, None,
                                     *p[13:15], 1 << 26, 1, 64, 2, 2, 128, -1, None), range(15)),
+    ("na_attn_fwd_rope", lambda p: (*p[:5], 64, 1e-6, *p[5:9], 1, 64, 2, 2, 128, -1, None),
+     range(9)),
 ]
 
 

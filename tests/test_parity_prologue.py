@@ -337,3 +337,78 @@ def test_bwd_with_prologue_folded_in_d20_sampled(dev):
         assert_close(f"dk[{b},{h}]", to_host(dk[b:b + 1, :, h:h + 1]),
                      oracle.qk_norm_rope_backward(xk, rdk, c64, s64, EPS), BF16_REL_L2,
                      BF16_MAX_ABS)
+
+
+@pytest.mark.parametrize("B,T,H,Hk,Wn", [(1, 1, 1, 1, None), (2, 96, 2, 2, None),
+                                         (2, 300, 4, 2, None), (1, 257, 2, 2, 64),
+                                         (3, 130, 6, 3, 40)])
+def test_fwd_with_prologue_folded_in(dev, B, T, H, Hk, Wn):
+    """na_attn_fwd_rope (the key rows by the prologue kernel, the query rows
+    normalised and rotated as the forward loads them) against the oracle chain
+    prologue -> attention forward: o, lse, and the rotated heads q_rot, k_rot.
+    k_rot is the prologue kernel's own output bit for bit; q_rot is within one
+    bf16 step of it (the row's mean square is summed in another order; plus
+    2^-16 where the rotation cancels to nearly zero, on rows of RMS 1).  Then
+    the folded backward on the folded forward's outputs, against the oracle
+    chain's gradients of the raw heads."""
+    import torch
+    import causal_self_attention_mha_amd as na
+    tr = W.make_train_inputs("d20", B=B, T=T, H=H, seed=660 + T)
+    kv = lambda a: np.ascontiguousarray(a[:, :, :Hk])  # noqa: E731
+    c, s = tables("rope", T, 0)
+    q_raw, k_raw = to_device(tr.q_store, dev), to_device(kv(tr.k_store), dev)
+    v, do = to_device(kv(tr.v_store), dev), to_device(tr.do_store, dev)
+    ct, sn = torch.from_numpy(c).to(dev), torch.from_numpy(s).to(dev)
+    o, lse, qr, kr = na.attn_fwd(q_raw, k_raw, v, window=Wn, rope=(ct, sn))
+    qr2, kr2 = na.qk_norm_rope_fwd(q_raw, k_raw, ct, sn)
+    dq, dk, dv = na.attn_bwd(qr, kr, v, o, do, lse, window=Wn, rope=(q_raw, k_raw, ct, sn))
+    torch.cuda.synchronize()
+    assert torch.equal(kr, kr2)
+    step = (qr.float() - qr2.float()).abs() - 2.0 ** -7 * qr2.float().abs() - 2.0 ** -16
+    assert float(step.max()) <= 0.0
+    c64, s64 = c.astype(np.float64), s.astype(np.float64)
+    xq, xk = tr.q.astype(np.float64), kv(tr.k).astype(np.float64)
+    rq = oracle.qk_norm_rope_forward(xq, c64, s64, EPS)
+    rk = oracle.qk_norm_rope_forward(xk, c64, s64, EPS)
+    ro, rl = oracle.forward(rq, rk, kv(tr.v), window=Wn)
+    assert_close("q_rot", to_host(qr), rq, BF16_REL_L2, BF16_MAX_ABS)
+    assert_close("k_rot", to_host(kr), rk, BF16_REL_L2, BF16_MAX_ABS)
+    assert_close("o", to_host(o), ro, BF16_REL_L2, BF16_MAX_ABS)
+    assert_close("lse", to_host(lse), rl, BF16_REL_L2, BF16_MAX_ABS)
+    rdq, rdk, rdv, _ = oracle.backward(rq, rk, kv(tr.v), tr.do, window=Wn)
+    assert_close("dv", to_host(dv), rdv, BF16_REL_L2, BF16_MAX_ABS)
+    assert_close("dq", to_host(dq), oracle.qk_norm_rope_backward(xq, rdq, c64, s64, EPS),
+                 BF16_REL_L2, BF16_MAX_ABS)
+    assert_close("dk", to_host(dk), oracle.qk_norm_rope_backward(xk, rdk, c64, s64, EPS),
+                 BF16_REL_L2, BF16_MAX_ABS)
+
+
+def test_fwd_with_prologue_folded_in_d20_sampled(dev):
+    """The d20 shape in the launch the benchmark times: the folded forward
+    against the two-step GPU path (prologue kernel, then the forward) on the
+    full tensors, and o, lse against the oracle chain on sampled heads."""
+    import torch
+    import causal_self_attention_mha_amd as na
+    tr = W.make_train_inputs("d20", seed=23)
+    B, T, H = tr.q.shape[:3]
+    c, s = tables("rope", T, 0)
+    q_raw, k_raw, v = (to_device(a, dev) for a in (tr.q_store, tr.k_store, tr.v_store))
+    ct, sn = torch.from_numpy(c).to(dev), torch.from_numpy(s).to(dev)
+    o, lse, qr, kr = na.attn_fwd(q_raw, k_raw, v, rope=(ct, sn))
+    qr2, kr2 = na.qk_norm_rope_fwd(q_raw, k_raw, ct, sn)
+    o2, lse2 = na.attn_fwd(qr2, kr2, v)
+    torch.cuda.synchronize()
+    assert torch.equal(kr, kr2)
+    step = (qr.float() - qr2.float()).abs() - 2.0 ** -7 * qr2.float().abs() - 2.0 ** -16
+    assert float(step.max()) <= 0.0
+    assert_close("o vs two-step", to_host(o), to_host(o2), BF16_REL_L2, BF16_MAX_ABS)
+    assert_close("lse vs two-step", to_host(lse), to_host(lse2), BF16_REL_L2, BF16_MAX_ABS)
+    c64, s64 = c.astype(np.float64), s.astype(np.float64)
+    for b, h in ((0, 0), (31, 9), (17, 5)):
+        sl = (slice(b, b + 1), slice(None), slice(h, h + 1))
+        rq = oracle.qk_norm_rope_forward(tr.q[sl].astype(np.float64), c64, s64, EPS)
+        rk = oracle.qk_norm_rope_forward(tr.k[sl].astype(np.float64), c64, s64, EPS)
+        ro, rl = oracle.forward(rq, rk, tr.v[sl])
+        assert_close(f"o[{b},{h}]", to_host(o[sl]), ro, BF16_REL_L2, BF16_MAX_ABS)
+        assert_close(f"lse[{b},{h}]", to_host(lse[b:b + 1, h:h + 1]), rl, BF16_REL_L2,
+                     BF16_MAX_ABS)
