@@ -65,4 +65,14 @@ def test_outputs_checked_before_any_call(dev):
                                                         device=dev))
     with pytest.raises(ValueError, match="workspace has"):
         na.attn_decode(qd, kc, kc, lens, workspace=torch.empty(8, dtype=torch.uint8, device=dev))
+    # the forward with the queries' prologue folded in: tables and rotated outputs
+    cos = torch.zeros((T, D // 2), dtype=torch.float32, device=dev)
+    with pytest.raises(ValueError, match="cos must be contiguous"):
+        na.attn_fwd(q, k, v, rope=(cos.cpu(), cos))
+    with pytest.raises(ValueError, match="T_tab >= T"):
+        na.attn_fwd(q, k, v, rope=(cos[:T - 1], cos[:T - 1]))
+    with pytest.raises(ValueError, match="q_rot has shape"):
+        na.attn_fwd(q, k, v, rope=(cos, cos), q_rot=torch.empty_like(q)[:, :T - 1])
+    with pytest.raises(ValueError, match="k_rot is on cpu"):
+        na.attn_fwd(q, k, v, rope=(cos, cos), k_rot=torch.empty(k.shape, dtype=k.dtype))
     torch.cuda.synchronize()
